@@ -1,0 +1,535 @@
+"""CPU oracle for the MoE expert-MLP path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The GPU library never calls it and
+shares no code with it.
+
+Plain, slow, obviously correct: numpy in float64, one Python loop per expert,
+a library matmul / stable sort as the only "fast" primitives.  No blocking, no
+fusion and no reordering beyond what the definitions below state.
+
+Sources (web pages; titles as published, sections as headed on the page):
+
+[PG1] "NVIDIA presents an efficient path for training biological MoE models"
+      (sitech.ge).  Sections: "Grouped experts instead of a Python loop",
+      "Reducing memory and quantisation cost".
+[PG2] "Efficient MoE training for biological foundation models (NVIDIA)"
+      (news.bpdata.com).  Sections: "Why dense and MoE models differ",
+      "1) Fragmented expert kernels", "2) Model size and activation memory",
+      "3) Quantisation overhead in low-precision training".
+[PG3] "Nous Research scales expert parallelism with DeepEP" (seventnews.com),
+      paragraph on practical implications (Top-k, capacity factor).
+[PG4] "NVIDIA NeMo AutoModel: 3.7x faster MoE fine-tuning with expert
+      parallelism and DeepEP" (seventnews.com).  Sections "Background",
+      "Using Transformers v5 features" (eager / batched_mm / grouped_mm).
+
+The pages state the problem (tokens, per-expert weights, split_sizes,
+routing weights scaled inside the grouped MLP, MXFP8 = 8-bit elements with one
+scale per 32 consecutive values, 16-bit master weights) but not every formula.
+Where they are silent this module takes the readings listed here:
+
+  R1  router: softmax over the E logits, keep the k largest; weights are the
+      softmax restricted to the chosen set (renormalize=True) or the plain
+      softmax over all E (renormalize=False); evaluated in float64, stored
+      float32.
+  R2  selection order: larger logit first; equal logits -> lower expert id;
+      +0 == -0.  Slot j=0 holds the top expert.
+  R3  permutation: pair p = t*k + j; stable by expert, then by p.
+  R4  expert weights nn.Linear-style [out, in]: W_gu [E, 2F, H] with gate rows
+      0..F-1 and up rows F..2F-1; W_dn [E, H, F]; no biases.
+  R5  SwiGLU(g, u) = silu(g) * u, silu(z) = z / (1 + exp(-z)).
+  R6  ScaledSwiGLU: the routing weight of the (token, expert) pair multiplies
+      the SwiGLU output before the down projection; the combine is then a
+      plain sum over the k slots.
+  R7  MXFP8 (OCP Microscaling reading): per block of 32 values along the
+      GEMM's K, scale exponent s = floor(log2 amax) - 8 clamped to
+      [-127, 127] (amax = 0 -> -127), stored E8M0 as s + 127; elements
+      E4M3 (bias 7, max 448, no infinities) of v * 2^-s, round to nearest
+      even, saturating at +-448, sign kept on zero.
+  R8  MXFP8 layer: quantise x_perm and W_gu along H, A and W_dn along F, GEMMs
+      on the dequantised values; backward quantises each GEMM operand along
+      that GEMM's K, token-direction blocks restarting at each expert segment
+      and zero-padded at its end.
+
+Pins of this module against things other than itself live in
+``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+f64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# Router top-k  [PG3 practical implications: Top-k routing;
+#                PG2 "Why dense and MoE models differ": a small subset of
+#                experts is active per token]
+# --------------------------------------------------------------------------
+def route_topk(logits: np.ndarray, k: int, renormalize: bool = True
+               ) -> Tuple[np.ndarray, np.ndarray]:
+    """logits float32 [T, E] -> (topk_idx int32 [T, k], topk_w float32 [T, k]).
+
+    Readings R1, R2.  The selection compares the float32 logits exactly.
+    """
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    if not (1 <= k <= E):
+        raise ValueError("need 1 <= k <= E")
+    lv = lg.astype(f64) + 0.0          # -0.0 + 0.0 == +0.0 (R2)
+    # a stable sort keeps the lower expert id first among equal logits
+    order = np.argsort(-lv, axis=1, kind="stable")
+    idx = order[:, :k]
+    m = lv.max(axis=1, keepdims=True)
+    ex = np.exp(lv - m)
+    sel = np.take_along_axis(ex, idx, axis=1)
+    denom = sel.sum(axis=1, keepdims=True) if renormalize else \
+        ex.sum(axis=1, keepdims=True)
+    w = sel / denom
+    return idx.astype(np.int32), w.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Permutation into expert-contiguous order with split_sizes
+# [PG1 "Grouped experts instead of a Python loop"; PG2 "1) Fragmented expert
+#  kernels": the grouped call receives the per-expert token counts
+#  (split_sizes); PG4 "Using Transformers v5 features": grouped_mm runs on
+#  sorted tokens]
+# --------------------------------------------------------------------------
+def permute_index(topk_idx: np.ndarray, E: int) -> Dict[str, np.ndarray]:
+    """topk_idx int [T, k] -> split_sizes [E], offsets [E+1], row_map [T*k],
+    src_row [T*k] (all int32).  Reading R3.
+
+    row_map[p] is the expert-ordered row of pair p; src_row is its inverse.
+    """
+    e = np.asarray(topk_idx).reshape(-1).astype(np.int64)
+    if e.size and (e.min() < 0 or e.max() >= E):
+        raise ValueError("expert id out of range")
+    split = np.bincount(e, minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(split)
+    src_row = np.argsort(e, kind="stable")   # by expert, then by pair index
+    row_map = np.empty_like(src_row)
+    row_map[src_row] = np.arange(e.size)
+    return {
+        "split_sizes": split.astype(np.int32),
+        "offsets": offsets.astype(np.int32),
+        "row_map": row_map.astype(np.int32),
+        "src_row": src_row.astype(np.int32),
+    }
+
+
+def permute_rows(x: np.ndarray, src_row: np.ndarray, k: int) -> np.ndarray:
+    """x_perm[r] = x[src_row[r] // k] (a row copy, any dtype)."""
+    return np.asarray(x)[np.asarray(src_row, dtype=np.int64) // k]
+
+
+def permute_weights(topk_w: np.ndarray, src_row: np.ndarray) -> np.ndarray:
+    """w_perm[r] = topk_w.flat[src_row[r]] (float32)."""
+    return np.asarray(topk_w, dtype=np.float32).reshape(-1)[
+        np.asarray(src_row, dtype=np.int64)]
+
+
+# --------------------------------------------------------------------------
+# Grouped MLP forward: grouped GEMM gate/up -> ScaledSwiGLU -> grouped GEMM
+# down  [PG1 "Reducing memory and quantisation cost": GroupedLinear ->
+#  ScaledSwiGLU -> GroupedLinear; PG1 "Grouped experts instead of a Python
+#  loop": routing weights scaled inside the grouped MLP]
+# --------------------------------------------------------------------------
+def silu(z: np.ndarray) -> np.ndarray:
+    """R5: z * sigmoid(z) = z / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def _as_f64(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) or any float array -> float64."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(f64)
+    return a.astype(f64)
+
+
+def grouped_mlp_fwd(x_perm, w_gu, w_dn, w_perm, offsets,
+                    keep: bool = False) -> Dict[str, np.ndarray]:
+    """Per expert e (ascending), rows [offsets[e], offsets[e+1]):
+         h1 = X_e W_gu[e]^T ; g = h1[:, :F] ; u = h1[:, F:]
+         a  = w * silu(g) * u           (R6: scaled before the down proj)
+         z  = a W_dn[e]^T
+    Returns z (float64 [rows, H]); with keep=True also h1 and a.
+    ``w_perm`` None means weight 1 (unweighted MLP).
+    """
+    E = len(offsets) - 1
+    rows = np.asarray(x_perm).shape[0]
+    F = np.asarray(w_gu).shape[1] // 2
+    H = np.asarray(w_dn).shape[1]
+    z = np.zeros((rows, H), dtype=f64)
+    h1_all = np.zeros((rows, 2 * F), dtype=f64) if keep else None
+    a_all = np.zeros((rows, F), dtype=f64) if keep else None
+    w = np.ones(rows) if w_perm is None else np.asarray(w_perm, dtype=f64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        X = _as_f64(x_perm[lo:hi])
+        h1 = X @ _as_f64(w_gu[e]).T
+        g, u = h1[:, :F], h1[:, F:]
+        a = w[lo:hi, None] * silu(g) * u
+        z[lo:hi] = a @ _as_f64(w_dn[e]).T
+        if keep:
+            h1_all[lo:hi] = h1
+            a_all[lo:hi] = a
+    out = {"z": z}
+    if keep:
+        out["h1"] = h1_all
+        out["a"] = a_all
+    return out
+
+
+# --------------------------------------------------------------------------
+# Unpermute / combine back to token order
+# [PG4 "Sources of speedup": dispatch and combine around the expert compute]
+# --------------------------------------------------------------------------
+def unpermute(z_perm: np.ndarray, row_map: np.ndarray, k: int,
+              topk_w: Optional[np.ndarray] = None) -> np.ndarray:
+    """y[t] = sum_{j ascending} c_j * z[row_map[t*k + j]], with c_j = 1
+    (weights already applied in the MLP, R6) or c_j = topk_w[t, j]."""
+    z = _as_f64(z_perm)
+    rm = np.asarray(row_map, dtype=np.int64).reshape(-1, k)
+    T = rm.shape[0]
+    y = np.zeros((T, z.shape[1]), dtype=f64)
+    for j in range(k):
+        c = 1.0 if topk_w is None else \
+            np.asarray(topk_w, dtype=f64).reshape(T, k)[:, j:j + 1]
+        y += c * z[rm[:, j]]
+    return y
+
+
+def layer_fwd(x, logits, w_gu, w_dn, k: int, renormalize: bool = True,
+              keep: bool = False) -> Dict[str, np.ndarray]:
+    """Whole forward: route -> permute -> grouped MLP -> unpermute."""
+    E = np.asarray(w_gu).shape[0]
+    idx, w = route_topk(logits, k, renormalize)
+    maps = permute_index(idx, E)
+    x_perm = permute_rows(x, maps["src_row"], k)
+    w_perm = permute_weights(w, maps["src_row"])
+    mlp = grouped_mlp_fwd(x_perm, w_gu, w_dn, w_perm, maps["offsets"],
+                          keep=keep)
+    y = unpermute(mlp["z"], maps["row_map"], k)
+    out = {"topk_idx": idx, "topk_w": w, "w_perm": w_perm, "x_perm": x_perm,
+           "y": y, **maps, **mlp}
+    return out
+
+
+# --------------------------------------------------------------------------
+# Backward  [PG1 "Reducing memory and quantisation cost": the fused forward
+#  op has a counterpart in the backward pass]
+# --------------------------------------------------------------------------
+def grouped_mlp_bwd(dz_perm, x_perm, w_gu, w_dn, w_perm, offsets
+                    ) -> Dict[str, np.ndarray]:
+    """Gradients of grouped_mlp_fwd's z w.r.t. x_perm, W_gu, W_dn, w_perm.
+
+    Per expert, with s = sigmoid(g):
+      dA  = dZ W_dn[e]
+      dg  = dA * w * u * s * (1 + g * (1 - s))   (d silu / dg)
+      du  = dA * w * silu(g)
+      dw  = sum_f dA * silu(g) * u
+      dW_dn[e] = dZ^T A ;  dW_gu[e] = dH1^T X ;  dX = dH1 W_gu[e]
+    Experts without tokens get dW = 0.
+    """
+    E = len(offsets) - 1
+    rows = np.asarray(x_perm).shape[0]
+    F = np.asarray(w_gu).shape[1] // 2
+    H = np.asarray(w_dn).shape[1]
+    w = np.ones(rows) if w_perm is None else np.asarray(w_perm, dtype=f64)
+    dx = np.zeros((rows, H), dtype=f64)
+    dh1_all = np.zeros((rows, 2 * F), dtype=f64)
+    dw_perm = np.zeros(rows, dtype=f64)
+    dw_gu = np.zeros((E, 2 * F, H), dtype=f64)
+    dw_dn = np.zeros((E, H, F), dtype=f64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        X = _as_f64(x_perm[lo:hi])
+        Wgu = _as_f64(w_gu[e])
+        Wdn = _as_f64(w_dn[e])
+        dZ = _as_f64(dz_perm[lo:hi])
+        h1 = X @ Wgu.T
+        g, u = h1[:, :F], h1[:, F:]
+        s = sigmoid(g)
+        sg = g * s
+        we = w[lo:hi, None]
+        A = we * sg * u
+        dA = dZ @ Wdn
+        dg = dA * we * u * (s * (1.0 + g * (1.0 - s)))
+        du = dA * we * sg
+        dh1 = np.concatenate([dg, du], axis=1)
+        dw_perm[lo:hi] = (dA * sg * u).sum(axis=1)
+        dw_dn[e] = dZ.T @ A
+        dw_gu[e] = dh1.T @ X
+        dx[lo:hi] = dh1 @ Wgu
+        dh1_all[lo:hi] = dh1
+    return {"dx_perm": dx, "dh1": dh1_all, "dw_perm": dw_perm,
+            "dw_gu": dw_gu, "dw_dn": dw_dn}
+
+
+def gather_rows(src: np.ndarray, src_row: np.ndarray, k: int) -> np.ndarray:
+    """dst[r] = src[src_row[r] // k]  (dY -> dZ in the backward pass)."""
+    return permute_rows(src, src_row, k)
+
+
+def probs_grad(dw_perm: np.ndarray, row_map: np.ndarray, k: int
+               ) -> np.ndarray:
+    """dprobs[t, j] = dw_perm[row_map[t*k + j]]."""
+    rm = np.asarray(row_map, dtype=np.int64)
+    return np.asarray(dw_perm, dtype=f64)[rm].reshape(-1, k)
+
+
+def layer_bwd(x, logits, w_gu, w_dn, dy, k: int, renormalize: bool = True
+              ) -> Dict[str, np.ndarray]:
+    """Backward of layer_fwd's y w.r.t. x, W_gu, W_dn and topk_w (routing
+    indices held fixed): dZ = gather(dY); MLP backward; dx = unweighted
+    combine of dX_perm; dprobs from dw_perm."""
+    fwd = layer_fwd(x, logits, w_gu, w_dn, k, renormalize)
+    dz = gather_rows(_as_f64(dy), fwd["src_row"], k)
+    g = grouped_mlp_bwd(dz, fwd["x_perm"], w_gu, w_dn, fwd["w_perm"],
+                        fwd["offsets"])
+    dx = unpermute(g["dx_perm"], fwd["row_map"], k)
+    dprobs = probs_grad(g["dw_perm"], fwd["row_map"], k)
+    return {**fwd, "dz": dz, **g, "dx": dx, "dprobs": dprobs}
+
+
+# --------------------------------------------------------------------------
+# MXFP8: E4M3 elements, one E8M0 scale per 32 consecutive values
+# [PG1 "Reducing memory and quantisation cost" and PG2 "2) Model size and
+#  activation memory": 8-bit elements, one scale per block of 32 consecutive
+#  values; PG2 "3) Quantisation overhead": 16-bit master weights quantised]
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+E4M3_EMAX = 8          # exponent of the largest normal (448 = 1.75 * 2^8)
+MX_BLOCK = 32
+
+
+def e8m0_exponent(amax: np.ndarray) -> np.ndarray:
+    """R7 scale exponent s (int) from a block's amax >= 0 (float64).
+
+    floor(log2 amax) comes from frexp (amax = m * 2^ex, m in [0.5, 1)), so it
+    is exact; amax = 0 gives the clamp -127."""
+    amax = np.asarray(amax, dtype=f64)
+    _, ex = np.frexp(amax)
+    s = ex.astype(np.int64) - 1 - E4M3_EMAX
+    s = np.where(amax > 0, s, -127)
+    return np.clip(s, -127, 127)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """float64 (already scaled) -> OCP E4M3 code (uint8), round to nearest
+    even, saturating at +-448, sign kept (also for zero results)."""
+    v = np.asarray(v, dtype=f64)
+    sign = np.signbit(v).astype(np.uint8) << 7
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    e = ex.astype(np.int64) - 1                 # floor(log2 a) for a > 0
+    e = np.where(a > 0, e, -7)
+    e = np.maximum(e, -6)                       # below 2^-6: subnormal grid
+    quantum = np.ldexp(1.0, e - 3)              # 3 mantissa bits
+    q = np.rint(a / quantum).astype(np.int64)   # exact division; RNE
+    # q in [0, 16]; q == 16 carries into the next binade
+    carry = q >= 16
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 8, q)
+    normal = q >= 8
+    code = np.where(normal, ((e + 7) << 3) | (q - 8), q)
+    code = np.where(a >= E4M3_MAX, 0x7E, code)  # saturation
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """OCP E4M3 code -> float64 (0x7F / 0xFF are NaN)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ef = (c >> 3) & 0xF
+    m = c & 7
+    val = np.where(ef == 0, np.ldexp(m.astype(f64), -9),
+                   np.ldexp((8 + m).astype(f64), ef - 10))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def mx_quantize_blocks(v: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """v float64 [..., nb, 32] -> (codes uint8 same shape, scale u8 [..., nb]).
+    R7 step by step: amax -> s -> E8M0 code s+127 -> E4M3(v * 2^-s)."""
+    v = np.asarray(v, dtype=f64)
+    amax = np.abs(v).max(axis=-1)
+    s = e8m0_exponent(amax)
+    scaled = np.ldexp(v, -s[..., None])
+    codes = e4m3_encode(scaled)
+    return codes, (s + 127).astype(np.uint8)
+
+
+def mx_dequantize_blocks(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    s = np.asarray(scales, dtype=np.int64) - 127
+    return np.ldexp(e4m3_decode(codes), s[..., None])
+
+
+def mxfp8_quantize_rows(a: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Row-wise: [R, C] (C % 32 == 0) -> codes u8 [R, C], scales u8 [R, C/32];
+    blocks run along each row (the row is the GEMM's K)."""
+    a = _as_f64(a)
+    R, C = a.shape
+    if C % MX_BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    codes, sc = mx_quantize_blocks(a.reshape(R, C // MX_BLOCK, MX_BLOCK))
+    return codes.reshape(R, C), sc
+
+
+def mxfp8_quantize_cols(a: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Column-wise: [R, C] (R % 32 == 0) -> codes u8 [C, R] (transposed so the
+    blocked dimension is contiguous), scales u8 [C, R/32]."""
+    return mxfp8_quantize_rows(_as_f64(a).T)
+
+
+def mxfp8_quantize_segments(a: np.ndarray, seg_offsets: np.ndarray
+                            ) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-segment column-wise (token direction, R8): rows of ``a`` [R, C] are
+    split at seg_offsets; within a segment blocks of 32 rows start at the
+    segment start, the last one zero-padded.  Output codes u8 [C, Rp] and
+    scales u8 [C, Rp/32], where each segment occupies ceil(n/32)*32 columns
+    starting at padded offset sum_{e'<e} ceil(n_e'/32)*32."""
+    a = _as_f64(a)
+    C = a.shape[1]
+    segs = []
+    for e in range(len(seg_offsets) - 1):
+        lo, hi = int(seg_offsets[e]), int(seg_offsets[e + 1])
+        n = hi - lo
+        npad = -(-n // MX_BLOCK) * MX_BLOCK
+        blk = np.zeros((C, npad), dtype=f64)
+        blk[:, :n] = a[lo:hi].T
+        segs.append(blk)
+    full = np.concatenate(segs, axis=1) if segs else np.zeros((C, 0))
+    return mxfp8_quantize_rows(full)
+
+
+def padded_offsets(offsets: np.ndarray) -> np.ndarray:
+    """Offsets of the 32-padded token segments used by the segment layout."""
+    n = np.diff(np.asarray(offsets, dtype=np.int64))
+    p = np.zeros(len(n) + 1, dtype=np.int64)
+    p[1:] = np.cumsum(-(-n // MX_BLOCK) * MX_BLOCK)
+    return p
+
+
+def _mx_rows(a):
+    """quantise row-wise then dequantise (the value the MX GEMM consumes)."""
+    c, s = mxfp8_quantize_rows(a)
+    R, C = c.shape
+    return mx_dequantize_blocks(c.reshape(R, C // 32, 32), s).reshape(R, C)
+
+
+def _mx_segment_cols(a, lo, hi):
+    """Token-direction quantisation of rows [lo, hi) of a (one segment),
+    returned dequantised in the original [n, C] orientation."""
+    sub = _as_f64(a[lo:hi])
+    n, C = sub.shape
+    npad = -(-n // MX_BLOCK) * MX_BLOCK
+    t = np.zeros((C, npad))
+    t[:, :n] = sub.T
+    return _mx_rows(t)[:, :n].T
+
+
+def grouped_mlp_fwd_mxfp8(x_perm, w_gu, w_dn, w_perm, offsets,
+                          keep: bool = False) -> Dict[str, np.ndarray]:
+    """R8 forward: x_perm and W_gu quantised along H, the SwiGLU*w output A
+    and W_dn along F; both GEMMs on the dequantised values (float64)."""
+    E = len(offsets) - 1
+    rows = np.asarray(x_perm).shape[0]
+    F = np.asarray(w_gu).shape[1] // 2
+    H = np.asarray(w_dn).shape[1]
+    w = np.ones(rows) if w_perm is None else np.asarray(w_perm, dtype=f64)
+    z = np.zeros((rows, H), dtype=f64)
+    a_all = np.zeros((rows, F), dtype=f64) if keep else None
+    h1_all = np.zeros((rows, 2 * F), dtype=f64) if keep else None
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        Xq = _mx_rows(x_perm[lo:hi])
+        Wguq = _mx_rows(w_gu[e])
+        h1 = Xq @ Wguq.T
+        g, u = h1[:, :F], h1[:, F:]
+        a = w[lo:hi, None] * silu(g) * u
+        Aq = _mx_rows(a)
+        Wdnq = _mx_rows(w_dn[e])
+        z[lo:hi] = Aq @ Wdnq.T
+        if keep:
+            a_all[lo:hi] = a
+            h1_all[lo:hi] = h1
+    out = {"z": z}
+    if keep:
+        out["a"] = a_all
+        out["h1"] = h1_all
+    return out
+
+
+def grouped_mlp_bwd_mxfp8(dz_perm, x_perm, w_gu, w_dn, w_perm, offsets
+                          ) -> Dict[str, np.ndarray]:
+    """R8 backward: every GEMM operand quantised along that GEMM's K.
+      dgrad2  dA = Q_H(dZ) Q_H(W_dn)            (W_dn blocks along H: col-wise)
+      wgrad2  dW_dn = Q_tok(dZ)^T Q_tok(A)
+      dgrad1  dX = Q_2F(dH1) Q_2F(W_gu)         (W_gu blocks along 2F)
+      wgrad1  dW_gu = Q_tok(dH1)^T Q_tok(X)
+    The forward intermediates (h1, A) are recomputed as in the MXFP8 forward;
+    SwiGLU backward and dw in float64."""
+    E = len(offsets) - 1
+    rows = np.asarray(x_perm).shape[0]
+    F = np.asarray(w_gu).shape[1] // 2
+    H = np.asarray(w_dn).shape[1]
+    w = np.ones(rows) if w_perm is None else np.asarray(w_perm, dtype=f64)
+    dx = np.zeros((rows, H))
+    dw_perm = np.zeros(rows)
+    dw_gu = np.zeros((E, 2 * F, H))
+    dw_dn = np.zeros((E, H, F))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        X = _as_f64(x_perm[lo:hi])
+        h1 = _mx_rows(X) @ _mx_rows(w_gu[e]).T
+        g, u = h1[:, :F], h1[:, F:]
+        s = sigmoid(g)
+        sg = g * s
+        we = w[lo:hi, None]
+        A = we * sg * u
+        dZ = _as_f64(dz_perm[lo:hi])
+        dA = _mx_rows(dZ) @ _mx_rows(_as_f64(w_dn[e]).T).T
+        dg = dA * we * u * (s * (1.0 + g * (1.0 - s)))
+        du = dA * we * sg
+        dh1 = np.concatenate([dg, du], axis=1)
+        dw_perm[lo:hi] = (dA * sg * u).sum(axis=1)
+        n = hi - lo
+        dw_dn[e] = _mx_segment_cols(dZ, 0, n).T @ _mx_segment_cols(A, 0, n)
+        dw_gu[e] = _mx_segment_cols(dh1, 0, n).T @ _mx_segment_cols(X, 0, n)
+        dx[lo:hi] = _mx_rows(dh1) @ _mx_rows(_as_f64(w_gu[e]).T).T
+    return {"dx_perm": dx, "dw_perm": dw_perm, "dw_gu": dw_gu,
+            "dw_dn": dw_dn}
+
+
+# --------------------------------------------------------------------------
+# Error metric used by the parity tests
+# --------------------------------------------------------------------------
+def rel_err(a: np.ndarray, b: np.ndarray) -> float:
+    """Normwise ||a - b||_2 / ||b||_2 (0 when both are zero)."""
+    a = np.asarray(a, dtype=f64)
+    b = np.asarray(b, dtype=f64)
+    nb = np.linalg.norm(b)
+    d = np.linalg.norm(a - b)
+    if nb == 0.0:
+        return 0.0 if d == 0.0 else float("inf")
+    return float(d / nb)

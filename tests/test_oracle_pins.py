@@ -1,0 +1,544 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against brute force, a closed form, an
+independent library routine, or an exact invariant, chosen so that a plausible
+slip in the oracle (a dropped term, a wrong sign or index, a transposed
+operand, a wrong tie-break, an off-by-one exponent) fails at least one of
+them.  CPU only.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synthetic import bf16_bits, bf16_to_f64, generate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------- routing
+def _brute_route(lrow, k):
+    """argmin over every ordered k-tuple of distinct experts of the key list
+    [(-l[e0], e0), (-l[e1], e1), ...]: an exhaustive formulation of
+    'descending logit, ties to the lower id'."""
+    E = len(lrow)
+    best, best_key = None, None
+    for tup in itertools.permutations(range(E), k):
+        key = [(-float(lrow[e]) + 0.0, e) for e in tup]
+        if best_key is None or key < best_key:
+            best, best_key = tup, key
+    return list(best)
+
+
+@pytest.mark.parametrize("E,k", [(4, 1), (4, 2), (5, 3), (8, 2), (8, 3),
+                                  (6, 6)])
+def test_route_brute_force_with_ties(E, k):
+    rng = _rng(E * 10 + k)
+    # small integer-valued logits force many exact ties; include -0.0
+    lg = rng.integers(-2, 3, size=(200, E)).astype(np.float32)
+    lg[rng.random(lg.shape) < 0.1] = -0.0
+    idx, w = O.route_topk(lg, k)
+    for t in range(lg.shape[0]):
+        assert list(idx[t]) == _brute_route(lg[t], k)
+        # the chosen set maximises the sum of logits over all k-subsets
+        best = max(sum(float(lg[t, e]) for e in s)
+                   for s in itertools.combinations(range(E), k))
+        assert sum(float(lg[t, e]) for e in idx[t]) == best
+
+
+def test_route_k_equals_E_is_softmax():
+    lg = _rng(1).standard_normal((64, 8)).astype(np.float32)
+    idx, w = O.route_topk(lg, 8, renormalize=True)
+    ref = torch.softmax(torch.from_numpy(lg.astype(np.float64)), dim=1)
+    ref = torch.gather(ref, 1, torch.from_numpy(idx.astype(np.int64)))
+    np.testing.assert_array_equal(w, ref.numpy().astype(np.float32))
+    # sorted descending
+    assert np.all(np.diff(np.take_along_axis(lg, idx, 1), axis=1) <= 0)
+
+
+def test_route_unrenormalised_is_plain_softmax_entries():
+    lg = _rng(2).standard_normal((64, 16)).astype(np.float32)
+    idx, w = O.route_topk(lg, 4, renormalize=False)
+    p = torch.softmax(torch.from_numpy(lg.astype(np.float64)), dim=1).numpy()
+    ref = np.take_along_axis(p, idx.astype(np.int64), 1).astype(np.float32)
+    np.testing.assert_array_equal(w, ref)
+    assert np.all(w.sum(1) < 1.0)
+
+
+def test_route_weights_sum_to_one_and_k1():
+    lg = _rng(3).standard_normal((500, 32)).astype(np.float32) * 3
+    for k in (2, 4, 8):
+        _, w = O.route_topk(lg, k)
+        ulp = np.spacing(np.float32(1.0))
+        assert np.all(np.abs(w.astype(np.float64).sum(1) - 1.0) <= k * ulp)
+    _, w1 = O.route_topk(lg, 1)
+    assert np.all(w1 == np.float32(1.0))
+
+
+def test_route_hand_worked_golden():
+    """tests/golden/route_hand.json: a routing example worked by hand."""
+    with open(os.path.join(GOLDEN, "route_hand.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        lg = np.array(case["logits"], dtype=np.float32)
+        idx, w = O.route_topk(lg, case["k"], bool(case["renormalize"]))
+        assert idx.tolist() == case["topk_idx"]
+        exp = np.array([[eval(s, {"math": math}) for s in row]
+                        for row in case["topk_w_expr"]], dtype=np.float64)
+        np.testing.assert_array_equal(w, exp.astype(np.float32))
+
+
+# ------------------------------------------------------------ permutation
+def _brute_permute(idx, E):
+    """Counting sort written as the definition: walk the pairs in order and
+    hand out the next free row of each expert's segment."""
+    flat = idx.reshape(-1)
+    counts = [0] * E
+    for e in flat:
+        counts[int(e)] += 1
+    starts = [0] * (E + 1)
+    for e in range(E):
+        starts[e + 1] = starts[e] + counts[e]
+    nxt = list(starts[:E])
+    row_map = []
+    for e in flat:
+        row_map.append(nxt[int(e)])
+        nxt[int(e)] += 1
+    return counts, starts, row_map
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(37, 5, 2, 0), (100, 16, 4, 1),
+                                        (64, 8, 8, 2), (1, 3, 2, 3)])
+def test_permute_matches_counting_sort(T, E, k, seed):
+    rng = _rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[:, 0] += 2.0                      # skew: expert 0 popular
+    idx, _ = O.route_topk(lg, k)
+    m = O.permute_index(idx, E)
+    counts, starts, row_map = _brute_permute(idx, E)
+    assert m["split_sizes"].tolist() == counts
+    assert m["offsets"].tolist() == starts
+    assert m["row_map"].tolist() == row_map
+    assert int(m["split_sizes"].sum()) == T * k
+    assert np.all(np.diff(m["offsets"]) >= 0)
+    # bijection, inverse, ascending tokens inside each segment
+    assert sorted(m["row_map"].tolist()) == list(range(T * k))
+    assert np.array_equal(m["src_row"][m["row_map"]], np.arange(T * k))
+    for e in range(E):
+        seg = m["src_row"][m["offsets"][e]:m["offsets"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all(idx.reshape(-1)[seg] == e)
+
+
+def test_permute_rows_bitwise_and_weights():
+    d = generate(50, 64, 32, 6, 3, want=("x", "logits"))
+    idx, w = O.route_topk(d["logits"], 3)
+    m = O.permute_index(idx, 6)
+    xp = O.permute_rows(d["x"], m["src_row"], 3)
+    wp = O.permute_weights(w, m["src_row"])
+    for p in range(50 * 3):
+        assert np.array_equal(xp[m["row_map"][p]], d["x"][p // 3])
+        assert wp[m["row_map"][p]] == w.reshape(-1)[p]
+
+
+@pytest.mark.parametrize("k", [1, 2, 8])
+def test_permute_unpermute_identity(k):
+    """Unweighted combine of permuted rows == k * x bitwise (k a power of
+    two, so the sum and the bf16 rounding are exact); with weights 1/k it is
+    x itself."""
+    E = 8
+    d = generate(40, 48, 32, E, k, want=("x", "logits"))
+    idx, _ = O.route_topk(d["logits"], k)
+    m = O.permute_index(idx, E)
+    xp = O.permute_rows(bf16_to_f64(d["x"]), m["src_row"], k)
+    y = O.unpermute(xp, m["row_map"], k)
+    x = bf16_to_f64(d["x"])
+    assert np.array_equal(y, k * x)
+    assert np.array_equal(bf16_bits(y.astype(np.float32)),
+                          bf16_bits((k * x).astype(np.float32)))
+    y2 = O.unpermute(xp, m["row_map"], k,
+                     topk_w=np.full((40, k), 1.0 / k, np.float32))
+    assert np.array_equal(y2, x)
+
+
+def test_permute_rejects_bad_ids():
+    with pytest.raises(ValueError):
+        O.permute_index(np.array([[0, 5]]), 4)
+
+
+# --------------------------------------------------------- grouped MLP fwd
+def _ffn(x, wgu, wdn, w):
+    F = wgu.shape[0] // 2
+    h = wgu @ x
+    return wdn @ (w * (h[:F] / (1 + np.exp(-h[:F]))) * h[F:])
+
+
+def _small_layer(T=24, H=32, F=16, E=5, k=2, seed=0, zipf=0.0):
+    d = generate(T, H, F, E, k, zipf=zipf, seed=seed,
+                 want=("x", "logits", "w_gu", "w_dn", "dy"))
+    return d
+
+
+def test_grouped_equals_per_token_loop():
+    """grouped (sorted-token) == per-token eager loop."""
+    T, H, F, E, k = 30, 32, 24, 6, 3
+    d = _small_layer(T, H, F, E, k, zipf=1.2)
+    out = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], k)
+    x = bf16_to_f64(d["x"])
+    wgu = bf16_to_f64(d["w_gu"])
+    wdn = bf16_to_f64(d["w_dn"])
+    y = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = out["topk_idx"][t, j]
+            y[t] += _ffn(x[t], wgu[e], wdn[e], float(out["topk_w"][t, j]))
+    np.testing.assert_allclose(out["y"], y, rtol=1e-12, atol=1e-13)
+
+
+def test_grouped_equals_dense_masked():
+    """grouped == the batched form that runs every expert on every token and
+    gates the result by a dense [T, E] weight matrix (0 off-route)."""
+    T, H, F, E, k = 20, 16, 8, 4, 2
+    d = _small_layer(T, H, F, E, k, seed=4)
+    out = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], k)
+    x = torch.from_numpy(bf16_to_f64(d["x"]))
+    wgu = torch.from_numpy(bf16_to_f64(d["w_gu"]))
+    wdn = torch.from_numpy(bf16_to_f64(d["w_dn"]))
+    gate = torch.zeros(T, E, dtype=torch.float64)
+    gate.scatter_(1, torch.from_numpy(out["topk_idx"].astype(np.int64)),
+                  torch.from_numpy(out["topk_w"].astype(np.float64)))
+    h = torch.einsum("th,eoh->eto", x, wgu)                 # [E, T, 2F]
+    a = torch.nn.functional.silu(h[..., :F]) * h[..., F:]
+    z = torch.einsum("etf,ehf->eth", a, wdn)                # [E, T, H]
+    y = (gate.T[..., None] * z).sum(0)
+    np.testing.assert_allclose(out["y"], y.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_single_expert_is_dense_swiglu_mlp():
+    """E = 1, k = 1: the layer is the textbook SwiGLU MLP (weight 1)."""
+    d = _small_layer(T=10, H=16, F=12, E=1, k=1)
+    out = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], 1)
+    x = torch.from_numpy(bf16_to_f64(d["x"]))
+    wg = torch.from_numpy(bf16_to_f64(d["w_gu"][0, :12]))
+    wu = torch.from_numpy(bf16_to_f64(d["w_gu"][0, 12:]))
+    wd = torch.from_numpy(bf16_to_f64(d["w_dn"][0]))
+    F_ = torch.nn.functional
+    ref = F_.linear(F_.silu(F_.linear(x, wg)) * F_.linear(x, wu), wd)
+    assert np.all(out["topk_w"] == 1.0)
+    np.testing.assert_allclose(out["y"], ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_linear_in_routing_weight():
+    """Scaling w_perm by 2^n scales z by exactly 2^n."""
+    d = _small_layer(T=16, H=16, F=8, E=3, k=2)
+    idx, w = O.route_topk(d["logits"], 2)
+    m = O.permute_index(idx, 3)
+    xp = O.permute_rows(d["x"], m["src_row"], 2)
+    wp = O.permute_weights(w, m["src_row"]).astype(np.float64)
+    z1 = O.grouped_mlp_fwd(xp, d["w_gu"], d["w_dn"], wp, m["offsets"])["z"]
+    z2 = O.grouped_mlp_fwd(xp, d["w_gu"], d["w_dn"], wp * 8.0,
+                           m["offsets"])["z"]
+    assert np.array_equal(z2, 8.0 * z1)
+
+
+def test_scaled_swiglu_equals_weighted_combine():
+    """Weight applied before the down projection == weight at the combine."""
+    d = _small_layer(T=16, H=16, F=8, E=4, k=2)
+    idx, w = O.route_topk(d["logits"], 2)
+    m = O.permute_index(idx, 4)
+    xp = O.permute_rows(d["x"], m["src_row"], 2)
+    wp = O.permute_weights(w, m["src_row"])
+    za = O.grouped_mlp_fwd(xp, d["w_gu"], d["w_dn"], wp, m["offsets"])["z"]
+    zb = O.grouped_mlp_fwd(xp, d["w_gu"], d["w_dn"], None, m["offsets"])["z"]
+    ya = O.unpermute(za, m["row_map"], 2)
+    yb = O.unpermute(zb, m["row_map"], 2, topk_w=w)
+    np.testing.assert_allclose(ya, yb, rtol=1e-12, atol=1e-14)
+
+
+def test_silu_closed_forms():
+    z = np.linspace(-30, 30, 1001)
+    s = O.silu(z)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(s - O.silu(-z), z, rtol=1e-13, atol=1e-13)
+    assert abs(O.silu(np.array([-800.0]))[0]) == 0.0
+    assert O.silu(np.array([800.0]))[0] == 800.0
+    np.testing.assert_allclose(O.sigmoid(z) + O.sigmoid(-z), 1.0, rtol=1e-15)
+
+
+# -------------------------------------------------------------- backward
+def _fwd_fixed_routing(x, w_gu, w_dn, topk_w, idx, k):
+    E = w_gu.shape[0]
+    m = O.permute_index(idx, E)
+    xp = O.permute_rows(x, m["src_row"], k)
+    wp = np.asarray(topk_w, np.float64).reshape(-1)[m["src_row"]]
+    z = O.grouped_mlp_fwd(xp, w_gu, w_dn, wp, m["offsets"])["z"]
+    return O.unpermute(z, m["row_map"], k)
+
+
+def test_backward_finite_differences():
+    T, H, F, E, k = 3, 8, 16, 3, 2
+    d = _small_layer(T, H, F, E, k, seed=7)
+    x = bf16_to_f64(d["x"])
+    wgu = bf16_to_f64(d["w_gu"]) * 10  # larger weights: non-trivial SwiGLU
+    wdn = bf16_to_f64(d["w_dn"]) * 10
+    dy = bf16_to_f64(d["dy"])
+    idx, w = O.route_topk(d["logits"], k)
+    w = w.astype(np.float64)
+    g = O.layer_bwd(x, d["logits"], wgu, wdn, dy, k)
+    eps = 1e-6
+
+    def L(x_, wgu_, wdn_, w_):
+        return float((dy * _fwd_fixed_routing(x_, wgu_, wdn_, w_, idx, k)
+                      ).sum())
+
+    def fd(arr, setter):
+        out = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            p = arr.copy(); p[i] += eps
+            m_ = arr.copy(); m_[i] -= eps
+            out[i] = (setter(p) - setter(m_)) / (2 * eps)
+        return out
+
+    gx = fd(x, lambda v: L(v, wgu, wdn, w))
+    np.testing.assert_allclose(g["dx"], gx, rtol=1e-6, atol=1e-8)
+    gdn = fd(wdn, lambda v: L(x, wgu, v, w))
+    np.testing.assert_allclose(g["dw_dn"], gdn, rtol=1e-6, atol=1e-8)
+    ggu = fd(wgu, lambda v: L(x, v, wdn, w))
+    np.testing.assert_allclose(g["dw_gu"], ggu, rtol=1e-6, atol=1e-8)
+    gw = fd(w, lambda v: L(x, wgu, wdn, v))
+    np.testing.assert_allclose(g["dprobs"], gw, rtol=1e-6, atol=1e-8)
+
+
+def test_backward_adjoint_and_dprobs_closed_form():
+    T, H, F, E, k = 12, 16, 8, 4, 2
+    d = _small_layer(T, H, F, E, k, seed=9)
+    x = bf16_to_f64(d["x"])
+    wgu = bf16_to_f64(d["w_gu"]) * 5
+    wdn = bf16_to_f64(d["w_dn"]) * 5
+    dy = bf16_to_f64(d["dy"])
+    g = O.layer_bwd(x, d["logits"], wgu, wdn, dy, k)
+    # adjoint: <dY, J v> == <J^T dY, v> along a random direction in x
+    idx, w = O.route_topk(d["logits"], k)
+    v = _rng(5).standard_normal(x.shape)
+    h = 1e-6
+    jv = (_fwd_fixed_routing(x + h * v, wgu, wdn, w, idx, k)
+          - _fwd_fixed_routing(x - h * v, wgu, wdn, w, idx, k)) / (2 * h)
+    assert abs((dy * jv).sum() - (g["dx"] * v).sum()) <= 1e-6 * abs(
+        (dy * jv).sum())
+    # dprobs[t, j] = <dY_t, FFN_e(x_t; weight 1)>
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            ref = float(dy[t] @ _ffn(x[t], wgu[e], wdn[e], 1.0))
+            assert abs(g["dprobs"][t, j] - ref) <= 1e-10 * max(1.0, abs(ref))
+
+
+def test_backward_zero_token_experts_get_zero_grads():
+    T, H, F, E, k = 16, 8, 8, 6, 1
+    d = _small_layer(T, H, F, E, k)
+    lg = d["logits"].copy()
+    lg[:, 2:] -= 100.0          # experts 2..5 never chosen
+    g = O.layer_bwd(d["x"], lg, d["w_gu"], d["w_dn"], d["dy"], k)
+    assert np.all(g["split_sizes"][2:] == 0)
+    assert np.all(g["dw_gu"][2:] == 0) and np.all(g["dw_dn"][2:] == 0)
+    assert np.any(g["dw_gu"][:2] != 0)
+
+
+# ------------------------------------------------------------------ MXFP8
+def _e4m3_grid():
+    """All finite non-negative E4M3 values from the bit-field definition
+    (sign | 4-bit exponent, bias 7 | 3-bit mantissa; exponent 0 subnormal;
+    0x7F NaN), computed with Python fractions-free integer arithmetic."""
+    vals = []
+    for c in range(0x7F):
+        ef, m = c >> 3, c & 7
+        if ef == 0:
+            vals.append(m * 2.0 ** -9)
+        else:
+            vals.append((1 + m / 8.0) * 2.0 ** (ef - 7))
+    return np.array(vals)
+
+
+def test_e4m3_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(ours[ok]), np.signbit(ref[ok]))
+    np.testing.assert_array_equal(ours[:0x7F], _e4m3_grid())
+
+
+def test_e4m3_encode_hand_points():
+    """tests/golden/e4m3_points.json: codes worked out by hand from the
+    format definition (bias 7, 3 mantissa bits, max 448)."""
+    with open(os.path.join(GOLDEN, "e4m3_points.json")) as f:
+        pts = json.load(f)["points"]
+    v = np.array([eval(p[0]) for p in pts], dtype=np.float64)
+    want = np.array([int(p[1], 16) for p in pts], dtype=np.uint8)
+    np.testing.assert_array_equal(O.e4m3_encode(v), want)
+
+
+def _all_finite_bf16():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp = (bits >> 7) & 0xFF
+    return bits[exp != 0xFF]
+
+
+def test_e4m3_encode_exhaustive_bf16_times_all_scales():
+    """Every finite bf16 value times every 2^-s, s in [-127, 127], encoded
+    and compared with a nearest-of-grid search (ties to the even code,
+    saturation at 448, sign kept)."""
+    grid = _e4m3_grid()                       # 127 ascending values
+    mids = (grid[:-1] + grid[1:]) / 2
+    v0 = bf16_to_f64(_all_finite_bf16())
+    for s in range(-127, 128):
+        v = np.ldexp(v0, -s)
+        a = np.abs(v)
+        j = np.searchsorted(mids, a, side="left")   # a <= mids[j]
+        j = np.minimum(j, len(grid) - 1)
+        # exact midpoint: searchsorted picked the lower code j where
+        # a == mids[j-?]; resolve ties toward the even code
+        at_mid = (j < len(mids)) & (a == mids[np.minimum(j, len(mids) - 1)])
+        j = np.where(at_mid & (j % 2 == 1), j + 1, j)
+        j = np.where(a >= 448.0, 0x7E, j)
+        want = (j.astype(np.uint8) | (np.signbit(v).astype(np.uint8) << 7))
+        got = O.e4m3_encode(v)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (s, v[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    v0 = bf16_to_f64(_all_finite_bf16())
+    for s in (-3, 0, 5, -10, 2):
+        v = np.ldexp(v0, -s)
+        v = v[np.abs(v) <= 448.0]
+        ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(
+            torch.uint8).numpy()
+        np.testing.assert_array_equal(O.e4m3_encode(v), ref)
+
+
+def test_e8m0_exponent_exhaustive_positive_bf16():
+    a = bf16_to_f64(_all_finite_bf16())
+    a = np.unique(np.abs(a))
+    s = O.e8m0_exponent(a)
+    pos = a > 0
+    unclamped = pos & (s > -127)
+    r = a[unclamped] / np.ldexp(1.0, s[unclamped])
+    assert np.all((r >= 256.0) & (r < 512.0))
+    assert s[~pos][0] == -127
+    # clamped ones really are below the un-clamped threshold 2^-119
+    assert np.all(a[pos & (s == -127)] < 2.0 ** -118)
+    assert s.max() <= 127
+
+
+def test_mx_round_trip_exact_on_representable_values():
+    rng = _rng(11)
+    nb = 4000
+    mags = rng.integers(0, 0x7F, size=(nb, 32))           # finite codes
+    # force each block's max magnitude into [256, 448] (binade 2^8)
+    top = rng.integers(0x78, 0x7F, size=nb)                 # 256 .. 448
+    mags[np.arange(nb), rng.integers(0, 32, size=nb)] = top
+    mags = np.minimum(mags, np.maximum(top, 0)[:, None])
+    codes = (mags | (rng.integers(0, 2, size=mags.shape) << 7)).astype(
+        np.uint8)
+    s = rng.integers(-100, 100, size=nb)
+    V = np.ldexp(O.e4m3_decode(codes), s[:, None])
+    c2, sc2 = O.mx_quantize_blocks(V)
+    # zero codes with the sign bit come back as signed zeros: same bits
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(sc2.astype(np.int64) - 127, s)
+    np.testing.assert_array_equal(O.mx_dequantize_blocks(c2, sc2), V)
+
+
+def test_mx_quantize_rows_cols_segments_layout():
+    rng = _rng(12)
+    a = rng.standard_normal((64, 96))
+    c, s = O.mxfp8_quantize_rows(a)
+    assert c.shape == (64, 96) and s.shape == (64, 3)
+    cb, sb = O.mx_quantize_blocks(a[5, 32:64][None, None, :])
+    np.testing.assert_array_equal(c[5, 32:64], cb[0, 0])
+    assert s[5, 1] == sb[0, 0]
+    ct, st = O.mxfp8_quantize_cols(a)
+    assert ct.shape == (96, 64) and st.shape == (96, 2)
+    cb, sb = O.mx_quantize_blocks(a[32:64, 7][None, None, :])
+    np.testing.assert_array_equal(ct[7, 32:64], cb[0, 0])
+    off = np.array([0, 10, 10, 64])
+    cs, ss = O.mxfp8_quantize_segments(a, off)
+    po = O.padded_offsets(off)
+    assert po.tolist() == [0, 32, 32, 96]
+    assert cs.shape == (96, 96) and ss.shape == (96, 3)
+    blk = np.zeros(32)
+    blk[:10] = a[0:10, 3]
+    cb, sb = O.mx_quantize_blocks(blk[None, None, :])
+    np.testing.assert_array_equal(cs[3, 0:32], cb[0, 0])
+    assert ss[3, 0] == sb[0, 0]
+    assert np.all(cs[3, 10:32] == 0)
+
+
+def test_mx_gemm_equals_exact_gemm_on_representable_operands():
+    """MXFP8 layer GEMM on operands that are exactly representable equals the
+    plain float64 GEMM on those values."""
+    rng = _rng(13)
+    M, K, N = 16, 64, 8
+
+    def rep(shape):
+        nb = shape[0] * shape[1] // 32
+        mags = rng.integers(0, 0x78, size=(nb, 32))
+        mags[:, 0] = rng.integers(0x78, 0x7F, size=nb)
+        codes = (mags | (rng.integers(0, 2, size=mags.shape) << 7))
+        s = rng.integers(-10, 0, size=nb)
+        return np.ldexp(O.e4m3_decode(codes), s[:, None]).reshape(shape)
+
+    X = rep((M, K))
+    W = rep((N, K))
+    Xq = O._mx_rows(X)
+    Wq = O._mx_rows(W)
+    assert np.array_equal(Xq, X) and np.array_equal(Wq, W)
+    np.testing.assert_allclose(Xq @ Wq.T, X @ W.T, rtol=0, atol=0)
+
+
+def test_mxfp8_layer_close_to_unquantised():
+    """Sanity: the MXFP8 layer tracks the unquantised one (normwise error of
+    a few percent, the format's resolution), and equals it exactly when every
+    operand is representable is covered above."""
+    T, H, F, E, k = 64, 128, 64, 4, 2
+    d = _small_layer(T, H, F, E, k, seed=3)
+    fwd = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], k)
+    zq = O.grouped_mlp_fwd_mxfp8(fwd["x_perm"], d["w_gu"], d["w_dn"],
+                                 fwd["w_perm"], fwd["offsets"])["z"]
+    err = O.rel_err(zq, fwd["z"])
+    assert 0.005 < err < 0.15
+
+
+def test_mxfp8_backward_tracks_bf16_backward():
+    T, H, F, E, k = 48, 64, 64, 3, 2
+    d = _small_layer(T, H, F, E, k, seed=5)
+    fwd = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], k)
+    dz = O.gather_rows(bf16_to_f64(d["dy"]), fwd["src_row"], k)
+    a = O.grouped_mlp_bwd(dz, fwd["x_perm"], d["w_gu"], d["w_dn"],
+                          fwd["w_perm"], fwd["offsets"])
+    b = O.grouped_mlp_bwd_mxfp8(dz, fwd["x_perm"], d["w_gu"], d["w_dn"],
+                                fwd["w_perm"], fwd["offsets"])
+    for key in ("dx_perm", "dw_gu", "dw_dn", "dw_perm"):
+        assert O.rel_err(b[key], a[key]) < 0.2, key
+
+
+def test_accounting_flops_and_rows():
+    from synthetic import CONFIGS
+    c = CONFIGS["mixtral"]
+    assert c.rows == 16384
+    assert abs(c.fwd_flop() - 5.772e12) / 5.772e12 < 1e-3
+    q = CONFIGS["qwen3_long"]
+    assert abs(q.bwd_flop() - 4.948e12) / 4.948e12 < 1e-3
