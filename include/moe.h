@@ -1,0 +1,301 @@
+/*
+ * moe.h -- C ABI of libmoe: the MoE expert-MLP hot path on one MI355X
+ * (gfx950).
+ *
+ * The path: router top-k -> permute tokens into expert-contiguous order with
+ * per-expert split_sizes -> grouped GEMM gate/up -> ScaledSwiGLU times the
+ * routing weight -> grouped GEMM down -> unpermute / combine, in bf16 or
+ * MXFP8 (E4M3 elements, one E8M0 scale per 32 consecutive values along K),
+ * forward and backward.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [PG1] "NVIDIA presents an efficient path for training biological MoE
+ *        models" (sitech.ge).
+ *  [PG2] "Efficient MoE training for biological foundation models (NVIDIA)"
+ *        (news.bpdata.com).
+ *  [PG3] "Nous Research scales expert parallelism with DeepEP"
+ *        (seventnews.com).
+ *  [PG4] "NVIDIA NeMo AutoModel: 3.7x faster MoE fine-tuning with expert
+ *        parallelism and DeepEP" (seventnews.com).
+ *
+ * Conventions for every call
+ *  - Memory: every tensor argument is DEVICE memory allocated and owned by
+ *    the caller (the library never allocates or frees per call); tensors are
+ *    dense row-major with the shapes given, 16-byte aligned.  bf16 tensors
+ *    are passed as void* (IEEE bfloat16 bit patterns); E4M3 codes and E8M0
+ *    scales as uint8_t*.  Scalars are host values.
+ *  - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls
+ *    enqueue work and return; none synchronises the host, except
+ *    moe_ctx_check_device_status.  The library creates no streams and never
+ *    copies split_sizes/offsets to the host.
+ *  - Errors: argument validation happens on the host before anything is
+ *    enqueued; a failing call enqueues nothing and returns a non-zero
+ *    moe_status_t.  moe_last_error() gives a thread-local message.
+ *    Data errors that only the device can see (an expert id outside [0, E))
+ *    are recorded in the context's device status word (first error wins),
+ *    the offending pair is skipped (its row_map entry is -1), and
+ *    moe_ctx_check_device_status reports them.
+ *  - Threading: a context may be used by one host thread at a time.
+ *  - Determinism: no floating-point atomics; results are bitwise
+ *    reproducible for the same inputs and sizes.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* null required pointer, bad sizes, k > E */
+  MOE_ERR_UNSUPPORTED = 2,   /* device not gfx950, size outside limits */
+  MOE_ERR_WORKSPACE = 3,     /* workspace missing or too small */
+  MOE_ERR_HIP = 4,           /* a HIP runtime call or launch failed */
+  MOE_ERR_DEVICE_CHECK = 5   /* a device-side data check fired */
+} moe_status_t;
+
+typedef enum moe_precision {
+  MOE_PREC_BF16 = 0,
+  MOE_PREC_MXFP8_E4M3 = 1
+} moe_precision_t;
+
+typedef enum moe_mx_axis {
+  MOE_MX_ROWWISE = 0,   /* blocks of 32 run along each row (cols) */
+  MOE_MX_COLWISE = 1    /* blocks of 32 run down each column; output transposed */
+} moe_mx_axis_t;
+
+/* Device status codes written by kernels into the context status word. */
+#define MOE_DEVERR_NONE 0
+#define MOE_DEVERR_EXPERT_ID 1     /* topk_idx entry outside [0, E) */
+
+typedef struct moe_ctx* moe_ctx_t;
+
+/* Limits (UNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+
+/* ------------------------------------------------------------------------
+ * Context.  moe_ctx_create checks that `device` is a gfx950 GPU, records its
+ * compute-unit count and allocates the 4-byte device status word (the only
+ * allocation the library makes, freed by moe_ctx_destroy).
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_ctx_create(int device, moe_ctx_t* ctx);
+moe_status_t moe_ctx_destroy(moe_ctx_t ctx);
+
+/* Synchronises `stream`, returns the first device-side error code recorded
+ * since the last check in *host_code (MOE_DEVERR_*), and clears it.  Returns
+ * MOE_ERR_DEVICE_CHECK when a code was set, MOE_OK otherwise. */
+moe_status_t moe_ctx_check_device_status(moe_ctx_t ctx, void* stream,
+                                         int32_t* host_code);
+
+const char* moe_status_string(moe_status_t status);
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * moe_route_topk -- router top-k.
+ * [PG3, practical-implications paragraph: Top-k routing; PG2, section "Why
+ *  dense and MoE models differ": only a small subset of experts is active
+ *  per token.]  The pages name Top-k but not the weight formula; the
+ * library takes the softmax reading.
+ *
+ *  logits   float32 [T, E]  router logits.
+ *  topk_idx int32   [T, k]  out: the k experts with the largest logits,
+ *                           slot 0 the largest; equal logits go to the lower
+ *                           expert id (+0 and -0 are equal).
+ *  topk_w   float32 [T, k]  out: exp(l - max) normalised over the chosen k
+ *                           (renormalize != 0) or over all E (== 0),
+ *                           evaluated in float64, rounded to float32.
+ *  1 <= k <= min(E, 32), E <= 1024, T >= 0 (T = 0 is a no-op).
+ *  Logits must be finite (NaN/Inf: unspecified selection).
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_route_topk(moe_ctx_t ctx, const float* logits, int64_t T,
+                            int32_t E, int32_t k, int32_t renormalize,
+                            int32_t* topk_idx, float* topk_w, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute -- expert-order permutation and row gather.
+ * [PG1, section "Grouped experts instead of a Python loop", and PG2, section
+ *  "1) Fragmented expert kernels": the grouped GEMM gathers the tokens of
+ *  every expert and takes the per-expert token counts (split_sizes); PG4,
+ *  section "Using Transformers v5 features": grouped_mm runs on sorted
+ *  tokens.]
+ *
+ * Pair p = t*k + j (token t, slot j) goes to expert e = topk_idx[t, j].
+ *  split_sizes int32 [E]    out: pairs per expert.
+ *  offsets     int32 [E+1]  out: exclusive prefix sum, offsets[E] = T*k.
+ *  row_map     int32 [T*k]  out: destination row of pair p; rows are ordered
+ *                           by expert, then by p (stable; unique).
+ *  src_row     int32 [T*k]  out: inverse of row_map (src_row[row_map[p]] = p).
+ *  x           bf16  [T, H] tokens.
+ *  x_perm      [T*k, H]     out: x_perm[row_map[t*k+j]] = x[t]; bf16 when
+ *                           out_prec = MOE_PREC_BF16, E4M3 codes (uint8) when
+ *                           out_prec = MOE_PREC_MXFP8_E4M3.
+ *  x_perm_scale uint8 [T*k, H/32] out (MXFP8 only, else NULL): E8M0 scales of
+ *                           the row-wise blocks of 32 along H.
+ *  topk_w      float32 [T, k] (nullable) routing weights;
+ *  w_perm      float32 [T*k]  (nullable) out: w_perm[row_map[p]] = topk_w[p].
+ *  ws          workspace of at least moe_permute_workspace_size() bytes.
+ *  H % 8 == 0 (bf16) or H % 32 == 0 (MXFP8).
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k,
+                                        size_t* bytes);
+moe_status_t moe_permute(moe_ctx_t ctx, const void* x,
+                         const int32_t* topk_idx, const float* topk_w,
+                         int64_t T, int32_t H, int32_t E, int32_t k,
+                         moe_precision_t out_prec, void* x_perm,
+                         uint8_t* x_perm_scale, float* w_perm,
+                         int32_t* row_map, int32_t* src_row,
+                         int32_t* split_sizes, int32_t* offsets, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* moe_gather_rows -- the row copy of moe_permute alone, for a tensor that
+ * shares an existing permutation (the upstream gradient dY -> dZ in the
+ * backward pass): dst[row_map[t*k+j]] = src[t] for all t, j; pairs with
+ * row_map < 0 are skipped.  src bf16 [T, H], dst bf16 [T*k, H]. */
+moe_status_t moe_gather_rows(moe_ctx_t ctx, const void* src,
+                             const int32_t* row_map, int64_t T, int32_t H,
+                             int32_t k, void* dst, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_unpermute -- combine back to token order.
+ * [PG4, section "Sources of speedup": the combine that follows the expert
+ *  compute.]
+ *  y[t] = sum_{j = 0..k-1, ascending} c_j * z_perm[row_map[t*k+j]],
+ *  c_j = 1 when topk_w is NULL (the weights were applied inside the grouped
+ *  MLP), else topk_w[t, j].  Accumulated in float32, rounded to bf16.
+ *  z_perm bf16 [T*k, H], y bf16 [T, H], H % 8 == 0.  Pairs with
+ *  row_map < 0 contribute nothing.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_unpermute(moe_ctx_t ctx, const void* z_perm,
+                           const int32_t* row_map, const float* topk_w,
+                           int64_t T, int32_t H, int32_t k, void* y,
+                           void* stream);
+
+/* moe_unpermute_probs_grad -- routing-weight gradient back to token order:
+ * dprobs[t, j] = dw_perm[row_map[t*k+j]] (0 where row_map < 0).
+ * dw_perm float32 [T*k], dprobs float32 [T, k]. */
+moe_status_t moe_unpermute_probs_grad(moe_ctx_t ctx, const float* dw_perm,
+                                      const int32_t* row_map, int64_t T,
+                                      int32_t k, float* dprobs, void* stream);
+
+/* ------------------------------------------------------------------------
+ * mxfp8_quantize -- MXFP8 quantisation of a bf16 tensor.
+ * [PG1, section "Reducing memory and quantisation cost", and PG2, section
+ *  "2) Model size and activation memory": 8-bit elements with one scale per
+ *  block of 32 consecutive values; PG2, section "3) Quantisation overhead in
+ *  low-precision training": 16-bit master weights are quantised.]
+ * Per block v[0..31]: s = floor(log2 max|v|) - 8 clamped to [-127, 127]
+ * (all-zero block: -127); scale byte = s + 127 (E8M0); code_i = OCP E4M3 of
+ * v_i * 2^-s, round to nearest even, saturating at +-448, sign kept.
+ *
+ *  src bf16 [batch, rows, cols].
+ *  ROWWISE: blocks along cols (cols % 32 == 0); codes [batch, rows, cols],
+ *           scales [batch, rows, cols/32].
+ *  COLWISE, seg_offsets == NULL: blocks along rows (rows % 32 == 0); output
+ *           transposed: codes [batch, cols, rows], scales
+ *           [batch, cols, rows/32].
+ *  COLWISE, seg_offsets != NULL (batch must be 1): rows are split into
+ *           n_seg segments [seg_offsets[s], seg_offsets[s+1]) (device int32,
+ *           seg_offsets[n_seg] == rows); blocks restart at each segment
+ *           start and the last block of a segment is zero-padded.  Segment s
+ *           occupies output columns [P_s, P_s + ceil(n_s/32)*32) with
+ *           P_s = sum_{s'<s} ceil(n_s'/32)*32.  codes [cols, ld],
+ *           scales [cols, ld/32], ld = rows + 32*n_seg rounded up to 32
+ *           (columns past the last segment are left untouched).
+ * ---------------------------------------------------------------------- */
+moe_status_t mxfp8_quantize(moe_ctx_t ctx, const void* src, int64_t batch,
+                            int64_t rows, int64_t cols, moe_mx_axis_t axis,
+                            const int32_t* seg_offsets, int32_t n_seg,
+                            uint8_t* codes, uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_mlp_fwd -- grouped GEMM gate/up -> ScaledSwiGLU x routing
+ * weight -> grouped GEMM down, over all experts in one call.
+ * [PG1, sections "Grouped experts instead of a Python loop" (one grouped
+ *  GEMM for all experts, split_sizes, routing weights scaled inside the
+ *  grouped-MLP kernel) and "Reducing memory and quantisation cost"
+ *  (GroupedLinear -> ScaledSwiGLU -> GroupedLinear fused into one op);
+ *  PG2, section "3) Quantisation overhead in low-precision training".]
+ * For each expert e with rows [offsets[e], offsets[e+1]) of x_perm:
+ *   h1 = X_e W_gu[e]^T  (float32 accumulate), g = h1[:, :F], u = h1[:, F:]
+ *   a  = w_perm * silu(g) * u        (silu(z) = z / (1 + exp(-z)))
+ *   z  = a W_dn[e]^T                 -> z_perm bf16
+ * Experts with no rows cost nothing.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_mlp_fwd_args {
+  int32_t E, H, F;               /* experts, hidden, expert FFN size */
+  int64_t rows;                  /* T*k = offsets[E] */
+  moe_precision_t precision;
+  /* x_perm: bf16 [rows, H]; in MXFP8 mode either E4M3 codes [rows, H] with
+   * x_perm_scale [rows, H/32], or bf16 with x_perm_scale NULL (then
+   * quantised row-wise inside the call). */
+  const void* x_perm;
+  const uint8_t* x_perm_scale;
+  const void* w_gu;              /* bf16 [E, 2F, H]: gate rows 0..F-1, up F..2F-1 */
+  const void* w_dn;              /* bf16 [E, H, F] */
+  /* MXFP8 only, optional: weights already quantised row-wise along K
+   * (w_gu_q [E, 2F, H] + w_gu_s [E, 2F, H/32]; w_dn_q [E, H, F] +
+   * w_dn_s [E, H, F/32]).  NULL: quantised from w_gu / w_dn inside the
+   * call (in the workspace). */
+  const uint8_t* w_gu_q; const uint8_t* w_gu_s;
+  const uint8_t* w_dn_q; const uint8_t* w_dn_s;
+  const float* w_perm;           /* float32 [rows] or NULL (weight 1) */
+  const int32_t* offsets;        /* int32 [E+1] on the device */
+  void* z_perm;                  /* out: bf16 [rows, H] */
+  void* h1_save;                 /* out, nullable: bf16 [rows, 2F] (g, u) */
+  void* a_save;                  /* out, nullable: bf16 [rows, F] */
+  void* ws;                      /* workspace */
+  size_t ws_bytes;
+} moe_mlp_fwd_args;
+
+moe_status_t moe_grouped_mlp_fwd_workspace_size(const moe_mlp_fwd_args* args,
+                                                size_t* bytes);
+moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* args,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_mlp_bwd -- the backward counterpart of moe_grouped_mlp_fwd.
+ * [PG1, section "Reducing memory and quantisation cost": the fused forward
+ *  op has a counterpart in the backward pass.]
+ * Per expert, with s = sigmoid(g), silu(g) = g*s, a = w*silu(g)*u:
+ *   dA   = dZ W_dn[e]
+ *   dg   = dA * w * u * s * (1 + g*(1 - s)),   du = dA * w * silu(g)
+ *   dw_perm = sum_f dA * silu(g) * u
+ *   dW_dn[e] = dZ^T a,  dW_gu[e] = [dg du]^T X,  dX = [dg du] W_gu[e]
+ * Experts with no rows get dW = 0.  MXFP8 mode quantises every GEMM operand
+ * along that GEMM's K (token-direction blocks restart at each expert's first
+ * row and are zero-padded).
+ * ---------------------------------------------------------------------- */
+typedef struct moe_mlp_bwd_args {
+  int32_t E, H, F;
+  int64_t rows;
+  moe_precision_t precision;
+  const void* x_perm;            /* bf16 [rows, H] */
+  const void* w_gu;              /* bf16 [E, 2F, H] */
+  const void* w_dn;              /* bf16 [E, H, F] */
+  const float* w_perm;           /* float32 [rows] or NULL (weight 1) */
+  const int32_t* offsets;        /* int32 [E+1] */
+  const void* h1_save;           /* bf16 [rows, 2F] saved by the forward */
+  const void* a_save;            /* bf16 [rows, F] saved by the forward */
+  const void* dz_perm;           /* bf16 [rows, H] gradient of z_perm */
+  void* dx_perm;                 /* out: bf16 [rows, H] */
+  void* dw_gu;                   /* out: bf16 [E, 2F, H] */
+  void* dw_dn;                   /* out: bf16 [E, H, F] */
+  float* dw_perm;                /* out: float32 [rows] (NULL if w_perm NULL) */
+  void* ws;
+  size_t ws_bytes;
+} moe_mlp_bwd_args;
+
+moe_status_t moe_grouped_mlp_bwd_workspace_size(const moe_mlp_bwd_args* args,
+                                                size_t* bytes);
+moe_status_t moe_grouped_mlp_bwd(moe_ctx_t ctx, const moe_mlp_bwd_args* args,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,436 @@
+// libmoe C ABI: argument validation, workspace sizing and kernel dispatch.
+// Every call validates on the host first and enqueues nothing on failure.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+struct moe_ctx {
+  int device;
+  int cu_count;
+  int32_t* status;  // device word: first data error
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status_t ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+#define MOE_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+moe_status_t check_ctx(moe_ctx_t ctx) {
+  MOE_REQUIRE(ctx != nullptr, MOE_ERR_INVALID_ARG, "null context");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device)
+    return fail(MOE_ERR_INVALID_ARG,
+                "context belongs to device %d but device %d is current",
+                ctx->device, cur);
+  return MOE_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    case MOE_ERR_DEVICE_CHECK: return "device-side data check failed";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status_t moe_ctx_create(int device, moe_ctx_t* out) {
+  MOE_REQUIRE(out != nullptr, MOE_ERR_INVALID_ARG, "null output pointer");
+  *out = nullptr;
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return hip_status(e, "hipGetDeviceCount");
+  MOE_REQUIRE(device >= 0 && device < n, MOE_ERR_INVALID_ARG,
+              "device %d out of range (%d devices)", device, n);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d is %s, libmoe needs gfx950",
+                device, prop.gcnArchName);
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  e = hipSetDevice(device);
+  if (e != hipSuccess) return hip_status(e, "hipSetDevice");
+  int32_t* status = nullptr;
+  e = hipMalloc(&status, sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemset(status, 0, sizeof(int32_t));
+  if (prev >= 0) (void)hipSetDevice(prev);
+  if (e != hipSuccess) {
+    if (status) (void)hipFree(status);
+    return hip_status(e, "status word");
+  }
+  moe_ctx* c = new moe_ctx;
+  c->device = device;
+  c->cu_count = prop.multiProcessorCount;
+  c->status = status;
+  *out = c;
+  return ok();
+}
+
+moe_status_t moe_ctx_destroy(moe_ctx_t ctx) {
+  if (!ctx) return ok();
+  (void)hipFree(ctx->status);
+  delete ctx;
+  return ok();
+}
+
+moe_status_t moe_ctx_check_device_status(moe_ctx_t ctx, void* stream,
+                                         int32_t* host_code) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(host_code != nullptr, MOE_ERR_INVALID_ARG, "null host_code");
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ctx->status, sizeof(v),
+                                hipMemcpyDeviceToHost, as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e == hipSuccess && v != 0)
+    e = hipMemsetAsync(ctx->status, 0, sizeof(int32_t), as_stream(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_status(e, "device status");
+  *host_code = v;
+  if (v != 0)
+    return fail(MOE_ERR_DEVICE_CHECK, "device check code %d", (int)v);
+  return ok();
+}
+
+moe_status_t moe_route_topk(moe_ctx_t ctx, const float* logits, int64_t T,
+                            int32_t E, int32_t k, int32_t renormalize,
+                            int32_t* topk_idx, float* topk_w, void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T < 0");
+  MOE_REQUIRE(E >= 1 && k >= 1 && k <= E, MOE_ERR_INVALID_ARG,
+              "need 1 <= k <= E (k=%d, E=%d)", k, E);
+  MOE_REQUIRE(E <= MOE_MAX_EXPERTS && k <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED,
+              "E <= %d and k <= %d required", MOE_MAX_EXPERTS, MOE_MAX_TOPK);
+  MOE_REQUIRE(T <= (int64_t)INT32_MAX / 64, MOE_ERR_UNSUPPORTED, "T too large");
+  if (T == 0) return ok();
+  MOE_REQUIRE(logits && topk_idx && topk_w, MOE_ERR_INVALID_ARG,
+              "null tensor pointer");
+  return hip_status(moe::launch_route_topk(logits, T, E, k, renormalize != 0,
+                                           topk_idx, topk_w, as_stream(stream)),
+                    "route_topk launch");
+}
+
+moe_status_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k,
+                                        size_t* bytes) {
+  MOE_REQUIRE(bytes != nullptr, MOE_ERR_INVALID_ARG, "null output pointer");
+  MOE_REQUIRE(T >= 0 && E >= 1 && k >= 1, MOE_ERR_INVALID_ARG, "bad sizes");
+  *bytes = moe::permute_ws_bytes(T, E, k);
+  return ok();
+}
+
+moe_status_t moe_permute(moe_ctx_t ctx, const void* x,
+                         const int32_t* topk_idx, const float* topk_w,
+                         int64_t T, int32_t H, int32_t E, int32_t k,
+                         moe_precision_t out_prec, void* x_perm,
+                         uint8_t* x_perm_scale, float* w_perm,
+                         int32_t* row_map, int32_t* src_row,
+                         int32_t* split_sizes, int32_t* offsets, void* ws,
+                         size_t ws_bytes, void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(T >= 0 && H >= 1 && E >= 1 && k >= 1 && k <= E,
+              MOE_ERR_INVALID_ARG, "bad sizes (T=%lld H=%d E=%d k=%d)",
+              (long long)T, H, E, k);
+  MOE_REQUIRE(E <= MOE_MAX_EXPERTS && k <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED,
+              "E <= %d and k <= %d required", MOE_MAX_EXPERTS, MOE_MAX_TOPK);
+  MOE_REQUIRE(T * (int64_t)k <= (int64_t)INT32_MAX, MOE_ERR_UNSUPPORTED,
+              "T*k must fit in int32");
+  MOE_REQUIRE(out_prec == MOE_PREC_BF16 || out_prec == MOE_PREC_MXFP8_E4M3,
+              MOE_ERR_INVALID_ARG, "bad precision");
+  if (out_prec == MOE_PREC_BF16)
+    MOE_REQUIRE(H % 8 == 0, MOE_ERR_UNSUPPORTED, "H %% 8 != 0");
+  else
+    MOE_REQUIRE(H % 32 == 0, MOE_ERR_UNSUPPORTED, "H %% 32 != 0 (MXFP8)");
+  MOE_REQUIRE(split_sizes && offsets, MOE_ERR_INVALID_ARG,
+              "null split_sizes/offsets");
+  if (T > 0) {
+    MOE_REQUIRE(x && topk_idx && x_perm && row_map && src_row,
+                MOE_ERR_INVALID_ARG, "null tensor pointer");
+    MOE_REQUIRE(aligned16(x) && aligned16(x_perm), MOE_ERR_UNSUPPORTED,
+                "x / x_perm must be 16-byte aligned");
+    if (out_prec == MOE_PREC_MXFP8_E4M3)
+      MOE_REQUIRE(x_perm_scale != nullptr, MOE_ERR_INVALID_ARG,
+                  "MXFP8 permute needs x_perm_scale");
+    MOE_REQUIRE(w_perm == nullptr || topk_w != nullptr, MOE_ERR_INVALID_ARG,
+                "w_perm requested without topk_w");
+  }
+  const size_t need = moe::permute_ws_bytes(T, E, k);
+  MOE_REQUIRE(ws != nullptr && ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "permute workspace needs %zu bytes", need);
+  hipStream_t st = as_stream(stream);
+  hipError_t e = moe::launch_permute_index(topk_idx, T, E, k, row_map, src_row,
+                                           split_sizes, offsets, ws,
+                                           ctx->status, st);
+  if (e != hipSuccess) return hip_status(e, "permute index");
+  if (out_prec == MOE_PREC_BF16)
+    e = moe::launch_gather_rows(x, row_map, topk_w, T, H, k, x_perm, w_perm, st);
+  else
+    e = moe::launch_gather_rows_mx(x, row_map, topk_w, T, H, k,
+                                   static_cast<uint8_t*>(x_perm), x_perm_scale,
+                                   w_perm, st);
+  return hip_status(e, "permute gather");
+}
+
+moe_status_t moe_gather_rows(moe_ctx_t ctx, const void* src,
+                             const int32_t* row_map, int64_t T, int32_t H,
+                             int32_t k, void* dst, void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(T >= 0 && H >= 1 && k >= 1 && k <= MOE_MAX_TOPK,
+              MOE_ERR_INVALID_ARG, "bad sizes");
+  MOE_REQUIRE(H % 8 == 0, MOE_ERR_UNSUPPORTED, "H %% 8 != 0");
+  if (T == 0) return ok();
+  MOE_REQUIRE(src && row_map && dst, MOE_ERR_INVALID_ARG, "null pointer");
+  MOE_REQUIRE(aligned16(src) && aligned16(dst), MOE_ERR_UNSUPPORTED,
+              "src / dst must be 16-byte aligned");
+  return hip_status(moe::launch_gather_rows(src, row_map, nullptr, T, H, k,
+                                            dst, nullptr, as_stream(stream)),
+                    "gather rows");
+}
+
+moe_status_t moe_unpermute(moe_ctx_t ctx, const void* z_perm,
+                           const int32_t* row_map, const float* topk_w,
+                           int64_t T, int32_t H, int32_t k, void* y,
+                           void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(T >= 0 && H >= 1 && k >= 1 && k <= MOE_MAX_TOPK,
+              MOE_ERR_INVALID_ARG, "bad sizes");
+  MOE_REQUIRE(H % 8 == 0, MOE_ERR_UNSUPPORTED, "H %% 8 != 0");
+  if (T == 0) return ok();
+  MOE_REQUIRE(z_perm && row_map && y, MOE_ERR_INVALID_ARG, "null pointer");
+  MOE_REQUIRE(aligned16(z_perm) && aligned16(y), MOE_ERR_UNSUPPORTED,
+              "z_perm / y must be 16-byte aligned");
+  return hip_status(moe::launch_unpermute(z_perm, row_map, topk_w, T, H, k, y,
+                                          as_stream(stream)),
+                    "unpermute");
+}
+
+moe_status_t moe_unpermute_probs_grad(moe_ctx_t ctx, const float* dw_perm,
+                                      const int32_t* row_map, int64_t T,
+                                      int32_t k, float* dprobs, void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(T >= 0 && k >= 1, MOE_ERR_INVALID_ARG, "bad sizes");
+  if (T == 0) return ok();
+  MOE_REQUIRE(dw_perm && row_map && dprobs, MOE_ERR_INVALID_ARG,
+              "null pointer");
+  return hip_status(moe::launch_probs_grad(dw_perm, row_map, T, k, dprobs,
+                                           as_stream(stream)),
+                    "probs grad");
+}
+
+moe_status_t mxfp8_quantize(moe_ctx_t ctx, const void* src, int64_t batch,
+                            int64_t rows, int64_t cols, moe_mx_axis_t axis,
+                            const int32_t* seg_offsets, int32_t n_seg,
+                            uint8_t* codes, uint8_t* scales, void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0, MOE_ERR_INVALID_ARG,
+              "negative size");
+  MOE_REQUIRE(axis == MOE_MX_ROWWISE || axis == MOE_MX_COLWISE,
+              MOE_ERR_INVALID_ARG, "bad axis");
+  if (batch * rows * cols == 0) return ok();
+  MOE_REQUIRE(src && codes && scales, MOE_ERR_INVALID_ARG, "null pointer");
+  MOE_REQUIRE(aligned16(src) && aligned16(codes), MOE_ERR_UNSUPPORTED,
+              "src / codes must be 16-byte aligned");
+  hipStream_t st = as_stream(stream);
+  if (axis == MOE_MX_ROWWISE) {
+    MOE_REQUIRE(seg_offsets == nullptr, MOE_ERR_INVALID_ARG,
+                "segments apply to COLWISE only");
+    MOE_REQUIRE(cols % 32 == 0, MOE_ERR_UNSUPPORTED, "cols %% 32 != 0");
+    return hip_status(moe::launch_mx_quant_rows(src, batch * rows, cols, codes,
+                                                scales, st),
+                      "mxfp8 rows");
+  }
+  MOE_REQUIRE(cols % 8 == 0, MOE_ERR_UNSUPPORTED, "cols %% 8 != 0 (COLWISE)");
+  if (seg_offsets == nullptr) {
+    MOE_REQUIRE(rows % 32 == 0, MOE_ERR_UNSUPPORTED, "rows %% 32 != 0");
+    MOE_REQUIRE(rows / 32 <= 0x7fffffff && batch <= 65535, MOE_ERR_UNSUPPORTED,
+                "tensor too large");
+    return hip_status(moe::launch_mx_quant_cols(src, batch, rows, cols, codes,
+                                                scales, st),
+                      "mxfp8 cols");
+  }
+  MOE_REQUIRE(batch == 1, MOE_ERR_INVALID_ARG, "segments need batch == 1");
+  MOE_REQUIRE(n_seg >= 1 && n_seg <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED,
+              "1 <= n_seg <= %d", MOE_MAX_EXPERTS);
+  const int64_t ld = (rows + 32 * (int64_t)n_seg + 31) / 32 * 32;
+  return hip_status(moe::launch_mx_quant_segments(src, rows, cols, seg_offsets,
+                                                  n_seg, ld, codes, scales, st),
+                    "mxfp8 segments");
+}
+
+namespace {
+
+moe_status_t check_mlp_dims(int32_t E, int32_t H, int32_t F, int64_t rows,
+                            moe_precision_t prec) {
+  MOE_REQUIRE(E >= 1 && H >= 1 && F >= 1 && rows >= 0, MOE_ERR_INVALID_ARG,
+              "bad sizes (E=%d H=%d F=%d rows=%lld)", E, H, F,
+              (long long)rows);
+  MOE_REQUIRE(E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "E > %d",
+              MOE_MAX_EXPERTS);
+  MOE_REQUIRE(prec == MOE_PREC_BF16 || prec == MOE_PREC_MXFP8_E4M3,
+              MOE_ERR_INVALID_ARG, "bad precision");
+  // K steps of 64 (bf16) / 128 (MXFP8) without masking; N tails are masked
+  const int kq = prec == MOE_PREC_BF16 ? 64 : 128;
+  MOE_REQUIRE(H % kq == 0 && F % kq == 0, MOE_ERR_UNSUPPORTED,
+              "H and F must be multiples of %d", kq);
+  MOE_REQUIRE(rows <= (int64_t)INT32_MAX / 2 && (int64_t)F * 2 * H < ((int64_t)1 << 40),
+              MOE_ERR_UNSUPPORTED, "tensor too large");
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status_t moe_grouped_mlp_fwd_workspace_size(const moe_mlp_fwd_args* a,
+                                                size_t* bytes) {
+  MOE_REQUIRE(a && bytes, MOE_ERR_INVALID_ARG, "null pointer");
+  moe_status_t s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
+  if (s != MOE_OK) return s;
+  if (a->precision == MOE_PREC_BF16)
+    *bytes = moe::mlp_fwd_bf16_ws_bytes(a->E, a->H, a->F, a->rows,
+                                        a->a_save == nullptr);
+  else
+    *bytes = moe::mlp_fwd_mx_ws_bytes(
+        a->E, a->H, a->F, a->rows, a->x_perm_scale == nullptr,
+        a->w_gu_q == nullptr || a->w_dn_q == nullptr);
+  return ok();
+}
+
+moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
+                                 void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(a != nullptr, MOE_ERR_INVALID_ARG, "null args");
+  s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(a->offsets && a->z_perm, MOE_ERR_INVALID_ARG,
+              "null offsets / z_perm");
+  MOE_REQUIRE(a->x_perm != nullptr || a->rows == 0, MOE_ERR_INVALID_ARG,
+              "null x_perm");
+  const bool mx = a->precision == MOE_PREC_MXFP8_E4M3;
+  if (!mx || a->w_gu_q == nullptr || a->w_dn_q == nullptr)
+    MOE_REQUIRE(a->w_gu && a->w_dn, MOE_ERR_INVALID_ARG, "null weights");
+  if (mx && a->w_gu_q) MOE_REQUIRE(a->w_gu_s, MOE_ERR_INVALID_ARG, "w_gu_s");
+  if (mx && a->w_dn_q) MOE_REQUIRE(a->w_dn_s, MOE_ERR_INVALID_ARG, "w_dn_s");
+  size_t need = 0;
+  moe_grouped_mlp_fwd_workspace_size(a, &need);
+  MOE_REQUIRE(a->ws != nullptr && a->ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "grouped_mlp_fwd workspace needs %zu bytes", need);
+  hipError_t e;
+  if (!mx) {
+    e = moe::launch_mlp_fwd_bf16(a->E, a->H, a->F, a->rows, a->x_perm, a->w_gu,
+                                 a->w_dn, a->w_perm, a->offsets, a->z_perm,
+                                 a->h1_save, a->a_save, a->ws,
+                                 as_stream(stream));
+  } else {
+    const bool xq = a->x_perm_scale != nullptr;
+    e = moe::launch_mlp_fwd_mx(
+        a->E, a->H, a->F, a->rows, xq ? nullptr : a->x_perm,
+        xq ? static_cast<const uint8_t*>(a->x_perm) : nullptr,
+        a->x_perm_scale, a->w_gu, a->w_dn, a->w_gu_q, a->w_gu_s, a->w_dn_q,
+        a->w_dn_s, a->w_perm, a->offsets, a->z_perm, a->h1_save, a->a_save,
+        a->ws, as_stream(stream));
+  }
+  return hip_status(e, "grouped_mlp_fwd");
+}
+
+moe_status_t moe_grouped_mlp_bwd_workspace_size(const moe_mlp_bwd_args* a,
+                                                size_t* bytes) {
+  MOE_REQUIRE(a && bytes, MOE_ERR_INVALID_ARG, "null pointer");
+  moe_status_t s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
+  if (s != MOE_OK) return s;
+  if (a->precision == MOE_PREC_BF16)
+    *bytes = moe::mlp_bwd_bf16_ws_bytes(a->E, a->H, a->F, a->rows);
+  else
+    *bytes = moe::mlp_bwd_mx_ws_bytes(a->E, a->H, a->F, a->rows);
+  return ok();
+}
+
+moe_status_t moe_grouped_mlp_bwd(moe_ctx_t ctx, const moe_mlp_bwd_args* a,
+                                 void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(a != nullptr, MOE_ERR_INVALID_ARG, "null args");
+  s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(a->offsets && a->w_gu && a->w_dn && a->dw_gu && a->dw_dn,
+              MOE_ERR_INVALID_ARG, "null offsets / weights / weight grads");
+  if (a->rows > 0)
+    MOE_REQUIRE(a->x_perm && a->h1_save && a->a_save && a->dz_perm &&
+                    a->dx_perm,
+                MOE_ERR_INVALID_ARG, "null activation pointer");
+  MOE_REQUIRE(a->w_perm != nullptr || a->dw_perm == nullptr ||
+                  a->rows == 0,
+              MOE_ERR_INVALID_ARG, "dw_perm needs w_perm");
+  size_t need = 0;
+  moe_grouped_mlp_bwd_workspace_size(a, &need);
+  MOE_REQUIRE(a->ws != nullptr && a->ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "grouped_mlp_bwd workspace needs %zu bytes", need);
+  hipError_t e;
+  if (a->precision == MOE_PREC_BF16)
+    e = moe::launch_mlp_bwd_bf16(a->E, a->H, a->F, a->rows, a->x_perm, a->w_gu,
+                                 a->w_dn, a->w_perm, a->offsets, a->h1_save,
+                                 a->a_save, a->dz_perm, a->dx_perm, a->dw_gu,
+                                 a->dw_dn, a->w_perm ? a->dw_perm : nullptr,
+                                 a->ws, as_stream(stream));
+  else
+    e = moe::launch_mlp_bwd_mx(a->E, a->H, a->F, a->rows, a->x_perm, a->w_gu,
+                               a->w_dn, a->w_perm, a->offsets, a->h1_save,
+                               a->a_save, a->dz_perm, a->dx_perm, a->dw_gu,
+                               a->dw_dn, a->w_perm ? a->dw_perm : nullptr,
+                               a->ws, as_stream(stream));
+  return hip_status(e, "grouped_mlp_bwd");
+}
+
+}  // extern "C"

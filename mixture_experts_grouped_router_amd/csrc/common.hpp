@@ -1,0 +1,77 @@
+// Device helpers shared by the libmoe kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx_codec.hpp"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) 16-byte global load / store.
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u32x4_t v =
+      __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(uint4* p, const uint4 v) {
+  u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
+// bfloat16 storage <-> float32.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf16lo(uint32_t pair) {
+  return __uint_as_float(pair << 16);
+}
+__device__ __forceinline__ float bf16hi(uint32_t pair) {
+  return __uint_as_float(pair & 0xffff0000u);
+}
+// float32 -> bfloat16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Record the first device-side data error (first error wins).
+__device__ __forceinline__ void report_error(int32_t* status, int32_t code) {
+  if (status) atomicCAS(status, 0, code);
+}
+
+// Exclusive scan of one int per thread over a block of exactly 256 threads.
+// Returns the thread's exclusive prefix and the block total in *total.
+__device__ __forceinline__ int32_t block_exclusive_scan_256(int32_t v,
+                                                            int32_t* total) {
+  __shared__ int32_t wsum[4];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int32_t s = wsum[w];
+    if (w < wid) before += s;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return incl - v + before;
+}
+
+}  // namespace moe

@@ -1,0 +1,84 @@
+// Internal launch wrappers of libmoe (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// router top-k
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
+                             int renorm, int32_t* idx, float* w,
+                             hipStream_t stream);
+
+// permutation
+size_t permute_ws_bytes(int64_t T, int E, int k);
+hipError_t launch_permute_index(const int32_t* topk_idx, int64_t T, int E,
+                                int k, int32_t* row_map, int32_t* src_row,
+                                int32_t* split, int32_t* offsets, void* ws,
+                                int32_t* status, hipStream_t stream);
+hipError_t launch_gather_rows(const void* x, const int32_t* row_map,
+                              const float* topk_w, int64_t T, int H, int k,
+                              void* x_perm, float* w_perm, hipStream_t stream);
+hipError_t launch_gather_rows_mx(const void* x, const int32_t* row_map,
+                                 const float* topk_w, int64_t T, int H, int k,
+                                 uint8_t* codes, uint8_t* scales,
+                                 float* w_perm, hipStream_t stream);
+hipError_t launch_unpermute(const void* z, const int32_t* row_map,
+                            const float* topk_w, int64_t T, int H, int k,
+                            void* y, hipStream_t stream);
+hipError_t launch_probs_grad(const float* dw_perm, const int32_t* row_map,
+                             int64_t T, int k, float* dprobs,
+                             hipStream_t stream);
+
+// MXFP8 quantisation
+hipError_t launch_mx_quant_rows(const void* src, int64_t rows, int64_t cols,
+                                uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream);
+hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
+                                int64_t cols, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream);
+hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
+                                    int64_t cols, const int32_t* seg_offsets,
+                                    int n_seg, int64_t ld, uint8_t* codes,
+                                    uint8_t* scales, hipStream_t stream);
+
+// bf16 grouped MLP
+size_t mlp_fwd_bf16_ws_bytes(int E, int H, int F, int64_t rows, bool need_a);
+hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
+                               const void* x_perm, const void* w_gu,
+                               const void* w_dn, const float* w_perm,
+                               const int32_t* offsets, void* z_perm,
+                               void* h1_save, void* a_save, void* ws,
+                               hipStream_t stream);
+size_t mlp_bwd_bf16_ws_bytes(int E, int H, int F, int64_t rows);
+hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
+                               const void* x_perm, const void* w_gu,
+                               const void* w_dn, const float* w_perm,
+                               const int32_t* offsets, const void* h1_save,
+                               const void* a_save, const void* dz_perm,
+                               void* dx_perm, void* dw_gu, void* dw_dn,
+                               float* dw_perm, void* ws, hipStream_t stream);
+
+// MXFP8 grouped MLP
+size_t mlp_fwd_mx_ws_bytes(int E, int H, int F, int64_t rows, bool quant_x,
+                           bool quant_w);
+hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
+                             const void* x_perm_bf16, const uint8_t* xq,
+                             const uint8_t* xs, const void* w_gu,
+                             const void* w_dn, const uint8_t* w_gu_q,
+                             const uint8_t* w_gu_s, const uint8_t* w_dn_q,
+                             const uint8_t* w_dn_s, const float* w_perm,
+                             const int32_t* offsets, void* z_perm,
+                             void* h1_save, void* a_save, void* ws,
+                             hipStream_t stream);
+size_t mlp_bwd_mx_ws_bytes(int E, int H, int F, int64_t rows);
+hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
+                             const void* x_perm, const void* w_gu,
+                             const void* w_dn, const float* w_perm,
+                             const int32_t* offsets, const void* h1_save,
+                             const void* a_save, const void* dz_perm,
+                             void* dx_perm, void* dw_gu, void* dw_dn,
+                             float* dw_perm, void* ws, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,85 @@
+// MXFP8 element/scale encoding with integer operations only.  Usable from
+// device code (hipcc) and from plain C++ host code (CPU checks of the exact
+// same functions).
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define MOE_HD __host__ __device__
+#else
+#define MOE_HD
+#endif
+
+namespace moe {
+
+// count of leading zero bits of a non-zero 32-bit value
+MOE_HD inline int moe_clz32(uint32_t v) { return __builtin_clz(v); }
+
+// E4M3 (OCP) code of a bfloat16 value scaled by 2^-s, computed with integer
+// operations only: round to nearest even on the 3-bit mantissa grid,
+// subnormals m*2^-9, saturation at 448 (0x7E), sign kept on zero results.
+// `b` is the 16-bit bf16 pattern (finite), `s` the block scale exponent.
+MOE_HD inline uint32_t e4m3_from_bf16(uint32_t b, int s) {
+  const uint32_t sign = (b >> 8) & 0x80u;
+  const int be = (int)((b >> 7) & 0xFF);
+  uint32_t man = b & 0x7Fu;
+  if (be == 0 && man == 0) return sign;
+  // value = sig * 2^(ex - 7) with sig a 8-bit integer in [128, 256) for
+  // normals; bf16 subnormals are normalised first.
+  int ex;
+  uint32_t sig;
+  if (be == 0) {
+    // subnormal: man * 2^-133; normalise to [128, 256)
+    int lz = moe_clz32(man) - 24;  // leading zeros within 8 bits
+    sig = man << lz;
+    ex = -126 - lz;
+  } else {
+    sig = 0x80u | man;
+    ex = be - 127;
+  }
+  ex -= s;  // scaled exponent: value = sig/128 * 2^ex
+  // target quantum exponent: max(ex, -6) - 3; value / quantum =
+  // sig * 2^(ex - 7 - q) with q = max(ex,-6)-3.
+  int qe = (ex > -6 ? ex : -6) - 3;
+  int shift = qe - (ex - 7);  // >= 4; right shift of sig
+  uint32_t q;
+  if (shift >= 32) {
+    q = 0;
+  } else {
+    uint32_t kept = sig >> shift;
+    uint32_t rem = sig & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    q = kept + ((rem > half || (rem == half && (kept & 1u))) ? 1u : 0u);
+  }
+  int e = (ex > -6 ? ex : -6);
+  if (q >= 16u) { e += 1; q = 8u; }
+  uint32_t code;
+  if (q >= 8u) {
+    if (e > 8) code = 0x7Eu;
+    else {
+      code = (uint32_t)((e + 7) << 3) | (q - 8u);
+      if (code > 0x7Eu) code = 0x7Eu;
+    }
+  } else {
+    code = q;  // subnormal (e == -6)
+  }
+  return code | sign;
+}
+
+// Scale exponent s of a block from the bf16 pattern of its amax (finite,
+// sign cleared): floor(log2 amax) - 8 clamped to [-127, 127]; zero -> -127.
+MOE_HD inline int e8m0_exp_from_bf16_amax(uint32_t a) {
+  const int be = (int)((a >> 7) & 0xFF);
+  const uint32_t man = a & 0x7Fu;
+  int fl;
+  if (be == 0) {
+    if (man == 0) return -127;
+    fl = -133 + (31 - moe_clz32(man));  // man * 2^-133: floor(log2) = -133 + msb
+  } else {
+    fl = be - 127;
+  }
+  int s = fl - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+}  // namespace moe

@@ -1,0 +1,204 @@
+// MXFP8 quantisation of bf16 tensors: E4M3 elements, one E8M0 scale per
+// block of 32 consecutive values ("NVIDIA presents an efficient path for
+// training biological MoE models", section "Reducing memory and quantisation
+// cost"; "Efficient MoE training for biological foundation models
+// (NVIDIA)", section "2) Model size and activation memory").  16-bit master
+// weights are quantised from bf16 on the fly ("Efficient MoE training ...",
+// section "3) Quantisation overhead in low-precision training").
+//
+// Encoding with integer operations only (mx_codec.hpp): scale exponent
+// s = floor(log2 amax) - 8, element = E4M3(v * 2^-s) with round to nearest
+// even and saturation at 448.  All three kernels are HBM-bound streaming
+// passes: 2 bytes read, 1 + 1/32 bytes written per element.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) {
+  return a > b ? a : b;
+}
+
+// 8 bf16 (one uint4) -> 8 E4M3 codes (uint2) with scale exponent s.
+__device__ __forceinline__ uint2 encode8(const uint4 v, int s) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t q[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[i >> 1] |= e4m3_from_bf16(w[i] & 0xffffu, s) << (16 * (i & 1));
+    q[i >> 1] |= e4m3_from_bf16(w[i] >> 16, s) << (16 * (i & 1) + 8);
+  }
+  return make_uint2(q[0], q[1]);
+}
+
+__device__ __forceinline__ uint32_t amax8(const uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t a = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a = umax(a, w[i] & 0x7fffu);
+    a = umax(a, (w[i] >> 16) & 0x7fffu);
+  }
+  return a;
+}
+
+// Row-wise: 4 consecutive lanes own one block of 32 along a row.
+__global__ __launch_bounds__(256) void mx_rows_kernel(
+    const uint4* __restrict__ src, int64_t n_chunks,
+    uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // n_chunks is a multiple of 4 and so is the stride: groups of 4 lanes stay
+  // aligned to blocks in every iteration.
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+       c - threadIdx.x % 4 < n_chunks; c += stride) {
+    const bool act = c < n_chunks;
+    const uint4 v = act ? ld_nt(src + c)
+                        : make_uint4(0, 0, 0, 0);
+    uint32_t a = amax8(v);
+    a = umax(a, __shfl_xor(a, 1, 64));
+    a = umax(a, __shfl_xor(a, 2, 64));
+    const int s = e8m0_exp_from_bf16_amax(a);
+    if (act) {
+      codes[c] = encode8(v, s);
+      if ((c & 3) == 0) scales[c >> 2] = (uint8_t)(s + 127);
+    }
+  }
+}
+
+// Column-wise tile kernel: a block covers 32 rows x 64 columns of one batch
+// entry; blocks run down the columns (32 values); output transposed.
+// Segment mode: rows come from one segment (zero-padded past its end) and
+// land at padded output offsets.
+template <bool SEG>
+__global__ __launch_bounds__(256) void mx_cols_kernel(
+    const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
+    const int32_t* __restrict__ seg_offsets, int n_seg, int64_t ld_out,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ uint16_t tile[32][64 + 2];
+  __shared__ int32_t tprefix[1025];
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.z;
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
+  int64_t r0, rend, out0;
+  if (SEG) {
+    // tile prefix over segments (ceil(n_s / 32) row tiles each): thread t
+    // owns segments 4t .. 4t+3, then a block-wide exclusive scan.
+    int32_t cnt4[4], own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sg = 4 * t + i;
+      cnt4[i] = sg < n_seg ? (seg_offsets[sg + 1] - seg_offsets[sg] + 31) / 32 : 0;
+      own += cnt4[i];
+    }
+    int32_t total;
+    int32_t run = block_exclusive_scan_256(own, &total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sg = 4 * t + i;
+      if (sg < n_seg) tprefix[sg] = run;
+      run += cnt4[i];
+    }
+    if (t == 0) tprefix[n_seg] = total;
+    __syncthreads();
+    const int g = blockIdx.x;
+    if (g >= tprefix[n_seg]) return;
+    int lo = 0, hi = n_seg;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tprefix[mid] <= g) lo = mid; else hi = mid;
+    }
+    const int lt = g - tprefix[lo];
+    r0 = seg_offsets[lo] + (int64_t)lt * 32;
+    rend = seg_offsets[lo + 1];
+    out0 = (int64_t)g * 32;
+  } else {
+    r0 = (int64_t)blockIdx.x * 32;
+    rend = rows;
+    out0 = r0;
+  }
+  const uint16_t* base = src + b * rows * cols;
+  // load 32 x 64: thread t -> row t / 8, 16-byte chunk t % 8
+  {
+    const int rr = t >> 3, ch = t & 7;
+    const int64_t r = r0 + rr;
+    const int64_t c = c0 + ch * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < rend && c < cols)
+      v = *reinterpret_cast<const uint4*>(base + r * cols + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[rr][ch * 8 + 2 * i] = (uint16_t)(w[i] & 0xffffu);
+      tile[rr][ch * 8 + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+    }
+  }
+  __syncthreads();
+  // thread t -> column t / 4, rows 8 (t % 4) .. +7
+  const int col = t >> 2, q = t & 3;
+  uint32_t a = 0;
+  uint32_t vals[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    vals[i] = tile[q * 8 + i][col];
+    a = umax(a, vals[i] & 0x7fffu);
+  }
+  a = umax(a, __shfl_xor(a, 1, 64));
+  a = umax(a, __shfl_xor(a, 2, 64));
+  const int s = e8m0_exp_from_bf16_amax(a);
+  const int64_t c = c0 + col;
+  if (c < cols) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= e4m3_from_bf16(vals[i], s) << (8 * i);
+      hi |= e4m3_from_bf16(vals[i + 4], s) << (8 * i);
+    }
+    const int64_t obase = (b * cols + c) * ld_out + out0 + q * 8;
+    *reinterpret_cast<uint2*>(codes + obase) = make_uint2(lo, hi);
+    if (q == 0) scales[(b * cols + c) * (ld_out / 32) + out0 / 32] = (uint8_t)(s + 127);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mx_quant_rows(const void* src, int64_t rows, int64_t cols,
+                                uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream) {
+  const int64_t n_chunks = rows * cols / 8;
+  if (n_chunks == 0) return hipSuccess;
+  int64_t blocks = (n_chunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(mx_rows_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     stream, static_cast<const uint4*>(src), n_chunks,
+                     reinterpret_cast<uint2*>(codes), scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
+                                int64_t cols, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream) {
+  if (batch * rows * cols == 0) return hipSuccess;
+  const dim3 grid((unsigned)(rows / 32), (unsigned)((cols + 63) / 64),
+                  (unsigned)batch);
+  hipLaunchKernelGGL(mx_cols_kernel<false>, grid, dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(src), rows, cols,
+                     (const int32_t*)nullptr, 0, rows, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
+                                    int64_t cols, const int32_t* seg_offsets,
+                                    int n_seg, int64_t ld, uint8_t* codes,
+                                    uint8_t* scales, hipStream_t stream) {
+  if (rows * cols == 0) return hipSuccess;
+  // sum_s ceil(n_s / 32) <= rows / 32 + n_seg
+  const int64_t tiles = rows / 32 + n_seg;
+  const dim3 grid((unsigned)tiles, (unsigned)((cols + 63) / 64), 1);
+  hipLaunchKernelGGL(mx_cols_kernel<true>, grid, dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(src), rows, cols,
+                     seg_offsets, n_seg, ld, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

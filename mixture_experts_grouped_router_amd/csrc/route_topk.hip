@@ -1,0 +1,139 @@
+// Router top-k: one wave64 per token.
+//
+// Top-k routing over the E router logits of each token ("Nous Research
+// scales expert parallelism with DeepEP", practical-implications paragraph;
+// "Efficient MoE training for biological foundation models (NVIDIA)",
+// section "Why dense and MoE models differ": a small subset of experts per
+// token).  Weights: softmax restricted to the chosen experts (or over all E),
+// evaluated in float64 and rounded to float32.
+//
+// Each lane holds E/64 logits in registers.  k rounds of a wave-wide argmax
+// (larger value first, lower expert id on ties) pick the experts; lane j
+// keeps slot j.  No LDS, no atomics.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+struct Cand {
+  float v;
+  int e;
+};
+
+// a beats b: larger logit, or equal logit and lower expert id.  +0 == -0
+// under float comparison, so signed zeros tie and fall to the id rule.
+__device__ __forceinline__ bool beats(float av, int ae, float bv, int be) {
+  return av > bv || (av == bv && ae < be);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void route_topk_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int renorm,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + t * (int64_t)E;
+
+  float v[VPL];
+  uint32_t taken = 0;  // bit i: v[i] already selected
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : 0.0f;
+    if (e >= E) taken |= 1u << i;
+  }
+
+  float my_v = 0.0f;  // lane j < k: logit of slot j
+  int my_e = 0;
+  float top_v = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    // lane-local best among not-yet-taken values
+    float bv = 0.0f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (!(taken >> i & 1u) && (be == 0x7fffffff || beats(v[i], e, bv, be))) {
+        bv = v[i];
+        be = e;
+      }
+    }
+    // wave-wide argmax (butterfly: every lane ends with the winner)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      if (oe != 0x7fffffff && (be == 0x7fffffff || beats(ov, oe, bv, be))) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == j) {
+      my_v = bv;
+      my_e = be;
+    }
+    if (j == 0) top_v = bv;
+  }
+
+  // weights in float64: exp(l - max) / sum
+  const double m = (double)top_v;
+  double num = 0.0;
+  if (lane < k) num = exp((double)my_v - m);
+  double part;
+  if (renorm) {
+    part = num;
+  } else {
+    part = 0.0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) part += exp((double)v[i] - m);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+  if (lane < k) {
+    topk_idx[t * k + lane] = my_e;
+    topk_w[t * k + lane] = (float)(num / part);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
+                             int renorm, int32_t* idx, float* w,
+                             hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int tokens_per_block = 4;
+  const dim3 grid((unsigned)((T + tokens_per_block - 1) / tokens_per_block));
+  const int vpl = (E + 63) / 64;
+#define MOE_ROUTE_CASE(N)                                                      \
+  case N:                                                                      \
+    hipLaunchKernelGGL(route_topk_kernel<N>, grid, dim3(256), 0, stream,      \
+                       logits, T, E, k, renorm, idx, w);                       \
+    break;
+  switch (vpl) {
+    MOE_ROUTE_CASE(1)
+    MOE_ROUTE_CASE(2)
+    MOE_ROUTE_CASE(4)
+    MOE_ROUTE_CASE(8)
+    MOE_ROUTE_CASE(16)
+    case 3: hipLaunchKernelGGL(route_topk_kernel<4>, grid, dim3(256), 0, stream,
+                               logits, T, E, k, renorm, idx, w); break;
+    default:
+      if (vpl <= 8)
+        hipLaunchKernelGGL(route_topk_kernel<8>, grid, dim3(256), 0, stream,
+                           logits, T, E, k, renorm, idx, w);
+      else
+        hipLaunchKernelGGL(route_topk_kernel<16>, grid, dim3(256), 0, stream,
+                           logits, T, E, k, renorm, idx, w);
+  }
+#undef MOE_ROUTE_CASE
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,369 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: routing indices, permutation maps, split_sizes/offsets and MXFP8 codes
+and scales bit-exact; routing weights within 1 float32 ulp; bf16 outputs and
+gradients within normwise relative error 2e-2 (and 4e-2 per token row /
+per expert slice); MXFP8 layer outputs within 6e-2 of the oracle running the
+same MXFP8 algorithm.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synthetic import CONFIGS, bf16_bits, bf16_to_f32, bf16_to_f64, generate
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_MX = 6e-2
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixture_experts_grouped_router_amd as mod
+    mod.load_library()   # raises if the HIP library is missing
+    return mod
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+        torch.bfloat16).cuda()
+
+
+def host_bits(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def host_f64(t):
+    return bf16_to_f64(host_bits(t))
+
+
+def _ulp_diff_f32(a, b):
+    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ai - bi)
+
+
+def assert_rows_close(got, ref, tol, name):
+    err = O.rel_err(got, ref)
+    assert err <= tol, f"{name}: normwise {err:.3e} > {tol}"
+    n = np.linalg.norm(ref, axis=-1)
+    d = np.linalg.norm(got - ref, axis=-1)
+    ok = n > 0
+    worst = (d[ok] / n[ok]).max() if ok.any() else 0.0
+    assert worst <= 2 * tol, f"{name}: worst row {worst:.3e}"
+    assert np.all(d[~ok] == 0), f"{name}: non-zero where reference is zero"
+
+
+# ---------------------------------------------------------------- routing
+@pytest.mark.parametrize("T,E,k,renorm,seed", [
+    (256, 8, 2, True, 0), (1000, 128, 8, True, 1), (333, 100, 5, False, 2),
+    (64, 8, 8, True, 3), (1, 3, 1, True, 4), (513, 1024, 32, True, 5),
+    (200, 64, 6, False, 6)])
+def test_route_topk_matches_oracle(m, T, E, k, renorm, seed):
+    lg = np.random.default_rng(seed).standard_normal((T, E)).astype(np.float32)
+    idx, w = m.moe_route_topk(torch.from_numpy(lg).cuda(), k, renorm)
+    ridx, rw = O.route_topk(lg, k, renorm)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    assert _ulp_diff_f32(w.cpu().numpy(), rw).max() <= 1
+
+
+def test_route_topk_ties_and_signed_zero(m):
+    rng = np.random.default_rng(7)
+    lg = rng.integers(-2, 3, size=(4096, 16)).astype(np.float32)
+    lg[rng.random(lg.shape) < 0.2] = -0.0
+    idx, w = m.moe_route_topk(torch.from_numpy(lg).cuda(), 4)
+    ridx, rw = O.route_topk(lg, 4)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    assert _ulp_diff_f32(w.cpu().numpy(), rw).max() <= 1
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3"])
+def test_route_topk_config_logits(m, name):
+    c = CONFIGS[name]
+    d = generate(c.T, c.H, c.F, c.E, c.k, zipf=c.zipf, want=("logits",))
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), c.k)
+    ridx, rw = O.route_topk(d["logits"], c.k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    assert _ulp_diff_f32(w.cpu().numpy(), rw).max() <= 1
+
+
+# ------------------------------------------------------------ permutation
+def _perm_case(m, T, H, E, k, zipf=0.0, seed=0, logits=None):
+    d = generate(T, H, 64, E, k, zipf=zipf, seed=seed, want=("x", "logits"))
+    lg = d["logits"] if logits is None else logits
+    ridx, rw = O.route_topk(lg, k)
+    x = dev_bf16(d["x"])
+    out = m.moe_permute(x, torch.from_numpy(ridx).cuda(), E,
+                        topk_w=torch.from_numpy(rw).cuda())
+    ref = O.permute_index(ridx, E)
+    for key in ("split_sizes", "offsets", "row_map", "src_row"):
+        np.testing.assert_array_equal(out[key].cpu().numpy(), ref[key], key)
+    np.testing.assert_array_equal(host_bits(out["x_perm"]),
+                                  O.permute_rows(d["x"], ref["src_row"], k))
+    np.testing.assert_array_equal(out["w_perm"].cpu().numpy(),
+                                  O.permute_weights(rw, ref["src_row"]))
+    return d, ridx, rw, out, ref
+
+
+@pytest.mark.parametrize("T,H,E,k,zipf", [
+    (256, 128, 8, 2, 0.0), (2000, 264, 128, 8, 1.2), (1025, 64, 16, 4, 0.0),
+    (1, 8, 4, 2, 0.0), (3000, 2048, 128, 8, 1.2)])
+def test_permute_bit_exact(m, T, H, E, k, zipf):
+    _perm_case(m, T, H, E, k, zipf)
+
+
+def test_permute_degenerate_routings(m):
+    T, H, E, k = 700, 96, 32, 1
+    lg = np.full((T, E), -5.0, np.float32)
+    lg[:, 17] = 3.0                      # every token to expert 17
+    _, _, _, out, _ = _perm_case(m, T, H, E, k, logits=lg)
+    sp = out["split_sizes"].cpu().numpy()
+    assert sp[17] == T and sp.sum() == T
+    # E = 1, k = 1: the identity permutation
+    _, _, _, out, _ = _perm_case(m, 100, 16, 1, 1)
+    assert np.array_equal(out["row_map"].cpu().numpy(), np.arange(100))
+
+
+@pytest.mark.parametrize("k", [1, 2, 8])
+def test_permute_unpermute_identity_bitwise(m, k):
+    T, H, E = 500, 256, 8
+    d, ridx, rw, out, ref = _perm_case(m, T, H, E, k)
+    y = m.moe_unpermute(out["x_perm"], out["row_map"], k)
+    x = bf16_to_f64(d["x"])
+    np.testing.assert_array_equal(host_bits(y),
+                                  bf16_bits((k * x).astype(np.float32)))
+    w = torch.full((T, k), 1.0 / k, dtype=torch.float32, device="cuda")
+    y2 = m.moe_unpermute(out["x_perm"], out["row_map"], k, topk_w=w)
+    np.testing.assert_array_equal(host_bits(y2), d["x"])
+
+
+def test_unpermute_weighted_matches_oracle(m):
+    T, H, E, k = 300, 128, 16, 4
+    rng = np.random.default_rng(3)
+    d, ridx, rw, out, ref = _perm_case(m, T, H, E, k)
+    z = bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    y = m.moe_unpermute(dev_bf16(z), out["row_map"], k,
+                        topk_w=torch.from_numpy(rw).cuda())
+    yr = O.unpermute(bf16_to_f64(z), ref["row_map"], k, topk_w=rw)
+    # float32 sum of k terms, then one bf16 rounding
+    np.testing.assert_allclose(host_f64(y), yr, rtol=2 ** -8, atol=1e-6)
+
+
+def test_gather_rows_and_probs_grad(m):
+    T, H, E, k = 400, 64, 8, 2
+    d, ridx, rw, out, ref = _perm_case(m, T, H, E, k)
+    dy = bf16_bits(np.random.default_rng(1).standard_normal(
+        (T, H)).astype(np.float32))
+    dz = m.moe_gather_rows(dev_bf16(dy), out["row_map"], k)
+    np.testing.assert_array_equal(host_bits(dz),
+                                  O.gather_rows(dy, ref["src_row"], k))
+    dwp = np.random.default_rng(2).standard_normal(T * k).astype(np.float32)
+    dp = m.moe_unpermute_probs_grad(torch.from_numpy(dwp).cuda(),
+                                    out["row_map"], k)
+    np.testing.assert_array_equal(dp.cpu().numpy(),
+                                  O.probs_grad(dwp, ref["row_map"], k)
+                                  .astype(np.float32))
+
+
+def test_device_check_flags_bad_expert_id(m):
+    T, H, E, k = 64, 32, 8, 2
+    idx = np.random.default_rng(0).integers(0, E, size=(T, k)).astype(np.int32)
+    idx[5, 1] = E + 3                    # written on the host, then uploaded
+    x = torch.zeros((T, H), dtype=torch.bfloat16, device="cuda")
+    assert m.check_device_status() == 0
+    out = m.moe_permute(x, torch.from_numpy(idx).cuda(), E)
+    assert m.check_device_status() == 1
+    assert out["row_map"][5 * k + 1].item() == -1
+    assert int(out["split_sizes"].sum().item()) == T * k - 1
+    assert m.check_device_status() == 0  # cleared by the previous check
+
+
+# ------------------------------------------------------------ MXFP8 quant
+def test_mxfp8_rowwise_all_bf16_patterns(m):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]          # finite values
+    rng = np.random.default_rng(0)
+    n = (bits.size // 32) * 32
+    a = rng.permutation(bits)[:n].reshape(-1, 64) if n % 64 == 0 else \
+        rng.permutation(bits)[:(n // 64) * 64].reshape(-1, 64)
+    codes, scales = m.mxfp8_quantize(dev_bf16(a), m.ROWWISE)
+    rc, rs = O.mxfp8_quantize_rows(a)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+def test_mxfp8_rowwise_scale_spread(m):
+    # blocks whose amax spans the whole exponent range, including subnormals
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal((512, 256)).astype(np.float32)
+    v *= np.ldexp(1.0, rng.integers(-140, 120, size=(512, 8))).repeat(
+        32, axis=1).astype(np.float32)
+    a = bf16_bits(v)
+    codes, scales = m.mxfp8_quantize(dev_bf16(a), m.ROWWISE)
+    rc, rs = O.mxfp8_quantize_rows(a)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+def test_mxfp8_colwise_and_batched(m):
+    rng = np.random.default_rng(2)
+    a = bf16_bits(rng.standard_normal((3, 96, 200)).astype(np.float32))
+    codes, scales = m.mxfp8_quantize(dev_bf16(a), m.COLWISE)
+    for b in range(3):
+        rc, rs = O.mxfp8_quantize_cols(a[b])
+        np.testing.assert_array_equal(codes[b].cpu().numpy(), rc)
+        np.testing.assert_array_equal(scales[b].cpu().numpy(), rs)
+
+
+def test_mxfp8_segments(m):
+    rng = np.random.default_rng(3)
+    off = np.array([0, 0, 45, 45, 77, 200, 200], dtype=np.int32)
+    a = bf16_bits(rng.standard_normal((200, 72)).astype(np.float32))
+    codes, scales = m.mxfp8_quantize(dev_bf16(a), m.COLWISE,
+                                     seg_offsets=torch.from_numpy(off).cuda())
+    rc, rs = O.mxfp8_quantize_segments(a, off)
+    w = rc.shape[1]
+    np.testing.assert_array_equal(codes[:, :w].cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales[:, :w // 32].cpu().numpy(), rs)
+
+
+def test_permute_fused_mxfp8_bit_exact(m):
+    T, H, E, k = 300, 256, 8, 2
+    d = generate(T, H, 64, E, k, want=("x", "logits"))
+    ridx, rw = O.route_topk(d["logits"], k)
+    out = m.moe_permute(dev_bf16(d["x"]), torch.from_numpy(ridx).cuda(), E,
+                        topk_w=torch.from_numpy(rw).cuda(),
+                        precision=m.PREC_MXFP8)
+    ref = O.permute_index(ridx, E)
+    rc, rs = O.mxfp8_quantize_rows(O.permute_rows(d["x"], ref["src_row"], k))
+    np.testing.assert_array_equal(out["x_perm"].cpu().numpy(), rc)
+    np.testing.assert_array_equal(out["x_perm_scale"].cpu().numpy(), rs)
+
+
+# ------------------------------------------------------- grouped MLP, bf16
+def _mlp_case(T, H, F, E, k, zipf, seed, logits_shift=None):
+    d = generate(T, H, F, E, k, zipf=zipf, seed=seed,
+                 want=("x", "logits", "w_gu", "w_dn", "dy"))
+    if logits_shift is not None:
+        d["logits"] = (d["logits"] + logits_shift).astype(np.float32)
+    return d
+
+
+MLP_CASES = [
+    # T, H, F, E, k, zipf
+    (256, 128, 256, 8, 2, 0.0),     # the tiny config
+    (700, 192, 320, 5, 2, 1.2),     # ragged M, F tail (320 = 2.5 x 128)
+    (900, 256, 128, 16, 4, 1.2),    # many experts, some empty
+    (64, 64, 64, 4, 1, 0.0),        # tiles larger than the problem
+]
+
+
+@pytest.mark.parametrize("T,H,F,E,k,zipf", MLP_CASES)
+def test_grouped_mlp_fwd_bf16(m, T, H, F, E, k, zipf):
+    d = _mlp_case(T, H, F, E, k, zipf, seed=1)
+    ref = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], k, keep=True)
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    r = m.moe_grouped_mlp_fwd(p["x_perm"], dev_bf16(d["w_gu"]),
+                              dev_bf16(d["w_dn"]), p["offsets"],
+                              w_perm=p["w_perm"], save=True)
+    y = m.moe_unpermute(r["z"], p["row_map"], k)
+    assert_rows_close(host_f64(r["z"]), ref["z"], TOL_BF16, "z")
+    assert_rows_close(host_f64(r["a"]), ref["a"], TOL_BF16, "a")
+    assert_rows_close(host_f64(r["h1"]), ref["h1"], TOL_BF16, "h1")
+    assert_rows_close(host_f64(y), ref["y"], TOL_BF16, "y")
+
+
+def test_grouped_mlp_one_expert_takes_all(m):
+    T, H, F, E, k = 600, 128, 256, 8, 1
+    shift = np.zeros(E, np.float32)
+    shift[3] = 100.0
+    d = _mlp_case(T, H, F, E, k, 0.0, 2, logits_shift=shift)
+    ref = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], k)
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    assert p["split_sizes"].cpu().numpy()[3] == T
+    r = m.moe_grouped_mlp_fwd(p["x_perm"], dev_bf16(d["w_gu"]),
+                              dev_bf16(d["w_dn"]), p["offsets"],
+                              w_perm=p["w_perm"])
+    y = m.moe_unpermute(r["z"], p["row_map"], k)
+    assert_rows_close(host_f64(y), ref["y"], TOL_BF16, "y")
+
+
+def test_scaled_swiglu_equals_weighted_combine(m):
+    T, H, F, E, k = 300, 128, 128, 8, 2
+    d = _mlp_case(T, H, F, E, k, 0.0, 3)
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
+    ya = m.moe_unpermute(m.moe_grouped_mlp_fwd(
+        p["x_perm"], wgu, wdn, p["offsets"], w_perm=p["w_perm"])["z"],
+        p["row_map"], k)
+    yb = m.moe_unpermute(m.moe_grouped_mlp_fwd(
+        p["x_perm"], wgu, wdn, p["offsets"])["z"], p["row_map"], k, topk_w=w)
+    assert O.rel_err(host_f64(ya), host_f64(yb)) < 1e-2
+
+
+def test_grouped_mlp_deterministic(m):
+    T, H, F, E, k = 500, 256, 256, 16, 4
+    d = _mlp_case(T, H, F, E, k, 1.2, 4)
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
+    z1 = m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
+                               w_perm=p["w_perm"])["z"]
+    z2 = m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
+                               w_perm=p["w_perm"])["z"]
+    assert torch.equal(z1.view(torch.int16), z2.view(torch.int16))
+
+
+def test_grouped_mlp_zero_rows(m):
+    E, H, F = 4, 64, 64
+    x = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    off = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    wgu = torch.zeros((E, 2 * F, H), dtype=torch.bfloat16, device="cuda")
+    wdn = torch.zeros((E, H, F), dtype=torch.bfloat16, device="cuda")
+    r = m.moe_grouped_mlp_fwd(x, wgu, wdn, off)
+    assert r["z"].shape == (0, H)
+
+
+# ------------------------------------------------------ backward, bf16
+BWD_CASES = [
+    (256, 128, 256, 8, 2, 0.0),
+    (700, 192, 320, 5, 2, 1.2),
+    (900, 256, 128, 16, 4, 1.2),
+]
+
+
+@pytest.mark.parametrize("T,H,F,E,k,zipf", BWD_CASES)
+def test_grouped_mlp_bwd_bf16(m, T, H, F, E, k, zipf):
+    d = _mlp_case(T, H, F, E, k, zipf, seed=5)
+    ref = O.layer_bwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], d["dy"], k)
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
+    f = m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
+                              w_perm=p["w_perm"], save=True)
+    dz = m.moe_gather_rows(dev_bf16(d["dy"]), p["row_map"], k)
+    g = m.moe_grouped_mlp_bwd(dz, p["x_perm"], wgu, wdn, p["offsets"],
+                              f["h1"], f["a"], w_perm=p["w_perm"])
+    dx = m.moe_unpermute(g["dx_perm"], p["row_map"], k)
+    dprobs = m.moe_unpermute_probs_grad(g["dw_perm"], p["row_map"], k)
+    assert_rows_close(host_f64(dx), ref["dx"], TOL_BF16, "dx")
+    assert_rows_close(dprobs.cpu().numpy().astype(np.float64).reshape(1, -1),
+                      ref["dprobs"].reshape(1, -1), TOL_BF16, "dprobs")
+    split = ref["split_sizes"]
+    gw_gu, gw_dn = host_f64(g["dw_gu"]), host_f64(g["dw_dn"])
+    for e in range(E):
+        if split[e] == 0:
+            assert np.all(gw_gu[e] == 0) and np.all(gw_dn[e] == 0)
+    assert O.rel_err(gw_gu, ref["dw_gu"]) <= TOL_BF16
+    assert O.rel_err(gw_dn, ref["dw_dn"]) <= TOL_BF16
+    for e in range(E):
+        if split[e] > 0:
+            assert O.rel_err(gw_gu[e], ref["dw_gu"][e]) <= 2 * TOL_BF16, e
+            assert O.rel_err(gw_dn[e], ref["dw_dn"][e]) <= 2 * TOL_BF16, e
