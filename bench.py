@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE expert-MLP hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic tokens, every stage in
+libmoe's HIP kernels through the C ABI:
+  router top-k -> permute (+split_sizes) -> grouped gate/up GEMM with
+  ScaledSwiGLU x routing weight -> grouped down GEMM -> unpermute/combine
+(+ for workloads with a backward pass: gather dY -> grouped MLP backward ->
+combine dX -> routing-weight grads; MXFP8 workloads quantise on the fly).
+
+Inputs are seeded synthetic tensors already resident in HBM; all buffers are
+allocated before the timed region.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload mixtral]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE grouped-MLP TFLOP/s + tokens/s (Mixtral layer, 1 GPU); "
+          "% MFMA peak")
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense (MX)fp8 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral",
+                    help="mixtral | qwen3 | mixtral_mxfp8 | qwen3_long | tiny")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens in the oracle's timed sample (0 = auto)")
+    return ap.parse_args()
+
+
+class Layer:
+    """All device buffers of one layer step, allocated once."""
+
+    def __init__(self, m, cfg, d, dev):
+        import torch
+        self.m, self.cfg, self.dev = m, cfg, dev
+        lib = m.load_library()
+        self.lib = lib
+        T, H, F, E, k = cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
+        rows = T * k
+        self.rows = rows
+
+        def bf(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(
+                torch.bfloat16).to(dev)
+
+        self.x = bf(d["x"])
+        self.logits = torch.from_numpy(d["logits"]).to(dev)
+        self.w_gu = bf(d["w_gu"])
+        self.w_dn = bf(d["w_dn"])
+        self.dy = bf(d["dy"]) if "dy" in d and d["dy"] is not None else None
+        i32, f32, b16, u8 = torch.int32, torch.float32, torch.bfloat16, \
+            torch.uint8
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        self.idx = e((T, k), i32)
+        self.w = e((T, k), f32)
+        self.mx = cfg.mode == "mxfp8"
+        self.x_perm = e((rows, H), b16)
+        self.w_perm = e(rows, f32)
+        self.row_map = e(rows, i32)
+        self.src_row = e(rows, i32)
+        self.split = e(E, i32)
+        self.offsets = e(E + 1, i32)
+        n = ctypes.c_size_t()
+        m._check(lib.moe_permute_workspace_size(T, E, k, ctypes.byref(n)))
+        self.pws = e(max(n.value, 256), u8)
+        self.z = e((rows, H), b16)
+        self.y = e((T, H), b16)
+        self.bwd = cfg.backward
+        save = self.bwd
+        self.h1 = e((rows, 2 * F), b16) if save else None
+        self.a = e((rows, F), b16) if save else None
+        fa = m._FwdArgs()
+        fa.E, fa.H, fa.F, fa.rows = E, H, F, rows
+        fa.precision = m.PREC_MXFP8 if self.mx else m.PREC_BF16
+        fa.x_perm = self.x_perm.data_ptr()
+        fa.x_perm_scale = None
+        fa.w_gu, fa.w_dn = self.w_gu.data_ptr(), self.w_dn.data_ptr()
+        fa.w_perm = self.w_perm.data_ptr()
+        fa.offsets = self.offsets.data_ptr()
+        fa.z_perm = self.z.data_ptr()
+        fa.h1_save = self.h1.data_ptr() if save else None
+        fa.a_save = self.a.data_ptr() if save else None
+        m._check(lib.moe_grouped_mlp_fwd_workspace_size(ctypes.byref(fa),
+                                                        ctypes.byref(n)))
+        self.fws = e(max(n.value, 256), u8)
+        fa.ws, fa.ws_bytes = self.fws.data_ptr(), self.fws.numel()
+        self.fa = fa
+        if self.bwd:
+            self.dz = e((rows, H), b16)
+            self.dx_perm = e((rows, H), b16)
+            self.dw_gu = e((E, 2 * F, H), b16)
+            self.dw_dn = e((E, H, F), b16)
+            self.dw_perm = e(rows, f32)
+            self.dx = e((T, H), b16)
+            self.dprobs = e((T, k), f32)
+            ba = m._BwdArgs()
+            ba.E, ba.H, ba.F, ba.rows = E, H, F, rows
+            ba.precision = fa.precision
+            ba.x_perm, ba.w_gu, ba.w_dn = fa.x_perm, fa.w_gu, fa.w_dn
+            ba.w_perm, ba.offsets = fa.w_perm, fa.offsets
+            ba.h1_save, ba.a_save = fa.h1_save, fa.a_save
+            ba.dz_perm, ba.dx_perm = self.dz.data_ptr(), \
+                self.dx_perm.data_ptr()
+            ba.dw_gu, ba.dw_dn = self.dw_gu.data_ptr(), self.dw_dn.data_ptr()
+            ba.dw_perm = self.dw_perm.data_ptr()
+            m._check(lib.moe_grouped_mlp_bwd_workspace_size(ctypes.byref(ba),
+                                                            ctypes.byref(n)))
+            self.bws = e(max(n.value, 256), u8)
+            ba.ws, ba.ws_bytes = self.bws.data_ptr(), self.bws.numel()
+            self.ba = ba
+        self.ctx = m._context(torch.device(dev))
+
+    # the stages of one step, in order
+    def stages(self):
+        c, L, m = self.cfg, self.lib, self.m
+        T, H, E, k = c.T, c.H, c.E, c.k
+        P = lambda t: t.data_ptr()
+
+        def route(st):
+            m._check(L.moe_route_topk(self.ctx, P(self.logits), T, E, k, 1,
+                                      P(self.idx), P(self.w), st))
+
+        def permute(st):
+            m._check(L.moe_permute(
+                self.ctx, P(self.x), P(self.idx), P(self.w), T, H, E, k,
+                m.PREC_BF16, P(self.x_perm), None, P(self.w_perm),
+                P(self.row_map), P(self.src_row), P(self.split),
+                P(self.offsets), P(self.pws), self.pws.numel(), st))
+
+        def mlp(st):
+            m._check(L.moe_grouped_mlp_fwd(self.ctx, ctypes.byref(self.fa),
+                                           st))
+
+        def unpermute(st):
+            m._check(L.moe_unpermute(self.ctx, P(self.z), P(self.row_map),
+                                     None, T, H, k, P(self.y), st))
+
+        out = [("route_topk", route), ("permute", permute),
+               ("grouped_mlp_fwd", mlp), ("unpermute", unpermute)]
+        if self.bwd:
+            def gather(st):
+                m._check(L.moe_gather_rows(self.ctx, P(self.dy),
+                                           P(self.row_map), T, H, k,
+                                           P(self.dz), st))
+
+            def mlp_bwd(st):
+                m._check(L.moe_grouped_mlp_bwd(self.ctx, ctypes.byref(self.ba),
+                                               st))
+
+            def combine_dx(st):
+                m._check(L.moe_unpermute(self.ctx, P(self.dx_perm),
+                                         P(self.row_map), None, T, H, k,
+                                         P(self.dx), st))
+
+            def probs(st):
+                m._check(L.moe_unpermute_probs_grad(
+                    self.ctx, P(self.dw_perm), P(self.row_map), T, k,
+                    P(self.dprobs), st))
+
+            out += [("gather_dy", gather), ("grouped_mlp_bwd", mlp_bwd),
+                    ("unpermute_dx", combine_dx), ("probs_grad", probs)]
+        return out
+
+
+def algorithmic(cfg):
+    """Algorithmic work per op (flop or bytes, per launch of that op)."""
+    T, H, F, k = cfg.T, cfg.H, cfg.F, cfg.k
+    rows = T * k
+    w = {
+        "grouped_mlp_fwd": ("flop", 6.0 * rows * H * F),
+        "grouped_mlp_bwd": ("flop", 12.0 * rows * H * F),
+        # permute: read x once, write k rows (+ 4-byte index/weight traffic)
+        "permute": ("bytes", (1 + k) * T * H * 2.0 + rows * 16.0),
+        "unpermute": ("bytes", (k + 1) * T * H * 2.0 + rows * 4.0),
+        "gather_dy": ("bytes", (1 + k) * T * H * 2.0 + rows * 4.0),
+        "unpermute_dx": ("bytes", (k + 1) * T * H * 2.0 + rows * 4.0),
+    }
+    return w
+
+
+def cpu_baseline(cfg, d, n_tokens):
+    """The oracle as it stands, timed on the host on the first n_tokens of
+    the same workload (full layer: route, permute, per-expert MLP in float64,
+    combine)."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] +
+                      [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x = d["x"][:n_tokens]
+    lg = d["logits"][:n_tokens]
+    t0 = time.perf_counter()
+    if cfg.backward:
+        O.layer_bwd(x, lg, d["w_gu"], d["w_dn"], d["dy"][:n_tokens], cfg.k)
+    else:
+        O.layer_fwd(x, lg, d["w_gu"], d["w_dn"], cfg.k)
+    dt = time.perf_counter() - t0
+    flop = (6.0 + (12.0 if cfg.backward else 0.0)) * n_tokens * cfg.k * \
+        cfg.H * cfg.F
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"first {n_tokens} of {cfg.T} tokens of the "
+                       f"{cfg.name} workload, whole layer "
+                       f"{'fwd+bwd' if cfg.backward else 'fwd'} in float64 "
+                       f"numpy ({dt:.1f} s wall)"),
+            "tokens_per_s": n_tokens / dt, "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding of this path is a design note, not a "
+              "runnable configuration.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mixture_experts_grouped_router_amd as m
+    from synthetic import CONFIGS, generate_config
+
+    cfg = CONFIGS[args.workload]
+    m.load_library()
+    t0 = time.time()
+    d = generate_config(cfg, seed=0)
+    gen_s = time.time() - t0
+    print(f"[bench] inputs for {cfg.name} generated in {gen_s:.1f} s",
+          file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layer = Layer(m, cfg, d, dev)
+    stages = layer.stages()
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        for _, fn in stages:
+            fn(st)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in stages]
+          for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for s in range(K):
+        for i, (_, fn) in enumerate(stages):
+            ev[s][i][0].record(stream)
+            fn(st)
+            ev[s][i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / K
+    per_stage = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1])
+                                      for s in range(K)]))
+                 for i, (name, _) in enumerate(stages)}
+    status = m.check_device_status()
+    if status != 0:
+        raise RuntimeError(f"device status {status}")
+
+    flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
+    tflops = flop / (ms_step * 1e-3) / 1e12
+    tokens_s = cfg.T / (ms_step * 1e-3)
+    work = algorithmic(cfg)
+    peak = PEAK_FP8_TFLOPS if cfg.mode == "mxfp8" else PEAK_BF16_TFLOPS
+    dom = "grouped_mlp_fwd"
+    dom_ms = per_stage[dom]
+    ach = work[dom][1] / (dom_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": "moe_grouped_mlp_fwd (grouped gate/up "
+            "GEMM + ScaledSwiGLU epilogue, grouped down GEMM)",
+            "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4), "traffic": None,
+            "avg_launch_ms": round(dom_ms, 4),
+            "work_per_launch": f"6*T*k*H*F = {work[dom][1]:.4e} flop"}
+    stage_rates = {}
+    for name, ms in per_stage.items():
+        if name in work:
+            kind, amt = work[name]
+            if kind == "bytes":
+                stage_rates[name] = {"ms": round(ms, 4), "GB/s": round(
+                    amt / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(
+                    amt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            else:
+                stage_rates[name] = {"ms": round(ms, 4), "TFLOP/s": round(
+                    amt / (ms * 1e-3) / 1e12, 1), "frac_mfma": round(
+                    amt / (ms * 1e-3) / 1e12 / peak, 4)}
+        else:
+            stage_rates[name] = {"ms": round(ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_tokens
+        if n_tok <= 0:
+            # about 10-30 s of host work for the oracle (float64 BLAS on
+            # 16 host threads runs the per-expert matmuls at ~0.1 TFLOP/s)
+            per_tok = (18.0 if cfg.backward else 6.0) * cfg.k * cfg.H * cfg.F
+            n_tok = max(16, min(cfg.T, int(1.5e12 / per_tok)))
+        cpu = cpu_baseline(cfg, d, n_tok)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-e4m3" if cfg.mode == "mxfp8" else "bf16",
+        "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": f"{cfg.name}: {cfg.description}",
+                   "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E,
+                   "k": cfg.k, "mode": cfg.mode,
+                   "passes": "fwd+bwd" if cfg.backward else "fwd",
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(tokens_s, 1),
+        "mfma_frac_step": round(tflops / peak, 4),
+        "roofline": roof,
+        "stages": stage_rates,
+        "wall_s_timed": round(wall, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -354,10 +354,9 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
   MOE_REQUIRE(a != nullptr, MOE_ERR_INVALID_ARG, "null args");
   s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
   if (s != MOE_OK) return s;
-  MOE_REQUIRE(a->offsets && a->z_perm, MOE_ERR_INVALID_ARG,
-              "null offsets / z_perm");
-  MOE_REQUIRE(a->x_perm != nullptr || a->rows == 0, MOE_ERR_INVALID_ARG,
-              "null x_perm");
+  MOE_REQUIRE(a->offsets != nullptr, MOE_ERR_INVALID_ARG, "null offsets");
+  MOE_REQUIRE((a->x_perm && a->z_perm) || a->rows == 0, MOE_ERR_INVALID_ARG,
+              "null x_perm / z_perm");
   const bool mx = a->precision == MOE_PREC_MXFP8_E4M3;
   if (!mx || a->w_gu_q == nullptr || a->w_dn_q == nullptr)
     MOE_REQUIRE(a->w_gu && a->w_dn, MOE_ERR_INVALID_ARG, "null weights");
