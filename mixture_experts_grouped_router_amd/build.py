@@ -24,7 +24,11 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are switched off for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # GEMM epilogues walk all 256 accumulators of a lane with
+                # fully unrolled loops; a partial unroll would index the
+                # accumulator array dynamically and move it to scratch
+                "-mllvm", "-pragma-unroll-threshold=1000000"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
           "-Wno-unused-result", "-Wno-unused-command-line-argument",

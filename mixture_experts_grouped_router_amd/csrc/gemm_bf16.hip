@@ -7,20 +7,25 @@
 // experts instead of a Python loop"; "Efficient MoE training for biological
 // foundation models (NVIDIA)", section "1) Fragmented expert kernels").
 // The gate/up GEMM carries ScaledSwiGLU times the routing weight in its
-// epilogue, so the intermediate h1 never has to go through HBM ("NVIDIA
-// presents ...", section "Reducing memory and quantisation cost";
-// "Efficient MoE training ...", section "3) Quantisation overhead in
-// low-precision training").
+// epilogue, so the gate/up product never goes through HBM ("NVIDIA presents
+// ...", section "Reducing memory and quantisation cost"; "Efficient MoE
+// training ...", section "3) Quantisation overhead in low-precision
+// training").
 //
-// Kernel shape: 256 x 256 output tile, K step 64, 512 threads = 8 waves in a
-// 2 (M) x 4 (N) grid, each wave 128 x 64 = 4 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16 with float32 accumulators.  Operands are staged
-// through LDS (two buffers, one barrier per K step) in a [mn][k] layout with
-// an XOR swizzle on 16-byte chunks; operands whose memory layout is
-// MN-contiguous (backward) are transposed in registers on the way in.
-// Tiles are ordered so that each XCD (blocks b = x mod 8) works on one
-// contiguous run of tiles: consecutive tiles share an expert's weight panel
-// and activation rows in that XCD's L2.
+// Kernel shape: 256 x 256 output tile, K step 64, 256 threads = 4 waves in a
+// 2 (M) x 2 (N) grid; each wave owns 128 x 128 = 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 (256 float32 accumulators per lane, which the
+// compiler keeps in AGPRs).  Operand tiles sit in LDS as [mn][k] rows of
+// 128 bytes with an XOR swizzle on the eight 16-byte chunks of a row; two
+// stages, one barrier per K step.
+//  * K-contiguous operands go global -> LDS directly (global_load_lds_dwordx4:
+//    each wave instruction fills one contiguous KiB of LDS, so every lane
+//    picks the global chunk that belongs at its LDS slot).
+//  * MN-contiguous operands (backward) go through registers and are
+//    transposed 8 x 8 on the way into LDS.
+// Tiles are ordered so that each XCD (blocks b = x mod 8) works through one
+// contiguous run of tiles, M fastest inside groups of 4 N tiles: the tiles in
+// flight on one XCD share activation rows and weight panels in its L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,9 +34,10 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+#define MOE_LDS __attribute__((address_space(3)))
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kTileBytes = BM * BK * 2;     // 32 KiB per operand tile
 constexpr int kGroupN = 4;                  // N tiles per scheduling group
 constexpr int kXcds = 8;
@@ -49,7 +55,7 @@ struct Params {
   int F;                  // EPI_SWIGLU / EPI_SWIGLU_BWD: expert FFN size
   int E;
   const int32_t* offsets;     // [E+1] rows per expert
-  const int32_t* tile_start;  // RAGGED_M: [E+1] tile prefix; [E+1]: total
+  const int32_t* tile_start;  // RAGGED_M: [E+1] tile prefix
   int tiles_n;                // tiles along N
   int tiles_m;                // RAGGED_K: tiles along M
   uint16_t* c;                // main output
@@ -61,34 +67,17 @@ struct Params {
   int64_t rows;
 };
 
-// byte offset of 16-byte chunk c (0..7) of LDS tile row r: XOR swizzle that
-// keeps 8 consecutive rows at one chunk (MFMA fragment reads) and rows
-// 8 apart at one chunk (transposed writes) on distinct bank groups.
+// Swizzle of the 16-byte chunk c of LDS tile row r.  Eight consecutive rows
+// (one MFMA fragment read per 8 lanes) and eight rows 8 apart (one transposed
+// register write per 8 lanes) both land on eight distinct chunk positions.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int c) {
-  return r * (BK * 2) + (((c ^ r ^ (r >> 3)) & 7) << 4);
-}
-
-// Register transpose of a 4 (k) x 8 (mn) block of bf16: in[i] holds row k=i
-// (8 values); out[j] gets the 4 k-values of column j packed as 2 dwords.
-__device__ __forceinline__ void transpose4x8(const uint4 in[4], uint2 out[8]) {
-  const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&in[0]);
-  const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&in[1]);
-  const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&in[2]);
-  const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&in[3]);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    // column 2d takes the low halves, column 2d+1 the high halves
-    out[2 * d].x = __builtin_amdgcn_perm(r1[d], r0[d], 0x05040100u);
-    out[2 * d].y = __builtin_amdgcn_perm(r3[d], r2[d], 0x05040100u);
-    out[2 * d + 1].x = __builtin_amdgcn_perm(r1[d], r0[d], 0x07060302u);
-    out[2 * d + 1].y = __builtin_amdgcn_perm(r3[d], r2[d], 0x07060302u);
-  }
+  return r * (BK * 2) + ((c ^ swz(r)) << 4);
 }
 
 struct TileCoord {
   int e;        // expert
   int m0;       // first row of the tile inside the expert's M range
-  int n0;       // first column (output units; f units for EPI_SWIGLU)
   int seg0;     // offsets[e]
   int seg_len;  // rows of expert e
   int nt;       // N tile index
@@ -98,7 +87,7 @@ template <int G>
 __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
   const int b = blockIdx.x;
   int total;
-  if (G == RAGGED_M) total = p.tile_start[p.E];
+  if constexpr (G == RAGGED_M) total = p.tile_start[p.E];
   else total = p.E * p.tiles_m * p.tiles_n;
   const int per = (total + kXcds - 1) / kXcds;
   const int idx = b / kXcds;
@@ -106,9 +95,10 @@ __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
   const int L = (b % kXcds) * per + idx;
   if (L >= total) return false;
   int e, local, mt_e;
-  if (G == RAGGED_M) {
-    // binary search: tile_start[e] <= L < tile_start[e+1]
-    int lo = 0, hi = p.E;  // invariant: tile_start[lo] <= L < tile_start[hi]
+  if constexpr (G == RAGGED_M) {
+    // tile_start[e] <= L < tile_start[e+1]; experts without tiles have
+    // tile_start[e] == tile_start[e+1] and are never selected
+    int lo = 0, hi = p.E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (p.tile_start[mid] <= L) lo = mid; else hi = mid;
@@ -126,66 +116,93 @@ __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
   // groups of kGroupN N-tiles, M tiles fastest inside a group
   const int ng = local / (mt_e * kGroupN);
   const int in_g = local - ng * mt_e * kGroupN;
-  const int gsz = min(kGroupN, p.tiles_n - ng * kGroupN);
-  const int mt = in_g % mt_e;
-  const int nt = ng * kGroupN + in_g / mt_e;
-  (void)gsz;
   tc.e = e;
-  tc.m0 = mt * BM;
-  tc.nt = nt;
+  tc.m0 = (in_g % mt_e) * BM;
+  tc.nt = ng * kGroupN + in_g / mt_e;
   tc.seg0 = p.offsets[e];
   tc.seg_len = p.offsets[e + 1] - tc.seg0;
   return true;
 }
 
-// ---- operand staging ------------------------------------------------------
-// K-contiguous operand: tile rows r = 0..255, 8 chunks of 16 B per row.
-// Thread t loads chunk (t & 7) of rows (t >> 3) + 64 i, i = 0..3.
-struct KcLoader {
-  const uint16_t* ptr[4];
-  __device__ __forceinline__ void load(uint4 (&v)[4], int k0) const {
+// ---- K-contiguous operand: direct global -> LDS ----------------------------
+// Wave w, instruction j fills KiB q = 4 j + w of the tile = tile rows
+// 8q .. 8q+7; lane i lands at row 8q + i/8, chunk slot i%8, which holds the
+// logical chunk (i%8) ^ swz(row).
+struct KcDirect {
+  const uint16_t* g[8];  // per instruction: global address at k = 0
+  __device__ __forceinline__ void issue(char* lds_tile, int k0,
+                                        int wave) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[i] = *reinterpret_cast<const uint4*>(ptr[i] + k0);
-  }
-  __device__ __forceinline__ static void store(char* lds, const uint4 (&v)[4]) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (t >> 3) + 64 * i;
-      *reinterpret_cast<uint4*>(lds + lds_off(r, t & 7)) = v[i];
+    for (int j = 0; j < 8; ++j) {
+      MOE_LDS void* dst =
+          (MOE_LDS void*)(lds_tile + (4 * j + wave) * 1024);
+      __builtin_amdgcn_global_load_lds((const void*)(g[j] + k0), dst, 16, 0,
+                                       0);
     }
   }
 };
 
-// MN-contiguous operand ([k][mn] in memory): thread t covers mn chunk
-// (t & 31) (8 values) for k rows 4 (t >> 5) .. +3; transposed in registers.
-struct McLoader {
-  const uint16_t* base;   // element (mn = 0, k = 0)
+// ---- MN-contiguous operand through registers --------------------------------
+// Thread t covers mn chunk (t & 31) (8 values) for k rows 8 (t >> 5) .. +7;
+// the 8 x 8 block is transposed in registers and written as 8 row chunks.
+struct McStaged {
+  const uint16_t* base;   // element (mn = this thread's chunk, k = 0)
   int64_t ld;             // elements between consecutive k rows
-  int kvalid;             // k rows < kvalid are real (rest read as zero)
-  __device__ __forceinline__ void load(uint4 (&v)[4], int k0) const {
-    const int t = threadIdx.x;
-    const int kr = k0 + 4 * (t >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kr + i < kvalid)
-        v[i] = *reinterpret_cast<const uint4*>(base + (int64_t)(kr + i) * ld);
-      else
-        v[i] = make_uint4(0, 0, 0, 0);
-    }
+  int kvalid;             // k rows >= kvalid read as zero
+  int kr;                 // first k row of the staged block
+  uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+
+  // Rows past kvalid load the last valid row; store() zeroes them, so the
+  // loads stay in flight until the LDS store (callers never load with
+  // kvalid == 0).
+  __device__ __forceinline__ uint4 row(int k) const {
+    const int kc = min(k, kvalid - 1);
+    return *reinterpret_cast<const uint4*>(base + (int64_t)kc * ld);
   }
-  __device__ __forceinline__ static void store(char* lds, const uint4 (&v)[4]) {
-    const int t = threadIdx.x;
-    uint2 o[8];
-    transpose4x8(v, o);
-    const int kg = t >> 5;            // k group of 4 (0..15)
-    const int mn0 = (t & 31) * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = mn0 + j;
-      *reinterpret_cast<uint2*>(lds + lds_off(r, kg >> 1) + (kg & 1) * 8) = o[j];
-    }
+  __device__ __forceinline__ void load(int k0) {
+    kr = k0 + 8 * (threadIdx.x >> 5);
+    v0 = row(kr + 0); v1 = row(kr + 1); v2 = row(kr + 2); v3 = row(kr + 3);
+    v4 = row(kr + 4); v5 = row(kr + 5); v6 = row(kr + 6); v7 = row(kr + 7);
+  }
+  static __device__ __forceinline__ uint4 keep(uint4 v, bool ok) {
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u,
+                      ok ? v.w : 0u);
+  }
+  // lo: halves 0 of the two inputs (k even, k odd); hi: halves 1
+  static __device__ __forceinline__ uint32_t plo(uint32_t ke, uint32_t ko) {
+    return __builtin_amdgcn_perm(ko, ke, 0x05040100u);
+  }
+  static __device__ __forceinline__ uint32_t phi(uint32_t ke, uint32_t ko) {
+    return __builtin_amdgcn_perm(ko, ke, 0x07060302u);
+  }
+  static __device__ __forceinline__ void put(char* lds, int r, int c,
+                                             uint4 val) {
+    *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = val;
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int kg = threadIdx.x >> 5;          // k chunk 0..7
+    const int r0 = (threadIdx.x & 31) * 8;    // first mn row
+    const uint4 w0 = keep(v0, kr + 0 < kvalid), w1 = keep(v1, kr + 1 < kvalid);
+    const uint4 w2 = keep(v2, kr + 2 < kvalid), w3 = keep(v3, kr + 3 < kvalid);
+    const uint4 w4 = keep(v4, kr + 4 < kvalid), w5 = keep(v5, kr + 5 < kvalid);
+    const uint4 w6 = keep(v6, kr + 6 < kvalid), w7 = keep(v7, kr + 7 < kvalid);
+    // column pair d of the inputs holds mn 2d (low half) and 2d+1 (high)
+    put(lds, r0 + 0, kg, make_uint4(plo(w0.x, w1.x), plo(w2.x, w3.x),
+                                    plo(w4.x, w5.x), plo(w6.x, w7.x)));
+    put(lds, r0 + 1, kg, make_uint4(phi(w0.x, w1.x), phi(w2.x, w3.x),
+                                    phi(w4.x, w5.x), phi(w6.x, w7.x)));
+    put(lds, r0 + 2, kg, make_uint4(plo(w0.y, w1.y), plo(w2.y, w3.y),
+                                    plo(w4.y, w5.y), plo(w6.y, w7.y)));
+    put(lds, r0 + 3, kg, make_uint4(phi(w0.y, w1.y), phi(w2.y, w3.y),
+                                    phi(w4.y, w5.y), phi(w6.y, w7.y)));
+    put(lds, r0 + 4, kg, make_uint4(plo(w0.z, w1.z), plo(w2.z, w3.z),
+                                    plo(w4.z, w5.z), plo(w6.z, w7.z)));
+    put(lds, r0 + 5, kg, make_uint4(phi(w0.z, w1.z), phi(w2.z, w3.z),
+                                    phi(w4.z, w5.z), phi(w6.z, w7.z)));
+    put(lds, r0 + 6, kg, make_uint4(plo(w0.w, w1.w), plo(w2.w, w3.w),
+                                    plo(w4.w, w5.w), plo(w6.w, w7.w)));
+    put(lds, r0 + 7, kg, make_uint4(phi(w0.w, w1.w), phi(w2.w, w3.w),
+                                    phi(w4.w, w5.w), phi(w6.w, w7.w)));
   }
 };
 
@@ -193,169 +210,244 @@ __device__ __forceinline__ float fast_sigmoid(float x) {
   return 1.0f / (1.0f + __expf(-x));
 }
 
+// Zero one operand stage (a padding K step past the end of K).
+__device__ __forceinline__ void zero_tile(char* lds) {
+#pragma unroll
+  for (int i = 0; i < kTileBytes / (16 * kThreads); ++i)
+    *reinterpret_cast<uint4*>(lds + (i * kThreads + threadIdx.x) * 16) =
+        make_uint4(0, 0, 0, 0);
+}
+
+// MFMA operand fragments of one 16-wide K slice of the wave's 128 x 128
+// block: lane l holds row l%32 (of each 32-row block), k 8 (l/32) .. +7.
+struct Frags {
+  bf16x8_t a0, a1, a2, a3, b0, b1, b2, b3;
+};
+
+__device__ __forceinline__ bf16x8_t frag_at(const char* s, int r, int ch) {
+  return *reinterpret_cast<const bf16x8_t*>(s + lds_off(r, ch));
+}
+
+__device__ __forceinline__ void load_frags(const char* sa, const char* sb,
+                                           int kk, int wm, int wn, int lane,
+                                           Frags& f) {
+  const int frow = lane & 31;
+  const int ch = kk * 2 + (lane >> 5);
+  f.a0 = frag_at(sa, wm * 128 + 0 * 32 + frow, ch);
+  f.a1 = frag_at(sa, wm * 128 + 1 * 32 + frow, ch);
+  f.a2 = frag_at(sa, wm * 128 + 2 * 32 + frow, ch);
+  f.a3 = frag_at(sa, wm * 128 + 3 * 32 + frow, ch);
+  f.b0 = frag_at(sb, wn * 128 + 0 * 32 + frow, ch);
+  f.b1 = frag_at(sb, wn * 128 + 1 * 32 + frow, ch);
+  f.b2 = frag_at(sb, wn * 128 + 2 * 32 + frow, ch);
+  f.b3 = frag_at(sb, wn * 128 + 3 * 32 + frow, ch);
+}
+
+#define MOE_MFMA(i, j, A, B) \
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[i][j], 0, 0, 0)
+
+__device__ __forceinline__ void mfma_frags(const Frags& f,
+                                           f32x16_t (&acc)[4][4]) {
+  MOE_MFMA(0, 0, f.a0, f.b0); MOE_MFMA(0, 1, f.a0, f.b1);
+  MOE_MFMA(0, 2, f.a0, f.b2); MOE_MFMA(0, 3, f.a0, f.b3);
+  MOE_MFMA(1, 0, f.a1, f.b0); MOE_MFMA(1, 1, f.a1, f.b1);
+  MOE_MFMA(1, 2, f.a1, f.b2); MOE_MFMA(1, 3, f.a1, f.b3);
+  MOE_MFMA(2, 0, f.a2, f.b0); MOE_MFMA(2, 1, f.a2, f.b1);
+  MOE_MFMA(2, 2, f.a2, f.b2); MOE_MFMA(2, 3, f.a2, f.b3);
+  MOE_MFMA(3, 0, f.a3, f.b0); MOE_MFMA(3, 1, f.a3, f.b1);
+  MOE_MFMA(3, 2, f.a3, f.b2); MOE_MFMA(3, 3, f.a3, f.b3);
+}
+#undef MOE_MFMA
+
 template <int LA, int LB, int G, int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sA0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sB0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sA1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sB1[kTileBytes];
   TileCoord tc;
   if (!decode_tile<G>(p, tc)) return;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave >> 2;   // 0..1
-  const int wn = wave & 3;    // 0..3
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1;   // 0..1
+  const int wn = wave & 1;    // 0..1
 
   // ---- tile geometry ----
   int kdim, n0;
-  if (G == RAGGED_M) kdim = p.K;
+  if constexpr (G == RAGGED_M) kdim = p.K;
   else kdim = tc.seg_len;
-  if (EPI == EPI_SWIGLU) n0 = tc.nt * (BN / 2);   // f units
+  if constexpr (EPI == EPI_SWIGLU) n0 = tc.nt * (BN / 2);   // f units
   else n0 = tc.nt * BN;
 
-  // ---- loaders ----
-  KcLoader la_kc, lb_kc;
-  McLoader la_mc, lb_mc;
-  if (LA == KC) {
-    // RAGGED_M: rows seg0 + m0 + r, clamped to the expert's last row
+  // ---- operand sources ----
+  KcDirect da, db;
+  McStaged ma, mb;
+  if constexpr (LA == KC) {
+    // RAGGED_M rows seg0 + m0 + r, clamped to the expert's last row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int r = tc.m0 + (t >> 3) + 64 * i;
-      r = min(r, tc.seg_len - 1);
-      la_kc.ptr[i] = p.a + (int64_t)(tc.seg0 + r) * p.lda + (t & 7) * 8;
+    for (int j = 0; j < 8; ++j) {
+      const int rr = 8 * (4 * j + wave) + (lane >> 3);
+      const int c = (lane & 7) ^ swz(rr);
+      const int r = min(tc.m0 + rr, tc.seg_len - 1);
+      da.g[j] = p.a + (int64_t)(tc.seg0 + r) * p.lda + c * 8;
     }
   } else {
-    // RAGGED_K: A element (m, k) at a[(seg0 + k) * lda + m]
-    int mc = tc.m0 + (t & 31) * 8;
-    mc = min(mc, p.M - 8);
-    la_mc.base = p.a + (int64_t)tc.seg0 * p.lda + mc;
-    la_mc.ld = p.lda;
-    la_mc.kvalid = kdim;
+    // A element (m, k) at a[(seg0 + k) * lda + m] (RAGGED_K: k = token)
+    const int mc = min(tc.m0 + (t & 31) * 8, p.M - 8);
+    ma.base = p.a + (int64_t)tc.seg0 * p.lda + mc;
+    ma.ld = p.lda;
+    ma.kvalid = kdim;
   }
   const uint16_t* bexp = p.b + (int64_t)tc.e * p.b_es;
-  if (LB == KC) {
+  if constexpr (LB == KC) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = (t >> 3) + 64 * i;
+    for (int j = 0; j < 8; ++j) {
+      const int rr = 8 * (4 * j + wave) + (lane >> 3);
+      const int c = (lane & 7) ^ swz(rr);
       int brow;
-      if (EPI == EPI_SWIGLU) {
+      if constexpr (EPI == EPI_SWIGLU) {
         // 32-row blocks alternate gate / up for the same 32 f columns
         const int blk = rr >> 5;
-        int f = n0 + (blk >> 1) * 32 + (rr & 31);
-        f = min(f, p.F - 1);
+        const int f = min(n0 + (blk >> 1) * 32 + (rr & 31), p.F - 1);
         brow = (blk & 1) ? p.F + f : f;
       } else {
         brow = min(n0 + rr, p.N - 1);
       }
-      lb_kc.ptr[i] = bexp + (int64_t)brow * p.ldb + (t & 7) * 8;
+      db.g[j] = bexp + (int64_t)brow * p.ldb + c * 8;
     }
   } else {
-    int nc = n0 + (t & 31) * 8;
-    nc = min(nc, p.N - 8);
-    if (G == RAGGED_M) {
-      lb_mc.base = bexp + nc;     // B element (n, k) at b_e[k * ldb + n]
-      lb_mc.kvalid = kdim;
-    } else {
-      lb_mc.base = p.b + (int64_t)tc.seg0 * p.ldb + nc;
-      lb_mc.kvalid = kdim;
-    }
-    lb_mc.ld = p.ldb;
+    const int nc = min(n0 + (t & 31) * 8, p.N - 8);
+    if constexpr (G == RAGGED_M) mb.base = bexp + nc;  // b_e[k * ldb + n]
+    else mb.base = p.b + (int64_t)tc.seg0 * p.ldb + nc;
+    mb.ld = p.ldb;
+    mb.kvalid = kdim;
   }
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
   const int nk = (kdim + BK - 1) / BK;
-  uint4 va[4], vb[4];
-  auto gload = [&](int kt) {
-    if (LA == KC) la_kc.load(va, kt * BK); else la_mc.load(va, kt * BK);
-    if (LB == KC) lb_kc.load(vb, kt * BK); else lb_mc.load(vb, kt * BK);
-  };
-  auto sstore = [&](int buf) {
-    char* sa = smem + buf * 2 * kTileBytes;
-    char* sb = sa + kTileBytes;
-    if (LA == KC) KcLoader::store(sa, va); else McLoader::store(sa, va);
-    if (LB == KC) KcLoader::store(sb, vb); else McLoader::store(sb, vb);
-  };
-
+  // Two K steps per loop trip, one per LDS stage, so each stage is a
+  // distinct LDS object: the compiler then knows that direct loads into one
+  // stage never alias fragment reads of the other and waits for them only
+  // at the barrier.  An odd last step computes on a zero-filled stage.
+  // Fragment reads run one 16-wide K slice ahead of the MFMAs; the barrier
+  // that publishes the next stage sits before the last slice's MFMAs so the
+  // first reads of the next stage overlap them.
+  const int nk2 = (nk + 1) & ~1;
   if (nk > 0) {
-    gload(0);
-    sstore(0);
+    if constexpr (LA == KC) da.issue(sA0, 0, wave); else ma.load(0);
+    if constexpr (LB == KC) db.issue(sB0, 0, wave); else mb.load(0);
+    if constexpr (LA == MC) ma.store(sA0);
+    if constexpr (LB == MC) mb.store(sB0);
   }
   __syncthreads();
+  Frags cur, nxt;
+  load_frags(sA0, sB0, 0, wm, wn, lane, cur);
 
-  const int frow = lane & 31;
-  const int fk = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const char* sa = smem + buf * 2 * kTileBytes;
-    const char* sb = sa + kTileBytes;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t fa[4], fb[2];
-      const int ch = kk * 2 + fk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(
-            sa + lds_off(wm * 128 + i * 32 + frow, ch));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8_t*>(
-            sb + lds_off(wn * 64 + j * 32 + frow, ch));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j],
-                                                              acc[i][j], 0, 0, 0);
+  for (int kt = 0; kt < nk2; kt += 2) {
+    // stage kt from buffers 0 while stage kt+1 loads into buffers 1
+    const bool real1 = kt + 1 < nk;
+    if (real1) {
+      if constexpr (LA == KC) da.issue(sA1, (kt + 1) * BK, wave);
+      else ma.load((kt + 1) * BK);
+      if constexpr (LB == KC) db.issue(sB1, (kt + 1) * BK, wave);
+      else mb.load((kt + 1) * BK);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+      load_frags(sA0, sB0, kk + 1, wm, wn, lane, nxt);
+      mfma_frags(cur, acc);
+      cur = nxt;
+    }
+    if (real1) {
+      if constexpr (LA == MC) ma.store(sA1);
+      if constexpr (LB == MC) mb.store(sB1);
+    } else {
+      zero_tile(sA1);
+      zero_tile(sB1);
+    }
     __syncthreads();
+    load_frags(sA1, sB1, 0, wm, wn, lane, nxt);
+    mfma_frags(cur, acc);
+    cur = nxt;
+
+    // stage kt+1 from buffers 1 while stage kt+2 loads into buffers 0
+    const bool real2 = kt + 2 < nk;
+    if (real2) {
+      if constexpr (LA == KC) da.issue(sA0, (kt + 2) * BK, wave);
+      else ma.load((kt + 2) * BK);
+      if constexpr (LB == KC) db.issue(sB0, (kt + 2) * BK, wave);
+      else mb.load((kt + 2) * BK);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+      load_frags(sA1, sB1, kk + 1, wm, wn, lane, nxt);
+      mfma_frags(cur, acc);
+      cur = nxt;
+    }
+    if (real2) {
+      if constexpr (LA == MC) ma.store(sA0);
+      if constexpr (LB == MC) mb.store(sB0);
+    }
+    __syncthreads();
+    if (real2) load_frags(sA0, sB0, 0, wm, wn, lane, nxt);
+    mfma_frags(cur, acc);
+    cur = nxt;
   }
 
   // ---- epilogue ----
-  // acc[i][j][r] is C[row][col] with
-  //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  col = lane%32 (+ j*32)
+  // acc[i][j][r] is C[row][col] of the wave's block with
+  //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
+  //   col = wn*128 + j*32 + lane%32
   const int colw = lane & 31;
   const int rsub = (lane >> 5) * 4;
-  if (EPI == EPI_SWIGLU) {
-    const int f = n0 + wn * 32 + colw;
-    const bool fok = f < p.F;
+  if constexpr (EPI == EPI_SWIGLU) {
+    // B rows of block j: gate f-block (2 wn + j/2) for even j, up for odd j
+    const int64_t ld1 = 2 * (int64_t)p.F;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int jj = 0; jj < 2; ++jj) {
+      const int f = n0 + (2 * wn + jj) * 32 + colw;
+      if (f >= p.F) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int mrow = tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-        if (mrow < tc.seg_len && fok) {
-          const int64_t row = tc.seg0 + mrow;
-          const float g = acc[i][0][r], u = acc[i][1][r];
-          const float wr = p.w ? p.w[row] : 1.0f;
-          const float a = wr * (g * fast_sigmoid(g)) * u;
-          p.c[row * p.ldc + f] = (uint16_t)f32_to_bf16(a);
-          if (p.c2) {
-            p.c2[row * (2 * (int64_t)p.F) + f] = (uint16_t)f32_to_bf16(g);
-            p.c2[row * (2 * (int64_t)p.F) + p.F + f] = (uint16_t)f32_to_bf16(u);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mrow =
+              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          if (mrow < tc.seg_len) {
+            const int64_t row = tc.seg0 + mrow;
+            const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+            const float wr = p.w ? p.w[row] : 1.0f;
+            const float a = wr * (g * fast_sigmoid(g)) * u;
+            p.c[row * p.ldc + f] = (uint16_t)f32_to_bf16(a);
+            if (p.c2) {
+              p.c2[row * ld1 + f] = (uint16_t)f32_to_bf16(g);
+              p.c2[row * ld1 + p.F + f] = (uint16_t)f32_to_bf16(u);
+            }
           }
         }
-      }
-  } else if (EPI == EPI_STORE) {
-    uint16_t* cbase = p.c + (G == RAGGED_K ? (int64_t)tc.e * p.c_es : 0);
+    }
+  } else if constexpr (EPI == EPI_STORE) {
+    uint16_t* cbase = p.c;
+    if constexpr (G == RAGGED_K) cbase += (int64_t)tc.e * p.c_es;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + colw;
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + colw;
       if (col >= p.N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int mrow = tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          const int mrow =
+              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
           int64_t row;
-          if (G == RAGGED_M) {
+          if constexpr (G == RAGGED_M) {
             if (mrow >= tc.seg_len) continue;
             row = tc.seg0 + mrow;
           } else {
@@ -365,9 +457,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
           cbase[row * p.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][r]);
         }
     }
-  } else {  // EPI_SWIGLU_BWD: acc = dA[row][f], f = n0 + wn*64 + j*32 + col
-    // One 32-row block at a time so only 16 partial row sums are live.
-    float* red = reinterpret_cast<float*>(smem);  // [4 N-waves][256 rows]
+  } else {  // EPI_SWIGLU_BWD: acc = dA[row][f], f = n0 + wn*128 + j*32 + col
+    float* red = reinterpret_cast<float*>(sA0);  // [2 N-waves][256 rows]
     const int64_t ld1 = 2 * (int64_t)p.F;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -375,12 +466,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) rs[r] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int f = n0 + wn * 64 + j * 32 + colw;
+      for (int j = 0; j < 4; ++j) {
+        const int f = n0 + wn * 128 + j * 32 + colw;
         const bool fok = f < p.F;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int mrow = tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          const int mrow =
+              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
           if (mrow < tc.seg_len && fok) {
             const int64_t row = tc.seg0 + mrow;
             const float g = bf16_to_f32(p.h1[row * ld1 + f]);
@@ -412,14 +504,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       }
     }
     if (p.dw_part) {
-      // across the 4 N-waves, fixed order
+      // across the 2 N-waves, fixed order
       __syncthreads();
-      if (t < 256) {
-        const int mrow = tc.m0 + t;
-        if (mrow < tc.seg_len) {
-          const float s = red[t] + red[256 + t] + red[512 + t] + red[768 + t];
-          p.dw_part[(int64_t)tc.nt * p.rows + tc.seg0 + mrow] = s;
-        }
+      const int mrow = tc.m0 + t;
+      if (mrow < tc.seg_len) {
+        const float s = red[t] + red[256 + t];
+        p.dw_part[(int64_t)tc.nt * p.rows + tc.seg0 + mrow] = s;
       }
     }
   }
