@@ -74,7 +74,11 @@ class Layer:
         self.idx = e((T, k), i32)
         self.w = e((T, k), f32)
         self.mx = cfg.mode == "mxfp8"
-        self.x_perm = e((rows, H), b16)
+        # MXFP8: the permute writes E4M3 codes + E8M0 scales of x (fused
+        # quantisation); the weights are quantised from the bf16 masters
+        # inside every grouped-MLP call
+        self.x_perm = e((rows, H), u8 if self.mx else b16)
+        self.x_perm_scale = e((rows, H // 32), u8) if self.mx else None
         self.w_perm = e(rows, f32)
         self.row_map = e(rows, i32)
         self.src_row = e(rows, i32)
@@ -93,7 +97,7 @@ class Layer:
         fa.E, fa.H, fa.F, fa.rows = E, H, F, rows
         fa.precision = m.PREC_MXFP8 if self.mx else m.PREC_BF16
         fa.x_perm = self.x_perm.data_ptr()
-        fa.x_perm_scale = None
+        fa.x_perm_scale = self.x_perm_scale.data_ptr() if self.mx else None
         fa.w_gu, fa.w_dn = self.w_gu.data_ptr(), self.w_dn.data_ptr()
         fa.w_perm = self.w_perm.data_ptr()
         fa.offsets = self.offsets.data_ptr()
@@ -143,7 +147,8 @@ class Layer:
         def permute(st):
             m._check(L.moe_permute(
                 self.ctx, P(self.x), P(self.idx), P(self.w), T, H, E, k,
-                m.PREC_BF16, P(self.x_perm), None, P(self.w_perm),
+                m.PREC_MXFP8 if self.mx else m.PREC_BF16, P(self.x_perm),
+                P(self.x_perm_scale) if self.mx else None, P(self.w_perm),
                 P(self.row_map), P(self.src_row), P(self.split),
                 P(self.offsets), P(self.pws), self.pws.numel(), st))
 
@@ -214,6 +219,15 @@ def cpu_baseline(cfg, d, n_tokens):
     t0 = time.perf_counter()
     if cfg.backward:
         O.layer_bwd(x, lg, d["w_gu"], d["w_dn"], d["dy"][:n_tokens], cfg.k)
+    elif cfg.mode == "mxfp8":
+        E = d["w_gu"].shape[0]
+        idx, w = O.route_topk(lg, cfg.k)
+        mp = O.permute_index(idx, E)
+        z = O.grouped_mlp_fwd_mxfp8(O.permute_rows(x, mp["src_row"], cfg.k),
+                                    d["w_gu"], d["w_dn"],
+                                    O.permute_weights(w, mp["src_row"]),
+                                    mp["offsets"])["z"]
+        O.unpermute(z, mp["row_map"], cfg.k)
     else:
         O.layer_fwd(x, lg, d["w_gu"], d["w_dn"], cfg.k)
     dt = time.perf_counter() - t0
@@ -224,7 +238,8 @@ def cpu_baseline(cfg, d, n_tokens):
             "sample": (f"first {n_tokens} of {cfg.T} tokens of the "
                        f"{cfg.name} workload, whole layer "
                        f"{'fwd+bwd' if cfg.backward else 'fwd'} in float64 "
-                       f"numpy ({dt:.1f} s wall)"),
+                       f"numpy{' (MXFP8 quantisation included)' if cfg.mode == 'mxfp8' else ''}"
+                       f" ({dt:.1f} s wall)"),
             "tokens_per_s": n_tokens / dt, "seconds": dt}
 
 

@@ -325,8 +325,14 @@ moe_status_t check_mlp_dims(int32_t E, int32_t H, int32_t F, int64_t rows,
   const int kq = prec == MOE_PREC_BF16 ? 64 : 128;
   MOE_REQUIRE(H % kq == 0 && F % kq == 0, MOE_ERR_UNSUPPORTED,
               "H and F must be multiples of %d", kq);
-  MOE_REQUIRE(rows <= (int64_t)INT32_MAX / 2 && (int64_t)F * 2 * H < ((int64_t)1 << 40),
-              MOE_ERR_UNSUPPORTED, "tensor too large");
+  // GEMM operands are addressed with 32-bit byte offsets inside one
+  // expert's activation rows (plus a 256-row tile overhang) or weights
+  const int64_t widest = (int64_t)(H > 2 * F ? H : 2 * F) * 2;
+  MOE_REQUIRE(rows <= (int64_t)INT32_MAX / 2 &&
+                  (rows + 256) * widest < ((int64_t)1 << 32) &&
+                  (int64_t)F * 2 * H * 2 < ((int64_t)1 << 32),
+              MOE_ERR_UNSUPPORTED,
+              "tensor too large (an expert's operand must stay below 4 GiB)");
   return MOE_OK;
 }
 
@@ -362,6 +368,17 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
     MOE_REQUIRE(a->w_gu && a->w_dn, MOE_ERR_INVALID_ARG, "null weights");
   if (mx && a->w_gu_q) MOE_REQUIRE(a->w_gu_s, MOE_ERR_INVALID_ARG, "w_gu_s");
   if (mx && a->w_dn_q) MOE_REQUIRE(a->w_dn_s, MOE_ERR_INVALID_ARG, "w_dn_s");
+  // scale rows are read one dword (4 blocks of 32) at a time
+  auto al4 = [](const void* q) {
+    return (reinterpret_cast<uintptr_t>(q) & 3u) == 0;
+  };
+  if (mx)
+    MOE_REQUIRE(al4(a->x_perm_scale) && al4(a->w_gu_s) && al4(a->w_dn_s),
+                MOE_ERR_UNSUPPORTED, "MXFP8 scale arrays must be 4-byte aligned");
+  MOE_REQUIRE(aligned16(a->x_perm) && aligned16(a->w_gu) &&
+                  aligned16(a->w_dn) && aligned16(a->w_gu_q) &&
+                  aligned16(a->w_dn_q) && aligned16(a->z_perm),
+              MOE_ERR_UNSUPPORTED, "operands must be 16-byte aligned");
   size_t need = 0;
   moe_grouped_mlp_fwd_workspace_size(a, &need);
   MOE_REQUIRE(a->ws != nullptr && a->ws_bytes >= need, MOE_ERR_WORKSPACE,

@@ -1,0 +1,809 @@
+// Persistent-free ragged grouped GEMM kernel template for gfx950, shared by
+// the bf16 and MXFP8 expert-MLP GEMMs.
+//
+// One launch covers every expert: the tile decoder reads the per-expert row
+// offsets (split_sizes) on the device, so experts with no tokens produce no
+// tiles and the host never waits ("NVIDIA presents an efficient path for
+// training biological MoE models", section "Grouped experts instead of a
+// Python loop"; "Efficient MoE training for biological foundation models
+// (NVIDIA)", section "1) Fragmented expert kernels").
+//
+// Tile: 256 x 256 outputs, K step = one 128-byte row per operand (64 bf16 or
+// 128 E4M3 values), 256 threads = 4 waves in a 2 (M) x 2 (N) grid; each wave
+// owns 128 x 128 outputs = 4 x 4 MFMA blocks of 32 x 32 with 256 float32
+// accumulators per lane (kept in AGPRs).
+//  * bf16: v_mfma_f32_32x32x16_bf16, four 16-wide K slices per step.
+//  * MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, one E8M0 scale
+//    per 32 consecutive K values of each row and column), two 64-wide K
+//    slices per step.  Lane l holds row l%32; with g = l/32 its 32 bytes are
+//    K [16g, 16g+16) and [32+16g, 32+16g+16) of the slice, and its scale
+//    byte is the one of K block g of the slice (block 2kk+g of the step).
+// Operand tiles sit in LDS as [mn][k] rows of 128 bytes with an XOR swizzle
+// on the eight 16-byte chunks of a row; two stages, one barrier per step.
+//  * K-contiguous operands go global -> LDS directly (global_load_lds_dwordx4:
+//    each wave instruction fills one contiguous KiB of LDS, so every lane
+//    picks the global chunk that belongs at its LDS slot).
+//  * MN-contiguous operands (bf16 backward) go through registers and are
+//    transposed 8 x 8 on the way into LDS.
+// Tiles are ordered so that each XCD (blocks b = x mod 8) works through one
+// contiguous run of tiles, M fastest inside groups of 4 N tiles: the tiles in
+// flight on one XCD share activation rows and weight panels in its L2.
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+namespace gg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+#define MOE_LDS __attribute__((address_space(3)))
+
+constexpr int BM = 256, BN = 256;
+constexpr int kRowBytes = 128;              // bytes of one K step per row
+constexpr int kThreads = 256;
+constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand stage
+constexpr int kGroupN = 4;                  // N tiles per scheduling group
+constexpr int kXcds = 8;
+
+enum Layout { KC = 0, MC = 1 };  // memory: [mn][k] or [k][mn]
+enum Group { RAGGED_M = 0, RAGGED_K = 1 };
+enum Epi {
+  EPI_STORE = 0,       // bf16 C
+  EPI_SWIGLU = 1,      // bf16 A = w * silu(g) * u (+ g, u save)
+  EPI_SWIGLU_BWD = 2,  // dgrad of the down projection + SwiGLU backward
+  EPI_SWIGLU_MX = 3    // as EPI_SWIGLU, A quantised to MXFP8 along f
+};
+enum Prec { P_BF16 = 0, P_FP8 = 1 };
+
+struct Params {
+  const char* a;          // operand A (rows = M)
+  int64_t lda;            // bytes between rows (KC) or k rows (MC)
+  const char* b;          // operand B (rows = N), expert e at b + e * b_es
+  int64_t ldb, b_es;      // bytes
+  int M, N, K;            // K in elements; RAGGED_K: K per expert
+  int F;                  // SwiGLU epilogues: expert FFN size
+  int E;
+  const int32_t* offsets;     // [E+1] rows per expert
+  const int32_t* tile_start;  // RAGGED_M: [E+1] tile prefix
+  int tiles_n;                // tiles along N
+  int tiles_m;                // RAGGED_K: tiles along M
+  int b_rows;                 // rows of one expert's B (KC direct loads)
+  // MXFP8 scales: row-major [rows][K/32] bytes
+  const uint8_t* sa;
+  int64_t ldsa;
+  const uint8_t* sb;
+  int64_t ldsb, sb_es;
+  uint16_t* c;                // bf16 output (EPI_SWIGLU_MX: optional A save)
+  int64_t ldc, c_es;          // elements
+  uint16_t* c2;               // SwiGLU epilogues: (g, u) save [rows, 2F]
+  uint8_t* cq;                // EPI_SWIGLU_MX: A codes [rows, F]
+  uint8_t* cs;                // EPI_SWIGLU_MX: A scales [rows, F/32]
+  const uint16_t* h1;         // EPI_SWIGLU_BWD: saved (g, u) [rows, 2F]
+  const float* w;             // routing weight per row (nullable -> 1)
+  float* dw_part;             // EPI_SWIGLU_BWD: [tiles_n][rows]
+  int64_t rows;
+};
+
+// Swizzle of the 16-byte chunk c of LDS tile row r.  It depends only on
+// r mod 32, so the four 32-row blocks a wave reads sit at constant offsets
+// from each other.  Eight consecutive rows (one MFMA fragment read per 8
+// lanes) land on eight distinct chunk positions; so do rows 8 apart within
+// 32 rows (transposed register writes, 4 per 8 lanes).
+__device__ __forceinline__ int swz32(int r) {
+  return (r & 7) ^ ((r >> 3) & 3);
+}
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return r * kRowBytes + ((c ^ swz32(r)) << 4);
+}
+
+struct TileCoord {
+  int e;        // expert
+  int m0;       // first row of the tile inside the expert's M range
+  int seg0;     // offsets[e]
+  int seg_len;  // rows of expert e
+  int nt;       // N tile index
+};
+
+template <int G>
+__device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
+  const int b = blockIdx.x;
+  int total;
+  if constexpr (G == RAGGED_M) total = p.tile_start[p.E];
+  else total = p.E * p.tiles_m * p.tiles_n;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int idx = b / kXcds;
+  if (idx >= per) return false;
+  const int L = (b % kXcds) * per + idx;
+  if (L >= total) return false;
+  int e, local, mt_e;
+  if constexpr (G == RAGGED_M) {
+    // tile_start[e] <= L < tile_start[e+1]; experts without tiles have
+    // tile_start[e] == tile_start[e+1] and are never selected
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tile_start[mid] <= L) lo = mid; else hi = mid;
+    }
+    e = lo;
+    local = L - p.tile_start[e];
+    const int len = p.offsets[e + 1] - p.offsets[e];
+    mt_e = (len + BM - 1) / BM;
+  } else {
+    const int per_e = p.tiles_m * p.tiles_n;
+    e = L / per_e;
+    local = L - e * per_e;
+    mt_e = p.tiles_m;
+  }
+  // groups of kGroupN N-tiles, M tiles fastest inside a group
+  const int ng = local / (mt_e * kGroupN);
+  const int in_g = local - ng * mt_e * kGroupN;
+  tc.e = e;
+  tc.m0 = (in_g % mt_e) * BM;
+  tc.nt = ng * kGroupN + in_g / mt_e;
+  tc.seg0 = p.offsets[e];
+  tc.seg_len = p.offsets[e + 1] - tc.seg0;
+  return true;
+}
+
+// B operand row of tile row rr.  SwiGLU epilogues: 32-row blocks alternate
+// gate / up rows for the same 32 f columns, so one tile row block of 64 holds
+// both halves of 32 outputs.
+template <int EPI>
+__device__ __forceinline__ int b_row(const Params& p, int n0, int rr) {
+  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
+    const int blk = rr >> 5;
+    const int f = min(n0 + (blk >> 1) * 32 + (rr & 31), p.F - 1);
+    return (blk & 1) ? p.F + f : f;
+  } else {
+    return min(n0 + rr, p.N - 1);
+  }
+}
+
+// ---- K-contiguous operand: direct global -> LDS ----------------------------
+// buffer_load_dwordx4 ... lds: each wave instruction fills one contiguous KiB
+// of LDS.  Wave w, instruction j fills KiB 4 j + w of the tile = tile rows
+// 32 j + (8 w + i/8) for lane i, chunk slot i%8, which holds the logical
+// chunk (i%8) ^ swz32(row).  The buffer descriptor covers exactly the
+// operand's valid bytes from the current K offset, so rows past the end of
+// an expert and a padding K step (descriptor of 0 bytes) read as zeros with
+// no branch.
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+template <int EPI, bool IS_B>
+struct KcDirect {
+  const char* base;  // wave-uniform: operand base of the expert
+  uint32_t rec;      // valid bytes from base
+  int64_t ld;        // bytes per row
+  int q;             // row inside each 32-row block: 8 w + lane / 8
+  int cl;            // the lane's logical chunk
+  int r0;            // A: first tile row (expert-relative)
+  int n0, F, N;      // B: tile's first output unit, FFN size, rows
+  uint32_t off[8];   // per instruction: byte offset of the lane's chunk
+
+  __device__ __forceinline__ int row(int j) const {
+    if constexpr (!IS_B) {
+      return r0 + 32 * j + q;   // past the expert's rows: out of range -> 0
+    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
+      const int f = min(n0 + (j >> 1) * 32 + q, F - 1);
+      return (j & 1) ? F + f : f;
+    } else {
+      return min(n0 + 32 * j + q, N - 1);
+    }
+  }
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      off[j] = (uint32_t)row(j) * (uint32_t)ld + (uint32_t)(cl * 16);
+  }
+  __device__ __forceinline__ void issue(char* lds_tile, uint32_t kbyte,
+                                        bool real, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + kbyte), (short)0, (int)(real ? rec - kbyte : 0u),
+        kBufFlags);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      MOE_LDS void* dst =
+          (MOE_LDS void*)(lds_tile + (4 * j + wave) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off[j], 0, 0, 0);
+    }
+  }
+};
+
+// ---- MN-contiguous bf16 operand through registers ---------------------------
+// Thread t covers mn chunk (t & 31) (8 values) for k rows 8 (t >> 5) .. +7;
+// the 8 x 8 block is transposed in registers and written as 8 row chunks.
+struct McStaged {
+  const char* base;       // element (mn = this thread's chunk, k = 0)
+  int64_t ld;             // bytes between consecutive k rows
+  int kvalid;             // k rows >= kvalid read as zero
+  int kr;                 // first k row of the staged block
+  uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+
+  // Rows past kvalid load the last valid row; store() zeroes them, so the
+  // loads stay in flight until the LDS store (callers never load with
+  // kvalid == 0).
+  __device__ __forceinline__ uint4 row(int k) const {
+    const int kc = min(k, kvalid - 1);
+    return *reinterpret_cast<const uint4*>(base + (int64_t)kc * ld);
+  }
+  __device__ __forceinline__ void load(int k0) {
+    kr = k0 + 8 * (threadIdx.x >> 5);
+    v0 = row(kr + 0); v1 = row(kr + 1); v2 = row(kr + 2); v3 = row(kr + 3);
+    v4 = row(kr + 4); v5 = row(kr + 5); v6 = row(kr + 6); v7 = row(kr + 7);
+  }
+  static __device__ __forceinline__ uint4 keep(uint4 v, bool ok) {
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u,
+                      ok ? v.w : 0u);
+  }
+  // lo: halves 0 of the two inputs (k even, k odd); hi: halves 1
+  static __device__ __forceinline__ uint32_t plo(uint32_t ke, uint32_t ko) {
+    return __builtin_amdgcn_perm(ko, ke, 0x05040100u);
+  }
+  static __device__ __forceinline__ uint32_t phi(uint32_t ke, uint32_t ko) {
+    return __builtin_amdgcn_perm(ko, ke, 0x07060302u);
+  }
+  static __device__ __forceinline__ void put(char* lds, int r, int c,
+                                             uint4 val) {
+    *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = val;
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int kg = threadIdx.x >> 5;          // k chunk 0..7
+    const int r0 = (threadIdx.x & 31) * 8;    // first mn row
+    const uint4 w0 = keep(v0, kr + 0 < kvalid), w1 = keep(v1, kr + 1 < kvalid);
+    const uint4 w2 = keep(v2, kr + 2 < kvalid), w3 = keep(v3, kr + 3 < kvalid);
+    const uint4 w4 = keep(v4, kr + 4 < kvalid), w5 = keep(v5, kr + 5 < kvalid);
+    const uint4 w6 = keep(v6, kr + 6 < kvalid), w7 = keep(v7, kr + 7 < kvalid);
+    // column pair d of the inputs holds mn 2d (low half) and 2d+1 (high)
+    put(lds, r0 + 0, kg, make_uint4(plo(w0.x, w1.x), plo(w2.x, w3.x),
+                                    plo(w4.x, w5.x), plo(w6.x, w7.x)));
+    put(lds, r0 + 1, kg, make_uint4(phi(w0.x, w1.x), phi(w2.x, w3.x),
+                                    phi(w4.x, w5.x), phi(w6.x, w7.x)));
+    put(lds, r0 + 2, kg, make_uint4(plo(w0.y, w1.y), plo(w2.y, w3.y),
+                                    plo(w4.y, w5.y), plo(w6.y, w7.y)));
+    put(lds, r0 + 3, kg, make_uint4(phi(w0.y, w1.y), phi(w2.y, w3.y),
+                                    phi(w4.y, w5.y), phi(w6.y, w7.y)));
+    put(lds, r0 + 4, kg, make_uint4(plo(w0.z, w1.z), plo(w2.z, w3.z),
+                                    plo(w4.z, w5.z), plo(w6.z, w7.z)));
+    put(lds, r0 + 5, kg, make_uint4(phi(w0.z, w1.z), phi(w2.z, w3.z),
+                                    phi(w4.z, w5.z), phi(w6.z, w7.z)));
+    put(lds, r0 + 6, kg, make_uint4(plo(w0.w, w1.w), plo(w2.w, w3.w),
+                                    plo(w4.w, w5.w), plo(w6.w, w7.w)));
+    put(lds, r0 + 7, kg, make_uint4(phi(w0.w, w1.w), phi(w2.w, w3.w),
+                                    phi(w4.w, w5.w), phi(w6.w, w7.w)));
+  }
+};
+
+// ---- MXFP8 scales of one K step --------------------------------------------
+// Lane l needs, for each of its 4 A row blocks and 4 B row blocks, the scale
+// bytes of K blocks g and 2+g of the step (g = l/32): one dword (4 blocks)
+// per row, rearranged so that byte 0 feeds slice 0 and byte 1 slice 1 (the
+// MFMA's opsel picks the byte).
+struct MxScales {
+  const uint8_t* a;  // wave-uniform: A scales at the expert's first row
+  const uint8_t* b;  // wave-uniform: B scales of the expert
+  uint32_t oa[4], ob[4];  // lane's row offsets (bytes)
+  uint32_t na[4], nb[4];  // next step, raw
+  __device__ __forceinline__ void load(int kblk) {
+    const uint8_t* ka = a + kblk;
+    const uint8_t* kb = b + kblk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      na[i] = *reinterpret_cast<const uint32_t*>(ka + oa[i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      nb[j] = *reinterpret_cast<const uint32_t*>(kb + ob[j]);
+  }
+  // bytes (g, 2+g) -> (0, 1)
+  static __device__ __forceinline__ uint32_t pick(uint32_t d, uint32_t sel) {
+    return __builtin_amdgcn_perm(0u, d, sel);
+  }
+};
+
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return 1.0f / (1.0f + __expf(-x));
+}
+
+// ---- MFMA fragments ---------------------------------------------------------
+template <int P>
+struct Frags;
+
+// Byte offset of chunk c in the lane's fragment row fr (0..31) of a 32-row
+// block; a block's rows start at a multiple of 32, where the swizzle
+// repeats, so block offsets are plain constants.
+__device__ __forceinline__ int frag_off(int fr, int c) {
+  return fr * kRowBytes + ((c ^ swz32(fr)) << 4);
+}
+
+template <>
+struct Frags<P_BF16> {
+  static constexpr int kSlices = 4;  // 16-wide K slices per step
+  bf16x8_t a0, a1, a2, a3, b0, b1, b2, b3;
+  static __device__ __forceinline__ bf16x8_t at(const char* s, int off) {
+    return *reinterpret_cast<const bf16x8_t*>(s + off);
+  }
+  // lane l: row l%32 of each 32-row block, k 8 (l/32) .. +7 of the slice
+  __device__ __forceinline__ void load(const char* sa, const char* sb, int kk,
+                                       int wm, int wn, int lane) {
+    const int o = frag_off(lane & 31, kk * 2 + (lane >> 5));
+    const char* pa = sa + wm * (128 * kRowBytes) + o;
+    const char* pb = sb + wn * (128 * kRowBytes) + o;
+    a0 = at(pa, 0 * 32 * kRowBytes);
+    a1 = at(pa, 1 * 32 * kRowBytes);
+    a2 = at(pa, 2 * 32 * kRowBytes);
+    a3 = at(pa, 3 * 32 * kRowBytes);
+    b0 = at(pb, 0 * 32 * kRowBytes);
+    b1 = at(pb, 1 * 32 * kRowBytes);
+    b2 = at(pb, 2 * 32 * kRowBytes);
+    b3 = at(pb, 3 * 32 * kRowBytes);
+  }
+};
+
+template <>
+struct Frags<P_FP8> {
+  static constexpr int kSlices = 2;  // 64-wide K slices per step
+  i32x8_t a0, a1, a2, a3, b0, b1, b2, b3;
+  static __device__ __forceinline__ i32x8_t at(const char* s0, const char* s1,
+                                               int off) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(s0 + off);
+    const uint4 hi = *reinterpret_cast<const uint4*>(s1 + off);
+    i32x8_t v;
+    v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
+    v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
+    return v;
+  }
+  // lane l (g = l/32): chunks 4kk+g and 4kk+2+g of its row
+  __device__ __forceinline__ void load(const char* sa, const char* sb, int kk,
+                                       int wm, int wn, int lane) {
+    const int c0 = kk * 4 + (lane >> 5);
+    const int o0 = frag_off(lane & 31, c0), o1 = frag_off(lane & 31, c0 + 2);
+    const char* pa0 = sa + wm * (128 * kRowBytes) + o0;
+    const char* pa1 = sa + wm * (128 * kRowBytes) + o1;
+    const char* pb0 = sb + wn * (128 * kRowBytes) + o0;
+    const char* pb1 = sb + wn * (128 * kRowBytes) + o1;
+    a0 = at(pa0, pa1, 0 * 32 * kRowBytes);
+    a1 = at(pa0, pa1, 1 * 32 * kRowBytes);
+    a2 = at(pa0, pa1, 2 * 32 * kRowBytes);
+    a3 = at(pa0, pa1, 3 * 32 * kRowBytes);
+    b0 = at(pb0, pb1, 0 * 32 * kRowBytes);
+    b1 = at(pb0, pb1, 1 * 32 * kRowBytes);
+    b2 = at(pb0, pb1, 2 * 32 * kRowBytes);
+    b3 = at(pb0, pb1, 3 * 32 * kRowBytes);
+  }
+};
+
+#define MOE_MFMA_BF(i, j, A, B) \
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[i][j], 0, 0, 0)
+
+__device__ __forceinline__ void mfma_bf16(const Frags<P_BF16>& f,
+                                          f32x16_t (&acc)[4][4]) {
+  MOE_MFMA_BF(0, 0, f.a0, f.b0); MOE_MFMA_BF(0, 1, f.a0, f.b1);
+  MOE_MFMA_BF(0, 2, f.a0, f.b2); MOE_MFMA_BF(0, 3, f.a0, f.b3);
+  MOE_MFMA_BF(1, 0, f.a1, f.b0); MOE_MFMA_BF(1, 1, f.a1, f.b1);
+  MOE_MFMA_BF(1, 2, f.a1, f.b2); MOE_MFMA_BF(1, 3, f.a1, f.b3);
+  MOE_MFMA_BF(2, 0, f.a2, f.b0); MOE_MFMA_BF(2, 1, f.a2, f.b1);
+  MOE_MFMA_BF(2, 2, f.a2, f.b2); MOE_MFMA_BF(2, 3, f.a2, f.b3);
+  MOE_MFMA_BF(3, 0, f.a3, f.b0); MOE_MFMA_BF(3, 1, f.a3, f.b1);
+  MOE_MFMA_BF(3, 2, f.a3, f.b2); MOE_MFMA_BF(3, 3, f.a3, f.b3);
+}
+#undef MOE_MFMA_BF
+
+// MXFP8 slice KK: scales sa[i], sb[j] hold slice 0 in byte 0, slice 1 in
+// byte 1 (opsel = KK); format code 0 = E4M3 for both operands.
+#define MOE_MFMA_MX(i, j, A, B)                                            \
+  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(             \
+      A, B, acc[i][j], 0, 0, KK, (int)sa[i], KK, (int)sb[j])
+
+template <int KK>
+__device__ __forceinline__ void mfma_fp8(const Frags<P_FP8>& f,
+                                         const uint32_t (&sa)[4],
+                                         const uint32_t (&sb)[4],
+                                         f32x16_t (&acc)[4][4]) {
+  MOE_MFMA_MX(0, 0, f.a0, f.b0); MOE_MFMA_MX(0, 1, f.a0, f.b1);
+  MOE_MFMA_MX(0, 2, f.a0, f.b2); MOE_MFMA_MX(0, 3, f.a0, f.b3);
+  MOE_MFMA_MX(1, 0, f.a1, f.b0); MOE_MFMA_MX(1, 1, f.a1, f.b1);
+  MOE_MFMA_MX(1, 2, f.a1, f.b2); MOE_MFMA_MX(1, 3, f.a1, f.b3);
+  MOE_MFMA_MX(2, 0, f.a2, f.b0); MOE_MFMA_MX(2, 1, f.a2, f.b1);
+  MOE_MFMA_MX(2, 2, f.a2, f.b2); MOE_MFMA_MX(2, 3, f.a2, f.b3);
+  MOE_MFMA_MX(3, 0, f.a3, f.b0); MOE_MFMA_MX(3, 1, f.a3, f.b1);
+  MOE_MFMA_MX(3, 2, f.a3, f.b2); MOE_MFMA_MX(3, 3, f.a3, f.b3);
+}
+#undef MOE_MFMA_MX
+
+template <int P>
+struct Mma;
+
+template <>
+struct Mma<P_BF16> {
+  template <int KK>
+  static __device__ __forceinline__ void run(const Frags<P_BF16>& f,
+                                             const uint32_t (&)[4],
+                                             const uint32_t (&)[4],
+                                             f32x16_t (&acc)[4][4]) {
+    mfma_bf16(f, acc);
+  }
+};
+
+template <>
+struct Mma<P_FP8> {
+  template <int KK>
+  static __device__ __forceinline__ void run(const Frags<P_FP8>& f,
+                                             const uint32_t (&sa)[4],
+                                             const uint32_t (&sb)[4],
+                                             f32x16_t (&acc)[4][4]) {
+    mfma_fp8<KK & 1>(f, sa, sb, acc);
+  }
+};
+
+// ---- the kernel -------------------------------------------------------------
+template <int P, int LA, int LB, int G, int EPI>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
+  static_assert(P == P_BF16 || (LA == KC && LB == KC),
+                "MXFP8 operands are K-contiguous");
+  using Fr = Frags<P>;
+  constexpr int kSl = Fr::kSlices;
+  constexpr int kElemBytes = P == P_FP8 ? 1 : 2;
+  constexpr int kStepK = kRowBytes / kElemBytes;  // K elements per step
+
+  __shared__ __attribute__((aligned(1024))) char sA0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sB0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sA1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sB1[kTileBytes];
+  TileCoord tc;
+  if (!decode_tile<G>(p, tc)) return;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1;   // 0..1
+  const int wn = wave & 1;    // 0..1
+
+  // ---- tile geometry ----
+  int kdim, n0;
+  if constexpr (G == RAGGED_M) kdim = p.K;
+  else kdim = tc.seg_len;
+  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX)
+    n0 = tc.nt * (BN / 2);   // f units
+  else
+    n0 = tc.nt * BN;
+
+  // ---- operand sources ----
+  KcDirect<EPI, false> da;
+  KcDirect<EPI, true> db;
+  McStaged ma, mb;
+  MxScales ms;
+  const int q = 8 * wave + (lane >> 3);   // direct-load row inside 32 rows
+  const int cl = (lane & 7) ^ swz32(q);   // its logical chunk
+  if constexpr (LA == KC) {
+    // RAGGED_M rows seg0 + m0 + r, clamped to the expert's last row
+    da.base = p.a + (int64_t)tc.seg0 * p.lda;
+    da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda;
+    da.ld = p.lda;
+    da.q = q;
+    da.cl = cl;
+    da.r0 = tc.m0;
+    da.init();
+  } else {
+    // A element (m, k) at a + (seg0 + k) * lda + 2 m (RAGGED_K: k = token)
+    const int mc = min(tc.m0 + (t & 31) * 8, p.M - 8);
+    ma.base = p.a + (int64_t)tc.seg0 * p.lda + 2 * (int64_t)mc;
+    ma.ld = p.lda;
+    ma.kvalid = kdim;
+  }
+  const char* bexp = p.b + (int64_t)tc.e * p.b_es;
+  if constexpr (LB == KC) {
+    db.base = bexp;
+    db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb;
+    db.ld = p.ldb;
+    db.q = q;
+    db.cl = cl;
+    db.n0 = n0;
+    db.F = p.F;
+    db.N = p.N;
+    db.init();
+  } else {
+    const int nc = min(n0 + (t & 31) * 8, p.N - 8);
+    if constexpr (G == RAGGED_M) mb.base = bexp + 2 * (int64_t)nc;
+    else mb.base = p.b + (int64_t)tc.seg0 * p.ldb + 2 * (int64_t)nc;
+    mb.ld = p.ldb;
+    mb.kvalid = kdim;
+  }
+  uint32_t sa_cur[4] = {0, 0, 0, 0}, sb_cur[4] = {0, 0, 0, 0};
+  // byte selector for v_perm: lane group g takes scale bytes (g, 2 + g)
+  const uint32_t sel = (lane >> 5) ? 0x0c0c0301u : 0x0c0c0200u;
+  if constexpr (P == P_FP8) {
+    ms.a = p.sa + (int64_t)tc.seg0 * p.ldsa;
+    ms.b = p.sb + (int64_t)tc.e * p.sb_es;
+    KcDirect<EPI, true> m;   // B row mapping of the lane's 32-row blocks
+    m.q = lane & 31;
+    m.n0 = n0;
+    m.F = p.F;
+    m.N = p.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = min(tc.m0 + wm * 128 + 32 * i + (lane & 31),
+                         tc.seg_len - 1);
+      ms.oa[i] = (uint32_t)ra * (uint32_t)p.ldsa;
+      // B tile row wn*128 + 32 i + lane%32 is direct-load block 4 wn + i
+      ms.ob[i] = (uint32_t)m.row(4 * wn + i) * (uint32_t)p.ldsb;
+    }
+  }
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+  const int nk = (kdim + kStepK - 1) / kStepK;
+  auto issue = [&](char* bufa, char* bufb, int kt, bool real) {
+    // a padding step (real == false) reads zeros: empty descriptors for
+    // direct loads, k rows past kvalid for staged loads; its scales are
+    // those of the last real step (finite; they multiply zeros)
+    if constexpr (LA == KC) da.issue(bufa, (uint32_t)kt * kRowBytes, real, wave);
+    else ma.load(kt * kStepK);
+    if constexpr (LB == KC) db.issue(bufb, (uint32_t)kt * kRowBytes, real, wave);
+    else mb.load(kt * kStepK);
+    if constexpr (P == P_FP8) ms.load(min(kt, nk - 1) * (kStepK / 32));
+  };
+  auto stage_store = [&](char* bufa, char* bufb) {
+    if constexpr (LA == MC) ma.store(bufa);
+    if constexpr (LB == MC) mb.store(bufb);
+  };
+  auto take_scales = [&]() {
+    if constexpr (P == P_FP8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa_cur[i] = MxScales::pick(ms.na[i], sel);
+        sb_cur[i] = MxScales::pick(ms.nb[i], sel);
+      }
+    }
+  };
+
+  // Two K steps per loop trip, one per LDS stage, so each stage is a
+  // distinct LDS object: the compiler then knows that direct loads into one
+  // stage never alias fragment reads of the other and waits for them only
+  // at the barrier.  An odd last step computes on a zero stage.  The trip
+  // has no branches, so the MFMAs stay where they are written.
+  // Fragment reads run one K slice ahead of the MFMAs; the barrier that
+  // publishes the next stage sits before the last slice's MFMAs so the first
+  // reads of the next stage overlap them.
+  const int nk2 = (nk + 1) & ~1;
+  if (nk > 0) {
+    issue(sA0, sB0, 0, true);
+    stage_store(sA0, sB0);
+  }
+  __syncthreads();
+  take_scales();
+  Fr cur, nxt;
+  cur.load(sA0, sB0, 0, wm, wn, lane);
+
+  for (int kt = 0; kt < nk2; kt += 2) {
+    // stage kt from buffers 0 while stage kt+1 loads into buffers 1
+    issue(sA1, sB1, kt + 1, kt + 1 < nk);
+#pragma unroll
+    for (int kk = 0; kk < kSl - 1; ++kk) {
+      nxt.load(sA0, sB0, kk + 1, wm, wn, lane);
+      if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
+      else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
+      cur = nxt;
+      // keep the scheduler from hoisting later slices' reads (registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage_store(sA1, sB1);
+    __syncthreads();
+    nxt.load(sA1, sB1, 0, wm, wn, lane);
+    Mma<P>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
+    cur = nxt;
+    take_scales();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // stage kt+1 from buffers 1 while stage kt+2 loads into buffers 0 (a
+    // step past nk2 is never computed; its zero loads are harmless)
+    issue(sA0, sB0, kt + 2, kt + 2 < nk);
+#pragma unroll
+    for (int kk = 0; kk < kSl - 1; ++kk) {
+      nxt.load(sA1, sB1, kk + 1, wm, wn, lane);
+      if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
+      else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
+      cur = nxt;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    stage_store(sA0, sB0);
+    __syncthreads();
+    nxt.load(sA0, sB0, 0, wm, wn, lane);
+    Mma<P>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
+    cur = nxt;
+    take_scales();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- epilogue ----
+  // acc[i][j][r] is C[row][col] of the wave's block with
+  //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
+  //   col = wn*128 + j*32 + lane%32
+  const int colw = lane & 31;
+  const int rsub = (lane >> 5) * 4;
+  if constexpr (EPI == EPI_SWIGLU) {
+    // B rows of block j: gate f-block (2 wn + j/2) for even j, up for odd j
+    const int64_t ld1 = 2 * (int64_t)p.F;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int f = n0 + (2 * wn + jj) * 32 + colw;
+      if (f >= p.F) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mrow =
+              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          if (mrow < tc.seg_len) {
+            const int64_t row = tc.seg0 + mrow;
+            const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+            const float wr = p.w ? p.w[row] : 1.0f;
+            const float a = wr * (g * fast_sigmoid(g)) * u;
+            p.c[row * p.ldc + f] = (uint16_t)f32_to_bf16(a);
+            if (p.c2) {
+              p.c2[row * ld1 + f] = (uint16_t)f32_to_bf16(g);
+              p.c2[row * ld1 + p.F + f] = (uint16_t)f32_to_bf16(u);
+            }
+          }
+        }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU_MX) {
+    // A = w * silu(g) * u in float32, then one E8M0 scale per 32 f columns:
+    // the 32 columns of an f block are the 32 lanes of a half-wave, so the
+    // block amax is a half-wave max.  F % 128 == 0: f blocks are whole.
+    const int64_t ld1 = 2 * (int64_t)p.F;
+    const int64_t lds = p.F / 32;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int fb = n0 + (2 * wn + jj) * 32;   // first f of the block
+      const int f = fb + colw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mrow =
+              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          const bool ok = mrow < tc.seg_len;
+          const int64_t row = tc.seg0 + (ok ? mrow : 0);
+          const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+          const float wr = ok ? (p.w ? p.w[row] : 1.0f) : 0.0f;
+          const float a = wr * (g * fast_sigmoid(g)) * u;
+          uint32_t am = __float_as_uint(a) & 0x7fffffffu;
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)am, off, 64);
+            am = am > o ? am : o;
+          }
+          const int s = e8m0_exp_from_f32_amax(am);
+          if (ok) {
+            p.cq[row * p.F + f] = (uint8_t)e4m3_from_f32(__float_as_uint(a), s);
+            if (colw == 0) p.cs[row * lds + fb / 32] = (uint8_t)(s + 127);
+            if (p.c) p.c[row * p.ldc + f] = (uint16_t)f32_to_bf16(a);
+            if (p.c2) {
+              p.c2[row * ld1 + f] = (uint16_t)f32_to_bf16(g);
+              p.c2[row * ld1 + p.F + f] = (uint16_t)f32_to_bf16(u);
+            }
+          }
+        }
+    }
+  } else if constexpr (EPI == EPI_STORE) {
+    uint16_t* cbase = p.c;
+    if constexpr (G == RAGGED_K) cbase += (int64_t)tc.e * p.c_es;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + colw;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mrow =
+              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          int64_t row;
+          if constexpr (G == RAGGED_M) {
+            if (mrow >= tc.seg_len) continue;
+            row = tc.seg0 + mrow;
+          } else {
+            if (mrow >= p.M) continue;
+            row = mrow;
+          }
+          cbase[row * p.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+        }
+    }
+  } else {  // EPI_SWIGLU_BWD: acc = dA[row][f], f = n0 + wn*128 + j*32 + col
+    // the loop's last (unused) fragment reads of stage 0 must finish before
+    // stage 0 becomes the row-sum scratch
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(sA0);  // [2 N-waves][256 rows]
+    const int64_t ld1 = 2 * (int64_t)p.F;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float rs[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rs[r] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f = n0 + wn * 128 + j * 32 + colw;
+        const bool fok = f < p.F;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mrow =
+              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          if (mrow < tc.seg_len && fok) {
+            const int64_t row = tc.seg0 + mrow;
+            const float g = bf16_to_f32(p.h1[row * ld1 + f]);
+            const float u = bf16_to_f32(p.h1[row * ld1 + p.F + f]);
+            const float wr = p.w ? p.w[row] : 1.0f;
+            const float s = fast_sigmoid(g);
+            const float sg = g * s;
+            const float da = acc[i][j][r];
+            const float dg = da * wr * u * (s * (1.0f + g * (1.0f - s)));
+            const float du = da * wr * sg;
+            p.c[row * ld1 + f] = (uint16_t)f32_to_bf16(dg);
+            p.c[row * ld1 + p.F + f] = (uint16_t)f32_to_bf16(du);
+            rs[r] += da * sg * u;
+          }
+        }
+      }
+      if (p.dw_part) {
+        // sum over the 32 columns held by the lanes with the same lane / 32
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = rs[r];
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off, 64);
+          if (colw == 0) {
+            const int tr = wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+            red[wn * 256 + tr] = v;
+          }
+        }
+      }
+    }
+    if (p.dw_part) {
+      // across the 2 N-waves, fixed order
+      __syncthreads();
+      const int mrow = tc.m0 + t;
+      if (mrow < tc.seg_len) {
+        const float s = red[t] + red[256 + t];
+        p.dw_part[(int64_t)tc.nt * p.rows + tc.seg0 + mrow] = s;
+      }
+    }
+  }
+}
+
+// Tile prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/BM) * tn.
+__global__ __launch_bounds__(1024) void tile_table_kernel(
+    const int32_t* __restrict__ offsets, int E, int tn,
+    int32_t* __restrict__ tile_start);
+
+// Grid for a RAGGED_M launch: sum_e ceil(M_e / BM) <= rows / BM + E tiles
+// per N tile, rounded up to whole XCD rounds.
+inline int ragged_m_grid(int64_t rows, int E, int tn) {
+  const int64_t mt = rows / BM + E;
+  int64_t g = mt * tn;
+  g = (g + kXcds - 1) / kXcds * kXcds;
+  return (int)g;
+}
+
+inline int ragged_k_grid(int E, int tiles_m, int tiles_n) {
+  return (E * tiles_m * tiles_n + kXcds - 1) / kXcds * kXcds;
+}
+
+template <int P, int LA, int LB, int G, int EPI>
+hipError_t launch(const Params& p, int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_kernel<P, LA, LB, G, EPI>), dim3(grid),
+                     dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
+                             int32_t* tile_start, hipStream_t stream);
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace gg
+}  // namespace moe

@@ -82,4 +82,68 @@ MOE_HD inline int e8m0_exp_from_bf16_amax(uint32_t a) {
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 
+// E4M3 (OCP) code of a float32 value scaled by 2^-s, integer operations
+// only, with the same rules as e4m3_from_bf16 (round to nearest even on the
+// 3-bit mantissa grid, subnormals m*2^-9, saturation at 448, sign kept).
+// `f` is the 32-bit pattern of a finite float.
+MOE_HD inline uint32_t e4m3_from_f32(uint32_t f, int s) {
+  const uint32_t sign = (f >> 24) & 0x80u;
+  const int be = (int)((f >> 23) & 0xFF);
+  const uint32_t man = f & 0x7FFFFFu;
+  if (be == 0 && man == 0) return sign;
+  // value = sig * 2^(ex - 23), sig in [2^23, 2^24)
+  int ex;
+  uint32_t sig;
+  if (be == 0) {
+    const int lz = moe_clz32(man) - 8;  // leading zeros within 24 bits
+    sig = man << lz;
+    ex = -126 - lz;
+  } else {
+    sig = 0x800000u | man;
+    ex = be - 127;
+  }
+  ex -= s;
+  const int e0 = ex > -6 ? ex : -6;
+  // quantum 2^(e0 - 3): value / quantum = sig * 2^(ex - 23 - (e0 - 3))
+  const int shift = (e0 - 3) - (ex - 23);  // >= 20
+  uint32_t q;
+  if (shift >= 25) {
+    q = 0;  // below half a quantum (sig < 2^24)
+  } else {
+    const uint32_t kept = sig >> shift;
+    const uint32_t rem = sig & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1);
+    q = kept + ((rem > half || (rem == half && (kept & 1u))) ? 1u : 0u);
+  }
+  int e = e0;
+  if (q >= 16u) { e += 1; q = 8u; }
+  uint32_t code;
+  if (q >= 8u) {
+    if (e > 8) code = 0x7Eu;
+    else {
+      code = (uint32_t)((e + 7) << 3) | (q - 8u);
+      if (code > 0x7Eu) code = 0x7Eu;
+    }
+  } else {
+    code = q;
+  }
+  return code | sign;
+}
+
+// Scale exponent of a block from the float32 pattern of its amax (finite,
+// sign cleared): floor(log2 amax) - 8 clamped to [-127, 127]; zero -> -127.
+MOE_HD inline int e8m0_exp_from_f32_amax(uint32_t a) {
+  const int be = (int)((a >> 23) & 0xFF);
+  const uint32_t man = a & 0x7FFFFFu;
+  int fl;
+  if (be == 0) {
+    if (man == 0) return -127;
+    fl = -149 + (31 - moe_clz32(man));
+  } else {
+    fl = be - 127;
+  }
+  const int s = fl - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
 }  // namespace moe

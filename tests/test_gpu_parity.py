@@ -367,3 +367,100 @@ def test_grouped_mlp_bwd_bf16(m, T, H, F, E, k, zipf):
         if split[e] > 0:
             assert O.rel_err(gw_gu[e], ref["dw_gu"][e]) <= 2 * TOL_BF16, e
             assert O.rel_err(gw_dn[e], ref["dw_dn"][e]) <= 2 * TOL_BF16, e
+
+
+# ------------------------------------------------------- grouped MLP, MXFP8
+MX_CASES = [
+    # T, H, F, E, k, zipf   (H and F multiples of 128)
+    (256, 128, 256, 8, 2, 0.0),
+    (700, 256, 384, 5, 2, 1.2),     # ragged M tails, odd K-step count (3)
+    (900, 384, 128, 16, 4, 1.2),    # many experts, some empty
+]
+
+
+@pytest.mark.parametrize("T,H,F,E,k,zipf", MX_CASES)
+def test_grouped_mlp_fwd_mxfp8(m, T, H, F, E, k, zipf):
+    d = _mlp_case(T, H, F, E, k, zipf, seed=7)
+    ref = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], k)
+    rq = O.grouped_mlp_fwd_mxfp8(ref["x_perm"], d["w_gu"], d["w_dn"],
+                                 ref["w_perm"], ref["offsets"], keep=True)
+    yq = O.unpermute(rq["z"], ref["row_map"], k)
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w,
+                      precision=m.PREC_MXFP8)
+    wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
+    r = m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
+                              w_perm=p["w_perm"], precision=m.PREC_MXFP8,
+                              x_perm_scale=p["x_perm_scale"], save=True)
+    y = m.moe_unpermute(r["z"], p["row_map"], k)
+    assert_rows_close(host_f64(r["z"]), rq["z"], TOL_MX, "z")
+    assert_rows_close(host_f64(y), yq, TOL_MX, "y")
+    # the bf16 A save is the pre-quantisation SwiGLU output
+    assert_rows_close(host_f64(r["a"]), rq["a"], TOL_BF16, "a")
+    # far below the bar in practice: only A's block codes can differ
+    assert O.rel_err(host_f64(y), yq) < 1e-2
+
+
+def test_mxfp8_fwd_prequantised_equals_on_the_fly(m):
+    T, H, F, E, k = 500, 256, 256, 8, 2
+    d = _mlp_case(T, H, F, E, k, 1.2, seed=8)
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    pb = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    pq = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w,
+                       precision=m.PREC_MXFP8)
+    wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
+    # x quantised inside the call, weights quantised inside the call
+    z1 = m.moe_grouped_mlp_fwd(pb["x_perm"], wgu, wdn, pb["offsets"],
+                               w_perm=pb["w_perm"],
+                               precision=m.PREC_MXFP8)["z"]
+    # x codes from the permute, weights quantised by mxfp8_quantize
+    gq = m.mxfp8_quantize(wgu.reshape(E * 2 * F, H), m.ROWWISE)
+    dq = m.mxfp8_quantize(wdn.reshape(E * H, F), m.ROWWISE)
+    z2 = m.moe_grouped_mlp_fwd(
+        pq["x_perm"], wgu, wdn, pq["offsets"], w_perm=pq["w_perm"],
+        precision=m.PREC_MXFP8, x_perm_scale=pq["x_perm_scale"],
+        w_gu_q=(gq[0].reshape(E, 2 * F, H), gq[1].reshape(E, 2 * F, H // 32)),
+        w_dn_q=(dq[0].reshape(E, H, F), dq[1].reshape(E, H, F // 32)))["z"]
+    assert torch.equal(z1.view(torch.int16), z2.view(torch.int16))
+
+
+def test_mxfp8_fwd_exact_on_representable_operands(m):
+    """Operands that MXFP8 represents exactly (block max in the top binade,
+    as built here) pass through the quantisation unchanged, so the gate/up
+    GEMM equals the float64 product of the same values up to float32
+    accumulation order and the bf16 rounding of the saved (g, u)."""
+    rng = np.random.default_rng(9)
+    T, H, F, E, k = 300, 256, 128, 4, 1
+
+    def rep(shape):
+        nb = int(np.prod(shape)) // 32
+        mags = rng.integers(0, 0x78, size=(nb, 32))
+        mags[:, 0] = rng.integers(0x78, 0x7F, size=nb)
+        codes = mags | (rng.integers(0, 2, size=mags.shape) << 7)
+        s = rng.integers(-14, -6, size=nb)
+        v = np.ldexp(O.e4m3_decode(codes), s[:, None]).reshape(shape)
+        return v.astype(np.float32)
+
+    x = rep((T, H))
+    wgu = rep((E, 2 * F, H))
+    wdn = rep((E, H, F))
+    xb, gb, db = bf16_bits(x), bf16_bits(wgu), bf16_bits(wdn)
+    # representable in E4M3 with these scales -> exactly representable in bf16
+    assert np.array_equal(bf16_to_f32(xb), x)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    idx, w = m.moe_route_topk(torch.from_numpy(lg).cuda(), k)
+    p = m.moe_permute(dev_bf16(xb), idx, E)
+    r = m.moe_grouped_mlp_fwd(p["x_perm"], dev_bf16(gb), dev_bf16(db),
+                              p["offsets"], precision=m.PREC_MXFP8, save=True)
+    ref = O.permute_index(idx.cpu().numpy(), E)
+    xp = x.astype(np.float64)[ref["src_row"] // k]
+    h1 = np.zeros((T * k, 2 * F))
+    for e in range(E):
+        lo, hi = ref["offsets"][e], ref["offsets"][e + 1]
+        h1[lo:hi] = xp[lo:hi] @ wgu[e].astype(np.float64).T
+    got = host_f64(r["h1"])
+    # products are exact; what is left is float32 accumulation order and the
+    # bf16 rounding of the saved value (relative 2^-9): a wrong scale byte or
+    # K block would be off by powers of two
+    assert O.rel_err(got, h1) < 3e-3
+    assert_rows_close(got, h1, 3e-3, "h1")
