@@ -44,7 +44,34 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (the "
+                         "reference kernel that scales HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written per
+    launch, three launches.  Profiling counters of this run give the
+    factor between the FETCH_SIZE / WRITE_SIZE readings and real bytes."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), \
+        torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 3
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n,
+                      "launches": 3, "ms_per_copy": round(ms, 4),
+                      "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
 
 
 class Layer:
@@ -250,6 +277,9 @@ def main():
               "the multi-GPU sharding of this path is a design note, not a "
               "runnable configuration.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import mixture_experts_grouped_router_amd as m
     from synthetic import CONFIGS, generate_config

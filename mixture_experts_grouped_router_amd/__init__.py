@@ -101,11 +101,12 @@ _ctx: Dict[int, int] = {}
 
 
 def load_library(path: Optional[str] = None) -> ctypes.CDLL:
-    """Load libmoe.so (raises if it has not been built)."""
+    """Load libmoe.so (raises if it has not been built).  The environment
+    variable MOE_LIBRARY_PATH selects another build of the same library."""
     global _lib
     with _lib_lock:
         if _lib is None:
-            p = path or lib_path
+            p = path or os.environ.get("MOE_LIBRARY_PATH") or lib_path
             if not os.path.exists(p):
                 raise ImportError(
                     f"{p} not found: build it with "

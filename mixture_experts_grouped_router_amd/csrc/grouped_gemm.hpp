@@ -56,6 +56,27 @@ enum Epi {
 };
 enum Prec { P_BF16 = 0, P_FP8 = 1 };
 
+#ifndef MOE_SCHED_GROUPS
+#define MOE_SCHED_GROUPS 1
+#endif
+
+
+// Instruction schedule of one MFMA region: NR LDS reads interleaved one to
+// one with the first NR of the region's NM MFMAs, then the remaining MFMAs,
+// so the reads for the next K slice go out early and their latency hides
+// under the MFMAs (the default schedule issued them after most MFMAs).
+template <int NR, int NM>
+__device__ __forceinline__ void sched_reads_mfma() {
+#if MOE_SCHED_GROUPS
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  }
+  if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+#endif
+}
+
 struct Params {
   const char* a;          // operand A (rows = M)
   int64_t lda;            // bytes between rows (KC) or k rows (MC)
@@ -436,6 +457,238 @@ struct Mma<P_FP8> {
 };
 
 // ---- the kernel -------------------------------------------------------------
+// ---- LDS-staged epilogue helpers ---------------------------------------------
+// A wave stages its outputs in its own 32 KiB LDS array: 128 rows of 256
+// bytes (64 float32 or 128 bf16), 16-byte chunk c of row r stored at chunk
+// c ^ (r & 3).  A staging write (one row, 32 lanes, 128 contiguous bytes)
+// and a readback (8 lanes = 4 rows x 2 halves, rotated chunk order) are
+// free of bank conflicts.  On readback lane l owns rows (l >> 1) + 32 q,
+// q = 0..3, and half h = l & 1 of each: whole 32-wide f blocks (float32)
+// or 64 contiguous bf16, written to HBM with 16-byte stores.
+__device__ __forceinline__ int stg_off(int r, int c) {
+  return r * 256 + ((c ^ (r & 3)) << 4);
+}
+// row of accumulator element (i, r) inside the wave's 128 rows
+__device__ __forceinline__ int acc_row(int i, int r, int lane) {
+  return i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+__device__ __forceinline__ void stage_f32(char* buf, int row, int col,
+                                          float v) {
+  *reinterpret_cast<float*>(buf + stg_off(row, col >> 2) + (col & 3) * 4) = v;
+}
+__device__ __forceinline__ void stage_bf16(char* buf, int row, int col,
+                                           float v) {
+  *reinterpret_cast<uint16_t*>(buf + stg_off(row, col >> 3) + (col & 7) * 2) =
+      (uint16_t)f32_to_bf16(v);
+}
+// read k (0..7) of half h of the row returns logical chunk k ^ 4h (lanes
+// of the two halves hit different banks)
+__device__ __forceinline__ uint4 stage_read(const char* buf, int row, int h,
+                                            int k) {
+  return *reinterpret_cast<const uint4*>(buf + stg_off(row, 8 * h + (k ^ (4 * h))));
+}
+
+// ---- epilogues -------------------------------------------------------------
+// acc[i][j][r] is C[row][col] of the wave's 128 x 128 block with
+//   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
+//   col = wn*128 + j*32 + lane%32
+// `scratch` is LDS the epilogue may use after a barrier (SWIGLU_BWD).
+template <int G, int EPI>
+__device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
+                                         f32x16_t (&acc)[4][4], int n0,
+                                         int wm, int wn, int lane, int t,
+                                         char* scratch, char* wbuf) {
+  // acc[i][j][r] is C[row][col] of the wave's block with
+  //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
+  //   col = wn*128 + j*32 + lane%32
+  const int colw = lane & 31;
+  const int rsub = (lane >> 5) * 4;
+  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
+    // B rows of block j: gate f-block (2 wn + j/2) for even j, up for odd j.
+    // silu(g) * u goes through LDS (float32); the routing weight, the
+    // bf16 / MXFP8 encoding and the stores happen per row on readback.
+    const int64_t ld1 = 2 * (int64_t)p.F;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+          stage_f32(wbuf, acc_row(i, r, lane), jj * 32 + colw,
+                    (g * fast_sigmoid(g)) * u);
+        }
+    if (p.c2) {   // (g, u) save for the backward pass: direct stores
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int f = n0 + (2 * wn + jj) * 32 + colw;
+        if (f >= p.F) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int mrow = tc.m0 + wm * 128 + acc_row(i, r, lane);
+            if (mrow < tc.seg_len) {
+              const int64_t row = tc.seg0 + mrow;
+              p.c2[row * ld1 + f] = (uint16_t)f32_to_bf16(acc[i][2 * jj][r]);
+              p.c2[row * ld1 + p.F + f] =
+                  (uint16_t)f32_to_bf16(acc[i][2 * jj + 1][r]);
+            }
+          }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
+    const int h = lane & 1;                // f block (2 wn + h)
+    const int fb = n0 + (2 * wn + h) * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = (lane >> 1) + 32 * q;
+      const int mrow = tc.m0 + wm * 128 + lr;
+      // chunk k of the read order is logical chunk k ^ 4h: undo with a
+      // per-lane select (static register indices)
+      uint4 raw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) raw[k] = stage_read(wbuf, lr, h, k);
+      float v[32];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint4 c4 = h ? raw[c ^ 4] : raw[c];
+        v[4 * c + 0] = __uint_as_float(c4.x); v[4 * c + 1] = __uint_as_float(c4.y);
+        v[4 * c + 2] = __uint_as_float(c4.z); v[4 * c + 3] = __uint_as_float(c4.w);
+      }
+      if (mrow >= tc.seg_len || fb >= p.F) continue;
+      const int64_t row = tc.seg0 + mrow;
+      const float wr = p.w ? p.w[row] : 1.0f;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) v[c] *= wr;
+      if constexpr (EPI == EPI_SWIGLU_MX) {
+        // F % 128 == 0: f blocks are whole
+        uint32_t am = 0;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+          const uint32_t a = __float_as_uint(v[c]) & 0x7fffffffu;
+          am = am > a ? am : a;
+        }
+        const int sx = e8m0_exp_from_f32_amax(am);
+        uint32_t w8[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+          w8[d] = e4m3_from_f32(__float_as_uint(v[4 * d]), sx) |
+                  (e4m3_from_f32(__float_as_uint(v[4 * d + 1]), sx) << 8) |
+                  (e4m3_from_f32(__float_as_uint(v[4 * d + 2]), sx) << 16) |
+                  (e4m3_from_f32(__float_as_uint(v[4 * d + 3]), sx) << 24);
+        uint4* dq = reinterpret_cast<uint4*>(p.cq + row * p.F + fb);
+        dq[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+        dq[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+        p.cs[row * (p.F / 32) + fb / 32] = (uint8_t)(sx + 127);
+      }
+      if (EPI == EPI_SWIGLU || p.c) {
+        uint4* dc = reinterpret_cast<uint4*>(p.c + row * p.ldc + fb);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          dc[d] = make_uint4(pack_bf16x2(v[8 * d + 0], v[8 * d + 1]),
+                             pack_bf16x2(v[8 * d + 2], v[8 * d + 3]),
+                             pack_bf16x2(v[8 * d + 4], v[8 * d + 5]),
+                             pack_bf16x2(v[8 * d + 6], v[8 * d + 7]));
+      }
+    }
+  } else if constexpr (EPI == EPI_STORE) {
+    // bf16 C through LDS, then 64 contiguous values per lane and row
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          stage_bf16(wbuf, acc_row(i, r, lane), j * 32 + colw, acc[i][j][r]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
+    uint16_t* cbase = p.c;
+    if constexpr (G == RAGGED_K) cbase += (int64_t)tc.e * p.c_es;
+    const int h = lane & 1;
+    const int col0 = n0 + wn * 128 + 64 * h;   // N % 64 == 0: whole halves
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = (lane >> 1) + 32 * q;
+      const int mrow = tc.m0 + wm * 128 + lr;
+      uint4 raw[8], v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) raw[k] = stage_read(wbuf, lr, h, k);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) v[c] = h ? raw[c ^ 4] : raw[c];
+      int64_t row;
+      if constexpr (G == RAGGED_M) {
+        if (mrow >= tc.seg_len) continue;
+        row = tc.seg0 + mrow;
+      } else {
+        if (mrow >= p.M) continue;
+        row = mrow;
+      }
+      if (col0 >= p.N) continue;
+      uint4* dst = reinterpret_cast<uint4*>(cbase + row * p.ldc + col0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[k] = v[k];
+    }
+  } else {  // EPI_SWIGLU_BWD: acc = dA[row][f], f = n0 + wn*128 + j*32 + col
+    // the loop's last (unused) fragment reads of stage 0 must finish before
+    // stage 0 becomes the row-sum scratch
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(scratch);  // [2 N-waves][256 rows]
+    const int64_t ld1 = 2 * (int64_t)p.F;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float rs[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rs[r] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f = n0 + wn * 128 + j * 32 + colw;
+        const bool fok = f < p.F;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mrow =
+              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+          if (mrow < tc.seg_len && fok) {
+            const int64_t row = tc.seg0 + mrow;
+            const float g = bf16_to_f32(p.h1[row * ld1 + f]);
+            const float u = bf16_to_f32(p.h1[row * ld1 + p.F + f]);
+            const float wr = p.w ? p.w[row] : 1.0f;
+            const float s = fast_sigmoid(g);
+            const float sg = g * s;
+            const float da = acc[i][j][r];
+            const float dg = da * wr * u * (s * (1.0f + g * (1.0f - s)));
+            const float du = da * wr * sg;
+            p.c[row * ld1 + f] = (uint16_t)f32_to_bf16(dg);
+            p.c[row * ld1 + p.F + f] = (uint16_t)f32_to_bf16(du);
+            rs[r] += da * sg * u;
+          }
+        }
+      }
+      if (p.dw_part) {
+        // sum over the 32 columns held by the lanes with the same lane / 32
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = rs[r];
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off, 64);
+          if (colw == 0) {
+            const int tr = wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
+            red[wn * 256 + tr] = v;
+          }
+        }
+      }
+    }
+    if (p.dw_part) {
+      // across the 2 N-waves, fixed order
+      __syncthreads();
+      const int mrow = tc.m0 + t;
+      if (mrow < tc.seg_len) {
+        const float s = red[t] + red[256 + t];
+        p.dw_part[(int64_t)tc.nt * p.rows + tc.seg0 + mrow] = s;
+      }
+    }
+  }
+}
+
 template <int P, int LA, int LB, int G, int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   static_assert(P == P_BF16 || (LA == KC && LB == KC),
@@ -587,6 +840,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
       else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
       cur = nxt;
+      sched_reads_mfma<P == P_FP8 ? 16 : 8, 16>();
       // keep the scheduler from hoisting later slices' reads (registers)
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -596,6 +850,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     Mma<P>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
     cur = nxt;
     take_scales();
+    sched_reads_mfma<P == P_FP8 ? 16 : 8, 16>();
     __builtin_amdgcn_sched_barrier(0);
 
     // stage kt+1 from buffers 1 while stage kt+2 loads into buffers 0 (a
@@ -607,6 +862,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
       else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
       cur = nxt;
+      sched_reads_mfma<P == P_FP8 ? 16 : 8, 16>();
       __builtin_amdgcn_sched_barrier(0);
     }
     stage_store(sA0, sB0);
@@ -615,163 +871,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     Mma<P>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
     cur = nxt;
     take_scales();
+    sched_reads_mfma<P == P_FP8 ? 16 : 8, 16>();
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue ----
-  // acc[i][j][r] is C[row][col] of the wave's block with
-  //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
-  //   col = wn*128 + j*32 + lane%32
-  const int colw = lane & 31;
-  const int rsub = (lane >> 5) * 4;
-  if constexpr (EPI == EPI_SWIGLU) {
-    // B rows of block j: gate f-block (2 wn + j/2) for even j, up for odd j
-    const int64_t ld1 = 2 * (int64_t)p.F;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int f = n0 + (2 * wn + jj) * 32 + colw;
-      if (f >= p.F) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mrow =
-              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-          if (mrow < tc.seg_len) {
-            const int64_t row = tc.seg0 + mrow;
-            const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
-            const float wr = p.w ? p.w[row] : 1.0f;
-            const float a = wr * (g * fast_sigmoid(g)) * u;
-            p.c[row * p.ldc + f] = (uint16_t)f32_to_bf16(a);
-            if (p.c2) {
-              p.c2[row * ld1 + f] = (uint16_t)f32_to_bf16(g);
-              p.c2[row * ld1 + p.F + f] = (uint16_t)f32_to_bf16(u);
-            }
-          }
-        }
-    }
-  } else if constexpr (EPI == EPI_SWIGLU_MX) {
-    // A = w * silu(g) * u in float32, then one E8M0 scale per 32 f columns:
-    // the 32 columns of an f block are the 32 lanes of a half-wave, so the
-    // block amax is a half-wave max.  F % 128 == 0: f blocks are whole.
-    const int64_t ld1 = 2 * (int64_t)p.F;
-    const int64_t lds = p.F / 32;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int fb = n0 + (2 * wn + jj) * 32;   // first f of the block
-      const int f = fb + colw;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mrow =
-              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-          const bool ok = mrow < tc.seg_len;
-          const int64_t row = tc.seg0 + (ok ? mrow : 0);
-          const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
-          const float wr = ok ? (p.w ? p.w[row] : 1.0f) : 0.0f;
-          const float a = wr * (g * fast_sigmoid(g)) * u;
-          uint32_t am = __float_as_uint(a) & 0x7fffffffu;
-#pragma unroll
-          for (int off = 1; off < 32; off <<= 1) {
-            const uint32_t o = (uint32_t)__shfl_xor((int)am, off, 64);
-            am = am > o ? am : o;
-          }
-          const int s = e8m0_exp_from_f32_amax(am);
-          if (ok) {
-            p.cq[row * p.F + f] = (uint8_t)e4m3_from_f32(__float_as_uint(a), s);
-            if (colw == 0) p.cs[row * lds + fb / 32] = (uint8_t)(s + 127);
-            if (p.c) p.c[row * p.ldc + f] = (uint16_t)f32_to_bf16(a);
-            if (p.c2) {
-              p.c2[row * ld1 + f] = (uint16_t)f32_to_bf16(g);
-              p.c2[row * ld1 + p.F + f] = (uint16_t)f32_to_bf16(u);
-            }
-          }
-        }
-    }
-  } else if constexpr (EPI == EPI_STORE) {
-    uint16_t* cbase = p.c;
-    if constexpr (G == RAGGED_K) cbase += (int64_t)tc.e * p.c_es;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + colw;
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mrow =
-              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-          int64_t row;
-          if constexpr (G == RAGGED_M) {
-            if (mrow >= tc.seg_len) continue;
-            row = tc.seg0 + mrow;
-          } else {
-            if (mrow >= p.M) continue;
-            row = mrow;
-          }
-          cbase[row * p.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][r]);
-        }
-    }
-  } else {  // EPI_SWIGLU_BWD: acc = dA[row][f], f = n0 + wn*128 + j*32 + col
-    // the loop's last (unused) fragment reads of stage 0 must finish before
-    // stage 0 becomes the row-sum scratch
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(sA0);  // [2 N-waves][256 rows]
-    const int64_t ld1 = 2 * (int64_t)p.F;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float rs[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rs[r] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = n0 + wn * 128 + j * 32 + colw;
-        const bool fok = f < p.F;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mrow =
-              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-          if (mrow < tc.seg_len && fok) {
-            const int64_t row = tc.seg0 + mrow;
-            const float g = bf16_to_f32(p.h1[row * ld1 + f]);
-            const float u = bf16_to_f32(p.h1[row * ld1 + p.F + f]);
-            const float wr = p.w ? p.w[row] : 1.0f;
-            const float s = fast_sigmoid(g);
-            const float sg = g * s;
-            const float da = acc[i][j][r];
-            const float dg = da * wr * u * (s * (1.0f + g * (1.0f - s)));
-            const float du = da * wr * sg;
-            p.c[row * ld1 + f] = (uint16_t)f32_to_bf16(dg);
-            p.c[row * ld1 + p.F + f] = (uint16_t)f32_to_bf16(du);
-            rs[r] += da * sg * u;
-          }
-        }
-      }
-      if (p.dw_part) {
-        // sum over the 32 columns held by the lanes with the same lane / 32
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = rs[r];
-#pragma unroll
-          for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off, 64);
-          if (colw == 0) {
-            const int tr = wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-            red[wn * 256 + tr] = v;
-          }
-        }
-      }
-    }
-    if (p.dw_part) {
-      // across the 2 N-waves, fixed order
-      __syncthreads();
-      const int mrow = tc.m0 + t;
-      if (mrow < tc.seg_len) {
-        const float s = red[t] + red[256 + t];
-        p.dw_part[(int64_t)tc.nt * p.rows + tc.seg0 + mrow] = s;
-      }
-    }
-  }
+  // every wave is past its last LDS read of the operand stages (and every
+  // direct load has landed) before the stages become epilogue staging
+  __syncthreads();
+  char* wbuf = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
+  epilogue<G, EPI>(p, tc, acc, n0, wm, wn, lane, t, sA0, wbuf);
 }
 
 // Tile prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/BM) * tn.
