@@ -44,10 +44,80 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0 = auto)")
+    ap.add_argument("--write-traffic", nargs=4, metavar="DB",
+                    help="FETCH_SIZE db, WRITE_SIZE db, copy FETCH_SIZE db, "
+                         "copy WRITE_SIZE db (rocprofv3 --pmc outputs of "
+                         "this workload and of --copy-calibration): record "
+                         "the dominant GEMMs' HBM traffic per launch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (the "
                          "reference kernel that scales HBM byte counters)")
     return ap.parse_args()
+
+
+# library kernel name -> template instantiation in profiler kernel names
+KERNEL_SYMBOL = {
+    "gemm_gate_up_swiglu_bf16": "grouped_gemm_kernel<0, 0, 0, 0, 1>",
+    "gemm_down_bf16": "grouped_gemm_kernel<0, 0, 0, 0, 0>",
+    "gemm_gate_up_swiglu_mxfp8": "grouped_gemm_kernel<1, 0, 0, 0, 3>",
+    "gemm_down_mxfp8": "grouped_gemm_kernel<1, 0, 0, 0, 0>",
+}
+
+
+def _pmc_means(db, counter):
+    """kernel name -> mean counter value (KiB) per dispatch."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    acc = {}
+    for name, v in con.execute(
+            "select kernel_name, value from counters_collection where "
+            "counter_name = ?", (counter,)):
+        acc.setdefault(name, []).append(float(v))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(workload, dbs, cmd):
+    fetch_db, write_db, cfetch_db, cwrite_db = dbs
+    fetch = _pmc_means(fetch_db, "FETCH_SIZE")
+    write = _pmc_means(write_db, "WRITE_SIZE")
+    cf = [v for k, v in _pmc_means(cfetch_db, "FETCH_SIZE").items()
+          if "copyBuffer" in k]
+    cw = [v for k, v in _pmc_means(cwrite_db, "WRITE_SIZE").items()
+          if "copyBuffer" in k]
+    if not cf or not cw:
+        raise SystemExit("no copy kernel in the calibration runs")
+    f_fac = (1 << 30) / (cf[0] * 1024.0)
+    w_fac = (1 << 30) / (cw[0] * 1024.0)
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        data = {"records": []}
+    dig = sources_digest()
+    recs = [r for r in data.get("records", [])
+            if r.get("workload") != workload]
+    for kname, sym in KERNEL_SYMBOL.items():
+        fk = [v for k, v in fetch.items() if sym in k]
+        wk = [v for k, v in write.items() if sym in k]
+        if not fk or not wk:
+            continue
+        recs.append({
+            "kernel": kname, "workload": workload, "source_digest": dig,
+            "fetch_kib_per_launch": round(fk[0], 1),
+            "write_kib_per_launch": round(wk[0], 1),
+            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
+            "bytes_per_launch": round(fk[0] * 1024 * f_fac +
+                                      wk[0] * 1024 * w_fac),
+            "command": cmd})
+    data["records"] = recs
+    data["about"] = ("HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE "
+                     "and WRITE_SIZE (separate runs), scaled by the readings "
+                     "of a plain 1 GiB copy (bench.py --copy-calibration); "
+                     "source_digest identifies the kernel sources measured")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(data, fh, indent=1)
+    print(json.dumps(recs[-4:], indent=1))
 
 
 def copy_calibration():
@@ -214,6 +284,71 @@ class Layer:
         return out
 
 
+# library kernels timed in the timed region (names as launched)
+KERNELS = [
+    "route_topk", "permute_index", "permute_gather", "permute_gather_mxfp8",
+    "gemm_gate_up_swiglu_bf16", "gemm_down_bf16", "gemm_gate_up_swiglu_mxfp8",
+    "gemm_down_mxfp8", "mxfp8_quantize_rows", "unpermute",
+    "gemm_dgrad_down_swiglu_bwd", "gemm_dgrad_gate_up", "gemm_wgrad_down",
+    "gemm_wgrad_gate_up", "routing_weight_grad_reduce", "probs_grad",
+    "tile_table",
+]
+# algorithmic flop per launch
+KERNEL_FLOP = {
+    "gemm_gate_up_swiglu_bf16": lambda c: 4.0 * c.rows * c.H * c.F,
+    "gemm_gate_up_swiglu_mxfp8": lambda c: 4.0 * c.rows * c.H * c.F,
+    "gemm_down_bf16": lambda c: 2.0 * c.rows * c.H * c.F,
+    "gemm_down_mxfp8": lambda c: 2.0 * c.rows * c.H * c.F,
+    "gemm_dgrad_down_swiglu_bwd": lambda c: 2.0 * c.rows * c.H * c.F,
+    "gemm_dgrad_gate_up": lambda c: 4.0 * c.rows * c.H * c.F,
+    "gemm_wgrad_down": lambda c: 2.0 * c.rows * c.H * c.F,
+    "gemm_wgrad_gate_up": lambda c: 4.0 * c.rows * c.H * c.F,
+}
+# algorithmic HBM bytes per launch (reads + writes)
+KERNEL_BYTES = {
+    # read x once, write k rows, + topk_w/row_map reads and w_perm writes
+    "permute_gather": lambda c: (1 + c.k) * c.T * c.H * 2.0 + c.rows * 12.0,
+    "permute_gather_mxfp8": lambda c: c.T * c.H * (2.0 + c.k * 1.03125)
+    + c.rows * 12.0,
+    # read k rows, write one, + row_map
+    "unpermute": lambda c: (c.k + 1) * c.T * c.H * 2.0 + c.rows * 4.0,
+    # per call: all weights of one projection; averaged over the two calls
+    "mxfp8_quantize_rows": lambda c: c.E * 3 * c.H * c.F * 3.03125 / 2.0,
+}
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_gemm.json")
+GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_grouped_router_amd",
+                             "csrc", f) for f in
+                ("grouped_gemm.hpp", "gemm_bf16.hip", "gemm_mxfp8.hip")]
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, cfg):
+    """HBM bytes per launch of `kernel` on this workload from the committed
+    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, scaled by the copy
+    calibration), or None when no record matches the current kernel
+    sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            recs = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    dig = sources_digest()
+    for r in recs.get("records", []):
+        if r.get("kernel") == kernel and r.get("workload") == cfg.name and \
+                r.get("source_digest") == dig:
+            return r.get("bytes_per_launch")
+    return None
+
+
 def algorithmic(cfg):
     """Algorithmic work per op (flop or bytes, per launch of that op)."""
     T, H, F, k = cfg.T, cfg.H, cfg.F, cfg.k
@@ -280,6 +415,13 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.write_traffic:
+        write_traffic(args.workload, args.write_traffic,
+                      "rocprofv3 --pmc FETCH_SIZE | WRITE_SIZE "
+                      "--kernel-include-regex grouped_gemm -- python3 "
+                      f"bench.py --workload {args.workload} --steps 1 "
+                      "--warmup 0 --no-cpu-baseline")
+        return
     import torch
     import mixture_experts_grouped_router_amd as m
     from synthetic import CONFIGS, generate_config
@@ -304,6 +446,10 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
+    # every library kernel of the timed region is bracketed by HIP events on
+    # the stream it runs on (the library's own timing facility)
+    m.reset_kernel_timing()
+    m.set_kernel_timing(True)
     K = args.steps
     ev = [[(torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True)) for _ in stages]
@@ -326,6 +472,13 @@ def main():
     per_stage = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1])
                                       for s in range(K)]))
                  for i, (name, _) in enumerate(stages)}
+    m.set_kernel_timing(False)
+    ktimes = {}
+    for name in KERNELS:
+        n, tot = m.kernel_time(name)
+        if n:
+            ktimes[name] = (n, tot / n)
+    m.reset_kernel_timing()
     status = m.check_device_status()
     if status != 0:
         raise RuntimeError(f"device status {status}")
@@ -335,15 +488,29 @@ def main():
     tokens_s = cfg.T / (ms_step * 1e-3)
     work = algorithmic(cfg)
     peak = PEAK_FP8_TFLOPS if cfg.mode == "mxfp8" else PEAK_BF16_TFLOPS
-    dom = "grouped_mlp_fwd"
-    dom_ms = per_stage[dom]
-    ach = work[dom][1] / (dom_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": "moe_grouped_mlp_fwd (grouped gate/up "
-            "GEMM + ScaledSwiGLU epilogue, grouped down GEMM)",
-            "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(ach / peak, 4), "traffic": None,
-            "avg_launch_ms": round(dom_ms, 4),
-            "work_per_launch": f"6*T*k*H*F = {work[dom][1]:.4e} flop"}
+    # dominant kernel: the grouped gate/up GEMM with the ScaledSwiGLU
+    # epilogue; one launch covers all T*k routed rows: 4*T*k*H*F flop
+    dom = "gemm_gate_up_swiglu_" + ("mxfp8" if cfg.mode == "mxfp8" else "bf16")
+    dom_flop = 4.0 * cfg.rows * cfg.H * cfg.F
+    n_dom, dom_ms = ktimes[dom]
+    ach = dom_flop / (dom_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1),
+            "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+            "traffic": traffic_for(dom, cfg),
+            "avg_launch_ms": round(dom_ms, 4), "launches": n_dom,
+            "work_per_launch": f"4*T*k*H*F = {dom_flop:.4e} flop"}
+    kernels = {}
+    for name, (n, ms) in ktimes.items():
+        kd = {"launches": n, "avg_ms": round(ms, 4)}
+        if name in KERNEL_FLOP:
+            f = KERNEL_FLOP[name](cfg)
+            kd["TFLOP/s"] = round(f / (ms * 1e-3) / 1e12, 1)
+            kd["frac_mfma"] = round(f / (ms * 1e-3) / 1e12 / peak, 4)
+        if name in KERNEL_BYTES:
+            b = KERNEL_BYTES[name](cfg)
+            kd["GB/s"] = round(b / (ms * 1e-3) / 1e9, 1)
+            kd["frac_hbm"] = round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        kernels[name] = kd
     stage_rates = {}
     for name, ms in per_stage.items():
         if name in work:
@@ -364,9 +531,12 @@ def main():
         n_tok = args.cpu_tokens
         if n_tok <= 0:
             # about 10-30 s of host work for the oracle (float64 BLAS on
-            # 16 host threads runs the per-expert matmuls at ~0.1 TFLOP/s)
+            # 16 host threads runs the per-expert matmuls at ~0.4 TFLOP/s)
             per_tok = (18.0 if cfg.backward else 6.0) * cfg.k * cfg.H * cfg.F
-            n_tok = max(16, min(cfg.T, int(1.5e12 / per_tok)))
+            # the MXFP8 oracle also quantises every block in numpy (about 10x
+            # the cost per flop)
+            budget = 6e12 if cfg.mode != "mxfp8" else 6e11
+            n_tok = max(16, min(cfg.T, int(budget / per_tok)))
         cpu = cpu_baseline(cfg, d, n_tok)
 
     out = {
@@ -391,6 +561,7 @@ def main():
         "mfma_frac_step": round(tflops / peak, 4),
         "roofline": roof,
         "stages": stage_rates,
+        "kernels": kernels,
         "wall_s_timed": round(wall, 3),
         "cpu_baseline": cpu,
     }

@@ -96,6 +96,23 @@ const char* moe_status_string(moe_status_t status);
 const char* moe_last_error(void);
 
 /* ------------------------------------------------------------------------
+ * Per-kernel timing (a measurement aid; off by default).
+ * moe_ctx_set_kernel_timing(ctx, 1): every kernel the library launches for
+ * this context is bracketed by two HIP events recorded on the launch stream
+ * (the stream passed to the call); 0 switches it off.  Records accumulate
+ * until moe_ctx_reset_kernel_timing.
+ * moe_ctx_kernel_time: waits for the recorded events and returns, for the
+ * kernel called `kernel` (e.g. "gemm_gate_up_swiglu_bf16",
+ * "gemm_down_bf16", "permute_gather", "unpermute"; the names are listed in
+ * the library's sources next to each launch), the number of launches and
+ * their summed duration in milliseconds (0 / 0.0 if none).
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_ctx_set_kernel_timing(moe_ctx_t ctx, int32_t enable);
+moe_status_t moe_ctx_reset_kernel_timing(moe_ctx_t ctx);
+moe_status_t moe_ctx_kernel_time(moe_ctx_t ctx, const char* kernel,
+                                 int64_t* launches, double* total_ms);
+
+/* ------------------------------------------------------------------------
  * moe_route_topk -- router top-k.
  * [PG3, practical-implications paragraph: Top-k routing; PG2, section "Why
  *  dense and MoE models differ": only a small subset of experts is active

@@ -21,7 +21,8 @@ __all__ = [
     "ROWWISE", "COLWISE", "moe_route_topk", "moe_permute", "moe_gather_rows",
     "moe_unpermute", "moe_unpermute_probs_grad", "mxfp8_quantize",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "check_device_status",
-    "mx_segment_ld",
+    "mx_segment_ld", "set_kernel_timing", "reset_kernel_timing",
+    "kernel_time",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,10 @@ _SIGS = {
     "moe_grouped_mlp_bwd_workspace_size": [ctypes.POINTER(_BwdArgs),
                                            ctypes.POINTER(_c_sz)],
     "moe_grouped_mlp_bwd": [_c_p, ctypes.POINTER(_BwdArgs), _c_p],
+    "moe_ctx_set_kernel_timing": [_c_p, _c_i32],
+    "moe_ctx_reset_kernel_timing": [_c_p],
+    "moe_ctx_kernel_time": [_c_p, ctypes.c_char_p, ctypes.POINTER(_c_i64),
+                            ctypes.POINTER(ctypes.c_double)],
 }
 
 _lib = None
@@ -173,6 +178,33 @@ def check_device_status(device=None) -> int:
     if st not in (0, 5):
         _check(st)
     return int(code.value)
+
+
+def set_kernel_timing(enable: bool, device=None) -> None:
+    """Bracket every library kernel launch with HIP events (measurement)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    _check(load_library().moe_ctx_set_kernel_timing(_context(dev),
+                                                    int(bool(enable))))
+
+
+def reset_kernel_timing(device=None) -> None:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    _check(load_library().moe_ctx_reset_kernel_timing(_context(dev)))
+
+
+def kernel_time(name: str, device=None) -> Tuple[int, float]:
+    """(launches, summed milliseconds) of the library kernel `name` since the
+    last reset (waits for the recorded events)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    n = _c_i64(0)
+    ms = ctypes.c_double(0.0)
+    _check(load_library().moe_ctx_kernel_time(_context(dev), name.encode(),
+                                              ctypes.byref(n),
+                                              ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
 
 
 # --------------------------------------------------------------------------

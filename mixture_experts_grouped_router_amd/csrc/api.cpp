@@ -9,11 +9,14 @@
 
 #include "../../include/moe.h"
 #include "kernels.hpp"
+#include "timer.hpp"
 
 struct moe_ctx {
   int device;
   int cu_count;
   int32_t* status;  // device word: first data error
+  bool timing;
+  moe::KernelTimer timer;
 };
 
 namespace {
@@ -61,6 +64,15 @@ moe_status_t check_ctx(moe_ctx_t ctx) {
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Publishes the context's kernel timer to the launch wrappers for the
+// duration of one library call.
+struct TimerGuard {
+  explicit TimerGuard(moe_ctx_t ctx) {
+    moe::tl_timer = (ctx && ctx->timing) ? &ctx->timer : nullptr;
+  }
+  ~TimerGuard() { moe::tl_timer = nullptr; }
+};
 
 }  // namespace
 
@@ -110,6 +122,7 @@ moe_status_t moe_ctx_create(int device, moe_ctx_t* out) {
   c->device = device;
   c->cu_count = prop.multiProcessorCount;
   c->status = status;
+  c->timing = false;
   *out = c;
   return ok();
 }
@@ -140,11 +153,35 @@ moe_status_t moe_ctx_check_device_status(moe_ctx_t ctx, void* stream,
   return ok();
 }
 
+moe_status_t moe_ctx_set_kernel_timing(moe_ctx_t ctx, int32_t enable) {
+  MOE_REQUIRE(ctx != nullptr, MOE_ERR_INVALID_ARG, "null context");
+  ctx->timing = enable != 0;
+  return ok();
+}
+
+moe_status_t moe_ctx_reset_kernel_timing(moe_ctx_t ctx) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  ctx->timer.reset();
+  return ok();
+}
+
+moe_status_t moe_ctx_kernel_time(moe_ctx_t ctx, const char* kernel,
+                                 int64_t* launches, double* total_ms) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(kernel && launches && total_ms, MOE_ERR_INVALID_ARG,
+              "null pointer");
+  return hip_status(ctx->timer.query(kernel, launches, total_ms),
+                    "kernel timing events");
+}
+
 moe_status_t moe_route_topk(moe_ctx_t ctx, const float* logits, int64_t T,
                             int32_t E, int32_t k, int32_t renormalize,
                             int32_t* topk_idx, float* topk_w, void* stream) {
   moe_status_t s = check_ctx(ctx);
   if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
   MOE_REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T < 0");
   MOE_REQUIRE(E >= 1 && k >= 1 && k <= E, MOE_ERR_INVALID_ARG,
               "need 1 <= k <= E (k=%d, E=%d)", k, E);
@@ -177,6 +214,7 @@ moe_status_t moe_permute(moe_ctx_t ctx, const void* x,
                          size_t ws_bytes, void* stream) {
   moe_status_t s = check_ctx(ctx);
   if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
   MOE_REQUIRE(T >= 0 && H >= 1 && E >= 1 && k >= 1 && k <= E,
               MOE_ERR_INVALID_ARG, "bad sizes (T=%lld H=%d E=%d k=%d)",
               (long long)T, H, E, k);
@@ -225,6 +263,7 @@ moe_status_t moe_gather_rows(moe_ctx_t ctx, const void* src,
                              int32_t k, void* dst, void* stream) {
   moe_status_t s = check_ctx(ctx);
   if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
   MOE_REQUIRE(T >= 0 && H >= 1 && k >= 1 && k <= MOE_MAX_TOPK,
               MOE_ERR_INVALID_ARG, "bad sizes");
   MOE_REQUIRE(H % 8 == 0, MOE_ERR_UNSUPPORTED, "H %% 8 != 0");
@@ -243,6 +282,7 @@ moe_status_t moe_unpermute(moe_ctx_t ctx, const void* z_perm,
                            void* stream) {
   moe_status_t s = check_ctx(ctx);
   if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
   MOE_REQUIRE(T >= 0 && H >= 1 && k >= 1 && k <= MOE_MAX_TOPK,
               MOE_ERR_INVALID_ARG, "bad sizes");
   MOE_REQUIRE(H % 8 == 0, MOE_ERR_UNSUPPORTED, "H %% 8 != 0");
@@ -260,6 +300,7 @@ moe_status_t moe_unpermute_probs_grad(moe_ctx_t ctx, const float* dw_perm,
                                       int32_t k, float* dprobs, void* stream) {
   moe_status_t s = check_ctx(ctx);
   if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
   MOE_REQUIRE(T >= 0 && k >= 1, MOE_ERR_INVALID_ARG, "bad sizes");
   if (T == 0) return ok();
   MOE_REQUIRE(dw_perm && row_map && dprobs, MOE_ERR_INVALID_ARG,
@@ -275,6 +316,7 @@ moe_status_t mxfp8_quantize(moe_ctx_t ctx, const void* src, int64_t batch,
                             uint8_t* codes, uint8_t* scales, void* stream) {
   moe_status_t s = check_ctx(ctx);
   if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
   MOE_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0, MOE_ERR_INVALID_ARG,
               "negative size");
   MOE_REQUIRE(axis == MOE_MX_ROWWISE || axis == MOE_MX_COLWISE,
@@ -357,6 +399,7 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
                                  void* stream) {
   moe_status_t s = check_ctx(ctx);
   if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
   MOE_REQUIRE(a != nullptr, MOE_ERR_INVALID_ARG, "null args");
   s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
   if (s != MOE_OK) return s;
@@ -417,6 +460,7 @@ moe_status_t moe_grouped_mlp_bwd(moe_ctx_t ctx, const moe_mlp_bwd_args* a,
                                  void* stream) {
   moe_status_t s = check_ctx(ctx);
   if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
   MOE_REQUIRE(a != nullptr, MOE_ERR_INVALID_ARG, "null args");
   s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
   if (s != MOE_OK) return s;

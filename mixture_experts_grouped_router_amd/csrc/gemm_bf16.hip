@@ -61,6 +61,7 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
                              int32_t* tile_start, hipStream_t stream) {
+  KernelScope ks("tile_table", stream);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
                      offsets, E, tn, tile_start);
   return hipGetLastError();
@@ -117,7 +118,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p1.w = w_perm;
   p1.rows = rows;
   err = launch<P_BF16, KC, KC, RAGGED_M, EPI_SWIGLU>(
-      p1, ragged_m_grid(rows, E, tn1), stream);
+      "gemm_gate_up_swiglu_bf16", p1, ragged_m_grid(rows, E, tn1), stream);
   if (err != hipSuccess) return err;
 
   Params p2{};
@@ -136,7 +137,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p2.c = static_cast<uint16_t*>(z_perm);
   p2.ldc = H;
   p2.rows = rows;
-  return launch<P_BF16, KC, KC, RAGGED_M, EPI_STORE>(p2, ragged_m_grid(rows, E, tn2),
+  return launch<P_BF16, KC, KC, RAGGED_M, EPI_STORE>("gemm_down_bf16", p2, ragged_m_grid(rows, E, tn2),
                                              stream);
 }
 
@@ -191,10 +192,12 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     p.w = w_perm;
     p.dw_part = dw_perm ? part : nullptr;
     p.rows = rows;
-    err = launch<P_BF16, KC, MC, RAGGED_M, EPI_SWIGLU_BWD>(p, ragged_m_grid(rows, E, tnf),
+    err = launch<P_BF16, KC, MC, RAGGED_M, EPI_SWIGLU_BWD>(
+        "gemm_dgrad_down_swiglu_bwd", p, ragged_m_grid(rows, E, tnf),
                                                    stream);
     if (err != hipSuccess) return err;
     if (dw_perm) {
+      KernelScope ks("routing_weight_grad_reduce", stream);
       hipLaunchKernelGGL(reduce_parts_kernel, dim3((unsigned)((rows + 255) / 256)),
                          dim3(256), 0, stream, part, tnf, rows, dw_perm);
     }
@@ -214,7 +217,7 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     q.c = static_cast<uint16_t*>(dx_perm);
     q.ldc = H;
     q.rows = rows;
-    err = launch<P_BF16, KC, MC, RAGGED_M, EPI_STORE>(q, ragged_m_grid(rows, E, tnh),
+    err = launch<P_BF16, KC, MC, RAGGED_M, EPI_STORE>("gemm_dgrad_gate_up", q, ragged_m_grid(rows, E, tnh),
                                               stream);
     if (err != hipSuccess) return err;
   }
@@ -236,7 +239,8 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     p.c_es = (int64_t)H * F;
     p.rows = rows;
     const int grid = ragged_k_grid(E, p.tiles_m, p.tiles_n);
-    err = launch<P_BF16, MC, MC, RAGGED_K, EPI_STORE>(p, grid, stream);
+    err = launch<P_BF16, MC, MC, RAGGED_K, EPI_STORE>("gemm_wgrad_down", p,
+                                                      grid, stream);
     if (err != hipSuccess) return err;
   }
   // wgrad1: dW_gu[e] [2F, H] = dH1_e^T X_e
@@ -257,7 +261,8 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     p.c_es = (int64_t)2 * F * H;
     p.rows = rows;
     const int grid = ragged_k_grid(E, p.tiles_m, p.tiles_n);
-    err = launch<P_BF16, MC, MC, RAGGED_K, EPI_STORE>(p, grid, stream);
+    err = launch<P_BF16, MC, MC, RAGGED_K, EPI_STORE>("gemm_wgrad_gate_up",
+                                                      p, grid, stream);
   }
   return err;
 }

@@ -132,7 +132,7 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p1.w = w_perm;
   p1.rows = rows;
   err = launch<P_FP8, KC, KC, RAGGED_M, EPI_SWIGLU_MX>(
-      p1, ragged_m_grid(rows, E, tn1), stream);
+      "gemm_gate_up_swiglu_mxfp8", p1, ragged_m_grid(rows, E, tn1), stream);
   if (err != hipSuccess) return err;
 
   Params p2{};
@@ -157,7 +157,7 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p2.ldc = H;
   p2.rows = rows;
   return launch<P_FP8, KC, KC, RAGGED_M, EPI_STORE>(
-      p2, ragged_m_grid(rows, E, tn2), stream);
+      "gemm_down_mxfp8", p2, ragged_m_grid(rows, E, tn2), stream);
 }
 
 size_t mlp_bwd_mx_ws_bytes(int, int, int, int64_t) { return 256; }

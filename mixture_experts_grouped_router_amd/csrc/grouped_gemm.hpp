@@ -30,6 +30,7 @@
 // flight on one XCD share activation rows and weight panels in its L2.
 #pragma once
 #include "common.hpp"
+#include "timer.hpp"
 
 namespace moe {
 namespace gg {
@@ -901,8 +902,10 @@ inline int ragged_k_grid(int E, int tiles_m, int tiles_n) {
 }
 
 template <int P, int LA, int LB, int G, int EPI>
-hipError_t launch(const Params& p, int grid, hipStream_t stream) {
+hipError_t launch(const char* name, const Params& p, int grid,
+                  hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
+  KernelScope ks(name, stream);
   hipLaunchKernelGGL((grouped_gemm_kernel<P, LA, LB, G, EPI>), dim3(grid),
                      dim3(kThreads), 0, stream, p);
   return hipGetLastError();

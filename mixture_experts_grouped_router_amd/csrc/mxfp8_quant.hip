@@ -12,6 +12,7 @@
 // passes: 2 bytes read, 1 + 1/32 bytes written per element.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "timer.hpp"
 
 namespace moe {
 namespace {
@@ -169,6 +170,7 @@ hipError_t launch_mx_quant_rows(const void* src, int64_t rows, int64_t cols,
   if (n_chunks == 0) return hipSuccess;
   int64_t blocks = (n_chunks + 255) / 256;
   if (blocks > 65536) blocks = 65536;
+  KernelScope ks("mxfp8_quantize_rows", stream);
   hipLaunchKernelGGL(mx_rows_kernel, dim3((unsigned)blocks), dim3(256), 0,
                      stream, static_cast<const uint4*>(src), n_chunks,
                      reinterpret_cast<uint2*>(codes), scales);
@@ -181,6 +183,7 @@ hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
   if (batch * rows * cols == 0) return hipSuccess;
   const dim3 grid((unsigned)(rows / 32), (unsigned)((cols + 63) / 64),
                   (unsigned)batch);
+  KernelScope ks("mxfp8_quantize_cols", stream);
   hipLaunchKernelGGL(mx_cols_kernel<false>, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(src), rows, cols,
                      (const int32_t*)nullptr, 0, rows, codes, scales);
@@ -195,6 +198,7 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
   // sum_s ceil(n_s / 32) <= rows / 32 + n_seg
   const int64_t tiles = rows / 32 + n_seg;
   const dim3 grid((unsigned)tiles, (unsigned)((cols + 63) / 64), 1);
+  KernelScope ks("mxfp8_quantize_segments", stream);
   hipLaunchKernelGGL(mx_cols_kernel<true>, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(src), rows, cols,
                      seg_offsets, n_seg, ld, codes, scales);

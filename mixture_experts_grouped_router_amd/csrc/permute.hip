@@ -20,6 +20,7 @@
 // the way.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "timer.hpp"
 
 namespace moe {
 
@@ -320,6 +321,7 @@ hipError_t launch_permute_index(const int32_t* topk_idx, int64_t T, int E,
   const int64_t n = T * (int64_t)k;
   const int nblk = (int)((n + kChunk - 1) / kChunk);
   int32_t* cnt = static_cast<int32_t*>(ws);
+  KernelScope ks("permute_index", stream);
   if (nblk > 0)
     hipLaunchKernelGGL(perm_count_kernel, dim3(nblk), dim3(256),
                        E * sizeof(int32_t), stream, topk_idx, n, E, cnt, status);
@@ -336,6 +338,7 @@ hipError_t launch_gather_rows(const void* x, const int32_t* row_map,
                               const float* topk_w, int64_t T, int H, int k,
                               void* x_perm, float* w_perm, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  KernelScope ks("permute_gather", stream);
   hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)T), dim3(256), 0,
                      stream, static_cast<const uint4*>(x), row_map, topk_w, T,
                      H / 8, k, static_cast<uint4*>(x_perm), w_perm);
@@ -347,6 +350,7 @@ hipError_t launch_gather_rows_mx(const void* x, const int32_t* row_map,
                                  uint8_t* codes, uint8_t* scales,
                                  float* w_perm, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  KernelScope ks("permute_gather_mxfp8", stream);
   hipLaunchKernelGGL(gather_rows_mx_kernel, dim3((unsigned)T), dim3(256), 0,
                      stream, static_cast<const uint4*>(x), row_map, topk_w, T,
                      H, k, codes, scales, w_perm);
@@ -357,6 +361,7 @@ hipError_t launch_unpermute(const void* z, const int32_t* row_map,
                             const float* topk_w, int64_t T, int H, int k,
                             void* y, hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  KernelScope ks("unpermute", stream);
   hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)T), dim3(256), 0, stream,
                      static_cast<const uint4*>(z), row_map, topk_w, T, H / 8,
                      k, static_cast<uint4*>(y));
@@ -368,6 +373,7 @@ hipError_t launch_probs_grad(const float* dw_perm, const int32_t* row_map,
                              hipStream_t stream) {
   const int64_t n = T * (int64_t)k;
   if (n == 0) return hipSuccess;
+  KernelScope ks("probs_grad", stream);
   hipLaunchKernelGGL(probs_grad_kernel, dim3((unsigned)((n + 255) / 256)),
                      dim3(256), 0, stream, dw_perm, row_map, n, dprobs);
   return hipGetLastError();

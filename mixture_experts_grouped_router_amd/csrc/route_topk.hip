@@ -12,6 +12,7 @@
 // keeps slot j.  No LDS, no atomics.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "timer.hpp"
 
 namespace moe {
 
@@ -111,6 +112,7 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
   const int tokens_per_block = 4;
   const dim3 grid((unsigned)((T + tokens_per_block - 1) / tokens_per_block));
   const int vpl = (E + 63) / 64;
+  KernelScope ks("route_topk", stream);
 #define MOE_ROUTE_CASE(N)                                                      \
   case N:                                                                      \
     hipLaunchKernelGGL(route_topk_kernel<N>, grid, dim3(256), 0, stream,      \
