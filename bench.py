@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral",
-                    help="mixtral | qwen3 | mixtral_mxfp8 | qwen3_long | tiny")
+                    help="mixtral | qwen3 | mixtral_mxfp8 | "
+                         "mixtral_mxfp8_bwd | qwen3_long | tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0 = auto)")
@@ -171,11 +172,14 @@ class Layer:
         self.idx = e((T, k), i32)
         self.w = e((T, k), f32)
         self.mx = cfg.mode == "mxfp8"
-        # MXFP8: the permute writes E4M3 codes + E8M0 scales of x (fused
-        # quantisation); the weights are quantised from the bf16 masters
-        # inside every grouped-MLP call
-        self.x_perm = e((rows, H), u8 if self.mx else b16)
-        self.x_perm_scale = e((rows, H // 32), u8) if self.mx else None
+        # MXFP8 forward only: the permute writes E4M3 codes + E8M0 scales of
+        # x (fused quantisation).  With a backward pass the bf16 x_perm is
+        # kept for the weight gradient (quantised along tokens there) and
+        # the forward call quantises it row-wise.  The weights are quantised
+        # from the bf16 masters inside every grouped-MLP call.
+        self.mx_codes = self.mx and not cfg.backward
+        self.x_perm = e((rows, H), u8 if self.mx_codes else b16)
+        self.x_perm_scale = e((rows, H // 32), u8) if self.mx_codes else None
         self.w_perm = e(rows, f32)
         self.row_map = e(rows, i32)
         self.src_row = e(rows, i32)
@@ -194,7 +198,8 @@ class Layer:
         fa.E, fa.H, fa.F, fa.rows = E, H, F, rows
         fa.precision = m.PREC_MXFP8 if self.mx else m.PREC_BF16
         fa.x_perm = self.x_perm.data_ptr()
-        fa.x_perm_scale = self.x_perm_scale.data_ptr() if self.mx else None
+        fa.x_perm_scale = self.x_perm_scale.data_ptr() if self.mx_codes \
+            else None
         fa.w_gu, fa.w_dn = self.w_gu.data_ptr(), self.w_dn.data_ptr()
         fa.w_perm = self.w_perm.data_ptr()
         fa.offsets = self.offsets.data_ptr()
@@ -244,8 +249,9 @@ class Layer:
         def permute(st):
             m._check(L.moe_permute(
                 self.ctx, P(self.x), P(self.idx), P(self.w), T, H, E, k,
-                m.PREC_MXFP8 if self.mx else m.PREC_BF16, P(self.x_perm),
-                P(self.x_perm_scale) if self.mx else None, P(self.w_perm),
+                m.PREC_MXFP8 if self.mx_codes else m.PREC_BF16, P(self.x_perm),
+                P(self.x_perm_scale) if self.mx_codes else None,
+                P(self.w_perm),
                 P(self.row_map), P(self.src_row), P(self.split),
                 P(self.offsets), P(self.pws), self.pws.numel(), st))
 
@@ -288,32 +294,54 @@ class Layer:
 KERNELS = [
     "route_topk", "permute_index", "permute_gather", "permute_gather_mxfp8",
     "gemm_gate_up_swiglu_bf16", "gemm_down_bf16", "gemm_gate_up_swiglu_mxfp8",
-    "gemm_down_mxfp8", "mxfp8_quantize_rows", "unpermute",
+    "gemm_down_mxfp8", "mxfp8_quantize_rows", "mxfp8_quantize_cols",
+    "mxfp8_quantize_segments", "unpermute",
     "gemm_dgrad_down_swiglu_bwd", "gemm_dgrad_gate_up", "gemm_wgrad_down",
-    "gemm_wgrad_gate_up", "routing_weight_grad_reduce", "probs_grad",
-    "tile_table",
+    "gemm_wgrad_gate_up", "gemm_dgrad_down_swiglu_bwd_mxfp8",
+    "gemm_dgrad_gate_up_mxfp8", "gemm_wgrad_down_mxfp8",
+    "gemm_wgrad_gate_up_mxfp8", "routing_weight_grad_reduce", "probs_grad",
+    "tile_table", "padded_offsets",
 ]
-# algorithmic flop per launch
+# algorithmic flop per step (each GEMM runs once per step)
+_F4 = lambda c: 4.0 * c.rows * c.H * c.F
+_F2 = lambda c: 2.0 * c.rows * c.H * c.F
 KERNEL_FLOP = {
-    "gemm_gate_up_swiglu_bf16": lambda c: 4.0 * c.rows * c.H * c.F,
-    "gemm_gate_up_swiglu_mxfp8": lambda c: 4.0 * c.rows * c.H * c.F,
-    "gemm_down_bf16": lambda c: 2.0 * c.rows * c.H * c.F,
-    "gemm_down_mxfp8": lambda c: 2.0 * c.rows * c.H * c.F,
-    "gemm_dgrad_down_swiglu_bwd": lambda c: 2.0 * c.rows * c.H * c.F,
-    "gemm_dgrad_gate_up": lambda c: 4.0 * c.rows * c.H * c.F,
-    "gemm_wgrad_down": lambda c: 2.0 * c.rows * c.H * c.F,
-    "gemm_wgrad_gate_up": lambda c: 4.0 * c.rows * c.H * c.F,
+    "gemm_gate_up_swiglu_bf16": _F4, "gemm_gate_up_swiglu_mxfp8": _F4,
+    "gemm_down_bf16": _F2, "gemm_down_mxfp8": _F2,
+    "gemm_dgrad_down_swiglu_bwd": _F2, "gemm_dgrad_gate_up": _F4,
+    "gemm_wgrad_down": _F2, "gemm_wgrad_gate_up": _F4,
+    "gemm_dgrad_down_swiglu_bwd_mxfp8": _F2, "gemm_dgrad_gate_up_mxfp8": _F4,
+    "gemm_wgrad_down_mxfp8": _F2, "gemm_wgrad_gate_up_mxfp8": _F4,
 }
-# algorithmic HBM bytes per launch (reads + writes)
+MX_BYTES = 2.0 + 1.0 + 1.0 / 32   # bf16 read, E4M3 code + E8M0/32 written
+
+
+def _mx_rows_elems(c):
+    """Values quantised row-wise per step: both weight tensors in the
+    forward; with a backward pass also x_perm (forward), dZ and dH1."""
+    n = c.E * 3.0 * c.H * c.F
+    if c.backward:
+        n += c.rows * c.H + c.rows * c.H + c.rows * 2.0 * c.F
+    return n
+
+
+# algorithmic HBM bytes per step (reads + writes)
 KERNEL_BYTES = {
-    # read x once, write k rows, + topk_w/row_map reads and w_perm writes
-    "permute_gather": lambda c: (1 + c.k) * c.T * c.H * 2.0 + c.rows * 12.0,
+    # read x once, write k rows, + topk_w/row_map reads and w_perm writes;
+    # with a backward pass dY is gathered the same way
+    "permute_gather": lambda c: (2 if c.backward else 1) * (
+        (1 + c.k) * c.T * c.H * 2.0 + c.rows * 12.0),
     "permute_gather_mxfp8": lambda c: c.T * c.H * (2.0 + c.k * 1.03125)
     + c.rows * 12.0,
-    # read k rows, write one, + row_map
-    "unpermute": lambda c: (c.k + 1) * c.T * c.H * 2.0 + c.rows * 4.0,
-    # per call: all weights of one projection; averaged over the two calls
-    "mxfp8_quantize_rows": lambda c: c.E * 3 * c.H * c.F * 3.03125 / 2.0,
+    # read k rows, write one, + row_map (forward y, backward dx)
+    "unpermute": lambda c: (2 if c.backward else 1) * (
+        (c.k + 1) * c.T * c.H * 2.0 + c.rows * 4.0),
+    "mxfp8_quantize_rows": lambda c: _mx_rows_elems(c) * MX_BYTES,
+    # backward: both weight tensors along their other dimension
+    "mxfp8_quantize_cols": lambda c: c.E * 3.0 * c.H * c.F * MX_BYTES,
+    # backward: dZ, A, dH1, X along tokens (padding not counted)
+    "mxfp8_quantize_segments": lambda c: c.rows * (2.0 * c.H + 3.0 * c.F)
+    * MX_BYTES,
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_gemm.json")
@@ -366,9 +394,14 @@ def algorithmic(cfg):
 
 
 def cpu_baseline(cfg, d, n_tokens):
-    """The oracle as it stands, timed on the host on the first n_tokens of
-    the same workload (full layer: route, permute, per-expert MLP in float64,
-    combine)."""
+    """The oracle as it stands, timed on the host on a bounded sample of the
+    same workload.  bf16: the first n_tokens, whole layer (route, permute,
+    per-expert MLP in float64, combine).  MXFP8 (whose oracle quantises every
+    block in numpy): the first n_tokens are routed and permuted, then the
+    MLP of expert 0 alone on its rows, restricted to FFN columns [0, Fs)
+    (gate and up rows and down columns of those f; the MLP is a sum of such
+    column slices, and 32-aligned slices keep every quantisation block
+    whole)."""
     from oracle import moe_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -378,31 +411,42 @@ def cpu_baseline(cfg, d, n_tokens):
         threads = os.cpu_count() or 1
     x = d["x"][:n_tokens]
     lg = d["logits"][:n_tokens]
+    passes = "fwd+bwd" if cfg.backward else "fwd"
+    per_flop = 6.0 + (12.0 if cfg.backward else 0.0)
     t0 = time.perf_counter()
-    if cfg.backward:
-        O.layer_bwd(x, lg, d["w_gu"], d["w_dn"], d["dy"][:n_tokens], cfg.k)
-    elif cfg.mode == "mxfp8":
-        E = d["w_gu"].shape[0]
-        idx, w = O.route_topk(lg, cfg.k)
-        mp = O.permute_index(idx, E)
-        z = O.grouped_mlp_fwd_mxfp8(O.permute_rows(x, mp["src_row"], cfg.k),
-                                    d["w_gu"], d["w_dn"],
-                                    O.permute_weights(w, mp["src_row"]),
-                                    mp["offsets"])["z"]
-        O.unpermute(z, mp["row_map"], cfg.k)
+    if cfg.mode != "mxfp8":
+        if cfg.backward:
+            O.layer_bwd(x, lg, d["w_gu"], d["w_dn"], d["dy"][:n_tokens],
+                        cfg.k)
+        else:
+            O.layer_fwd(x, lg, d["w_gu"], d["w_dn"], cfg.k)
+        flop = per_flop * n_tokens * cfg.k * cfg.H * cfg.F
+        what = (f"first {n_tokens} of {cfg.T} tokens of the {cfg.name} "
+                f"workload, whole layer {passes} in float64 numpy")
     else:
-        O.layer_fwd(x, lg, d["w_gu"], d["w_dn"], cfg.k)
+        F, Fs = cfg.F, min(cfg.F, 3584 if cfg.backward else 7168)
+        idx, w = O.route_topk(lg, cfg.k)
+        mp = O.permute_index(idx, d["w_gu"].shape[0])
+        lo, hi = int(mp["offsets"][0]), int(mp["offsets"][1])
+        sr = mp["src_row"][lo:hi]
+        xp = O.permute_rows(x, sr, cfg.k)
+        wp = O.permute_weights(w, sr)
+        off = np.array([0, hi - lo], dtype=np.int32)
+        wgu = np.concatenate([d["w_gu"][0, :Fs], d["w_gu"][0, F:F + Fs]])[None]
+        wdn = np.ascontiguousarray(d["w_dn"][0][:, :Fs])[None]
+        O.grouped_mlp_fwd_mxfp8(xp, wgu, wdn, wp, off)
+        if cfg.backward:
+            dz = O.gather_rows(d["dy"][:n_tokens], sr, cfg.k)
+            O.grouped_mlp_bwd_mxfp8(dz, xp, wgu, wdn, wp, off)
+        flop = per_flop * (hi - lo) * cfg.H * Fs
+        what = (f"MXFP8 MLP {passes} (quantisation included) of expert 0 "
+                f"on its {hi - lo} rows among the first {n_tokens} of "
+                f"{cfg.T} tokens of the {cfg.name} workload, FFN columns "
+                f"[0, {Fs}) of {F}, float64 numpy")
     dt = time.perf_counter() - t0
-    flop = (6.0 + (12.0 if cfg.backward else 0.0)) * n_tokens * cfg.k * \
-        cfg.H * cfg.F
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": (f"first {n_tokens} of {cfg.T} tokens of the "
-                       f"{cfg.name} workload, whole layer "
-                       f"{'fwd+bwd' if cfg.backward else 'fwd'} in float64 "
-                       f"numpy{' (MXFP8 quantisation included)' if cfg.mode == 'mxfp8' else ''}"
-                       f" ({dt:.1f} s wall)"),
-            "tokens_per_s": n_tokens / dt, "seconds": dt}
+            "kind": "oracle", "sample": f"{what} ({dt:.1f} s wall)",
+            "seconds": dt}
 
 
 def main():
@@ -473,11 +517,11 @@ def main():
                                       for s in range(K)]))
                  for i, (name, _) in enumerate(stages)}
     m.set_kernel_timing(False)
-    ktimes = {}
+    ktimes = {}      # name -> (launches, average ms, ms per step)
     for name in KERNELS:
         n, tot = m.kernel_time(name)
         if n:
-            ktimes[name] = (n, tot / n)
+            ktimes[name] = (n, tot / n, tot / K)
     m.reset_kernel_timing()
     status = m.check_device_status()
     if status != 0:
@@ -492,7 +536,7 @@ def main():
     # epilogue; one launch covers all T*k routed rows: 4*T*k*H*F flop
     dom = "gemm_gate_up_swiglu_" + ("mxfp8" if cfg.mode == "mxfp8" else "bf16")
     dom_flop = 4.0 * cfg.rows * cfg.H * cfg.F
-    n_dom, dom_ms = ktimes[dom]
+    n_dom, dom_ms, _ = ktimes[dom]
     ach = dom_flop / (dom_ms * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1),
             "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
@@ -500,16 +544,18 @@ def main():
             "avg_launch_ms": round(dom_ms, 4), "launches": n_dom,
             "work_per_launch": f"4*T*k*H*F = {dom_flop:.4e} flop"}
     kernels = {}
-    for name, (n, ms) in ktimes.items():
-        kd = {"launches": n, "avg_ms": round(ms, 4)}
+    for name, (n, ms, ms_s) in ktimes.items():
+        # rates from the kernel's time per step and its work per step
+        kd = {"launches": n, "avg_ms": round(ms, 4), "ms_per_step":
+              round(ms_s, 4)}
         if name in KERNEL_FLOP:
             f = KERNEL_FLOP[name](cfg)
-            kd["TFLOP/s"] = round(f / (ms * 1e-3) / 1e12, 1)
-            kd["frac_mfma"] = round(f / (ms * 1e-3) / 1e12 / peak, 4)
+            kd["TFLOP/s"] = round(f / (ms_s * 1e-3) / 1e12, 1)
+            kd["frac_mfma"] = round(f / (ms_s * 1e-3) / 1e12 / peak, 4)
         if name in KERNEL_BYTES:
             b = KERNEL_BYTES[name](cfg)
-            kd["GB/s"] = round(b / (ms * 1e-3) / 1e9, 1)
-            kd["frac_hbm"] = round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            kd["GB/s"] = round(b / (ms_s * 1e-3) / 1e9, 1)
+            kd["frac_hbm"] = round(b / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         kernels[name] = kd
     stage_rates = {}
     for name, ms in per_stage.items():
@@ -533,10 +579,9 @@ def main():
             # about 10-30 s of host work for the oracle (float64 BLAS on
             # 16 host threads runs the per-expert matmuls at ~0.4 TFLOP/s)
             per_tok = (18.0 if cfg.backward else 6.0) * cfg.k * cfg.H * cfg.F
-            # the MXFP8 oracle also quantises every block in numpy (about 10x
-            # the cost per flop)
-            budget = 6e12 if cfg.mode != "mxfp8" else 6e11
-            n_tok = max(16, min(cfg.T, int(budget / per_tok)))
+            n_tok = max(16, min(cfg.T, int(6e12 / per_tok)))
+            if cfg.mode == "mxfp8":   # one expert, one FFN slice (above)
+                n_tok = min(cfg.T, 8192)
         cpu = cpu_baseline(cfg, d, n_tok)
 
     out = {

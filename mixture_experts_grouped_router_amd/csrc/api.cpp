@@ -348,7 +348,8 @@ moe_status_t mxfp8_quantize(moe_ctx_t ctx, const void* src, int64_t batch,
               "1 <= n_seg <= %d", MOE_MAX_EXPERTS);
   const int64_t ld = (rows + 32 * (int64_t)n_seg + 31) / 32 * 32;
   return hip_status(moe::launch_mx_quant_segments(src, rows, cols, seg_offsets,
-                                                  n_seg, ld, codes, scales, st),
+                                                  n_seg, 32, ld, codes, scales,
+                                                  st),
                     "mxfp8 segments");
 }
 
@@ -423,7 +424,8 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
                   aligned16(a->w_dn_q) && aligned16(a->z_perm),
               MOE_ERR_UNSUPPORTED, "operands must be 16-byte aligned");
   size_t need = 0;
-  moe_grouped_mlp_fwd_workspace_size(a, &need);
+  s = moe_grouped_mlp_fwd_workspace_size(a, &need);
+  if (s != MOE_OK) return s;
   MOE_REQUIRE(a->ws != nullptr && a->ws_bytes >= need, MOE_ERR_WORKSPACE,
               "grouped_mlp_fwd workspace needs %zu bytes", need);
   hipError_t e;
@@ -449,6 +451,14 @@ moe_status_t moe_grouped_mlp_bwd_workspace_size(const moe_mlp_bwd_args* a,
   MOE_REQUIRE(a && bytes, MOE_ERR_INVALID_ARG, "null pointer");
   moe_status_t s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
   if (s != MOE_OK) return s;
+  if (a->precision == MOE_PREC_MXFP8_E4M3) {
+    // token-direction operands [max(H, 2F)][rows + 128 E (+128)] are
+    // addressed with 32-bit byte offsets
+    const int64_t widest = (a->H > 2 * a->F ? a->H : 2 * (int64_t)a->F) + 256;
+    const int64_t ld = a->rows + 128 * (int64_t)a->E + 128;
+    MOE_REQUIRE(widest * ld < ((int64_t)1 << 32), MOE_ERR_UNSUPPORTED,
+                "tensor too large for the MXFP8 weight-gradient operands");
+  }
   if (a->precision == MOE_PREC_BF16)
     *bytes = moe::mlp_bwd_bf16_ws_bytes(a->E, a->H, a->F, a->rows);
   else
@@ -474,7 +484,8 @@ moe_status_t moe_grouped_mlp_bwd(moe_ctx_t ctx, const moe_mlp_bwd_args* a,
                   a->rows == 0,
               MOE_ERR_INVALID_ARG, "dw_perm needs w_perm");
   size_t need = 0;
-  moe_grouped_mlp_bwd_workspace_size(a, &need);
+  s = moe_grouped_mlp_bwd_workspace_size(a, &need);
+  if (s != MOE_OK) return s;
   MOE_REQUIRE(a->ws != nullptr && a->ws_bytes >= need, MOE_ERR_WORKSPACE,
               "grouped_mlp_bwd workspace needs %zu bytes", need);
   hipError_t e;

@@ -15,15 +15,17 @@
 namespace moe {
 namespace gg {
 
-// Tile prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/BM) * tn.
+// Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn.
+// With unit = BM it counts GEMM tiles; with unit = tn = P it gives the
+// offsets of segments padded to multiples of P.
 __global__ __launch_bounds__(1024) void tile_table_kernel(
-    const int32_t* __restrict__ offsets, int E, int tn,
+    const int32_t* __restrict__ offsets, int E, int unit, int tn,
     int32_t* __restrict__ tile_start) {
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
   const int lane = e & 63, wid = e >> 6;
   int32_t v = 0;
-  if (e < E) v = ((offsets[e + 1] - offsets[e] + BM - 1) / BM) * tn;
+  if (e < E) v = ((offsets[e + 1] - offsets[e] + unit - 1) / unit) * tn;
   int32_t incl = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -63,7 +65,15 @@ hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
                              int32_t* tile_start, hipStream_t stream) {
   KernelScope ks("tile_table", stream);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
-                     offsets, E, tn, tile_start);
+                     offsets, E, BM, tn, tile_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_padded_offsets(const int32_t* offsets, int E, int pad,
+                                 int32_t* poff, hipStream_t stream) {
+  KernelScope ks("padded_offsets", stream);
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
+                     offsets, E, pad, pad, poff);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@
 //     -> epilogue: ScaledSwiGLU x routing weight in float32, then row-wise
 //        MXFP8 quantisation of A along F (one half-wave = one block of 32)
 //   A codes  x  W_dn codes -> scaled-MFMA grouped GEMM -> bf16 Z
-// Kernel: grouped_gemm.hpp.
+// Backward: below.  Kernel: grouped_gemm.hpp.
 #include "grouped_gemm.hpp"
 #include "kernels.hpp"
 
@@ -160,12 +160,241 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
       "gemm_down_mxfp8", p2, ragged_m_grid(rows, E, tn2), stream);
 }
 
-size_t mlp_bwd_mx_ws_bytes(int, int, int, int64_t) { return 256; }
-hipError_t launch_mlp_bwd_mx(int, int, int, int64_t, const void*, const void*,
-                             const void*, const float*, const int32_t*,
-                             const void*, const void*, const void*, void*,
-                             void*, void*, float*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+// ---- backward ----------------------------------------------------------------
+// Every GEMM operand is quantised along that GEMM's K:
+//   dgrad2  dA  = Q_H(dZ) Q_H(W_dn)     dZ row-wise, W_dn [H, F] blocks along H
+//   dgrad1  dX  = Q_2F(dH1) Q_2F(W_gu)  dH1 row-wise, W_gu [2F, H] along 2F
+//   wgrad2  dW_dn = Q_tok(dZ)^T Q_tok(A)
+//   wgrad1  dW_gu = Q_tok(dH1)^T Q_tok(X)
+// Token-direction blocks restart at each expert's first row and the last one
+// is zero-padded.  Here each expert's token range is padded to whole K steps
+// of the GEMM (128): the extra blocks are all zero, so the products are those
+// of the 32-padded layout.  The SwiGLU backward runs in float32 in the dgrad2
+// epilogue, which writes dH1 in bf16; dH1 is quantised from that bf16 copy.
+namespace {
+
+constexpr int kTokPad = 128;   // token segments padded to one K step
+
+struct MxBwdWs {
+  int32_t* ts_f;   // tile prefix, N = F
+  int32_t* ts_h;   // tile prefix, N = H
+  int32_t* poff;   // padded token offsets [E+1]
+  uint16_t* dh1;   // bf16 [rows, 2F]
+  float* part;     // dw partial sums [tiles along F][rows]
+  uint8_t *dzq, *dzs;      // dZ row-wise [rows, H]
+  uint8_t *wdq, *wds;      // W_dn blocks along H: [E, F, H]
+  uint8_t *wgq, *wgs;      // W_gu blocks along 2F: [E, H, 2F]
+  uint8_t *hq, *hs;        // dH1 row-wise [rows, 2F]
+  uint8_t *dzt, *dzts;     // dZ token-wise [H, ld]
+  uint8_t *at, *ats;       // A token-wise [F, ld]
+  uint8_t *ht, *hts;       // dH1 token-wise [2F, ld]
+  uint8_t *xt, *xts;       // X token-wise [H, ld]
+  int64_t ld;              // padded token columns
+  size_t bytes;
+};
+
+int64_t tok_ld(int64_t rows, int E) {
+  // sum_e ceil(n_e / 128) * 128 <= rows + 127 E
+  return (rows + (int64_t)kTokPad * E + kTokPad - 1) / kTokPad * kTokPad;
+}
+
+MxBwdWs carve_bwd(void* base, int E, int H, int F, int64_t rows) {
+  MxBwdWs w{};
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* q = p ? p + off : nullptr;
+    off += align256(n);
+    return q;
+  };
+  auto take8 = [&](size_t n) { return reinterpret_cast<uint8_t*>(take(n)); };
+  const int tnf = (F + BN - 1) / BN;
+  const size_t F2 = 2 * (size_t)F;
+  w.ld = tok_ld(rows, E);
+  const size_t ld = (size_t)w.ld;
+  w.ts_f = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  w.ts_h = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  w.poff = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  w.dh1 = reinterpret_cast<uint16_t*>(take((size_t)rows * F2 * 2));
+  w.part = reinterpret_cast<float*>(take((size_t)tnf * rows * 4));
+  w.dzq = take8((size_t)rows * H);
+  w.dzs = take8((size_t)rows * H / 32);
+  w.wdq = take8((size_t)E * H * F);
+  w.wds = take8((size_t)E * H * F / 32);
+  w.wgq = take8((size_t)E * F2 * H);
+  w.wgs = take8((size_t)E * F2 * H / 32);
+  w.hq = take8((size_t)rows * F2);
+  w.hs = take8((size_t)rows * F2 / 32);
+  w.dzt = take8((size_t)H * ld);
+  w.dzts = take8((size_t)H * ld / 32);
+  w.at = take8((size_t)F * ld);
+  w.ats = take8((size_t)F * ld / 32);
+  w.ht = take8(F2 * ld);
+  w.hts = take8(F2 * ld / 32);
+  w.xt = take8((size_t)H * ld);
+  w.xts = take8((size_t)H * ld / 32);
+  w.bytes = off;
+  return w;
+}
+
+// dw_perm[r] = sum over N tiles (ascending) of the partial row sums.
+__global__ __launch_bounds__(256) void mx_reduce_parts_kernel(
+    const float* __restrict__ part, int nparts, int64_t rows,
+    float* __restrict__ out) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  float s = 0.0f;
+  for (int i = 0; i < nparts; ++i) s += part[(int64_t)i * rows + r];
+  out[r] = s;
+}
+
+// Token-direction GEMM dW[e] [M, N] = sum over the expert's padded tokens of
+// At[m][tok] Bt[n][tok] (both quantised along tokens).
+hipError_t wgrad_mx(const char* name, int E, int M, int N, int64_t ld,
+                    const int32_t* poff, const uint8_t* aq, const uint8_t* as,
+                    const uint8_t* bq, const uint8_t* bs, void* dw,
+                    hipStream_t stream) {
+  Params p{};
+  p.a = reinterpret_cast<const char*>(aq);
+  p.lda = ld;
+  p.sa = as;
+  p.ldsa = ld / 32;
+  p.b = reinterpret_cast<const char*>(bq);
+  p.ldb = ld;
+  p.sb = bs;
+  p.ldsb = ld / 32;
+  p.b_rows = N;
+  p.M = M;
+  p.N = N;
+  p.E = E;
+  p.offsets = poff;
+  p.tiles_m = (M + BM - 1) / BM;
+  p.tiles_n = (N + BN - 1) / BN;
+  p.c = static_cast<uint16_t*>(dw);
+  p.ldc = N;
+  p.c_es = (int64_t)M * N;
+  return launch<P_FP8, KC, KC, RAGGED_K, EPI_STORE>(
+      name, p, ragged_k_grid(E, p.tiles_m, p.tiles_n), stream);
+}
+
+}  // namespace
+
+size_t mlp_bwd_mx_ws_bytes(int E, int H, int F, int64_t rows) {
+  return carve_bwd(nullptr, E, H, F, rows).bytes;
+}
+
+hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
+                             const void* x_perm, const void* w_gu,
+                             const void* w_dn, const float* w_perm,
+                             const int32_t* offsets, const void* h1_save,
+                             const void* a_save, const void* dz_perm,
+                             void* dx_perm, void* dw_gu, void* dw_dn,
+                             float* dw_perm, void* ws, hipStream_t stream) {
+  MxBwdWs w = carve_bwd(ws, E, H, F, rows);
+  const int tnf = (F + BN - 1) / BN;
+  const int tnh = (H + BN - 1) / BN;
+  const int F2 = 2 * F;
+  hipError_t err = launch_padded_offsets(offsets, E, kTokPad, w.poff, stream);
+  if (rows > 0) {
+    if (err == hipSuccess) err = launch_tile_table(offsets, E, tnf, w.ts_f, stream);
+    if (err == hipSuccess) err = launch_tile_table(offsets, E, tnh, w.ts_h, stream);
+    // operands of the two dgrad GEMMs
+    if (err == hipSuccess)
+      err = launch_mx_quant_rows(dz_perm, rows, H, w.dzq, w.dzs, stream);
+    if (err == hipSuccess)
+      err = launch_mx_quant_cols(w_dn, E, H, F, w.wdq, w.wds, stream);
+    if (err == hipSuccess)
+      err = launch_mx_quant_cols(w_gu, E, F2, H, w.wgq, w.wgs, stream);
+    if (err != hipSuccess) return err;
+
+    // dgrad2 + SwiGLU backward: dA = dZ W_dn[e]; B = W_dn[e]^T [F, H]
+    Params p{};
+    p.a = reinterpret_cast<const char*>(w.dzq);
+    p.lda = H;
+    p.sa = w.dzs;
+    p.ldsa = H / 32;
+    p.b = reinterpret_cast<const char*>(w.wdq);
+    p.ldb = H;
+    p.b_es = (int64_t)F * H;
+    p.sb = w.wds;
+    p.ldsb = H / 32;
+    p.sb_es = (int64_t)F * H / 32;
+    p.b_rows = F;
+    p.N = F;
+    p.K = H;
+    p.F = F;
+    p.E = E;
+    p.offsets = offsets;
+    p.tile_start = w.ts_f;
+    p.tiles_n = tnf;
+    p.c = w.dh1;
+    p.h1 = static_cast<const uint16_t*>(h1_save);
+    p.w = w_perm;
+    p.dw_part = dw_perm ? w.part : nullptr;
+    p.rows = rows;
+    err = launch<P_FP8, KC, KC, RAGGED_M, EPI_SWIGLU_BWD>(
+        "gemm_dgrad_down_swiglu_bwd_mxfp8", p, ragged_m_grid(rows, E, tnf),
+        stream);
+    if (err != hipSuccess) return err;
+    if (dw_perm) {
+      KernelScope ks("routing_weight_grad_reduce", stream);
+      hipLaunchKernelGGL(mx_reduce_parts_kernel,
+                         dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                         stream, w.part, tnf, rows, dw_perm);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+
+    // dgrad1: dX = dH1 W_gu[e]; B = W_gu[e]^T [H, 2F]
+    err = launch_mx_quant_rows(w.dh1, rows, F2, w.hq, w.hs, stream);
+    if (err != hipSuccess) return err;
+    Params q{};
+    q.a = reinterpret_cast<const char*>(w.hq);
+    q.lda = F2;
+    q.sa = w.hs;
+    q.ldsa = F2 / 32;
+    q.b = reinterpret_cast<const char*>(w.wgq);
+    q.ldb = F2;
+    q.b_es = (int64_t)H * F2;
+    q.sb = w.wgs;
+    q.ldsb = F2 / 32;
+    q.sb_es = (int64_t)H * F2 / 32;
+    q.b_rows = H;
+    q.N = H;
+    q.K = F2;
+    q.E = E;
+    q.offsets = offsets;
+    q.tile_start = w.ts_h;
+    q.tiles_n = tnh;
+    q.c = static_cast<uint16_t*>(dx_perm);
+    q.ldc = H;
+    q.rows = rows;
+    err = launch<P_FP8, KC, KC, RAGGED_M, EPI_STORE>(
+        "gemm_dgrad_gate_up_mxfp8", q, ragged_m_grid(rows, E, tnh), stream);
+    if (err != hipSuccess) return err;
+
+    // token-direction operands of the two wgrad GEMMs
+    err = launch_mx_quant_segments(dz_perm, rows, H, offsets, E, kTokPad,
+                                   w.ld, w.dzt, w.dzts, stream);
+    if (err == hipSuccess)
+      err = launch_mx_quant_segments(a_save, rows, F, offsets, E, kTokPad,
+                                     w.ld, w.at, w.ats, stream);
+    if (err == hipSuccess)
+      err = launch_mx_quant_segments(w.dh1, rows, F2, offsets, E, kTokPad,
+                                     w.ld, w.ht, w.hts, stream);
+    if (err == hipSuccess)
+      err = launch_mx_quant_segments(x_perm, rows, H, offsets, E, kTokPad,
+                                     w.ld, w.xt, w.xts, stream);
+  }
+  if (err != hipSuccess) return err;
+  // wgrad: every expert gets a tile set; K = its padded token count (0 for
+  // an expert without rows, whose weight gradient is then stored as zeros)
+  err = wgrad_mx("gemm_wgrad_down_mxfp8", E, H, F, w.ld, w.poff, w.dzt,
+                 w.dzts, w.at, w.ats, dw_dn, stream);
+  if (err == hipSuccess)
+    err = wgrad_mx("gemm_wgrad_gate_up_mxfp8", E, F2, H, w.ld, w.poff, w.ht,
+                   w.hts, w.xt, w.xts, dw_gu, stream);
+  return err;
 }
 
 }  // namespace moe

@@ -694,6 +694,10 @@ template <int P, int LA, int LB, int G, int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   static_assert(P == P_BF16 || (LA == KC && LB == KC),
                 "MXFP8 operands are K-contiguous");
+  // RAGGED_K with K-contiguous operands needs every expert's K range padded
+  // to whole K steps (the MXFP8 token-direction layout)
+  static_assert(G == RAGGED_M || P == P_FP8 || (LA == MC && LB == MC),
+                "bf16 RAGGED_K operands are MN-contiguous");
   using Fr = Frags<P>;
   constexpr int kSl = Fr::kSlices;
   constexpr int kElemBytes = P == P_FP8 ? 1 : 2;
@@ -729,9 +733,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   const int q = 8 * wave + (lane >> 3);   // direct-load row inside 32 rows
   const int cl = (lane & 7) ^ swz32(q);   // its logical chunk
   if constexpr (LA == KC) {
-    // RAGGED_M rows seg0 + m0 + r, clamped to the expert's last row
-    da.base = p.a + (int64_t)tc.seg0 * p.lda;
-    da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda;
+    if constexpr (G == RAGGED_M) {
+      // rows seg0 + m0 + r; rows past the expert's last read as zeros
+      da.base = p.a + (int64_t)tc.seg0 * p.lda;
+      da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda;
+    } else {
+      // A [M][K]: the expert's K range starts at element seg0 of every row
+      // (a multiple of the K step); rows past M read as zeros
+      const uint32_t kofs = (uint32_t)tc.seg0 * kElemBytes;
+      da.base = p.a + kofs;
+      da.rec = (uint32_t)p.M * (uint32_t)p.lda - kofs;
+    }
     da.ld = p.lda;
     da.q = q;
     da.cl = cl;
@@ -746,8 +758,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   }
   const char* bexp = p.b + (int64_t)tc.e * p.b_es;
   if constexpr (LB == KC) {
-    db.base = bexp;
-    db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb;
+    if constexpr (G == RAGGED_M) {
+      db.base = bexp;
+      db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb;
+    } else {
+      // B [N][K], same K range as A
+      const uint32_t kofs = (uint32_t)tc.seg0 * kElemBytes;
+      db.base = p.b + kofs;
+      db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb - kofs;
+    }
     db.ld = p.ldb;
     db.q = q;
     db.cl = cl;
@@ -766,8 +785,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // byte selector for v_perm: lane group g takes scale bytes (g, 2 + g)
   const uint32_t sel = (lane >> 5) ? 0x0c0c0301u : 0x0c0c0200u;
   if constexpr (P == P_FP8) {
-    ms.a = p.sa + (int64_t)tc.seg0 * p.ldsa;
-    ms.b = p.sb + (int64_t)tc.e * p.sb_es;
+    if constexpr (G == RAGGED_M) {
+      ms.a = p.sa + (int64_t)tc.seg0 * p.ldsa;
+      ms.b = p.sb + (int64_t)tc.e * p.sb_es;
+    } else {   // K blocks of the expert's range
+      ms.a = p.sa + tc.seg0 / 32;
+      ms.b = p.sb + tc.seg0 / 32;
+    }
     KcDirect<EPI, true> m;   // B row mapping of the lane's 32-row blocks
     m.q = lane & 31;
     m.n0 = n0;
@@ -776,7 +800,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ra = min(tc.m0 + wm * 128 + 32 * i + (lane & 31),
-                         tc.seg_len - 1);
+                         (G == RAGGED_M ? tc.seg_len : p.M) - 1);
       ms.oa[i] = (uint32_t)ra * (uint32_t)p.ldsa;
       // B tile row wn*128 + 32 i + lane%32 is direct-load block 4 wn + i
       ms.ob[i] = (uint32_t)m.row(4 * wn + i) * (uint32_t)p.ldsb;
@@ -883,9 +907,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   epilogue<G, EPI>(p, tc, acc, n0, wm, wn, lane, t, sA0, wbuf);
 }
 
-// Tile prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/BM) * tn.
+// Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn.
 __global__ __launch_bounds__(1024) void tile_table_kernel(
-    const int32_t* __restrict__ offsets, int E, int tn,
+    const int32_t* __restrict__ offsets, int E, int unit, int tn,
     int32_t* __restrict__ tile_start);
 
 // Grid for a RAGGED_M launch: sum_e ceil(M_e / BM) <= rows / BM + E tiles
@@ -913,6 +937,9 @@ hipError_t launch(const char* name, const Params& p, int grid,
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
                              int32_t* tile_start, hipStream_t stream);
+// poff[e] = sum_{e' < e} ceil(M_e' / pad) * pad, poff[E] the total
+hipError_t launch_padded_offsets(const int32_t* offsets, int E, int pad,
+                                 int32_t* poff, hipStream_t stream);
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

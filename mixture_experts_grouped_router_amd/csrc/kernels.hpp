@@ -38,10 +38,12 @@ hipError_t launch_mx_quant_rows(const void* src, int64_t rows, int64_t cols,
 hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
                                 int64_t cols, uint8_t* codes, uint8_t* scales,
                                 hipStream_t stream);
+// pad: segments start at multiples of pad (a multiple of 32) in the output
 hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
                                     int64_t cols, const int32_t* seg_offsets,
-                                    int n_seg, int64_t ld, uint8_t* codes,
-                                    uint8_t* scales, hipStream_t stream);
+                                    int n_seg, int pad, int64_t ld,
+                                    uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream);
 
 // bf16 grouped MLP
 size_t mlp_fwd_bf16_ws_bytes(int E, int H, int F, int64_t rows, bool need_a);

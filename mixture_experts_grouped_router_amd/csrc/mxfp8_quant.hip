@@ -70,12 +70,14 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(
 // Column-wise tile kernel: a block covers 32 rows x 64 columns of one batch
 // entry; blocks run down the columns (32 values); output transposed.
 // Segment mode: rows come from one segment (zero-padded past its end) and
-// land at padded output offsets.
+// land at output offsets where every segment starts on a multiple of
+// 32 * pad_tiles.
 template <bool SEG>
 __global__ __launch_bounds__(256) void mx_cols_kernel(
     const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
-    const int32_t* __restrict__ seg_offsets, int n_seg, int64_t ld_out,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const int32_t* __restrict__ seg_offsets, int n_seg, int pad_tiles,
+    int64_t ld_out, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
   __shared__ uint16_t tile[32][64 + 2];
   __shared__ int32_t tprefix[1025];
   const int t = threadIdx.x;
@@ -83,13 +85,18 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(
   const int64_t c0 = (int64_t)blockIdx.y * 64;
   int64_t r0, rend, out0;
   if (SEG) {
-    // tile prefix over segments (ceil(n_s / 32) row tiles each): thread t
-    // owns segments 4t .. 4t+3, then a block-wide exclusive scan.
+    // tile prefix over segments (ceil(n_s / (32 pad_tiles)) * pad_tiles
+    // row tiles each): thread t owns segments 4t .. 4t+3, then a block-wide
+    // exclusive scan.
+    const int pad = 32 * pad_tiles;
     int32_t cnt4[4], own = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int sg = 4 * t + i;
-      cnt4[i] = sg < n_seg ? (seg_offsets[sg + 1] - seg_offsets[sg] + 31) / 32 : 0;
+      cnt4[i] = sg < n_seg
+                    ? (seg_offsets[sg + 1] - seg_offsets[sg] + pad - 1) / pad *
+                          pad_tiles
+                    : 0;
       own += cnt4[i];
     }
     int32_t total;
@@ -186,22 +193,24 @@ hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
   KernelScope ks("mxfp8_quantize_cols", stream);
   hipLaunchKernelGGL(mx_cols_kernel<false>, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(src), rows, cols,
-                     (const int32_t*)nullptr, 0, rows, codes, scales);
+                     (const int32_t*)nullptr, 0, 1, rows, codes, scales);
   return hipGetLastError();
 }
 
 hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
                                     int64_t cols, const int32_t* seg_offsets,
-                                    int n_seg, int64_t ld, uint8_t* codes,
-                                    uint8_t* scales, hipStream_t stream) {
+                                    int n_seg, int pad, int64_t ld,
+                                    uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream) {
   if (rows * cols == 0) return hipSuccess;
-  // sum_s ceil(n_s / 32) <= rows / 32 + n_seg
-  const int64_t tiles = rows / 32 + n_seg;
+  const int pad_tiles = pad / 32;
+  // sum_s ceil(n_s / pad) * pad / 32 <= rows / 32 + n_seg * pad / 32
+  const int64_t tiles = rows / 32 + (int64_t)n_seg * pad_tiles;
   const dim3 grid((unsigned)tiles, (unsigned)((cols + 63) / 64), 1);
   KernelScope ks("mxfp8_quantize_segments", stream);
   hipLaunchKernelGGL(mx_cols_kernel<true>, grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(src), rows, cols,
-                     seg_offsets, n_seg, ld, codes, scales);
+                     seg_offsets, n_seg, pad_tiles, ld, codes, scales);
   return hipGetLastError();
 }
 

@@ -78,6 +78,10 @@ CONFIGS: Dict[str, MoEConfig] = {
         "mixtral_mxfp8", T=8192, H=4096, F=14336, E=8, k=2, mode="mxfp8",
         backward=False, zipf=0.0,
         description="Mixtral-8x7B-shaped layer fwd, MXFP8 E4M3 + E8M0/32"),
+    "mixtral_mxfp8_bwd": MoEConfig(
+        "mixtral_mxfp8_bwd", T=8192, H=4096, F=14336, E=8, k=2, mode="mxfp8",
+        backward=True, zipf=0.0,
+        description="Mixtral-8x7B-shaped layer fwd + bwd, MXFP8, dY ~ N(0,1)"),
     "qwen3_long": MoEConfig(
         "qwen3_long", T=32768, H=2048, F=768, E=128, k=8, mode="bf16",
         backward=True, zipf=1.2,

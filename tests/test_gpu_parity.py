@@ -464,3 +464,76 @@ def test_mxfp8_fwd_exact_on_representable_operands(m):
     # K block would be off by powers of two
     assert O.rel_err(got, h1) < 3e-3
     assert_rows_close(got, h1, 3e-3, "h1")
+
+
+# ---------------------------------------------- grouped MLP backward, MXFP8
+MX_BWD_CASES = [
+    # T, H, F, E, k, zipf   (H and F multiples of 128)
+    (256, 128, 256, 8, 2, 0.0),
+    (700, 256, 384, 5, 2, 1.2),     # ragged token segments, odd K steps
+    (900, 384, 128, 16, 4, 1.2),    # many experts, some empty
+    (130, 128, 128, 3, 1, 0.0),     # k = 1, segments shorter than a K step
+]
+
+
+def _mx_bwd_run(m, d, T, H, F, E, k):
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
+    f = m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
+                              w_perm=p["w_perm"], precision=m.PREC_MXFP8,
+                              save=True)
+    dz = m.moe_gather_rows(dev_bf16(d["dy"]), p["row_map"], k)
+    g = m.moe_grouped_mlp_bwd(dz, p["x_perm"], wgu, wdn, p["offsets"],
+                              f["h1"], f["a"], w_perm=p["w_perm"],
+                              precision=m.PREC_MXFP8)
+    return p, g
+
+
+@pytest.mark.parametrize("T,H,F,E,k,zipf", MX_BWD_CASES)
+def test_grouped_mlp_bwd_mxfp8(m, T, H, F, E, k, zipf):
+    d = _mlp_case(T, H, F, E, k, zipf, seed=11)
+    ref = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], k)
+    dz_ref = O.gather_rows(O._as_f64(d["dy"]), ref["src_row"], k)
+    rq = O.grouped_mlp_bwd_mxfp8(dz_ref, ref["x_perm"], d["w_gu"],
+                                 d["w_dn"], ref["w_perm"], ref["offsets"])
+    p, g = _mx_bwd_run(m, d, T, H, F, E, k)
+    assert np.array_equal(p["offsets"].cpu().numpy(), ref["offsets"])
+    assert_rows_close(host_f64(g["dx_perm"]), rq["dx_perm"], TOL_MX,
+                      "dx_perm")
+    dx = m.moe_unpermute(g["dx_perm"], p["row_map"], k)
+    assert_rows_close(host_f64(dx), O.unpermute(rq["dx_perm"], ref["row_map"],
+                                                k), TOL_MX, "dx")
+    dwp = g["dw_perm"].cpu().numpy().astype(np.float64)
+    assert O.rel_err(dwp, rq["dw_perm"]) <= TOL_MX
+    split = np.diff(ref["offsets"])
+    gw_gu, gw_dn = host_f64(g["dw_gu"]), host_f64(g["dw_dn"])
+    for e in range(E):
+        if split[e] == 0:   # no tokens: exactly zero
+            assert np.all(gw_gu[e] == 0) and np.all(gw_dn[e] == 0), e
+        else:
+            assert O.rel_err(gw_gu[e], rq["dw_gu"][e]) <= TOL_MX, e
+            assert O.rel_err(gw_dn[e], rq["dw_dn"][e]) <= TOL_MX, e
+    assert O.rel_err(gw_gu, rq["dw_gu"]) <= TOL_MX
+    assert O.rel_err(gw_dn, rq["dw_dn"]) <= TOL_MX
+
+
+def test_grouped_mlp_bwd_mxfp8_close_to_bf16(m):
+    """The MXFP8 backward approximates the bf16 backward of the same forward
+    saves to within the E4M3 quantisation noise (about 2^-4 per operand)."""
+    T, H, F, E, k = 512, 256, 256, 4, 2
+    d = _mlp_case(T, H, F, E, k, 0.0, seed=12)
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
+    f = m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
+                              w_perm=p["w_perm"], save=True)
+    dz = m.moe_gather_rows(dev_bf16(d["dy"]), p["row_map"], k)
+    gb = m.moe_grouped_mlp_bwd(dz, p["x_perm"], wgu, wdn, p["offsets"],
+                               f["h1"], f["a"], w_perm=p["w_perm"])
+    gq = m.moe_grouped_mlp_bwd(dz, p["x_perm"], wgu, wdn, p["offsets"],
+                               f["h1"], f["a"], w_perm=p["w_perm"],
+                               precision=m.PREC_MXFP8)
+    for key in ("dx_perm", "dw_gu", "dw_dn"):
+        err = O.rel_err(host_f64(gq[key]), host_f64(gb[key]))
+        assert 1e-3 < err < 0.12, (key, err)
