@@ -295,7 +295,7 @@ KERNELS = [
     "route_topk", "permute_index", "permute_gather", "permute_gather_mxfp8",
     "gemm_gate_up_swiglu_bf16", "gemm_down_bf16", "gemm_gate_up_swiglu_mxfp8",
     "gemm_down_mxfp8", "mxfp8_quantize_rows", "mxfp8_quantize_cols",
-    "mxfp8_quantize_segments", "unpermute",
+    "mxfp8_quantize_segments", "mxfp8_scales_retile", "unpermute",
     "gemm_dgrad_down_swiglu_bwd", "gemm_dgrad_gate_up", "gemm_wgrad_down",
     "gemm_wgrad_gate_up", "gemm_dgrad_down_swiglu_bwd_mxfp8",
     "gemm_dgrad_gate_up_mxfp8", "gemm_wgrad_down_mxfp8",

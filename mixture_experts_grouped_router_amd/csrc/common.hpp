@@ -43,6 +43,74 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// ---- MXFP8 encoding with the gfx950 scaled conversion ----------------------
+// v_cvt_scalef32_pk_fp8_bf16 converts two bf16 values divided by a float
+// scale to E4M3 with round to nearest even.  For every finite bf16 value v
+// and block exponent s with |v| < 2^(s+9) (all values a block with scale s
+// can hold) it returns the same code as e4m3_from_bf16(v, s), except that a
+// value rounding above 448 gives the NaN code 0x7F / 0xFF where the
+// encoding saturates to 448 (0x7E / 0xFE); sat_e4m3x4 repairs those bytes.
+// 2^-127 is passed as the subnormal float it is.
+__device__ __forceinline__ float mx_scale_f32(int s) {
+  return s > -127 ? __uint_as_float((uint32_t)(127 + s) << 23)
+                  : __uint_as_float(0x00400000u);
+}
+// bytes 0x7F / 0xFF -> 0x7E / 0xFE, other bytes unchanged
+__device__ __forceinline__ uint32_t sat_e4m3x4(uint32_t x) {
+  const uint32_t m = ((x & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u;
+  return x ^ (m >> 7);
+}
+typedef short mx_v2i16 __attribute__((ext_vector_type(2)));
+typedef __bf16 mx_v2bf16 __attribute__((ext_vector_type(2)));
+// four E4M3 codes from two dwords of packed bf16 pairs (low halves first)
+__device__ __forceinline__ uint32_t e4m3x4_hw(uint32_t lo2, uint32_t hi2,
+                                              float scale) {
+  mx_v2i16 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      r, __builtin_bit_cast(mx_v2bf16, lo2), scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      r, __builtin_bit_cast(mx_v2bf16, hi2), scale, true);
+  return sat_e4m3x4(__builtin_bit_cast(uint32_t, r));
+}
+// 8 bf16 (one uint4) -> 8 E4M3 codes with block exponent s
+__device__ __forceinline__ uint2 e4m3x8_hw(const uint4 v, int s) {
+  const float sc = mx_scale_f32(s);
+  return make_uint2(e4m3x4_hw(v.x, v.y, sc), e4m3x4_hw(v.z, v.w, sc));
+}
+
+// n / d for n < 2^31 by multiply and shift: m = ceil(2^k / d) with
+// k = 31 + ceil(log2 d) (so m < 2^32) is exact for every n < 2^31, since the
+// rounding excess m d - 2^k is below d <= 2^(k - 31).
+struct FastDiv {
+  uint64_t m;
+  uint32_t d;
+  int k;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.d = d;
+  f.k = 31 + l;
+  f.m = ((1ull << f.k) + d - 1) / d;
+  return f;
+}
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+  return (uint32_t)(((uint64_t)n * f.m) >> f.k);
+}
+
+// MXFP8 scales in the layout the scaled-MFMA GEMM reads: for an operand of
+// rows r with K = 128 * nks values each, the four scale bytes of row r and
+// K step s (K blocks 4s .. 4s+3) sit at ((r / 32) * nks + s) * 128 +
+// (r % 32) * 4, so the 32 rows of one MFMA row block read one contiguous
+// 128-byte line per K step.  Storage covers rows rounded up to 32.
+MOE_HD inline uint32_t mx_tile_off(uint32_t r, uint32_t kb, uint32_t nks) {
+  return ((r >> 5) * nks + (kb >> 2)) * 128u + ((r & 31u) << 2) + (kb & 3u);
+}
+inline size_t mx_tile_bytes(int64_t rows, int64_t k) {
+  return (size_t)((rows + 31) / 32) * 32 * (size_t)(k / 32);
+}
+
 // Record the first device-side data error (first error wins).
 __device__ __forceinline__ void report_error(int32_t* status, int32_t code) {
   if (status) atomicCAS(status, 0, code);

@@ -25,16 +25,18 @@ struct MxFwdWs {
   int32_t* ts1;
   int32_t* ts2;
   uint8_t* aq;   // A codes [rows, F]
-  uint8_t* as;   // A scales [rows, F/32]
+  uint8_t* as;   // A scales (GEMM layout, K = F)
   uint8_t* xq;   // x_perm codes [rows, H] (quantised here)
-  uint8_t* xs;
-  uint8_t* guq;  // W_gu codes [E, 2F, H]
-  uint8_t* gus;
-  uint8_t* dnq;  // W_dn codes [E, H, F]
-  uint8_t* dns;
+  uint8_t* xs;   // x_perm scales (GEMM layout, K = H)
+  uint8_t* guq;  // W_gu codes [E, 2F, H] (quantised here)
+  uint8_t* gus;  // W_gu scales (GEMM layout, K = H)
+  uint8_t* dnq;  // W_dn codes [E, H, F] (quantised here)
+  uint8_t* dns;  // W_dn scales (GEMM layout, K = F)
   size_t bytes;
 };
 
+// Scales always live here in the GEMM layout: quantised in the call, or
+// rearranged from the caller's row-major scales.
 MxFwdWs carve_fwd(void* base, int E, int H, int F, int64_t rows, bool quant_x,
                   bool quant_w) {
   MxFwdWs w{};
@@ -45,21 +47,20 @@ MxFwdWs carve_fwd(void* base, int E, int H, int F, int64_t rows, bool quant_x,
     off += align256(n);
     return q;
   };
+  auto take8 = [&](size_t n) { return reinterpret_cast<uint8_t*>(take(n)); };
   w.ts1 = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
   w.ts2 = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
-  w.aq = reinterpret_cast<uint8_t*>(take((size_t)rows * F));
-  w.as = reinterpret_cast<uint8_t*>(take((size_t)rows * F / 32));
-  if (quant_x) {
-    w.xq = reinterpret_cast<uint8_t*>(take((size_t)rows * H));
-    w.xs = reinterpret_cast<uint8_t*>(take((size_t)rows * H / 32));
-  }
+  w.aq = take8((size_t)rows * F);
+  w.as = take8(mx_tile_bytes(rows, F));
+  if (quant_x) w.xq = take8((size_t)rows * H);
+  w.xs = take8(mx_tile_bytes(rows, H));
+  const size_t ngu = (size_t)E * 2 * F * H, ndn = (size_t)E * H * F;
   if (quant_w) {
-    const size_t ngu = (size_t)E * 2 * F * H, ndn = (size_t)E * H * F;
-    w.guq = reinterpret_cast<uint8_t*>(take(ngu));
-    w.gus = reinterpret_cast<uint8_t*>(take(ngu / 32));
-    w.dnq = reinterpret_cast<uint8_t*>(take(ndn));
-    w.dns = reinterpret_cast<uint8_t*>(take(ndn / 32));
+    w.guq = take8(ngu);
+    w.dnq = take8(ndn);
   }
+  w.gus = take8(ngu / 32);
+  w.dns = take8(ndn / 32);
   w.bytes = off;
   return w;
 }
@@ -84,21 +85,28 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   const bool quant_w = w_gu_q == nullptr || w_dn_q == nullptr;
   MxFwdWs w = carve_fwd(ws, E, H, F, rows, quant_x, quant_w);
   hipError_t err = hipSuccess;
+  const int64_t ngu = (int64_t)E * 2 * F, ndn = (int64_t)E * H;  // rows
   if (quant_w) {
-    err = launch_mx_quant_rows(w_gu, (int64_t)E * 2 * F, H, w.guq, w.gus,
-                               stream);
+    err = launch_mx_quant_rows(w_gu, ngu, H, w.guq, w.gus, stream, true);
     if (err == hipSuccess)
-      err = launch_mx_quant_rows(w_dn, (int64_t)E * H, F, w.dnq, w.dns,
-                                 stream);
-    if (err != hipSuccess) return err;
-    w_gu_q = w.guq; w_gu_s = w.gus; w_dn_q = w.dnq; w_dn_s = w.dns;
+      err = launch_mx_quant_rows(w_dn, ndn, F, w.dnq, w.dns, stream, true);
+    w_gu_q = w.guq;
+    w_dn_q = w.dnq;
+  } else {
+    err = launch_mx_scales_retile(w_gu_s, ngu, H, w.gus, stream);
+    if (err == hipSuccess)
+      err = launch_mx_scales_retile(w_dn_s, ndn, F, w.dns, stream);
   }
+  if (err != hipSuccess) return err;
   if (rows == 0) return hipSuccess;
   if (quant_x) {
-    err = launch_mx_quant_rows(x_perm_bf16, rows, H, w.xq, w.xs, stream);
-    if (err != hipSuccess) return err;
-    xq = w.xq; xs = w.xs;
+    err = launch_mx_quant_rows(x_perm_bf16, rows, H, w.xq, w.xs, stream,
+                               true);
+    xq = w.xq;
+  } else {
+    err = launch_mx_scales_retile(xs, rows, H, w.xs, stream);
   }
+  if (err != hipSuccess) return err;
   const int tn1 = (F + BN / 2 - 1) / (BN / 2);
   const int tn2 = (H + BN - 1) / BN;
   err = launch_tile_table(offsets, E, tn1, w.ts1, stream);
@@ -108,13 +116,13 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   Params p1{};
   p1.a = reinterpret_cast<const char*>(xq);
   p1.lda = H;
-  p1.sa = xs;
-  p1.ldsa = H / 32;
+  p1.sa = w.xs;
+  p1.ldsa = H / 128;
   p1.b = reinterpret_cast<const char*>(w_gu_q);
   p1.ldb = H;
   p1.b_es = (int64_t)2 * F * H;
-  p1.sb = w_gu_s;
-  p1.ldsb = H / 32;
+  p1.sb = w.gus;
+  p1.ldsb = H / 128;
   p1.sb_es = (int64_t)2 * F * H / 32;
   p1.N = 2 * F;
   p1.b_rows = 2 * F;
@@ -139,12 +147,12 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p2.a = reinterpret_cast<const char*>(w.aq);
   p2.lda = F;
   p2.sa = w.as;
-  p2.ldsa = F / 32;
+  p2.ldsa = F / 128;
   p2.b = reinterpret_cast<const char*>(w_dn_q);
   p2.ldb = F;
   p2.b_es = (int64_t)H * F;
-  p2.sb = w_dn_s;
-  p2.ldsb = F / 32;
+  p2.sb = w.dns;
+  p2.ldsb = F / 128;
   p2.sb_es = (int64_t)H * F / 32;
   p2.N = H;
   p2.b_rows = H;
@@ -181,6 +189,7 @@ struct MxBwdWs {
   int32_t* poff;   // padded token offsets [E+1]
   uint16_t* dh1;   // bf16 [rows, 2F]
   float* part;     // dw partial sums [tiles along F][rows]
+  // codes, and scales in the GEMM layout
   uint8_t *dzq, *dzs;      // dZ row-wise [rows, H]
   uint8_t *wdq, *wds;      // W_dn blocks along H: [E, F, H]
   uint8_t *wgq, *wgs;      // W_gu blocks along 2F: [E, H, 2F]
@@ -218,13 +227,13 @@ MxBwdWs carve_bwd(void* base, int E, int H, int F, int64_t rows) {
   w.dh1 = reinterpret_cast<uint16_t*>(take((size_t)rows * F2 * 2));
   w.part = reinterpret_cast<float*>(take((size_t)tnf * rows * 4));
   w.dzq = take8((size_t)rows * H);
-  w.dzs = take8((size_t)rows * H / 32);
+  w.dzs = take8(mx_tile_bytes(rows, H));
   w.wdq = take8((size_t)E * H * F);
   w.wds = take8((size_t)E * H * F / 32);
   w.wgq = take8((size_t)E * F2 * H);
   w.wgs = take8((size_t)E * F2 * H / 32);
   w.hq = take8((size_t)rows * F2);
-  w.hs = take8((size_t)rows * F2 / 32);
+  w.hs = take8(mx_tile_bytes(rows, F2));
   w.dzt = take8((size_t)H * ld);
   w.dzts = take8((size_t)H * ld / 32);
   w.at = take8((size_t)F * ld);
@@ -258,11 +267,11 @@ hipError_t wgrad_mx(const char* name, int E, int M, int N, int64_t ld,
   p.a = reinterpret_cast<const char*>(aq);
   p.lda = ld;
   p.sa = as;
-  p.ldsa = ld / 32;
+  p.ldsa = ld / 128;
   p.b = reinterpret_cast<const char*>(bq);
   p.ldb = ld;
   p.sb = bs;
-  p.ldsb = ld / 32;
+  p.ldsb = ld / 128;
   p.b_rows = N;
   p.M = M;
   p.N = N;
@@ -300,11 +309,12 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
     if (err == hipSuccess) err = launch_tile_table(offsets, E, tnh, w.ts_h, stream);
     // operands of the two dgrad GEMMs
     if (err == hipSuccess)
-      err = launch_mx_quant_rows(dz_perm, rows, H, w.dzq, w.dzs, stream);
+      err = launch_mx_quant_rows(dz_perm, rows, H, w.dzq, w.dzs, stream,
+                                 true);
     if (err == hipSuccess)
-      err = launch_mx_quant_cols(w_dn, E, H, F, w.wdq, w.wds, stream);
+      err = launch_mx_quant_cols(w_dn, E, H, F, w.wdq, w.wds, stream, true);
     if (err == hipSuccess)
-      err = launch_mx_quant_cols(w_gu, E, F2, H, w.wgq, w.wgs, stream);
+      err = launch_mx_quant_cols(w_gu, E, F2, H, w.wgq, w.wgs, stream, true);
     if (err != hipSuccess) return err;
 
     // dgrad2 + SwiGLU backward: dA = dZ W_dn[e]; B = W_dn[e]^T [F, H]
@@ -312,12 +322,12 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
     p.a = reinterpret_cast<const char*>(w.dzq);
     p.lda = H;
     p.sa = w.dzs;
-    p.ldsa = H / 32;
+    p.ldsa = H / 128;
     p.b = reinterpret_cast<const char*>(w.wdq);
     p.ldb = H;
     p.b_es = (int64_t)F * H;
     p.sb = w.wds;
-    p.ldsb = H / 32;
+    p.ldsb = H / 128;
     p.sb_es = (int64_t)F * H / 32;
     p.b_rows = F;
     p.N = F;
@@ -346,18 +356,18 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
     }
 
     // dgrad1: dX = dH1 W_gu[e]; B = W_gu[e]^T [H, 2F]
-    err = launch_mx_quant_rows(w.dh1, rows, F2, w.hq, w.hs, stream);
+    err = launch_mx_quant_rows(w.dh1, rows, F2, w.hq, w.hs, stream, true);
     if (err != hipSuccess) return err;
     Params q{};
     q.a = reinterpret_cast<const char*>(w.hq);
     q.lda = F2;
     q.sa = w.hs;
-    q.ldsa = F2 / 32;
+    q.ldsa = F2 / 128;
     q.b = reinterpret_cast<const char*>(w.wgq);
     q.ldb = F2;
     q.b_es = (int64_t)H * F2;
     q.sb = w.wgs;
-    q.ldsb = F2 / 32;
+    q.ldsb = F2 / 128;
     q.sb_es = (int64_t)H * F2 / 32;
     q.b_rows = H;
     q.N = H;
@@ -375,16 +385,16 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
 
     // token-direction operands of the two wgrad GEMMs
     err = launch_mx_quant_segments(dz_perm, rows, H, offsets, E, kTokPad,
-                                   w.ld, w.dzt, w.dzts, stream);
+                                   w.ld, w.dzt, w.dzts, stream, true);
     if (err == hipSuccess)
       err = launch_mx_quant_segments(a_save, rows, F, offsets, E, kTokPad,
-                                     w.ld, w.at, w.ats, stream);
+                                     w.ld, w.at, w.ats, stream, true);
     if (err == hipSuccess)
       err = launch_mx_quant_segments(w.dh1, rows, F2, offsets, E, kTokPad,
-                                     w.ld, w.ht, w.hts, stream);
+                                     w.ld, w.ht, w.hts, stream, true);
     if (err == hipSuccess)
       err = launch_mx_quant_segments(x_perm, rows, H, offsets, E, kTokPad,
-                                     w.ld, w.xt, w.xts, stream);
+                                     w.ld, w.xt, w.xts, stream, true);
   }
   if (err != hipSuccess) return err;
   // wgrad: every expert gets a tile set; K = its padded token count (0 for

@@ -69,12 +69,21 @@ enum Prec { P_BF16 = 0, P_FP8 = 1 };
 template <int NR, int NM>
 __device__ __forceinline__ void sched_reads_mfma() {
 #if MOE_SCHED_GROUPS
+  if constexpr (NR <= NM) {
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    for (int i = 0; i < NR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+    if constexpr (NM > NR)
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+  } else {   // NR / NM reads before each MFMA
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, NR / NM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
   }
-  if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
 #endif
 }
 
@@ -91,7 +100,8 @@ struct Params {
   int tiles_n;                // tiles along N
   int tiles_m;                // RAGGED_K: tiles along M
   int b_rows;                 // rows of one expert's B (KC direct loads)
-  // MXFP8 scales: row-major [rows][K/32] bytes
+  // MXFP8 scales in the GEMM layout (mx_tile_off); ldsa / ldsb: K steps
+  // (128 values) per row of A / B; sb_es: scale bytes per expert of B
   const uint8_t* sa;
   int64_t ldsa;
   const uint8_t* sb;
@@ -100,7 +110,7 @@ struct Params {
   int64_t ldc, c_es;          // elements
   uint16_t* c2;               // SwiGLU epilogues: (g, u) save [rows, 2F]
   uint8_t* cq;                // EPI_SWIGLU_MX: A codes [rows, F]
-  uint8_t* cs;                // EPI_SWIGLU_MX: A scales [rows, F/32]
+  uint8_t* cs;                // EPI_SWIGLU_MX: A scales (GEMM layout)
   const uint16_t* h1;         // EPI_SWIGLU_BWD: saved (g, u) [rows, 2F]
   const float* w;             // routing weight per row (nullable -> 1)
   float* dw_part;             // EPI_SWIGLU_BWD: [tiles_n][rows]
@@ -300,15 +310,17 @@ struct McStaged {
 // Lane l needs, for each of its 4 A row blocks and 4 B row blocks, the scale
 // bytes of K blocks g and 2+g of the step (g = l/32): one dword (4 blocks)
 // per row, rearranged so that byte 0 feeds slice 0 and byte 1 slice 1 (the
-// MFMA's opsel picks the byte).
+// MFMA's opsel picks the byte).  In the GEMM scale layout the 32 rows of a
+// row block read one 128-byte line per step (two when an expert's rows
+// start inside a 32-row group).
 struct MxScales {
-  const uint8_t* a;  // wave-uniform: A scales at the expert's first row
+  const uint8_t* a;  // wave-uniform: A scales at the first K step
   const uint8_t* b;  // wave-uniform: B scales of the expert
-  uint32_t oa[4], ob[4];  // lane's row offsets (bytes)
+  uint32_t oa[4], ob[4];  // lane's row offsets (bytes, K step 0)
   uint32_t na[4], nb[4];  // next step, raw
-  __device__ __forceinline__ void load(int kblk) {
-    const uint8_t* ka = a + kblk;
-    const uint8_t* kb = b + kblk;
+  __device__ __forceinline__ void load(int kstep) {
+    const uint8_t* ka = a + kstep * 128;
+    const uint8_t* kb = b + kstep * 128;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       na[i] = *reinterpret_cast<const uint32_t*>(ka + oa[i]);
@@ -394,19 +406,26 @@ struct Frags<P_FP8> {
   }
 };
 
+// The 16 MFMAs of one K slice in row-block order; HALF = 0 issues row
+// blocks 0-1, HALF = 1 row blocks 2-3, HALF = 2 all four.
 #define MOE_MFMA_BF(i, j, A, B) \
   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[i][j], 0, 0, 0)
 
+template <int HALF>
 __device__ __forceinline__ void mfma_bf16(const Frags<P_BF16>& f,
                                           f32x16_t (&acc)[4][4]) {
-  MOE_MFMA_BF(0, 0, f.a0, f.b0); MOE_MFMA_BF(0, 1, f.a0, f.b1);
-  MOE_MFMA_BF(0, 2, f.a0, f.b2); MOE_MFMA_BF(0, 3, f.a0, f.b3);
-  MOE_MFMA_BF(1, 0, f.a1, f.b0); MOE_MFMA_BF(1, 1, f.a1, f.b1);
-  MOE_MFMA_BF(1, 2, f.a1, f.b2); MOE_MFMA_BF(1, 3, f.a1, f.b3);
-  MOE_MFMA_BF(2, 0, f.a2, f.b0); MOE_MFMA_BF(2, 1, f.a2, f.b1);
-  MOE_MFMA_BF(2, 2, f.a2, f.b2); MOE_MFMA_BF(2, 3, f.a2, f.b3);
-  MOE_MFMA_BF(3, 0, f.a3, f.b0); MOE_MFMA_BF(3, 1, f.a3, f.b1);
-  MOE_MFMA_BF(3, 2, f.a3, f.b2); MOE_MFMA_BF(3, 3, f.a3, f.b3);
+  if constexpr (HALF != 1) {
+    MOE_MFMA_BF(0, 0, f.a0, f.b0); MOE_MFMA_BF(0, 1, f.a0, f.b1);
+    MOE_MFMA_BF(0, 2, f.a0, f.b2); MOE_MFMA_BF(0, 3, f.a0, f.b3);
+    MOE_MFMA_BF(1, 0, f.a1, f.b0); MOE_MFMA_BF(1, 1, f.a1, f.b1);
+    MOE_MFMA_BF(1, 2, f.a1, f.b2); MOE_MFMA_BF(1, 3, f.a1, f.b3);
+  }
+  if constexpr (HALF != 0) {
+    MOE_MFMA_BF(2, 0, f.a2, f.b0); MOE_MFMA_BF(2, 1, f.a2, f.b1);
+    MOE_MFMA_BF(2, 2, f.a2, f.b2); MOE_MFMA_BF(2, 3, f.a2, f.b3);
+    MOE_MFMA_BF(3, 0, f.a3, f.b0); MOE_MFMA_BF(3, 1, f.a3, f.b1);
+    MOE_MFMA_BF(3, 2, f.a3, f.b2); MOE_MFMA_BF(3, 3, f.a3, f.b3);
+  }
 }
 #undef MOE_MFMA_BF
 
@@ -416,19 +435,23 @@ __device__ __forceinline__ void mfma_bf16(const Frags<P_BF16>& f,
   acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(             \
       A, B, acc[i][j], 0, 0, KK, (int)sa[i], KK, (int)sb[j])
 
-template <int KK>
+template <int KK, int HALF>
 __device__ __forceinline__ void mfma_fp8(const Frags<P_FP8>& f,
                                          const uint32_t (&sa)[4],
                                          const uint32_t (&sb)[4],
                                          f32x16_t (&acc)[4][4]) {
-  MOE_MFMA_MX(0, 0, f.a0, f.b0); MOE_MFMA_MX(0, 1, f.a0, f.b1);
-  MOE_MFMA_MX(0, 2, f.a0, f.b2); MOE_MFMA_MX(0, 3, f.a0, f.b3);
-  MOE_MFMA_MX(1, 0, f.a1, f.b0); MOE_MFMA_MX(1, 1, f.a1, f.b1);
-  MOE_MFMA_MX(1, 2, f.a1, f.b2); MOE_MFMA_MX(1, 3, f.a1, f.b3);
-  MOE_MFMA_MX(2, 0, f.a2, f.b0); MOE_MFMA_MX(2, 1, f.a2, f.b1);
-  MOE_MFMA_MX(2, 2, f.a2, f.b2); MOE_MFMA_MX(2, 3, f.a2, f.b3);
-  MOE_MFMA_MX(3, 0, f.a3, f.b0); MOE_MFMA_MX(3, 1, f.a3, f.b1);
-  MOE_MFMA_MX(3, 2, f.a3, f.b2); MOE_MFMA_MX(3, 3, f.a3, f.b3);
+  if constexpr (HALF != 1) {
+    MOE_MFMA_MX(0, 0, f.a0, f.b0); MOE_MFMA_MX(0, 1, f.a0, f.b1);
+    MOE_MFMA_MX(0, 2, f.a0, f.b2); MOE_MFMA_MX(0, 3, f.a0, f.b3);
+    MOE_MFMA_MX(1, 0, f.a1, f.b0); MOE_MFMA_MX(1, 1, f.a1, f.b1);
+    MOE_MFMA_MX(1, 2, f.a1, f.b2); MOE_MFMA_MX(1, 3, f.a1, f.b3);
+  }
+  if constexpr (HALF != 0) {
+    MOE_MFMA_MX(2, 0, f.a2, f.b0); MOE_MFMA_MX(2, 1, f.a2, f.b1);
+    MOE_MFMA_MX(2, 2, f.a2, f.b2); MOE_MFMA_MX(2, 3, f.a2, f.b3);
+    MOE_MFMA_MX(3, 0, f.a3, f.b0); MOE_MFMA_MX(3, 1, f.a3, f.b1);
+    MOE_MFMA_MX(3, 2, f.a3, f.b2); MOE_MFMA_MX(3, 3, f.a3, f.b3);
+  }
 }
 #undef MOE_MFMA_MX
 
@@ -437,23 +460,23 @@ struct Mma;
 
 template <>
 struct Mma<P_BF16> {
-  template <int KK>
+  template <int KK, int HALF = 2>
   static __device__ __forceinline__ void run(const Frags<P_BF16>& f,
                                              const uint32_t (&)[4],
                                              const uint32_t (&)[4],
                                              f32x16_t (&acc)[4][4]) {
-    mfma_bf16(f, acc);
+    mfma_bf16<HALF>(f, acc);
   }
 };
 
 template <>
 struct Mma<P_FP8> {
-  template <int KK>
+  template <int KK, int HALF = 2>
   static __device__ __forceinline__ void run(const Frags<P_FP8>& f,
                                              const uint32_t (&sa)[4],
                                              const uint32_t (&sb)[4],
                                              f32x16_t (&acc)[4][4]) {
-    mfma_fp8<KK & 1>(f, sa, sb, acc);
+    mfma_fp8<KK & 1, HALF>(f, sa, sb, acc);
   }
 };
 
@@ -581,7 +604,8 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
         uint4* dq = reinterpret_cast<uint4*>(p.cq + row * p.F + fb);
         dq[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
         dq[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
-        p.cs[row * (p.F / 32) + fb / 32] = (uint8_t)(sx + 127);
+        p.cs[mx_tile_off((uint32_t)row, (uint32_t)(fb / 32),
+                         (uint32_t)(p.F / 128))] = (uint8_t)(sx + 127);
       }
       if (EPI == EPI_SWIGLU || p.c) {
         uint4* dc = reinterpret_cast<uint4*>(p.c + row * p.ldc + fb);
@@ -786,11 +810,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   const uint32_t sel = (lane >> 5) ? 0x0c0c0301u : 0x0c0c0200u;
   if constexpr (P == P_FP8) {
     if constexpr (G == RAGGED_M) {
-      ms.a = p.sa + (int64_t)tc.seg0 * p.ldsa;
+      ms.a = p.sa;
       ms.b = p.sb + (int64_t)tc.e * p.sb_es;
-    } else {   // K blocks of the expert's range
-      ms.a = p.sa + tc.seg0 / 32;
-      ms.b = p.sb + tc.seg0 / 32;
+    } else {   // the expert's first K step (seg0 is a multiple of 128)
+      ms.a = p.sa + tc.seg0;
+      ms.b = p.sb + tc.seg0;
     }
     KcDirect<EPI, true> m;   // B row mapping of the lane's 32-row blocks
     m.q = lane & 31;
@@ -801,9 +825,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     for (int i = 0; i < 4; ++i) {
       const int ra = min(tc.m0 + wm * 128 + 32 * i + (lane & 31),
                          (G == RAGGED_M ? tc.seg_len : p.M) - 1);
-      ms.oa[i] = (uint32_t)ra * (uint32_t)p.ldsa;
+      const uint32_t rabs = G == RAGGED_M ? (uint32_t)(tc.seg0 + ra) : ra;
+      ms.oa[i] = mx_tile_off(rabs, 0, (uint32_t)p.ldsa);
       // B tile row wn*128 + 32 i + lane%32 is direct-load block 4 wn + i
-      ms.ob[i] = (uint32_t)m.row(4 * wn + i) * (uint32_t)p.ldsb;
+      ms.ob[i] = mx_tile_off((uint32_t)m.row(4 * wn + i), 0,
+                             (uint32_t)p.ldsb);
     }
   }
 
@@ -822,7 +848,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     else ma.load(kt * kStepK);
     if constexpr (LB == KC) db.issue(bufb, (uint32_t)kt * kRowBytes, real, wave);
     else mb.load(kt * kStepK);
-    if constexpr (P == P_FP8) ms.load(min(kt, nk - 1) * (kStepK / 32));
+    if constexpr (P == P_FP8) ms.load(min(kt, nk - 1));
   };
   auto stage_store = [&](char* bufa, char* bufb) {
     if constexpr (LA == MC) ma.store(bufa);
@@ -844,8 +870,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // at the barrier.  An odd last step computes on a zero stage.  The trip
   // has no branches, so the MFMAs stay where they are written.
   // Fragment reads run one K slice ahead of the MFMAs; the barrier that
-  // publishes the next stage sits before the last slice's MFMAs so the first
-  // reads of the next stage overlap them.
+  // publishes the next stage sits halfway through the last slice's MFMAs:
+  // the loads of the next stage get all MFMAs before it to land, and the
+  // first reads of the next stage overlap the MFMAs after it.
   const int nk2 = (nk + 1) & ~1;
   if (nk > 0) {
     issue(sA0, sB0, 0, true);
@@ -870,12 +897,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     stage_store(sA1, sB1);
+    Mma<P>::template run<kSl - 1, 0>(cur, sa_cur, sb_cur, acc);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     nxt.load(sA1, sB1, 0, wm, wn, lane);
-    Mma<P>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
+    Mma<P>::template run<kSl - 1, 1>(cur, sa_cur, sb_cur, acc);
     cur = nxt;
     take_scales();
-    sched_reads_mfma<P == P_FP8 ? 16 : 8, 16>();
+    sched_reads_mfma<P == P_FP8 ? 16 : 8, 8>();
     __builtin_amdgcn_sched_barrier(0);
 
     // stage kt+1 from buffers 1 while stage kt+2 loads into buffers 0 (a
@@ -891,12 +920,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     stage_store(sA0, sB0);
+    Mma<P>::template run<kSl - 1, 0>(cur, sa_cur, sb_cur, acc);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     nxt.load(sA0, sB0, 0, wm, wn, lane);
-    Mma<P>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
+    Mma<P>::template run<kSl - 1, 1>(cur, sa_cur, sb_cur, acc);
     cur = nxt;
     take_scales();
-    sched_reads_mfma<P == P_FP8 ? 16 : 8, 16>();
+    sched_reads_mfma<P == P_FP8 ? 16 : 8, 8>();
     __builtin_amdgcn_sched_barrier(0);
   }
 

@@ -31,19 +31,26 @@ hipError_t launch_probs_grad(const float* dw_perm, const int32_t* row_map,
                              int64_t T, int k, float* dprobs,
                              hipStream_t stream);
 
-// MXFP8 quantisation
+// MXFP8 quantisation.  tiled: scales in the GEMM layout (mx_tile_off;
+// K = cols for rows, K = rows / ld for the transposed outputs, which then
+// must be multiples of 128); otherwise row-major [rows][K / 32].
 hipError_t launch_mx_quant_rows(const void* src, int64_t rows, int64_t cols,
                                 uint8_t* codes, uint8_t* scales,
-                                hipStream_t stream);
+                                hipStream_t stream, bool tiled = false);
 hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
                                 int64_t cols, uint8_t* codes, uint8_t* scales,
-                                hipStream_t stream);
+                                hipStream_t stream, bool tiled = false);
 // pad: segments start at multiples of pad (a multiple of 32) in the output
 hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
                                     int64_t cols, const int32_t* seg_offsets,
                                     int n_seg, int pad, int64_t ld,
                                     uint8_t* codes, uint8_t* scales,
-                                    hipStream_t stream);
+                                    hipStream_t stream, bool tiled = false);
+// row-major scales [rows][k / 32] (k % 128 == 0, 4-byte aligned) -> GEMM
+// layout
+hipError_t launch_mx_scales_retile(const uint8_t* src, int64_t rows,
+                                   int64_t k, uint8_t* dst,
+                                   hipStream_t stream);
 
 // bf16 grouped MLP
 size_t mlp_fwd_bf16_ws_bytes(int E, int H, int F, int64_t rows, bool need_a);

@@ -70,15 +70,11 @@ MOE_HD inline uint32_t e4m3_from_bf16(uint32_t b, int s) {
 // sign cleared): floor(log2 amax) - 8 clamped to [-127, 127]; zero -> -127.
 MOE_HD inline int e8m0_exp_from_bf16_amax(uint32_t a) {
   const int be = (int)((a >> 7) & 0xFF);
-  const uint32_t man = a & 0x7Fu;
-  int fl;
-  if (be == 0) {
-    if (man == 0) return -127;
-    fl = -133 + (31 - moe_clz32(man));  // man * 2^-133: floor(log2) = -133 + msb
-  } else {
-    fl = be - 127;
-  }
-  int s = fl - 8;
+  // subnormal: man * 2^-133, floor(log2) = -133 + msb(man); zero gives
+  // -133 here and clamps to -127 below (selects, no branches)
+  const int msb = 31 - moe_clz32((a & 0x7Fu) | 1u);
+  const int fl = be != 0 ? be - 127 : msb - 133;
+  const int s = fl - 8;
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 

@@ -6,10 +6,11 @@
 // weights are quantised from bf16 on the fly ("Efficient MoE training ...",
 // section "3) Quantisation overhead in low-precision training").
 //
-// Encoding with integer operations only (mx_codec.hpp): scale exponent
-// s = floor(log2 amax) - 8, element = E4M3(v * 2^-s) with round to nearest
-// even and saturation at 448.  All three kernels are HBM-bound streaming
-// passes: 2 bytes read, 1 + 1/32 bytes written per element.
+// Scale exponent s = floor(log2 amax) - 8 (integer operations on the bf16
+// amax, mx_codec.hpp); elements E4M3(v * 2^-s) with round to nearest even
+// and saturation at 448, by the gfx950 scaled conversion (common.hpp).  All
+// kernels are HBM-bound streaming passes: 2 bytes read, 1 + 1/32 bytes
+// written per element.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timer.hpp"
@@ -21,17 +22,6 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) {
   return a > b ? a : b;
 }
 
-// 8 bf16 (one uint4) -> 8 E4M3 codes (uint2) with scale exponent s.
-__device__ __forceinline__ uint2 encode8(const uint4 v, int s) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t q[2] = {0, 0};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    q[i >> 1] |= e4m3_from_bf16(w[i] & 0xffffu, s) << (16 * (i & 1));
-    q[i >> 1] |= e4m3_from_bf16(w[i] >> 16, s) << (16 * (i & 1) + 8);
-  }
-  return make_uint2(q[0], q[1]);
-}
 
 __device__ __forceinline__ uint32_t amax8(const uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -44,25 +34,44 @@ __device__ __forceinline__ uint32_t amax8(const uint4 v) {
   return a;
 }
 
-// Row-wise: 4 consecutive lanes own one block of 32 along a row.
+// Row-wise: 4 consecutive lanes own one block of 32 along a row; every
+// thread keeps U independent 16-byte loads in flight.
+constexpr int kRowsUnroll = 4;
+
+template <bool TILED>
 __global__ __launch_bounds__(256) void mx_rows_kernel(
-    const uint4* __restrict__ src, int64_t n_chunks,
-    uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  // n_chunks is a multiple of 4 and so is the stride: groups of 4 lanes stay
-  // aligned to blocks in every iteration.
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-       c - threadIdx.x % 4 < n_chunks; c += stride) {
-    const bool act = c < n_chunks;
-    const uint4 v = act ? ld_nt(src + c)
-                        : make_uint4(0, 0, 0, 0);
-    uint32_t a = amax8(v);
-    a = umax(a, __shfl_xor(a, 1, 64));
-    a = umax(a, __shfl_xor(a, 2, 64));
-    const int s = e8m0_exp_from_bf16_amax(a);
-    if (act) {
-      codes[c] = encode8(v, s);
-      if ((c & 3) == 0) scales[c >> 2] = (uint8_t)(s + 127);
+    const uint4* __restrict__ src, int64_t n_chunks, FastDiv bpr,
+    uint32_t nks, uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t S = (int64_t)gridDim.x * blockDim.x;
+  // n_chunks and S are multiples of 4: groups of 4 lanes stay aligned to
+  // blocks and are either wholly in range or wholly out
+  for (int64_t c0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+       c0 - threadIdx.x % 4 < n_chunks; c0 += kRowsUnroll * S) {
+    uint4 v[kRowsUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowsUnroll; ++u) {
+      const int64_t c = c0 + u * S;
+      v[u] = c < n_chunks ? ld_nt(src + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsUnroll; ++u) {
+      const int64_t c = c0 + u * S;
+      uint32_t a = amax8(v[u]);
+      a = umax(a, __shfl_xor(a, 1, 64));
+      a = umax(a, __shfl_xor(a, 2, 64));
+      const int s = e8m0_exp_from_bf16_amax(a);
+      if (c < n_chunks) {
+        codes[c] = e4m3x8_hw(v[u], s);
+        if ((c & 3) == 0) {
+          const uint32_t b = (uint32_t)(c >> 2);   // block index < 2^31
+          uint32_t off = b;
+          if (TILED) {
+            const uint32_t r = fastdiv(b, bpr);
+            off = mx_tile_off(r, b - r * bpr.d, nks);
+          }
+          scales[off] = (uint8_t)(s + 127);
+        }
+      }
     }
   }
 }
@@ -72,7 +81,7 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(
 // Segment mode: rows come from one segment (zero-padded past its end) and
 // land at output offsets where every segment starts on a multiple of
 // 32 * pad_tiles.
-template <bool SEG>
+template <bool SEG, bool TILED>
 __global__ __launch_bounds__(256) void mx_cols_kernel(
     const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
     const int32_t* __restrict__ seg_offsets, int n_seg, int pad_tiles,
@@ -156,44 +165,79 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(
   const int s = e8m0_exp_from_bf16_amax(a);
   const int64_t c = c0 + col;
   if (c < cols) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= e4m3_from_bf16(vals[i], s) << (8 * i);
-      hi |= e4m3_from_bf16(vals[i + 4], s) << (8 * i);
+    const float sc = mx_scale_f32(s);
+    const uint32_t lo = e4m3x4_hw(vals[0] | (vals[1] << 16),
+                                  vals[2] | (vals[3] << 16), sc);
+    const uint32_t hi = e4m3x4_hw(vals[4] | (vals[5] << 16),
+                                  vals[6] | (vals[7] << 16), sc);
+    const int64_t orow = b * cols + c;   // output row
+    *reinterpret_cast<uint2*>(codes + orow * ld_out + out0 + q * 8) =
+        make_uint2(lo, hi);
+    if (q == 0) {
+      const int64_t kb = out0 / 32;
+      if (TILED)
+        scales[mx_tile_off((uint32_t)orow, (uint32_t)kb,
+                           (uint32_t)(ld_out / 128))] = (uint8_t)(s + 127);
+      else
+        scales[orow * (ld_out / 32) + kb] = (uint8_t)(s + 127);
     }
-    const int64_t obase = (b * cols + c) * ld_out + out0 + q * 8;
-    *reinterpret_cast<uint2*>(codes + obase) = make_uint2(lo, hi);
-    if (q == 0) scales[(b * cols + c) * (ld_out / 32) + out0 / 32] = (uint8_t)(s + 127);
   }
+}
+
+// Row-major scales [rows][4 nks] -> the GEMM layout; one thread per row and
+// K step (a dword), consecutive threads write consecutive dwords.
+__global__ __launch_bounds__(256) void mx_retile_kernel(
+    const uint32_t* __restrict__ src, int64_t rows, uint32_t nks,
+    uint32_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t rb = i / (32 * (int64_t)nks);
+  const uint32_t rem = (uint32_t)(i - rb * 32 * (int64_t)nks);
+  const uint32_t st = rem / 32, rr = rem % 32;
+  const int64_t r = rb * 32 + rr;
+  if (r >= rows) return;
+  dst[i] = src[r * nks + st];
 }
 
 }  // namespace
 
 hipError_t launch_mx_quant_rows(const void* src, int64_t rows, int64_t cols,
                                 uint8_t* codes, uint8_t* scales,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool tiled) {
   const int64_t n_chunks = rows * cols / 8;
   if (n_chunks == 0) return hipSuccess;
-  int64_t blocks = (n_chunks + 255) / 256;
+  int64_t blocks = (n_chunks + 256 * kRowsUnroll - 1) / (256 * kRowsUnroll);
   if (blocks > 65536) blocks = 65536;
+  if (n_chunks / 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const FastDiv bpr = make_fastdiv((uint32_t)(cols / 32));
+  const uint32_t nks = (uint32_t)(cols / 128);
   KernelScope ks("mxfp8_quantize_rows", stream);
-  hipLaunchKernelGGL(mx_rows_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                     stream, static_cast<const uint4*>(src), n_chunks,
-                     reinterpret_cast<uint2*>(codes), scales);
+  if (tiled)
+    hipLaunchKernelGGL(mx_rows_kernel<true>, dim3((unsigned)blocks), dim3(256),
+                       0, stream, static_cast<const uint4*>(src), n_chunks,
+                       bpr, nks, reinterpret_cast<uint2*>(codes), scales);
+  else
+    hipLaunchKernelGGL(mx_rows_kernel<false>, dim3((unsigned)blocks),
+                       dim3(256), 0, stream, static_cast<const uint4*>(src),
+                       n_chunks, bpr, nks, reinterpret_cast<uint2*>(codes),
+                       scales);
   return hipGetLastError();
 }
 
 hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
                                 int64_t cols, uint8_t* codes, uint8_t* scales,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool tiled) {
   if (batch * rows * cols == 0) return hipSuccess;
   const dim3 grid((unsigned)(rows / 32), (unsigned)((cols + 63) / 64),
                   (unsigned)batch);
   KernelScope ks("mxfp8_quantize_cols", stream);
-  hipLaunchKernelGGL(mx_cols_kernel<false>, grid, dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(src), rows, cols,
-                     (const int32_t*)nullptr, 0, 1, rows, codes, scales);
+  if (tiled)
+    hipLaunchKernelGGL((mx_cols_kernel<false, true>), grid, dim3(256), 0,
+                       stream, static_cast<const uint16_t*>(src), rows, cols,
+                       (const int32_t*)nullptr, 0, 1, rows, codes, scales);
+  else
+    hipLaunchKernelGGL((mx_cols_kernel<false, false>), grid, dim3(256), 0,
+                       stream, static_cast<const uint16_t*>(src), rows, cols,
+                       (const int32_t*)nullptr, 0, 1, rows, codes, scales);
   return hipGetLastError();
 }
 
@@ -201,16 +245,35 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
                                     int64_t cols, const int32_t* seg_offsets,
                                     int n_seg, int pad, int64_t ld,
                                     uint8_t* codes, uint8_t* scales,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, bool tiled) {
   if (rows * cols == 0) return hipSuccess;
   const int pad_tiles = pad / 32;
   // sum_s ceil(n_s / pad) * pad / 32 <= rows / 32 + n_seg * pad / 32
   const int64_t tiles = rows / 32 + (int64_t)n_seg * pad_tiles;
   const dim3 grid((unsigned)tiles, (unsigned)((cols + 63) / 64), 1);
   KernelScope ks("mxfp8_quantize_segments", stream);
-  hipLaunchKernelGGL(mx_cols_kernel<true>, grid, dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(src), rows, cols,
-                     seg_offsets, n_seg, pad_tiles, ld, codes, scales);
+  if (tiled)
+    hipLaunchKernelGGL((mx_cols_kernel<true, true>), grid, dim3(256), 0,
+                       stream, static_cast<const uint16_t*>(src), rows, cols,
+                       seg_offsets, n_seg, pad_tiles, ld, codes, scales);
+  else
+    hipLaunchKernelGGL((mx_cols_kernel<true, false>), grid, dim3(256), 0,
+                       stream, static_cast<const uint16_t*>(src), rows, cols,
+                       seg_offsets, n_seg, pad_tiles, ld, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_scales_retile(const uint8_t* src, int64_t rows,
+                                   int64_t k, uint8_t* dst,
+                                   hipStream_t stream) {
+  const uint32_t nks = (uint32_t)(k / 128);
+  const int64_t n = (rows + 31) / 32 * 32 * nks;   // dwords
+  if (n == 0) return hipSuccess;
+  KernelScope ks("mxfp8_scales_retile", stream);
+  hipLaunchKernelGGL(mx_retile_kernel, dim3((unsigned)((n + 255) / 256)),
+                     dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t*>(src), rows, nks,
+                     reinterpret_cast<uint32_t*>(dst));
   return hipGetLastError();
 }
 

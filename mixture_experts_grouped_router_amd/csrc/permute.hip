@@ -240,14 +240,8 @@ __global__ __launch_bounds__(256) void gather_rows_mx_kernel(
     o = __shfl_xor(amax, 2, 64);
     amax = amax > o ? amax : o;
     const int s = e8m0_exp_from_bf16_amax(amax);
-    uint32_t q0 = 0, q1 = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      q0 |= e4m3_from_bf16(w[i] & 0xffffu, s) << (16 * i);
-      q0 |= e4m3_from_bf16(w[i] >> 16, s) << (16 * i + 8);
-      q1 |= e4m3_from_bf16(w[i + 2] & 0xffffu, s) << (16 * i);
-      q1 |= e4m3_from_bf16(w[i + 2] >> 16, s) << (16 * i + 8);
-    }
+    const uint2 qq = e4m3x8_hw(v, s);
+    const uint32_t q0 = qq.x, q1 = qq.y;
     if (act) {
       for (int j = 0; j < k; ++j) {
         const int32_t r = rows[j];

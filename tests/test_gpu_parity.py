@@ -196,6 +196,38 @@ def test_mxfp8_rowwise_all_bf16_patterns(m):
     np.testing.assert_array_equal(scales.cpu().numpy(), rs)
 
 
+def _every_scale_blocks(seed):
+    """One block per (block exponent, magnitude) pair: element 0 is 2^e
+    (e = -133 .. 127, so the scale exponent runs over its whole range and
+    clamps at -127 for tiny blocks), the other 31 are every finite bf16
+    magnitude not above 2^e, with random signs."""
+    rng = np.random.default_rng(seed)
+    mags = np.arange(0x7f80, dtype=np.uint32)      # finite, non-negative
+    rows = []
+    for e in range(-133, 128):
+        top = (e + 127) << 7 if e >= -126 else 1 << (e + 133)
+        cand = mags[mags <= top]
+        cand = np.concatenate([cand, np.zeros(-len(cand) % 31, np.uint32)])
+        cand |= rng.integers(0, 2, size=cand.size).astype(np.uint32) << 15
+        blk = cand.reshape(-1, 31)
+        rows.append(np.concatenate(
+            [np.full((blk.shape[0], 1), top, np.uint32), blk], axis=1))
+    return np.concatenate(rows).astype(np.uint16)
+
+
+def test_mxfp8_every_scale_and_pattern(m):
+    a = _every_scale_blocks(4)                      # [blocks, 32]
+    codes, scales = m.mxfp8_quantize(dev_bf16(a), m.ROWWISE)
+    rc, rs = O.mxfp8_quantize_rows(a)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    # the same blocks down the columns (transposed output)
+    at = np.ascontiguousarray(a[:4096].T)           # [32, 4096]
+    codes, scales = m.mxfp8_quantize(dev_bf16(at), m.COLWISE)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc[:4096])
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs[:4096])
+
+
 def test_mxfp8_rowwise_scale_spread(m):
     # blocks whose amax spans the whole exponent range, including subnormals
     rng = np.random.default_rng(1)
