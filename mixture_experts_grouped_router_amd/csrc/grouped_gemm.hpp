@@ -505,6 +505,14 @@ __device__ __forceinline__ void stage_bf16(char* buf, int row, int col,
   *reinterpret_cast<uint16_t*>(buf + stg_off(row, col >> 3) + (col & 7) * 2) =
       (uint16_t)f32_to_bf16(v);
 }
+// pick a (h == 0) or b (h == 1) with bit operations: a select between two
+// elements of a register array can otherwise become a dynamically indexed
+// array in scratch memory
+__device__ __forceinline__ uint4 pick_half(const uint4 a, const uint4 b,
+                                           uint32_t hmask) {
+  return make_uint4((a.x & ~hmask) | (b.x & hmask), (a.y & ~hmask) | (b.y & hmask),
+                    (a.z & ~hmask) | (b.z & hmask), (a.w & ~hmask) | (b.w & hmask));
+}
 // read k (0..7) of half h of the row returns logical chunk k ^ 4h (lanes
 // of the two halves hit different banks)
 __device__ __forceinline__ uint4 stage_read(const char* buf, int row, int h,
@@ -516,12 +524,11 @@ __device__ __forceinline__ uint4 stage_read(const char* buf, int row, int h,
 // acc[i][j][r] is C[row][col] of the wave's 128 x 128 block with
 //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
 //   col = wn*128 + j*32 + lane%32
-// `scratch` is LDS the epilogue may use after a barrier (SWIGLU_BWD).
 template <int G, int EPI>
 __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
                                          f32x16_t (&acc)[4][4], int n0,
                                          int wm, int wn, int lane, int t,
-                                         char* scratch, char* wbuf) {
+                                         char* wbuf) {
   // acc[i][j][r] is C[row][col] of the wave's block with
   //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
   //   col = wn*128 + j*32 + lane%32
@@ -532,6 +539,42 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
     // silu(g) * u goes through LDS (float32); the routing weight, the
     // bf16 / MXFP8 encoding and the stores happen per row on readback.
     const int64_t ld1 = 2 * (int64_t)p.F;
+    if (p.c2) {
+      // (g, u) save for the backward pass, through LDS as bf16: row r holds
+      // g of the wave's 64 f in columns 0..63 and u in 64..127; on readback
+      // half 0 of a row is its g run, half 1 its u run (128 bytes each)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            stage_bf16(wbuf, acc_row(i, r, lane), jj * 32 + colw,
+                       acc[i][2 * jj][r]);
+            stage_bf16(wbuf, acc_row(i, r, lane), 64 + jj * 32 + colw,
+                       acc[i][2 * jj + 1][r]);
+          }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
+      const int hs = lane & 1;
+      const int f0 = n0 + 64 * wn;          // F % 64 == 0: whole runs
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lr = (lane >> 1) + 32 * q;
+        const int mrow = tc.m0 + wm * 128 + lr;
+        uint4 raw[8], v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) raw[k] = stage_read(wbuf, lr, hs, k);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          v[c] = pick_half(raw[c], raw[c ^ 4], 0u - (uint32_t)hs);
+        if (mrow >= tc.seg_len || f0 >= p.F) continue;
+        const int64_t row = tc.seg0 + mrow;
+        uint4* dst = reinterpret_cast<uint4*>(p.c2 + row * ld1 + hs * p.F + f0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) dst[k] = v[k];
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // readback done before reuse
+    }
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -542,25 +585,6 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
           stage_f32(wbuf, acc_row(i, r, lane), jj * 32 + colw,
                     (g * fast_sigmoid(g)) * u);
         }
-    if (p.c2) {   // (g, u) save for the backward pass: direct stores
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int f = n0 + (2 * wn + jj) * 32 + colw;
-        if (f >= p.F) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int mrow = tc.m0 + wm * 128 + acc_row(i, r, lane);
-            if (mrow < tc.seg_len) {
-              const int64_t row = tc.seg0 + mrow;
-              p.c2[row * ld1 + f] = (uint16_t)f32_to_bf16(acc[i][2 * jj][r]);
-              p.c2[row * ld1 + p.F + f] =
-                  (uint16_t)f32_to_bf16(acc[i][2 * jj + 1][r]);
-            }
-          }
-      }
-    }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
     const int h = lane & 1;                // f block (2 wn + h)
     const int fb = n0 + (2 * wn + h) * 32;
@@ -576,7 +600,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
       float v[32];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const uint4 c4 = h ? raw[c ^ 4] : raw[c];
+        const uint4 c4 = pick_half(raw[c], raw[c ^ 4], 0u - (uint32_t)h);
         v[4 * c + 0] = __uint_as_float(c4.x); v[4 * c + 1] = __uint_as_float(c4.y);
         v[4 * c + 2] = __uint_as_float(c4.z); v[4 * c + 3] = __uint_as_float(c4.w);
       }
@@ -639,7 +663,8 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
 #pragma unroll
       for (int k = 0; k < 8; ++k) raw[k] = stage_read(wbuf, lr, h, k);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) v[c] = h ? raw[c ^ 4] : raw[c];
+      for (int c = 0; c < 8; ++c)
+        v[c] = pick_half(raw[c], raw[c ^ 4], 0u - (uint32_t)h);
       int64_t row;
       if constexpr (G == RAGGED_M) {
         if (mrow >= tc.seg_len) continue;
@@ -654,60 +679,92 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
       for (int k = 0; k < 8; ++k) dst[k] = v[k];
     }
   } else {  // EPI_SWIGLU_BWD: acc = dA[row][f], f = n0 + wn*128 + j*32 + col
-    // the loop's last (unused) fragment reads of stage 0 must finish before
-    // stage 0 becomes the row-sum scratch
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(scratch);  // [2 N-waves][256 rows]
+    // Two passes of 64 f columns through the wave's LDS buffer (float32);
+    // on readback lane l owns rows (l >> 1) + 32 q and the 32 f values of
+    // half h = l & 1: it reads (g, u) of those f with 16-byte loads, writes
+    // dg and du with 16-byte stores and sums dA * silu(g) * u for dw.
+    __shared__ float red[2 * BM];   // row sums of the two N-waves
     const int64_t ld1 = 2 * (int64_t)p.F;
+    const int h = lane & 1;
+    float rsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float rs[16];
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass) __builtin_amdgcn_s_waitcnt(0xc07f);   // readback done
 #pragma unroll
-      for (int r = 0; r < 16; ++r) rs[r] = 0.0f;
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = n0 + wn * 128 + j * 32 + colw;
-        const bool fok = f < p.F;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mrow =
-              tc.m0 + wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-          if (mrow < tc.seg_len && fok) {
-            const int64_t row = tc.seg0 + mrow;
-            const float g = bf16_to_f32(p.h1[row * ld1 + f]);
-            const float u = bf16_to_f32(p.h1[row * ld1 + p.F + f]);
-            const float wr = p.w ? p.w[row] : 1.0f;
-            const float s = fast_sigmoid(g);
-            const float sg = g * s;
-            const float da = acc[i][j][r];
-            const float dg = da * wr * u * (s * (1.0f + g * (1.0f - s)));
-            const float du = da * wr * sg;
-            p.c[row * ld1 + f] = (uint16_t)f32_to_bf16(dg);
-            p.c[row * ld1 + p.F + f] = (uint16_t)f32_to_bf16(du);
-            rs[r] += da * sg * u;
-          }
+          for (int r = 0; r < 16; ++r)
+            stage_f32(wbuf, acc_row(i, r, lane), jj * 32 + colw,
+                      acc[i][2 * pass + jj][r]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
+      const int fb = n0 + wn * 128 + 64 * pass + 32 * h;   // F % 32 == 0
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lr = (lane >> 1) + 32 * q;
+        const int mrow = tc.m0 + wm * 128 + lr;
+        uint4 raw[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) raw[k] = stage_read(wbuf, lr, h, k);
+        if (mrow >= tc.seg_len || fb >= p.F) continue;
+        const int64_t row = tc.seg0 + mrow;
+        float da[32];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint4 c4 = pick_half(raw[c], raw[c ^ 4], 0u - (uint32_t)h);
+          da[4 * c + 0] = __uint_as_float(c4.x);
+          da[4 * c + 1] = __uint_as_float(c4.y);
+          da[4 * c + 2] = __uint_as_float(c4.z);
+          da[4 * c + 3] = __uint_as_float(c4.w);
         }
-      }
-      if (p.dw_part) {
-        // sum over the 32 columns held by the lanes with the same lane / 32
+        const uint4* gp = reinterpret_cast<const uint4*>(p.h1 + row * ld1 + fb);
+        const uint4* up =
+            reinterpret_cast<const uint4*>(p.h1 + row * ld1 + p.F + fb);
+        const float wr = p.w ? p.w[row] : 1.0f;
+        uint4* dgp = reinterpret_cast<uint4*>(p.c + row * ld1 + fb);
+        uint4* dup = reinterpret_cast<uint4*>(p.c + row * ld1 + p.F + fb);
+        float part = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = rs[r];
+        for (int d = 0; d < 4; ++d) {   // 8 f values per 16-byte vector
+          const uint4 g4 = gp[d], u4 = up[d];
+          const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
+          const uint32_t uw[4] = {u4.x, u4.y, u4.z, u4.w};
+          uint32_t dgw[4], duw[4];
 #pragma unroll
-          for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off, 64);
-          if (colw == 0) {
-            const int tr = wm * 128 + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-            red[wn * 256 + tr] = v;
+          for (int e = 0; e < 4; ++e) {
+            float dgv[2], duv[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const float g = hh ? bf16hi(gw[e]) : bf16lo(gw[e]);
+              const float u = hh ? bf16hi(uw[e]) : bf16lo(uw[e]);
+              const float a = da[8 * d + 2 * e + hh];
+              const float sgm = fast_sigmoid(g);
+              const float sg = g * sgm;
+              dgv[hh] = a * wr * u * (sgm * (1.0f + g * (1.0f - sgm)));
+              duv[hh] = a * wr * sg;
+              part += a * sg * u;
+            }
+            dgw[e] = pack_bf16x2(dgv[0], dgv[1]);
+            duw[e] = pack_bf16x2(duv[0], duv[1]);
           }
+          dgp[d] = make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]);
+          dup[d] = make_uint4(duw[0], duw[1], duw[2], duw[3]);
         }
+        rsum[q] += part;
       }
     }
     if (p.dw_part) {
-      // across the 2 N-waves, fixed order
+      // the two halves of a row, then the two N-waves in a fixed order
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float v = rsum[q] + __shfl_xor(rsum[q], 1, 64);
+        if (h == 0) red[wn * BM + wm * 128 + (lane >> 1) + 32 * q] = v;
+      }
       __syncthreads();
       const int mrow = tc.m0 + t;
       if (mrow < tc.seg_len) {
-        const float s = red[t] + red[256 + t];
+        const float s = red[t] + red[BM + t];
         p.dw_part[(int64_t)tc.nt * p.rows + tc.seg0 + mrow] = s;
       }
     }
@@ -935,7 +992,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // direct load has landed) before the stages become epilogue staging
   __syncthreads();
   char* wbuf = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
-  epilogue<G, EPI>(p, tc, acc, n0, wm, wn, lane, t, sA0, wbuf);
+  epilogue<G, EPI>(p, tc, acc, n0, wm, wn, lane, t, wbuf);
 }
 
 // Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn.
