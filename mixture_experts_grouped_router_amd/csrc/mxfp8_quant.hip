@@ -184,6 +184,122 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(
   }
 }
 
+// Column-wise with 128-row tiles: a block covers 128 rows x 64 columns
+// (four blocks of 32 down each column) and writes 128 contiguous code bytes
+// per column.  Thread t loads rows 4 (t >> 3) .. +3 of 16-byte column chunk
+// t & 7 and writes them transposed into LDS ([column][row]); then thread t
+// quantises rows 32 (t & 3) .. +31 of column t >> 2 from four 16-byte LDS
+// reads.  Segment mode: tiles of one segment (zero past its end), output at
+// offsets where every segment starts on a multiple of 128 * pad_tiles.
+template <bool SEG, bool TILED>
+__global__ __launch_bounds__(256) void mx_cols128_kernel(
+    const uint4* __restrict__ src, int64_t rows, int64_t cols,
+    const int32_t* __restrict__ seg_offsets, int n_seg, int pad_tiles,
+    int64_t ld_out, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) uint16_t tileT[64][128 + 8];
+  __shared__ int32_t tprefix[1025];
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.z;
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
+  int64_t r0, rend, out0;
+  if (SEG) {
+    const int pad = 128 * pad_tiles;
+    int32_t cnt4[4], own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sg = 4 * t + i;
+      cnt4[i] = sg < n_seg
+                    ? (seg_offsets[sg + 1] - seg_offsets[sg] + pad - 1) / pad *
+                          pad_tiles
+                    : 0;
+      own += cnt4[i];
+    }
+    int32_t total;
+    int32_t run = block_exclusive_scan_256(own, &total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sg = 4 * t + i;
+      if (sg < n_seg) tprefix[sg] = run;
+      run += cnt4[i];
+    }
+    if (t == 0) tprefix[n_seg] = total;
+    __syncthreads();
+    const int g = blockIdx.x;
+    if (g >= tprefix[n_seg]) return;
+    int lo = 0, hi = n_seg;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tprefix[mid] <= g) lo = mid; else hi = mid;
+    }
+    r0 = seg_offsets[lo] + (int64_t)(g - tprefix[lo]) * 128;
+    rend = seg_offsets[lo + 1];
+    out0 = (int64_t)g * 128;
+  } else {
+    r0 = (int64_t)blockIdx.x * 128;
+    rend = rows;
+    out0 = r0;
+  }
+  const int64_t cpr = cols / 8;   // 16-byte chunks per row (cols % 8 == 0)
+  const uint4* base = src + b * rows * cpr;
+  {
+    const int ch = t & 7, rq = t >> 3;
+    const int64_t c = c0 / 8 + ch;
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 4 * rq + i;
+      v[i] = (r < rend && c < cpr) ? ld_nt(base + r * cpr + c)
+                                   : make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w},
+                              {v[1].x, v[1].y, v[1].z, v[1].w},
+                              {v[2].x, v[2].y, v[2].z, v[2].w},
+                              {v[3].x, v[3].y, v[3].z, v[3].w}};
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const int sh = (cc & 1) * 16;
+      const uint32_t e0 = (w[0][cc >> 1] >> sh) & 0xffffu;
+      const uint32_t e1 = (w[1][cc >> 1] >> sh) & 0xffffu;
+      const uint32_t e2 = (w[2][cc >> 1] >> sh) & 0xffffu;
+      const uint32_t e3 = (w[3][cc >> 1] >> sh) & 0xffffu;
+      *reinterpret_cast<uint2*>(&tileT[8 * ch + cc][4 * rq]) =
+          make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+    }
+  }
+  __syncthreads();
+  const int col = t >> 2, q = t & 3;
+  const int64_t c = c0 + col;
+  const uint4* lp = reinterpret_cast<const uint4*>(&tileT[col][32 * q]);
+  uint32_t x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = lp[i];
+    x[4 * i] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
+  }
+  uint32_t a = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    a = umax(a, umax(x[i] & 0x7fffu, (x[i] >> 16) & 0x7fffu));
+  const int s = e8m0_exp_from_bf16_amax(a);
+  const float sc = mx_scale_f32(s);
+  uint32_t o[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = e4m3x4_hw(x[2 * d], x[2 * d + 1], sc);
+  if (c < cols) {
+    const int64_t orow = b * cols + c;   // output row
+    uint4* dst = reinterpret_cast<uint4*>(codes + orow * ld_out + out0 + 32 * q);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    const int64_t kb = out0 / 32 + q;
+    if (TILED)
+      scales[mx_tile_off((uint32_t)orow, (uint32_t)kb,
+                         (uint32_t)(ld_out / 128))] = (uint8_t)(s + 127);
+    else
+      scales[orow * (ld_out / 32) + kb] = (uint8_t)(s + 127);
+  }
+}
+
 // Row-major scales [rows][4 nks] -> the GEMM layout; one thread per row and
 // K step (a dword), consecutive threads write consecutive dwords.
 __global__ __launch_bounds__(256) void mx_retile_kernel(
@@ -227,9 +343,23 @@ hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
                                 int64_t cols, uint8_t* codes, uint8_t* scales,
                                 hipStream_t stream, bool tiled) {
   if (batch * rows * cols == 0) return hipSuccess;
+  KernelScope ks("mxfp8_quantize_cols", stream);
+  if (rows % 128 == 0) {
+    const dim3 g128((unsigned)(rows / 128), (unsigned)((cols + 63) / 64),
+                    (unsigned)batch);
+    if (tiled)
+      hipLaunchKernelGGL((mx_cols128_kernel<false, true>), g128, dim3(256), 0,
+                         stream, static_cast<const uint4*>(src), rows, cols,
+                         (const int32_t*)nullptr, 0, 1, rows, codes, scales);
+    else
+      hipLaunchKernelGGL((mx_cols128_kernel<false, false>), g128, dim3(256),
+                         0, stream, static_cast<const uint4*>(src), rows,
+                         cols, (const int32_t*)nullptr, 0, 1, rows, codes,
+                         scales);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(rows / 32), (unsigned)((cols + 63) / 64),
                   (unsigned)batch);
-  KernelScope ks("mxfp8_quantize_cols", stream);
   if (tiled)
     hipLaunchKernelGGL((mx_cols_kernel<false, true>), grid, dim3(256), 0,
                        stream, static_cast<const uint16_t*>(src), rows, cols,
@@ -247,11 +377,26 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
                                     uint8_t* codes, uint8_t* scales,
                                     hipStream_t stream, bool tiled) {
   if (rows * cols == 0) return hipSuccess;
+  KernelScope ks("mxfp8_quantize_segments", stream);
+  if (pad % 128 == 0) {
+    const int pt = pad / 128;
+    // sum_s ceil(n_s / pad) * pad / 128 <= rows / 128 + n_seg * pad / 128
+    const int64_t tiles = rows / 128 + (int64_t)n_seg * pt;
+    const dim3 g128((unsigned)tiles, (unsigned)((cols + 63) / 64), 1);
+    if (tiled)
+      hipLaunchKernelGGL((mx_cols128_kernel<true, true>), g128, dim3(256), 0,
+                         stream, static_cast<const uint4*>(src), rows, cols,
+                         seg_offsets, n_seg, pt, ld, codes, scales);
+    else
+      hipLaunchKernelGGL((mx_cols128_kernel<true, false>), g128, dim3(256), 0,
+                         stream, static_cast<const uint4*>(src), rows, cols,
+                         seg_offsets, n_seg, pt, ld, codes, scales);
+    return hipGetLastError();
+  }
   const int pad_tiles = pad / 32;
   // sum_s ceil(n_s / pad) * pad / 32 <= rows / 32 + n_seg * pad / 32
   const int64_t tiles = rows / 32 + (int64_t)n_seg * pad_tiles;
   const dim3 grid((unsigned)tiles, (unsigned)((cols + 63) / 64), 1);
-  KernelScope ks("mxfp8_quantize_segments", stream);
   if (tiled)
     hipLaunchKernelGGL((mx_cols_kernel<true, true>), grid, dim3(256), 0,
                        stream, static_cast<const uint16_t*>(src), rows, cols,

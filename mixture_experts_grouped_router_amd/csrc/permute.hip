@@ -182,6 +182,11 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(
   }
 }
 
+// Row kernels below: one block per token; every thread issues the loads of
+// all its 16-byte chunks of the row (kRowU per pass) before the first use,
+// and the row_map read overlaps them.
+constexpr int kRowU = 4;
+
 // bf16 row copy: x[t] -> x_perm[row_map[t*k+j]] for j < k.
 __global__ __launch_bounds__(256) void gather_rows_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ row_map,
@@ -189,18 +194,31 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(
     uint4* __restrict__ x_perm, float* __restrict__ w_perm) {
   const int64_t t = blockIdx.x;
   __shared__ int32_t rows[64];
-  if (threadIdx.x < k) {
-    const int32_t r = row_map[t * k + threadIdx.x];
-    rows[threadIdx.x] = r;
-    if (w_perm && r >= 0) w_perm[r] = topk_w[t * k + threadIdx.x];
-  }
-  __syncthreads();
   const uint4* src = x + t * (int64_t)H8;
-  for (int c = threadIdx.x; c < H8; c += blockDim.x) {
-    const uint4 v = ld_nt(src + c);
+  for (int c0 = 0; c0 < H8; c0 += 256 * kRowU) {
+    uint4 v[kRowU];
+#pragma unroll
+    for (int u = 0; u < kRowU; ++u) {
+      const int c = c0 + 256 * u + threadIdx.x;
+      v[u] = c < H8 ? ld_nt(src + c) : make_uint4(0, 0, 0, 0);
+    }
+    if (c0 == 0) {
+      if (threadIdx.x < k) {
+        const int32_t r = row_map[t * k + threadIdx.x];
+        rows[threadIdx.x] = r;
+        if (w_perm && r >= 0) w_perm[r] = topk_w[t * k + threadIdx.x];
+      }
+      __syncthreads();
+    }
     for (int j = 0; j < k; ++j) {
       const int32_t r = rows[j];
-      if (r >= 0) st_nt(x_perm + (int64_t)r * H8 + c, v);
+      if (r < 0) continue;
+      uint4* dst = x_perm + (int64_t)r * H8;
+#pragma unroll
+      for (int u = 0; u < kRowU; ++u) {
+        const int c = c0 + 256 * u + threadIdx.x;
+        if (c < H8) st_nt(dst + c, v[u]);
+      }
     }
   }
 }
@@ -214,47 +232,59 @@ __global__ __launch_bounds__(256) void gather_rows_mx_kernel(
     float* __restrict__ w_perm) {
   const int64_t t = blockIdx.x;
   __shared__ int32_t rows[64];
-  if (threadIdx.x < k) {
-    const int32_t r = row_map[t * k + threadIdx.x];
-    rows[threadIdx.x] = r;
-    if (w_perm && r >= 0) w_perm[r] = topk_w[t * k + threadIdx.x];
-  }
-  __syncthreads();
   const int H8 = H >> 3;
   const uint4* src = x + t * (int64_t)H8;
   // H8 is a multiple of 4, so the 4 lanes of a block stay in one pass
-  for (int c0 = 0; c0 < H8; c0 += blockDim.x) {
-    const int c = c0 + threadIdx.x;
-    const bool act = c < H8;
-    uint4 v = act ? src[c] : make_uint4(0, 0, 0, 0);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t amax = 0;
+  for (int c0 = 0; c0 < H8; c0 += 256 * kRowU) {
+    uint4 v[kRowU];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
-      amax = amax > lo ? amax : lo;
-      amax = amax > hi ? amax : hi;
+    for (int u = 0; u < kRowU; ++u) {
+      const int c = c0 + 256 * u + threadIdx.x;
+      v[u] = c < H8 ? ld_nt(src + c) : make_uint4(0, 0, 0, 0);
     }
-    uint32_t o = __shfl_xor(amax, 1, 64);
-    amax = amax > o ? amax : o;
-    o = __shfl_xor(amax, 2, 64);
-    amax = amax > o ? amax : o;
-    const int s = e8m0_exp_from_bf16_amax(amax);
-    const uint2 qq = e4m3x8_hw(v, s);
-    const uint32_t q0 = qq.x, q1 = qq.y;
-    if (act) {
-      for (int j = 0; j < k; ++j) {
-        const int32_t r = rows[j];
-        if (r < 0) continue;
-        uint2* dst = reinterpret_cast<uint2*>(codes + (int64_t)r * H) + c;
-        *dst = make_uint2(q0, q1);
-        if ((c & 3) == 0) scales[(int64_t)r * (H >> 5) + (c >> 2)] = (uint8_t)(s + 127);
+    if (c0 == 0) {
+      if (threadIdx.x < k) {
+        const int32_t r = row_map[t * k + threadIdx.x];
+        rows[threadIdx.x] = r;
+        if (w_perm && r >= 0) w_perm[r] = topk_w[t * k + threadIdx.x];
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < kRowU; ++u) {
+      const int c = c0 + 256 * u + threadIdx.x;
+      if (c0 + 256 * u >= H8) break;   // uniform: the pass ends here
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+        amax = amax > lo ? amax : lo;
+        amax = amax > hi ? amax : hi;
+      }
+      uint32_t o = __shfl_xor(amax, 1, 64);
+      amax = amax > o ? amax : o;
+      o = __shfl_xor(amax, 2, 64);
+      amax = amax > o ? amax : o;
+      const int s = e8m0_exp_from_bf16_amax(amax);
+      const uint2 qq = e4m3x8_hw(v[u], s);
+      if (c < H8) {
+        for (int j = 0; j < k; ++j) {
+          const int32_t r = rows[j];
+          if (r < 0) continue;
+          reinterpret_cast<uint2*>(codes + (int64_t)r * H)[c] = qq;
+          if ((c & 3) == 0)
+            scales[(int64_t)r * (H >> 5) + (c >> 2)] = (uint8_t)(s + 127);
+        }
       }
     }
   }
 }
 
-// y[t] = sum_j c_j * z[row_map[t*k+j]] in float32, ascending j.
+// y[t] = sum_j c_j * z[row_map[t*k+j]] in float32, ascending j; the rows of
+// up to kUnpJ slots are loaded before they are added.
+constexpr int kUnpU = 2, kUnpJ = 4;
+
 __global__ __launch_bounds__(256) void unpermute_kernel(
     const uint4* __restrict__ z, const int32_t* __restrict__ row_map,
     const float* __restrict__ topk_w, int64_t T, int H8, int k,
@@ -267,26 +297,53 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
     cw[threadIdx.x] = topk_w ? topk_w[t * k + threadIdx.x] : 1.0f;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < H8; c += blockDim.x) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const int32_t r = rows[j];
-      if (r < 0) continue;
-      const uint4 v = ld_nt(z + (int64_t)r * H8 + c);
-      const float cj = cw[j];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int c0 = 0; c0 < H8; c0 += 256 * kUnpU) {
+    float acc[kUnpU][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += cj * bf16lo(w[i]);
-        acc[2 * i + 1] += cj * bf16hi(w[i]);
+    for (int u = 0; u < kUnpU; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += kUnpJ) {
+      uint4 v[kUnpJ][kUnpU];
+#pragma unroll
+      for (int jj = 0; jj < kUnpJ; ++jj) {
+        const int j = j0 + jj;
+        const int32_t r = j < k ? rows[j] : -1;
+#pragma unroll
+        for (int u = 0; u < kUnpU; ++u) {
+          const int c = c0 + 256 * u + threadIdx.x;
+          v[jj][u] = (r >= 0 && c < H8) ? ld_nt(z + (int64_t)r * H8 + c)
+                                        : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < kUnpJ; ++jj) {
+        const int j = j0 + jj;
+        if (j >= k || rows[j] < 0) continue;   // uniform over the block
+        const float cj = cw[j];
+#pragma unroll
+        for (int u = 0; u < kUnpU; ++u) {
+          const uint32_t w[4] = {v[jj][u].x, v[jj][u].y, v[jj][u].z,
+                                 v[jj][u].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[u][2 * i] += cj * bf16lo(w[i]);
+            acc[u][2 * i + 1] += cj * bf16hi(w[i]);
+          }
+        }
       }
     }
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    st_nt(y + t * (int64_t)H8 + c, o);
+#pragma unroll
+    for (int u = 0; u < kUnpU; ++u) {
+      const int c = c0 + 256 * u + threadIdx.x;
+      if (c >= H8) continue;
+      uint4 o;
+      o.x = pack_bf16x2(acc[u][0], acc[u][1]);
+      o.y = pack_bf16x2(acc[u][2], acc[u][3]);
+      o.z = pack_bf16x2(acc[u][4], acc[u][5]);
+      o.w = pack_bf16x2(acc[u][6], acc[u][7]);
+      st_nt(y + t * (int64_t)H8 + c, o);
+    }
   }
 }
 

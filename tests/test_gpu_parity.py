@@ -221,11 +221,20 @@ def test_mxfp8_every_scale_and_pattern(m):
     rc, rs = O.mxfp8_quantize_rows(a)
     np.testing.assert_array_equal(scales.cpu().numpy(), rs)
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
-    # the same blocks down the columns (transposed output)
+    # the same blocks down the columns (transposed output): 32 rows, and
+    # 128 rows (four blocks per column, the 128-row tile kernel)
     at = np.ascontiguousarray(a[:4096].T)           # [32, 4096]
     codes, scales = m.mxfp8_quantize(dev_bf16(at), m.COLWISE)
     np.testing.assert_array_equal(codes.cpu().numpy(), rc[:4096])
     np.testing.assert_array_equal(scales.cpu().numpy(), rs[:4096])
+    n = 4000
+    at4 = np.ascontiguousarray(
+        a[:4 * n].reshape(4, n, 32).transpose(0, 2, 1).reshape(128, n))
+    codes, scales = m.mxfp8_quantize(dev_bf16(at4), m.COLWISE)
+    want_c = rc[:4 * n].reshape(4, n, 32).transpose(1, 0, 2).reshape(n, 128)
+    want_s = rs[:4 * n].reshape(4, n).T
+    np.testing.assert_array_equal(codes.cpu().numpy(), want_c)
+    np.testing.assert_array_equal(scales.cpu().numpy(), want_s)
 
 
 def test_mxfp8_rowwise_scale_spread(m):
@@ -241,9 +250,10 @@ def test_mxfp8_rowwise_scale_spread(m):
     np.testing.assert_array_equal(scales.cpu().numpy(), rs)
 
 
-def test_mxfp8_colwise_and_batched(m):
+@pytest.mark.parametrize("rows", [96, 256])   # 32-row and 128-row tiles
+def test_mxfp8_colwise_and_batched(m, rows):
     rng = np.random.default_rng(2)
-    a = bf16_bits(rng.standard_normal((3, 96, 200)).astype(np.float32))
+    a = bf16_bits(rng.standard_normal((3, rows, 200)).astype(np.float32))
     codes, scales = m.mxfp8_quantize(dev_bf16(a), m.COLWISE)
     for b in range(3):
         rc, rs = O.mxfp8_quantize_cols(a[b])
