@@ -449,6 +449,108 @@ def cpu_baseline(cfg, d, n_tokens):
             "seconds": dt}
 
 
+def hbm_extras(m, layer, cfg, st):
+    """HBM-bound kernels timed alone after writing a 1 GiB buffer (which
+    evicts L2 and the 256 MB Infinity Cache), next to a plain device copy
+    of the permute's traffic as the achievable reference."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    stages = dict(layer.stages())
+    res = {}
+    work = {
+        "permute_gather": KERNEL_BYTES["permute_gather"],
+        "permute_gather_mxfp8": KERNEL_BYTES["permute_gather_mxfp8"],
+        "unpermute": KERNEL_BYTES["unpermute"],
+    }
+    fwd_only = lambda c: dataclasses_replace(c)
+    for stage, kname in (("permute", "permute_gather_mxfp8"
+                          if layer.mx_codes else "permute_gather"),
+                         ("unpermute", "unpermute")):
+        times = []
+        for _ in range(5):
+            flush.fill_(1.0)
+            m.reset_kernel_timing()
+            m.set_kernel_timing(True)
+            stages[stage](st)
+            m.set_kernel_timing(False)
+            torch.cuda.synchronize()
+            n, tot = m.kernel_time(kname)
+            times.append(tot / max(n, 1))
+        ms = float(np.median(times))
+        b = work[kname](fwd_only(cfg))
+        res[kname] = {"ms": round(ms, 4), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    m.reset_kernel_timing()
+    # plain device copy with the gather's traffic (read T*H*2, write k
+    # copies), through torch, as the achievable HBM reference
+    nbytes = cfg.T * cfg.H * 2
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dsts = [torch.empty_like(src) for _ in range(cfg.k)]
+    cts = []
+    for _ in range(5):
+        flush.fill_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for d in dsts:
+            d.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        cts.append(e0.elapsed_time(e1))
+    cms = float(np.median(cts))
+    cb = (1 + cfg.k) * nbytes
+    ref = round(cb / (cms * 1e-3) / 1e9, 1)
+    for v in res.values():
+        v["frac_of_copy"] = round(v["GB/s"] / ref, 4)
+    del flush, src, dsts
+    return {"kernels": res,
+            "copy_reference": {"GB/s": ref, "bytes": cb, "what":
+                               f"torch copy of {nbytes} bytes to {cfg.k} "
+                               "destinations, caches flushed"}}
+
+
+def dataclasses_replace(c):
+    """The config with the backward pass off (per-call forward bytes)."""
+    import dataclasses
+    return dataclasses.replace(c, backward=False)
+
+
+def prequantised_step(m, layer, cfg, st, K):
+    """MXFP8 forward with the weights quantised once beforehand (codes and
+    scales passed to the call) instead of inside every call."""
+    import torch
+    E, H, F = cfg.E, cfg.H, cfg.F
+    gq = m.mxfp8_quantize(layer.w_gu.reshape(E * 2 * F, H), m.ROWWISE)
+    dq = m.mxfp8_quantize(layer.w_dn.reshape(E * H, F), m.ROWWISE)
+    fa = layer.fa
+    saved = (fa.w_gu_q, fa.w_gu_s, fa.w_dn_q, fa.w_dn_s, fa.ws, fa.ws_bytes)
+    fa.w_gu_q, fa.w_gu_s = gq[0].data_ptr(), gq[1].data_ptr()
+    fa.w_dn_q, fa.w_dn_s = dq[0].data_ptr(), dq[1].data_ptr()
+    n = ctypes.c_size_t()
+    m._check(layer.lib.moe_grouped_mlp_fwd_workspace_size(ctypes.byref(fa),
+                                                          ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device="cuda")
+    fa.ws, fa.ws_bytes = ws.data_ptr(), ws.numel()
+    stages = layer.stages()
+    for _ in range(2):
+        for _, fn in stages:
+            fn(st)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        for _, fn in stages:
+            fn(st)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    (fa.w_gu_q, fa.w_gu_s, fa.w_dn_q, fa.w_dn_s, fa.ws, fa.ws_bytes) = saved
+    return {"ms_per_step": round(ms, 4),
+            "value": round(cfg.fwd_flop() / (ms * 1e-3) / 1e12, 2)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -526,6 +628,12 @@ def main():
     status = m.check_device_status()
     if status != 0:
         raise RuntimeError(f"device status {status}")
+    peak_mem = torch.cuda.max_memory_allocated()
+    extras = {"hbm_flushed": hbm_extras(m, layer, cfg, st),
+              "peak_device_mem_GiB": round(peak_mem / 2**30, 2)}
+    if cfg.mode == "mxfp8" and not cfg.backward:
+        extras["prequantised_weights"] = prequantised_step(m, layer, cfg, st,
+                                                           max(1, K // 2))
 
     flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
     tflops = flop / (ms_step * 1e-3) / 1e12
@@ -609,6 +717,7 @@ def main():
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),
         "cpu_baseline": cpu,
+        **extras,
     }
     print(json.dumps(out), flush=True)
 
