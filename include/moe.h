@@ -242,6 +242,19 @@ moe_status_t mxfp8_quantize(moe_ctx_t ctx, const void* src, int64_t batch,
  *   a  = w_perm * silu(g) * u        (silu(z) = z / (1 + exp(-z)))
  *   z  = a W_dn[e]^T                 -> z_perm bf16
  * Experts with no rows cost nothing.
+ * MXFP8: X and W_gu are quantised along H, a and W_dn along F (E4M3 + E8M0
+ * per 32, as in mxfp8_quantize ROWWISE); the GEMMs use the gfx950 scaled
+ * MFMA with float32 accumulation; a is quantised from float32 in the gate/up
+ * epilogue; h1_save / a_save hold the unquantised float32 values rounded to
+ * bf16.
+ * Sizes: 1 <= E <= 1024; H and F multiples of 64 (bf16) or 128 (MXFP8);
+ * one expert's operands must stay below 4 GiB (byte offsets are 32-bit).
+ * Errors: MOE_ERR_INVALID_ARG (null required pointer, bad sizes),
+ * MOE_ERR_UNSUPPORTED (size limits, misaligned pointers: operands 16-byte,
+ * MXFP8 scale arrays 4-byte), MOE_ERR_WORKSPACE (ws NULL or smaller than
+ * moe_grouped_mlp_fwd_workspace_size), MOE_ERR_HIP.  The workspace is
+ * scratch owned by the caller; its contents after the call are undefined.
+ * offsets[E] must equal rows (the device reads the per-expert counts).
  * ---------------------------------------------------------------------- */
 typedef struct moe_mlp_fwd_args {
   int32_t E, H, F;               /* experts, hidden, expert FFN size */
@@ -284,8 +297,16 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* args,
  *   dw_perm = sum_f dA * silu(g) * u
  *   dW_dn[e] = dZ^T a,  dW_gu[e] = [dg du]^T X,  dX = [dg du] W_gu[e]
  * Experts with no rows get dW = 0.  MXFP8 mode quantises every GEMM operand
- * along that GEMM's K (token-direction blocks restart at each expert's first
- * row and are zero-padded).
+ * along that GEMM's K: dZ and dH1 = [dg du] row-wise, W_dn and W_gu along
+ * their output dimension, and dZ, a, dH1, X along tokens for the weight
+ * gradients (token-direction blocks restart at each expert's first row and
+ * are zero-padded); dH1 is quantised from its bf16 rounding.  h1_save and
+ * a_save are the forward's saves (bf16) in both modes.
+ * Sizes and errors as moe_grouped_mlp_fwd; MXFP8 also needs
+ * (max(H, 2F) + 256) * (rows + 128 E + 128) < 2^32 (the token-direction
+ * operand copies use 32-bit byte offsets).  The workspace holds dH1 and, in
+ * MXFP8 mode, every quantised operand copy (about 4 GB for T*k = 16384,
+ * H = 4096, F = 14336, E = 8); its contents after the call are undefined.
  * ---------------------------------------------------------------------- */
 typedef struct moe_mlp_bwd_args {
   int32_t E, H, F;

@@ -78,39 +78,6 @@ __device__ __forceinline__ uint2 e4m3x8_hw(const uint4 v, int s) {
   return make_uint2(e4m3x4_hw(v.x, v.y, sc), e4m3x4_hw(v.z, v.w, sc));
 }
 
-// n / d for n < 2^31 by multiply and shift: m = ceil(2^k / d) with
-// k = 31 + ceil(log2 d) (so m < 2^32) is exact for every n < 2^31, since the
-// rounding excess m d - 2^k is below d <= 2^(k - 31).
-struct FastDiv {
-  uint64_t m;
-  uint32_t d;
-  int k;
-};
-inline FastDiv make_fastdiv(uint32_t d) {
-  int l = 0;
-  while ((1ull << l) < d) ++l;
-  FastDiv f;
-  f.d = d;
-  f.k = 31 + l;
-  f.m = ((1ull << f.k) + d - 1) / d;
-  return f;
-}
-__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
-  return (uint32_t)(((uint64_t)n * f.m) >> f.k);
-}
-
-// MXFP8 scales in the layout the scaled-MFMA GEMM reads: for an operand of
-// rows r with K = 128 * nks values each, the four scale bytes of row r and
-// K step s (K blocks 4s .. 4s+3) sit at ((r / 32) * nks + s) * 128 +
-// (r % 32) * 4, so the 32 rows of one MFMA row block read one contiguous
-// 128-byte line per K step.  Storage covers rows rounded up to 32.
-MOE_HD inline uint32_t mx_tile_off(uint32_t r, uint32_t kb, uint32_t nks) {
-  return ((r >> 5) * nks + (kb >> 2)) * 128u + ((r & 31u) << 2) + (kb & 3u);
-}
-inline size_t mx_tile_bytes(int64_t rows, int64_t k) {
-  return (size_t)((rows + 31) / 32) * 32 * (size_t)(k / 32);
-}
-
 // Record the first device-side data error (first error wins).
 __device__ __forceinline__ void report_error(int32_t* status, int32_t code) {
   if (status) atomicCAS(status, 0, code);

@@ -1,7 +1,8 @@
-// MXFP8 element/scale encoding with integer operations only.  Usable from
-// device code (hipcc) and from plain C++ host code (CPU checks of the exact
-// same functions).
+// MXFP8 element/scale encoding with integer operations only, and the index
+// arithmetic of the GEMM scale layout.  Usable from device code (hipcc) and
+// from plain C++ host code (CPU checks of the exact same functions).
 #pragma once
+#include <stddef.h>
 #include <stdint.h>
 
 #if defined(__HIPCC__)
@@ -140,6 +141,39 @@ MOE_HD inline int e8m0_exp_from_f32_amax(uint32_t a) {
   }
   const int s = fl - 8;
   return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// n / d for n < 2^31 by multiply and shift: m = ceil(2^k / d) with
+// k = 31 + ceil(log2 d) (so m < 2^32) is exact for every n < 2^31, since the
+// rounding excess m d - 2^k is below d <= 2^(k - 31).
+struct FastDiv {
+  uint64_t m;
+  uint32_t d;
+  int k;
+};
+MOE_HD inline FastDiv make_fastdiv(uint32_t d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.d = d;
+  f.k = 31 + l;
+  f.m = ((1ull << f.k) + d - 1) / d;
+  return f;
+}
+MOE_HD inline uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+  return (uint32_t)(((uint64_t)n * f.m) >> f.k);
+}
+
+// MXFP8 scales in the layout the scaled-MFMA GEMM reads: for an operand of
+// rows r with K = 128 * nks values each, the four scale bytes of row r and
+// K step s (K blocks 4s .. 4s+3) sit at ((r / 32) * nks + s) * 128 +
+// (r % 32) * 4, so the 32 rows of one MFMA row block read one contiguous
+// 128-byte line per K step.  Storage covers rows rounded up to 32.
+MOE_HD inline uint32_t mx_tile_off(uint32_t r, uint32_t kb, uint32_t nks) {
+  return ((r >> 5) * nks + (kb >> 2)) * 128u + ((r & 31u) << 2) + (kb & 3u);
+}
+inline size_t mx_tile_bytes(int64_t rows, int64_t k) {
+  return (size_t)((rows + 31) / 32) * 32 * (size_t)(k / 32);
 }
 
 }  // namespace moe

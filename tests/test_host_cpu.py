@@ -101,3 +101,14 @@ def test_library_e8m0_exponent_equals_oracle_exhaustive(codec_tables):
     finite = ((a >> 7) & 0xFF) != 0xFF
     want = O.e8m0_exponent(bf16_to_f64(a[finite]))
     np.testing.assert_array_equal(sc[finite].astype(np.int64), want)
+
+
+def test_library_index_helpers(tmp_path):
+    """Multiply-shift division and the MXFP8 GEMM scale layout (host build
+    of the library's helpers)."""
+    exe = str(tmp_path / "layout_check")
+    src = os.path.join(ROOT, "tests", "native", "layout_check.cpp")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, src, "-o", exe],
+                   check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout
