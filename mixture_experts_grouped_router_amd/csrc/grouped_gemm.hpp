@@ -23,8 +23,9 @@
 //  * K-contiguous operands go global -> LDS directly (global_load_lds_dwordx4:
 //    each wave instruction fills one contiguous KiB of LDS, so every lane
 //    picks the global chunk that belongs at its LDS slot).
-//  * MN-contiguous operands (bf16 backward) go through registers and are
-//    transposed 8 x 8 on the way into LDS.
+//  * MN-contiguous operands (bf16 backward) also go global -> LDS directly,
+//    as [k][mn] rows, and the MFMA fragments are read with the transposing
+//    LDS read (ds_read_b64_tr_b16).
 // Tiles are ordered so that each XCD (blocks b = x mod 8) works through one
 // contiguous run of tiles, M fastest inside groups of 4 N tiles: the tiles in
 // flight on one XCD share activation rows and weight panels in its L2.
@@ -242,67 +243,57 @@ struct KcDirect {
   }
 };
 
-// ---- MN-contiguous bf16 operand through registers ---------------------------
-// Thread t covers mn chunk (t & 31) (8 values) for k rows 8 (t >> 5) .. +7;
-// the 8 x 8 block is transposed in registers and written as 8 row chunks.
-struct McStaged {
-  const char* base;       // element (mn = this thread's chunk, k = 0)
-  int64_t ld;             // bytes between consecutive k rows
-  int kvalid;             // k rows >= kvalid read as zero
-  int kr;                 // first k row of the staged block
-  uint4 v0, v1, v2, v3, v4, v5, v6, v7;
-
-  // Rows past kvalid load the last valid row; store() zeroes them, so the
-  // loads stay in flight until the LDS store (callers never load with
-  // kvalid == 0).
-  __device__ __forceinline__ uint4 row(int k) const {
-    const int kc = min(k, kvalid - 1);
-    return *reinterpret_cast<const uint4*>(base + (int64_t)kc * ld);
+// ---- MN-contiguous bf16 operand: direct global -> LDS, transposed reads -----
+// The stage holds the step's 64 k rows of the tile's 256 mn values (512
+// bytes each) as they lie in memory; 16-byte chunk c of row k sits at chunk
+// c ^ 4 (k & 3).  Wave w, instruction j fills KiB 4 j + w = rows
+// 2 (4 j + w) + lane / 32, and each lane loads the logical chunk that
+// belongs at its slot.  MFMA fragments come from ds_read_b64_tr_b16: in a
+// group of 16 lanes, lane i receives element i % 4 of the 8 bytes addressed
+// by lane 4 j + i / 4 as its element j; with lane 4 j + q addressing row
+// k0 + j, mn mb + 4 q .. +3, lane i gets mn mb + i at k0 .. k0 + 3.  Two
+// such reads (k and k + 4) give a lane its 8 k values; the swizzle puts the
+// 4 rows x 2 groups of a read on 16 distinct chunks (no bank conflicts).
+// Rows at or past kvalid read as zeros through the buffer descriptor; mn
+// past the operand's end reads the next row (or zeros): those outputs are
+// never stored.
+struct McDirect {
+  const char* base;  // wave-uniform: element (k = 0, mn = tile start)
+  uint32_t rec;      // valid bytes from base
+  int64_t ld;        // bytes per k row
+  uint32_t off[8];   // per instruction: byte offset of the lane's chunk
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 2 * (4 * j + wave) + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (row & 3));
+      off[j] = (uint32_t)row * (uint32_t)ld + (uint32_t)(c * 16);
+    }
   }
-  __device__ __forceinline__ void load(int k0) {
-    kr = k0 + 8 * (threadIdx.x >> 5);
-    v0 = row(kr + 0); v1 = row(kr + 1); v2 = row(kr + 2); v3 = row(kr + 3);
-    v4 = row(kr + 4); v5 = row(kr + 5); v6 = row(kr + 6); v7 = row(kr + 7);
+  __device__ __forceinline__ void issue(char* lds_tile, int kt, bool real,
+                                        int wave) const {
+    const uint32_t kb = (uint32_t)kt * 64u * (uint32_t)ld;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + kb), (short)0, (int)(real ? rec - kb : 0u),
+        kBufFlags);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      MOE_LDS void* dst =
+          (MOE_LDS void*)(lds_tile + (4 * j + wave) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off[j], 0, 0, 0);
+    }
   }
-  static __device__ __forceinline__ uint4 keep(uint4 v, bool ok) {
-    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u,
-                      ok ? v.w : 0u);
-  }
-  // lo: halves 0 of the two inputs (k even, k odd); hi: halves 1
-  static __device__ __forceinline__ uint32_t plo(uint32_t ke, uint32_t ko) {
-    return __builtin_amdgcn_perm(ko, ke, 0x05040100u);
-  }
-  static __device__ __forceinline__ uint32_t phi(uint32_t ke, uint32_t ko) {
-    return __builtin_amdgcn_perm(ko, ke, 0x07060302u);
-  }
-  static __device__ __forceinline__ void put(char* lds, int r, int c,
-                                             uint4 val) {
-    *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = val;
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-    const int kg = threadIdx.x >> 5;          // k chunk 0..7
-    const int r0 = (threadIdx.x & 31) * 8;    // first mn row
-    const uint4 w0 = keep(v0, kr + 0 < kvalid), w1 = keep(v1, kr + 1 < kvalid);
-    const uint4 w2 = keep(v2, kr + 2 < kvalid), w3 = keep(v3, kr + 3 < kvalid);
-    const uint4 w4 = keep(v4, kr + 4 < kvalid), w5 = keep(v5, kr + 5 < kvalid);
-    const uint4 w6 = keep(v6, kr + 6 < kvalid), w7 = keep(v7, kr + 7 < kvalid);
-    // column pair d of the inputs holds mn 2d (low half) and 2d+1 (high)
-    put(lds, r0 + 0, kg, make_uint4(plo(w0.x, w1.x), plo(w2.x, w3.x),
-                                    plo(w4.x, w5.x), plo(w6.x, w7.x)));
-    put(lds, r0 + 1, kg, make_uint4(phi(w0.x, w1.x), phi(w2.x, w3.x),
-                                    phi(w4.x, w5.x), phi(w6.x, w7.x)));
-    put(lds, r0 + 2, kg, make_uint4(plo(w0.y, w1.y), plo(w2.y, w3.y),
-                                    plo(w4.y, w5.y), plo(w6.y, w7.y)));
-    put(lds, r0 + 3, kg, make_uint4(phi(w0.y, w1.y), phi(w2.y, w3.y),
-                                    phi(w4.y, w5.y), phi(w6.y, w7.y)));
-    put(lds, r0 + 4, kg, make_uint4(plo(w0.z, w1.z), plo(w2.z, w3.z),
-                                    plo(w4.z, w5.z), plo(w6.z, w7.z)));
-    put(lds, r0 + 5, kg, make_uint4(phi(w0.z, w1.z), phi(w2.z, w3.z),
-                                    phi(w4.z, w5.z), phi(w6.z, w7.z)));
-    put(lds, r0 + 6, kg, make_uint4(plo(w0.w, w1.w), plo(w2.w, w3.w),
-                                    plo(w4.w, w5.w), plo(w6.w, w7.w)));
-    put(lds, r0 + 7, kg, make_uint4(phi(w0.w, w1.w), phi(w2.w, w3.w),
-                                    phi(w4.w, w5.w), phi(w6.w, w7.w)));
+  // lane's byte offsets of its 4 32-row blocks (K slice 0, first read) in
+  // the wave's half (side = wm or wn) of the stage
+  static __device__ __forceinline__ void frag_offsets(int side, int lane,
+                                                      uint32_t (&o)[4]) {
+    const int G = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
+    const int k0 = 8 * (G >> 1) + j;
+    const int x = 2 * (G & 1) + (q >> 1) + 16 * side;   // chunk, bits 2-3 clear
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)(k0 * 512 + (((x + 4 * i) ^ (4 * j)) * 16) +
+                        (q & 1) * 8);
   }
 };
 
@@ -349,6 +340,9 @@ __device__ __forceinline__ int frag_off(int fr, int c) {
   return fr * kRowBytes + ((c ^ swz32(fr)) << 4);
 }
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+
 template <>
 struct Frags<P_BF16> {
   static constexpr int kSlices = 4;  // 16-wide K slices per step
@@ -357,19 +351,48 @@ struct Frags<P_BF16> {
     return *reinterpret_cast<const bf16x8_t*>(s + off);
   }
   // lane l: row l%32 of each 32-row block, k 8 (l/32) .. +7 of the slice
-  __device__ __forceinline__ void load(const char* sa, const char* sb, int kk,
-                                       int wm, int wn, int lane) {
-    const int o = frag_off(lane & 31, kk * 2 + (lane >> 5));
-    const char* pa = sa + wm * (128 * kRowBytes) + o;
-    const char* pb = sb + wn * (128 * kRowBytes) + o;
+  __device__ __forceinline__ void load_a(const char* sa, int kk, int wm,
+                                         int lane) {
+    const char* pa = sa + wm * (128 * kRowBytes) +
+                     frag_off(lane & 31, kk * 2 + (lane >> 5));
     a0 = at(pa, 0 * 32 * kRowBytes);
     a1 = at(pa, 1 * 32 * kRowBytes);
     a2 = at(pa, 2 * 32 * kRowBytes);
     a3 = at(pa, 3 * 32 * kRowBytes);
+  }
+  __device__ __forceinline__ void load_b(const char* sb, int kk, int wn,
+                                         int lane) {
+    const char* pb = sb + wn * (128 * kRowBytes) +
+                     frag_off(lane & 31, kk * 2 + (lane >> 5));
     b0 = at(pb, 0 * 32 * kRowBytes);
     b1 = at(pb, 1 * 32 * kRowBytes);
     b2 = at(pb, 2 * 32 * kRowBytes);
     b3 = at(pb, 3 * 32 * kRowBytes);
+  }
+  __device__ __forceinline__ void load(const char* sa, const char* sb, int kk,
+                                       int wm, int wn, int lane) {
+    load_a(sa, kk, wm, lane);
+    load_b(sb, kk, wn, lane);
+  }
+  // 8 k values of the lane from a [k][mn] stage (McDirect layout): two
+  // transposed 8-byte reads, k and k + 4 rows apart
+  static __device__ __forceinline__ bf16x8_t tr8(const char* p) {
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MOE_LDS i16x4_t*)(p));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MOE_LDS i16x4_t*)(p + 4 * 512));
+    const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+  __device__ __forceinline__ void load_a_tr(const char* sa, int kk,
+                                            const uint32_t (&o)[4]) {
+    const char* s = sa + kk * 16 * 512;
+    a0 = tr8(s + o[0]); a1 = tr8(s + o[1]); a2 = tr8(s + o[2]); a3 = tr8(s + o[3]);
+  }
+  __device__ __forceinline__ void load_b_tr(const char* sb, int kk,
+                                            const uint32_t (&o)[4]) {
+    const char* s = sb + kk * 16 * 512;
+    b0 = tr8(s + o[0]); b1 = tr8(s + o[1]); b2 = tr8(s + o[2]); b3 = tr8(s + o[3]);
   }
 };
 
@@ -809,7 +832,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // ---- operand sources ----
   KcDirect<EPI, false> da;
   KcDirect<EPI, true> db;
-  McStaged ma, mb;
+  McDirect ma, mb;
   MxScales ms;
   const int q = 8 * wave + (lane >> 3);   // direct-load row inside 32 rows
   const int cl = (lane & 7) ^ swz32(q);   // its logical chunk
@@ -832,10 +855,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     da.init();
   } else {
     // A element (m, k) at a + (seg0 + k) * lda + 2 m (RAGGED_K: k = token)
-    const int mc = min(tc.m0 + (t & 31) * 8, p.M - 8);
-    ma.base = p.a + (int64_t)tc.seg0 * p.lda + 2 * (int64_t)mc;
+    ma.base = p.a + (int64_t)tc.seg0 * p.lda + 2 * (int64_t)tc.m0;
+    ma.rec = (uint32_t)kdim * (uint32_t)p.lda - 2u * (uint32_t)tc.m0;
     ma.ld = p.lda;
-    ma.kvalid = kdim;
+    ma.init(wave, lane);
   }
   const char* bexp = p.b + (int64_t)tc.e * p.b_es;
   if constexpr (LB == KC) {
@@ -856,12 +879,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     db.N = p.N;
     db.init();
   } else {
-    const int nc = min(n0 + (t & 31) * 8, p.N - 8);
-    if constexpr (G == RAGGED_M) mb.base = bexp + 2 * (int64_t)nc;
-    else mb.base = p.b + (int64_t)tc.seg0 * p.ldb + 2 * (int64_t)nc;
+    // B element (n, k) at b_e + k * ldb + 2 n (RAGGED_K: b + (seg0 + k) ...)
+    if constexpr (G == RAGGED_M) mb.base = bexp + 2 * (int64_t)n0;
+    else mb.base = p.b + (int64_t)tc.seg0 * p.ldb + 2 * (int64_t)n0;
+    mb.rec = (uint32_t)kdim * (uint32_t)p.ldb - 2u * (uint32_t)n0;
     mb.ld = p.ldb;
-    mb.kvalid = kdim;
+    mb.init(wave, lane);
   }
+  // transposed-read offsets of the MN-contiguous sides
+  uint32_t tra[4], trb[4];
+  if constexpr (LA == MC) McDirect::frag_offsets(wm, lane, tra);
+  if constexpr (LB == MC) McDirect::frag_offsets(wn, lane, trb);
   uint32_t sa_cur[4] = {0, 0, 0, 0}, sb_cur[4] = {0, 0, 0, 0};
   // byte selector for v_perm: lane group g takes scale bytes (g, 2 + g)
   const uint32_t sel = (lane >> 5) ? 0x0c0c0301u : 0x0c0c0200u;
@@ -902,15 +930,26 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     // direct loads, k rows past kvalid for staged loads; its scales are
     // those of the last real step (finite; they multiply zeros)
     if constexpr (LA == KC) da.issue(bufa, (uint32_t)kt * kRowBytes, real, wave);
-    else ma.load(kt * kStepK);
+    else ma.issue(bufa, kt, real, wave);
     if constexpr (LB == KC) db.issue(bufb, (uint32_t)kt * kRowBytes, real, wave);
-    else mb.load(kt * kStepK);
+    else mb.issue(bufb, kt, real, wave);
     if constexpr (P == P_FP8) ms.load(min(kt, nk - 1));
   };
-  auto stage_store = [&](char* bufa, char* bufb) {
-    if constexpr (LA == MC) ma.store(bufa);
-    if constexpr (LB == MC) mb.store(bufb);
+  // fragments of K slice kk from stage (sa, sb)
+  auto fload = [&](Fr& f, const char* sa, const char* sb, int kk) {
+    if constexpr (LA == KC && LB == KC) {
+      f.load(sa, sb, kk, wm, wn, lane);
+    } else {
+      if constexpr (LA == MC) f.load_a_tr(sa, kk, tra);
+      else f.load_a(sa, kk, wm, lane);
+      if constexpr (LB == MC) f.load_b_tr(sb, kk, trb);
+      else f.load_b(sb, kk, wn, lane);
+    }
   };
+  // LDS reads per K slice: 4 per K-contiguous side (16-byte reads), 8 per
+  // MN-contiguous side (two 8-byte transposed reads per block); MXFP8 16
+  constexpr int kNR = P == P_FP8 ? 16
+                                 : (LA == KC ? 4 : 8) + (LB == KC ? 4 : 8);
   auto take_scales = [&]() {
     if constexpr (P == P_FP8) {
 #pragma unroll
@@ -931,37 +970,33 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // the loads of the next stage get all MFMAs before it to land, and the
   // first reads of the next stage overlap the MFMAs after it.
   const int nk2 = (nk + 1) & ~1;
-  if (nk > 0) {
-    issue(sA0, sB0, 0, true);
-    stage_store(sA0, sB0);
-  }
+  if (nk > 0) issue(sA0, sB0, 0, true);
   __syncthreads();
   take_scales();
   Fr cur, nxt;
-  cur.load(sA0, sB0, 0, wm, wn, lane);
+  fload(cur, sA0, sB0, 0);
 
   for (int kt = 0; kt < nk2; kt += 2) {
     // stage kt from buffers 0 while stage kt+1 loads into buffers 1
     issue(sA1, sB1, kt + 1, kt + 1 < nk);
 #pragma unroll
     for (int kk = 0; kk < kSl - 1; ++kk) {
-      nxt.load(sA0, sB0, kk + 1, wm, wn, lane);
+      fload(nxt, sA0, sB0, kk + 1);
       if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
       else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
       cur = nxt;
-      sched_reads_mfma<P == P_FP8 ? 16 : 8, 16>();
+      sched_reads_mfma<kNR, 16>();
       // keep the scheduler from hoisting later slices' reads (registers)
       __builtin_amdgcn_sched_barrier(0);
     }
-    stage_store(sA1, sB1);
     Mma<P>::template run<kSl - 1, 0>(cur, sa_cur, sb_cur, acc);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    nxt.load(sA1, sB1, 0, wm, wn, lane);
+    fload(nxt, sA1, sB1, 0);
     Mma<P>::template run<kSl - 1, 1>(cur, sa_cur, sb_cur, acc);
     cur = nxt;
     take_scales();
-    sched_reads_mfma<P == P_FP8 ? 16 : 8, 8>();
+    sched_reads_mfma<kNR, 8>();
     __builtin_amdgcn_sched_barrier(0);
 
     // stage kt+1 from buffers 1 while stage kt+2 loads into buffers 0 (a
@@ -969,22 +1004,21 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     issue(sA0, sB0, kt + 2, kt + 2 < nk);
 #pragma unroll
     for (int kk = 0; kk < kSl - 1; ++kk) {
-      nxt.load(sA1, sB1, kk + 1, wm, wn, lane);
+      fload(nxt, sA1, sB1, kk + 1);
       if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
       else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
       cur = nxt;
-      sched_reads_mfma<P == P_FP8 ? 16 : 8, 16>();
+      sched_reads_mfma<kNR, 16>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    stage_store(sA0, sB0);
     Mma<P>::template run<kSl - 1, 0>(cur, sa_cur, sb_cur, acc);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    nxt.load(sA0, sB0, 0, wm, wn, lane);
+    fload(nxt, sA0, sB0, 0);
     Mma<P>::template run<kSl - 1, 1>(cur, sa_cur, sb_cur, acc);
     cur = nxt;
     take_scales();
-    sched_reads_mfma<P == P_FP8 ? 16 : 8, 8>();
+    sched_reads_mfma<kNR, 8>();
     __builtin_amdgcn_sched_barrier(0);
   }
 
