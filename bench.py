@@ -300,7 +300,7 @@ KERNELS = [
     "gemm_wgrad_gate_up", "gemm_dgrad_down_swiglu_bwd_mxfp8",
     "gemm_dgrad_gate_up_mxfp8", "gemm_wgrad_down_mxfp8",
     "gemm_wgrad_gate_up_mxfp8", "routing_weight_grad_reduce", "probs_grad",
-    "tile_table", "padded_offsets",
+    "tile_table", "padded_offsets", "expert_order",
 ]
 # algorithmic flop per step (each GEMM runs once per step)
 _F4 = lambda c: 4.0 * c.rows * c.H * c.F

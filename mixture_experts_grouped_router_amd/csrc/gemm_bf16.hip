@@ -48,6 +48,23 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(
   if (e == E - 1) tile_start[E] = excl + v;
 }
 
+// Rank of expert e by rows, descending; equal counts keep index order.
+__global__ __launch_bounds__(1024) void expert_order_kernel(
+    const int32_t* __restrict__ offsets, int E, int32_t* __restrict__ order) {
+  __shared__ int32_t len[1024];
+  const int e = threadIdx.x;
+  if (e < E) len[e] = offsets[e + 1] - offsets[e];
+  __syncthreads();
+  if (e >= E) return;
+  const int le = len[e];
+  int r = 0;
+  for (int j = 0; j < E; ++j) {
+    const int lj = len[j];
+    r += (lj > le) | ((lj == le) & (j < e));
+  }
+  order[r] = e;
+}
+
 namespace {
 // dw_perm[r] = sum over N tiles (ascending) of the partial row sums.
 __global__ __launch_bounds__(256) void reduce_parts_kernel(
@@ -66,6 +83,14 @@ hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
   KernelScope ks("tile_table", stream);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
                      offsets, E, BM, tn, tile_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_order(const int32_t* offsets, int E, int32_t* order,
+                               hipStream_t stream) {
+  KernelScope ks("expert_order", stream);
+  hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(1024), 0, stream,
+                     offsets, E, order);
   return hipGetLastError();
 }
 
@@ -153,7 +178,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
 
 size_t mlp_bwd_bf16_ws_bytes(int E, int H, int F, int64_t rows) {
   const int tnf = (F + BN - 1) / BN;
-  size_t b = 2 * align256((size_t)(E + 1) * sizeof(int32_t));
+  size_t b = 3 * align256((size_t)(E + 1) * sizeof(int32_t));
   b += align256((size_t)rows * 2 * F * 2);        // dH1
   b += align256((size_t)tnf * rows * sizeof(float));  // dw partials
   return b;
@@ -172,6 +197,8 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
   int32_t* ts_f = reinterpret_cast<int32_t*>(wp);
   wp += align256((size_t)(E + 1) * sizeof(int32_t));
   int32_t* ts_h = reinterpret_cast<int32_t*>(wp);
+  wp += align256((size_t)(E + 1) * sizeof(int32_t));
+  int32_t* order = reinterpret_cast<int32_t*>(wp);
   wp += align256((size_t)(E + 1) * sizeof(int32_t));
   uint16_t* dh1 = reinterpret_cast<uint16_t*>(wp);
   wp += align256((size_t)rows * 2 * F * 2);
@@ -232,8 +259,11 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     if (err != hipSuccess) return err;
   }
   // wgrad2: dW_dn[e] [H, F] = dZ_e^T A_e   (K = rows of expert e)
+  err = launch_expert_order(offsets, E, order, stream);
+  if (err != hipSuccess) return err;
   {
     Params p{};
+    p.order = order;
     p.a = static_cast<const char*>(dz_perm);
     p.lda = 2 * (int64_t)H;
     p.b = static_cast<const char*>(a_save);
@@ -256,6 +286,7 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
   // wgrad1: dW_gu[e] [2F, H] = dH1_e^T X_e
   {
     Params p{};
+    p.order = order;
     p.a = reinterpret_cast<const char*>(dh1);
     p.lda = 4 * (int64_t)F;
     p.b = static_cast<const char*>(x_perm);

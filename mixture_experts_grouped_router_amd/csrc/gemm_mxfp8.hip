@@ -187,6 +187,7 @@ struct MxBwdWs {
   int32_t* ts_f;   // tile prefix, N = F
   int32_t* ts_h;   // tile prefix, N = H
   int32_t* poff;   // padded token offsets [E+1]
+  int32_t* order;  // experts by decreasing rows
   uint16_t* dh1;   // bf16 [rows, 2F]
   float* part;     // dw partial sums [tiles along F][rows]
   // codes, and scales in the GEMM layout
@@ -224,6 +225,7 @@ MxBwdWs carve_bwd(void* base, int E, int H, int F, int64_t rows) {
   w.ts_f = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
   w.ts_h = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
   w.poff = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  w.order = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
   w.dh1 = reinterpret_cast<uint16_t*>(take((size_t)rows * F2 * 2));
   w.part = reinterpret_cast<float*>(take((size_t)tnf * rows * 4));
   w.dzq = take8((size_t)rows * H);
@@ -260,10 +262,11 @@ __global__ __launch_bounds__(256) void mx_reduce_parts_kernel(
 // Token-direction GEMM dW[e] [M, N] = sum over the expert's padded tokens of
 // At[m][tok] Bt[n][tok] (both quantised along tokens).
 hipError_t wgrad_mx(const char* name, int E, int M, int N, int64_t ld,
-                    const int32_t* poff, const uint8_t* aq, const uint8_t* as,
-                    const uint8_t* bq, const uint8_t* bs, void* dw,
-                    hipStream_t stream) {
+                    const int32_t* poff, const int32_t* order,
+                    const uint8_t* aq, const uint8_t* as, const uint8_t* bq,
+                    const uint8_t* bs, void* dw, hipStream_t stream) {
   Params p{};
+  p.order = order;
   p.a = reinterpret_cast<const char*>(aq);
   p.lda = ld;
   p.sa = as;
@@ -304,6 +307,7 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
   const int tnh = (H + BN - 1) / BN;
   const int F2 = 2 * F;
   hipError_t err = launch_padded_offsets(offsets, E, kTokPad, w.poff, stream);
+  if (err == hipSuccess) err = launch_expert_order(offsets, E, w.order, stream);
   if (rows > 0) {
     if (err == hipSuccess) err = launch_tile_table(offsets, E, tnf, w.ts_f, stream);
     if (err == hipSuccess) err = launch_tile_table(offsets, E, tnh, w.ts_h, stream);
@@ -399,10 +403,10 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
   if (err != hipSuccess) return err;
   // wgrad: every expert gets a tile set; K = its padded token count (0 for
   // an expert without rows, whose weight gradient is then stored as zeros)
-  err = wgrad_mx("gemm_wgrad_down_mxfp8", E, H, F, w.ld, w.poff, w.dzt,
+  err = wgrad_mx("gemm_wgrad_down_mxfp8", E, H, F, w.ld, w.poff, w.order, w.dzt,
                  w.dzts, w.at, w.ats, dw_dn, stream);
   if (err == hipSuccess)
-    err = wgrad_mx("gemm_wgrad_gate_up_mxfp8", E, F2, H, w.ld, w.poff, w.ht,
+    err = wgrad_mx("gemm_wgrad_gate_up_mxfp8", E, F2, H, w.ld, w.poff, w.order, w.ht,
                    w.hts, w.xt, w.xts, dw_gu, stream);
   return err;
 }

@@ -47,6 +47,12 @@ constexpr int kThreads = 256;
 constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand stage
 constexpr int kGroupN = 4;                  // N tiles per scheduling group
 constexpr int kXcds = 8;
+#ifndef MOE_DEAL_K
+#define MOE_DEAL_K 4
+#endif
+// RAGGED_K launches: consecutive tiles (largest expert first) are dealt to
+// the XCDs in runs of this many, so every XCD gets a share of each expert
+constexpr int kDealK = MOE_DEAL_K;
 
 enum Layout { KC = 0, MC = 1 };  // memory: [mn][k] or [k][mn]
 enum Group { RAGGED_M = 0, RAGGED_K = 1 };
@@ -98,6 +104,7 @@ struct Params {
   int E;
   const int32_t* offsets;     // [E+1] rows per expert
   const int32_t* tile_start;  // RAGGED_M: [E+1] tile prefix
+  const int32_t* order;       // RAGGED_K: experts by decreasing rows
   int tiles_n;                // tiles along N
   int tiles_m;                // RAGGED_K: tiles along M
   int b_rows;                 // rows of one expert's B (KC direct loads)
@@ -141,16 +148,16 @@ struct TileCoord {
 template <int G>
 __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
   const int b = blockIdx.x;
-  int total;
-  if constexpr (G == RAGGED_M) total = p.tile_start[p.E];
-  else total = p.E * p.tiles_m * p.tiles_n;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int idx = b / kXcds;
-  if (idx >= per) return false;
-  const int L = (b % kXcds) * per + idx;
-  if (L >= total) return false;
   int e, local, mt_e;
   if constexpr (G == RAGGED_M) {
+    // XCD x (= b mod 8) takes the x-th contiguous eighth of the tile list,
+    // so an expert's tiles share one L2
+    const int total = p.tile_start[p.E];
+    const int per = (total + kXcds - 1) / kXcds;
+    const int idx = b / kXcds;
+    if (idx >= per) return false;
+    const int L = (b % kXcds) * per + idx;
+    if (L >= total) return false;
     // tile_start[e] <= L < tile_start[e+1]; experts without tiles have
     // tile_start[e] == tile_start[e+1] and are never selected
     int lo = 0, hi = p.E;
@@ -163,9 +170,16 @@ __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
     const int len = p.offsets[e + 1] - p.offsets[e];
     mt_e = (len + BM - 1) / BM;
   } else {
+    // a tile's cost is its expert's row count: tiles are taken largest
+    // expert first and dealt round the XCDs in runs of kDealK, so every
+    // XCD gets an even share of the long tiles and runs them first
     const int per_e = p.tiles_m * p.tiles_n;
-    e = L / per_e;
-    local = L - e * per_e;
+    const int x = b % kXcds, idx = b / kXcds;
+    const int L = ((idx / kDealK) * kXcds + x) * kDealK + idx % kDealK;
+    if (L >= p.E * per_e) return false;
+    const int rank = L / per_e;
+    e = p.order[rank];
+    local = L - rank * per_e;
     mt_e = p.tiles_m;
   }
   // groups of kGroupN N-tiles, M tiles fastest inside a group
@@ -1044,7 +1058,8 @@ inline int ragged_m_grid(int64_t rows, int E, int tn) {
 }
 
 inline int ragged_k_grid(int E, int tiles_m, int tiles_n) {
-  return (E * tiles_m * tiles_n + kXcds - 1) / kXcds * kXcds;
+  constexpr int r = kXcds * kDealK;
+  return (E * tiles_m * tiles_n + r - 1) / r * r;
 }
 
 template <int P, int LA, int LB, int G, int EPI>
@@ -1059,6 +1074,10 @@ hipError_t launch(const char* name, const Params& p, int grid,
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
                              int32_t* tile_start, hipStream_t stream);
+// order[i] = the expert with the i-th most rows (equal counts: lower index
+// first); E <= 1024
+hipError_t launch_expert_order(const int32_t* offsets, int E, int32_t* order,
+                               hipStream_t stream);
 // poff[e] = sum_{e' < e} ceil(M_e' / pad) * pad, poff[E] the total
 hipError_t launch_padded_offsets(const int32_t* offsets, int E, int pad,
                                  int32_t* poff, hipStream_t stream);
