@@ -32,15 +32,15 @@ __device__ __forceinline__ float bf16lo(uint32_t pair) {
 __device__ __forceinline__ float bf16hi(uint32_t pair) {
   return __uint_as_float(pair & 0xffff0000u);
 }
-// float32 -> bfloat16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// float -> bf16 with round to nearest even (v_cvt_pk_bf16_f32)
+typedef __bf16 moe_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(
+      uint32_t, __builtin_convertvector(moe_f32x2_t{lo, hi}, moe_bf16x2_t));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // ---- MXFP8 encoding with the gfx950 scaled conversion ----------------------

@@ -522,10 +522,9 @@ struct Mma<P_FP8> {
 // A wave stages its outputs in its own 32 KiB LDS array: 128 rows of 256
 // bytes (64 float32 or 128 bf16), 16-byte chunk c of row r stored at chunk
 // c ^ (r & 3).  A staging write (one row, 32 lanes, 128 contiguous bytes)
-// and a readback (8 lanes = 4 rows x 2 halves, rotated chunk order) are
-// free of bank conflicts.  On readback lane l owns rows (l >> 1) + 32 q,
-// q = 0..3, and half h = l & 1 of each: whole 32-wide f blocks (float32)
-// or 64 contiguous bf16, written to HBM with 16-byte stores.
+// is free of bank conflicts.  Readback gives consecutive lanes consecutive
+// 16-byte chunks of a row (16 lanes per bf16 row, 8 lanes per 32 float32
+// of a row), so each wave-wide global store covers whole 128-byte lines.
 __device__ __forceinline__ int stg_off(int r, int c) {
   return r * 256 + ((c ^ (r & 3)) << 4);
 }
@@ -542,25 +541,36 @@ __device__ __forceinline__ void stage_bf16(char* buf, int row, int col,
   *reinterpret_cast<uint16_t*>(buf + stg_off(row, col >> 3) + (col & 7) * 2) =
       (uint16_t)f32_to_bf16(v);
 }
-// pick a (h == 0) or b (h == 1) with bit operations: a select between two
-// elements of a register array can otherwise become a dynamically indexed
-// array in scratch memory
-__device__ __forceinline__ uint4 pick_half(const uint4 a, const uint4 b,
-                                           uint32_t hmask) {
-  return make_uint4((a.x & ~hmask) | (b.x & hmask), (a.y & ~hmask) | (b.y & hmask),
-                    (a.z & ~hmask) | (b.z & hmask), (a.w & ~hmask) | (b.w & hmask));
-}
-// read k (0..7) of half h of the row returns logical chunk k ^ 4h (lanes
-// of the two halves hit different banks)
-__device__ __forceinline__ uint4 stage_read(const char* buf, int row, int h,
-                                            int k) {
-  return *reinterpret_cast<const uint4*>(buf + stg_off(row, 8 * h + (k ^ (4 * h))));
+__device__ __forceinline__ uint4 stage_chunk(const char* buf, int row, int c) {
+  return *reinterpret_cast<const uint4*>(buf + stg_off(row, c));
 }
 
 // ---- epilogues -------------------------------------------------------------
 // acc[i][j][r] is C[row][col] of the wave's 128 x 128 block with
 //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
 //   col = wn*128 + j*32 + lane%32
+// Routing weights of the wave's 128 rows in the wave's own LDS array: lane l
+// loads rows l and 64 + l (clamped to the expert; 1 without weights) before
+// any store of the epilogue, so the wait for them waits for no store.
+__device__ __forceinline__ float* row_weights(const Params& p,
+                                              const TileCoord& tc, int mw,
+                                              int lane, int t) {
+  __shared__ float wrow_all[kThreads / 64][128];
+  float* wrow = wrow_all[t >> 6];
+  float w0 = 1.0f, w1 = 1.0f;
+  if (p.w) {
+    w0 = p.w[tc.seg0 + min(mw + lane, tc.seg_len - 1)];
+    w1 = p.w[tc.seg0 + min(mw + 64 + lane, tc.seg_len - 1)];
+  }
+  wrow[lane] = w0;
+  wrow[64 + lane] = w1;
+  return wrow;
+}
+
+// Global loads and stores share one in-order counter (vmcnt): a wait for a
+// load also waits for every store issued before it.  So each epilogue issues
+// its loads (routing weights, saved g and u) ahead of the stores they would
+// otherwise wait behind, and reads LDS in batches before storing.
 template <int G, int EPI>
 __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
                                          f32x16_t (&acc)[4][4], int n0,
@@ -570,16 +580,20 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
   //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
   //   col = wn*128 + j*32 + lane%32
   const int colw = lane & 31;
-  const int rsub = (lane >> 5) * 4;
+  const int mw = tc.m0 + wm * 128;   // first row of the wave's block
   if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
     // B rows of block j: gate f-block (2 wn + j/2) for even j, up for odd j.
     // silu(g) * u goes through LDS (float32); the routing weight, the
-    // bf16 / MXFP8 encoding and the stores happen per row on readback.
+    // bf16 / MXFP8 encoding and the stores happen per row on readback,
+    // where lane l owns rows 8 q + l / 8 and f values 8 (l % 8) .. + 7 of
+    // the wave's 64 (a quad of lanes holds one 32-value MXFP8 block).
     const int64_t ld1 = 2 * (int64_t)p.F;
+    const bool fvalid = n0 + 64 * wn < p.F;   // F % 64 == 0: whole runs
+    float* wrow = row_weights(p, tc, mw, lane, t);
     if (p.c2) {
       // (g, u) save for the backward pass, through LDS as bf16: row r holds
       // g of the wave's 64 f in columns 0..63 and u in 64..127; on readback
-      // half 0 of a row is its g run, half 1 its u run (128 bytes each)
+      // lane l takes chunk l % 16 of row 4 q + l / 16 (chunks 0-7 g, 8-15 u)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -592,23 +606,21 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
                        acc[i][2 * jj + 1][r]);
           }
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
-      const int hs = lane & 1;
-      const int f0 = n0 + 64 * wn;          // F % 64 == 0: whole runs
+      const int ch = lane & 15;
+      const int coff = (ch >> 3) * p.F + n0 + 64 * wn + 8 * (ch & 7);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int lr = (lane >> 1) + 32 * q;
-        const int mrow = tc.m0 + wm * 128 + lr;
-        uint4 raw[8], v[8];
+      for (int qb = 0; qb < 32; qb += 4) {
+        uint4 v[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) raw[k] = stage_read(wbuf, lr, hs, k);
+        for (int q = 0; q < 4; ++q)
+          v[q] = stage_chunk(wbuf, 4 * (qb + q) + (lane >> 4), ch);
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          v[c] = pick_half(raw[c], raw[c ^ 4], 0u - (uint32_t)hs);
-        if (mrow >= tc.seg_len || f0 >= p.F) continue;
-        const int64_t row = tc.seg0 + mrow;
-        uint4* dst = reinterpret_cast<uint4*>(p.c2 + row * ld1 + hs * p.F + f0);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) dst[k] = v[k];
+        for (int q = 0; q < 4; ++q) {
+          const int mrow = mw + 4 * (qb + q) + (lane >> 4);
+          if (fvalid && mrow < tc.seg_len)
+            *reinterpret_cast<uint4*>(p.c2 + (tc.seg0 + mrow) * ld1 + coff) =
+                v[q];
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);   // readback done before reuse
     }
@@ -623,63 +635,67 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
                     (g * fast_sigmoid(g)) * u);
         }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
-    const int h = lane & 1;                // f block (2 wn + h)
-    const int fb = n0 + (2 * wn + h) * 32;
+    const int c8 = lane & 7;
+    const int f = n0 + 64 * wn + 8 * c8;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lr = (lane >> 1) + 32 * q;
-      const int mrow = tc.m0 + wm * 128 + lr;
-      // chunk k of the read order is logical chunk k ^ 4h: undo with a
-      // per-lane select (static register indices)
-      uint4 raw[8];
+    for (int qb = 0; qb < 16; qb += 4) {
+      uint4 c0[4], c1[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) raw[k] = stage_read(wbuf, lr, h, k);
-      float v[32];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint4 c4 = pick_half(raw[c], raw[c ^ 4], 0u - (uint32_t)h);
-        v[4 * c + 0] = __uint_as_float(c4.x); v[4 * c + 1] = __uint_as_float(c4.y);
-        v[4 * c + 2] = __uint_as_float(c4.z); v[4 * c + 3] = __uint_as_float(c4.w);
+      for (int q = 0; q < 4; ++q) {
+        const int lr = 8 * (qb + q) + (lane >> 3);
+        c0[q] = stage_chunk(wbuf, lr, 2 * c8);
+        c1[q] = stage_chunk(wbuf, lr, 2 * c8 + 1);
       }
-      if (mrow >= tc.seg_len || fb >= p.F) continue;
-      const int64_t row = tc.seg0 + mrow;
-      const float wr = p.w ? p.w[row] : 1.0f;
 #pragma unroll
-      for (int c = 0; c < 32; ++c) v[c] *= wr;
-      if constexpr (EPI == EPI_SWIGLU_MX) {
-        // F % 128 == 0: f blocks are whole
-        uint32_t am = 0;
+      for (int q = 0; q < 4; ++q) {
+        const int mrow = mw + 8 * (qb + q) + (lane >> 3);
+        const bool ok = fvalid && mrow < tc.seg_len;
+        const int64_t row = tc.seg0 + mrow;
+        const float wr = wrow[8 * (qb + q) + (lane >> 3)];
+        float v[8] = {__uint_as_float(c0[q].x), __uint_as_float(c0[q].y),
+                      __uint_as_float(c0[q].z), __uint_as_float(c0[q].w),
+                      __uint_as_float(c1[q].x), __uint_as_float(c1[q].y),
+                      __uint_as_float(c1[q].z), __uint_as_float(c1[q].w)};
 #pragma unroll
-        for (int c = 0; c < 32; ++c) {
-          const uint32_t a = __float_as_uint(v[c]) & 0x7fffffffu;
-          am = am > a ? am : a;
+        for (int c = 0; c < 8; ++c) v[c] *= wr;
+        if constexpr (EPI == EPI_SWIGLU_MX) {
+          // F % 128 == 0: blocks are whole; every lane takes part in the
+          // quad reduction, rows past the expert just do not store
+          uint32_t am = 0;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t a = __float_as_uint(v[c]) & 0x7fffffffu;
+            am = am > a ? am : a;
+          }
+          uint32_t o = __shfl_xor(am, 1, 64);
+          am = am > o ? am : o;
+          o = __shfl_xor(am, 2, 64);
+          am = am > o ? am : o;
+          const int sx = e8m0_exp_from_f32_amax(am);
+          uint32_t w8[2];
+#pragma unroll
+          for (int d = 0; d < 2; ++d)
+            w8[d] = e4m3_from_f32(__float_as_uint(v[4 * d]), sx) |
+                    (e4m3_from_f32(__float_as_uint(v[4 * d + 1]), sx) << 8) |
+                    (e4m3_from_f32(__float_as_uint(v[4 * d + 2]), sx) << 16) |
+                    (e4m3_from_f32(__float_as_uint(v[4 * d + 3]), sx) << 24);
+          if (ok) {
+            *reinterpret_cast<uint2*>(p.cq + row * p.F + f) =
+                make_uint2(w8[0], w8[1]);
+            if ((c8 & 3) == 0)
+              p.cs[mx_tile_off((uint32_t)row, (uint32_t)(f / 32),
+                               (uint32_t)(p.F / 128))] = (uint8_t)(sx + 127);
+          }
         }
-        const int sx = e8m0_exp_from_f32_amax(am);
-        uint32_t w8[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-          w8[d] = e4m3_from_f32(__float_as_uint(v[4 * d]), sx) |
-                  (e4m3_from_f32(__float_as_uint(v[4 * d + 1]), sx) << 8) |
-                  (e4m3_from_f32(__float_as_uint(v[4 * d + 2]), sx) << 16) |
-                  (e4m3_from_f32(__float_as_uint(v[4 * d + 3]), sx) << 24);
-        uint4* dq = reinterpret_cast<uint4*>(p.cq + row * p.F + fb);
-        dq[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
-        dq[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
-        p.cs[mx_tile_off((uint32_t)row, (uint32_t)(fb / 32),
-                         (uint32_t)(p.F / 128))] = (uint8_t)(sx + 127);
-      }
-      if (EPI == EPI_SWIGLU || p.c) {
-        uint4* dc = reinterpret_cast<uint4*>(p.c + row * p.ldc + fb);
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-          dc[d] = make_uint4(pack_bf16x2(v[8 * d + 0], v[8 * d + 1]),
-                             pack_bf16x2(v[8 * d + 2], v[8 * d + 3]),
-                             pack_bf16x2(v[8 * d + 4], v[8 * d + 5]),
-                             pack_bf16x2(v[8 * d + 6], v[8 * d + 7]));
+        if (ok && (EPI == EPI_SWIGLU || p.c))
+          *reinterpret_cast<uint4*>(p.c + row * p.ldc + f) =
+              make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                         pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
       }
     }
   } else if constexpr (EPI == EPI_STORE) {
-    // bf16 C through LDS, then 64 contiguous values per lane and row
+    // bf16 C through LDS; on readback lane l takes chunk l % 16 (8 columns)
+    // of row 4 q + l / 16
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -690,43 +706,54 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
     uint16_t* cbase = p.c;
     if constexpr (G == RAGGED_K) cbase += (int64_t)tc.e * p.c_es;
-    const int h = lane & 1;
-    const int col0 = n0 + wn * 128 + 64 * h;   // N % 64 == 0: whole halves
+    const int ch = lane & 15;
+    const int col = n0 + wn * 128 + 8 * ch;   // N % 64 == 0
+    const int mlim = G == RAGGED_M ? tc.seg_len : p.M;
+    const int64_t rbase = G == RAGGED_M ? tc.seg0 : 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lr = (lane >> 1) + 32 * q;
-      const int mrow = tc.m0 + wm * 128 + lr;
-      uint4 raw[8], v[8];
+    for (int qb = 0; qb < 32; qb += 16) {
+      uint4 v[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) raw[k] = stage_read(wbuf, lr, h, k);
+      for (int q = 0; q < 16; ++q)
+        v[q] = stage_chunk(wbuf, 4 * (qb + q) + (lane >> 4), ch);
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        v[c] = pick_half(raw[c], raw[c ^ 4], 0u - (uint32_t)h);
-      int64_t row;
-      if constexpr (G == RAGGED_M) {
-        if (mrow >= tc.seg_len) continue;
-        row = tc.seg0 + mrow;
-      } else {
-        if (mrow >= p.M) continue;
-        row = mrow;
+      for (int q = 0; q < 16; ++q) {
+        const int mrow = mw + 4 * (qb + q) + (lane >> 4);
+        if (col < p.N && mrow < mlim)
+          *reinterpret_cast<uint4*>(cbase + (rbase + mrow) * p.ldc + col) =
+              v[q];
       }
-      if (col0 >= p.N) continue;
-      uint4* dst = reinterpret_cast<uint4*>(cbase + row * p.ldc + col0);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) dst[k] = v[k];
     }
   } else {  // EPI_SWIGLU_BWD: acc = dA[row][f], f = n0 + wn*128 + j*32 + col
-    // Two passes of 64 f columns through the wave's LDS buffer (float32);
-    // on readback lane l owns rows (l >> 1) + 32 q and the 32 f values of
-    // half h = l & 1: it reads (g, u) of those f with 16-byte loads, writes
-    // dg and du with 16-byte stores and sums dA * silu(g) * u for dw.
+    // Two passes of 64 f columns through the wave's LDS buffer (float32).
+    // On readback lane l owns rows 8 q + l / 8 and 8 f values (l % 8) of
+    // the pass: it reads (g, u) of those f with 16-byte loads, writes dg
+    // and du with 16-byte stores and sums dA * silu(g) * u for dw; the
+    // eight lanes of a row then add their sums in a fixed tree.  The
+    // (g, u) loads of the next batch of four rows go out before the
+    // stores of the current one.
     __shared__ float red[2 * BM];   // row sums of the two N-waves
     const int64_t ld1 = 2 * (int64_t)p.F;
-    const int h = lane & 1;
-    float rsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int c8 = lane & 7;
+    float* wrow = row_weights(p, tc, mw, lane, t);
+    float rsum[16];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      if (pass) __builtin_amdgcn_s_waitcnt(0xc07f);   // readback done
+    for (int q = 0; q < 16; ++q) rsum[q] = 0.0f;
+    // batch b: pass b / 4, rows q = 4 (b % 4) .. + 3
+    auto fcol = [&](int pass) { return n0 + wn * 128 + 64 * pass; };
+    auto load_gu = [&](int b, uint4 (&g4)[4], uint4 (&u4)[4]) {
+      const int f = fcol(b >> 2) + 8 * c8;
+      if (fcol(b >> 2) >= p.F) return;   // F % 64 == 0
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int mrow = min(mw + 8 * (4 * (b & 3) + q) + (lane >> 3),
+                             tc.seg_len - 1);
+        const uint16_t* h = p.h1 + (tc.seg0 + mrow) * ld1 + f;
+        g4[q] = *reinterpret_cast<const uint4*>(h);
+        u4[q] = *reinterpret_cast<const uint4*>(h + p.F);
+      }
+    };
+    auto stage_pass = [&](int pass) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -736,67 +763,82 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
             stage_f32(wbuf, acc_row(i, r, lane), jj * 32 + colw,
                       acc[i][2 * pass + jj][r]);
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
-      const int fb = n0 + wn * 128 + 64 * pass + 32 * h;   // F % 32 == 0
+    };
+    uint4 gA[4], uA[4], gB[4], uB[4];
+    load_gu(0, gA, uA);
+    stage_pass(0);
+    auto run_batch = [&](int b, const uint4 (&g4)[4], const uint4 (&u4)[4]) {
+      const int pass = b >> 2;
+      const int f = fcol(pass) + 8 * c8;
+      if (fcol(pass) >= p.F) return;
+      uint4 c0[4], c1[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int lr = (lane >> 1) + 32 * q;
-        const int mrow = tc.m0 + wm * 128 + lr;
-        uint4 raw[8];
+        const int lr = 8 * (4 * (b & 3) + q) + (lane >> 3);
+        c0[q] = stage_chunk(wbuf, lr, 2 * c8);
+        c1[q] = stage_chunk(wbuf, lr, 2 * c8 + 1);
+      }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) raw[k] = stage_read(wbuf, lr, h, k);
-        if (mrow >= tc.seg_len || fb >= p.F) continue;
-        const int64_t row = tc.seg0 + mrow;
-        float da[32];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint4 c4 = pick_half(raw[c], raw[c ^ 4], 0u - (uint32_t)h);
-          da[4 * c + 0] = __uint_as_float(c4.x);
-          da[4 * c + 1] = __uint_as_float(c4.y);
-          da[4 * c + 2] = __uint_as_float(c4.z);
-          da[4 * c + 3] = __uint_as_float(c4.w);
-        }
-        const uint4* gp = reinterpret_cast<const uint4*>(p.h1 + row * ld1 + fb);
-        const uint4* up =
-            reinterpret_cast<const uint4*>(p.h1 + row * ld1 + p.F + fb);
-        const float wr = p.w ? p.w[row] : 1.0f;
-        uint4* dgp = reinterpret_cast<uint4*>(p.c + row * ld1 + fb);
-        uint4* dup = reinterpret_cast<uint4*>(p.c + row * ld1 + p.F + fb);
+      for (int q = 0; q < 4; ++q) {
+        const int qq = 4 * (b & 3) + q;
+        const int mrow = mw + 8 * qq + (lane >> 3);
+        const float da[8] = {
+            __uint_as_float(c0[q].x), __uint_as_float(c0[q].y),
+            __uint_as_float(c0[q].z), __uint_as_float(c0[q].w),
+            __uint_as_float(c1[q].x), __uint_as_float(c1[q].y),
+            __uint_as_float(c1[q].z), __uint_as_float(c1[q].w)};
+        const uint32_t gw[4] = {g4[q].x, g4[q].y, g4[q].z, g4[q].w};
+        const uint32_t uw[4] = {u4[q].x, u4[q].y, u4[q].z, u4[q].w};
+        const float wr = wrow[8 * qq + (lane >> 3)];
+        uint32_t dgw[4], duw[4];
         float part = 0.0f;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {   // 8 f values per 16-byte vector
-          const uint4 g4 = gp[d], u4 = up[d];
-          const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
-          const uint32_t uw[4] = {u4.x, u4.y, u4.z, u4.w};
-          uint32_t dgw[4], duw[4];
+        for (int e = 0; e < 4; ++e) {
+          float dgv[2], duv[2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float dgv[2], duv[2];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const float g = hh ? bf16hi(gw[e]) : bf16lo(gw[e]);
-              const float u = hh ? bf16hi(uw[e]) : bf16lo(uw[e]);
-              const float a = da[8 * d + 2 * e + hh];
-              const float sgm = fast_sigmoid(g);
-              const float sg = g * sgm;
-              dgv[hh] = a * wr * u * (sgm * (1.0f + g * (1.0f - sgm)));
-              duv[hh] = a * wr * sg;
-              part += a * sg * u;
-            }
-            dgw[e] = pack_bf16x2(dgv[0], dgv[1]);
-            duw[e] = pack_bf16x2(duv[0], duv[1]);
+          for (int hh = 0; hh < 2; ++hh) {
+            const float g = hh ? bf16hi(gw[e]) : bf16lo(gw[e]);
+            const float u = hh ? bf16hi(uw[e]) : bf16lo(uw[e]);
+            const float a = da[2 * e + hh];
+            const float sgm = fast_sigmoid(g);
+            const float sg = g * sgm;
+            dgv[hh] = a * wr * u * (sgm * (1.0f + g * (1.0f - sgm)));
+            duv[hh] = a * wr * sg;
+            part += a * sg * u;
           }
-          dgp[d] = make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]);
-          dup[d] = make_uint4(duw[0], duw[1], duw[2], duw[3]);
+          dgw[e] = pack_bf16x2(dgv[0], dgv[1]);
+          duw[e] = pack_bf16x2(duv[0], duv[1]);
         }
-        rsum[q] += part;
+        if (mrow < tc.seg_len) {
+          uint16_t* d = p.c + (tc.seg0 + mrow) * ld1 + f;
+          *reinterpret_cast<uint4*>(d) =
+              make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]);
+          *reinterpret_cast<uint4*>(d + p.F) =
+              make_uint4(duw[0], duw[1], duw[2], duw[3]);
+          rsum[qq] += part;
+        }
       }
+    };
+#pragma unroll
+    for (int b = 0; b < 8; b += 2) {
+      if (b == 4) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // pass 0 readback done
+        stage_pass(1);
+      }
+      load_gu(b + 1, gB, uB);
+      run_batch(b, gA, uA);
+      if (b + 2 < 8) load_gu(b + 2, gA, uA);
+      run_batch(b + 1, gB, uB);
     }
     if (p.dw_part) {
-      // the two halves of a row, then the two N-waves in a fixed order
+      // the eight lanes of a row, then the two N-waves in a fixed order
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float v = rsum[q] + __shfl_xor(rsum[q], 1, 64);
-        if (h == 0) red[wn * BM + wm * 128 + (lane >> 1) + 32 * q] = v;
+      for (int q = 0; q < 16; ++q) {
+        float v = rsum[q];
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        v += __shfl_xor(v, 4, 64);
+        if (c8 == 0) red[wn * BM + wm * 128 + 8 * q + (lane >> 3)] = v;
       }
       __syncthreads();
       const int mrow = tc.m0 + t;

@@ -153,6 +153,27 @@ def test_unpermute_weighted_matches_oracle(m):
     np.testing.assert_allclose(host_f64(y), yr, rtol=2 ** -8, atol=1e-6)
 
 
+def test_unpermute_k1_rounds_to_nearest_even(m):
+    """k = 1: y = bf16(w * z) with one float32 product, so every output
+    checks the float32 -> bf16 rounding bit for bit, ties included."""
+    T, H, E, k = 256, 128, 4, 1
+    rng = np.random.default_rng(11)
+    d, ridx, rw, out, ref = _perm_case(m, T, H, E, k)
+    zf = (rng.standard_normal((T, H)) *
+          np.exp2(rng.integers(-20, 20, (T, H)))).astype(np.float32)
+    zf[:, :4] = 1.0                        # products that are exact ties
+    z = bf16_bits(zf)
+    w = rng.uniform(0.01, 1.0, (T, 1)).astype(np.float32)
+    w[:64] = np.float32(1 + 2 ** -8)       # tie, rounds down to even
+    w[64:128] = np.float32(1 + 3 * 2 ** -8)  # tie, rounds up to even
+    y = m.moe_unpermute(dev_bf16(z), out["row_map"], k,
+                        topk_w=torch.from_numpy(w).cuda())
+    # y[t] = w[t] * z[row_map[t]]: one float32 product, one bf16 rounding
+    zt = bf16_to_f64(z).astype(np.float32)[ref["row_map"]]
+    want = bf16_bits((w * zt).astype(np.float32))
+    np.testing.assert_array_equal(host_bits(y), want)
+
+
 def test_gather_rows_and_probs_grad(m):
     T, H, E, k = 400, 64, 8, 2
     d, ridx, rw, out, ref = _perm_case(m, T, H, E, k)
