@@ -567,6 +567,20 @@ __device__ __forceinline__ float* row_weights(const Params& p,
   return wrow;
 }
 
+// SwiGLU epilogues: gate block 2 jj of each row block becomes
+// silu(g) * u, with u from block 2 jj + 1
+__device__ __forceinline__ void silu_mul_in_place(f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float g = acc[i][2 * jj][r];
+        acc[i][2 * jj][r] = (g * fast_sigmoid(g)) * acc[i][2 * jj + 1][r];
+      }
+}
+
 // Global loads and stores share one in-order counter (vmcnt): a wait for a
 // load also waits for every store issued before it.  So each epilogue issues
 // its loads (routing weights, saved g and u) ahead of the stores they would
@@ -605,6 +619,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
             stage_bf16(wbuf, acc_row(i, r, lane), 64 + jj * 32 + colw,
                        acc[i][2 * jj + 1][r]);
           }
+      silu_mul_in_place(acc);   // frees the u registers for the readback
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
       const int ch = lane & 15;
       const int coff = (ch >> 3) * p.F + n0 + 64 * wn + 8 * (ch & 7);
@@ -623,17 +638,17 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);   // readback done before reuse
+    } else {
+      silu_mul_in_place(acc);
     }
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+        for (int r = 0; r < 16; ++r)
           stage_f32(wbuf, acc_row(i, r, lane), jj * 32 + colw,
-                    (g * fast_sigmoid(g)) * u);
-        }
+                    acc[i][2 * jj][r]);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
     const int c8 = lane & 7;
     const int f = n0 + 64 * wn + 8 * c8;
