@@ -72,6 +72,14 @@ __device__ __forceinline__ uint32_t e4m3x4_hw(uint32_t lo2, uint32_t hi2,
       r, __builtin_bit_cast(mx_v2bf16, hi2), scale, true);
   return sat_e4m3x4(__builtin_bit_cast(uint32_t, r));
 }
+// four E4M3 codes from four floats (first value in the low byte)
+__device__ __forceinline__ uint32_t e4m3x4_hw_f32(float a, float b, float c,
+                                                  float d, float scale) {
+  mx_v2i16 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, a, b, scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, scale, true);
+  return sat_e4m3x4(__builtin_bit_cast(uint32_t, r));
+}
 // 8 bf16 (one uint4) -> 8 E4M3 codes with block exponent s
 __device__ __forceinline__ uint2 e4m3x8_hw(const uint4 v, int s) {
   const float sc = mx_scale_f32(s);

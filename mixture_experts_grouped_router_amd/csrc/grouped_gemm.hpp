@@ -687,13 +687,12 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
           o = __shfl_xor(am, 2, 64);
           am = am > o ? am : o;
           const int sx = e8m0_exp_from_f32_amax(am);
+          const float sc = mx_scale_f32(sx);
           uint32_t w8[2];
 #pragma unroll
           for (int d = 0; d < 2; ++d)
-            w8[d] = e4m3_from_f32(__float_as_uint(v[4 * d]), sx) |
-                    (e4m3_from_f32(__float_as_uint(v[4 * d + 1]), sx) << 8) |
-                    (e4m3_from_f32(__float_as_uint(v[4 * d + 2]), sx) << 16) |
-                    (e4m3_from_f32(__float_as_uint(v[4 * d + 3]), sx) << 24);
+            w8[d] = e4m3x4_hw_f32(v[4 * d], v[4 * d + 1], v[4 * d + 2],
+                                  v[4 * d + 3], sc);
           if (ok) {
             *reinterpret_cast<uint2*>(p.cq + row * p.F + f) =
                 make_uint2(w8[0], w8[1]);
