@@ -94,6 +94,35 @@ __device__ __forceinline__ void sched_reads_mfma() {
 #endif
 }
 
+// As sched_reads_mfma, with the region's NV vector-memory instructions (the
+// next K step's direct loads) issued VPM per MFMA from the first MFMA on:
+// issued all at once they fill the texture unit's queue and the wave stalls
+// on the load issue instead of issuing MFMAs.
+template <int NV, int NR, int NM, int VPM, int MPV = 1, int I = 0>
+__device__ __forceinline__ void sched_vmem_reads_mfma() {
+#if MOE_SCHED_GROUPS
+  if constexpr (I < NM) {
+    // before every MPV-th MFMA, VPM vector-memory instructions
+    constexpr int rem = NV - (I / MPV) * VPM;
+    constexpr int v = (I % MPV != 0 || rem <= 0) ? 0 : (rem < VPM ? rem : VPM);
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x010, v, 0);
+    if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    sched_vmem_reads_mfma<NV, NR, NM, VPM, MPV, I + 1>();
+  }
+#endif
+}
+
+#ifndef MOE_LOAD_SPLIT
+#define MOE_LOAD_SPLIT 1
+#endif
+#ifndef MOE_LOAD_VPM
+#define MOE_LOAD_VPM 1
+#endif
+#ifndef MOE_LOAD_MPV
+#define MOE_LOAD_MPV 1
+#endif
+
 struct Params {
   const char* a;          // operand A (rows = M)
   int64_t lda;            // bytes between rows (KC) or k rows (MC)
@@ -995,15 +1024,42 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
   const int nk = (kdim + kStepK - 1) / kStepK;
-  auto issue = [&](char* bufa, char* bufb, int kt, bool real) {
+  // LDS reads per K slice: 4 per K-contiguous side (16-byte reads), 8 per
+  // MN-contiguous side (two 8-byte transposed reads per block); MXFP8 16
+  constexpr int kNR = P == P_FP8 ? 16
+                                 : (LA == KC ? 4 : 8) + (LB == KC ? 4 : 8);
+  // part 1: A (and the MXFP8 scales), part 2: B, 3: both
+  auto issue_part = [&](char* bufa, char* bufb, int kt, bool real, int part) {
     // a padding step (real == false) reads zeros: empty descriptors for
     // direct loads, k rows past kvalid for staged loads; its scales are
     // those of the last real step (finite; they multiply zeros)
-    if constexpr (LA == KC) da.issue(bufa, (uint32_t)kt * kRowBytes, real, wave);
-    else ma.issue(bufa, kt, real, wave);
-    if constexpr (LB == KC) db.issue(bufb, (uint32_t)kt * kRowBytes, real, wave);
-    else mb.issue(bufb, kt, real, wave);
-    if constexpr (P == P_FP8) ms.load(min(kt, nk - 1));
+    if (part & 1) {
+      if constexpr (LA == KC) da.issue(bufa, (uint32_t)kt * kRowBytes, real, wave);
+      else ma.issue(bufa, kt, real, wave);
+      if constexpr (P == P_FP8) ms.load(min(kt, nk - 1));
+    }
+    if (part & 2) {
+      if constexpr (LB == KC) db.issue(bufb, (uint32_t)kt * kRowBytes, real, wave);
+      else mb.issue(bufb, kt, real, wave);
+    }
+  };
+  auto issue = [&](char* bufa, char* bufb, int kt, bool real) {
+    issue_part(bufa, bufb, kt, real, 3);
+  };
+  // The next K step's loads go out over the first slice (or, split, A over
+  // the first slice and B over the second), spread between the MFMAs.
+  constexpr bool kSplit = MOE_LOAD_SPLIT && kSl >= 3;
+  constexpr int kVmA = 8 + (P == P_FP8 ? 8 : 0);   // A loads (+ scales)
+  constexpr int kVmB = 8;
+  auto slice_sched = [&](int kk) {
+    if (kk == 0) {
+      if constexpr (kSplit) sched_vmem_reads_mfma<kVmA, kNR, 16, MOE_LOAD_VPM, MOE_LOAD_MPV>();
+      else sched_vmem_reads_mfma<kVmA + kVmB, kNR, 16, MOE_LOAD_VPM, MOE_LOAD_MPV>();
+    } else if (kSplit && kk == 1) {
+      sched_vmem_reads_mfma<kVmB, kNR, 16, MOE_LOAD_VPM, MOE_LOAD_MPV>();
+    } else {
+      sched_reads_mfma<kNR, 16>();
+    }
   };
   // fragments of K slice kk from stage (sa, sb)
   auto fload = [&](Fr& f, const char* sa, const char* sb, int kk) {
@@ -1016,10 +1072,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       else f.load_b(sb, kk, wn, lane);
     }
   };
-  // LDS reads per K slice: 4 per K-contiguous side (16-byte reads), 8 per
-  // MN-contiguous side (two 8-byte transposed reads per block); MXFP8 16
-  constexpr int kNR = P == P_FP8 ? 16
-                                 : (LA == KC ? 4 : 8) + (LB == KC ? 4 : 8);
   auto take_scales = [&]() {
     if constexpr (P == P_FP8) {
 #pragma unroll
@@ -1048,14 +1100,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 
   for (int kt = 0; kt < nk2; kt += 2) {
     // stage kt from buffers 0 while stage kt+1 loads into buffers 1
-    issue(sA1, sB1, kt + 1, kt + 1 < nk);
+    issue_part(sA1, sB1, kt + 1, kt + 1 < nk, kSplit ? 1 : 3);
 #pragma unroll
     for (int kk = 0; kk < kSl - 1; ++kk) {
+      if (kSplit && kk == 1) issue_part(sA1, sB1, kt + 1, kt + 1 < nk, 2);
       fload(nxt, sA0, sB0, kk + 1);
       if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
       else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
       cur = nxt;
-      sched_reads_mfma<kNR, 16>();
+      slice_sched(kk);
       // keep the scheduler from hoisting later slices' reads (registers)
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1071,14 +1124,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 
     // stage kt+1 from buffers 1 while stage kt+2 loads into buffers 0 (a
     // step past nk2 is never computed; its zero loads are harmless)
-    issue(sA0, sB0, kt + 2, kt + 2 < nk);
+    issue_part(sA0, sB0, kt + 2, kt + 2 < nk, kSplit ? 1 : 3);
 #pragma unroll
     for (int kk = 0; kk < kSl - 1; ++kk) {
+      if (kSplit && kk == 1) issue_part(sA0, sB0, kt + 2, kt + 2 < nk, 2);
       fload(nxt, sA1, sB1, kk + 1);
       if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
       else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
       cur = nxt;
-      sched_reads_mfma<kNR, 16>();
+      slice_sched(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
     Mma<P>::template run<kSl - 1, 0>(cur, sa_cur, sb_cur, acc);
