@@ -551,6 +551,53 @@ def prequantised_step(m, layer, cfg, st, K):
             "value": round(cfg.fwd_flop() / (ms * 1e-3) / 1e12, 2)}
 
 
+def expert_loop_extra(m, layer, cfg, st, K):
+    """The grouped MLP against the per-expert loop baseline on the same
+    permuted inputs: wall time per call, stream synchronised around each
+    run (the loop waits for the stream itself to read the row counts)."""
+    import torch
+    fa = layer.fa
+    la = m._FwdArgs()
+    for f, _ in m._FwdArgs._fields_:
+        setattr(la, f, getattr(fa, f))
+    la.h1_save, la.a_save = None, None
+    n = ctypes.c_size_t()
+    m._check(layer.lib.moe_expert_loop_mlp_fwd_workspace_size(
+        ctypes.byref(la), ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device="cuda")
+    la.ws, la.ws_bytes = ws.data_ptr(), ws.numel()
+    z_loop = torch.empty_like(layer.z)
+    la.z_perm = z_loop.data_ptr()
+    for _, fn in layer.stages():     # valid x_perm / offsets / w_perm
+        fn(st)
+
+    def loop():
+        m._check(layer.lib.moe_expert_loop_mlp_fwd(layer.ctx, ctypes.byref(la),
+                                                   st))
+
+    def grouped():
+        m._check(layer.lib.moe_grouped_mlp_fwd(layer.ctx, ctypes.byref(fa),
+                                               st))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / K * 1e3
+
+    t_loop, t_grp = timed(loop), timed(grouped)
+    diff = (z_loop.float() - layer.z.float()).norm() / layer.z.float().norm()
+    return {"loop_ms": round(t_loop, 4), "grouped_ms": round(t_grp, 4),
+            "speedup_grouped_vs_loop": round(t_loop / t_grp, 3),
+            "rel_diff_z": float(f"{diff.item():.3e}"),
+            "what": "moe_expert_loop_mlp_fwd (per expert: gate/up GEMM, "
+                    "SwiGLU kernel, down GEMM; host reads the row counts) "
+                    "vs moe_grouped_mlp_fwd, wall ms per call"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -634,6 +681,9 @@ def main():
     if cfg.mode == "mxfp8" and not cfg.backward:
         extras["prequantised_weights"] = prequantised_step(m, layer, cfg, st,
                                                            max(1, K // 2))
+    if cfg.mode == "bf16" and not cfg.backward:
+        extras["expert_loop"] = expert_loop_extra(m, layer, cfg, st,
+                                                  max(2, K // 4))
 
     flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
     tflops = flop / (ms_step * 1e-3) / 1e12

@@ -288,6 +288,31 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* args,
                                  void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_expert_loop_mlp_fwd -- the computation of moe_grouped_mlp_fwd (bf16)
+ * done the way a per-expert Python loop does it: the baseline the grouped
+ * path is measured against.
+ * [PG1, section "Grouped experts instead of a Python loop": a loop over
+ *  experts launches separate small kernels per expert; the grouped GEMM
+ *  replaces it.]
+ * The call copies offsets to the host and waits for the stream, then for
+ * every expert with rows, in ascending order, launches: a gate/up GEMM
+ * writing h1 = X_e W_gu[e]^T (bf16), a SwiGLU kernel writing
+ * a = w_perm * silu(g) * u (float32 arithmetic on the bf16 h1, bf16 out),
+ * and a down GEMM writing z = a W_dn[e]^T.  Results equal the grouped
+ * path's up to the bf16 rounding of h1 before the SwiGLU.
+ * args: as moe_grouped_mlp_fwd with precision MOE_PREC_BF16 (MXFP8 fields
+ * ignored); h1_save / a_save nullable (then held in the workspace).
+ * Errors: MOE_ERR_INVALID_ARG (null required pointer, bad sizes, offsets
+ * read back not non-decreasing from 0 to rows), MOE_ERR_UNSUPPORTED (MXFP8,
+ * size limits, misaligned pointers), MOE_ERR_WORKSPACE, MOE_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_expert_loop_mlp_fwd_workspace_size(
+    const moe_mlp_fwd_args* args, size_t* bytes);
+moe_status_t moe_expert_loop_mlp_fwd(moe_ctx_t ctx,
+                                     const moe_mlp_fwd_args* args,
+                                     void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_mlp_bwd -- the backward counterpart of moe_grouped_mlp_fwd.
  * [PG1, section "Reducing memory and quantisation cost": the fused forward
  *  op has a counterpart in the backward pass.]

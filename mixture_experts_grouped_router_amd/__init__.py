@@ -20,7 +20,8 @@ __all__ = [
     "lib_path", "load_library", "MoEError", "PREC_BF16", "PREC_MXFP8",
     "ROWWISE", "COLWISE", "moe_route_topk", "moe_permute", "moe_gather_rows",
     "moe_unpermute", "moe_unpermute_probs_grad", "mxfp8_quantize",
-    "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd", "check_device_status",
+    "moe_grouped_mlp_fwd", "moe_expert_loop_mlp_fwd", "moe_grouped_mlp_bwd",
+    "check_device_status",
     "mx_segment_ld", "set_kernel_timing", "reset_kernel_timing",
     "kernel_time",
 ]
@@ -91,6 +92,9 @@ _SIGS = {
     "moe_grouped_mlp_fwd_workspace_size": [ctypes.POINTER(_FwdArgs),
                                            ctypes.POINTER(_c_sz)],
     "moe_grouped_mlp_fwd": [_c_p, ctypes.POINTER(_FwdArgs), _c_p],
+    "moe_expert_loop_mlp_fwd_workspace_size": [ctypes.POINTER(_FwdArgs),
+                                               ctypes.POINTER(_c_sz)],
+    "moe_expert_loop_mlp_fwd": [_c_p, ctypes.POINTER(_FwdArgs), _c_p],
     "moe_grouped_mlp_bwd_workspace_size": [ctypes.POINTER(_BwdArgs),
                                            ctypes.POINTER(_c_sz)],
     "moe_grouped_mlp_bwd": [_c_p, ctypes.POINTER(_BwdArgs), _c_p],
@@ -413,6 +417,59 @@ def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gu: torch.Tensor,
         res["h1"], res["a"] = h1, a
     return res
 
+
+
+def moe_expert_loop_mlp_fwd(x_perm: torch.Tensor, w_gu: torch.Tensor,
+                            w_dn: torch.Tensor, offsets: torch.Tensor,
+                            w_perm: Optional[torch.Tensor] = None,
+                            save: bool = False,
+                            out: Optional[torch.Tensor] = None,
+                            ws: Optional[torch.Tensor] = None,
+                            ) -> Dict[str, torch.Tensor]:
+    """The bf16 expert MLP as a per-expert loop (separate gate/up GEMM,
+    SwiGLU and down GEMM launches per expert; the call waits for the
+    stream to read the row counts): the baseline of moe_grouped_mlp_fwd.
+    Returns {"z"} (+ "h1", "a" when save=True)."""
+    E, F2, H = w_gu.shape
+    F = F2 // 2
+    rows = x_perm.shape[0]
+    dev = x_perm.device
+    _need(w_gu, torch.bfloat16, (E, 2 * F, H), "w_gu")
+    _need(w_dn, torch.bfloat16, (E, H, F), "w_dn")
+    _need(offsets, torch.int32, (E + 1,), "offsets")
+    _need(x_perm, torch.bfloat16, (rows, H), "x_perm")
+    if w_perm is not None:
+        _need(w_perm, torch.float32, (rows,), "w_perm")
+    z = out if out is not None else torch.empty((rows, H), dtype=torch.bfloat16,
+                                                device=dev)
+    _need(z, torch.bfloat16, (rows, H), "out")
+    h1 = torch.empty((rows, 2 * F), dtype=torch.bfloat16, device=dev) \
+        if save else None
+    a = torch.empty((rows, F), dtype=torch.bfloat16, device=dev) \
+        if save else None
+    args = _FwdArgs()
+    args.E, args.H, args.F, args.rows = E, H, F, rows
+    args.precision = PREC_BF16
+    args.x_perm = _ptr(x_perm)
+    args.w_gu, args.w_dn = _ptr(w_gu), _ptr(w_dn)
+    args.w_perm = _ptr(w_perm)
+    args.offsets = _ptr(offsets)
+    args.z_perm = _ptr(z)
+    args.h1_save, args.a_save = _ptr(h1), _ptr(a)
+    lib = load_library()
+    nbytes = _c_sz(0)
+    _check(lib.moe_expert_loop_mlp_fwd_workspace_size(ctypes.byref(args),
+                                                      ctypes.byref(nbytes)))
+    if ws is None or ws.numel() < int(nbytes.value):
+        ws = torch.empty(max(int(nbytes.value), 256), dtype=torch.uint8,
+                         device=dev)
+    args.ws, args.ws_bytes = _ptr(ws), ws.numel()
+    _check(lib.moe_expert_loop_mlp_fwd(_context(dev), ctypes.byref(args),
+                                       _stream()))
+    res = {"z": z}
+    if save:
+        res["h1"], res["a"] = h1, a
+    return res
 
 def moe_grouped_mlp_bwd(dz_perm: torch.Tensor, x_perm: torch.Tensor,
                         w_gu: torch.Tensor, w_dn: torch.Tensor,

@@ -1,5 +1,6 @@
 // libmoe C ABI: argument validation, workspace sizing and kernel dispatch.
 // Every call validates on the host first and enqueues nothing on failure.
+#include <vector>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -444,6 +445,59 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
         a->ws, as_stream(stream));
   }
   return hip_status(e, "grouped_mlp_fwd");
+}
+
+moe_status_t moe_expert_loop_mlp_fwd_workspace_size(const moe_mlp_fwd_args* a,
+                                                    size_t* bytes) {
+  MOE_REQUIRE(a && bytes, MOE_ERR_INVALID_ARG, "null pointer");
+  MOE_REQUIRE(a->precision == MOE_PREC_BF16, MOE_ERR_UNSUPPORTED,
+              "the per-expert loop is bf16 only");
+  moe_status_t s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
+  if (s != MOE_OK) return s;
+  *bytes = moe::expert_loop_fwd_ws_bytes(a->E, a->F, a->rows,
+                                         a->h1_save == nullptr,
+                                         a->a_save == nullptr);
+  return ok();
+}
+
+moe_status_t moe_expert_loop_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
+                                     void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
+  MOE_REQUIRE(a != nullptr, MOE_ERR_INVALID_ARG, "null args");
+  size_t need = 0;
+  s = moe_expert_loop_mlp_fwd_workspace_size(a, &need);
+  if (s != MOE_OK) return s;
+  MOE_REQUIRE(a->offsets != nullptr, MOE_ERR_INVALID_ARG, "null offsets");
+  MOE_REQUIRE((a->x_perm && a->z_perm) || a->rows == 0, MOE_ERR_INVALID_ARG,
+              "null x_perm / z_perm");
+  MOE_REQUIRE(a->w_gu && a->w_dn, MOE_ERR_INVALID_ARG, "null weights");
+  MOE_REQUIRE(aligned16(a->x_perm) && aligned16(a->w_gu) &&
+                  aligned16(a->w_dn) && aligned16(a->z_perm) &&
+                  aligned16(a->h1_save) && aligned16(a->a_save),
+              MOE_ERR_UNSUPPORTED, "operands must be 16-byte aligned");
+  MOE_REQUIRE(a->ws != nullptr && a->ws_bytes >= need, MOE_ERR_WORKSPACE,
+              "expert_loop_mlp_fwd workspace needs %zu bytes", need);
+  // the loop reads the per-expert row counts on the host, as a Python loop
+  // over experts does: wait for the stream
+  hipStream_t st = as_stream(stream);
+  std::vector<int32_t> off((size_t)a->E + 1);
+  hipError_t e = hipMemcpyAsync(off.data(), a->offsets,
+                                off.size() * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_status(e, "expert_loop_mlp_fwd offsets");
+  MOE_REQUIRE(off[0] == 0 && off[a->E] == a->rows, MOE_ERR_INVALID_ARG,
+              "offsets must run from 0 to rows");
+  for (int32_t i = 0; i < a->E; ++i)
+    MOE_REQUIRE(off[i + 1] >= off[i], MOE_ERR_INVALID_ARG,
+                "offsets must not decrease");
+  e = moe::launch_expert_loop_fwd(a->E, a->H, a->F, a->rows, a->x_perm,
+                                  a->w_gu, a->w_dn, a->w_perm, a->offsets,
+                                  off.data(), a->z_perm, a->h1_save,
+                                  a->a_save, a->ws, st);
+  return hip_status(e, "expert_loop_mlp_fwd");
 }
 
 moe_status_t moe_grouped_mlp_bwd_workspace_size(const moe_mlp_bwd_args* a,

@@ -60,6 +60,17 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
                                hipStream_t stream);
+// per-expert loop (baseline of the grouped path), bf16; offsets_host is
+// the host copy of offsets
+size_t expert_loop_fwd_ws_bytes(int E, int F, int64_t rows, bool need_h1,
+                                bool need_a);
+hipError_t launch_expert_loop_fwd(int E, int H, int F, int64_t rows,
+                                  const void* x_perm, const void* w_gu,
+                                  const void* w_dn, const float* w_perm,
+                                  const int32_t* offsets,
+                                  const int32_t* offsets_host, void* z_perm,
+                                  void* h1_save, void* a_save, void* ws,
+                                  hipStream_t stream);
 size_t mlp_bwd_bf16_ws_bytes(int E, int H, int F, int64_t rows);
 hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
                                const void* x_perm, const void* w_gu,

@@ -66,6 +66,14 @@ def test_workspace_queries(lib):
     a.H = 100                                    # not a multiple of 64
     assert lib.moe_grouped_mlp_fwd_workspace_size(ctypes.byref(a),
                                                   ctypes.byref(n)) == 2
+    # per-expert loop: h1 and a in the workspace unless saved; bf16 only
+    a.H = 4096
+    assert lib.moe_expert_loop_mlp_fwd_workspace_size(ctypes.byref(a),
+                                                      ctypes.byref(n)) == 0
+    assert n.value >= 16384 * 3 * 14336 * 2
+    a.precision = 1
+    assert lib.moe_expert_loop_mlp_fwd_workspace_size(ctypes.byref(a),
+                                                      ctypes.byref(n)) == 2
 
 
 @pytest.fixture(scope="module")
