@@ -50,6 +50,17 @@ Where they are silent this module takes the readings listed here:
       on the dequantised values; backward quantises each GEMM operand along
       that GEMM's K, token-direction blocks restarting at each expert segment
       and zero-padded at its end.
+  R9  router projection: logits = x W_r^T (+ optional per-expert bias), the
+      gate W_r [E, H] bf16; each logit is accumulated in float64 one term at
+      a time in ascending h (products of two bf16 values are exact in
+      float64), the bias added last, then rounded once to float32.  The
+      fixed order makes the result a function of the inputs alone, so the
+      routing it feeds can be compared bit for bit.
+  R10 router backward: the routing-weight gradient reaches the logits only
+      through the softmax the forward used (over the chosen set, or over all
+      E without renormalisation); the top-k selection itself is piecewise
+      constant and passes no gradient.  dW_r = dlogits^T x, and the router's
+      share of dx = dlogits W_r.
 
 Pins of this module against things other than itself live in
 ``tests/test_oracle_pins.py``.
@@ -519,6 +530,62 @@ def grouped_mlp_bwd_mxfp8(dz_perm, x_perm, w_gu, w_dn, w_perm, offsets
         dx[lo:hi] = _mx_rows(dh1) @ _mx_rows(_as_f64(w_gu[e]).T).T
     return {"dx_perm": dx, "dw_perm": dw_perm, "dw_gu": dw_gu,
             "dw_dn": dw_dn}
+
+
+# --------------------------------------------------------------------------
+# Router projection and router backward  [PG3 practical implications: Top-k
+# routing; PG4 "Background": tokens are routed across many experts]
+# --------------------------------------------------------------------------
+def router_logits(x, w_r, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """x bf16 [T, H], w_r bf16 [E, H] (bit patterns or floats), bias [E] or
+    None -> logits float32 [T, E].  Reading R9: float64, one term at a time
+    in ascending h (ufunc accumulate adds left to right), bias last, one
+    rounding to float32."""
+    X = _as_f64(x)
+    W = _as_f64(w_r)
+    T = X.shape[0]
+    E = W.shape[0]
+    out = np.empty((T, E), dtype=f64)
+    for t in range(T):
+        prod = W * X[t][None, :]                 # exact products
+        out[t] = np.add.accumulate(prod, axis=1)[:, -1]
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=f64)[None, :]
+    return out.astype(np.float32)
+
+
+def router_bwd(logits: np.ndarray, topk_idx: np.ndarray, dtopk_w: np.ndarray,
+               renormalize: bool = True) -> np.ndarray:
+    """dlogits float64 [T, E] from the gradient of the routing weights
+    dtopk_w [T, k] (reading R10).  With w the forward's softmax (over the
+    chosen set S, or p over all E):
+      renormalize:  dl_i = w_i (dw_i - sum_{j in S} w_j dw_j) for i in S, else 0
+      otherwise:    dl_e = p_e (g_e - sum_{j in S} p_j dw_j), g = dw on S, 0 off S
+    """
+    lv = np.asarray(logits, dtype=np.float32).astype(f64) + 0.0
+    idx = np.asarray(topk_idx).astype(np.int64)
+    dw = np.asarray(dtopk_w, dtype=f64)
+    T, E = lv.shape
+    dl = np.zeros((T, E), dtype=f64)
+    for t in range(T):
+        S = idx[t]
+        ex = np.exp(lv[t] - lv[t].max())
+        if renormalize:
+            w = ex[S] / ex[S].sum()
+            dl[t, S] = w * (dw[t] - (w * dw[t]).sum())
+        else:
+            p = ex / ex.sum()
+            g = np.zeros(E, dtype=f64)
+            g[S] = dw[t]
+            dl[t] = p * (g - (p * g).sum())
+    return dl
+
+
+def router_weight_grads(dlogits: np.ndarray, x, w_r
+                        ) -> Tuple[np.ndarray, np.ndarray]:
+    """(dW_r [E, H], dx [T, H]) = (dlogits^T x, dlogits W_r), float64."""
+    dl = np.asarray(dlogits, dtype=f64)
+    return dl.T @ _as_f64(x), dl @ _as_f64(w_r)
 
 
 # --------------------------------------------------------------------------

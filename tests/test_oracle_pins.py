@@ -542,3 +542,121 @@ def test_accounting_flops_and_rows():
     assert abs(c.fwd_flop() - 5.772e12) / 5.772e12 < 1e-3
     q = CONFIGS["qwen3_long"]
     assert abs(q.bwd_flop() - 4.948e12) / 4.948e12 < 1e-3
+
+
+# ---------------------------------------------------------------- router
+def _small_int_bf16(rng, shape, lo=-8, hi=8):
+    """bf16 bit patterns of small integers (exact in bf16)."""
+    return bf16_bits(rng.integers(lo, hi + 1, shape).astype(np.float32))
+
+
+def test_router_logits_exact_on_integer_operands():
+    """Small-integer operands keep every partial sum exact, so the logits
+    are the integer matrix product (plus a dyadic bias), whatever the
+    summation order: catches a dropped term or a transposed operand."""
+    rng = np.random.default_rng(40)
+    T, H, E = 37, 96, 11
+    x = _small_int_bf16(rng, (T, H))
+    w = _small_int_bf16(rng, (E, H))
+    bias = rng.integers(-4, 5, E).astype(np.float64) * 0.25
+    got = O.router_logits(x, w, bias)
+    xi = bf16_to_f64(x).astype(np.int64)
+    wi = bf16_to_f64(w).astype(np.int64)
+    want = (xi @ wi.T).astype(np.float64) + bias[None, :]
+    assert got.dtype == np.float32
+    np.testing.assert_array_equal(got.astype(np.float64), want)
+
+
+def test_router_logits_single_rounding_to_float32():
+    """The float64 sum is rounded to float32 once: 1 + 2^-30 summed from
+    exact bf16 terms stays 1 in float32, and 2^24 + 1 rounds to even."""
+    one = bf16_bits(np.array([[1.0, 2.0 ** -30]], np.float32))
+    w = bf16_bits(np.array([[1.0, 1.0]], np.float32))
+    assert O.router_logits(one, w)[0, 0] == np.float32(1.0)
+    big = bf16_bits(np.array([[2.0 ** 24, 1.0]], np.float32))
+    assert O.router_logits(big, w)[0, 0] == np.float32(2.0 ** 24)
+    big3 = bf16_bits(np.array([[2.0 ** 24, 1.0, 2.0]], np.float32))
+    w3 = bf16_bits(np.array([[1.0, 1.0, 1.0]], np.float32))
+    assert O.router_logits(big3, w3)[0, 0] == np.float32(2.0 ** 24 + 4)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_router_bwd_finite_differences(renorm):
+    """dlogits is the derivative of L = sum_j dw_j * w_j(logits) with the
+    selected set held fixed (central differences in float64)."""
+    rng = np.random.default_rng(41)
+    T, E, k = 5, 9, 3
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    dw = rng.standard_normal((T, k))
+    idx, _ = O.route_topk(lg, k, renorm)
+    dl = O.router_bwd(lg, idx, dw, renorm)
+    lv = lg.astype(np.float64)
+
+    def loss(l):
+        tot = 0.0
+        for t in range(T):
+            ex = np.exp(l[t] - l[t].max())
+            S = idx[t]
+            den = ex[S].sum() if renorm else ex.sum()
+            tot += float((dw[t] * ex[S] / den).sum())
+        return tot
+
+    eps = 1e-6
+    for t in range(T):
+        for e in range(E):
+            lp, lm = lv.copy(), lv.copy()
+            lp[t, e] += eps
+            lm[t, e] -= eps
+            num = (loss(lp) - loss(lm)) / (2 * eps)
+            assert abs(num - dl[t, e]) < 1e-7, (t, e, num, dl[t, e])
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_router_bwd_rows_sum_to_zero_and_support(renorm):
+    """Softmax Jacobian rows sum to zero; with renormalisation the gradient
+    lives on the chosen set only; k = E without renormalisation is the
+    plain softmax backward."""
+    rng = np.random.default_rng(42)
+    T, E, k = 40, 16, 4
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    dw = rng.standard_normal((T, k))
+    idx, w = O.route_topk(lg, k, renorm)
+    dl = O.router_bwd(lg, idx, dw, renorm)
+    np.testing.assert_allclose(dl.sum(axis=1), 0.0, atol=1e-14)
+    if renorm:
+        mask = np.zeros((T, E), bool)
+        np.put_along_axis(mask, idx.astype(np.int64), True, axis=1)
+        assert np.all(dl[~mask] == 0.0)
+    else:
+        idx_all, p = O.route_topk(lg, E, False)
+        g = np.zeros((T, E))
+        np.put_along_axis(g, idx_all.astype(np.int64),
+                          rng.standard_normal((T, E)), axis=1)
+        ga = np.take_along_axis(g, idx_all.astype(np.int64), axis=1)
+        dla = O.router_bwd(lg, idx_all, ga, False)
+        pe = np.exp(lg - lg.max(axis=1, keepdims=True).astype(np.float64))
+        pe = pe / pe.sum(axis=1, keepdims=True)
+        want = pe * (g - (pe * g).sum(axis=1, keepdims=True))
+        np.testing.assert_allclose(dla, want, rtol=1e-12, atol=1e-15)
+
+
+def test_router_weight_grads_adjoint():
+    """<dl, x W^T> is bilinear: its derivatives w.r.t. W and x are
+    dl^T x and dl W (checked entry by entry with exact perturbations)."""
+    rng = np.random.default_rng(43)
+    T, H, E = 6, 10, 4
+    x = rng.standard_normal((T, H))
+    w = rng.standard_normal((E, H))
+    dl = rng.standard_normal((T, E))
+    dW, dx = O.router_weight_grads(dl, x, w)
+    base = float((dl * (x @ w.T)).sum())
+    for e in range(E):
+        for h in range(H):
+            w2 = w.copy()
+            w2[e, h] += 1.0
+            assert abs(float((dl * (x @ w2.T)).sum()) - base - dW[e, h]) < 1e-9
+    for t in range(T):
+        for h in range(H):
+            x2 = x.copy()
+            x2[t, h] += 1.0
+            assert abs(float((dl * (x2 @ w.T)).sum()) - base - dx[t, h]) < 1e-9
