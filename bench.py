@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("MoE grouped-MLP TFLOP/s + tokens/s (Mixtral layer, 1 GPU); "
           "% MFMA peak")
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_FP64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix)
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense (MX)fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -598,6 +599,71 @@ def expert_loop_extra(m, layer, cfg, st, K):
                     "vs moe_grouped_mlp_fwd, wall ms per call"}
 
 
+def router_extra(m, layer, cfg, d, st, K):
+    """Router projection (and, with a backward pass, the router backward)
+    on the workload's tokens, timed with HIP events on the library stream;
+    reported beside the step, not inside it."""
+    import torch
+    E, H, T, k = cfg.E, cfg.H, cfg.T, cfg.k
+    w_r = torch.from_numpy(d["w_r"].view(np.int16)).view(torch.bfloat16).cuda()
+    bias = None
+    if cfg.zipf > 0.0:
+        bias = torch.from_numpy(d["bias"].astype(np.float32)).cuda()
+    out = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    P = lambda t: t.data_ptr() if t is not None else None
+    lib = layer.lib
+
+    def logits():
+        m._check(lib.moe_router_logits(layer.ctx, P(layer.x), P(w_r), P(bias),
+                                       T, H, E, P(out), st))
+
+    def timed(fn):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    ms = timed(logits)
+    fl = 2.0 * T * E * H
+    res = {"logits_ms": round(ms, 4),
+           "logits_fp64_TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+           "fp64_peak_TFLOP/s": PEAK_FP64_TFLOPS}
+    if bias is None:   # the generator's bias is float64, the call's float32
+        res["logits_equal_to_input_logits"] = float(
+            (out.cpu().numpy() == d["logits"]).mean())
+    if cfg.backward:
+        idx = layer.idx
+        dw = torch.randn((T, k), dtype=torch.float32, device="cuda")
+        dl = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        dW = torch.empty((E, H), dtype=torch.float32, device="cuda")
+        dx = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        n = ctypes.c_size_t()
+        m._check(lib.moe_router_bwd_workspace_size(T, H, E, ctypes.byref(n)))
+        ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device="cuda")
+
+        def bwd():
+            m._check(lib.moe_router_bwd(layer.ctx, P(out), P(idx), P(dw),
+                                        P(layer.x), P(w_r), T, H, E, k, 1,
+                                        P(dl), P(dW), P(dx), P(ws), ws.numel(),
+                                        st))
+        msb = timed(bwd)
+        res["bwd_ms"] = round(msb, 4)
+        res["bwd_fp32_TFLOP/s"] = round(4.0 * T * E * H / (msb * 1e-3) / 1e12,
+                                        2)
+    res["what"] = ("moe_router_logits (float64, ascending h, bit-exact) and "
+                   "moe_router_bwd (dlogits + dW_r + dx, float32) per call; "
+                   "logits_equal_to_input_logits (no bias): share of the "
+                   "workload's generated logits (numpy float64 matmul) "
+                   "reproduced bit for bit")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -684,6 +750,7 @@ def main():
     if cfg.mode == "bf16" and not cfg.backward:
         extras["expert_loop"] = expert_loop_extra(m, layer, cfg, st,
                                                   max(2, K // 4))
+    extras["router"] = router_extra(m, layer, cfg, d, st, max(2, K // 2))
 
     flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
     tflops = flop / (ms_step * 1e-3) / 1e12

@@ -113,6 +113,65 @@ moe_status_t moe_ctx_kernel_time(moe_ctx_t ctx, const char* kernel,
                                  int64_t* launches, double* total_ms);
 
 /* ------------------------------------------------------------------------
+ * moe_router_logits -- router projection in front of the top-k.
+ * [PG3, practical-implications paragraph: Top-k routing; PG4, section
+ *  "Background": tokens are routed across many experts.]  The pages do not
+ * give the router's form; the library takes the linear gate reading.
+ * logits[t, e] = sum over h in ascending order of x[t, h] * W_r[e, h],
+ * accumulated in float64 one term at a time (the bf16 products are exact),
+ * plus bias[e], rounded once to float32.  The result does not depend on the
+ * launch shape, so the routing decided on it is reproducible bit for bit.
+ *
+ *  x       bf16    [T, H]
+ *  w_r     bf16    [E, H]   the gate
+ *  bias    float32 [E] or NULL
+ *  logits  float32 [T, E]   out
+ *  T >= 0 (T = 0 is a no-op), H >= 8 with H % 8 == 0, 1 <= E <= 1024;
+ *  x and w_r 16-byte aligned.
+ * Errors: MOE_ERR_INVALID_ARG (null pointer, bad sizes), MOE_ERR_UNSUPPORTED
+ * (E > 1024, H % 8 != 0, misaligned x / w_r, T * max(H, E) >= 2^62),
+ * MOE_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_router_logits(moe_ctx_t ctx, const void* x, const void* w_r,
+                               const float* bias, int64_t T, int32_t H,
+                               int32_t E, float* logits, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_router_bwd -- router backward.
+ * [Same passages as moe_router_logits.]  The routing-weight gradient
+ * reaches the logits only through the softmax the forward used (the top-k
+ * selection passes no gradient).  With the forward weights recomputed from
+ * the logits in float64:
+ *   renormalize != 0:  dl_i = w_i (dw_i - sum_j w_j dw_j) on the chosen set,
+ *                      0 elsewhere
+ *   renormalize == 0:  dl_e = p_e (g_e - sum_j p_j dw_j), p the softmax over
+ *                      all E, g_e = dw on the chosen set and 0 elsewhere
+ * then dW_r = dlogits^T x and the router's share of dx = dlogits W_r, in
+ * float32 with a fixed summation order (deterministic).
+ *
+ *  logits   float32 [T, E];  topk_idx int32 [T, k] (entries in [0, E): ids
+ *           outside are clamped when read and give unspecified values)
+ *  dtopk_w  float32 [T, k]   gradient of the routing weights
+ *  x        bf16 [T, H];  w_r bf16 [E, H]
+ *  dlogits  float32 [T, E]   out (required)
+ *  dw_r     float32 [E, H]   out, or NULL to skip
+ *  dx       float32 [T, H]   out, or NULL to skip
+ *  ws       moe_router_bwd_workspace_size bytes (NULL when that is 0)
+ *  T >= 0, H >= 1, 1 <= k <= min(E, 32), E <= 1024.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
+ * MOE_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_router_bwd_workspace_size(int64_t T, int32_t H, int32_t E,
+                                           size_t* bytes);
+moe_status_t moe_router_bwd(moe_ctx_t ctx, const float* logits,
+                            const int32_t* topk_idx, const float* dtopk_w,
+                            const void* x, const void* w_r, int64_t T,
+                            int32_t H, int32_t E, int32_t k,
+                            int32_t renormalize, float* dlogits, float* dw_r,
+                            float* dx, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_route_topk -- router top-k.
  * [PG3, practical-implications paragraph: Top-k routing; PG2, section "Why
  *  dense and MoE models differ": only a small subset of experts is active

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "lib_path", "load_library", "MoEError", "PREC_BF16", "PREC_MXFP8",
-    "ROWWISE", "COLWISE", "moe_route_topk", "moe_permute", "moe_gather_rows",
+    "ROWWISE", "COLWISE", "moe_router_logits", "moe_router_bwd",
+    "moe_route_topk", "moe_permute", "moe_gather_rows",
     "moe_unpermute", "moe_unpermute_probs_grad", "mxfp8_quantize",
     "moe_grouped_mlp_fwd", "moe_expert_loop_mlp_fwd", "moe_grouped_mlp_bwd",
     "check_device_status",
@@ -76,6 +77,13 @@ _SIGS = {
     "moe_ctx_destroy": [_c_p],
     "moe_ctx_check_device_status": [_c_p, _c_p, ctypes.POINTER(_c_i32)],
     "moe_route_topk": [_c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_i32, _c_p, _c_p,
+                       _c_p],
+    "moe_router_logits": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32,
+                          _c_p, _c_p],
+    "moe_router_bwd_workspace_size": [_c_i64, _c_i32, _c_i32,
+                                      ctypes.POINTER(_c_sz)],
+    "moe_router_bwd": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32,
+                       _c_i32, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_sz,
                        _c_p],
     "moe_permute_workspace_size": [_c_i64, _c_i32, _c_i32,
                                    ctypes.POINTER(_c_sz)],
@@ -224,6 +232,59 @@ def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool = True
                               int(bool(renormalize)), _ptr(idx), _ptr(w),
                               _stream()))
     return idx, w
+
+
+def moe_router_logits(x: torch.Tensor, w_r: torch.Tensor,
+                      bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x bf16 [T, H], w_r bf16 [E, H], bias float32 [E] -> logits float32
+    [T, E] (float64 accumulation in ascending h, one rounding)."""
+    T, H = x.shape
+    E = w_r.shape[0]
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(w_r, torch.bfloat16, (E, H), "w_r")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    lib = load_library()
+    _check(lib.moe_router_logits(_context(x.device), _ptr(x), _ptr(w_r),
+                                 _ptr(bias), T, H, E, _ptr(out), _stream()))
+    return out
+
+
+def moe_router_bwd(logits: torch.Tensor, topk_idx: torch.Tensor,
+                   dtopk_w: torch.Tensor, x: torch.Tensor, w_r: torch.Tensor,
+                   renormalize: bool = True, want_dw: bool = True,
+                   want_dx: bool = True) -> Dict[str, torch.Tensor]:
+    """Router backward: {"dlogits" [T, E]} (+ "dw_r" [E, H], "dx" [T, H]),
+    float32."""
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    H = x.shape[1]
+    dev = logits.device
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    _need(dtopk_w, torch.float32, (T, k), "dtopk_w")
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(w_r, torch.bfloat16, (E, H), "w_r")
+    dl = torch.empty((T, E), dtype=torch.float32, device=dev)
+    dw = torch.empty((E, H), dtype=torch.float32, device=dev) \
+        if want_dw else None
+    dx = torch.empty((T, H), dtype=torch.float32, device=dev) \
+        if want_dx else None
+    lib = load_library()
+    n = _c_sz(0)
+    _check(lib.moe_router_bwd_workspace_size(T, H, E, ctypes.byref(n)))
+    ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+    _check(lib.moe_router_bwd(_context(dev), _ptr(logits), _ptr(topk_idx),
+                              _ptr(dtopk_w), _ptr(x), _ptr(w_r), T, H, E, k,
+                              int(bool(renormalize)), _ptr(dl), _ptr(dw),
+                              _ptr(dx), _ptr(ws), ws.numel(), _stream()))
+    res = {"dlogits": dl}
+    if want_dw:
+        res["dw_r"] = dw
+    if want_dx:
+        res["dx"] = dx
+    return res
 
 
 def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int,

@@ -177,6 +177,71 @@ moe_status_t moe_ctx_kernel_time(moe_ctx_t ctx, const char* kernel,
                     "kernel timing events");
 }
 
+moe_status_t moe_router_logits(moe_ctx_t ctx, const void* x, const void* w_r,
+                               const float* bias, int64_t T, int32_t H,
+                               int32_t E, float* logits, void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
+  MOE_REQUIRE(T >= 0 && H >= 1 && E >= 1, MOE_ERR_INVALID_ARG, "bad sizes");
+  MOE_REQUIRE(E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "E <= %d required",
+              MOE_MAX_EXPERTS);
+  MOE_REQUIRE(T < ((int64_t)1 << 62) / (H > E ? H : E), MOE_ERR_UNSUPPORTED,
+              "T too large");
+  MOE_REQUIRE((int64_t)T / 32 < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+              "T too large");
+  MOE_REQUIRE(H % 8 == 0, MOE_ERR_UNSUPPORTED, "H must be a multiple of 8");
+  if (T == 0) return ok();
+  MOE_REQUIRE(x && w_r && logits, MOE_ERR_INVALID_ARG, "null tensor pointer");
+  MOE_REQUIRE(aligned16(x) && aligned16(w_r), MOE_ERR_UNSUPPORTED,
+              "x and w_r must be 16-byte aligned");
+  return hip_status(moe::launch_router_logits(x, w_r, bias, T, H, E, logits,
+                                              as_stream(stream)),
+                    "router_logits launch");
+}
+
+moe_status_t moe_router_bwd_workspace_size(int64_t T, int32_t H, int32_t E,
+                                           size_t* bytes) {
+  MOE_REQUIRE(bytes != nullptr, MOE_ERR_INVALID_ARG, "null output pointer");
+  MOE_REQUIRE(T >= 0 && H >= 1 && E >= 1, MOE_ERR_INVALID_ARG, "bad sizes");
+  *bytes = moe::router_bwd_ws_bytes(T, H, E);
+  return ok();
+}
+
+moe_status_t moe_router_bwd(moe_ctx_t ctx, const float* logits,
+                            const int32_t* topk_idx, const float* dtopk_w,
+                            const void* x, const void* w_r, int64_t T,
+                            int32_t H, int32_t E, int32_t k,
+                            int32_t renormalize, float* dlogits, float* dw_r,
+                            float* dx, void* ws, size_t ws_bytes,
+                            void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
+  MOE_REQUIRE(T >= 0 && H >= 1 && E >= 1 && k >= 1 && k <= E,
+              MOE_ERR_INVALID_ARG, "bad sizes");
+  MOE_REQUIRE(E <= MOE_MAX_EXPERTS && k <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED,
+              "E <= %d and k <= %d required", MOE_MAX_EXPERTS, MOE_MAX_TOPK);
+  MOE_REQUIRE(T < ((int64_t)1 << 62) / (H > E ? H : E), MOE_ERR_UNSUPPORTED,
+              "T too large");
+  MOE_REQUIRE((T + 3) / 4 < ((int64_t)1 << 31), MOE_ERR_UNSUPPORTED,
+              "T too large");
+  const size_t need = moe::router_bwd_ws_bytes(T, H, E);
+  if (T == 0) return ok();
+  MOE_REQUIRE(logits && topk_idx && dtopk_w && dlogits, MOE_ERR_INVALID_ARG,
+              "null tensor pointer");
+  MOE_REQUIRE((dw_r == nullptr || x != nullptr) &&
+                  (dx == nullptr || w_r != nullptr),
+              MOE_ERR_INVALID_ARG, "dw_r needs x, dx needs w_r");
+  MOE_REQUIRE(dw_r == nullptr || need == 0 || (ws && ws_bytes >= need),
+              MOE_ERR_WORKSPACE, "router_bwd workspace needs %zu bytes", need);
+  return hip_status(moe::launch_router_bwd(logits, topk_idx, dtopk_w, x, w_r,
+                                           T, H, E, k, renormalize != 0,
+                                           dlogits, dw_r, dx, ws,
+                                           as_stream(stream)),
+                    "router_bwd launch");
+}
+
 moe_status_t moe_route_topk(moe_ctx_t ctx, const float* logits, int64_t T,
                             int32_t E, int32_t k, int32_t renormalize,
                             int32_t* topk_idx, float* topk_w, void* stream) {

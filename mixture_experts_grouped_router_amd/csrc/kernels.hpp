@@ -60,6 +60,17 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
                                hipStream_t stream);
+// router projection (float64 accumulation in ascending h) and backward
+hipError_t launch_router_logits(const void* x, const void* w_r,
+                                const float* bias, int64_t T, int H, int E,
+                                float* logits, hipStream_t stream);
+size_t router_bwd_ws_bytes(int64_t T, int H, int E);
+hipError_t launch_router_bwd(const float* logits, const int32_t* topk_idx,
+                             const float* dtopk_w, const void* x,
+                             const void* w_r, int64_t T, int H, int E, int k,
+                             bool renorm, float* dlogits, float* dw_r,
+                             float* dx, void* ws, hipStream_t stream);
+
 // per-expert loop (baseline of the grouped path), bf16; offsets_host is
 // the host copy of offsets
 size_t expert_loop_fwd_ws_bytes(int E, int F, int64_t rows, bool need_h1,
