@@ -61,6 +61,14 @@ Where they are silent this module takes the readings listed here:
       E without renormalisation); the top-k selection itself is piecewise
       constant and passes no gradient.  dW_r = dlogits^T x, and the router's
       share of dx = dlogits W_r.
+  R11 tensor-scaled FP8 (the other 8-bit mode the pages name): one float32
+      scale per tensor, s = amax / 448 from an amax pass (s = 1 for an
+      all-zero tensor), codes = E4M3(float32(v / s)) (round to nearest even,
+      saturating), value = decode(code) * s.  A "tensor" is x_perm, each
+      expert's W_gu[e] and W_dn[e] (separate weight tensors per expert, as
+      in a grouped linear layer), and the SwiGLU output A stored as bf16
+      (its amax taken over the bf16 values).  GEMMs run on the codes and
+      multiply by the two scales.
 
 Pins of this module against things other than itself live in
 ``tests/test_oracle_pins.py``.
@@ -530,6 +538,72 @@ def grouped_mlp_bwd_mxfp8(dz_perm, x_perm, w_gu, w_dn, w_perm, offsets
         dx[lo:hi] = _mx_rows(dh1) @ _mx_rows(_as_f64(w_gu[e]).T).T
     return {"dx_perm": dx, "dw_perm": dw_perm, "dw_gu": dw_gu,
             "dw_dn": dw_dn}
+
+
+# --------------------------------------------------------------------------
+# Tensor-scaled FP8  [PG1 "Reducing memory and quantisation cost" and PG2
+# "3) Quantisation overhead in low-precision training": 8-bit formats with
+# scales, from 16-bit masters]; reading R11
+# --------------------------------------------------------------------------
+def fp8_tensor_scale(amax) -> np.float32:
+    """s = amax / 448 in float32 (1 for amax == 0)."""
+    a = np.float32(amax)
+    return np.float32(a / np.float32(E4M3_MAX)) if a > 0 else np.float32(1.0)
+
+
+def fp8_tensor_quantize(v) -> Tuple[np.ndarray, np.float32]:
+    """One tensor (bf16 bit patterns or floats exactly representable in
+    float32) -> (E4M3 codes, float32 scale)."""
+    vf = _as_f64(v).astype(np.float32)
+    s = fp8_tensor_scale(np.abs(vf).max() if vf.size else 0.0)
+    q = (vf / s).astype(np.float32)              # IEEE float32 division
+    return e4m3_encode(q.astype(f64)), s
+
+
+def fp8_tensor_dequantize(codes, s) -> np.ndarray:
+    return e4m3_decode(codes) * f64(s)
+
+
+def grouped_mlp_fwd_fp8_tensor(x_perm, w_gu, w_dn, w_perm, offsets
+                               ) -> Dict[str, np.ndarray]:
+    """R11 forward: x_perm, each W_gu[e] and W_dn[e] quantised per tensor;
+    h1 = Xq Wq^T (float64 on the dequantised values); A = w * silu(g) * u
+    rounded to bf16, quantised per tensor over all rows; z = Aq Wdnq^T."""
+    E = len(offsets) - 1
+    rows = np.asarray(x_perm).shape[0]
+    F = np.asarray(w_gu).shape[1] // 2
+    H = np.asarray(w_dn).shape[1]
+    w = np.ones(rows) if w_perm is None else np.asarray(w_perm, dtype=f64)
+    xc, xs = fp8_tensor_quantize(x_perm)
+    X = fp8_tensor_dequantize(xc, xs)
+    a = np.zeros((rows, F), dtype=f64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        wc, ws = fp8_tensor_quantize(w_gu[e])
+        h1 = X[lo:hi] @ fp8_tensor_dequantize(wc, ws).T
+        g, u = h1[:, :F], h1[:, F:]
+        a[lo:hi] = w[lo:hi, None] * silu(g) * u
+    a16 = _as_f64(_bf16_round_bits(a))
+    ac, as_ = fp8_tensor_quantize(a16)
+    A = fp8_tensor_dequantize(ac, as_)
+    z = np.zeros((rows, H), dtype=f64)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        wc, ws = fp8_tensor_quantize(w_dn[e])
+        z[lo:hi] = A[lo:hi] @ fp8_tensor_dequantize(wc, ws).T
+    return {"z": z, "a": a16, "a_scale": as_}
+
+
+def _bf16_round_bits(a: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bit patterns (uint16): to float32, then round to
+    nearest even on the upper 16 bits."""
+    b = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
 
 
 # --------------------------------------------------------------------------

@@ -660,3 +660,60 @@ def test_router_weight_grads_adjoint():
             x2 = x.copy()
             x2[t, h] += 1.0
             assert abs(float((dl * (x2 @ w.T)).sum()) - base - dx[t, h]) < 1e-9
+
+
+# ------------------------------------------------------ tensor-scaled FP8
+def test_fp8_tensor_round_trip_exact_with_power_of_two_scale():
+    """Values decode(c) * 2^k with one of them at 448 * 2^k: the scale is
+    2^k exactly and every code comes back."""
+    rng = np.random.default_rng(50)
+    codes = rng.integers(0, 256, 4000).astype(np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]          # no NaN codes
+    codes[0] = 0x7E                                 # +448
+    for k in (-20, -3, 0, 5):
+        v = O.e4m3_decode(codes) * 2.0 ** k
+        c2, s = O.fp8_tensor_quantize(v.astype(np.float32))
+        assert s == np.float32(2.0 ** k)
+        # equal codes, except that -0 and +0 both decode to zero
+        d = O.e4m3_decode(c2) * 2.0 ** k
+        np.testing.assert_array_equal(d, v)
+
+
+def test_fp8_tensor_scale_and_error_bound():
+    rng = np.random.default_rng(51)
+    v = (rng.standard_normal(5000) * 3.7).astype(np.float32)
+    c, s = O.fp8_tensor_quantize(v)
+    amax = np.abs(v).max()
+    assert s == np.float32(np.float32(amax) / np.float32(448.0))
+    assert (c & 0x7F).max() == 0x7E               # the amax lands on 448
+    d = O.fp8_tensor_dequantize(c, s)
+    a = np.abs(v.astype(np.float64))
+    normal = a / s >= 2.0 ** -6
+    # 3 mantissa bits: half an ulp is 2^-4 relative on the normal grid,
+    # 2^-10 * s absolute on the subnormal one
+    assert np.all(np.abs(d - v)[normal] <= 2.0 ** -4 * a[normal] * (1 + 1e-6))
+    assert np.all(np.abs(d - v)[~normal] <= 2.0 ** -10 * s * (1 + 1e-6))
+    # an all-zero tensor has scale 1 and zero codes
+    c0, s0 = O.fp8_tensor_quantize(np.zeros(64, np.float32))
+    assert s0 == 1.0 and not np.any(c0 & 0x7F)
+
+
+def test_bf16_round_bits_matches_torch():
+    rng = np.random.default_rng(52)
+    v = rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))
+    np.testing.assert_array_equal(O._bf16_round_bits(v),
+                                  bf16_bits(v.astype(np.float32)))
+
+
+def test_fp8_tensor_layer_close_to_unquantised():
+    T, H, F, E, k = 256, 128, 256, 8, 2
+    d = generate(T, H, F, E, k, seed=4, want=("x", "logits", "w_gu", "w_dn"))
+    idx, w = O.route_topk(d["logits"], k)
+    maps = O.permute_index(idx, E)
+    xp = O.permute_rows(d["x"], maps["src_row"], k)
+    wp = O.permute_weights(w, maps["src_row"])
+    ref = O.grouped_mlp_fwd(xp, d["w_gu"], d["w_dn"], wp, maps["offsets"])
+    q = O.grouped_mlp_fwd_fp8_tensor(xp, d["w_gu"], d["w_dn"], wp,
+                                     maps["offsets"])
+    err = O.rel_err(q["z"], ref["z"])
+    assert 1e-3 < err < 0.12, err
