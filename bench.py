@@ -173,6 +173,7 @@ class Layer:
         self.idx = e((T, k), i32)
         self.w = e((T, k), f32)
         self.mx = cfg.mode == "mxfp8"
+        self.f8t = cfg.mode == "fp8t"
         # MXFP8 forward only: the permute writes E4M3 codes + E8M0 scales of
         # x (fused quantisation).  With a backward pass the bf16 x_perm is
         # kept for the weight gradient (quantised along tokens there) and
@@ -197,7 +198,8 @@ class Layer:
         self.a = e((rows, F), b16) if save else None
         fa = m._FwdArgs()
         fa.E, fa.H, fa.F, fa.rows = E, H, F, rows
-        fa.precision = m.PREC_MXFP8 if self.mx else m.PREC_BF16
+        fa.precision = m.PREC_MXFP8 if self.mx else (
+            m.PREC_FP8_TENSOR if self.f8t else m.PREC_BF16)
         fa.x_perm = self.x_perm.data_ptr()
         fa.x_perm_scale = self.x_perm_scale.data_ptr() if self.mx_codes \
             else None
@@ -300,7 +302,9 @@ KERNELS = [
     "gemm_dgrad_down_swiglu_bwd", "gemm_dgrad_gate_up", "gemm_wgrad_down",
     "gemm_wgrad_gate_up", "gemm_dgrad_down_swiglu_bwd_mxfp8",
     "gemm_dgrad_gate_up_mxfp8", "gemm_wgrad_down_mxfp8",
-    "gemm_wgrad_gate_up_mxfp8", "routing_weight_grad_reduce", "probs_grad",
+    "gemm_wgrad_gate_up_mxfp8", "gemm_gate_up_swiglu_fp8t", "gemm_down_fp8t",
+    "fp8_amax", "fp8_tensor_quantize", "fp8_amax_clear",
+    "routing_weight_grad_reduce", "probs_grad",
     "tile_table", "padded_offsets", "expert_order",
 ]
 # algorithmic flop per step (each GEMM runs once per step)
@@ -313,6 +317,7 @@ KERNEL_FLOP = {
     "gemm_wgrad_down": _F2, "gemm_wgrad_gate_up": _F4,
     "gemm_dgrad_down_swiglu_bwd_mxfp8": _F2, "gemm_dgrad_gate_up_mxfp8": _F4,
     "gemm_wgrad_down_mxfp8": _F2, "gemm_wgrad_gate_up_mxfp8": _F4,
+    "gemm_gate_up_swiglu_fp8t": _F4, "gemm_down_fp8t": _F2,
 }
 MX_BYTES = 2.0 + 1.0 + 1.0 / 32   # bf16 read, E4M3 code + E8M0/32 written
 
@@ -343,6 +348,11 @@ KERNEL_BYTES = {
     # backward: dZ, A, dH1, X along tokens (padding not counted)
     "mxfp8_quantize_segments": lambda c: c.rows * (2.0 * c.H + 3.0 * c.F)
     * MX_BYTES,
+    # tensor-scaled FP8: an amax read and a quantising pass (read bf16,
+    # write codes) over both weight tensors, x_perm and A
+    "fp8_amax": lambda c: 2.0 * (3.0 * c.E * c.H * c.F + c.rows * (c.H + c.F)),
+    "fp8_tensor_quantize": lambda c: 3.0 * (3.0 * c.E * c.H * c.F
+                                            + c.rows * (c.H + c.F)),
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_gemm.json")
@@ -415,7 +425,7 @@ def cpu_baseline(cfg, d, n_tokens):
     passes = "fwd+bwd" if cfg.backward else "fwd"
     per_flop = 6.0 + (12.0 if cfg.backward else 0.0)
     t0 = time.perf_counter()
-    if cfg.mode != "mxfp8":
+    if cfg.mode == "bf16":
         if cfg.backward:
             O.layer_bwd(x, lg, d["w_gu"], d["w_dn"], d["dy"][:n_tokens],
                         cfg.k)
@@ -424,6 +434,24 @@ def cpu_baseline(cfg, d, n_tokens):
         flop = per_flop * n_tokens * cfg.k * cfg.H * cfg.F
         what = (f"first {n_tokens} of {cfg.T} tokens of the {cfg.name} "
                 f"workload, whole layer {passes} in float64 numpy")
+    elif cfg.mode == "fp8t":
+        F, Fs = cfg.F, min(cfg.F, 7168)
+        idx, w = O.route_topk(lg, cfg.k)
+        mp = O.permute_index(idx, d["w_gu"].shape[0])
+        lo, hi = int(mp["offsets"][0]), int(mp["offsets"][1])
+        sr = mp["src_row"][lo:hi]
+        xp = O.permute_rows(x, sr, cfg.k)
+        wp = O.permute_weights(w, sr)
+        off = np.array([0, hi - lo], dtype=np.int32)
+        wgu = np.concatenate([d["w_gu"][0, :Fs], d["w_gu"][0, F:F + Fs]])[None]
+        wdn = np.ascontiguousarray(d["w_dn"][0][:, :Fs])[None]
+        O.grouped_mlp_fwd_fp8_tensor(xp, wgu, wdn, wp, off)
+        flop = per_flop * (hi - lo) * cfg.H * Fs
+        what = (f"tensor-scaled FP8 MLP fwd (quantisation included; each "
+                f"sampled operand scaled as its own tensor) of expert 0 on "
+                f"its {hi - lo} rows among the first {n_tokens} of {cfg.T} "
+                f"tokens of the {cfg.name} workload, FFN columns [0, {Fs}) "
+                f"of {F}, float64 numpy")
     else:
         F, Fs = cfg.F, min(cfg.F, 3584 if cfg.backward else 7168)
         idx, w = O.route_topk(lg, cfg.k)
@@ -756,10 +784,11 @@ def main():
     tflops = flop / (ms_step * 1e-3) / 1e12
     tokens_s = cfg.T / (ms_step * 1e-3)
     work = algorithmic(cfg)
-    peak = PEAK_FP8_TFLOPS if cfg.mode == "mxfp8" else PEAK_BF16_TFLOPS
+    peak = PEAK_BF16_TFLOPS if cfg.mode == "bf16" else PEAK_FP8_TFLOPS
     # dominant kernel: the grouped gate/up GEMM with the ScaledSwiGLU
     # epilogue; one launch covers all T*k routed rows: 4*T*k*H*F flop
-    dom = "gemm_gate_up_swiglu_" + ("mxfp8" if cfg.mode == "mxfp8" else "bf16")
+    dom = "gemm_gate_up_swiglu_" + {"mxfp8": "mxfp8", "fp8t": "fp8t"}.get(
+        cfg.mode, "bf16")
     dom_flop = 4.0 * cfg.rows * cfg.H * cfg.F
     n_dom, dom_ms, _ = ktimes[dom]
     ach = dom_flop / (dom_ms * 1e-3) / 1e12
@@ -805,7 +834,7 @@ def main():
             # 16 host threads runs the per-expert matmuls at ~0.4 TFLOP/s)
             per_tok = (18.0 if cfg.backward else 6.0) * cfg.k * cfg.H * cfg.F
             n_tok = max(16, min(cfg.T, int(6e12 / per_tok)))
-            if cfg.mode == "mxfp8":   # one expert, one FFN slice (above)
+            if cfg.mode != "bf16":   # one expert, one FFN slice (above)
                 n_tok = min(cfg.T, 8192)
         cpu = cpu_baseline(cfg, d, n_tok)
 
@@ -820,7 +849,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8-e4m3" if cfg.mode == "mxfp8" else "bf16",
+        "dtype": {"mxfp8": "mxfp8-e4m3", "fp8t": "fp8-e4m3-tensor-scaled"}.get(
+            cfg.mode, "bf16"),
         "data": "synthetic (seeded; random-init expert weights)",
         "config": {"workload": f"{cfg.name}: {cfg.description}",
                    "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E,

@@ -60,7 +60,9 @@ typedef enum moe_status {
 
 typedef enum moe_precision {
   MOE_PREC_BF16 = 0,
-  MOE_PREC_MXFP8_E4M3 = 1
+  MOE_PREC_MXFP8_E4M3 = 1,
+  /* E4M3 with one float32 scale per tensor (forward only) */
+  MOE_PREC_FP8_TENSOR = 2
 } moe_precision_t;
 
 typedef enum moe_mx_axis {
@@ -289,6 +291,26 @@ moe_status_t mxfp8_quantize(moe_ctx_t ctx, const void* src, int64_t batch,
                             uint8_t* codes, uint8_t* scales, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_fp8_tensor_quantize -- tensor-scaled FP8 quantisation.
+ * [PG1, section "Reducing memory and quantisation cost"; PG2, section "3)
+ *  Quantisation overhead in low-precision training".]
+ * src bf16 holds n_seg tensors of seg_elems values each (seg_elems % 8 ==
+ * 0, 16-byte aligned).  Per tensor: amax = max |v|, s = amax / 448 in
+ * float32 (1 when amax is 0), code = OCP E4M3 of float32(v / s), round to
+ * nearest even, saturating at +-448.
+ *  codes  uint8 [n_seg, seg_elems] out;  scales float32 [n_seg] out
+ *  ws     moe_fp8_tensor_quantize_workspace_size bytes (the amax pass)
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED (seg_elems % 8,
+ * alignment, n_seg >= 2^16), MOE_ERR_WORKSPACE, MOE_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_fp8_tensor_quantize_workspace_size(int64_t n_seg,
+                                                    size_t* bytes);
+moe_status_t moe_fp8_tensor_quantize(moe_ctx_t ctx, const void* src,
+                                     int64_t n_seg, int64_t seg_elems,
+                                     uint8_t* codes, float* scales, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_mlp_fwd -- grouped GEMM gate/up -> ScaledSwiGLU x routing
  * weight -> grouped GEMM down, over all experts in one call.
  * [PG1, sections "Grouped experts instead of a Python loop" (one grouped
@@ -306,7 +328,16 @@ moe_status_t mxfp8_quantize(moe_ctx_t ctx, const void* src, int64_t batch,
  * MFMA with float32 accumulation; a is quantised from float32 in the gate/up
  * epilogue; h1_save / a_save hold the unquantised float32 values rounded to
  * bf16.
- * Sizes: 1 <= E <= 1024; H and F multiples of 64 (bf16) or 128 (MXFP8);
+ * FP8 tensor-scaled (MOE_PREC_FP8_TENSOR, forward only) [PG1, section
+ * "Reducing memory and quantisation cost"; PG2, section "3) Quantisation
+ * overhead in low-precision training": 8-bit elements with scales from
+ * 16-bit masters]: x_perm (bf16), each W_gu[e] and each W_dn[e] get one
+ * float32 scale s = amax / 448 (1 if all zero) and E4M3 codes of
+ * float32(v / s), as in moe_fp8_tensor_quantize; the GEMMs multiply the
+ * E4M3 products by the two scales; a (bf16, over all rows) is quantised the
+ * same way for the down GEMM; h1_save / a_save hold the bf16 values.
+ * x_perm_scale and the pre-quantised weight fields must be NULL.
+ * Sizes: 1 <= E <= 1024; H and F multiples of 64 (bf16) or 128 (8-bit);
  * one expert's operands must stay below 4 GiB (byte offsets are 32-bit).
  * Errors: MOE_ERR_INVALID_ARG (null required pointer, bad sizes),
  * MOE_ERR_UNSUPPORTED (size limits, misaligned pointers: operands 16-byte,

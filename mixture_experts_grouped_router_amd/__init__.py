@@ -18,6 +18,7 @@ import torch
 
 __all__ = [
     "lib_path", "load_library", "MoEError", "PREC_BF16", "PREC_MXFP8",
+    "PREC_FP8_TENSOR", "fp8_tensor_quantize",
     "ROWWISE", "COLWISE", "moe_router_logits", "moe_router_bwd",
     "moe_route_topk", "moe_permute", "moe_gather_rows",
     "moe_unpermute", "moe_unpermute_probs_grad", "mxfp8_quantize",
@@ -32,6 +33,7 @@ lib_path = os.path.join(_HERE, "libmoe.so")
 
 PREC_BF16 = 0
 PREC_MXFP8 = 1
+PREC_FP8_TENSOR = 2
 ROWWISE = 0
 COLWISE = 1
 
@@ -80,6 +82,9 @@ _SIGS = {
                        _c_p],
     "moe_router_logits": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32,
                           _c_p, _c_p],
+    "moe_fp8_tensor_quantize_workspace_size": [_c_i64, ctypes.POINTER(_c_sz)],
+    "moe_fp8_tensor_quantize": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p,
+                                _c_sz, _c_p],
     "moe_router_bwd_workspace_size": [_c_i64, _c_i32, _c_i32,
                                       ctypes.POINTER(_c_sz)],
     "moe_router_bwd": [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32,
@@ -232,6 +237,28 @@ def moe_route_topk(logits: torch.Tensor, k: int, renormalize: bool = True
                               int(bool(renormalize)), _ptr(idx), _ptr(w),
                               _stream()))
     return idx, w
+
+
+def fp8_tensor_quantize(src: torch.Tensor, n_seg: int = 1
+                        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 tensor holding n_seg equal tensors -> (E4M3 codes uint8 of the
+    same shape, float32 scales [n_seg]); one scale amax / 448 per tensor."""
+    if src.dtype != torch.bfloat16 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous bf16 tensor")
+    n = src.numel()
+    if n_seg < 1 or n % n_seg:
+        raise ValueError("numel must split into n_seg equal tensors")
+    dev = src.device
+    codes = torch.empty(src.shape, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n_seg, dtype=torch.float32, device=dev)
+    lib = load_library()
+    nb = _c_sz(0)
+    _check(lib.moe_fp8_tensor_quantize_workspace_size(n_seg, ctypes.byref(nb)))
+    ws = torch.empty(max(int(nb.value), 256), dtype=torch.uint8, device=dev)
+    _check(lib.moe_fp8_tensor_quantize(_context(dev), _ptr(src), n_seg,
+                                       n // n_seg, _ptr(codes), _ptr(scales),
+                                       _ptr(ws), ws.numel(), _stream()))
+    return codes, scales
 
 
 def moe_router_logits(x: torch.Tensor, w_r: torch.Tensor,

@@ -177,6 +177,42 @@ moe_status_t moe_ctx_kernel_time(moe_ctx_t ctx, const char* kernel,
                     "kernel timing events");
 }
 
+moe_status_t moe_fp8_tensor_quantize_workspace_size(int64_t n_seg,
+                                                    size_t* bytes) {
+  MOE_REQUIRE(bytes != nullptr && n_seg >= 0, MOE_ERR_INVALID_ARG,
+              "bad arguments");
+  *bytes = (size_t)n_seg * sizeof(uint32_t);
+  return ok();
+}
+
+moe_status_t moe_fp8_tensor_quantize(moe_ctx_t ctx, const void* src,
+                                     int64_t n_seg, int64_t seg_elems,
+                                     uint8_t* codes, float* scales, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
+  MOE_REQUIRE(n_seg >= 0 && seg_elems >= 0, MOE_ERR_INVALID_ARG, "bad sizes");
+  MOE_REQUIRE(n_seg < 65536 && seg_elems % 8 == 0, MOE_ERR_UNSUPPORTED,
+              "n_seg < 65536 and seg_elems % 8 == 0 required");
+  if (n_seg == 0) return ok();
+  MOE_REQUIRE(scales && (seg_elems == 0 || (src && codes)),
+              MOE_ERR_INVALID_ARG, "null tensor pointer");
+  MOE_REQUIRE(aligned16(src) && (reinterpret_cast<uintptr_t>(codes) & 7u) == 0,
+              MOE_ERR_UNSUPPORTED, "src 16-byte and codes 8-byte aligned");
+  MOE_REQUIRE(ws && ws_bytes >= (size_t)n_seg * 4, MOE_ERR_WORKSPACE,
+              "fp8_tensor_quantize workspace needs %lld bytes",
+              (long long)n_seg * 4);
+  hipStream_t st = as_stream(stream);
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  hipError_t e = moe::launch_zero_u32(amax, (int)n_seg, st);
+  if (e == hipSuccess) e = moe::launch_seg_amax(src, seg_elems, (int)n_seg, amax, st);
+  if (e == hipSuccess)
+    e = moe::launch_tensor_quant(src, seg_elems, (int)n_seg, amax, codes,
+                                 scales, st);
+  return hip_status(e, "fp8_tensor_quantize");
+}
+
 moe_status_t moe_router_logits(moe_ctx_t ctx, const void* x, const void* w_r,
                                const float* bias, int64_t T, int32_t H,
                                int32_t E, float* logits, void* stream) {
@@ -428,9 +464,10 @@ moe_status_t check_mlp_dims(int32_t E, int32_t H, int32_t F, int64_t rows,
               (long long)rows);
   MOE_REQUIRE(E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED, "E > %d",
               MOE_MAX_EXPERTS);
-  MOE_REQUIRE(prec == MOE_PREC_BF16 || prec == MOE_PREC_MXFP8_E4M3,
+  MOE_REQUIRE(prec == MOE_PREC_BF16 || prec == MOE_PREC_MXFP8_E4M3 ||
+                  prec == MOE_PREC_FP8_TENSOR,
               MOE_ERR_INVALID_ARG, "bad precision");
-  // K steps of 64 (bf16) / 128 (MXFP8) without masking; N tails are masked
+  // K steps of 64 (bf16) / 128 (8-bit) without masking; N tails are masked
   const int kq = prec == MOE_PREC_BF16 ? 64 : 128;
   MOE_REQUIRE(H % kq == 0 && F % kq == 0, MOE_ERR_UNSUPPORTED,
               "H and F must be multiples of %d", kq);
@@ -455,6 +492,9 @@ moe_status_t moe_grouped_mlp_fwd_workspace_size(const moe_mlp_fwd_args* a,
   if (a->precision == MOE_PREC_BF16)
     *bytes = moe::mlp_fwd_bf16_ws_bytes(a->E, a->H, a->F, a->rows,
                                         a->a_save == nullptr);
+  else if (a->precision == MOE_PREC_FP8_TENSOR)
+    *bytes = moe::mlp_fwd_fp8t_ws_bytes(a->E, a->H, a->F, a->rows,
+                                        a->a_save == nullptr);
   else
     *bytes = moe::mlp_fwd_mx_ws_bytes(
         a->E, a->H, a->F, a->rows, a->x_perm_scale == nullptr,
@@ -474,6 +514,12 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
   MOE_REQUIRE((a->x_perm && a->z_perm) || a->rows == 0, MOE_ERR_INVALID_ARG,
               "null x_perm / z_perm");
   const bool mx = a->precision == MOE_PREC_MXFP8_E4M3;
+  const bool f8t = a->precision == MOE_PREC_FP8_TENSOR;
+  if (f8t)
+    MOE_REQUIRE(!a->x_perm_scale && !a->w_gu_q && !a->w_gu_s && !a->w_dn_q &&
+                    !a->w_dn_s,
+                MOE_ERR_INVALID_ARG,
+                "FP8 tensor mode takes bf16 x_perm and bf16 weights");
   if (!mx || a->w_gu_q == nullptr || a->w_dn_q == nullptr)
     MOE_REQUIRE(a->w_gu && a->w_dn, MOE_ERR_INVALID_ARG, "null weights");
   if (mx && a->w_gu_q) MOE_REQUIRE(a->w_gu_s, MOE_ERR_INVALID_ARG, "w_gu_s");
@@ -495,7 +541,14 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
   MOE_REQUIRE(a->ws != nullptr && a->ws_bytes >= need, MOE_ERR_WORKSPACE,
               "grouped_mlp_fwd workspace needs %zu bytes", need);
   hipError_t e;
-  if (!mx) {
+  if (f8t) {
+    MOE_REQUIRE(aligned16(a->h1_save) && aligned16(a->a_save),
+                MOE_ERR_UNSUPPORTED, "saves must be 16-byte aligned");
+    e = moe::launch_mlp_fwd_fp8t(a->E, a->H, a->F, a->rows, a->x_perm,
+                                 a->w_gu, a->w_dn, a->w_perm, a->offsets,
+                                 a->z_perm, a->h1_save, a->a_save, a->ws,
+                                 as_stream(stream));
+  } else if (!mx) {
     e = moe::launch_mlp_fwd_bf16(a->E, a->H, a->F, a->rows, a->x_perm, a->w_gu,
                                  a->w_dn, a->w_perm, a->offsets, a->z_perm,
                                  a->h1_save, a->a_save, a->ws,
@@ -570,6 +623,8 @@ moe_status_t moe_grouped_mlp_bwd_workspace_size(const moe_mlp_bwd_args* a,
   MOE_REQUIRE(a && bytes, MOE_ERR_INVALID_ARG, "null pointer");
   moe_status_t s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
   if (s != MOE_OK) return s;
+  MOE_REQUIRE(a->precision != MOE_PREC_FP8_TENSOR, MOE_ERR_UNSUPPORTED,
+              "the FP8 tensor-scaled mode is forward only");
   if (a->precision == MOE_PREC_MXFP8_E4M3) {
     // token-direction operands [max(H, 2F)][rows + 128 E (+128)] are
     // addressed with 32-bit byte offsets
@@ -593,6 +648,8 @@ moe_status_t moe_grouped_mlp_bwd(moe_ctx_t ctx, const moe_mlp_bwd_args* a,
   MOE_REQUIRE(a != nullptr, MOE_ERR_INVALID_ARG, "null args");
   s = check_mlp_dims(a->E, a->H, a->F, a->rows, a->precision);
   if (s != MOE_OK) return s;
+  MOE_REQUIRE(a->precision != MOE_PREC_FP8_TENSOR, MOE_ERR_UNSUPPORTED,
+              "the FP8 tensor-scaled mode is forward only");
   MOE_REQUIRE(a->offsets && a->w_gu && a->w_dn && a->dw_gu && a->dw_dn,
               MOE_ERR_INVALID_ARG, "null offsets / weights / weight grads");
   if (a->rows > 0)

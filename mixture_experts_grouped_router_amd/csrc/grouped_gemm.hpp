@@ -62,7 +62,10 @@ enum Epi {
   EPI_SWIGLU_BWD = 2,  // dgrad of the down projection + SwiGLU backward
   EPI_SWIGLU_MX = 3    // as EPI_SWIGLU, A quantised to MXFP8 along f
 };
-enum Prec { P_BF16 = 0, P_FP8 = 1 };
+// P_FP8: MXFP8 (E8M0 scale per 32 along K, scaled MFMA); P_FP8T: E4M3
+// with one float32 scale per tensor (unit MFMA scales, the tensor scales
+// applied to the accumulators before the epilogue)
+enum Prec { P_BF16 = 0, P_FP8 = 1, P_FP8T = 2 };
 
 #ifndef MOE_SCHED_GROUPS
 #define MOE_SCHED_GROUPS 1
@@ -152,6 +155,12 @@ struct Params {
   const float* w;             // routing weight per row (nullable -> 1)
   float* dw_part;             // EPI_SWIGLU_BWD: [tiles_n][rows]
   int64_t rows;
+  // P_FP8T: tensor scales of A (tsa[0]) and of expert e's B (tsb[e])
+  const float* tsa;
+  const float* tsb;
+  // EPI_SWIGLU, nullable: amax of the bf16 A output (float32 bits,
+  // atomic max)
+  uint32_t* amax_out;
 };
 
 // Swizzle of the 16-byte chunk c of LDS tile row r.  It depends only on
@@ -681,6 +690,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
     const int c8 = lane & 7;
     const int f = n0 + 64 * wn + 8 * c8;
+    uint32_t amx = 0;   // amax_out: largest |A| of the lane, bf16 bits
 #pragma unroll
     for (int qb = 0; qb < 16; qb += 4) {
       uint4 c0[4], c1[4];
@@ -730,11 +740,26 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
                                (uint32_t)(p.F / 128))] = (uint8_t)(sx + 127);
           }
         }
-        if (ok && (EPI == EPI_SWIGLU || p.c))
-          *reinterpret_cast<uint4*>(p.c + row * p.ldc + f) =
+        if (ok && (EPI == EPI_SWIGLU || p.c)) {
+          const uint4 o =
               make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+          *reinterpret_cast<uint4*>(p.c + row * p.ldc + f) = o;
+          if (p.amax_out) {
+            const uint32_t w4[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+              amx = max(amx, max(w4[d] & 0x7fffu, (w4[d] >> 16) & 0x7fffu));
+          }
+        }
       }
+    }
+    if (p.amax_out) {
+      // the bf16 magnitudes order like their float32 bits
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1)
+        amx = max(amx, (uint32_t)__shfl_xor((int)amx, off, 64));
+      if (lane == 0) atomicMax(p.amax_out, amx << 16);
     }
   } else if constexpr (EPI == EPI_STORE) {
     // bf16 C through LDS; on readback lane l takes chunk l % 16 (8 columns)
@@ -899,11 +924,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
                 "MXFP8 operands are K-contiguous");
   // RAGGED_K with K-contiguous operands needs every expert's K range padded
   // to whole K steps (the MXFP8 token-direction layout)
-  static_assert(G == RAGGED_M || P == P_FP8 || (LA == MC && LB == MC),
+  static_assert(G == RAGGED_M || P != P_BF16 || (LA == MC && LB == MC),
                 "bf16 RAGGED_K operands are MN-contiguous");
-  using Fr = Frags<P>;
+  // the 8-bit modes share fragments and MFMAs (unit scales for P_FP8T)
+  constexpr int PF = P == P_BF16 ? P_BF16 : P_FP8;
+  using Fr = Frags<PF>;
   constexpr int kSl = Fr::kSlices;
-  constexpr int kElemBytes = P == P_FP8 ? 1 : 2;
+  constexpr int kElemBytes = P == P_BF16 ? 2 : 1;
   constexpr int kStepK = kRowBytes / kElemBytes;  // K elements per step
 
   __shared__ __attribute__((aligned(1024))) char sA0[kTileBytes];
@@ -989,7 +1016,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   uint32_t tra[4], trb[4];
   if constexpr (LA == MC) McDirect::frag_offsets(wm, lane, tra);
   if constexpr (LB == MC) McDirect::frag_offsets(wn, lane, trb);
-  uint32_t sa_cur[4] = {0, 0, 0, 0}, sb_cur[4] = {0, 0, 0, 0};
+  // E8M0 scale bytes of the current K step (P_FP8T: 127 = 2^0 throughout)
+  constexpr uint32_t kS0 = P == P_FP8T ? 0x7f7f7f7fu : 0u;
+  uint32_t sa_cur[4] = {kS0, kS0, kS0, kS0}, sb_cur[4] = {kS0, kS0, kS0, kS0};
   // byte selector for v_perm: lane group g takes scale bytes (g, 2 + g)
   const uint32_t sel = (lane >> 5) ? 0x0c0c0301u : 0x0c0c0200u;
   if constexpr (P == P_FP8) {
@@ -1026,7 +1055,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   const int nk = (kdim + kStepK - 1) / kStepK;
   // LDS reads per K slice: 4 per K-contiguous side (16-byte reads), 8 per
   // MN-contiguous side (two 8-byte transposed reads per block); MXFP8 16
-  constexpr int kNR = P == P_FP8 ? 16
+  constexpr int kNR = P != P_BF16 ? 16
                                  : (LA == KC ? 4 : 8) + (LB == KC ? 4 : 8);
   // part 1: A (and the MXFP8 scales), part 2: B, 3: both
   auto issue_part = [&](char* bufa, char* bufb, int kt, bool real, int part) {
@@ -1105,18 +1134,18 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     for (int kk = 0; kk < kSl - 1; ++kk) {
       if (kSplit && kk == 1) issue_part(sA1, sB1, kt + 1, kt + 1 < nk, 2);
       fload(nxt, sA0, sB0, kk + 1);
-      if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
-      else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
+      if (kk == 0) Mma<PF>::template run<0>(cur, sa_cur, sb_cur, acc);
+      else Mma<PF>::template run<1>(cur, sa_cur, sb_cur, acc);
       cur = nxt;
       slice_sched(kk);
       // keep the scheduler from hoisting later slices' reads (registers)
       __builtin_amdgcn_sched_barrier(0);
     }
-    Mma<P>::template run<kSl - 1, 0>(cur, sa_cur, sb_cur, acc);
+    Mma<PF>::template run<kSl - 1, 0>(cur, sa_cur, sb_cur, acc);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     fload(nxt, sA1, sB1, 0);
-    Mma<P>::template run<kSl - 1, 1>(cur, sa_cur, sb_cur, acc);
+    Mma<PF>::template run<kSl - 1, 1>(cur, sa_cur, sb_cur, acc);
     cur = nxt;
     take_scales();
     sched_reads_mfma<kNR, 8>();
@@ -1129,17 +1158,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     for (int kk = 0; kk < kSl - 1; ++kk) {
       if (kSplit && kk == 1) issue_part(sA0, sB0, kt + 2, kt + 2 < nk, 2);
       fload(nxt, sA1, sB1, kk + 1);
-      if (kk == 0) Mma<P>::template run<0>(cur, sa_cur, sb_cur, acc);
-      else Mma<P>::template run<1>(cur, sa_cur, sb_cur, acc);
+      if (kk == 0) Mma<PF>::template run<0>(cur, sa_cur, sb_cur, acc);
+      else Mma<PF>::template run<1>(cur, sa_cur, sb_cur, acc);
       cur = nxt;
       slice_sched(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
-    Mma<P>::template run<kSl - 1, 0>(cur, sa_cur, sb_cur, acc);
+    Mma<PF>::template run<kSl - 1, 0>(cur, sa_cur, sb_cur, acc);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     fload(nxt, sA0, sB0, 0);
-    Mma<P>::template run<kSl - 1, 1>(cur, sa_cur, sb_cur, acc);
+    Mma<PF>::template run<kSl - 1, 1>(cur, sa_cur, sb_cur, acc);
     cur = nxt;
     take_scales();
     sched_reads_mfma<kNR, 8>();
@@ -1150,6 +1179,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // direct load has landed) before the stages become epilogue staging
   __syncthreads();
   char* wbuf = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
+  if constexpr (P == P_FP8T) {
+    // the two tensor scales
+    const float f = p.tsa[0] * p.tsb[tc.e];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] *= f;
+  }
   epilogue<G, EPI>(p, tc, acc, n0, wm, wn, lane, t, wbuf);
 }
 

@@ -60,6 +60,21 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
                                hipStream_t stream);
+// tensor-scaled FP8
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
+hipError_t launch_seg_amax(const void* src, int64_t seg_elems, int n_seg,
+                           uint32_t* amax_bits, hipStream_t stream);
+hipError_t launch_tensor_quant(const void* src, int64_t seg_elems, int n_seg,
+                               const uint32_t* amax_bits, uint8_t* codes,
+                               float* scales, hipStream_t stream);
+size_t mlp_fwd_fp8t_ws_bytes(int E, int H, int F, int64_t rows, bool need_a);
+hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
+                               const void* x_perm, const void* w_gu,
+                               const void* w_dn, const float* w_perm,
+                               const int32_t* offsets, void* z_perm,
+                               void* h1_save, void* a_save, void* ws,
+                               hipStream_t stream);
+
 // router projection (float64 accumulation in ascending h) and backward
 hipError_t launch_router_logits(const void* x, const void* w_r,
                                 const float* bias, int64_t T, int H, int E,

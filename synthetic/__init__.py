@@ -42,7 +42,7 @@ class MoEConfig:
     F: int          # expert FFN size
     E: int          # experts
     k: int          # experts per token
-    mode: str       # "bf16" or "mxfp8"
+    mode: str       # "bf16", "mxfp8" or "fp8t" (tensor-scaled E4M3)
     backward: bool  # the workload includes the backward pass
     zipf: float     # Zipf exponent of the per-expert router bias (0 = none)
     renormalize: bool = True
@@ -82,6 +82,11 @@ CONFIGS: Dict[str, MoEConfig] = {
         "mixtral_mxfp8_bwd", T=8192, H=4096, F=14336, E=8, k=2, mode="mxfp8",
         backward=True, zipf=0.0,
         description="Mixtral-8x7B-shaped layer fwd + bwd, MXFP8, dY ~ N(0,1)"),
+    "mixtral_fp8t": MoEConfig(
+        "mixtral_fp8t", T=8192, H=4096, F=14336, E=8, k=2, mode="fp8t",
+        backward=False, zipf=0.0,
+        description="Mixtral-8x7B-shaped layer fwd, E4M3 with one float32 "
+                    "scale per tensor"),
     "qwen3_long": MoEConfig(
         "qwen3_long", T=32768, H=2048, F=768, E=128, k=8, mode="bf16",
         backward=True, zipf=1.2,
