@@ -44,6 +44,11 @@ def parse():
                     help="mixtral | qwen3 | mixtral_mxfp8 | "
                          "mixtral_mxfp8_bwd | qwen3_long | tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the passes after the timed region (flushed "
+                         "HBM timing, per-expert loop, router, pre-quantised "
+                         "weights): profiler counter runs see the timed "
+                         "step's launches only")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0 = auto)")
     ap.add_argument("--write-traffic", nargs=4, metavar="DB",
@@ -63,6 +68,8 @@ KERNEL_SYMBOL = {
     "gemm_down_bf16": "grouped_gemm_kernel<0, 0, 0, 0, 0>",
     "gemm_gate_up_swiglu_mxfp8": "grouped_gemm_kernel<1, 0, 0, 0, 3>",
     "gemm_down_mxfp8": "grouped_gemm_kernel<1, 0, 0, 0, 0>",
+    "gemm_gate_up_swiglu_fp8t": "grouped_gemm_kernel<2, 0, 0, 0, 1>",
+    "gemm_down_fp8t": "grouped_gemm_kernel<2, 0, 0, 0, 0>",
 }
 
 
@@ -358,7 +365,8 @@ KERNEL_BYTES = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_gemm.json")
 GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_grouped_router_amd",
                              "csrc", f) for f in
-                ("grouped_gemm.hpp", "gemm_bf16.hip", "gemm_mxfp8.hip")]
+                ("grouped_gemm.hpp", "gemm_bf16.hip", "gemm_mxfp8.hip",
+                 "gemm_fp8t.hip")]
 
 
 def sources_digest():
@@ -707,7 +715,7 @@ def main():
                       "rocprofv3 --pmc FETCH_SIZE | WRITE_SIZE "
                       "--kernel-include-regex grouped_gemm -- python3 "
                       f"bench.py --workload {args.workload} --steps 1 "
-                      "--warmup 0 --no-cpu-baseline")
+                      "--warmup 0 --no-cpu-baseline --no-extras")
         return
     import torch
     import mixture_experts_grouped_router_amd as m
@@ -770,15 +778,16 @@ def main():
     if status != 0:
         raise RuntimeError(f"device status {status}")
     peak_mem = torch.cuda.max_memory_allocated()
-    extras = {"hbm_flushed": hbm_extras(m, layer, cfg, st),
-              "peak_device_mem_GiB": round(peak_mem / 2**30, 2)}
-    if cfg.mode == "mxfp8" and not cfg.backward:
-        extras["prequantised_weights"] = prequantised_step(m, layer, cfg, st,
-                                                           max(1, K // 2))
-    if cfg.mode == "bf16" and not cfg.backward:
-        extras["expert_loop"] = expert_loop_extra(m, layer, cfg, st,
-                                                  max(2, K // 4))
-    extras["router"] = router_extra(m, layer, cfg, d, st, max(2, K // 2))
+    extras = {"peak_device_mem_GiB": round(peak_mem / 2**30, 2)}
+    if not args.no_extras:
+        extras["hbm_flushed"] = hbm_extras(m, layer, cfg, st)
+        if cfg.mode == "mxfp8" and not cfg.backward:
+            extras["prequantised_weights"] = prequantised_step(
+                m, layer, cfg, st, max(1, K // 2))
+        if cfg.mode == "bf16" and not cfg.backward:
+            extras["expert_loop"] = expert_loop_extra(m, layer, cfg, st,
+                                                      max(2, K // 4))
+        extras["router"] = router_extra(m, layer, cfg, d, st, max(2, K // 2))
 
     flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
     tflops = flop / (ms_step * 1e-3) / 1e12
