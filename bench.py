@@ -62,14 +62,17 @@ def parse():
     return ap.parse_args()
 
 
-# library kernel name -> template instantiation in profiler kernel names
+# library kernel name -> template instantiations in profiler kernel names
+# (the bf16 forward runs the eight-wave kernel for the down GEMM, and for
+# gate/up up to H = 2048)
 KERNEL_SYMBOL = {
-    "gemm_gate_up_swiglu_bf16": "grouped_gemm_kernel<0, 0, 0, 0, 1>",
-    "gemm_down_bf16": "grouped_gemm_kernel<0, 0, 0, 0, 0>",
-    "gemm_gate_up_swiglu_mxfp8": "grouped_gemm_kernel<1, 0, 0, 0, 3>",
-    "gemm_down_mxfp8": "grouped_gemm_kernel<1, 0, 0, 0, 0>",
-    "gemm_gate_up_swiglu_fp8t": "grouped_gemm_kernel<2, 0, 0, 0, 1>",
-    "gemm_down_fp8t": "grouped_gemm_kernel<2, 0, 0, 0, 0>",
+    "gemm_gate_up_swiglu_bf16": ("grouped_gemm_kernel<0, 0, 0, 0, 1>",
+                                 "grouped_gemm_w8_kernel<1>"),
+    "gemm_down_bf16": ("grouped_gemm_w8_kernel<0>",),
+    "gemm_gate_up_swiglu_mxfp8": ("grouped_gemm_kernel<1, 0, 0, 0, 3>",),
+    "gemm_down_mxfp8": ("grouped_gemm_kernel<1, 0, 0, 0, 0>",),
+    "gemm_gate_up_swiglu_fp8t": ("grouped_gemm_kernel<2, 0, 0, 0, 1>",),
+    "gemm_down_fp8t": ("grouped_gemm_kernel<2, 0, 0, 0, 0>",),
 }
 
 
@@ -105,9 +108,9 @@ def write_traffic(workload, dbs, cmd):
     dig = sources_digest()
     recs = [r for r in data.get("records", [])
             if r.get("workload") != workload]
-    for kname, sym in KERNEL_SYMBOL.items():
-        fk = [v for k, v in fetch.items() if sym in k]
-        wk = [v for k, v in write.items() if sym in k]
+    for kname, syms in KERNEL_SYMBOL.items():
+        fk = [v for k, v in fetch.items() if any(s in k for s in syms)]
+        wk = [v for k, v in write.items() if any(s in k for s in syms)]
         if not fk or not wk:
             continue
         recs.append({
@@ -365,8 +368,8 @@ KERNEL_BYTES = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_gemm.json")
 GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_grouped_router_amd",
                              "csrc", f) for f in
-                ("grouped_gemm.hpp", "gemm_bf16.hip", "gemm_mxfp8.hip",
-                 "gemm_fp8t.hip")]
+                ("grouped_gemm.hpp", "grouped_gemm_w8.hpp", "gemm_bf16.hip",
+                 "gemm_mxfp8.hip", "gemm_fp8t.hip")]
 
 
 def sources_digest():

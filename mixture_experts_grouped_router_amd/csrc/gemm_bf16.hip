@@ -8,8 +8,10 @@
 // grouped MLP), then the grouped down GEMM.  Backward: the counterpart GEMMs
 // (dgrad of both projections, the first with the SwiGLU backward and the
 // routing-weight gradient in its epilogue; wgrad of both projections with K
-// running over each expert's tokens).  Kernel: grouped_gemm.hpp.
+// running over each expert's tokens).  Kernels: grouped_gemm.hpp, and for
+// the forward GEMMs grouped_gemm_w8.hpp (eight waves per tile).
 #include "grouped_gemm.hpp"
+#include "grouped_gemm_w8.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -152,8 +154,16 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p1.c2 = static_cast<uint16_t*>(h1_save);
   p1.w = w_perm;
   p1.rows = rows;
-  err = launch<P_BF16, KC, KC, RAGGED_M, EPI_SWIGLU>(
-      "gemm_gate_up_swiglu_bf16", p1, ragged_m_grid(rows, E, tn1), stream);
+  // Eight waves per tile hide more latency but read 50% more LDS per MFMA;
+  // on the gate/up GEMM with a long K loop over large expert weights the
+  // extra power lowers the clock by more than the latency gained (H = 4096:
+  // 3% slower), so four waves run it there.
+  if (H <= kW8MaxGateUpK)
+    err = launch_w8<EPI_SWIGLU>("gemm_gate_up_swiglu_bf16", p1,
+                                ragged_m_grid(rows, E, tn1), stream);
+  else
+    err = launch<P_BF16, KC, KC, RAGGED_M, EPI_SWIGLU>(
+        "gemm_gate_up_swiglu_bf16", p1, ragged_m_grid(rows, E, tn1), stream);
   if (err != hipSuccess) return err;
 
   Params p2{};
@@ -172,8 +182,8 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p2.c = static_cast<uint16_t*>(z_perm);
   p2.ldc = H;
   p2.rows = rows;
-  return launch<P_BF16, KC, KC, RAGGED_M, EPI_STORE>("gemm_down_bf16", p2, ragged_m_grid(rows, E, tn2),
-                                             stream);
+  return launch_w8<EPI_STORE>("gemm_down_bf16", p2,
+                             ragged_m_grid(rows, E, tn2), stream);
 }
 
 size_t mlp_bwd_bf16_ws_bytes(int E, int H, int F, int64_t rows) {

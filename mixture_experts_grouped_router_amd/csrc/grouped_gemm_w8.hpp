@@ -1,0 +1,386 @@
+// The bf16 forward grouped GEMM with eight waves per 256 x 256 tile, two per
+// SIMD: while one wave of a SIMD waits (its load queue, an LDS read, the
+// barrier) the other issues MFMAs.  Tile, LDS stages, direct loads, tile
+// order and arithmetic are those of grouped_gemm.hpp (the results are bit
+// for bit the same); the wave layout and the epilogues' staging differ.
+// K-contiguous operands, ragged M, EPI_STORE and EPI_SWIGLU.
+//
+// Wave shapes: EPI_STORE, 128 rows x 64 columns (a 2 x 4 wave grid);
+// EPI_SWIGLU, 64 rows x 128 B rows (4 x 2), i.e. gate and up of 64 f, so
+// each wave stores whole 128-byte lines of A and of the (g, u) save.
+#pragma once
+
+#include "grouped_gemm.hpp"
+
+namespace moe {
+namespace gg {
+
+constexpr int kThreads8 = 512;
+// largest K (= H) for which the gate/up GEMM runs with eight waves
+constexpr int kW8MaxGateUpK = 2048;
+
+template <int EPI>
+struct Shape8 {
+  static constexpr int MI = EPI == EPI_SWIGLU ? 2 : 4;  // 32-row A blocks
+  static constexpr int NJ = 8 / MI;                     // 32-row B blocks
+  static constexpr int WN = 8 / (8 / MI);               // waves along N
+};
+
+// Direct loads with eight waves: wave w, instruction j (of 4) fills KiB
+// 8 j + w of the stage = tile rows 32 (2 j + w / 4) + 8 (w % 4) + lane / 8,
+// the same bytes as the four-wave loader puts there.
+template <int EPI, bool IS_B>
+struct KcDirect8 {
+  const char* base;
+  uint32_t rec;
+  int64_t ld;
+  int q;             // row inside the 32-row block: 8 (w % 4) + lane / 8
+  int cl;            // the lane's logical chunk
+  int r0;
+  int n0, F, N;
+  uint32_t off[4];
+  __device__ __forceinline__ int row(int blk) const {
+    if constexpr (!IS_B) {
+      return r0 + 32 * blk + q;
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      const int f = min(n0 + (blk >> 1) * 32 + q, F - 1);
+      return (blk & 1) ? F + f : f;
+    } else {
+      return min(n0 + 32 * blk + q, N - 1);
+    }
+  }
+  __device__ __forceinline__ void init(int wave) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      off[j] = (uint32_t)row(2 * j + (wave >> 2)) * (uint32_t)ld +
+               (uint32_t)(cl * 16);
+  }
+  __device__ __forceinline__ void issue(char* lds_tile, uint32_t kbyte,
+                                        bool real, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + kbyte), (short)0, (int)(real ? rec - kbyte : 0u),
+        kBufFlags);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      MOE_LDS void* dst = (MOE_LDS void*)(lds_tile + (8 * j + wave) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off[j], 0, 0, 0);
+    }
+  }
+};
+
+// Fragments of one 16-wide K slice: MI A blocks and NJ B blocks (six reads).
+template <int MI, int NJ>
+struct Frags8 {
+  bf16x8_t a[MI], b[NJ];
+  static __device__ __forceinline__ bf16x8_t at(const char* s, int off) {
+    return *reinterpret_cast<const bf16x8_t*>(s + off);
+  }
+  __device__ __forceinline__ void load(const char* sa, const char* sb, int kk,
+                                       int wm, int wn, int lane) {
+    const int o = frag_off(lane & 31, kk * 2 + (lane >> 5));
+    const char* pa = sa + wm * (MI * 32 * kRowBytes) + o;
+    const char* pb = sb + wn * (NJ * 32 * kRowBytes) + o;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) a[i] = at(pa, i * 32 * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b[j] = at(pb, j * 32 * kRowBytes);
+  }
+};
+
+// The slice's eight MFMAs (HALF 0 / 1: those of the first / second half of
+// the A blocks; 2: all)
+template <int HALF, int MI, int NJ>
+__device__ __forceinline__ void mfma_bf16_w8(const Frags8<MI, NJ>& f,
+                                             f32x16_t (&acc)[MI][NJ]) {
+  constexpr int i0 = HALF == 1 ? MI / 2 : 0;
+  constexpr int i1 = HALF == 0 ? MI / 2 : MI;
+#pragma unroll
+  for (int i = i0; i < i1; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j],
+                                                          acc[i][j], 0, 0, 0);
+}
+
+// Staging with 128-byte rows: 16-byte chunk c of row r at chunk c ^ (r & 7).
+__device__ __forceinline__ int stg8(int r, int c) {
+  return r * 128 + ((c ^ (r & 7)) << 4);
+}
+
+// EPI_STORE of a wave's 128 x 64 block (acc[i][j][r]: row acc_row(i, r),
+// column 32 j + lane % 32) through its 16 KiB of LDS: 128-byte rows of 64
+// bf16; on readback lane l takes chunk l % 8 of row 8 q + l / 8.
+__device__ __forceinline__ void epilogue_w8_store(const Params& p,
+                                                  const TileCoord& tc,
+                                                  f32x16_t (&acc)[4][2],
+                                                  int n0, int wm, int wn,
+                                                  int lane, char* wbuf) {
+  const int colw = lane & 31;
+  const int mw = tc.m0 + wm * 128;
+  // Accumulator row acc_row(i, r) = 32 i + 8 (r / 4) + lo with lo =
+  // 4 (lane / 32) + r % 4, so its swizzle depends on lo alone: a staging
+  // address is one of a few per-lane bases plus a constant.
+  int bb[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r3 = 0; r3 < 4; ++r3) {
+      const int lo = 4 * (lane >> 5) + r3;
+      const int c = 4 * j + (colw >> 3);
+      bb[j][r3] = lo * 128 + ((c ^ lo) << 4) + (colw & 7) * 2;
+    }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        *reinterpret_cast<uint16_t*>(wbuf + bb[j][r & 3] +
+                                     (32 * i + 8 * (r >> 2)) * 128) =
+            (uint16_t)f32_to_bf16(acc[i][j][r]);
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
+  const int ch = lane & 7;
+  const int col = n0 + wn * 64 + 8 * ch;   // N % 64 == 0
+#pragma unroll
+  for (int qb = 0; qb < 16; qb += 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      v[q] = *reinterpret_cast<const uint4*>(
+          wbuf + stg8(8 * (qb + q) + (lane >> 3), ch));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int mrow = mw + 8 * (qb + q) + (lane >> 3);
+      if (col < p.N && mrow < tc.seg_len)
+        *reinterpret_cast<uint4*>(p.c + (tc.seg0 + mrow) * p.ldc + col) = v[q];
+    }
+  }
+}
+
+// EPI_SWIGLU of a wave's 64 rows x 64 f: acc[i][2 jj] is g and
+// acc[i][2 jj + 1] is u of f = n0 + 64 wn + 32 jj + lane % 32 at row
+// acc_row(i, r).  Staging in 256-byte rows (stg_off): (g, u) as bf16 for the
+// save, then silu(g) * u as float32; the routing weight and the bf16
+// rounding of A happen per row on readback, as in the four-wave epilogue.
+__device__ __forceinline__ void epilogue_w8_swiglu(const Params& p,
+                                                   const TileCoord& tc,
+                                                   f32x16_t (&acc)[2][4],
+                                                   int n0, int wm, int wn,
+                                                   int lane, int wave,
+                                                   char* wbuf) {
+  const int colw = lane & 31;
+  const int mw = tc.m0 + wm * 64;
+  // routing weights of the wave's 64 rows, loaded before any store
+  __shared__ float wrow_all[kThreads8 / 64][64];
+  float* wrow = wrow_all[wave];
+  wrow[lane] = p.w ? p.w[tc.seg0 + min(mw + lane, tc.seg_len - 1)] : 1.0f;
+  const int64_t ld1 = 2 * (int64_t)p.F;
+  const int f0 = n0 + 64 * wn;
+  const bool fvalid = f0 < p.F;   // F % 64 == 0: whole runs
+  auto silu_mul = [&]() {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float g = acc[i][2 * jj][r];
+          acc[i][2 * jj][r] = (g * fast_sigmoid(g)) * acc[i][2 * jj + 1][r];
+        }
+  };
+  if (p.c2) {
+    // row r: g of the wave's 64 f in columns 0..63, u in 64..127; on
+    // readback lane l takes chunk l % 16 of row 4 q + l / 16
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          stage_bf16(wbuf, acc_row(i, r, lane), jj * 32 + colw,
+                     acc[i][2 * jj][r]);
+          stage_bf16(wbuf, acc_row(i, r, lane), 64 + jj * 32 + colw,
+                     acc[i][2 * jj + 1][r]);
+        }
+    silu_mul();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
+    const int ch = lane & 15;
+    const int coff = (ch >> 3) * p.F + f0 + 8 * (ch & 7);
+#pragma unroll
+    for (int qb = 0; qb < 16; qb += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[q] = stage_chunk(wbuf, 4 * (qb + q) + (lane >> 4), ch);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int mrow = mw + 4 * (qb + q) + (lane >> 4);
+        if (fvalid && mrow < tc.seg_len)
+          *reinterpret_cast<uint4*>(p.c2 + (tc.seg0 + mrow) * ld1 + coff) =
+              v[q];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // readback done before reuse
+  } else {
+    silu_mul();
+  }
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        stage_f32(wbuf, acc_row(i, r, lane), jj * 32 + colw,
+                  acc[i][2 * jj][r]);
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
+  // lane l: rows 8 q + l / 8, f values 8 (l % 8) .. + 7
+  const int c8 = lane & 7;
+  const int f = f0 + 8 * c8;
+#pragma unroll
+  for (int qb = 0; qb < 8; qb += 4) {
+    uint4 c0[4], c1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = 8 * (qb + q) + (lane >> 3);
+      c0[q] = stage_chunk(wbuf, lr, 2 * c8);
+      c1[q] = stage_chunk(wbuf, lr, 2 * c8 + 1);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = 8 * (qb + q) + (lane >> 3);
+      const int mrow = mw + lr;
+      const float wr = wrow[lr];
+      if (fvalid && mrow < tc.seg_len) {
+        const float v[8] = {
+            __uint_as_float(c0[q].x) * wr, __uint_as_float(c0[q].y) * wr,
+            __uint_as_float(c0[q].z) * wr, __uint_as_float(c0[q].w) * wr,
+            __uint_as_float(c1[q].x) * wr, __uint_as_float(c1[q].y) * wr,
+            __uint_as_float(c1[q].z) * wr, __uint_as_float(c1[q].w) * wr};
+        *reinterpret_cast<uint4*>(p.c + (tc.seg0 + mrow) * p.ldc + f) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      }
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
+  static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU, "forward epilogues");
+  using S = Shape8<EPI>;
+  constexpr int MI = S::MI, NJ = S::NJ;
+  constexpr int kSl = 4;         // 16-wide K slices per 64-wide step
+  constexpr int kStepK = 64;
+  __shared__ __attribute__((aligned(1024))) char sA0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sB0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sA1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sB1[kTileBytes];
+  TileCoord tc;
+  if (!decode_tile<RAGGED_M>(p, tc)) return;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave / S::WN;
+  const int wn = wave % S::WN;
+  const int n0 = EPI == EPI_SWIGLU ? tc.nt * (BN / 2) : tc.nt * BN;
+
+  KcDirect8<EPI, false> da;
+  KcDirect8<EPI, true> db;
+  const int q = 8 * (wave & 3) + (lane >> 3);
+  const int cl = (lane & 7) ^ swz32(q);
+  // rows past the expert's last read as zeros (buffer descriptor range)
+  da.base = p.a + (int64_t)tc.seg0 * p.lda;
+  da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda;
+  da.ld = p.lda;
+  da.q = q;
+  da.cl = cl;
+  da.r0 = tc.m0;
+  da.init(wave);
+  db.base = p.b + (int64_t)tc.e * p.b_es;
+  db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb;
+  db.ld = p.ldb;
+  db.q = q;
+  db.cl = cl;
+  db.n0 = n0;
+  db.F = p.F;
+  db.N = p.N;
+  db.init(wave);
+
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16_t{};
+
+  const int nk = (p.K + kStepK - 1) / kStepK;
+  // 6 LDS reads and 8 MFMAs per slice; the next step's A loads go out one
+  // per MFMA over the first slice, its B loads over the second
+  auto slice_sched = [&](int kk) {
+    if (kk <= 1) sched_vmem_reads_mfma<4, 6, 8, 1>();
+    else sched_reads_mfma<6, 8>();
+  };
+
+  // Two K steps per loop trip, one per LDS stage, as in the four-wave
+  // kernel; fragment reads run one slice ahead of the MFMAs and the barrier
+  // that publishes the next stage sits inside the last slice's MFMAs.
+  const int nk2 = (nk + 1) & ~1;
+  if (nk > 0) {
+    da.issue(sA0, 0, true, wave);
+    db.issue(sB0, 0, true, wave);
+  }
+  __syncthreads();
+  Frags8<MI, NJ> cur, nxt;
+  cur.load(sA0, sB0, 0, wm, wn, lane);
+
+  auto step = [&](const char* sa, const char* sb, char* na, char* nb, int kn) {
+    // compute the step in (sa, sb); step kn loads into (na, nb) (a step
+    // past nk reads zeros and is never computed)
+    const bool real = kn < nk;
+#pragma unroll
+    for (int kk = 0; kk < kSl - 1; ++kk) {
+      if (kk == 0) da.issue(na, (uint32_t)kn * kRowBytes, real, wave);
+      if (kk == 1) db.issue(nb, (uint32_t)kn * kRowBytes, real, wave);
+      nxt.load(sa, sb, kk + 1, wm, wn, lane);
+      mfma_bf16_w8<2>(cur, acc);
+      cur = nxt;
+      slice_sched(kk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mfma_bf16_w8<0>(cur, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    nxt.load(na, nb, 0, wm, wn, lane);
+    mfma_bf16_w8<1>(cur, acc);
+    cur = nxt;
+    sched_reads_mfma<6, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int kt = 0; kt < nk2; kt += 2) {
+    step(sA0, sB0, sA1, sB1, kt + 1);
+    step(sA1, sB1, sA0, sB0, kt + 2);
+  }
+
+  // every wave is past its last read of the stages (and every direct load
+  // has landed) before they become epilogue staging: 16 KiB per wave
+  __syncthreads();
+  char* wbuf = (wave < 2 ? sA0 : wave < 4 ? sB0 : wave < 6 ? sA1 : sB1) +
+               (wave & 1) * (kTileBytes / 2);
+  if constexpr (EPI == EPI_STORE)
+    epilogue_w8_store(p, tc, acc, n0, wm, wn, lane, wbuf);
+  else
+    epilogue_w8_swiglu(p, tc, acc, n0, wm, wn, lane, wave, wbuf);
+}
+
+template <int EPI>
+hipError_t launch_w8(const char* name, const Params& p, int grid,
+                     hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  KernelScope ks(name, stream);
+  hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI>), dim3(grid),
+                     dim3(kThreads8), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace gg
+}  // namespace moe

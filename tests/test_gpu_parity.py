@@ -322,6 +322,7 @@ MLP_CASES = [
     (700, 192, 320, 5, 2, 1.2),     # ragged M, F tail (320 = 2.5 x 128)
     (900, 256, 128, 16, 4, 1.2),    # many experts, some empty
     (64, 64, 64, 4, 1, 0.0),        # tiles larger than the problem
+    (300, 2112, 192, 4, 2, 1.2),    # H > 2048: the four-wave gate/up GEMM
 ]
 
 
