@@ -638,6 +638,78 @@ def expert_loop_extra(m, layer, cfg, st, K):
                     "vs moe_grouped_mlp_fwd, wall ms per call"}
 
 
+def ep_share_extra(m, layer, cfg, st, K, G=8):
+    """One GPU's share of an expert-parallel layer over G GPUs: experts
+    [g E/G, (g+1) E/G) live on GPU g and every GPU routes T tokens like this
+    workload, so GPU g receives G times the rows its experts get here (the
+    other GPUs' tokens are drawn alike; their rows are stood in for by G
+    copies of the local ones).  The grouped MLP forward on the heaviest
+    GPU's share (it bounds the step), timed with HIP events; the all-to-all
+    exchanges around it are not run (one GPU)."""
+    import torch
+    E, H, F = cfg.E, cfg.H, cfg.F
+    if E % G:
+        return None
+    for _, fn in layer.stages():     # valid x_perm / offsets / w_perm
+        fn(st)
+    torch.cuda.synchronize()
+    off = layer.offsets.cpu().numpy().astype(np.int64)
+    el = E // G
+    loads = [int(off[(g + 1) * el] - off[g * el]) for g in range(G)]
+    g = int(np.argmax(loads))
+    e0 = g * el
+    cnt = np.diff(off[e0:e0 + el + 1]) * G
+    offl = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+    rows = int(offl[-1])
+    dev = layer.x_perm.device
+    x = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    wp = torch.empty(rows, dtype=torch.float32, device=dev)
+    for i in range(el):
+        a, b = int(off[e0 + i]), int(off[e0 + i + 1])
+        x[offl[i]:offl[i + 1]] = layer.x_perm[a:b].repeat(G, 1)
+        wp[offl[i]:offl[i + 1]] = layer.w_perm[a:b].repeat(G)
+    z = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    offs = torch.from_numpy(offl).to(dev)
+    fa = m._FwdArgs()
+    fa.E, fa.H, fa.F, fa.rows = el, H, F, rows
+    fa.precision = m.PREC_BF16
+    fa.x_perm, fa.x_perm_scale = x.data_ptr(), None
+    fa.w_gu = layer.w_gu[e0:e0 + el].data_ptr()
+    fa.w_dn = layer.w_dn[e0:e0 + el].data_ptr()
+    fa.w_perm, fa.offsets, fa.z_perm = wp.data_ptr(), offs.data_ptr(), \
+        z.data_ptr()
+    fa.h1_save, fa.a_save = None, None
+    n = ctypes.c_size_t()
+    m._check(layer.lib.moe_grouped_mlp_fwd_workspace_size(ctypes.byref(fa),
+                                                          ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    fa.ws, fa.ws_bytes = ws.data_ptr(), ws.numel()
+
+    def run():
+        m._check(layer.lib.moe_grouped_mlp_fwd(layer.ctx, ctypes.byref(fa),
+                                               st))
+
+    run()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(K):
+        run()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    tf = 6.0 * rows * H * F / (ms * 1e-3) / 1e12
+    return {"gpus": G, "gpu": g, "experts": [e0, e0 + el],
+            "rows": rows, "rows_per_gpu": [r * G for r in loads],
+            "grouped_mlp_ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+            "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4),
+            "what": "grouped MLP forward (bf16) on the heaviest GPU's "
+                    "experts of an expert-parallel split over 8 GPUs, "
+                    "8x this workload's rows for them; exchanges not run"}
+
+
 def router_extra(m, layer, cfg, d, st, K):
     """Router projection (and, with a backward pass, the router backward)
     on the workload's tokens, timed with HIP events on the library stream;
@@ -770,6 +842,7 @@ def main():
     per_stage = {name: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1])
                                       for s in range(K)]))
                  for i, (name, _) in enumerate(stages)}
+    step_ms = [ev[s][0][0].elapsed_time(ev[s][-1][1]) for s in range(K)]
     m.set_kernel_timing(False)
     ktimes = {}      # name -> (launches, average ms, ms per step)
     for name in KERNELS:
@@ -790,6 +863,8 @@ def main():
         if cfg.mode == "bf16" and not cfg.backward:
             extras["expert_loop"] = expert_loop_extra(m, layer, cfg, st,
                                                       max(2, K // 4))
+            extras["ep_share"] = ep_share_extra(m, layer, cfg, st,
+                                                max(2, K // 4))
         extras["router"] = router_extra(m, layer, cfg, d, st, max(2, K // 2))
 
     flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
@@ -869,6 +944,9 @@ def main():
                    "k": cfg.k, "mode": cfg.mode,
                    "passes": "fwd+bwd" if cfg.backward else "fwd",
                    "parallelism": "single GPU"},
+        "step_ms_spread": {"min": round(min(step_ms), 4),
+                           "median": round(float(np.median(step_ms)), 4),
+                           "max": round(max(step_ms), 4)},
         "tokens_per_s": round(tokens_s, 1),
         "mfma_frac_step": round(tflops / peak, 4),
         "roofline": roof,
