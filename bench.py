@@ -710,6 +710,49 @@ def ep_share_extra(m, layer, cfg, st, K, G=8):
                     "8x this workload's rows for them; exchanges not run"}
 
 
+def graph_extra(layer, st, K):
+    """The step captured once in a HIP graph and replayed, against the same
+    stages launched eagerly: what launch overhead costs at this size."""
+    import torch
+    stages = layer.stages()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _, fn in stages:
+            fn(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for _, fn in stages:
+            fn(cs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(run):
+        run()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(K):
+            run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K
+
+    def eager():
+        for _, fn in stages:
+            fn(st)
+
+    t_graph, t_eager = timed(g.replay), timed(eager)
+    return {"graph_ms_per_step": round(t_graph, 4),
+            "eager_ms_per_step": round(t_eager, 4),
+            "what": "the whole step captured in one HIP graph and replayed "
+                    "vs launched call by call (HIP events, same stream)"}
+
+
 def router_extra(m, layer, cfg, d, st, K):
     """Router projection (and, with a backward pass, the router backward)
     on the workload's tokens, timed with HIP events on the library stream;
@@ -866,6 +909,7 @@ def main():
             extras["ep_share"] = ep_share_extra(m, layer, cfg, st,
                                                 max(2, K // 4))
         extras["router"] = router_extra(m, layer, cfg, d, st, max(2, K // 2))
+        extras["graph"] = graph_extra(layer, st, max(2, K // 2))
 
     flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
     tflops = flop / (ms_step * 1e-3) / 1e12
