@@ -551,7 +551,7 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
   } else if (!mx) {
     e = moe::launch_mlp_fwd_bf16(a->E, a->H, a->F, a->rows, a->x_perm, a->w_gu,
                                  a->w_dn, a->w_perm, a->offsets, a->z_perm,
-                                 a->h1_save, a->a_save, a->ws,
+                                 a->h1_save, a->a_save, a->ws, ctx->cu_count,
                                  as_stream(stream));
   } else {
     const bool xq = a->x_perm_scale != nullptr;

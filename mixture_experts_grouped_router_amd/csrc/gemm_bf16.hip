@@ -22,9 +22,11 @@ namespace gg {
 // offsets of segments padded to multiples of P.
 __global__ __launch_bounds__(1024) void tile_table_kernel(
     const int32_t* __restrict__ offsets, int E, int unit, int tn,
-    int32_t* __restrict__ tile_start) {
+    int32_t* __restrict__ tile_start, uint32_t* __restrict__ zero,
+    int nzero) {
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
+  for (int i = e; i < nzero; i += 1024) zero[i] = 0u;
   const int lane = e & 63, wid = e >> 6;
   int32_t v = 0;
   if (e < E) v = ((offsets[e + 1] - offsets[e] + unit - 1) / unit) * tn;
@@ -81,10 +83,11 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(
 }  // namespace
 
 hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
-                             int32_t* tile_start, hipStream_t stream) {
+                             int32_t* tile_start, hipStream_t stream,
+                             uint32_t* zero, int nzero) {
   KernelScope ks("tile_table", stream);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
-                     offsets, E, BM, tn, tile_start);
+                     offsets, E, BM, tn, tile_start, zero, nzero);
   return hipGetLastError();
 }
 
@@ -100,7 +103,7 @@ hipError_t launch_padded_offsets(const int32_t* offsets, int E, int pad,
                                  int32_t* poff, hipStream_t stream) {
   KernelScope ks("padded_offsets", stream);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
-                     offsets, E, pad, pad, poff);
+                     offsets, E, pad, pad, poff, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -108,9 +111,30 @@ hipError_t launch_padded_offsets(const int32_t* offsets, int E, int pad,
 
 using namespace gg;
 
+namespace {
+// Split slots per XCD of the eight-wave forward GEMMs (the gate/up GEMM
+// runs with eight waves up to H = kW8MaxGateUpK).
+int fwd_split_slots_x(int E, int H, int F, int64_t rows) {
+  const int64_t mt = rows / BM + E;
+  const int tn1 = (F + BN / 2 - 1) / (BN / 2);
+  const int tn2 = (H + BN - 1) / BN;
+  int s = split_slots_x(mt * tn2, F / 64);
+  if (H <= kW8MaxGateUpK) s = std::max(s, split_slots_x(mt * tn1, H / 64));
+  return s;
+}
+size_t split_part_bytes(int slots_x) {
+  return align256((size_t)kXcds * slots_x * BM * BN * sizeof(float));
+}
+size_t split_cnt_bytes(int slots_x) {
+  return align256((size_t)kXcds * slots_x * sizeof(uint32_t));
+}
+}  // namespace
+
 size_t mlp_fwd_bf16_ws_bytes(int E, int H, int F, int64_t rows, bool need_a) {
   size_t b = 2 * align256((size_t)(E + 1) * sizeof(int32_t));
   if (need_a) b += align256((size_t)rows * F * 2);
+  const int sx = fwd_split_slots_x(E, H, F, rows);
+  b += split_part_bytes(sx) + split_cnt_bytes(sx);
   return b;
 }
 
@@ -119,21 +143,38 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
                                const void* w_dn, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
-                               hipStream_t stream) {
+                               int cu_count, hipStream_t stream) {
   char* wp = static_cast<char*>(ws);
   int32_t* ts1 = reinterpret_cast<int32_t*>(wp);
   wp += align256((size_t)(E + 1) * sizeof(int32_t));
   int32_t* ts2 = reinterpret_cast<int32_t*>(wp);
   wp += align256((size_t)(E + 1) * sizeof(int32_t));
   uint16_t* a_buf = static_cast<uint16_t*>(a_save);
-  if (!a_buf) a_buf = reinterpret_cast<uint16_t*>(wp);
+  if (!a_buf) {
+    a_buf = reinterpret_cast<uint16_t*>(wp);
+    wp += align256((size_t)rows * F * 2);
+  }
+  const int sx = fwd_split_slots_x(E, H, F, rows);
+  float* split_part = reinterpret_cast<float*>(wp);
+  wp += split_part_bytes(sx);
+  uint32_t* split_cnt = reinterpret_cast<uint32_t*>(wp);
   if (rows == 0) return hipSuccess;
 
   const int tn1 = (F + BN / 2 - 1) / (BN / 2);
   const int tn2 = (H + BN - 1) / BN;
-  hipError_t err = launch_tile_table(offsets, E, tn1, ts1, stream);
+  hipError_t err = launch_tile_table(offsets, E, tn1, ts1, stream, split_cnt,
+                                     kXcds * sx);
   if (err == hipSuccess) err = launch_tile_table(offsets, E, tn2, ts2, stream);
   if (err != hipSuccess) return err;
+  // the eight-wave GEMMs split the last, partly filled round of tiles
+  auto set_split = [&](Params& p) {
+    if (sx > 0) {
+      p.split_part = split_part;
+      p.split_cnt = split_cnt;
+      p.split_slots_x = sx;
+      p.cus_per_xcd = cu_count / kXcds;
+    }
+  };
 
   Params p1{};
   p1.a = static_cast<const char*>(x_perm);
@@ -158,10 +199,11 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   // on the gate/up GEMM with a long K loop over large expert weights the
   // extra power lowers the clock by more than the latency gained (H = 4096:
   // 3% slower), so four waves run it there.
-  if (H <= kW8MaxGateUpK)
+  if (H <= kW8MaxGateUpK) {
+    set_split(p1);
     err = launch_w8<EPI_SWIGLU>("gemm_gate_up_swiglu_bf16", p1,
-                                ragged_m_grid(rows, E, tn1), stream);
-  else
+                                ragged_m_grid_w8(rows, E, tn1, p1), stream);
+  } else
     err = launch<P_BF16, KC, KC, RAGGED_M, EPI_SWIGLU>(
         "gemm_gate_up_swiglu_bf16", p1, ragged_m_grid(rows, E, tn1), stream);
   if (err != hipSuccess) return err;
@@ -182,8 +224,9 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p2.c = static_cast<uint16_t*>(z_perm);
   p2.ldc = H;
   p2.rows = rows;
+  set_split(p2);
   return launch_w8<EPI_STORE>("gemm_down_bf16", p2,
-                             ragged_m_grid(rows, E, tn2), stream);
+                             ragged_m_grid_w8(rows, E, tn2, p2), stream);
 }
 
 size_t mlp_bwd_bf16_ws_bytes(int E, int H, int F, int64_t rows) {

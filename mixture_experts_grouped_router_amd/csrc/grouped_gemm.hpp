@@ -161,6 +161,14 @@ struct Params {
   // EPI_SWIGLU, nullable: amax of the bf16 A output (float32 bits,
   // atomic max)
   uint32_t* amax_out;
+  // Eight-wave forward kernel, nullable: float32 partial tiles and arrival
+  // counters (zero on entry) of the last, partly filled round of tiles,
+  // whose K range is split over several work-groups; split_slots_x slots
+  // and counters per XCD; cus_per_xcd work-groups make one round
+  float* split_part;
+  uint32_t* split_cnt;
+  int split_slots_x;
+  int cus_per_xcd;
 };
 
 // Swizzle of the 16-byte chunk c of LDS tile row r.  It depends only on
@@ -183,10 +191,33 @@ struct TileCoord {
   int nt;       // N tile index
 };
 
+// Coordinates of tile L of a RAGGED_M launch: tile_start[e] <= L <
+// tile_start[e+1] (experts without tiles have tile_start[e] ==
+// tile_start[e+1] and are never selected); groups of kGroupN N tiles, M
+// tiles fastest inside a group.
+__device__ __forceinline__ void ragged_m_tile(const Params& p, int L,
+                                              TileCoord& tc) {
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_start[mid] <= L) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int local = L - p.tile_start[e];
+  const int len = p.offsets[e + 1] - p.offsets[e];
+  const int mt_e = (len + BM - 1) / BM;
+  const int ng = local / (mt_e * kGroupN);
+  const int in_g = local - ng * mt_e * kGroupN;
+  tc.e = e;
+  tc.m0 = (in_g % mt_e) * BM;
+  tc.nt = ng * kGroupN + in_g / mt_e;
+  tc.seg0 = p.offsets[e];
+  tc.seg_len = len;
+}
+
 template <int G>
 __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
   const int b = blockIdx.x;
-  int e, local, mt_e;
   if constexpr (G == RAGGED_M) {
     // XCD x (= b mod 8) takes the x-th contiguous eighth of the tile list,
     // so an expert's tiles share one L2
@@ -196,17 +227,7 @@ __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
     if (idx >= per) return false;
     const int L = (b % kXcds) * per + idx;
     if (L >= total) return false;
-    // tile_start[e] <= L < tile_start[e+1]; experts without tiles have
-    // tile_start[e] == tile_start[e+1] and are never selected
-    int lo = 0, hi = p.E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tile_start[mid] <= L) lo = mid; else hi = mid;
-    }
-    e = lo;
-    local = L - p.tile_start[e];
-    const int len = p.offsets[e + 1] - p.offsets[e];
-    mt_e = (len + BM - 1) / BM;
+    ragged_m_tile(p, L, tc);
   } else {
     // a tile's cost is its expert's row count: tiles are taken largest
     // expert first and dealt round the XCDs in runs of kDealK, so every
@@ -216,18 +237,18 @@ __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
     const int L = ((idx / kDealK) * kXcds + x) * kDealK + idx % kDealK;
     if (L >= p.E * per_e) return false;
     const int rank = L / per_e;
-    e = p.order[rank];
-    local = L - rank * per_e;
-    mt_e = p.tiles_m;
+    const int e = p.order[rank];
+    const int local = L - rank * per_e;
+    const int mt_e = p.tiles_m;
+    // groups of kGroupN N-tiles, M tiles fastest inside a group
+    const int ng = local / (mt_e * kGroupN);
+    const int in_g = local - ng * mt_e * kGroupN;
+    tc.e = e;
+    tc.m0 = (in_g % mt_e) * BM;
+    tc.nt = ng * kGroupN + in_g / mt_e;
+    tc.seg0 = p.offsets[e];
+    tc.seg_len = p.offsets[e + 1] - tc.seg0;
   }
-  // groups of kGroupN N-tiles, M tiles fastest inside a group
-  const int ng = local / (mt_e * kGroupN);
-  const int in_g = local - ng * mt_e * kGroupN;
-  tc.e = e;
-  tc.m0 = (in_g % mt_e) * BM;
-  tc.nt = ng * kGroupN + in_g / mt_e;
-  tc.seg0 = p.offsets[e];
-  tc.seg_len = p.offsets[e + 1] - tc.seg0;
   return true;
 }
 
@@ -1193,7 +1214,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 // Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn.
 __global__ __launch_bounds__(1024) void tile_table_kernel(
     const int32_t* __restrict__ offsets, int E, int unit, int tn,
-    int32_t* __restrict__ tile_start);
+    int32_t* __restrict__ tile_start, uint32_t* __restrict__ zero,
+    int nzero);
 
 // Grid for a RAGGED_M launch: sum_e ceil(M_e / BM) <= rows / BM + E tiles
 // per N tile, rounded up to whole XCD rounds.
@@ -1219,8 +1241,10 @@ hipError_t launch(const char* name, const Params& p, int grid,
   return hipGetLastError();
 }
 
+// (also clears zero[0 .. nzero), e.g. the split tiles' arrival counters)
 hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
-                             int32_t* tile_start, hipStream_t stream);
+                             int32_t* tile_start, hipStream_t stream,
+                             uint32_t* zero = nullptr, int nzero = 0);
 // order[i] = the expert with the i-th most rows (equal counts: lower index
 // first); E <= 1024
 hipError_t launch_expert_order(const int32_t* offsets, int E, int32_t* order,

@@ -10,6 +10,8 @@
 // each wave stores whole 128-byte lines of A and of the (g, u) save.
 #pragma once
 
+#include <algorithm>
+
 #include "grouped_gemm.hpp"
 
 namespace moe {
@@ -18,6 +20,140 @@ namespace gg {
 constexpr int kThreads8 = 512;
 // largest K (= H) for which the gate/up GEMM runs with eight waves
 constexpr int kW8MaxGateUpK = 2048;
+
+// ---- The last round of tiles, split along K ---------------------------------
+// An XCD runs its contiguous run of tiles in rounds of one tile per CU.  A
+// run of R rounds plus `rem` more tiles takes R + 1 tile times even when rem
+// is small (a tile with a few valid rows costs as much as a full one: the
+// weight panel and the MFMAs are the same).  When rem is at most half a
+// round, each of those rem tiles is split into S <= kMaxSplit ranges of K
+// steps (rem * S <= CUs of the XCD), run by S work-groups that each write
+// their float32 partial tile to a slot of the workspace; the last to arrive
+// (an arrival counter per tile) adds the S partials in slot order and runs
+// the tile's epilogue.  The sums are fixed by the tile list alone, so the
+// result is deterministic.
+constexpr int kMaxSplit = 8;
+constexpr int kMaxSplitSlotsX = 32;   // slots (and counters) per XCD
+// Fewest K steps of a split work-group: the partial tile's round trip and
+// the cache write-back / invalidate of the hand-over cost tens of
+// microseconds per tile, which only long K ranges repay (the Mixtral-shaped
+// down GEMM, K = 14336, gains 7%; the Qwen3-shaped gate/up GEMM, K = 2048,
+// loses 3% with 16-step ranges).
+constexpr int kMinSplitSteps = 32;
+
+struct SplitRange {
+  int ks, ke;    // K steps [ks, ke) of this work-group
+  int S;         // work-groups sharing the tile (1: not split)
+  int slot0;     // first partial slot of the tile; this one is slot0 + s
+  int s;
+  int id;        // arrival counter
+};
+
+__device__ __forceinline__ bool decode_tile_w8(const Params& p, int nk,
+                                               TileCoord& tc,
+                                               SplitRange& sr) {
+  const int b = blockIdx.x;
+  const int total = p.tile_start[p.E];
+  const int per = (total + kXcds - 1) / kXcds;
+  const int x = b % kXcds, idx = b / kXcds;
+  const int cnt = min(per, total - x * per);   // tiles of this XCD
+  if (cnt <= 0) return false;
+  int S = 1, rem = 0;
+  const int C = p.cus_per_xcd;
+  if (p.split_part != nullptr && C > 0) {
+    rem = cnt % C;
+    if (rem > 0 && 2 * rem <= C) {
+      S = min(min(C / rem, kMaxSplit),
+              min(p.split_slots_x / rem, nk / kMinSplitSteps));
+      if (S < 2) S = 1;
+    }
+  }
+  const int whole = S > 1 ? cnt - rem : cnt;
+  sr.ks = 0;
+  sr.ke = nk;
+  sr.S = 1;
+  sr.slot0 = sr.s = sr.id = 0;
+  int L;
+  if (idx < whole) {
+    L = x * per + idx;
+  } else {
+    if (S == 1) return false;
+    const int c = idx - whole;
+    if (c >= rem * S) return false;
+    const int rt = c / S;
+    sr.s = c - rt * S;
+    sr.S = S;
+    sr.ks = sr.s * nk / S;
+    sr.ke = (sr.s + 1) * nk / S;
+    sr.slot0 = x * p.split_slots_x + rt * S;
+    sr.id = x * p.split_slots_x + rt;
+    L = x * per + whole + rt;
+  }
+  ragged_m_tile(p, L, tc);
+  return true;
+}
+
+// Partial tile of a split work-group: float4 q of accumulator block (i, j)
+// of thread t at float4 index ((i NJ + j) 4 + q) 512 + t of its slot, so
+// every wave-wide store and load covers one contiguous KiB.  Returns true
+// for the last arrival, whose accumulators then hold the sum of the S
+// partials, added in slot order.
+template <int MI, int NJ>
+__device__ __forceinline__ bool split_reduce(const Params& p,
+                                             const SplitRange& sr,
+                                             f32x16_t (&acc)[MI][NJ], int t) {
+  constexpr int kSlot4 = BM * BN / 4;   // float4 per slot
+  float4* own = reinterpret_cast<float4*>(p.split_part) +
+                (int64_t)(sr.slot0 + sr.s) * kSlot4;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        own[((i * NJ + j) * 4 + q) * kThreads8 + t] =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                        acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+  // Every wave's partial stores have reached the L2 (vmcnt(0)) before the
+  // barrier; then one release at agent scope (an L2 write-back ahead of the
+  // counter increment) publishes them all, instead of one per wave.
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+  __syncthreads();
+  __shared__ uint32_t arrived;
+  if (t == 0)
+    arrived = __hip_atomic_fetch_add(p.split_cnt + sr.id, 1u,
+                                     __ATOMIC_RELEASE,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (arrived != (uint32_t)(sr.S - 1)) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16_t{};
+  const float4* part =
+      reinterpret_cast<const float4*>(p.split_part) + (int64_t)sr.slot0 * kSlot4;
+  for (int s = 0; s < sr.S; ++s) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v =
+              part[(int64_t)s * kSlot4 + ((i * NJ + j) * 4 + q) * kThreads8 + t];
+          acc[i][j][4 * q] += v.x;
+          acc[i][j][4 * q + 1] += v.y;
+          acc[i][j][4 * q + 2] += v.z;
+          acc[i][j][4 * q + 3] += v.w;
+        }
+  }
+  // the counter is zero again for the next launch
+  if (t == 0)
+    __hip_atomic_store(p.split_cnt + sr.id, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
 
 template <int EPI>
 struct Shape8 {
@@ -276,7 +412,8 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char sA1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sB1[kTileBytes];
   TileCoord tc;
-  if (!decode_tile<RAGGED_M>(p, tc)) return;
+  SplitRange sr;
+  if (!decode_tile_w8(p, (p.K + kStepK - 1) / kStepK, tc, sr)) return;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -289,16 +426,18 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   KcDirect8<EPI, true> db;
   const int q = 8 * (wave & 3) + (lane >> 3);
   const int cl = (lane & 7) ^ swz32(q);
-  // rows past the expert's last read as zeros (buffer descriptor range)
-  da.base = p.a + (int64_t)tc.seg0 * p.lda;
-  da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda;
+  // rows past the expert's last read as zeros (buffer descriptor range);
+  // a split work-group starts at K step ks
+  const uint32_t kofs = (uint32_t)sr.ks * kRowBytes;
+  da.base = p.a + (int64_t)tc.seg0 * p.lda + kofs;
+  da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda - kofs;
   da.ld = p.lda;
   da.q = q;
   da.cl = cl;
   da.r0 = tc.m0;
   da.init(wave);
-  db.base = p.b + (int64_t)tc.e * p.b_es;
-  db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb;
+  db.base = p.b + (int64_t)tc.e * p.b_es + kofs;
+  db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb - kofs;
   db.ld = p.ldb;
   db.q = q;
   db.cl = cl;
@@ -313,7 +452,7 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16_t{};
 
-  const int nk = (p.K + kStepK - 1) / kStepK;
+  const int nk = sr.ke - sr.ks;
   // 6 LDS reads and 8 MFMAs per slice; the next step's A loads go out one
   // per MFMA over the first slice, its B loads over the second
   auto slice_sched = [&](int kk) {
@@ -364,12 +503,29 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   // every wave is past its last read of the stages (and every direct load
   // has landed) before they become epilogue staging: 16 KiB per wave
   __syncthreads();
+  if (sr.S > 1 && !split_reduce(p, sr, acc, t)) return;
   char* wbuf = (wave < 2 ? sA0 : wave < 4 ? sB0 : wave < 6 ? sA1 : sB1) +
                (wave & 1) * (kTileBytes / 2);
   if constexpr (EPI == EPI_STORE)
     epilogue_w8_store(p, tc, acc, n0, wm, wn, lane, wbuf);
   else
     epilogue_w8_swiglu(p, tc, acc, n0, wm, wn, lane, wave, wbuf);
+}
+
+// Grid of an eight-wave RAGGED_M launch: ragged_m_grid plus one round of
+// split work-groups per XCD.
+inline int ragged_m_grid_w8(int64_t rows, int E, int tn, const Params& p) {
+  return ragged_m_grid(rows, E, tn) +
+         (p.split_part ? kXcds * p.split_slots_x : 0);
+}
+
+// Partial-tile slots per XCD worth allocating for a launch with at most
+// `tiles` tiles and nk K steps (0: no split); float32 partials of BM x BN
+// per slot, plus one counter per slot.
+inline int split_slots_x(int64_t tiles, int nk) {
+  if (nk < 4) return 0;
+  const int64_t per = (tiles + kXcds - 1) / kXcds;
+  return (int)std::min<int64_t>(kMaxSplitSlotsX, per * kMaxSplit);
 }
 
 template <int EPI>

@@ -59,7 +59,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
                                const void* w_dn, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
-                               hipStream_t stream);
+                               int cu_count, hipStream_t stream);
 // tensor-scaled FP8
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 hipError_t launch_seg_amax(const void* src, int64_t seg_elems, int n_seg,
