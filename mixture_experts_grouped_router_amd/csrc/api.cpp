@@ -547,7 +547,7 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
     e = moe::launch_mlp_fwd_fp8t(a->E, a->H, a->F, a->rows, a->x_perm,
                                  a->w_gu, a->w_dn, a->w_perm, a->offsets,
                                  a->z_perm, a->h1_save, a->a_save, a->ws,
-                                 as_stream(stream));
+                                 ctx->cu_count, as_stream(stream));
   } else if (!mx) {
     e = moe::launch_mlp_fwd_bf16(a->E, a->H, a->F, a->rows, a->x_perm, a->w_gu,
                                  a->w_dn, a->w_perm, a->offsets, a->z_perm,
@@ -560,7 +560,7 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
         xq ? static_cast<const uint8_t*>(a->x_perm) : nullptr,
         a->x_perm_scale, a->w_gu, a->w_dn, a->w_gu_q, a->w_gu_s, a->w_dn_q,
         a->w_dn_s, a->w_perm, a->offsets, a->z_perm, a->h1_save, a->a_save,
-        a->ws, as_stream(stream));
+        a->ws, ctx->cu_count, as_stream(stream));
   }
   return hip_status(e, "grouped_mlp_fwd");
 }

@@ -122,12 +122,6 @@ int fwd_split_slots_x(int E, int H, int F, int64_t rows) {
   if (H <= kW8MaxGateUpK) s = std::max(s, split_slots_x(mt * tn1, H / 64));
   return s;
 }
-size_t split_part_bytes(int slots_x) {
-  return align256((size_t)kXcds * slots_x * BM * BN * sizeof(float));
-}
-size_t split_cnt_bytes(int slots_x) {
-  return align256((size_t)kXcds * slots_x * sizeof(uint32_t));
-}
 }  // namespace
 
 size_t mlp_fwd_bf16_ws_bytes(int E, int H, int F, int64_t rows, bool need_a) {
@@ -168,12 +162,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   if (err != hipSuccess) return err;
   // the eight-wave GEMMs split the last, partly filled round of tiles
   auto set_split = [&](Params& p) {
-    if (sx > 0) {
-      p.split_part = split_part;
-      p.split_cnt = split_cnt;
-      p.split_slots_x = sx;
-      p.cus_per_xcd = cu_count / kXcds;
-    }
+    enable_split(p, split_part, split_cnt, sx, cu_count);
   };
 
   Params p1{};
@@ -202,7 +191,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   if (H <= kW8MaxGateUpK) {
     set_split(p1);
     err = launch_w8<EPI_SWIGLU>("gemm_gate_up_swiglu_bf16", p1,
-                                ragged_m_grid_w8(rows, E, tn1, p1), stream);
+                                ragged_m_grid_split(rows, E, tn1, p1), stream);
   } else
     err = launch<P_BF16, KC, KC, RAGGED_M, EPI_SWIGLU>(
         "gemm_gate_up_swiglu_bf16", p1, ragged_m_grid(rows, E, tn1), stream);
@@ -226,7 +215,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p2.rows = rows;
   set_split(p2);
   return launch_w8<EPI_STORE>("gemm_down_bf16", p2,
-                             ragged_m_grid_w8(rows, E, tn2, p2), stream);
+                             ragged_m_grid_split(rows, E, tn2, p2), stream);
 }
 
 size_t mlp_bwd_bf16_ws_bytes(int E, int H, int F, int64_t rows) {

@@ -20,6 +20,9 @@ struct Fp8tWs {
   int32_t *ts1, *ts2;
   uint8_t *xq, *guq, *dnq, *aq;
   uint16_t* a;      // bf16 A (when a_save is NULL)
+  int split_x;          // down GEMM: split slots per XCD
+  float* split_part;    // down GEMM: partial tiles of a split tail
+  uint32_t* split_cnt;  // down GEMM: arrival counters
   size_t bytes;
 };
 
@@ -42,6 +45,11 @@ Fp8tWs carve(void* base, int E, int H, int F, int64_t rows, bool need_a) {
   w.aq = reinterpret_cast<uint8_t*>(take((size_t)rows * F));
   w.a = need_a ? reinterpret_cast<uint16_t*>(take((size_t)rows * F * 2))
                : nullptr;
+  // K steps of 128 values
+  w.split_x = split_slots_x((rows / BM + E) * (int64_t)((H + BN - 1) / BN),
+                            F / 128);
+  w.split_part = reinterpret_cast<float*>(take(split_part_bytes(w.split_x)));
+  w.split_cnt = reinterpret_cast<uint32_t*>(take(split_cnt_bytes(w.split_x)));
   w.bytes = off;
   return w;
 }
@@ -57,7 +65,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
                                const void* w_dn, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
-                               hipStream_t stream) {
+                               int cu_count, hipStream_t stream) {
   Fp8tWs w = carve(ws, E, H, F, rows, a_save == nullptr);
   uint16_t* a = a_save ? static_cast<uint16_t*>(a_save) : w.a;
   // scale slots: 0 x, 1 A, 2 + e W_gu[e], 2 + E + e W_dn[e]
@@ -79,7 +87,9 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
                               stream);
   const int tn1 = (F + BN / 2 - 1) / (BN / 2);
   const int tn2 = (H + BN - 1) / BN;
-  if (err == hipSuccess) err = launch_tile_table(offsets, E, tn1, w.ts1, stream);
+  if (err == hipSuccess)
+    err = launch_tile_table(offsets, E, tn1, w.ts1, stream, w.split_cnt,
+                            kXcds * w.split_x);
   if (err == hipSuccess) err = launch_tile_table(offsets, E, tn2, w.ts2, stream);
   if (err != hipSuccess) return err;
 
@@ -131,8 +141,9 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   p2.rows = rows;
   p2.tsa = w.scale + 1;
   p2.tsb = w.scale + 2 + E;
+  enable_split(p2, w.split_part, w.split_cnt, w.split_x, cu_count);
   return launch<P_FP8T, KC, KC, RAGGED_M, EPI_STORE>(
-      "gemm_down_fp8t", p2, ragged_m_grid(rows, E, tn2), stream);
+      "gemm_down_fp8t", p2, ragged_m_grid_split(rows, E, tn2, p2), stream);
 }
 
 }  // namespace moe

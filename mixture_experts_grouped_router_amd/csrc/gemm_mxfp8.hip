@@ -32,6 +32,9 @@ struct MxFwdWs {
   uint8_t* gus;  // W_gu scales (GEMM layout, K = H)
   uint8_t* dnq;  // W_dn codes [E, H, F] (quantised here)
   uint8_t* dns;  // W_dn scales (GEMM layout, K = F)
+  int split_x;          // down GEMM: split slots per XCD
+  float* split_part;    // down GEMM: partial tiles of a split tail
+  uint32_t* split_cnt;  // down GEMM: arrival counters
   size_t bytes;
 };
 
@@ -61,6 +64,11 @@ MxFwdWs carve_fwd(void* base, int E, int H, int F, int64_t rows, bool quant_x,
   }
   w.gus = take8(ngu / 32);
   w.dns = take8(ndn / 32);
+  // K steps of 128 values
+  w.split_x = split_slots_x((rows / BM + E) * (int64_t)((H + BN - 1) / BN),
+                            F / 128);
+  w.split_part = reinterpret_cast<float*>(take(split_part_bytes(w.split_x)));
+  w.split_cnt = reinterpret_cast<uint32_t*>(take(split_cnt_bytes(w.split_x)));
   w.bytes = off;
   return w;
 }
@@ -80,7 +88,7 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
                              const uint8_t* w_dn_s, const float* w_perm,
                              const int32_t* offsets, void* z_perm,
                              void* h1_save, void* a_save, void* ws,
-                             hipStream_t stream) {
+                             int cu_count, hipStream_t stream) {
   const bool quant_x = xq == nullptr;
   const bool quant_w = w_gu_q == nullptr || w_dn_q == nullptr;
   MxFwdWs w = carve_fwd(ws, E, H, F, rows, quant_x, quant_w);
@@ -109,7 +117,8 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   if (err != hipSuccess) return err;
   const int tn1 = (F + BN / 2 - 1) / (BN / 2);
   const int tn2 = (H + BN - 1) / BN;
-  err = launch_tile_table(offsets, E, tn1, w.ts1, stream);
+  err = launch_tile_table(offsets, E, tn1, w.ts1, stream, w.split_cnt,
+                          kXcds * w.split_x);
   if (err == hipSuccess) err = launch_tile_table(offsets, E, tn2, w.ts2, stream);
   if (err != hipSuccess) return err;
 
@@ -164,8 +173,9 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p2.c = static_cast<uint16_t*>(z_perm);
   p2.ldc = H;
   p2.rows = rows;
+  enable_split(p2, w.split_part, w.split_cnt, w.split_x, cu_count);
   return launch<P_FP8, KC, KC, RAGGED_M, EPI_STORE>(
-      "gemm_down_mxfp8", p2, ragged_m_grid(rows, E, tn2), stream);
+      "gemm_down_mxfp8", p2, ragged_m_grid_split(rows, E, tn2, p2), stream);
 }
 
 // ---- backward ----------------------------------------------------------------

@@ -30,6 +30,8 @@
 // contiguous run of tiles, M fastest inside groups of 4 N tiles: the tiles in
 // flight on one XCD share activation rows and weight panels in its L2.
 #pragma once
+#include <algorithm>
+
 #include "common.hpp"
 #include "timer.hpp"
 
@@ -939,6 +941,147 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
   }
 }
 
+// ---- The last round of tiles, split along K ---------------------------------
+// An XCD runs its contiguous run of tiles in rounds of one tile per CU.  A
+// run of R rounds plus `rem` more tiles takes R + 1 tile times even when rem
+// is small (a tile with a few valid rows costs as much as a full one: the
+// weight panel and the MFMAs are the same).  When rem is at most half a
+// round, each of those rem tiles is split into S <= kMaxSplit ranges of K
+// steps (rem * S <= CUs of the XCD), run by S work-groups that each write
+// their float32 partial tile to a slot of the workspace; the last to arrive
+// (an arrival counter per tile) adds the S partials in slot order and runs
+// the tile's epilogue.  The sums are fixed by the tile list alone, so the
+// result is deterministic.
+constexpr int kMaxSplit = 8;
+constexpr int kMaxSplitSlotsX = 32;   // slots (and counters) per XCD
+// Fewest K steps of a split work-group: the partial tile's round trip and
+// the cache write-back / invalidate of the hand-over cost tens of
+// microseconds per tile, which only long K ranges repay (the Mixtral-shaped
+// down GEMM, K = 14336, gains 7%; the Qwen3-shaped gate/up GEMM, K = 2048,
+// loses 3% with 16-step ranges).
+constexpr int kMinSplitSteps = 32;
+
+struct SplitRange {
+  int ks, ke;    // K steps [ks, ke) of this work-group
+  int S;         // work-groups sharing the tile (1: not split)
+  int slot0;     // first partial slot of the tile; this one is slot0 + s
+  int s;
+  int id;        // arrival counter
+};
+
+__device__ __forceinline__ bool decode_tile_split(const Params& p, int nk,
+                                               TileCoord& tc,
+                                               SplitRange& sr) {
+  const int b = blockIdx.x;
+  const int total = p.tile_start[p.E];
+  const int per = (total + kXcds - 1) / kXcds;
+  const int x = b % kXcds, idx = b / kXcds;
+  const int cnt = min(per, total - x * per);   // tiles of this XCD
+  if (cnt <= 0) return false;
+  int S = 1, rem = 0;
+  const int C = p.cus_per_xcd;
+  if (p.split_part != nullptr && C > 0) {
+    rem = cnt % C;
+    if (rem > 0 && 2 * rem <= C) {
+      S = min(min(C / rem, kMaxSplit),
+              min(p.split_slots_x / rem, nk / kMinSplitSteps));
+      if (S < 2) S = 1;
+    }
+  }
+  const int whole = S > 1 ? cnt - rem : cnt;
+  sr.ks = 0;
+  sr.ke = nk;
+  sr.S = 1;
+  sr.slot0 = sr.s = sr.id = 0;
+  int L;
+  if (idx < whole) {
+    L = x * per + idx;
+  } else {
+    if (S == 1) return false;
+    const int c = idx - whole;
+    if (c >= rem * S) return false;
+    const int rt = c / S;
+    sr.s = c - rt * S;
+    sr.S = S;
+    sr.ks = sr.s * nk / S;
+    sr.ke = (sr.s + 1) * nk / S;
+    sr.slot0 = x * p.split_slots_x + rt * S;
+    sr.id = x * p.split_slots_x + rt;
+    L = x * per + whole + rt;
+  }
+  ragged_m_tile(p, L, tc);
+  return true;
+}
+
+// Partial tile of a split work-group: float4 q of accumulator block (i, j)
+// of thread t at float4 index ((i NJ + j) 4 + q) NT + t of its slot, so
+// every wave-wide store and load covers one contiguous KiB.  Returns true
+// for the last arrival, whose accumulators then hold the sum of the S
+// partials, added in slot order.
+template <int NT, int MI, int NJ>
+__device__ __forceinline__ bool split_reduce(const Params& p,
+                                             const SplitRange& sr,
+                                             f32x16_t (&acc)[MI][NJ], int t) {
+  constexpr int kSlot4 = BM * BN / 4;   // float4 per slot
+  float4* own = reinterpret_cast<float4*>(p.split_part) +
+                (int64_t)(sr.slot0 + sr.s) * kSlot4;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        own[((i * NJ + j) * 4 + q) * NT + t] =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                        acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+  // Every wave's partial stores have reached the L2 (vmcnt(0)) before the
+  // barrier; then one release at agent scope (an L2 write-back ahead of the
+  // counter increment) publishes them all, instead of one per wave.
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+  __syncthreads();
+  __shared__ uint32_t arrived;
+  if (t == 0)
+    arrived = __hip_atomic_fetch_add(p.split_cnt + sr.id, 1u,
+                                     __ATOMIC_RELEASE,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (arrived != (uint32_t)(sr.S - 1)) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16_t{};
+  const float4* part =
+      reinterpret_cast<const float4*>(p.split_part) + (int64_t)sr.slot0 * kSlot4;
+  for (int s = 0; s < sr.S; ++s) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v =
+              part[(int64_t)s * kSlot4 + ((i * NJ + j) * 4 + q) * NT + t];
+          acc[i][j][4 * q] += v.x;
+          acc[i][j][4 * q + 1] += v.y;
+          acc[i][j][4 * q + 2] += v.z;
+          acc[i][j][4 * q + 3] += v.w;
+        }
+  }
+  // the counter is zero again for the next launch
+  if (t == 0)
+    __hip_atomic_store(p.split_cnt + sr.id, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+template <int EPI>
+struct Shape8 {
+  static constexpr int MI = EPI == EPI_SWIGLU ? 2 : 4;  // 32-row A blocks
+  static constexpr int NJ = 8 / MI;                     // 32-row B blocks
+  static constexpr int WN = 8 / (8 / MI);               // waves along N
+};
+
 template <int P, int LA, int LB, int G, int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   static_assert(P == P_BF16 || (LA == KC && LB == KC),
@@ -958,8 +1101,21 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char sB0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sA1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sB1[kTileBytes];
+  // the forward down GEMM (ragged M, K-contiguous operands, plain store)
+  // may split the K range of its last round of tiles
+  constexpr bool kMaySplit = G == RAGGED_M && EPI == EPI_STORE && LA == KC &&
+                             LB == KC;
   TileCoord tc;
-  if (!decode_tile<G>(p, tc)) return;
+  SplitRange sr;
+  if constexpr (kMaySplit) {
+    if (!decode_tile_split(p, (p.K + kStepK - 1) / kStepK, tc, sr)) return;
+  } else {
+    if (!decode_tile<G>(p, tc)) return;
+    sr.ks = 0;
+    sr.S = 1;
+  }
+  // a split work-group starts at K step ks (bytes into every row)
+  const uint32_t kofs = (uint32_t)sr.ks * kRowBytes;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -986,8 +1142,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   if constexpr (LA == KC) {
     if constexpr (G == RAGGED_M) {
       // rows seg0 + m0 + r; rows past the expert's last read as zeros
-      da.base = p.a + (int64_t)tc.seg0 * p.lda;
-      da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda;
+      da.base = p.a + (int64_t)tc.seg0 * p.lda + kofs;
+      da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda - kofs;
     } else {
       // A [M][K]: the expert's K range starts at element seg0 of every row
       // (a multiple of the K step); rows past M read as zeros
@@ -1010,8 +1166,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   const char* bexp = p.b + (int64_t)tc.e * p.b_es;
   if constexpr (LB == KC) {
     if constexpr (G == RAGGED_M) {
-      db.base = bexp;
-      db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb;
+      db.base = bexp + kofs;
+      db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb - kofs;
     } else {
       // B [N][K], same K range as A
       const uint32_t kofs = (uint32_t)tc.seg0 * kElemBytes;
@@ -1044,8 +1200,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   const uint32_t sel = (lane >> 5) ? 0x0c0c0301u : 0x0c0c0200u;
   if constexpr (P == P_FP8) {
     if constexpr (G == RAGGED_M) {
-      ms.a = p.sa;
-      ms.b = p.sb + (int64_t)tc.e * p.sb_es;
+      // scales of K step s at byte 128 s of a row block's run
+      ms.a = p.sa + kofs;
+      ms.b = p.sb + (int64_t)tc.e * p.sb_es + kofs;
     } else {   // the expert's first K step (seg0 is a multiple of 128)
       ms.a = p.sa + tc.seg0;
       ms.b = p.sb + tc.seg0;
@@ -1073,7 +1230,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  const int nk = (kdim + kStepK - 1) / kStepK;
+  const int nk = kMaySplit ? sr.ke - sr.ks : (kdim + kStepK - 1) / kStepK;
   // LDS reads per K slice: 4 per K-contiguous side (16-byte reads), 8 per
   // MN-contiguous side (two 8-byte transposed reads per block); MXFP8 16
   constexpr int kNR = P != P_BF16 ? 16
@@ -1199,6 +1356,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // every wave is past its last LDS read of the operand stages (and every
   // direct load has landed) before the stages become epilogue staging
   __syncthreads();
+  if constexpr (kMaySplit)
+    if (sr.S > 1 && !split_reduce<kThreads>(p, sr, acc, t)) return;
   char* wbuf = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
   if constexpr (P == P_FP8T) {
     // the two tensor scales
@@ -1224,6 +1383,42 @@ inline int ragged_m_grid(int64_t rows, int E, int tn) {
   int64_t g = mt * tn;
   g = (g + kXcds - 1) / kXcds * kXcds;
   return (int)g;
+}
+
+// Grid of a RAGGED_M launch that may split its tail: ragged_m_grid plus
+// one round of split work-groups per XCD.
+inline int ragged_m_grid_split(int64_t rows, int E, int tn, const Params& p) {
+  return ragged_m_grid(rows, E, tn) +
+         (p.split_part ? kXcds * p.split_slots_x : 0);
+}
+
+// Partial-tile slots per XCD worth allocating for a launch with at most
+// `tiles` tiles and nk K steps (0: no split); float32 partials of BM x BN
+// per slot, plus one counter per slot.
+inline int split_slots_x(int64_t tiles, int nk) {
+  if (nk < 4) return 0;
+  const int64_t per = (tiles + kXcds - 1) / kXcds;
+  return (int)std::min<int64_t>(kMaxSplitSlotsX, per * kMaxSplit);
+}
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace bytes of the float32 partial tiles and of the arrival counters
+// for slots_x slots per XCD.
+inline size_t split_part_bytes(int slots_x) {
+  return align256((size_t)kXcds * slots_x * BM * BN * sizeof(float));
+}
+inline size_t split_cnt_bytes(int slots_x) {
+  return align256((size_t)kXcds * slots_x * sizeof(uint32_t));
+}
+// Lets launch p split its tail (slots_x > 0); the counters must be zero.
+inline void enable_split(Params& p, float* part, uint32_t* cnt, int slots_x,
+                         int cu_count) {
+  if (slots_x <= 0) return;
+  p.split_part = part;
+  p.split_cnt = cnt;
+  p.split_slots_x = slots_x;
+  p.cus_per_xcd = cu_count / kXcds;
 }
 
 inline int ragged_k_grid(int E, int tiles_m, int tiles_n) {
@@ -1253,7 +1448,6 @@ hipError_t launch_expert_order(const int32_t* offsets, int E, int32_t* order,
 hipError_t launch_padded_offsets(const int32_t* offsets, int E, int pad,
                                  int32_t* poff, hipStream_t stream);
 
-constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace gg
 }  // namespace moe

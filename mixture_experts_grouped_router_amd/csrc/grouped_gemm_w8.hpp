@@ -21,147 +21,6 @@ constexpr int kThreads8 = 512;
 // largest K (= H) for which the gate/up GEMM runs with eight waves
 constexpr int kW8MaxGateUpK = 2048;
 
-// ---- The last round of tiles, split along K ---------------------------------
-// An XCD runs its contiguous run of tiles in rounds of one tile per CU.  A
-// run of R rounds plus `rem` more tiles takes R + 1 tile times even when rem
-// is small (a tile with a few valid rows costs as much as a full one: the
-// weight panel and the MFMAs are the same).  When rem is at most half a
-// round, each of those rem tiles is split into S <= kMaxSplit ranges of K
-// steps (rem * S <= CUs of the XCD), run by S work-groups that each write
-// their float32 partial tile to a slot of the workspace; the last to arrive
-// (an arrival counter per tile) adds the S partials in slot order and runs
-// the tile's epilogue.  The sums are fixed by the tile list alone, so the
-// result is deterministic.
-constexpr int kMaxSplit = 8;
-constexpr int kMaxSplitSlotsX = 32;   // slots (and counters) per XCD
-// Fewest K steps of a split work-group: the partial tile's round trip and
-// the cache write-back / invalidate of the hand-over cost tens of
-// microseconds per tile, which only long K ranges repay (the Mixtral-shaped
-// down GEMM, K = 14336, gains 7%; the Qwen3-shaped gate/up GEMM, K = 2048,
-// loses 3% with 16-step ranges).
-constexpr int kMinSplitSteps = 32;
-
-struct SplitRange {
-  int ks, ke;    // K steps [ks, ke) of this work-group
-  int S;         // work-groups sharing the tile (1: not split)
-  int slot0;     // first partial slot of the tile; this one is slot0 + s
-  int s;
-  int id;        // arrival counter
-};
-
-__device__ __forceinline__ bool decode_tile_w8(const Params& p, int nk,
-                                               TileCoord& tc,
-                                               SplitRange& sr) {
-  const int b = blockIdx.x;
-  const int total = p.tile_start[p.E];
-  const int per = (total + kXcds - 1) / kXcds;
-  const int x = b % kXcds, idx = b / kXcds;
-  const int cnt = min(per, total - x * per);   // tiles of this XCD
-  if (cnt <= 0) return false;
-  int S = 1, rem = 0;
-  const int C = p.cus_per_xcd;
-  if (p.split_part != nullptr && C > 0) {
-    rem = cnt % C;
-    if (rem > 0 && 2 * rem <= C) {
-      S = min(min(C / rem, kMaxSplit),
-              min(p.split_slots_x / rem, nk / kMinSplitSteps));
-      if (S < 2) S = 1;
-    }
-  }
-  const int whole = S > 1 ? cnt - rem : cnt;
-  sr.ks = 0;
-  sr.ke = nk;
-  sr.S = 1;
-  sr.slot0 = sr.s = sr.id = 0;
-  int L;
-  if (idx < whole) {
-    L = x * per + idx;
-  } else {
-    if (S == 1) return false;
-    const int c = idx - whole;
-    if (c >= rem * S) return false;
-    const int rt = c / S;
-    sr.s = c - rt * S;
-    sr.S = S;
-    sr.ks = sr.s * nk / S;
-    sr.ke = (sr.s + 1) * nk / S;
-    sr.slot0 = x * p.split_slots_x + rt * S;
-    sr.id = x * p.split_slots_x + rt;
-    L = x * per + whole + rt;
-  }
-  ragged_m_tile(p, L, tc);
-  return true;
-}
-
-// Partial tile of a split work-group: float4 q of accumulator block (i, j)
-// of thread t at float4 index ((i NJ + j) 4 + q) 512 + t of its slot, so
-// every wave-wide store and load covers one contiguous KiB.  Returns true
-// for the last arrival, whose accumulators then hold the sum of the S
-// partials, added in slot order.
-template <int MI, int NJ>
-__device__ __forceinline__ bool split_reduce(const Params& p,
-                                             const SplitRange& sr,
-                                             f32x16_t (&acc)[MI][NJ], int t) {
-  constexpr int kSlot4 = BM * BN / 4;   // float4 per slot
-  float4* own = reinterpret_cast<float4*>(p.split_part) +
-                (int64_t)(sr.slot0 + sr.s) * kSlot4;
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        own[((i * NJ + j) * 4 + q) * kThreads8 + t] =
-            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                        acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-  // Every wave's partial stores have reached the L2 (vmcnt(0)) before the
-  // barrier; then one release at agent scope (an L2 write-back ahead of the
-  // counter increment) publishes them all, instead of one per wave.
-  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-  __syncthreads();
-  __shared__ uint32_t arrived;
-  if (t == 0)
-    arrived = __hip_atomic_fetch_add(p.split_cnt + sr.id, 1u,
-                                     __ATOMIC_RELEASE,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (arrived != (uint32_t)(sr.S - 1)) return false;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16_t{};
-  const float4* part =
-      reinterpret_cast<const float4*>(p.split_part) + (int64_t)sr.slot0 * kSlot4;
-  for (int s = 0; s < sr.S; ++s) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float4 v =
-              part[(int64_t)s * kSlot4 + ((i * NJ + j) * 4 + q) * kThreads8 + t];
-          acc[i][j][4 * q] += v.x;
-          acc[i][j][4 * q + 1] += v.y;
-          acc[i][j][4 * q + 2] += v.z;
-          acc[i][j][4 * q + 3] += v.w;
-        }
-  }
-  // the counter is zero again for the next launch
-  if (t == 0)
-    __hip_atomic_store(p.split_cnt + sr.id, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  return true;
-}
-
-template <int EPI>
-struct Shape8 {
-  static constexpr int MI = EPI == EPI_SWIGLU ? 2 : 4;  // 32-row A blocks
-  static constexpr int NJ = 8 / MI;                     // 32-row B blocks
-  static constexpr int WN = 8 / (8 / MI);               // waves along N
-};
-
 // Direct loads with eight waves: wave w, instruction j (of 4) fills KiB
 // 8 j + w of the stage = tile rows 32 (2 j + w / 4) + 8 (w % 4) + lane / 8,
 // the same bytes as the four-wave loader puts there.
@@ -413,7 +272,7 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char sB1[kTileBytes];
   TileCoord tc;
   SplitRange sr;
-  if (!decode_tile_w8(p, (p.K + kStepK - 1) / kStepK, tc, sr)) return;
+  if (!decode_tile_split(p, (p.K + kStepK - 1) / kStepK, tc, sr)) return;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -503,29 +362,13 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   // every wave is past its last read of the stages (and every direct load
   // has landed) before they become epilogue staging: 16 KiB per wave
   __syncthreads();
-  if (sr.S > 1 && !split_reduce(p, sr, acc, t)) return;
+  if (sr.S > 1 && !split_reduce<kThreads8>(p, sr, acc, t)) return;
   char* wbuf = (wave < 2 ? sA0 : wave < 4 ? sB0 : wave < 6 ? sA1 : sB1) +
                (wave & 1) * (kTileBytes / 2);
   if constexpr (EPI == EPI_STORE)
     epilogue_w8_store(p, tc, acc, n0, wm, wn, lane, wbuf);
   else
     epilogue_w8_swiglu(p, tc, acc, n0, wm, wn, lane, wave, wbuf);
-}
-
-// Grid of an eight-wave RAGGED_M launch: ragged_m_grid plus one round of
-// split work-groups per XCD.
-inline int ragged_m_grid_w8(int64_t rows, int E, int tn, const Params& p) {
-  return ragged_m_grid(rows, E, tn) +
-         (p.split_part ? kXcds * p.split_slots_x : 0);
-}
-
-// Partial-tile slots per XCD worth allocating for a launch with at most
-// `tiles` tiles and nk K steps (0: no split); float32 partials of BM x BN
-// per slot, plus one counter per slot.
-inline int split_slots_x(int64_t tiles, int nk) {
-  if (nk < 4) return 0;
-  const int64_t per = (tiles + kXcds - 1) / kXcds;
-  return (int)std::min<int64_t>(kMaxSplitSlotsX, per * kMaxSplit);
 }
 
 template <int EPI>

@@ -73,7 +73,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
                                const void* w_dn, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
-                               hipStream_t stream);
+                               int cu_count, hipStream_t stream);
 
 // router projection (float64 accumulation in ascending h) and backward
 hipError_t launch_router_logits(const void* x, const void* w_r,
@@ -117,7 +117,7 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
                              const uint8_t* w_dn_s, const float* w_perm,
                              const int32_t* offsets, void* z_perm,
                              void* h1_save, void* a_save, void* ws,
-                             hipStream_t stream);
+                             int cu_count, hipStream_t stream);
 size_t mlp_bwd_mx_ws_bytes(int E, int H, int F, int64_t rows);
 hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
                              const void* x_perm, const void* w_gu,

@@ -62,6 +62,7 @@ FP8T_CASES = [
     (256, 128, 256, 8, 2, 0.0),
     (700, 256, 384, 5, 2, 1.2),     # ragged M, F not a multiple of 256
     (900, 128, 128, 16, 4, 1.2),    # many experts, some empty
+    (512, 256, 8192, 4, 2, 0.0),    # down GEMM's last tiles split along K
 ]
 
 

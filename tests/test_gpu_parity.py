@@ -323,8 +323,7 @@ MLP_CASES = [
     (900, 256, 128, 16, 4, 1.2),    # many experts, some empty
     (64, 64, 64, 4, 1, 0.0),        # tiles larger than the problem
     (300, 2112, 192, 4, 2, 1.2),    # H > 2048: the four-wave gate/up GEMM
-    (512, 256, 1024, 4, 2, 0.0),    # down GEMM's tiles split 8 ways along K
-    (4096, 2048, 1024, 8, 2, 0.0),  # whole rounds of tiles + a split tail
+    (512, 256, 8192, 4, 2, 0.0),    # down GEMM's tiles split 4 ways along K
 ]
 
 
@@ -346,7 +345,7 @@ def split_plan(offsets, tn, nk, cus):
         rem = cnt % C
         S = 1
         if slots_x and rem and 2 * rem <= C:
-            S = min(C // rem, 8, slots_x // rem, nk // 2)
+            S = min(C // rem, 8, slots_x // rem, nk // 32)
             S = S if S >= 2 else 1
         out.append(S)
     return out
@@ -455,18 +454,16 @@ def test_grouped_mlp_deterministic(m):
 
 def test_grouped_mlp_split_tail(m):
     """Whole rounds of tiles plus a last round whose tiles are split along K
-    over several work-groups (partials added in a fixed order): matches the
-    oracle and the per-expert loop (which never splits), bit for bit the
-    same over repeated calls."""
-    T, H, F, E, k = 4096, 2048, 1024, 8, 2
+    over several work-groups (partials added in a fixed order), in the down
+    GEMM (K = F = 4096): matches the oracle and the per-expert loop (which
+    never splits), bit for bit the same over repeated calls."""
+    T, H, F, E, k = 4096, 2048, 4096, 8, 2
     d = _mlp_case(T, H, F, E, k, 0.0, 5)
     idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
     p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     offs = p["offsets"].cpu().numpy()
-    # both GEMMs split their tail here (gate/up: 128-column f tiles, K = H;
-    # down: K = F)
-    assert max(split_plan(offs, F // 128, H // 64, cus)) > 1
+    # the down GEMM (256-column tiles, 64-wide K steps) splits its tail
     assert max(split_plan(offs, H // 256, F // 64, cus)) > 1
     wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
     runs = [m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
@@ -481,9 +478,8 @@ def test_grouped_mlp_split_tail(m):
     assert_rows_close(host_f64(runs[0]["h1"]), ref["h1"], TOL_BF16, "h1")
     loop = m.moe_expert_loop_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
                                      w_perm=p["w_perm"], save=True)
-    gh, rh = runs[0]["h1"].float(), loop["h1"].float()
-    assert torch.all((gh - rh).abs() <= 2.0 ** -7 * rh.abs()
-                     + 1e-4 * rh.abs().max())
+    # the loop rounds h1 and A to bf16 on the way: close, not bit-equal
+    assert O.rel_err(host_f64(runs[0]["z"]), host_f64(loop["z"])) < 1e-2
 
 
 def test_grouped_mlp_zero_rows(m):
@@ -540,6 +536,7 @@ MX_CASES = [
     (256, 128, 256, 8, 2, 0.0),
     (700, 256, 384, 5, 2, 1.2),     # ragged M tails, odd K-step count (3)
     (900, 384, 128, 16, 4, 1.2),    # many experts, some empty
+    (512, 256, 8192, 4, 2, 0.0),    # down GEMM's last tiles split along K
 ]
 
 
