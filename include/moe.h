@@ -343,7 +343,10 @@ moe_status_t moe_fp8_tensor_quantize(moe_ctx_t ctx, const void* src,
  * MOE_ERR_UNSUPPORTED (size limits, misaligned pointers: operands 16-byte,
  * MXFP8 scale arrays 4-byte), MOE_ERR_WORKSPACE (ws NULL or smaller than
  * moe_grouped_mlp_fwd_workspace_size), MOE_ERR_HIP.  The workspace is
- * scratch owned by the caller; its contents after the call are undefined.
+ * scratch owned by the caller; its contents after the call are undefined
+ * (besides tile tables and quantised operands it holds the float32 partial
+ * tiles of a down GEMM whose last round of tiles is split along K, up to
+ * 64 MiB).  Results are deterministic: the same inputs give the same bits.
  * offsets[E] must equal rows (the device reads the per-expert counts).
  * ---------------------------------------------------------------------- */
 typedef struct moe_mlp_fwd_args {
