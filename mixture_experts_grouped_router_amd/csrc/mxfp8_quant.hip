@@ -34,14 +34,14 @@ __device__ __forceinline__ uint32_t amax8(const uint4 v) {
   return a;
 }
 
-// Row-wise: 4 consecutive lanes own one block of 32 along a row; every
-// thread keeps U independent 16-byte loads in flight.
+// Row-wise with row-major scales [rows, cols / 32]: 4 consecutive lanes own
+// one block of 32 along a row; every thread keeps U independent 16-byte
+// loads in flight.
 constexpr int kRowsUnroll = 4;
 
-template <bool TILED>
 __global__ __launch_bounds__(256) void mx_rows_kernel(
-    const uint4* __restrict__ src, int64_t n_chunks, FastDiv bpr,
-    uint32_t nks, uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const uint4* __restrict__ src, int64_t n_chunks,
+    uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int64_t S = (int64_t)gridDim.x * blockDim.x;
   // n_chunks and S are multiples of 4: groups of 4 lanes stay aligned to
   // blocks and are either wholly in range or wholly out
@@ -62,17 +62,61 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(
       const int s = e8m0_exp_from_bf16_amax(a);
       if (c < n_chunks) {
         codes[c] = e4m3x8_hw(v[u], s);
-        if ((c & 3) == 0) {
-          const uint32_t b = (uint32_t)(c >> 2);   // block index < 2^31
-          uint32_t off = b;
-          if (TILED) {
-            const uint32_t r = fastdiv(b, bpr);
-            off = mx_tile_off(r, b - r * bpr.d, nks);
-          }
-          scales[off] = (uint8_t)(s + 127);
-        }
+        if ((c & 3) == 0) scales[c >> 2] = (uint8_t)(s + 127);
       }
     }
+  }
+}
+
+// Row-wise into the GEMM scale layout: a block covers 32 rows x 256 values
+// (two K steps of 128).  Wave w takes rows 8w .. 8w+7; lane l row 8w + l/8
+// and, for load u, chunk 8u + l%8 of the window, so the 8 lanes of a row
+// read 128 contiguous bytes and 4 consecutive lanes hold one block of 32.
+// The block's scale bytes (32 rows x 2 steps x 4 blocks) are gathered in
+// LDS and leave as whole 128-byte lines, one per step (in the GEMM layout
+// the 32 rows x 4 blocks of one step are one line); single-byte stores
+// scattered over those lines cost the HBM-bound pass ~15% extra write
+// traffic.  Rows past the end of the last group get the scale of an
+// all-zero block (storage covers rows rounded up to 32).
+constexpr int kTiledWin = 32;   // 16-byte chunks per window (256 values)
+
+__global__ __launch_bounds__(256) void mx_rows_tiled_kernel(
+    const uint4* __restrict__ src, int64_t rows, int cols8, int nwin,
+    uint32_t nks, uint2* __restrict__ codes, uint32_t* __restrict__ scales) {
+  __shared__ uint32_t sc[64];   // [step][row]: the 4 block scales of a step
+  const int64_t g = blockIdx.x / nwin;
+  const int win = (int)(blockIdx.x - g * nwin);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int rr = 8 * wave + (lane >> 3);
+  const int64_t row = g * 32 + rr;
+  const bool rv = row < rows;
+  const int cw0 = win * kTiledWin;
+  const uint4* srow = src + row * cols8;
+  uint4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = cw0 + 8 * u + (lane & 7);
+    v[u] = (rv && c < cols8) ? ld_nt(srow + c) : make_uint4(0, 0, 0, 0);
+  }
+  uint8_t* scb = reinterpret_cast<uint8_t*>(sc);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = cw0 + 8 * u + (lane & 7);
+    uint32_t a = amax8(v[u]);
+    a = umax(a, __shfl_xor(a, 1, 64));
+    a = umax(a, __shfl_xor(a, 2, 64));
+    const int s = e8m0_exp_from_bf16_amax(a);
+    if (rv && c < cols8) codes[row * cols8 + c] = e4m3x8_hw(v[u], s);
+    if ((lane & 3) == 0) {
+      const int blk = (8 * u + (lane & 7)) >> 2;   // block of the window
+      scb[((blk >> 2) * 32 + rr) * 4 + (blk & 3)] = (uint8_t)(s + 127);
+    }
+  }
+  __syncthreads();
+  if (t < 64) {
+    const int step = t >> 5;
+    if (cw0 + 16 * step < cols8)
+      scales[(g * nks + 2 * win + step) * 32 + (t & 31)] = sc[t];
   }
 }
 
@@ -324,18 +368,25 @@ hipError_t launch_mx_quant_rows(const void* src, int64_t rows, int64_t cols,
   int64_t blocks = (n_chunks + 256 * kRowsUnroll - 1) / (256 * kRowsUnroll);
   if (blocks > 65536) blocks = 65536;
   if (n_chunks / 4 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const FastDiv bpr = make_fastdiv((uint32_t)(cols / 32));
   const uint32_t nks = (uint32_t)(cols / 128);
   KernelScope ks("mxfp8_quantize_rows", stream);
-  if (tiled)
-    hipLaunchKernelGGL(mx_rows_kernel<true>, dim3((unsigned)blocks), dim3(256),
-                       0, stream, static_cast<const uint4*>(src), n_chunks,
-                       bpr, nks, reinterpret_cast<uint2*>(codes), scales);
-  else
-    hipLaunchKernelGGL(mx_rows_kernel<false>, dim3((unsigned)blocks),
-                       dim3(256), 0, stream, static_cast<const uint4*>(src),
-                       n_chunks, bpr, nks, reinterpret_cast<uint2*>(codes),
-                       scales);
+  if (tiled) {
+    // cols is a multiple of 128 (whole K steps); scales 4-byte aligned
+    if (cols % 128 != 0 || reinterpret_cast<uintptr_t>(scales) % 4 != 0)
+      return hipErrorInvalidValue;
+    const int cols8 = (int)(cols / 8);
+    const int nwin = (cols8 + kTiledWin - 1) / kTiledWin;
+    const int64_t nblk = (rows + 31) / 32 * nwin;
+    if (nblk >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mx_rows_tiled_kernel, dim3((unsigned)nblk), dim3(256),
+                       0, stream, static_cast<const uint4*>(src), rows, cols8,
+                       nwin, nks, reinterpret_cast<uint2*>(codes),
+                       reinterpret_cast<uint32_t*>(scales));
+  } else {
+    hipLaunchKernelGGL(mx_rows_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, static_cast<const uint4*>(src), n_chunks,
+                       reinterpret_cast<uint2*>(codes), scales);
+  }
   return hipGetLastError();
 }
 
