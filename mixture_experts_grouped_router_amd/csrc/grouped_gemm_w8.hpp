@@ -312,10 +312,12 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16_t{};
 
   const int nk = sr.ke - sr.ks;
-  // 6 LDS reads and 8 MFMAs per slice; the next step's A loads go out one
-  // per MFMA over the first slice, its B loads over the second
+  // 6 LDS reads and 8 MFMAs per slice; the next step's A loads go out two
+  // per MFMA in the first slice, its B loads in the second
+  // (two loads per MFMA: Mixtral-shaped down GEMM 1.771 -> 1.750 ms,
+  // against one per MFMA and against all eight in the first slice)
   auto slice_sched = [&](int kk) {
-    if (kk <= 1) sched_vmem_reads_mfma<4, 6, 8, 1>();
+    if (kk <= 1) sched_vmem_reads_mfma<4, 6, 8, 2>();
     else sched_reads_mfma<6, 8>();
   };
 
