@@ -324,6 +324,7 @@ MLP_CASES = [
     (64, 64, 64, 4, 1, 0.0),        # tiles larger than the problem
     (300, 2112, 192, 4, 2, 1.2),    # H > 2048: the four-wave gate/up GEMM
     (512, 256, 8192, 4, 2, 0.0),    # down GEMM's tiles split 4 ways along K
+    (700, 256, 8192, 8, 2, 1.2),    # the same with empty and one-row experts
 ]
 
 
@@ -537,6 +538,7 @@ MX_CASES = [
     (700, 256, 384, 5, 2, 1.2),     # ragged M tails, odd K-step count (3)
     (900, 384, 128, 16, 4, 1.2),    # many experts, some empty
     (512, 256, 8192, 4, 2, 0.0),    # down GEMM's last tiles split along K
+    (700, 256, 8192, 8, 2, 1.2),    # the same with empty and one-row experts
 ]
 
 
