@@ -1258,12 +1258,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // the first slice and B over the second), spread between the MFMAs.
   constexpr bool kSplit = MOE_LOAD_SPLIT && kSl >= 3;
   constexpr int kVmA = 8 + (P == P_FP8 ? 8 : 0);   // A loads (+ scales)
-  // bf16 dgrad (N-contiguous B): three per MFMA (Qwen3-shaped long-sequence
-  // dgrad of the down projection with the SwiGLU backward 1.356 -> 1.329 ms;
-  // the wgrads, both operands M-contiguous, stay at one: 1.546 -> 1.57 ms
+  // bf16 dgrad (N-contiguous B): six per MFMA (Qwen3-shaped long-sequence
+  // dgrad of the down projection with the SwiGLU backward: one 1.356, three
+  // 1.329-1.334, six 1.311-1.313 ms; the 8-bit modes did best with three);
+  // the wgrads, both operands M-contiguous, stay at one (1.546 -> 1.57 ms
   // with three)
   constexpr int kVpm = P != P_BF16 ? kLoadVpm8
-                       : (LA == KC && LB == MC) ? 3 : kLoadVpmBf16;
+                       : (LA == KC && LB == MC) ? 6 : kLoadVpmBf16;
   constexpr int kVmB = 8;
   auto slice_sched = [&](int kk) {
     if (kk == 0) {
