@@ -956,10 +956,10 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
 constexpr int kMaxSplit = 8;
 constexpr int kMaxSplitSlotsX = 32;   // slots (and counters) per XCD
 // Fewest K steps of a split work-group: the partial tile's round trip and
-// the cache write-back / invalidate of the hand-over cost tens of
-// microseconds per tile, which only long K ranges repay (the Mixtral-shaped
-// down GEMM, K = 14336, gains 7%; the Qwen3-shaped gate/up GEMM, K = 2048,
-// loses 3% with 16-step ranges).
+// the cache write-back / invalidate of the hand-over cost ~15 microseconds
+// per split tile, which only long K ranges repay (the Mixtral-shaped down
+// GEMM, K = 14336, gains 10% in bf16 and 4% in MXFP8; the Qwen3-shaped
+// gate/up GEMM, K = 2048, loses 3% with 16-step ranges).
 constexpr int kMinSplitSteps = 32;
 
 struct SplitRange {
