@@ -259,7 +259,15 @@ __device__ __forceinline__ void epilogue_w8_swiglu(const Params& p,
   }
 }
 
-template <int EPI>
+// BAR_END: the stage barrier follows the step's last MFMA (the next stage's
+// loads get the whole step to land) instead of sitting halfway through the
+// last slice (the next stage's first fragment reads overlap the last four
+// MFMAs).  Long K loops gain from the former (Mixtral-shaped down GEMM,
+// K = 14336: 1.679 -> 1.656 ms), short ones from the latter (Qwen3-shaped
+// down GEMM, K = 768: 0.525 -> 0.532 ms with BAR_END).
+constexpr int kW8BarEndMinSteps = 64;
+
+template <int EPI, bool BAR_END>
 __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU, "forward epilogues");
   using S = Shape8<EPI>;
@@ -348,14 +356,23 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
       slice_sched(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
-    mfma_bf16_w8<0>(cur, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    nxt.load(na, nb, 0, wm, wn, lane);
-    mfma_bf16_w8<1>(cur, acc);
-    cur = nxt;
-    sched_reads_mfma<6, 4>();
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (BAR_END) {
+      mfma_bf16_w8<2>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      nxt.load(na, nb, 0, wm, wn, lane);
+      cur = nxt;
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      mfma_bf16_w8<0>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      nxt.load(na, nb, 0, wm, wn, lane);
+      mfma_bf16_w8<1>(cur, acc);
+      cur = nxt;
+      sched_reads_mfma<6, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   for (int kt = 0; kt < nk2; kt += 2) {
     step(sA0, sB0, sA1, sB1, kt + 1);
@@ -379,8 +396,12 @@ hipError_t launch_w8(const char* name, const Params& p, int grid,
                      hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   KernelScope ks(name, stream);
-  hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI>), dim3(grid),
-                     dim3(kThreads8), 0, stream, p);
+  if ((p.K + 63) / 64 >= kW8BarEndMinSteps)
+    hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, true>), dim3(grid),
+                       dim3(kThreads8), 0, stream, p);
+  else
+    hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, false>), dim3(grid),
+                       dim3(kThreads8), 0, stream, p);
   return hipGetLastError();
 }
 
