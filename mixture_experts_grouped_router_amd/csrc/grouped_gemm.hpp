@@ -513,15 +513,17 @@ struct Frags<P_FP8> {
 template <int HALF>
 __device__ __forceinline__ void mfma_bf16(const Frags<P_BF16>& f,
                                           f32x16_t (&acc)[4][4]) {
-  if constexpr (HALF != 1) {
+  if constexpr (HALF == 0 || HALF == 2 || HALF == 3) {
     MOE_MFMA_BF(0, 0, f.a0, f.b0); MOE_MFMA_BF(0, 1, f.a0, f.b1);
     MOE_MFMA_BF(0, 2, f.a0, f.b2); MOE_MFMA_BF(0, 3, f.a0, f.b3);
     MOE_MFMA_BF(1, 0, f.a1, f.b0); MOE_MFMA_BF(1, 1, f.a1, f.b1);
     MOE_MFMA_BF(1, 2, f.a1, f.b2); MOE_MFMA_BF(1, 3, f.a1, f.b3);
   }
-  if constexpr (HALF != 0) {
+  if constexpr (HALF == 1 || HALF == 2 || HALF == 3) {
     MOE_MFMA_BF(2, 0, f.a2, f.b0); MOE_MFMA_BF(2, 1, f.a2, f.b1);
     MOE_MFMA_BF(2, 2, f.a2, f.b2); MOE_MFMA_BF(2, 3, f.a2, f.b3);
+  }
+  if constexpr (HALF == 1 || HALF == 2 || HALF == 4) {
     MOE_MFMA_BF(3, 0, f.a3, f.b0); MOE_MFMA_BF(3, 1, f.a3, f.b1);
     MOE_MFMA_BF(3, 2, f.a3, f.b2); MOE_MFMA_BF(3, 3, f.a3, f.b3);
   }
@@ -539,15 +541,17 @@ __device__ __forceinline__ void mfma_fp8(const Frags<P_FP8>& f,
                                          const uint32_t (&sa)[4],
                                          const uint32_t (&sb)[4],
                                          f32x16_t (&acc)[4][4]) {
-  if constexpr (HALF != 1) {
+  if constexpr (HALF == 0 || HALF == 2 || HALF == 3) {
     MOE_MFMA_MX(0, 0, f.a0, f.b0); MOE_MFMA_MX(0, 1, f.a0, f.b1);
     MOE_MFMA_MX(0, 2, f.a0, f.b2); MOE_MFMA_MX(0, 3, f.a0, f.b3);
     MOE_MFMA_MX(1, 0, f.a1, f.b0); MOE_MFMA_MX(1, 1, f.a1, f.b1);
     MOE_MFMA_MX(1, 2, f.a1, f.b2); MOE_MFMA_MX(1, 3, f.a1, f.b3);
   }
-  if constexpr (HALF != 0) {
+  if constexpr (HALF == 1 || HALF == 2 || HALF == 3) {
     MOE_MFMA_MX(2, 0, f.a2, f.b0); MOE_MFMA_MX(2, 1, f.a2, f.b1);
     MOE_MFMA_MX(2, 2, f.a2, f.b2); MOE_MFMA_MX(2, 3, f.a2, f.b3);
+  }
+  if constexpr (HALF == 1 || HALF == 2 || HALF == 4) {
     MOE_MFMA_MX(3, 0, f.a3, f.b0); MOE_MFMA_MX(3, 1, f.a3, f.b1);
     MOE_MFMA_MX(3, 2, f.a3, f.b2); MOE_MFMA_MX(3, 3, f.a3, f.b3);
   }
@@ -1265,6 +1269,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // with three)
   constexpr int kVpm = P != P_BF16 ? kLoadVpm8
                        : (LA == KC && LB == MC) ? 6 : kLoadVpmBf16;
+  // 8-bit modes: the stage barrier after three of the last slice's four
+  // row blocks of MFMAs, the last four overlapping the next stage's first
+  // fragment reads (MXFP8 gate/up 1.888-1.903 -> 1.857-1.868 ms, down
+  // 0.962-0.966 -> 0.947); bf16: after the last MFMA (three quarters:
+  // gate/up 3.229 -> 3.236 ms)
+  constexpr bool kBarQ = P != P_BF16;
   constexpr int kVmB = 8;
   auto slice_sched = [&](int kk) {
     if (kk == 0) {
@@ -1303,8 +1313,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // at the barrier.  An odd last step computes on a zero stage.  The trip
   // has no branches, so the MFMAs stay where they are written.
   // Fragment reads run one K slice ahead of the MFMAs; the barrier that
-  // publishes the next stage follows the step's last MFMA, so the next
-  // stage's loads get the whole step to land.  (With the barrier halfway
+  // publishes the next stage follows the step's last MFMA (8-bit modes: the
+  // last slice's third row block of MFMAs), so the next stage's loads get
+  // (nearly) the whole step to land.  (With the barrier halfway
   // through the last slice, the next stage's first fragment reads overlapped
   // the MFMAs after it but the loads had half a slice less: Mixtral-shaped
   // gate/up 3.298 -> 3.206 ms, MXFP8 gate/up 1.963 -> 1.911 ms, MXFP8 down
@@ -1330,13 +1341,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       // keep the scheduler from hoisting later slices' reads (registers)
       __builtin_amdgcn_sched_barrier(0);
     }
-    Mma<PF>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    fload(nxt, sA1, sB1, 0);
-    cur = nxt;
-    take_scales();
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kBarQ) {
+      Mma<PF>::template run<kSl - 1, 3>(cur, sa_cur, sb_cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      fload(nxt, sA1, sB1, 0);
+      Mma<PF>::template run<kSl - 1, 4>(cur, sa_cur, sb_cur, acc);
+      cur = nxt;
+      take_scales();
+      sched_reads_mfma<kNR, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      Mma<PF>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      fload(nxt, sA1, sB1, 0);
+      cur = nxt;
+      take_scales();
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     // stage kt+1 from buffers 1 while stage kt+2 loads into buffers 0 (a
     // step past nk2 is never computed; its zero loads are harmless)
@@ -1351,13 +1374,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       slice_sched(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
-    Mma<PF>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    fload(nxt, sA0, sB0, 0);
-    cur = nxt;
-    take_scales();
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kBarQ) {
+      Mma<PF>::template run<kSl - 1, 3>(cur, sa_cur, sb_cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      fload(nxt, sA0, sB0, 0);
+      Mma<PF>::template run<kSl - 1, 4>(cur, sa_cur, sb_cur, acc);
+      cur = nxt;
+      take_scales();
+      sched_reads_mfma<kNR, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      Mma<PF>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      fload(nxt, sA0, sB0, 0);
+      cur = nxt;
+      take_scales();
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // every wave is past its last LDS read of the operand stages (and every
