@@ -283,15 +283,10 @@ def grouped_mlp_bwd(dz_perm, x_perm, w_gu, w_dn, w_perm, offsets
         dZ = _as_f64(dz_perm[lo:hi])
         h1 = X @ Wgu.T
         g, u = h1[:, :F], h1[:, F:]
-        s = sigmoid(g)
-        sg = g * s
         we = w[lo:hi, None]
-        A = we * sg * u
+        A = we * (g * sigmoid(g)) * u
         dA = dZ @ Wdn
-        dg = dA * we * u * (s * (1.0 + g * (1.0 - s)))
-        du = dA * we * sg
-        dh1 = np.concatenate([dg, du], axis=1)
-        dw_perm[lo:hi] = (dA * sg * u).sum(axis=1)
+        dh1, dw_perm[lo:hi] = swiglu_bwd(dA, g, u, we)
         dw_dn[e] = dZ.T @ A
         dw_gu[e] = dh1.T @ X
         dx[lo:hi] = dh1 @ Wgu
@@ -445,11 +440,21 @@ def padded_offsets(offsets: np.ndarray) -> np.ndarray:
     return p
 
 
-def _mx_rows(a):
+def _mx_rows_np(a):
     """quantise row-wise then dequantise (the value the MX GEMM consumes)."""
     c, s = mxfp8_quantize_rows(a)
     R, C = c.shape
     return mx_dequantize_blocks(c.reshape(R, C // 32, 32), s).reshape(R, C)
+
+
+def _mx_rows(a):
+    """_mx_rows_np; bf16 input (uint16 bit patterns, e.g. whole expert
+    weights) goes through the C statement of the same rule in mx_fast.c,
+    which is pinned bit for bit against the numpy one."""
+    if np.asarray(a).dtype == np.uint16:
+        from oracle import mx_fast
+        return mx_fast.dequantized_rows(a)
+    return _mx_rows_np(a)
 
 
 def _mx_segment_cols(a, lo, hi):
@@ -461,6 +466,49 @@ def _mx_segment_cols(a, lo, hi):
     t = np.zeros((C, npad))
     t[:, :n] = sub.T
     return _mx_rows(t)[:, :n].T
+
+
+def mx_gemm_rows(a, b) -> np.ndarray:
+    """C = Q_K(a) Q_K(b)^T for a [M, K], b [N, K]: both operands quantised
+    with blocks of 32 along their rows (the GEMM's K), then multiplied
+    (float64).  The forward GEMMs: x_perm W_gu^T and A W_dn^T (R8)."""
+    return _mx_rows(a) @ _mx_rows(b).T
+
+
+def mx_dgrad(dy, w) -> np.ndarray:
+    """dX = Q_N(dY) Q_N(W) for dY [M, N], W [N, K]: the contraction runs over
+    N, so dY is quantised along its rows and W along its columns (blocks of
+    32 consecutive rows of W).  dgrad of the down projection (N = H) and of
+    the gate/up projection (N = 2F) (R8)."""
+    return mx_gemm_rows(dy, np.asarray(w).T)
+
+
+def mx_wgrad_segment(a, b, offsets, e: int) -> np.ndarray:
+    """dW = Q_tok(A_e)^T Q_tok(B_e) for the rows [offsets[e], offsets[e+1])
+    of a [R, M] and b [R, N]: the contraction runs over the expert's tokens,
+    so both are quantised along tokens with blocks restarting at the
+    segment's first row, the last block zero-padded (R8).  [M, N] float64;
+    zeros for an expert without tokens."""
+    lo, hi = int(offsets[e]), int(offsets[e + 1])
+    a = np.asarray(a)
+    b = np.asarray(b)
+    if hi == lo:
+        return np.zeros((a.shape[1], b.shape[1]), dtype=f64)
+    n = hi - lo
+    return _mx_segment_cols(a, lo, hi).T @ _mx_segment_cols(b, lo, hi)
+
+
+def swiglu_bwd(da, g, u, w) -> Tuple[np.ndarray, np.ndarray]:
+    """SwiGLU backward of a = w * silu(g) * u (R5, R6), with s = sigmoid(g):
+      dg = dA * w * u * s * (1 + g * (1 - s))      (d silu / dg)
+      du = dA * w * silu(g)
+      dw = sum_f dA * silu(g) * u
+    Returns (dH1 = [dg, du] along columns, dw per row)."""
+    s = sigmoid(g)
+    sg = g * s
+    dg = da * w * u * (s * (1.0 + g * (1.0 - s)))
+    du = da * w * sg
+    return np.concatenate([dg, du], axis=1), (da * sg * u).sum(axis=1)
 
 
 def grouped_mlp_fwd_mxfp8(x_perm, w_gu, w_dn, w_perm, offsets,
@@ -479,14 +527,10 @@ def grouped_mlp_fwd_mxfp8(x_perm, w_gu, w_dn, w_perm, offsets,
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
-        Xq = _mx_rows(x_perm[lo:hi])
-        Wguq = _mx_rows(w_gu[e])
-        h1 = Xq @ Wguq.T
+        h1 = mx_gemm_rows(x_perm[lo:hi], w_gu[e])
         g, u = h1[:, :F], h1[:, F:]
         a = w[lo:hi, None] * silu(g) * u
-        Aq = _mx_rows(a)
-        Wdnq = _mx_rows(w_dn[e])
-        z[lo:hi] = Aq @ Wdnq.T
+        z[lo:hi] = mx_gemm_rows(a, w_dn[e])
         if keep:
             a_all[lo:hi] = a
             h1_all[lo:hi] = h1
@@ -515,27 +559,24 @@ def grouped_mlp_bwd_mxfp8(dz_perm, x_perm, w_gu, w_dn, w_perm, offsets
     dw_perm = np.zeros(rows)
     dw_gu = np.zeros((E, 2 * F, H))
     dw_dn = np.zeros((E, H, F))
+    X = _as_f64(x_perm)
+    dZ = _as_f64(dz_perm)
+    A = np.zeros((rows, F))
+    dh1 = np.zeros((rows, 2 * F))
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
             continue
-        X = _as_f64(x_perm[lo:hi])
-        h1 = _mx_rows(X) @ _mx_rows(w_gu[e]).T
+        h1 = mx_gemm_rows(X[lo:hi], w_gu[e])
         g, u = h1[:, :F], h1[:, F:]
-        s = sigmoid(g)
-        sg = g * s
         we = w[lo:hi, None]
-        A = we * sg * u
-        dZ = _as_f64(dz_perm[lo:hi])
-        dA = _mx_rows(dZ) @ _mx_rows(_as_f64(w_dn[e]).T).T
-        dg = dA * we * u * (s * (1.0 + g * (1.0 - s)))
-        du = dA * we * sg
-        dh1 = np.concatenate([dg, du], axis=1)
-        dw_perm[lo:hi] = (dA * sg * u).sum(axis=1)
-        n = hi - lo
-        dw_dn[e] = _mx_segment_cols(dZ, 0, n).T @ _mx_segment_cols(A, 0, n)
-        dw_gu[e] = _mx_segment_cols(dh1, 0, n).T @ _mx_segment_cols(X, 0, n)
-        dx[lo:hi] = _mx_rows(dh1) @ _mx_rows(_as_f64(w_gu[e]).T).T
+        A[lo:hi] = we * silu(g) * u
+        dA = mx_dgrad(dZ[lo:hi], w_dn[e])
+        dh1[lo:hi], dw_perm[lo:hi] = swiglu_bwd(dA, g, u, we)
+        dx[lo:hi] = mx_dgrad(dh1[lo:hi], w_gu[e])
+    for e in range(E):
+        dw_dn[e] = mx_wgrad_segment(dZ, A, offsets, e)
+        dw_gu[e] = mx_wgrad_segment(dh1, X, offsets, e)
     return {"dx_perm": dx, "dw_perm": dw_perm, "dw_gu": dw_gu,
             "dw_dn": dw_dn}
 
@@ -568,7 +609,8 @@ def grouped_mlp_fwd_fp8_tensor(x_perm, w_gu, w_dn, w_perm, offsets
                                ) -> Dict[str, np.ndarray]:
     """R11 forward: x_perm, each W_gu[e] and W_dn[e] quantised per tensor;
     h1 = Xq Wq^T (float64 on the dequantised values); A = w * silu(g) * u
-    rounded to bf16, quantised per tensor over all rows; z = Aq Wdnq^T."""
+    rounded to bf16, quantised per tensor over all rows; z = Aq Wdnq^T.
+    Returns z, h1, A (rounded to bf16; all float64) and A's scale."""
     E = len(offsets) - 1
     rows = np.asarray(x_perm).shape[0]
     F = np.asarray(w_gu).shape[1] // 2
@@ -577,6 +619,7 @@ def grouped_mlp_fwd_fp8_tensor(x_perm, w_gu, w_dn, w_perm, offsets
     xc, xs = fp8_tensor_quantize(x_perm)
     X = fp8_tensor_dequantize(xc, xs)
     a = np.zeros((rows, F), dtype=f64)
+    h1_all = np.zeros((rows, 2 * F), dtype=f64)
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi == lo:
@@ -585,6 +628,7 @@ def grouped_mlp_fwd_fp8_tensor(x_perm, w_gu, w_dn, w_perm, offsets
         h1 = X[lo:hi] @ fp8_tensor_dequantize(wc, ws).T
         g, u = h1[:, :F], h1[:, F:]
         a[lo:hi] = w[lo:hi, None] * silu(g) * u
+        h1_all[lo:hi] = h1
     a16 = _as_f64(_bf16_round_bits(a))
     ac, as_ = fp8_tensor_quantize(a16)
     A = fp8_tensor_dequantize(ac, as_)
@@ -595,7 +639,7 @@ def grouped_mlp_fwd_fp8_tensor(x_perm, w_gu, w_dn, w_perm, offsets
             continue
         wc, ws = fp8_tensor_quantize(w_dn[e])
         z[lo:hi] = A[lo:hi] @ fp8_tensor_dequantize(wc, ws).T
-    return {"z": z, "a": a16, "a_scale": as_}
+    return {"z": z, "a": a16, "a_scale": as_, "h1": h1_all}
 
 
 def _bf16_round_bits(a: np.ndarray) -> np.ndarray:

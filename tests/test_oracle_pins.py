@@ -509,6 +509,266 @@ def test_mx_gemm_equals_exact_gemm_on_representable_operands():
     np.testing.assert_allclose(Xq @ Wq.T, X @ W.T, rtol=0, atol=0)
 
 
+# ------------------------------------------- MXFP8 layer: exact, by direction
+# Operands built block by block from E4M3 codes times a power of two, so that
+# quantising along the intended axis returns them unchanged (the round trip
+# pinned above), while quantising along the other axis does not (blocks of
+# that axis mix scales 2^0 .. 2^-4, so small values lose bits).  Values are
+# multiples of 2^-13 below 448, products multiples of 2^-26 below 2^18: every
+# float64 sum of up to 2^8 products is exact in any order.
+
+def _rep_blocks(rng, n_blocks, valid=32, smin=-4, smax=0):
+    """[n_blocks, 32] float64: each block decode(code) * 2^s with one element
+    of magnitude in [256, 448] * 2^s among its first ``valid`` entries and
+    zeros past them."""
+    mags = rng.integers(0, 0x7F, size=(n_blocks, 32))
+    top = rng.integers(0x78, 0x7F, size=n_blocks)
+    mags = np.minimum(mags, top[:, None])
+    mags[np.arange(n_blocks), rng.integers(0, valid, size=n_blocks)] = top
+    codes = mags | (rng.integers(0, 2, size=mags.shape) << 7)
+    s = rng.integers(smin, smax + 1, size=n_blocks)
+    v = np.ldexp(O.e4m3_decode(codes), s[:, None])
+    v[:, valid:] = 0.0
+    return v
+
+
+def _rep_rows(rng, R, C):
+    """[R, C] exactly representable with blocks of 32 along each row."""
+    return _rep_blocks(rng, R * (C // 32)).reshape(R, C)
+
+
+def _rep_token_segments(rng, offsets, C):
+    """[rows, C], exactly representable along tokens with blocks restarting
+    at every offsets[e] (last block of a segment zero-padded)."""
+    rows = int(offsets[-1])
+    out = np.zeros((rows, C))
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        for b0 in range(lo, hi, 32):
+            n = min(32, hi - b0)
+            out[b0:b0 + n] = _rep_blocks(rng, C, valid=n)[:, :n].T
+    return out
+
+
+def _q_rows(a):
+    c, s = O.mxfp8_quantize_rows(a)
+    R, C = c.shape
+    return O.mx_dequantize_blocks(c.reshape(R, C // 32, 32), s).reshape(R, C)
+
+
+def test_rep_operands_are_direction_sensitive():
+    """The constructions above are exact along their axis only."""
+    rng = _rng(60)
+    a = _rep_rows(rng, 64, 128)
+    assert np.array_equal(_q_rows(a), a)
+    assert not np.array_equal(_q_rows(a.T).T, a)
+    off = np.array([0, 20, 20, 75])
+    t = _rep_token_segments(rng, off, 64)
+    for e in range(3):
+        lo, hi = off[e], off[e + 1]
+        n = hi - lo
+        pad = np.zeros((-(-n // 32) * 32, 64))
+        pad[:n] = t[lo:hi]
+        assert np.array_equal(_q_rows(pad.T).T[:n], t[lo:hi])
+    glob = np.zeros((96, 64))
+    glob[:75] = t
+    assert not np.array_equal(_q_rows(glob.T).T[:75], t)
+
+
+def test_mx_gemm_rows_exact_along_k_only():
+    rng = _rng(61)
+    a = _rep_rows(rng, 64, 256)
+    b = _rep_rows(rng, 32, 256)
+    c = O.mx_gemm_rows(a, b)
+    np.testing.assert_array_equal(c, a @ b.T)
+    # the same operands blocked along M / N would not give the product
+    wrong = _q_rows(a.T).T @ _q_rows(b.T).T.T
+    assert O.rel_err(wrong, a @ b.T) > 1e-4
+
+
+def test_mx_dgrad_quantises_weights_along_n():
+    """dX = Q_N(dY) Q_N(W), W [N, K]: W representable along N (its columns)
+    but not along K gives the exact product; the row-wise reading of W
+    (blocks along K) does not."""
+    rng = _rng(62)
+    N, K, M = 128, 96, 64
+    dy = _rep_rows(rng, M, N)
+    w = _rep_rows(rng, K, N).T.copy()          # [N, K], exact along N
+    np.testing.assert_array_equal(O.mx_dgrad(dy, w), dy @ w)
+    assert not np.array_equal(_q_rows(w), w)
+    assert O.rel_err(_q_rows(dy) @ _q_rows(w), dy @ w) > 1e-4
+
+
+@pytest.mark.parametrize("offsets", [[0, 20, 20, 75], [0, 0, 45, 77, 160]])
+def test_mx_wgrad_segment_blocks_restart_at_segment(offsets):
+    """Token-direction blocks start at each expert's first row (here rows 20
+    and 45 and 77: inside a 32-row block of the whole tensor) and the last
+    block is zero-padded; operands representable in those blocks give the
+    exact dW, and blocks aligned to the whole tensor would not."""
+    rng = _rng(63)
+    off = np.array(offsets)
+    M, N = 64, 96
+    a = _rep_token_segments(rng, off, M)
+    b = _rep_token_segments(rng, off, N)
+    rows = int(off[-1])
+    ga = np.zeros((-(-rows // 32) * 32, M))
+    gb = np.zeros((ga.shape[0], N))
+    ga[:rows], gb[:rows] = a, b
+    qa, qb = _q_rows(ga.T).T[:rows], _q_rows(gb.T).T[:rows]
+    moved = False
+    for e in range(len(off) - 1):
+        lo, hi = off[e], off[e + 1]
+        dw = O.mx_wgrad_segment(a, b, off, e)
+        np.testing.assert_array_equal(dw, a[lo:hi].T @ b[lo:hi])
+        if hi > lo and lo % 32:
+            moved |= O.rel_err(qa[lo:hi].T @ qb[lo:hi],
+                               a[lo:hi].T @ b[lo:hi]) > 1e-4
+        if hi == lo:
+            assert dw.shape == (M, N) and not dw.any()
+    assert moved
+
+
+def test_mxfp8_forward_exact_h1_and_quantised_a():
+    """grouped_mlp_fwd_mxfp8 with x_perm and W_gu representable along H and
+    W_dn representable along F (none of them along the other axis):
+      h1 equals the float64 product exactly;
+      a equals w * silu(g) * u on that h1;
+      z equals Q_F(a) W_dn^T (a quantised row-wise, W_dn unchanged).
+    Quantising W_dn along H, skipping A's quantisation or quantising x_perm
+    along tokens fails by far more than rounding."""
+    rng = _rng(64)
+    E, H, F = 3, 128, 64
+    off = np.array([0, 37, 37, 90])
+    rows = int(off[-1])
+    x = _rep_rows(rng, rows, H)
+    w_gu = np.stack([_rep_rows(rng, 2 * F, H) for _ in range(E)])
+    w_dn = np.stack([_rep_rows(rng, H, F) for _ in range(E)])
+    for e in range(E):
+        assert not np.array_equal(_q_rows(w_dn[e].T).T, w_dn[e])
+    wp = np.ldexp(1.0, -rng.integers(0, 3, size=rows))  # 1, 1/2, 1/4
+    out = O.grouped_mlp_fwd_mxfp8(x, w_gu, w_dn, wp, off, keep=True)
+    z_unq = np.zeros_like(out["z"])
+    z_dn_h = np.zeros_like(out["z"])
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        h1 = x[lo:hi] @ w_gu[e].T
+        np.testing.assert_array_equal(out["h1"][lo:hi], h1)
+        g, u = h1[:, :F], h1[:, F:]
+        np.testing.assert_array_equal(out["a"][lo:hi],
+                                      wp[lo:hi, None] * O.silu(g) * u)
+        aq = _q_rows(out["a"][lo:hi])
+        np.testing.assert_allclose(out["z"][lo:hi], aq @ w_dn[e].T,
+                                   rtol=1e-12, atol=0)
+        z_unq[lo:hi] = out["a"][lo:hi] @ w_dn[e].T
+        z_dn_h[lo:hi] = aq @ _q_rows(w_dn[e].T).T.T
+    assert O.rel_err(z_unq, out["z"]) > 1e-3
+    assert O.rel_err(z_dn_h, out["z"]) > 1e-3
+    assert not out["z"][0:0].size and not out["z"][37:37].size
+
+
+def test_mxfp8_backward_is_its_pinned_gemms():
+    """grouped_mlp_bwd_mxfp8 composes the pinned pieces expert by expert:
+    dA = mx_dgrad(dZ, W_dn), (dH1, dw) = swiglu_bwd (pinned through the
+    float64 backward's finite differences), dX = mx_dgrad(dH1, W_gu),
+    dW_dn = mx_wgrad_segment(dZ, A), dW_gu = mx_wgrad_segment(dH1, X), with
+    (g, u) and A from the MXFP8 forward.  An expert boundary at row 21 falls
+    inside a 32-row block; an expert without tokens gets dW = 0."""
+    rng = _rng(65)
+    E, H, F = 4, 64, 32
+    off = np.array([0, 21, 21, 58, 70])
+    rows = int(off[-1])
+    x = rng.standard_normal((rows, H))
+    w_gu = 0.1 * rng.standard_normal((E, 2 * F, H))
+    w_dn = 0.1 * rng.standard_normal((E, H, F))
+    wp = rng.random(rows)
+    dz = rng.standard_normal((rows, H))
+    got = O.grouped_mlp_bwd_mxfp8(dz, x, w_gu, w_dn, wp, off)
+    fwd = O.grouped_mlp_fwd_mxfp8(x, w_gu, w_dn, wp, off, keep=True)
+    dh1 = np.zeros((rows, 2 * F))
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            assert not got["dw_dn"][e].any() and not got["dw_gu"][e].any()
+            continue
+        g, u = fwd["h1"][lo:hi, :F], fwd["h1"][lo:hi, F:]
+        da = O.mx_dgrad(dz[lo:hi], w_dn[e])
+        dh1[lo:hi], dwp = O.swiglu_bwd(da, g, u, wp[lo:hi, None])
+        np.testing.assert_array_equal(got["dw_perm"][lo:hi], dwp)
+        np.testing.assert_array_equal(got["dx_perm"][lo:hi],
+                                      O.mx_dgrad(dh1[lo:hi], w_gu[e]))
+    for e in range(E):
+        np.testing.assert_array_equal(
+            got["dw_dn"][e], O.mx_wgrad_segment(dz, fwd["a"], off, e))
+        np.testing.assert_array_equal(
+            got["dw_gu"][e], O.mx_wgrad_segment(dh1, x, off, e))
+
+
+def test_swiglu_bwd_matches_finite_differences():
+    """d/d(g, u, w) of sum(dA * w * silu(g) * u), central differences."""
+    rng = _rng(66)
+    g, u = rng.standard_normal((5, 7)), rng.standard_normal((5, 7))
+    w = rng.random((5, 1)) + 0.5
+    da = rng.standard_normal((5, 7))
+    dh1, dw = O.swiglu_bwd(da, g, u, w)
+
+    def f(g_, u_, w_):
+        return float((da * w_ * O.silu(g_) * u_).sum())
+
+    h = 1e-6
+    for (i, j) in [(0, 0), (2, 3), (4, 6)]:
+        for which, col in ((0, j), (1, 7 + j)):
+            gp, up, gm, um = g.copy(), u.copy(), g.copy(), u.copy()
+            if which == 0:
+                gp[i, j] += h
+                gm[i, j] -= h
+            else:
+                up[i, j] += h
+                um[i, j] -= h
+            fd = (f(gp, up, w) - f(gm, um, w)) / (2 * h)
+            assert abs(fd - dh1[i, col]) < 1e-7 * max(1.0, abs(fd))
+        wp_, wm_ = w.copy(), w.copy()
+        wp_[i] += h
+        wm_[i] -= h
+    for i in range(5):
+        wp_, wm_ = w.copy(), w.copy()
+        wp_[i] += h
+        wm_[i] -= h
+        fd = (f(g, u, wp_) - f(g, u, wm_)) / (2 * h)
+        assert abs(fd - dw[i]) < 1e-7 * max(1.0, abs(fd))
+
+
+def test_mx_fast_equals_numpy_oracle_every_bf16_and_scale():
+    """The C restatement of R7 (oracle/mx_fast.c) gives the numpy oracle's
+    codes and scales bit for bit: every finite bf16 pattern, in blocks whose
+    amax sets each reachable scale exponent, plus all-zero and tiny
+    blocks."""
+    from oracle import mx_fast
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]
+    rng = np.random.default_rng(68)
+    rows = []
+    for be in range(0, 255, 3):          # block amax exponent field
+        perm = rng.permutation(bits)[: 31 * 64]
+        blk = perm.reshape(64, 31)
+        lead = np.full((64, 1), (be << 7) | 0x7F, dtype=np.uint16)
+        # keep the other values at or below the lead's magnitude
+        mag = blk & 0x7FFF
+        blk = np.where(mag > (lead & 0x7FFF), blk & 0x8000, blk)
+        rows.append(np.concatenate([lead, blk.astype(np.uint16)], axis=1))
+    rows.append(np.zeros((2, 32), dtype=np.uint16))
+    rows.append(np.full((2, 32), 0x8001, dtype=np.uint16))
+    a = np.concatenate(rows, axis=0).reshape(-1, 64)
+    c, s = mx_fast.quantize_rows(a)
+    cw, sw = O.mxfp8_quantize_rows(a)
+    np.testing.assert_array_equal(c, cw)
+    np.testing.assert_array_equal(s, sw)
+    np.testing.assert_array_equal(mx_fast.dequantized_rows(a), O._mx_rows_np(a))
+    np.testing.assert_array_equal(O._mx_rows(a), O._mx_rows_np(a))
+    assert len(np.unique(sw)) > 80
+
+
 def test_mxfp8_layer_close_to_unquantised():
     """Sanity: the MXFP8 layer tracks the unquantised one (normwise error of
     a few percent, the format's resolution), and equals it exactly when every
@@ -703,6 +963,62 @@ def test_bf16_round_bits_matches_torch():
     v = rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))
     np.testing.assert_array_equal(O._bf16_round_bits(v),
                                   bf16_bits(v.astype(np.float32)))
+
+
+def _fp8_rep(rng, shape, k):
+    """decode(code) * 2^k with one element at +448 * 2^k (so the tensor's
+    scale amax / 448 is exactly 2^k) and many small codes, subnormals
+    included."""
+    c = rng.integers(0, 0x7E, size=shape)
+    c = np.where(rng.random(shape) < 0.3, rng.integers(1, 0x10, size=shape),
+                 c)
+    c = c | (rng.integers(0, 2, size=shape) << 7)
+    v = np.ldexp(O.e4m3_decode(c), k)
+    v.reshape(-1)[rng.integers(0, v.size)] = 448.0 * 2.0 ** k
+    return v
+
+
+def test_fp8_tensor_layer_scales_per_expert_weight_and_whole_a():
+    """R11 on operands whose per-tensor scales are powers of two: x_perm at
+    2^-8, expert 0's weights at 2^-8 and expert 1's at 2^-16 (amax 2^8 apart,
+    small codes in both).  Each expert's own scale leaves its weights exact,
+    so h1 is the exact float64 product; one scale shared by both experts
+    would flush expert 1's small values.  A is the bf16 SwiGLU output and z
+    its quantisation with ONE scale over all rows (amax of the whole bf16
+    A) times W_dn[e]."""
+    rng = _rng(67)
+    E, H, F = 2, 64, 32
+    off = np.array([0, 23, 50])
+    rows = int(off[-1])
+    x = _fp8_rep(rng, (rows, H), -8)
+    w_gu = np.stack([_fp8_rep(rng, (2 * F, H), -8),
+                     _fp8_rep(rng, (2 * F, H), -16)])
+    w_dn = np.stack([_fp8_rep(rng, (H, F), -8), _fp8_rep(rng, (H, F), -16)])
+    wp = rng.random(rows).astype(np.float32).astype(np.float64)
+    out = O.grouped_mlp_fwd_fp8_tensor(x.astype(np.float32), w_gu, w_dn, wp,
+                                       off)
+    shared = np.ldexp(O.e4m3_decode(O.e4m3_encode(w_gu[1] / 2.0 ** -8)), -8)
+    assert not np.array_equal(shared, w_gu[1])     # flushes under 2^-8
+    a16 = np.zeros((rows, F))
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        h1 = x[lo:hi] @ w_gu[e].T
+        np.testing.assert_array_equal(out["h1"][lo:hi], h1)
+        a16[lo:hi] = bf16_to_f64(O._bf16_round_bits(
+            wp[lo:hi, None] * O.silu(h1[:, :F]) * h1[:, F:]))
+    np.testing.assert_array_equal(out["a"], a16)
+    ac, as_ = O.fp8_tensor_quantize(a16)
+    assert as_ == np.float32(np.abs(a16).max() / 448.0)
+    aq = O.fp8_tensor_dequantize(ac, as_)
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        np.testing.assert_allclose(out["z"][lo:hi], aq[lo:hi] @ w_dn[e].T,
+                                   rtol=1e-12, atol=0)
+        # a per-expert A scale would change expert 1's rows
+        pc, ps = O.fp8_tensor_quantize(a16[lo:hi])
+        if e == 1:
+            assert O.rel_err(O.fp8_tensor_dequantize(pc, ps) @ w_dn[e].T,
+                             out["z"][lo:hi]) > 1e-3
 
 
 def test_fp8_tensor_layer_close_to_unquantised():
