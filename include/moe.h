@@ -31,10 +31,12 @@
  *  - Errors: argument validation happens on the host before anything is
  *    enqueued; a failing call enqueues nothing and returns a non-zero
  *    moe_status_t.  moe_last_error() gives a thread-local message.
- *    Data errors that only the device can see (an expert id outside [0, E))
- *    are recorded in the context's device status word (first error wins),
- *    the offending pair is skipped (its row_map entry is -1), and
- *    moe_ctx_check_device_status reports them.
+ *    Data errors that only the device can see are recorded in the context's
+ *    device status word (first error wins) and moe_ctx_check_device_status
+ *    reports them: an expert id outside [0, E) (the offending pair is
+ *    skipped, its row_map entry is -1), and a per-expert offsets array that
+ *    does not run non-decreasing from 0 to the row count (the call then
+ *    processes no expert; its outputs are undefined).
  *  - Threading: a context may be used by one host thread at a time.
  *  - Determinism: no floating-point atomics; results are bitwise
  *    reproducible for the same inputs and sizes.
@@ -73,6 +75,7 @@ typedef enum moe_mx_axis {
 /* Device status codes written by kernels into the context status word. */
 #define MOE_DEVERR_NONE 0
 #define MOE_DEVERR_EXPERT_ID 1     /* topk_idx entry outside [0, E) */
+#define MOE_DEVERR_OFFSETS 2       /* offsets not non-decreasing from 0 to rows */
 
 typedef struct moe_ctx* moe_ctx_t;
 
@@ -284,11 +287,33 @@ moe_status_t moe_unpermute_probs_grad(moe_ctx_t ctx, const float* dw_perm,
  *           P_s = sum_{s'<s} ceil(n_s'/32)*32.  codes [cols, ld],
  *           scales [cols, ld/32], ld = rows + 32*n_seg rounded up to 32
  *           (columns past the last segment are left untouched).
+ *           seg_offsets not running non-decreasing from 0 to rows: nothing
+ *           is written and MOE_DEVERR_OFFSETS is recorded.
  * ---------------------------------------------------------------------- */
 moe_status_t mxfp8_quantize(moe_ctx_t ctx, const void* src, int64_t batch,
                             int64_t rows, int64_t cols, moe_mx_axis_t axis,
                             const int32_t* seg_offsets, int32_t n_seg,
                             uint8_t* codes, uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------
+ * mxfp8_quantize_f32 -- row-wise MXFP8 quantisation of float32 values.
+ * [PG1, section "Reducing memory and quantisation cost": the SwiGLU output
+ *  is quantised inside the fused grouped MLP; PG2, section "2) Model size
+ *  and activation memory": one scale per block of 32 consecutive values.]
+ * The same rule as mxfp8_quantize ROWWISE, applied to float32 input with the
+ * encoder that moe_grouped_mlp_fwd's MXFP8 gate/up epilogue runs on its
+ * float32 ScaledSwiGLU output (so the epilogue's rounding can be checked
+ * value by value): per block of 32, s = floor(log2 max|v|) - 8 clamped to
+ * [-127, 127], scale byte s + 127, code = E4M3 of v * 2^-s (round to
+ * nearest even, saturating at +-448, sign kept).  Values must be finite.
+ *  src float32 [rows, cols] (cols % 32 == 0, 16-byte aligned)
+ *  codes uint8 [rows, cols] (8-byte aligned), scales uint8 [rows, cols/32]
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED (cols % 32, alignment),
+ * MOE_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+moe_status_t mxfp8_quantize_f32(moe_ctx_t ctx, const float* src, int64_t rows,
+                                int64_t cols, uint8_t* codes, uint8_t* scales,
+                                void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_fp8_tensor_quantize -- tensor-scaled FP8 quantisation.
@@ -327,7 +352,8 @@ moe_status_t moe_fp8_tensor_quantize(moe_ctx_t ctx, const void* src,
  * per 32, as in mxfp8_quantize ROWWISE); the GEMMs use the gfx950 scaled
  * MFMA with float32 accumulation; a is quantised from float32 in the gate/up
  * epilogue; h1_save / a_save hold the unquantised float32 values rounded to
- * bf16.
+ * bf16, and a_q_save / a_s_save (optional) A's E4M3 codes and row-major E8M0
+ * scales as the down GEMM consumes them.
  * FP8 tensor-scaled (MOE_PREC_FP8_TENSOR, forward only) [PG1, section
  * "Reducing memory and quantisation cost"; PG2, section "3) Quantisation
  * overhead in low-precision training": 8-bit elements with scales from
@@ -347,7 +373,9 @@ moe_status_t moe_fp8_tensor_quantize(moe_ctx_t ctx, const void* src,
  * (besides tile tables and quantised operands it holds the float32 partial
  * tiles of a down GEMM whose last round of tiles is split along K, up to
  * 64 MiB).  Results are deterministic: the same inputs give the same bits.
- * offsets[E] must equal rows (the device reads the per-expert counts).
+ * offsets must run non-decreasing from 0 to rows; the device checks this
+ * (it reads the per-expert counts) and otherwise records MOE_DEVERR_OFFSETS
+ * and runs no GEMM tile (outputs undefined).
  * ---------------------------------------------------------------------- */
 typedef struct moe_mlp_fwd_args {
   int32_t E, H, F;               /* experts, hidden, expert FFN size */
@@ -373,6 +401,10 @@ typedef struct moe_mlp_fwd_args {
   void* a_save;                  /* out, nullable: bf16 [rows, F] */
   void* ws;                      /* workspace */
   size_t ws_bytes;
+  /* MXFP8 only, out, nullable: A's E4M3 codes [rows, F] (16-byte aligned)
+   * and E8M0 scales [rows, F/32] (row-major), as the down GEMM reads them */
+  uint8_t* a_q_save;
+  uint8_t* a_s_save;
 } moe_mlp_fwd_args;
 
 moe_status_t moe_grouped_mlp_fwd_workspace_size(const moe_mlp_fwd_args* args,

@@ -22,6 +22,7 @@ __all__ = [
     "ROWWISE", "COLWISE", "moe_router_logits", "moe_router_bwd",
     "moe_route_topk", "moe_permute", "moe_gather_rows",
     "moe_unpermute", "moe_unpermute_probs_grad", "mxfp8_quantize",
+    "mxfp8_quantize_f32",
     "moe_grouped_mlp_fwd", "moe_expert_loop_mlp_fwd", "moe_grouped_mlp_bwd",
     "check_device_status",
     "mx_segment_ld", "set_kernel_timing", "reset_kernel_timing",
@@ -59,6 +60,7 @@ class _FwdArgs(ctypes.Structure):
         ("w_perm", _c_p), ("offsets", _c_p),
         ("z_perm", _c_p), ("h1_save", _c_p), ("a_save", _c_p),
         ("ws", _c_p), ("ws_bytes", _c_sz),
+        ("a_q_save", _c_p), ("a_s_save", _c_p),
     ]
 
 
@@ -102,6 +104,7 @@ _SIGS = {
                                  _c_p],
     "mxfp8_quantize": [_c_p, _c_p, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_p,
                        _c_i32, _c_p, _c_p, _c_p],
+    "mxfp8_quantize_f32": [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p],
     "moe_grouped_mlp_fwd_workspace_size": [ctypes.POINTER(_FwdArgs),
                                            ctypes.POINTER(_c_sz)],
     "moe_grouped_mlp_fwd": [_c_p, ctypes.POINTER(_FwdArgs), _c_p],
@@ -442,6 +445,20 @@ def mxfp8_quantize(src: torch.Tensor, axis: int = ROWWISE,
     return codes, scales
 
 
+def mxfp8_quantize_f32(src: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Row-wise MXFP8 codes + E8M0 scales of a float32 tensor [rows, cols]
+    (the encoder of the MXFP8 gate/up epilogue)."""
+    rows, cols = src.shape
+    _need(src, torch.float32, (rows, cols), "src")
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=src.device)
+    scales = torch.empty((rows, cols // 32), dtype=torch.uint8,
+                         device=src.device)
+    lib = load_library()
+    _check(lib.mxfp8_quantize_f32(_context(src.device), _ptr(src), rows, cols,
+                                  _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
 def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gu: torch.Tensor,
                         w_dn: torch.Tensor, offsets: torch.Tensor,
                         w_perm: Optional[torch.Tensor] = None,
@@ -452,9 +469,12 @@ def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gu: torch.Tensor,
                         save: bool = False,
                         out: Optional[torch.Tensor] = None,
                         ws: Optional[torch.Tensor] = None,
+                        save_a_codes: bool = False,
                         ) -> Dict[str, torch.Tensor]:
     """Grouped gate/up GEMM -> ScaledSwiGLU x w -> grouped down GEMM.
-    Returns {"z": bf16 [rows, H]} (+ "h1", "a" when save=True)."""
+    Returns {"z": bf16 [rows, H]} (+ "h1", "a" when save=True; + "a_q",
+    "a_s", A's MXFP8 codes and row-major scales, when save_a_codes=True in
+    MXFP8 mode)."""
     E, F2, H = w_gu.shape
     F = F2 // 2
     rows = x_perm.shape[0]
@@ -490,6 +510,11 @@ def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gu: torch.Tensor,
     args.offsets = _ptr(offsets)
     args.z_perm = _ptr(z)
     args.h1_save, args.a_save = _ptr(h1), _ptr(a)
+    aq = as_ = None
+    if save_a_codes:
+        aq = torch.empty((rows, F), dtype=torch.uint8, device=dev)
+        as_ = torch.empty((rows, F // 32), dtype=torch.uint8, device=dev)
+        args.a_q_save, args.a_s_save = _ptr(aq), _ptr(as_)
     lib = load_library()
     nbytes = _c_sz(0)
     _check(lib.moe_grouped_mlp_fwd_workspace_size(ctypes.byref(args),
@@ -503,6 +528,8 @@ def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gu: torch.Tensor,
     res = {"z": z}
     if save:
         res["h1"], res["a"] = h1, a
+    if save_a_codes:
+        res["a_q"], res["a_s"] = aq, as_
     return res
 
 

@@ -306,17 +306,19 @@ moe_status_t moe_permute_workspace_size(int64_t T, int32_t E, int32_t k,
   return ok();
 }
 
-moe_status_t moe_permute(moe_ctx_t ctx, const void* x,
-                         const int32_t* topk_idx, const float* topk_w,
-                         int64_t T, int32_t H, int32_t E, int32_t k,
-                         moe_precision_t out_prec, void* x_perm,
-                         uint8_t* x_perm_scale, float* w_perm,
-                         int32_t* row_map, int32_t* src_row,
-                         int32_t* split_sizes, int32_t* offsets, void* ws,
-                         size_t ws_bytes, void* stream) {
-  moe_status_t s = check_ctx(ctx);
-  if (s != MOE_OK) return s;
-  TimerGuard tg(ctx);
+}  // extern "C"
+
+namespace {
+
+// moe_permute after the context check; ws holds ws_bytes of scratch.
+moe_status_t permute_impl(moe_ctx_t ctx, const void* x,
+                          const int32_t* topk_idx, const float* topk_w,
+                          int64_t T, int32_t H, int32_t E, int32_t k,
+                          moe_precision_t out_prec, void* x_perm,
+                          uint8_t* x_perm_scale, float* w_perm,
+                          int32_t* row_map, int32_t* src_row,
+                          int32_t* split_sizes, int32_t* offsets, void* ws,
+                          size_t ws_bytes, void* stream) {
   MOE_REQUIRE(T >= 0 && H >= 1 && E >= 1 && k >= 1 && k <= E,
               MOE_ERR_INVALID_ARG, "bad sizes (T=%lld H=%d E=%d k=%d)",
               (long long)T, H, E, k);
@@ -358,6 +360,26 @@ moe_status_t moe_permute(moe_ctx_t ctx, const void* x,
                                    static_cast<uint8_t*>(x_perm), x_perm_scale,
                                    w_perm, st);
   return hip_status(e, "permute gather");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_permute(moe_ctx_t ctx, const void* x,
+                         const int32_t* topk_idx, const float* topk_w,
+                         int64_t T, int32_t H, int32_t E, int32_t k,
+                         moe_precision_t out_prec, void* x_perm,
+                         uint8_t* x_perm_scale, float* w_perm,
+                         int32_t* row_map, int32_t* src_row,
+                         int32_t* split_sizes, int32_t* offsets, void* ws,
+                         size_t ws_bytes, void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
+  return permute_impl(ctx, x, topk_idx, topk_w, T, H, E, k, out_prec, x_perm,
+                      x_perm_scale, w_perm, row_map, src_row, split_sizes,
+                      offsets, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_gather_rows(moe_ctx_t ctx, const void* src,
@@ -451,8 +473,26 @@ moe_status_t mxfp8_quantize(moe_ctx_t ctx, const void* src, int64_t batch,
   const int64_t ld = (rows + 32 * (int64_t)n_seg + 31) / 32 * 32;
   return hip_status(moe::launch_mx_quant_segments(src, rows, cols, seg_offsets,
                                                   n_seg, 32, ld, codes, scales,
-                                                  st),
+                                                  ctx->status, st),
                     "mxfp8 segments");
+}
+
+moe_status_t mxfp8_quantize_f32(moe_ctx_t ctx, const float* src, int64_t rows,
+                                int64_t cols, uint8_t* codes, uint8_t* scales,
+                                void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
+  MOE_REQUIRE(rows >= 0 && cols >= 0, MOE_ERR_INVALID_ARG, "negative size");
+  MOE_REQUIRE(cols % 32 == 0, MOE_ERR_UNSUPPORTED, "cols %% 32 != 0");
+  if (rows * cols == 0) return ok();
+  MOE_REQUIRE(src && codes && scales, MOE_ERR_INVALID_ARG, "null pointer");
+  MOE_REQUIRE(aligned16(src) && (reinterpret_cast<uintptr_t>(codes) & 7) == 0,
+              MOE_ERR_UNSUPPORTED,
+              "src must be 16-byte and codes 8-byte aligned");
+  return hip_status(moe::launch_mx_quant_f32(src, rows * cols, codes, scales,
+                                             as_stream(stream)),
+                    "mxfp8 f32 rows");
 }
 
 namespace {
@@ -531,6 +571,10 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
   if (mx)
     MOE_REQUIRE(al4(a->x_perm_scale) && al4(a->w_gu_s) && al4(a->w_dn_s),
                 MOE_ERR_UNSUPPORTED, "MXFP8 scale arrays must be 4-byte aligned");
+  MOE_REQUIRE(mx || (!a->a_q_save && !a->a_s_save), MOE_ERR_INVALID_ARG,
+              "a_q_save / a_s_save are MXFP8 outputs");
+  MOE_REQUIRE(aligned16(a->a_q_save), MOE_ERR_UNSUPPORTED,
+              "a_q_save must be 16-byte aligned");
   MOE_REQUIRE(aligned16(a->x_perm) && aligned16(a->w_gu) &&
                   aligned16(a->w_dn) && aligned16(a->w_gu_q) &&
                   aligned16(a->w_dn_q) && aligned16(a->z_perm),
@@ -547,12 +591,13 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
     e = moe::launch_mlp_fwd_fp8t(a->E, a->H, a->F, a->rows, a->x_perm,
                                  a->w_gu, a->w_dn, a->w_perm, a->offsets,
                                  a->z_perm, a->h1_save, a->a_save, a->ws,
-                                 ctx->cu_count, as_stream(stream));
+                                 ctx->cu_count, ctx->status,
+                                 as_stream(stream));
   } else if (!mx) {
     e = moe::launch_mlp_fwd_bf16(a->E, a->H, a->F, a->rows, a->x_perm, a->w_gu,
                                  a->w_dn, a->w_perm, a->offsets, a->z_perm,
                                  a->h1_save, a->a_save, a->ws, ctx->cu_count,
-                                 as_stream(stream));
+                                 ctx->status, as_stream(stream));
   } else {
     const bool xq = a->x_perm_scale != nullptr;
     e = moe::launch_mlp_fwd_mx(
@@ -560,7 +605,8 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
         xq ? static_cast<const uint8_t*>(a->x_perm) : nullptr,
         a->x_perm_scale, a->w_gu, a->w_dn, a->w_gu_q, a->w_gu_s, a->w_dn_q,
         a->w_dn_s, a->w_perm, a->offsets, a->z_perm, a->h1_save, a->a_save,
-        a->ws, ctx->cu_count, as_stream(stream));
+        a->a_q_save, a->a_s_save, a->ws, ctx->cu_count, ctx->status,
+        as_stream(stream));
   }
   return hip_status(e, "grouped_mlp_fwd");
 }
@@ -670,13 +716,13 @@ moe_status_t moe_grouped_mlp_bwd(moe_ctx_t ctx, const moe_mlp_bwd_args* a,
                                  a->w_dn, a->w_perm, a->offsets, a->h1_save,
                                  a->a_save, a->dz_perm, a->dx_perm, a->dw_gu,
                                  a->dw_dn, a->w_perm ? a->dw_perm : nullptr,
-                                 a->ws, as_stream(stream));
+                                 a->ws, ctx->status, as_stream(stream));
   else
     e = moe::launch_mlp_bwd_mx(a->E, a->H, a->F, a->rows, a->x_perm, a->w_gu,
                                a->w_dn, a->w_perm, a->offsets, a->h1_save,
                                a->a_save, a->dz_perm, a->dx_perm, a->dw_gu,
                                a->dw_dn, a->w_perm ? a->dw_perm : nullptr,
-                               a->ws, as_stream(stream));
+                               a->ws, ctx->status, as_stream(stream));
   return hip_status(e, "grouped_mlp_bwd");
 }
 

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "mx_codec.hpp"
+#include "offsets_check.hpp"
 
 namespace moe {
 
@@ -80,6 +81,32 @@ __device__ __forceinline__ uint32_t e4m3x4_hw_f32(float a, float b, float c,
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, scale, true);
   return sat_e4m3x4(__builtin_bit_cast(uint32_t, r));
 }
+// MXFP8 encoding of one block of 32 float32 values held by a quad of lanes
+// (4 consecutive lanes starting at a multiple of 4, 8 consecutive values
+// each, in lane order): the block exponent from the quad's amax (two lane
+// swaps, float32 magnitudes compared as integers), then the E4M3 codes with
+// the scaled conversion and the 448 fix-up.  Every lane of the quad must be
+// active.  Returns the lane's 8 codes (first value in the low byte) and the
+// block exponent in *sx.
+__device__ __forceinline__ uint2 mx_quad_encode_f32(const float (&v)[8],
+                                                    int* sx) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t a = __float_as_uint(v[c]) & 0x7fffffffu;
+    am = am > a ? am : a;
+  }
+  uint32_t o = __shfl_xor(am, 1, 64);
+  am = am > o ? am : o;
+  o = __shfl_xor(am, 2, 64);
+  am = am > o ? am : o;
+  const int s = e8m0_exp_from_f32_amax(am);
+  const float sc = mx_scale_f32(s);
+  *sx = s;
+  return make_uint2(e4m3x4_hw_f32(v[0], v[1], v[2], v[3], sc),
+                    e4m3x4_hw_f32(v[4], v[5], v[6], v[7], sc));
+}
+
 // 8 bf16 (one uint4) -> 8 E4M3 codes with block exponent s
 __device__ __forceinline__ uint2 e4m3x8_hw(const uint4 v, int s) {
   const float sc = mx_scale_f32(s);
@@ -89,6 +116,25 @@ __device__ __forceinline__ uint2 e4m3x8_hw(const uint4 v, int s) {
 // Record the first device-side data error (first error wins).
 __device__ __forceinline__ void report_error(int32_t* status, int32_t code) {
   if (status) atomicCAS(status, 0, code);
+}
+
+// Block-wide check of a segment offsets array [n_seg + 1] against `rows`,
+// by a block of exactly 256 threads, thread t taking pairs 4t .. 4t+3
+// (n_seg <= 1024).  Every thread of the block must call it; all get the
+// same answer.  An invalid array is recorded once, by block (0, 0, 0).
+__device__ __forceinline__ bool seg_offsets_ok(const int32_t* off, int n_seg,
+                                               int64_t rows, int t,
+                                               int32_t* status) {
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sg = 4 * t + i;
+    if (sg < n_seg) ok = ok && offsets_pair_ok(off, sg, n_seg, rows);
+  }
+  const bool bad = __syncthreads_or(!ok);
+  if (bad && t == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    report_error(status, kDevErrOffsets);
+  return !bad;
 }
 
 // Exclusive scan of one int per thread over a block of exactly 256 threads.

@@ -19,14 +19,21 @@ namespace gg {
 
 // Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn.
 // With unit = BM it counts GEMM tiles; with unit = tn = P it gives the
-// offsets of segments padded to multiples of P.
+// offsets of segments padded to multiples of P.  Offsets that do not run
+// non-decreasing from 0 to rows give an all-zero table (no tile runs, every
+// padded segment is empty) and record MOE_DEVERR_OFFSETS.
 __global__ __launch_bounds__(1024) void tile_table_kernel(
-    const int32_t* __restrict__ offsets, int E, int unit, int tn,
-    int32_t* __restrict__ tile_start, uint32_t* __restrict__ zero,
-    int nzero) {
+    const int32_t* __restrict__ offsets, int E, int64_t rows, int unit,
+    int tn, int32_t* __restrict__ tile_start, uint32_t* __restrict__ zero,
+    int nzero, int32_t* status) {
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
   for (int i = e; i < nzero; i += 1024) zero[i] = 0u;
+  if (__syncthreads_or(e < E && !offsets_pair_ok(offsets, e, E, rows))) {
+    for (int i = e; i <= E; i += 1024) tile_start[i] = 0;
+    if (e == 0) report_error(status, kDevErrOffsets);
+    return;
+  }
   const int lane = e & 63, wid = e >> 6;
   int32_t v = 0;
   if (e < E) v = ((offsets[e + 1] - offsets[e] + unit - 1) / unit) * tn;
@@ -53,10 +60,18 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(
 }
 
 // Rank of expert e by rows, descending; equal counts keep index order.
+// Invalid offsets (as in tile_table_kernel) give order[] = -1: every tile of
+// a RAGGED_K launch then exits without work.
 __global__ __launch_bounds__(1024) void expert_order_kernel(
-    const int32_t* __restrict__ offsets, int E, int32_t* __restrict__ order) {
+    const int32_t* __restrict__ offsets, int E, int64_t rows,
+    int32_t* __restrict__ order, int32_t* status) {
   __shared__ int32_t len[1024];
   const int e = threadIdx.x;
+  if (__syncthreads_or(e < E && !offsets_pair_ok(offsets, e, E, rows))) {
+    if (e < E) order[e] = -1;
+    if (e == 0) report_error(status, kDevErrOffsets);
+    return;
+  }
   if (e < E) len[e] = offsets[e + 1] - offsets[e];
   __syncthreads();
   if (e >= E) return;
@@ -82,28 +97,31 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(
 }
 }  // namespace
 
-hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
-                             int32_t* tile_start, hipStream_t stream,
-                             uint32_t* zero, int nzero) {
+hipError_t launch_tile_table(const int32_t* offsets, int E, int64_t rows,
+                             int tn, int32_t* tile_start, int32_t* status,
+                             hipStream_t stream, uint32_t* zero, int nzero) {
   KernelScope ks("tile_table", stream);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
-                     offsets, E, BM, tn, tile_start, zero, nzero);
+                     offsets, E, rows, BM, tn, tile_start, zero, nzero,
+                     status);
   return hipGetLastError();
 }
 
-hipError_t launch_expert_order(const int32_t* offsets, int E, int32_t* order,
+hipError_t launch_expert_order(const int32_t* offsets, int E, int64_t rows,
+                               int32_t* order, int32_t* status,
                                hipStream_t stream) {
   KernelScope ks("expert_order", stream);
   hipLaunchKernelGGL(expert_order_kernel, dim3(1), dim3(1024), 0, stream,
-                     offsets, E, order);
+                     offsets, E, rows, order, status);
   return hipGetLastError();
 }
 
-hipError_t launch_padded_offsets(const int32_t* offsets, int E, int pad,
-                                 int32_t* poff, hipStream_t stream) {
+hipError_t launch_padded_offsets(const int32_t* offsets, int E, int64_t rows,
+                                 int pad, int32_t* poff, int32_t* status,
+                                 hipStream_t stream) {
   KernelScope ks("padded_offsets", stream);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
-                     offsets, E, pad, pad, poff, nullptr, 0);
+                     offsets, E, rows, pad, pad, poff, nullptr, 0, status);
   return hipGetLastError();
 }
 
@@ -137,7 +155,8 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
                                const void* w_dn, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
-                               int cu_count, hipStream_t stream) {
+                               int cu_count, int32_t* status,
+                               hipStream_t stream) {
   char* wp = static_cast<char*>(ws);
   int32_t* ts1 = reinterpret_cast<int32_t*>(wp);
   wp += align256((size_t)(E + 1) * sizeof(int32_t));
@@ -156,9 +175,10 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
 
   const int tn1 = (F + BN / 2 - 1) / (BN / 2);
   const int tn2 = (H + BN - 1) / BN;
-  hipError_t err = launch_tile_table(offsets, E, tn1, ts1, stream, split_cnt,
-                                     kXcds * sx);
-  if (err == hipSuccess) err = launch_tile_table(offsets, E, tn2, ts2, stream);
+  hipError_t err = launch_tile_table(offsets, E, rows, tn1, ts1, status,
+                                     stream, split_cnt, kXcds * sx);
+  if (err == hipSuccess)
+    err = launch_tile_table(offsets, E, rows, tn2, ts2, status, stream);
   if (err != hipSuccess) return err;
   // the eight-wave GEMMs split the last, partly filled round of tiles
   auto set_split = [&](Params& p) {
@@ -232,7 +252,8 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
                                const int32_t* offsets, const void* h1_save,
                                const void* a_save, const void* dz_perm,
                                void* dx_perm, void* dw_gu, void* dw_dn,
-                               float* dw_perm, void* ws, hipStream_t stream) {
+                               float* dw_perm, void* ws, int32_t* status,
+                               hipStream_t stream) {
   const int tnf = (F + BN - 1) / BN;
   const int tnh = (H + BN - 1) / BN;
   char* wp = static_cast<char*>(ws);
@@ -248,8 +269,9 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
 
   hipError_t err;
   if (rows > 0) {
-    err = launch_tile_table(offsets, E, tnf, ts_f, stream);
-    if (err == hipSuccess) err = launch_tile_table(offsets, E, tnh, ts_h, stream);
+    err = launch_tile_table(offsets, E, rows, tnf, ts_f, status, stream);
+    if (err == hipSuccess)
+      err = launch_tile_table(offsets, E, rows, tnh, ts_h, status, stream);
     if (err != hipSuccess) return err;
     // dgrad2 + SwiGLU backward: dA = dZ W_dn[e]  (B = W_dn[e] [H, F] is
     // N-contiguous)
@@ -301,7 +323,7 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     if (err != hipSuccess) return err;
   }
   // wgrad2: dW_dn[e] [H, F] = dZ_e^T A_e   (K = rows of expert e)
-  err = launch_expert_order(offsets, E, order, stream);
+  err = launch_expert_order(offsets, E, rows, order, status, stream);
   if (err != hipSuccess) return err;
   {
     Params p{};

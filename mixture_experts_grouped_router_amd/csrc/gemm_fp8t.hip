@@ -65,7 +65,8 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
                                const void* w_dn, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
-                               int cu_count, hipStream_t stream) {
+                               int cu_count, int32_t* status,
+                               hipStream_t stream) {
   Fp8tWs w = carve(ws, E, H, F, rows, a_save == nullptr);
   uint16_t* a = a_save ? static_cast<uint16_t*>(a_save) : w.a;
   // scale slots: 0 x, 1 A, 2 + e W_gu[e], 2 + E + e W_dn[e]
@@ -88,9 +89,10 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   const int tn1 = (F + BN / 2 - 1) / (BN / 2);
   const int tn2 = (H + BN - 1) / BN;
   if (err == hipSuccess)
-    err = launch_tile_table(offsets, E, tn1, w.ts1, stream, w.split_cnt,
-                            kXcds * w.split_x);
-  if (err == hipSuccess) err = launch_tile_table(offsets, E, tn2, w.ts2, stream);
+    err = launch_tile_table(offsets, E, rows, tn1, w.ts1, status, stream,
+                            w.split_cnt, kXcds * w.split_x);
+  if (err == hipSuccess)
+    err = launch_tile_table(offsets, E, rows, tn2, w.ts2, status, stream);
   if (err != hipSuccess) return err;
 
   // gate/up + ScaledSwiGLU: A in bf16 (and its amax), (g, u) save optional

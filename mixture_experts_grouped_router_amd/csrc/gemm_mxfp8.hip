@@ -87,11 +87,14 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
                              const uint8_t* w_gu_s, const uint8_t* w_dn_q,
                              const uint8_t* w_dn_s, const float* w_perm,
                              const int32_t* offsets, void* z_perm,
-                             void* h1_save, void* a_save, void* ws,
-                             int cu_count, hipStream_t stream) {
+                             void* h1_save, void* a_save, uint8_t* a_q_save,
+                             uint8_t* a_s_save, void* ws, int cu_count,
+                             int32_t* status, hipStream_t stream) {
   const bool quant_x = xq == nullptr;
   const bool quant_w = w_gu_q == nullptr || w_dn_q == nullptr;
   MxFwdWs w = carve_fwd(ws, E, H, F, rows, quant_x, quant_w);
+  // A's codes go to the caller's buffer when it keeps them
+  if (a_q_save) w.aq = a_q_save;
   hipError_t err = hipSuccess;
   const int64_t ngu = (int64_t)E * 2 * F, ndn = (int64_t)E * H;  // rows
   if (quant_w) {
@@ -117,9 +120,10 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   if (err != hipSuccess) return err;
   const int tn1 = (F + BN / 2 - 1) / (BN / 2);
   const int tn2 = (H + BN - 1) / BN;
-  err = launch_tile_table(offsets, E, tn1, w.ts1, stream, w.split_cnt,
-                          kXcds * w.split_x);
-  if (err == hipSuccess) err = launch_tile_table(offsets, E, tn2, w.ts2, stream);
+  err = launch_tile_table(offsets, E, rows, tn1, w.ts1, status, stream,
+                          w.split_cnt, kXcds * w.split_x);
+  if (err == hipSuccess)
+    err = launch_tile_table(offsets, E, rows, tn2, w.ts2, status, stream);
   if (err != hipSuccess) return err;
 
   Params p1{};
@@ -146,6 +150,7 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p1.c2 = static_cast<uint16_t*>(h1_save);
   p1.cq = w.aq;
   p1.cs = w.as;
+  p1.cs_rm = a_s_save;
   p1.w = w_perm;
   p1.rows = rows;
   err = launch<P_FP8, KC, KC, RAGGED_M, EPI_SWIGLU_MX>(
@@ -311,16 +316,21 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
                              const int32_t* offsets, const void* h1_save,
                              const void* a_save, const void* dz_perm,
                              void* dx_perm, void* dw_gu, void* dw_dn,
-                             float* dw_perm, void* ws, hipStream_t stream) {
+                             float* dw_perm, void* ws, int32_t* status,
+                             hipStream_t stream) {
   MxBwdWs w = carve_bwd(ws, E, H, F, rows);
   const int tnf = (F + BN - 1) / BN;
   const int tnh = (H + BN - 1) / BN;
   const int F2 = 2 * F;
-  hipError_t err = launch_padded_offsets(offsets, E, kTokPad, w.poff, stream);
-  if (err == hipSuccess) err = launch_expert_order(offsets, E, w.order, stream);
+  hipError_t err = launch_padded_offsets(offsets, E, rows, kTokPad, w.poff,
+                                         status, stream);
+  if (err == hipSuccess)
+    err = launch_expert_order(offsets, E, rows, w.order, status, stream);
   if (rows > 0) {
-    if (err == hipSuccess) err = launch_tile_table(offsets, E, tnf, w.ts_f, stream);
-    if (err == hipSuccess) err = launch_tile_table(offsets, E, tnh, w.ts_h, stream);
+    if (err == hipSuccess)
+      err = launch_tile_table(offsets, E, rows, tnf, w.ts_f, status, stream);
+    if (err == hipSuccess)
+      err = launch_tile_table(offsets, E, rows, tnh, w.ts_h, status, stream);
     // operands of the two dgrad GEMMs
     if (err == hipSuccess)
       err = launch_mx_quant_rows(dz_perm, rows, H, w.dzq, w.dzs, stream,
@@ -399,16 +409,16 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
 
     // token-direction operands of the two wgrad GEMMs
     err = launch_mx_quant_segments(dz_perm, rows, H, offsets, E, kTokPad,
-                                   w.ld, w.dzt, w.dzts, stream, true);
+                                   w.ld, w.dzt, w.dzts, status, stream, true);
     if (err == hipSuccess)
       err = launch_mx_quant_segments(a_save, rows, F, offsets, E, kTokPad,
-                                     w.ld, w.at, w.ats, stream, true);
+                                     w.ld, w.at, w.ats, status, stream, true);
     if (err == hipSuccess)
       err = launch_mx_quant_segments(w.dh1, rows, F2, offsets, E, kTokPad,
-                                     w.ld, w.ht, w.hts, stream, true);
+                                     w.ld, w.ht, w.hts, status, stream, true);
     if (err == hipSuccess)
       err = launch_mx_quant_segments(x_perm, rows, H, offsets, E, kTokPad,
-                                     w.ld, w.xt, w.xts, stream, true);
+                                     w.ld, w.xt, w.xts, status, stream, true);
   }
   if (err != hipSuccess) return err;
   // wgrad: every expert gets a tile set; K = its padded token count (0 for

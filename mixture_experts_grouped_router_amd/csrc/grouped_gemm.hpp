@@ -154,6 +154,7 @@ struct Params {
   uint16_t* c2;               // SwiGLU epilogues: (g, u) save [rows, 2F]
   uint8_t* cq;                // EPI_SWIGLU_MX: A codes [rows, F]
   uint8_t* cs;                // EPI_SWIGLU_MX: A scales (GEMM layout)
+  uint8_t* cs_rm;             // EPI_SWIGLU_MX: optional row-major copy
   const uint16_t* h1;         // EPI_SWIGLU_BWD: saved (g, u) [rows, 2F]
   const float* w;             // routing weight per row (nullable -> 1)
   float* dw_part;             // EPI_SWIGLU_BWD: [tiles_n][rows]
@@ -241,6 +242,7 @@ __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
     if (L >= p.E * per_e) return false;
     const int rank = L / per_e;
     const int e = p.order[rank];
+    if (e < 0) return false;   // offsets were invalid: nothing runs
     const int local = L - rank * per_e;
     const int mt_e = p.tiles_m;
     // groups of kGroupN N-tiles, M tiles fastest inside a group
@@ -743,29 +745,16 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
         if constexpr (EPI == EPI_SWIGLU_MX) {
           // F % 128 == 0: blocks are whole; every lane takes part in the
           // quad reduction, rows past the expert just do not store
-          uint32_t am = 0;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const uint32_t a = __float_as_uint(v[c]) & 0x7fffffffu;
-            am = am > a ? am : a;
-          }
-          uint32_t o = __shfl_xor(am, 1, 64);
-          am = am > o ? am : o;
-          o = __shfl_xor(am, 2, 64);
-          am = am > o ? am : o;
-          const int sx = e8m0_exp_from_f32_amax(am);
-          const float sc = mx_scale_f32(sx);
-          uint32_t w8[2];
-#pragma unroll
-          for (int d = 0; d < 2; ++d)
-            w8[d] = e4m3x4_hw_f32(v[4 * d], v[4 * d + 1], v[4 * d + 2],
-                                  v[4 * d + 3], sc);
+          int sx;
+          const uint2 w8 = mx_quad_encode_f32(v, &sx);
           if (ok) {
-            *reinterpret_cast<uint2*>(p.cq + row * p.F + f) =
-                make_uint2(w8[0], w8[1]);
-            if ((c8 & 3) == 0)
+            *reinterpret_cast<uint2*>(p.cq + row * p.F + f) = w8;
+            if ((c8 & 3) == 0) {
               p.cs[mx_tile_off((uint32_t)row, (uint32_t)(f / 32),
                                (uint32_t)(p.F / 128))] = (uint8_t)(sx + 127);
+              if (p.cs_rm)
+                p.cs_rm[row * (p.F / 32) + f / 32] = (uint8_t)(sx + 127);
+            }
           }
         }
         if (ok && (EPI == EPI_SWIGLU || p.c)) {
@@ -1412,11 +1401,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   epilogue<G, EPI>(p, tc, acc, n0, wm, wn, lane, t, wbuf);
 }
 
-// Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn.
+// Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn
+// (all zero, and MOE_DEVERR_OFFSETS recorded, for invalid offsets).
 __global__ __launch_bounds__(1024) void tile_table_kernel(
-    const int32_t* __restrict__ offsets, int E, int unit, int tn,
-    int32_t* __restrict__ tile_start, uint32_t* __restrict__ zero,
-    int nzero);
+    const int32_t* __restrict__ offsets, int E, int64_t rows, int unit,
+    int tn, int32_t* __restrict__ tile_start, uint32_t* __restrict__ zero,
+    int nzero, int32_t* status);
 
 // Grid for a RAGGED_M launch: sum_e ceil(M_e / BM) <= rows / BM + E tiles
 // per N tile, rounded up to whole XCD rounds.
@@ -1478,17 +1468,23 @@ hipError_t launch(const char* name, const Params& p, int grid,
   return hipGetLastError();
 }
 
+// Each of these checks offsets (non-decreasing from 0 to rows) and, if
+// they are not, records MOE_DEVERR_OFFSETS in *status and publishes an
+// empty table, so that no GEMM tile and no segment is processed.
 // (also clears zero[0 .. nzero), e.g. the split tiles' arrival counters)
-hipError_t launch_tile_table(const int32_t* offsets, int E, int tn,
-                             int32_t* tile_start, hipStream_t stream,
-                             uint32_t* zero = nullptr, int nzero = 0);
+hipError_t launch_tile_table(const int32_t* offsets, int E, int64_t rows,
+                             int tn, int32_t* tile_start, int32_t* status,
+                             hipStream_t stream, uint32_t* zero = nullptr,
+                             int nzero = 0);
 // order[i] = the expert with the i-th most rows (equal counts: lower index
 // first); E <= 1024
-hipError_t launch_expert_order(const int32_t* offsets, int E, int32_t* order,
+hipError_t launch_expert_order(const int32_t* offsets, int E, int64_t rows,
+                               int32_t* order, int32_t* status,
                                hipStream_t stream);
 // poff[e] = sum_{e' < e} ceil(M_e' / pad) * pad, poff[E] the total
-hipError_t launch_padded_offsets(const int32_t* offsets, int E, int pad,
-                                 int32_t* poff, hipStream_t stream);
+hipError_t launch_padded_offsets(const int32_t* offsets, int E, int64_t rows,
+                                 int pad, int32_t* poff, int32_t* status,
+                                 hipStream_t stream);
 
 
 }  // namespace gg

@@ -45,7 +45,12 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
                                     int64_t cols, const int32_t* seg_offsets,
                                     int n_seg, int pad, int64_t ld,
                                     uint8_t* codes, uint8_t* scales,
-                                    hipStream_t stream, bool tiled = false);
+                                    int32_t* status, hipStream_t stream,
+                                    bool tiled = false);
+// row-wise MXFP8 of float32 values [n / cols][cols] (n % 32 == 0) with the
+// encoder of the MXFP8 gate/up epilogue; row-major scales [n / 32]
+hipError_t launch_mx_quant_f32(const float* src, int64_t n, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream);
 // row-major scales [rows][k / 32] (k % 128 == 0, 4-byte aligned) -> GEMM
 // layout
 hipError_t launch_mx_scales_retile(const uint8_t* src, int64_t rows,
@@ -59,7 +64,8 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
                                const void* w_dn, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
-                               int cu_count, hipStream_t stream);
+                               int cu_count, int32_t* status,
+                               hipStream_t stream);
 // tensor-scaled FP8
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream);
 hipError_t launch_seg_amax(const void* src, int64_t seg_elems, int n_seg,
@@ -73,7 +79,8 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
                                const void* w_dn, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
-                               int cu_count, hipStream_t stream);
+                               int cu_count, int32_t* status,
+                               hipStream_t stream);
 
 // router projection (float64 accumulation in ascending h) and backward
 hipError_t launch_router_logits(const void* x, const void* w_r,
@@ -104,7 +111,8 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
                                const int32_t* offsets, const void* h1_save,
                                const void* a_save, const void* dz_perm,
                                void* dx_perm, void* dw_gu, void* dw_dn,
-                               float* dw_perm, void* ws, hipStream_t stream);
+                               float* dw_perm, void* ws, int32_t* status,
+                               hipStream_t stream);
 
 // MXFP8 grouped MLP
 size_t mlp_fwd_mx_ws_bytes(int E, int H, int F, int64_t rows, bool quant_x,
@@ -116,8 +124,9 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
                              const uint8_t* w_gu_s, const uint8_t* w_dn_q,
                              const uint8_t* w_dn_s, const float* w_perm,
                              const int32_t* offsets, void* z_perm,
-                             void* h1_save, void* a_save, void* ws,
-                             int cu_count, hipStream_t stream);
+                             void* h1_save, void* a_save, uint8_t* a_q_save,
+                             uint8_t* a_s_save, void* ws, int cu_count,
+                             int32_t* status, hipStream_t stream);
 size_t mlp_bwd_mx_ws_bytes(int E, int H, int F, int64_t rows);
 hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
                              const void* x_perm, const void* w_gu,
@@ -125,6 +134,7 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
                              const int32_t* offsets, const void* h1_save,
                              const void* a_save, const void* dz_perm,
                              void* dx_perm, void* dw_gu, void* dw_dn,
-                             float* dw_perm, void* ws, hipStream_t stream);
+                             float* dw_perm, void* ws, int32_t* status,
+                             hipStream_t stream);
 
 }  // namespace moe

@@ -11,6 +11,8 @@
 // and saturation at 448, by the gfx950 scaled conversion (common.hpp).  All
 // kernels are HBM-bound streaming passes: 2 bytes read, 1 + 1/32 bytes
 // written per element.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timer.hpp"
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(
     const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
     const int32_t* __restrict__ seg_offsets, int n_seg, int pad_tiles,
     int64_t ld_out, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ scales, int32_t* status) {
   __shared__ uint16_t tile[32][64 + 2];
   __shared__ int32_t tprefix[1025];
   const int t = threadIdx.x;
@@ -142,6 +144,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(
     // row tiles each): thread t owns segments 4t .. 4t+3, then a block-wide
     // exclusive scan.
     const int pad = 32 * pad_tiles;
+    if (!seg_offsets_ok(seg_offsets, n_seg, rows, t, status)) return;
     int32_t cnt4[4], own = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(256) void mx_cols128_kernel(
     const uint4* __restrict__ src, int64_t rows, int64_t cols,
     const int32_t* __restrict__ seg_offsets, int n_seg, int pad_tiles,
     int64_t ld_out, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ scales, int32_t* status) {
   __shared__ __attribute__((aligned(16))) uint16_t tileT[64][128 + 8];
   __shared__ int32_t tprefix[1025];
   const int t = threadIdx.x;
@@ -249,6 +252,7 @@ __global__ __launch_bounds__(256) void mx_cols128_kernel(
   int64_t r0, rend, out0;
   if (SEG) {
     const int pad = 128 * pad_tiles;
+    if (!seg_offsets_ok(seg_offsets, n_seg, rows, t, status)) return;
     int32_t cnt4[4], own = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -401,12 +405,13 @@ hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
     if (tiled)
       hipLaunchKernelGGL((mx_cols128_kernel<false, true>), g128, dim3(256), 0,
                          stream, static_cast<const uint4*>(src), rows, cols,
-                         (const int32_t*)nullptr, 0, 1, rows, codes, scales);
+                         (const int32_t*)nullptr, 0, 1, rows, codes, scales,
+                       nullptr);
     else
       hipLaunchKernelGGL((mx_cols128_kernel<false, false>), g128, dim3(256),
                          0, stream, static_cast<const uint4*>(src), rows,
                          cols, (const int32_t*)nullptr, 0, 1, rows, codes,
-                         scales);
+                         scales, nullptr);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(rows / 32), (unsigned)((cols + 63) / 64),
@@ -414,11 +419,13 @@ hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
   if (tiled)
     hipLaunchKernelGGL((mx_cols_kernel<false, true>), grid, dim3(256), 0,
                        stream, static_cast<const uint16_t*>(src), rows, cols,
-                       (const int32_t*)nullptr, 0, 1, rows, codes, scales);
+                       (const int32_t*)nullptr, 0, 1, rows, codes, scales,
+                       nullptr);
   else
     hipLaunchKernelGGL((mx_cols_kernel<false, false>), grid, dim3(256), 0,
                        stream, static_cast<const uint16_t*>(src), rows, cols,
-                       (const int32_t*)nullptr, 0, 1, rows, codes, scales);
+                       (const int32_t*)nullptr, 0, 1, rows, codes, scales,
+                       nullptr);
   return hipGetLastError();
 }
 
@@ -426,7 +433,8 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
                                     int64_t cols, const int32_t* seg_offsets,
                                     int n_seg, int pad, int64_t ld,
                                     uint8_t* codes, uint8_t* scales,
-                                    hipStream_t stream, bool tiled) {
+                                    int32_t* status, hipStream_t stream,
+                                    bool tiled) {
   if (rows * cols == 0) return hipSuccess;
   KernelScope ks("mxfp8_quantize_segments", stream);
   if (pad % 128 == 0) {
@@ -437,11 +445,11 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
     if (tiled)
       hipLaunchKernelGGL((mx_cols128_kernel<true, true>), g128, dim3(256), 0,
                          stream, static_cast<const uint4*>(src), rows, cols,
-                         seg_offsets, n_seg, pt, ld, codes, scales);
+                         seg_offsets, n_seg, pt, ld, codes, scales, status);
     else
       hipLaunchKernelGGL((mx_cols128_kernel<true, false>), g128, dim3(256), 0,
                          stream, static_cast<const uint4*>(src), rows, cols,
-                         seg_offsets, n_seg, pt, ld, codes, scales);
+                         seg_offsets, n_seg, pt, ld, codes, scales, status);
     return hipGetLastError();
   }
   const int pad_tiles = pad / 32;
@@ -451,11 +459,45 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
   if (tiled)
     hipLaunchKernelGGL((mx_cols_kernel<true, true>), grid, dim3(256), 0,
                        stream, static_cast<const uint16_t*>(src), rows, cols,
-                       seg_offsets, n_seg, pad_tiles, ld, codes, scales);
+                       seg_offsets, n_seg, pad_tiles, ld, codes, scales,
+                       status);
   else
     hipLaunchKernelGGL((mx_cols_kernel<true, false>), grid, dim3(256), 0,
                        stream, static_cast<const uint16_t*>(src), rows, cols,
-                       seg_offsets, n_seg, pad_tiles, ld, codes, scales);
+                       seg_offsets, n_seg, pad_tiles, ld, codes, scales,
+                       status);
+  return hipGetLastError();
+}
+
+namespace {
+// Row-wise MXFP8 of float32 values, a quad of lanes per block of 32 (lane l
+// holds values 8 l .. 8 l + 7 of the flat array): the encoder the MXFP8
+// gate/up epilogue runs on its float32 ScaledSwiGLU outputs.
+__global__ __launch_bounds__(256) void mx_f32_kernel(
+    const float4* __restrict__ src, int64_t n8, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // n8 is a multiple of 4, so a quad is either wholly in range or wholly out
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += stride) {
+    const float4 a = src[2 * i], b = src[2 * i + 1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    int sx;
+    codes[i] = mx_quad_encode_f32(v, &sx);
+    if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(sx + 127);
+  }
+}
+}  // namespace
+
+hipError_t launch_mx_quant_f32(const float* src, int64_t n, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  KernelScope ks("mxfp8_quantize_f32", stream);
+  const int64_t n8 = n / 8;
+  const int64_t blocks = std::min<int64_t>((n8 + 255) / 256, 65536);
+  hipLaunchKernelGGL(mx_f32_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     stream, reinterpret_cast<const float4*>(src), n8,
+                     reinterpret_cast<uint2*>(codes), scales);
   return hipGetLastError();
 }
 

@@ -203,7 +203,125 @@ def test_device_check_flags_bad_expert_id(m):
     assert m.check_device_status() == 0  # cleared by the previous check
 
 
+def test_device_check_flags_bad_offsets(m):
+    """Per-expert offsets written on the host that end below the row count
+    (non-decreasing, so every access stays in bounds even unchecked) are
+    caught on the device by every call that reads them: the grouped MLP
+    forward (bf16, MXFP8, FP8 tensor-scaled) and backward (bf16, MXFP8) and
+    the token-segment MXFP8 quantiser record the offsets error, run no tile
+    and return normally; a following call with valid offsets is unaffected.
+    (Decreasing arrays and arrays ending past the rows are rejected by the
+    same guard; tests/native/offsets_check.cpp covers them on the host.)"""
+    E, H, F, rows = 4, 128, 128, 64
+    rng = np.random.default_rng(9)
+    x = dev_bf16(bf16_bits(rng.standard_normal((rows, H)).astype(np.float32)))
+    dz = dev_bf16(bf16_bits(rng.standard_normal((rows, H)).astype(np.float32)))
+    wgu_h = bf16_bits((0.05 * rng.standard_normal((E, 2 * F, H))).astype(
+        np.float32))
+    wdn_h = bf16_bits((0.05 * rng.standard_normal((E, H, F))).astype(
+        np.float32))
+    wgu, wdn = dev_bf16(wgu_h), dev_bf16(wdn_h)
+    good = torch.tensor([0, 10, 20, 40, 64], dtype=torch.int32, device="cuda")
+    bad = torch.tensor([0, 10, 20, 40, 60], dtype=torch.int32, device="cuda")
+    assert m.check_device_status() == 0
+    for prec in (m.PREC_BF16, m.PREC_MXFP8, m.PREC_FP8_TENSOR):
+        m.moe_grouped_mlp_fwd(x, wgu, wdn, bad, precision=prec)
+        assert m.check_device_status() == 2, prec
+    f = m.moe_grouped_mlp_fwd(x, wgu, wdn, good, save=True)
+    assert m.check_device_status() == 0
+    for prec in (m.PREC_BF16, m.PREC_MXFP8):
+        m.moe_grouped_mlp_bwd(dz, x, wgu, wdn, bad, f["h1"], f["a"],
+                              precision=prec)
+        assert m.check_device_status() == 2, prec
+    m.mxfp8_quantize(x, m.COLWISE, seg_offsets=bad)
+    assert m.check_device_status() == 2
+    # the valid call after them matches the oracle
+    r = m.moe_grouped_mlp_fwd(x, wgu, wdn, good)
+    assert m.check_device_status() == 0
+    ref = O.grouped_mlp_fwd(host_bits(x), wgu_h, wdn_h, None,
+                            good.cpu().numpy())
+    assert_rows_close(host_f64(r["z"]), ref["z"], TOL_BF16, "z")
+
+
 # ------------------------------------------------------------ MXFP8 quant
+def _f32_encoder_cases(rng):
+    """float32 rows of 32-value blocks that exercise the E4M3 encoder:
+    random magnitudes over the whole float32 range (subnormals included),
+    exact ties between neighbouring codes, values rounding past 448, small
+    values under a large block maximum, zeros and negative zeros."""
+    blocks = []
+    # random blocks at every block exponent reachable from float32
+    for e in range(-149, 121, 2):
+        v = rng.standard_normal((4, 32)) * 2.0 ** e
+        blocks.append(v.astype(np.float32))
+    # exact midpoints between consecutive E4M3 values, times 2^t, in blocks
+    # whose lead value pins the scale to 2^t (448 * 2^t as the block max)
+    mags = O.e4m3_decode(np.arange(0, 0x7E, dtype=np.uint8))
+    mids = (mags[:-1] + mags[1:]) / 2.0
+    for t in (-130, -20, 0, 3, 100):
+        v = np.resize(mids, (4, 31)) * rng.choice([-1.0, 1.0], (4, 31))
+        lead = np.full((4, 1), 448.0)
+        blk = np.concatenate([lead, v], axis=1) * 2.0 ** t
+        blocks.append(blk.astype(np.float32))
+    # leads whose scaled value falls in (448, 512): saturate to 448;
+    # 464 is the tie between 448 and the (NaN) next code
+    for lead in (449.0, 463.9, 464.0, 480.0, 500.0, 511.75):
+        v = rng.standard_normal((2, 32)) * 100.0
+        v[:, 0] = lead
+        v[1, 0] = -lead
+        blocks.append((v * 2.0 ** -3).astype(np.float32))
+    # tiny values under a large maximum: subnormal codes and flushes
+    v = rng.standard_normal((8, 32)) * 2.0 ** rng.integers(-14, -4, (8, 32))
+    v[:, 0] = 300.0
+    blocks.append(v.astype(np.float32))
+    z = np.zeros((2, 32), np.float32)
+    z[1] = -0.0
+    z[1, 5] = -1e-3
+    blocks.append(z)
+    return np.concatenate(blocks, axis=0).reshape(-1, 64)
+
+
+def test_mxfp8_quantize_f32_epilogue_encoder(m):
+    """The float32 -> MXFP8 encoder of the MXFP8 gate/up epilogue (block
+    exponent from the float32 amax, gfx950 scaled conversion, 448 fix-up)
+    against the oracle's R7 rule, bit for bit."""
+    v = _f32_encoder_cases(np.random.default_rng(21))
+    assert np.all(np.isfinite(v))
+    codes, scales = m.mxfp8_quantize_f32(torch.from_numpy(v).cuda())
+    want_c, want_s = O.mxfp8_quantize_rows(v.astype(np.float64))
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    bad = np.argwhere(gc != want_c)
+    assert bad.size == 0, (bad[:4], v[tuple(bad[0])], gc[tuple(bad[0])],
+                           want_c[tuple(bad[0])])
+    np.testing.assert_array_equal(gs, want_s)
+    assert (want_c & 0x7F).max() == 0x7E and np.any(want_c == 0x80)
+
+
+def test_mxfp8_a_codes_match_fraction(m):
+    """A's on-the-fly MXFP8 codes (quantised from float32 in the gate/up
+    epilogue) against the oracle's codes of its float64 A: not bit-gated,
+    since the two A values differ by accumulation order, but nearly all
+    equal (the share is printed)."""
+    T, H, F, E, k = 512, 256, 512, 8, 2
+    d = _mlp_case(T, H, F, E, k, 0.0, seed=8)
+    ref = O.layer_fwd(d["x"], d["logits"], d["w_gu"], d["w_dn"], k)
+    rq = O.grouped_mlp_fwd_mxfp8(ref["x_perm"], d["w_gu"], d["w_dn"],
+                                 ref["w_perm"], ref["offsets"], keep=True)
+    want_c, want_s = O.mxfp8_quantize_rows(rq["a"])
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w,
+                      precision=m.PREC_MXFP8)
+    r = m.moe_grouped_mlp_fwd(p["x_perm"], dev_bf16(d["w_gu"]),
+                              dev_bf16(d["w_dn"]), p["offsets"],
+                              w_perm=p["w_perm"], precision=m.PREC_MXFP8,
+                              x_perm_scale=p["x_perm_scale"],
+                              save_a_codes=True)
+    fc = float((r["a_q"].cpu().numpy() == want_c).mean())
+    fs = float((r["a_s"].cpu().numpy() == want_s).mean())
+    print(f"A codes equal to the oracle's: {fc:.6f}; scales: {fs:.6f}")
+    assert fc >= 0.99 and fs >= 0.99, (fc, fs)
+
+
 def test_mxfp8_rowwise_all_bf16_patterns(m):
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     bits = bits[((bits >> 7) & 0xFF) != 0xFF]          # finite values
@@ -527,8 +645,8 @@ def test_grouped_mlp_bwd_bf16(m, T, H, F, E, k, zipf):
     assert O.rel_err(gw_dn, ref["dw_dn"]) <= TOL_BF16
     for e in range(E):
         if split[e] > 0:
-            assert O.rel_err(gw_gu[e], ref["dw_gu"][e]) <= 2 * TOL_BF16, e
-            assert O.rel_err(gw_dn[e], ref["dw_dn"][e]) <= 2 * TOL_BF16, e
+            assert O.rel_err(gw_gu[e], ref["dw_gu"][e]) <= TOL_BF16, e
+            assert O.rel_err(gw_dn[e], ref["dw_dn"][e]) <= TOL_BF16, e
 
 
 # ------------------------------------------------------- grouped MLP, MXFP8

@@ -120,3 +120,15 @@ def test_library_index_helpers(tmp_path):
                    check=True)
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout
+
+
+def test_offsets_guard_host_build(tmp_path):
+    """The device-side offsets guard, built for the host: accepts exactly
+    the arrays that run non-decreasing from 0 to rows (exhaustive over small
+    arrays), and a rejected array yields an empty tile table."""
+    exe = str(tmp_path / "offsets_check")
+    src = os.path.join(ROOT, "tests", "native", "offsets_check.cpp")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, src, "-o", exe],
+                   check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout
