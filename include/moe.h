@@ -233,6 +233,35 @@ moe_status_t moe_permute(moe_ctx_t ctx, const void* x,
                          int32_t* split_sizes, int32_t* offsets, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * moe_permute_noalloc -- moe_permute without a workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors as moe_permute, minus ws / ws_bytes.  The
+ * index build's per-block expert histograms (moe_permute_workspace_size
+ * bytes) live instead in a static device array of 4 MiB that every GPU the
+ * library runs on holds until the process ends; its address is looked up
+ * once per device when the context is created.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).
+ * Limit: moe_permute_workspace_size(T, E, k) <= 4 MiB, i.e.
+ * ceil(T*k / 1024) * E <= 1048576 (e.g. E = 128 up to T*k = 8M pairs,
+ * E = 1024 up to 1M); larger sizes return MOE_ERR_UNSUPPORTED and enqueue
+ * nothing.  The kernels write every histogram entry before reading it, so
+ * the array needs no clearing between calls; it keeps the last call's
+ * contents.  All calls on one GPU share the one array: calls that overlap
+ * in time on a GPU (different streams, or host threads) race and give
+ * undefined results; calls ordered on one stream are safe.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_permute_noalloc(moe_ctx_t ctx, const void* x,
+                                 const int32_t* topk_idx,
+                                 const float* topk_w, int64_t T, int32_t H,
+                                 int32_t E, int32_t k,
+                                 moe_precision_t out_prec, void* x_perm,
+                                 uint8_t* x_perm_scale, float* w_perm,
+                                 int32_t* row_map, int32_t* src_row,
+                                 int32_t* split_sizes, int32_t* offsets,
+                                 void* stream);
+
 /* moe_gather_rows -- the row copy of moe_permute alone, for a tensor that
  * shares an existing permutation (the upstream gradient dY -> dZ in the
  * backward pass): dst[row_map[t*k+j]] = src[t] for all t, j; pairs with

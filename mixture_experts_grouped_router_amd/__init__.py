@@ -20,7 +20,8 @@ __all__ = [
     "lib_path", "load_library", "MoEError", "PREC_BF16", "PREC_MXFP8",
     "PREC_FP8_TENSOR", "fp8_tensor_quantize",
     "ROWWISE", "COLWISE", "moe_router_logits", "moe_router_bwd",
-    "moe_route_topk", "moe_permute", "moe_gather_rows",
+    "moe_route_topk", "moe_permute", "moe_permute_noalloc",
+    "moe_gather_rows",
     "moe_unpermute", "moe_unpermute_probs_grad", "mxfp8_quantize",
     "mxfp8_quantize_f32",
     "moe_grouped_mlp_fwd", "moe_expert_loop_mlp_fwd", "moe_grouped_mlp_bwd",
@@ -97,6 +98,9 @@ _SIGS = {
     "moe_permute": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_i32,
                     ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                     _c_p, _c_sz, _c_p],
+    "moe_permute_noalloc": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32,
+                            _c_i32, ctypes.c_int, _c_p, _c_p, _c_p, _c_p,
+                            _c_p, _c_p, _c_p, _c_p],
     "moe_gather_rows": [_c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p],
     "moe_unpermute": [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_p,
                       _c_p],
@@ -358,6 +362,43 @@ def moe_permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int,
         out["x_perm_scale"] = xs
     if w_perm is not None:
         out["w_perm"] = w_perm
+    return out
+
+
+def moe_permute_noalloc(x: torch.Tensor, topk_idx: torch.Tensor,
+                        topk_w: Optional[torch.Tensor],
+                        out: Dict[str, torch.Tensor],
+                        precision: int = PREC_BF16) -> Dict[str, torch.Tensor]:
+    """moe_permute into caller-provided outputs ``out`` (keys x_perm, row_map,
+    src_row, split_sizes, offsets, and x_perm_scale / w_perm as needed),
+    with the library's static scratch instead of a workspace: the library
+    call allocates nothing."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    E = out["split_sizes"].shape[0]
+    rows = T * k
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    if topk_w is not None:
+        _need(topk_w, torch.float32, (T, k), "topk_w")
+    if precision == PREC_BF16:
+        _need(out["x_perm"], torch.bfloat16, (rows, H), "x_perm")
+    else:
+        _need(out["x_perm"], torch.uint8, (rows, H), "x_perm")
+        _need(out["x_perm_scale"], torch.uint8, (rows, H // 32),
+              "x_perm_scale")
+    for key in ("row_map", "src_row"):
+        _need(out[key], torch.int32, (rows,), key)
+    _need(out["split_sizes"], torch.int32, (E,), "split_sizes")
+    _need(out["offsets"], torch.int32, (E + 1,), "offsets")
+    if out.get("w_perm") is not None:
+        _need(out["w_perm"], torch.float32, (rows,), "w_perm")
+    lib = load_library()
+    _check(lib.moe_permute_noalloc(
+        _context(x.device), _ptr(x), _ptr(topk_idx), _ptr(topk_w), T, H, E,
+        k, precision, _ptr(out["x_perm"]), _ptr(out.get("x_perm_scale")),
+        _ptr(out.get("w_perm")), _ptr(out["row_map"]), _ptr(out["src_row"]),
+        _ptr(out["split_sizes"]), _ptr(out["offsets"]), _stream()))
     return out
 
 

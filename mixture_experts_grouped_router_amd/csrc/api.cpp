@@ -16,6 +16,7 @@ struct moe_ctx {
   int device;
   int cu_count;
   int32_t* status;  // device word: first data error
+  void* perm_scratch;  // this device's static scratch of moe_permute_noalloc
   bool timing;
   moe::KernelTimer timer;
 };
@@ -112,17 +113,22 @@ moe_status_t moe_ctx_create(int device, moe_ctx_t* out) {
   e = hipSetDevice(device);
   if (e != hipSuccess) return hip_status(e, "hipSetDevice");
   int32_t* status = nullptr;
+  void* scratch = nullptr;
   e = hipMalloc(&status, sizeof(int32_t));
   if (e == hipSuccess) e = hipMemset(status, 0, sizeof(int32_t));
+  const hipError_t es =
+      e == hipSuccess ? moe::permute_scratch_address(device, &scratch) : e;
   if (prev >= 0) (void)hipSetDevice(prev);
-  if (e != hipSuccess) {
+  if (e != hipSuccess || es != hipSuccess) {
     if (status) (void)hipFree(status);
-    return hip_status(e, "status word");
+    return e != hipSuccess ? hip_status(e, "status word")
+                           : hip_status(es, "static scratch address");
   }
   moe_ctx* c = new moe_ctx;
   c->device = device;
   c->cu_count = prop.multiProcessorCount;
   c->status = status;
+  c->perm_scratch = scratch;
   c->timing = false;
   *out = c;
   return ok();
@@ -380,6 +386,32 @@ moe_status_t moe_permute(moe_ctx_t ctx, const void* x,
   return permute_impl(ctx, x, topk_idx, topk_w, T, H, E, k, out_prec, x_perm,
                       x_perm_scale, w_perm, row_map, src_row, split_sizes,
                       offsets, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_permute_noalloc(moe_ctx_t ctx, const void* x,
+                                 const int32_t* topk_idx,
+                                 const float* topk_w, int64_t T, int32_t H,
+                                 int32_t E, int32_t k,
+                                 moe_precision_t out_prec, void* x_perm,
+                                 uint8_t* x_perm_scale, float* w_perm,
+                                 int32_t* row_map, int32_t* src_row,
+                                 int32_t* split_sizes, int32_t* offsets,
+                                 void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
+  MOE_REQUIRE(T >= 0 && E >= 1 && k >= 1, MOE_ERR_INVALID_ARG,
+              "bad sizes (T=%lld E=%d k=%d)", (long long)T, E, k);
+  const size_t need = moe::permute_ws_bytes(T, E, k);
+  const size_t have = moe::permute_scratch_bytes();
+  MOE_REQUIRE(need <= have, MOE_ERR_UNSUPPORTED,
+              "moe_permute_noalloc: T*k = %lld pairs over E = %d experts need "
+              "%zu bytes of scratch, more than the %zu of its static array "
+              "(call moe_permute with a workspace)",
+              (long long)(T * (int64_t)k), E, need, have);
+  return permute_impl(ctx, x, topk_idx, topk_w, T, H, E, k, out_prec, x_perm,
+                      x_perm_scale, w_perm, row_map, src_row, split_sizes,
+                      offsets, ctx->perm_scratch, have, stream);
 }
 
 moe_status_t moe_gather_rows(moe_ctx_t ctx, const void* src,

@@ -13,6 +13,10 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
 
 // permutation
 size_t permute_ws_bytes(int64_t T, int E, int k);
+// the static scratch of moe_permute_noalloc: its size, and its device address
+// on `device` (which must be current; looked up once per device)
+size_t permute_scratch_bytes();
+hipError_t permute_scratch_address(int device, void** out);
 hipError_t launch_permute_index(const int32_t* topk_idx, int64_t T, int E,
                                 int k, int32_t* row_map, int32_t* src_row,
                                 int32_t* split, int32_t* offsets, void* ws,

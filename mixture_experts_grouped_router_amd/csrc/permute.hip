@@ -18,6 +18,8 @@
 // Row copy: one block per token reads x[t] once and writes it to its k
 // destination rows (16-byte vectors); optional row-wise MXFP8 quantisation on
 // the way.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timer.hpp"
@@ -358,6 +360,36 @@ __global__ __launch_bounds__(256) void probs_grad_kernel(
 }
 
 }  // namespace
+
+namespace {
+// Scratch of moe_permute_noalloc: the per-block expert histograms of the
+// index build (what moe_permute keeps in its workspace), in a static device
+// array, so that the call allocates nothing.  Every GPU holds its own copy,
+// at its own address, for the life of the process; host code reaches it
+// only through the address hipGetSymbolAddress returns for the current
+// device (the array's name is a host-side stand-in).
+constexpr size_t kPermScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) int32_t scratch[kPermScratchBytes /
+                                                 sizeof(int32_t)];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t permute_scratch_bytes() { return kPermScratchBytes; }
+
+hipError_t permute_scratch_address(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 size_t permute_ws_bytes(int64_t T, int E, int k) {
   const int64_t n = T * (int64_t)k;
