@@ -49,6 +49,9 @@ def parse():
                          "HBM timing, per-expert loop, router, pre-quantised "
                          "weights): profiler counter runs see the timed "
                          "step's launches only")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other workloads after the headline "
+                         "one (the 'configs' entry of the line)")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0 = auto)")
     ap.add_argument("--write-traffic", nargs=4, metavar="DB",
@@ -491,8 +494,8 @@ def cpu_baseline(cfg, d, n_tokens):
 
 def hbm_extras(m, layer, cfg, st):
     """HBM-bound kernels timed alone after writing a 1 GiB buffer (which
-    evicts L2 and the 256 MB Infinity Cache), next to a plain device copy
-    of the permute's traffic as the achievable reference."""
+    evicts L2 and the 256 MB Infinity Cache), next to the library's stream
+    kernel with the permute's traffic shape as the achievable reference."""
     import torch
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     stages = dict(layer.stages())
@@ -521,33 +524,37 @@ def hbm_extras(m, layer, cfg, st):
         res[kname] = {"ms": round(ms, 4), "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
                       "frac_hbm": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     m.reset_kernel_timing()
-    # plain device copy with the gather's traffic (read T*H*2, write k
-    # copies), through torch, as the achievable HBM reference
+    # the achievable reference: the library's stream kernel reading the
+    # gather's bytes once and writing k copies (its traffic shape, no
+    # indexing), caches flushed the same way
     nbytes = cfg.T * cfg.H * 2
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.fill_(1)
-    dsts = [torch.empty_like(src) for _ in range(cfg.k)]
+    dst = torch.empty(cfg.k * nbytes, dtype=torch.uint8, device="cuda")
+    ctx = m._context(torch.device("cuda"))
     cts = []
     for _ in range(5):
         flush.fill_(1.0)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for d in dsts:
-            d.copy_(src)
-        e1.record()
+        m.reset_kernel_timing()
+        m.set_kernel_timing(True)
+        m._check(layer.lib.moe_hbm_stream_reference(
+            ctx, src.data_ptr(), nbytes, cfg.k, dst.data_ptr(), st))
+        m.set_kernel_timing(False)
         torch.cuda.synchronize()
-        cts.append(e0.elapsed_time(e1))
+        n, tot = m.kernel_time("hbm_stream_reference")
+        cts.append(tot / max(n, 1))
+    m.reset_kernel_timing()
     cms = float(np.median(cts))
     cb = (1 + cfg.k) * nbytes
     ref = round(cb / (cms * 1e-3) / 1e9, 1)
     for v in res.values():
-        v["frac_of_copy"] = round(v["GB/s"] / ref, 4)
-    del flush, src, dsts
+        v["frac_of_stream"] = round(v["GB/s"] / ref, 4)
+    del flush, src, dst
     return {"kernels": res,
-            "copy_reference": {"GB/s": ref, "bytes": cb, "what":
-                               f"torch copy of {nbytes} bytes to {cfg.k} "
-                               "destinations, caches flushed"}}
+            "stream_reference": {
+                "GB/s": ref, "frac_hbm": round(ref / PEAK_HBM_GBS, 4),
+                "bytes": cb, "what": f"moe_hbm_stream_reference: read "
+                f"{nbytes} bytes once, write {cfg.k} copies, caches flushed"}}
 
 
 def dataclasses_replace(c):
@@ -557,8 +564,10 @@ def dataclasses_replace(c):
 
 
 def prequantised_step(m, layer, cfg, st, K):
-    """MXFP8 forward with the weights quantised once beforehand (codes and
-    scales passed to the call) instead of inside every call."""
+    """MXFP8 step with the weights quantised once beforehand (as a trainer
+    does once per weight update and reuses for every micro-batch): row-wise
+    codes for the forward call, column-wise codes for the backward, instead
+    of quantising them inside every call."""
     import torch
     E, H, F = cfg.E, cfg.H, cfg.F
     gq = m.mxfp8_quantize(layer.w_gu.reshape(E * 2 * F, H), m.ROWWISE)
@@ -572,6 +581,19 @@ def prequantised_step(m, layer, cfg, st, K):
                                                           ctypes.byref(n)))
     ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device="cuda")
     fa.ws, fa.ws_bytes = ws.data_ptr(), ws.numel()
+    if layer.bwd:
+        ba = layer.ba
+        bsaved = (ba.w_gu_qt, ba.w_gu_st, ba.w_dn_qt, ba.w_dn_st, ba.ws,
+                  ba.ws_bytes)
+        gqt = m.mxfp8_quantize(layer.w_gu, m.COLWISE)
+        dqt = m.mxfp8_quantize(layer.w_dn, m.COLWISE)
+        ba.w_gu_qt, ba.w_gu_st = gqt[0].data_ptr(), gqt[1].data_ptr()
+        ba.w_dn_qt, ba.w_dn_st = dqt[0].data_ptr(), dqt[1].data_ptr()
+        m._check(layer.lib.moe_grouped_mlp_bwd_workspace_size(
+            ctypes.byref(ba), ctypes.byref(n)))
+        bws = torch.empty(max(n.value, 256), dtype=torch.uint8,
+                          device="cuda")
+        ba.ws, ba.ws_bytes = bws.data_ptr(), bws.numel()
     stages = layer.stages()
     for _ in range(2):
         for _, fn in stages:
@@ -587,8 +609,15 @@ def prequantised_step(m, layer, cfg, st, K):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     (fa.w_gu_q, fa.w_gu_s, fa.w_dn_q, fa.w_dn_s, fa.ws, fa.ws_bytes) = saved
+    if layer.bwd:
+        (ba.w_gu_qt, ba.w_gu_st, ba.w_dn_qt, ba.w_dn_st, ba.ws,
+         ba.ws_bytes) = bsaved
+    flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
     return {"ms_per_step": round(ms, 4),
-            "value": round(cfg.fwd_flop() / (ms * 1e-3) / 1e12, 2)}
+            "value": round(flop / (ms * 1e-3) / 1e12, 2),
+            "what": "weights quantised once outside the timed step (row-wise "
+                    "for the forward" + (", column-wise for the backward"
+                                          if layer.bwd else "") + ")"}
 
 
 def expert_loop_extra(m, layer, cfg, st, K):
@@ -818,6 +847,108 @@ def router_extra(m, layer, cfg, d, st, K):
     return res
 
 
+# the other workloads, each timed in the default run after the headline one
+CONFIG_EXTRAS = ("tiny", "qwen3", "mixtral_mxfp8", "mixtral_mxfp8_bwd",
+                 "qwen3_long")
+
+
+def _config_data(cfg, base_cfg, base_d):
+    """Inputs of cfg; a workload with the headline's shapes and router reuses
+    its tensors (same seed, same streams), drawing only dY if needed."""
+    from synthetic import generate, generate_config
+    same = all(getattr(cfg, a) == getattr(base_cfg, a)
+               for a in ("T", "H", "F", "E", "k", "zipf"))
+    if not same:
+        return generate_config(cfg, seed=0)
+    d = dict(base_d)
+    if cfg.backward and d.get("dy") is None:
+        d["dy"] = generate(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, zipf=cfg.zipf,
+                           seed=0, want=("dy",))["dy"]
+    return d
+
+
+def config_run(m, cfg, d, dev, K, W):
+    """One workload's step, timed like the headline run (K steps after W
+    warm-up steps, every library kernel bracketed by HIP events): step time,
+    TFLOP/s, tokens/s, and each GEMM's and HBM kernel's roofline fraction."""
+    import torch
+    layer = Layer(m, cfg, d, dev)
+    stages = layer.stages()
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(W):
+        for _, fn in stages:
+            fn(st)
+    torch.cuda.synchronize()
+    m.reset_kernel_timing()
+    m.set_kernel_timing(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        for _, fn in stages:
+            fn(st)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    m.set_kernel_timing(False)
+    peak = PEAK_BF16_TFLOPS if cfg.mode == "bf16" else PEAK_FP8_TFLOPS
+    gemms, hbm = {}, {}
+    for name in KERNELS:
+        n, tot = m.kernel_time(name)
+        if not n:
+            continue
+        ms_s = tot / K
+        if name in KERNEL_FLOP:
+            tf = KERNEL_FLOP[name](cfg) / (ms_s * 1e-3) / 1e12
+            gemms[name] = {"ms_per_step": round(ms_s, 4),
+                           "TFLOP/s": round(tf, 1),
+                           "frac_mfma": round(tf / peak, 4)}
+        elif name in KERNEL_BYTES:
+            gb = KERNEL_BYTES[name](cfg) / (ms_s * 1e-3) / 1e9
+            hbm[name] = {"ms_per_step": round(ms_s, 4), "GB/s": round(gb, 1),
+                         "frac_hbm": round(gb / PEAK_HBM_GBS, 4)}
+    m.reset_kernel_timing()
+    if m.check_device_status() != 0:
+        raise RuntimeError(f"device status set by {cfg.name}")
+    flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
+    tf = flop / (ms * 1e-3) / 1e12
+    dom = "gemm_gate_up_swiglu_" + {"mxfp8": "mxfp8", "fp8t": "fp8t"}.get(
+        cfg.mode, "bf16")
+    out = {"workload": f"{cfg.name}: {cfg.description}",
+           "passes": "fwd+bwd" if cfg.backward else "fwd",
+           "steps": K, "warmup": W, "ms_per_step": round(ms, 4),
+           "TFLOP/s": round(tf, 2), "tokens_per_s": round(cfg.T / (ms * 1e-3),
+                                                            1),
+           "mfma_frac_step": round(tf / peak, 4),
+           "dominant": {"kernel": dom, **gemms.get(dom, {})},
+           "gemms": gemms, "hbm_kernels": hbm}
+    if cfg.mode == "mxfp8":
+        out["prequantised_weights"] = prequantised_step(m, layer, cfg, st,
+                                                        max(2, K // 2))
+    del layer
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def configs_extra(m, base_cfg, base_d, dev, K):
+    from synthetic import CONFIGS
+    res = {}
+    for name in CONFIG_EXTRAS:
+        if name == base_cfg.name:
+            continue
+        cfg = CONFIGS[name]
+        t0 = time.time()
+        d = _config_data(cfg, base_cfg, base_d)
+        print(f"[bench] configs: {name} inputs in {time.time() - t0:.1f} s",
+              file=sys.stderr, flush=True)
+        res[name] = config_run(m, cfg, d, dev, K, 2)
+        del d
+        print(f"[bench] configs: {name} {res[name]['ms_per_step']} ms/step",
+              file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -900,7 +1031,7 @@ def main():
     extras = {"peak_device_mem_GiB": round(peak_mem / 2**30, 2)}
     if not args.no_extras:
         extras["hbm_flushed"] = hbm_extras(m, layer, cfg, st)
-        if cfg.mode == "mxfp8" and not cfg.backward:
+        if cfg.mode == "mxfp8":
             extras["prequantised_weights"] = prequantised_step(
                 m, layer, cfg, st, max(1, K // 2))
         if cfg.mode == "bf16" and not cfg.backward:
@@ -910,6 +1041,11 @@ def main():
                                                 max(2, K // 4))
         extras["router"] = router_extra(m, layer, cfg, d, st, max(2, K // 2))
         extras["graph"] = graph_extra(layer, st, max(2, K // 2))
+    if not args.no_extras and not args.no_configs:
+        del layer, stages
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        extras["configs"] = configs_extra(m, cfg, d, dev, max(4, K // 2))
 
     flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
     tflops = flop / (ms_step * 1e-3) / 1e12

@@ -117,6 +117,16 @@ moe_status_t moe_ctx_reset_kernel_timing(moe_ctx_t ctx);
 moe_status_t moe_ctx_kernel_time(moe_ctx_t ctx, const char* kernel,
                                  int64_t* launches, double* total_ms);
 
+/* moe_hbm_stream_reference -- a measurement aid, not a step of the path:
+ * reads `bytes` of src once and writes k copies of them to dst
+ * ([k][bytes], device memory, 16-byte aligned, bytes % 16 == 0), the
+ * traffic shape of moe_permute's row gather without its indexing, as the
+ * achievable HBM bandwidth the gather and combine are compared with
+ * (kernel name "hbm_stream_reference" for moe_ctx_kernel_time). */
+moe_status_t moe_hbm_stream_reference(moe_ctx_t ctx, const void* src,
+                                      int64_t bytes, int32_t k, void* dst,
+                                      void* stream);
+
 /* ------------------------------------------------------------------------
  * moe_router_logits -- router projection in front of the top-k.
  * [PG3, practical-implications paragraph: Top-k routing; PG4, section
@@ -505,6 +515,19 @@ typedef struct moe_mlp_bwd_args {
   float* dw_perm;                /* out: float32 [rows] (NULL if w_perm NULL) */
   void* ws;
   size_t ws_bytes;
+  /* MXFP8 only, optional (each codes/scales pair both set or both NULL):
+   * the weights already quantised along the dgrad GEMMs' K, as
+   * mxfp8_quantize(w, COLWISE, batch = E) returns them:
+   *   w_gu_qt [E, H, 2F] codes + w_gu_st [E, H, 2F/32] scales (W_gu blocked
+   *   along 2F); w_dn_qt [E, F, H] + w_dn_st [E, F, H/32] (W_dn along H).
+   * NULL: quantised from w_gu / w_dn inside the call (and held in the
+   * workspace).  Reuse contract: they must be the quantisation of the w_gu
+   * / w_dn of this call (not checked).  Weights change only at an
+   * optimizer step, so a caller quantises them once per update and passes
+   * the same codes to every micro-batch's backward (and the row-wise ones,
+   * w_gu_q / w_dn_q, to every forward). */
+  const uint8_t* w_gu_qt; const uint8_t* w_gu_st;
+  const uint8_t* w_dn_qt; const uint8_t* w_dn_st;
 } moe_mlp_bwd_args;
 
 moe_status_t moe_grouped_mlp_bwd_workspace_size(const moe_mlp_bwd_args* args,

@@ -74,6 +74,8 @@ class _BwdArgs(ctypes.Structure):
         ("dz_perm", _c_p), ("dx_perm", _c_p), ("dw_gu", _c_p),
         ("dw_dn", _c_p), ("dw_perm", _c_p),
         ("ws", _c_p), ("ws_bytes", _c_sz),
+        ("w_gu_qt", _c_p), ("w_gu_st", _c_p), ("w_dn_qt", _c_p),
+        ("w_dn_st", _c_p),
     ]
 
 
@@ -118,6 +120,7 @@ _SIGS = {
     "moe_grouped_mlp_bwd_workspace_size": [ctypes.POINTER(_BwdArgs),
                                            ctypes.POINTER(_c_sz)],
     "moe_grouped_mlp_bwd": [_c_p, ctypes.POINTER(_BwdArgs), _c_p],
+    "moe_hbm_stream_reference": [_c_p, _c_p, _c_i64, _c_i32, _c_p, _c_p],
     "moe_ctx_set_kernel_timing": [_c_p, _c_i32],
     "moe_ctx_reset_kernel_timing": [_c_p],
     "moe_ctx_kernel_time": [_c_p, ctypes.c_char_p, ctypes.POINTER(_c_i64),
@@ -633,9 +636,15 @@ def moe_grouped_mlp_bwd(dz_perm: torch.Tensor, x_perm: torch.Tensor,
                         a: torch.Tensor, w_perm: Optional[torch.Tensor] = None,
                         precision: int = PREC_BF16,
                         ws: Optional[torch.Tensor] = None,
+                        w_gu_qt: Optional[Tuple[torch.Tensor,
+                                                torch.Tensor]] = None,
+                        w_dn_qt: Optional[Tuple[torch.Tensor,
+                                                torch.Tensor]] = None,
                         ) -> Dict[str, torch.Tensor]:
     """Backward of moe_grouped_mlp_fwd: returns dx_perm, dw_gu, dw_dn (bf16)
-    and dw_perm (float32, when w_perm is given)."""
+    and dw_perm (float32, when w_perm is given).  MXFP8: w_gu_qt / w_dn_qt
+    are optional (codes, scales) of the weights quantised COLWISE
+    (mxfp8_quantize(w, COLWISE)), reused instead of quantised in the call."""
     E, F2, H = w_gu.shape
     F = F2 // 2
     rows = x_perm.shape[0]
@@ -661,6 +670,14 @@ def moe_grouped_mlp_bwd(dz_perm: torch.Tensor, x_perm: torch.Tensor,
     args.dz_perm, args.dx_perm = _ptr(dz_perm), _ptr(dx)
     args.dw_gu, args.dw_dn, args.dw_perm = _ptr(dw_gu), _ptr(dw_dn), \
         _ptr(dw_perm)
+    if w_gu_qt is not None:
+        _need(w_gu_qt[0], torch.uint8, (E, H, 2 * F), "w_gu_qt codes")
+        _need(w_gu_qt[1], torch.uint8, (E, H, 2 * F // 32), "w_gu_qt scales")
+        args.w_gu_qt, args.w_gu_st = _ptr(w_gu_qt[0]), _ptr(w_gu_qt[1])
+    if w_dn_qt is not None:
+        _need(w_dn_qt[0], torch.uint8, (E, F, H), "w_dn_qt codes")
+        _need(w_dn_qt[1], torch.uint8, (E, F, H // 32), "w_dn_qt scales")
+        args.w_dn_qt, args.w_dn_st = _ptr(w_dn_qt[0]), _ptr(w_dn_qt[1])
     lib = load_library()
     nbytes = _c_sz(0)
     _check(lib.moe_grouped_mlp_bwd_workspace_size(ctypes.byref(args),

@@ -183,6 +183,24 @@ moe_status_t moe_ctx_kernel_time(moe_ctx_t ctx, const char* kernel,
                     "kernel timing events");
 }
 
+moe_status_t moe_hbm_stream_reference(moe_ctx_t ctx, const void* src,
+                                      int64_t bytes, int32_t k, void* dst,
+                                      void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
+  MOE_REQUIRE(bytes >= 0 && k >= 1 && k <= MOE_MAX_TOPK, MOE_ERR_INVALID_ARG,
+              "bad sizes");
+  MOE_REQUIRE(bytes % 16 == 0, MOE_ERR_UNSUPPORTED, "bytes %% 16 != 0");
+  if (bytes == 0) return ok();
+  MOE_REQUIRE(src && dst, MOE_ERR_INVALID_ARG, "null pointer");
+  MOE_REQUIRE(aligned16(src) && aligned16(dst), MOE_ERR_UNSUPPORTED,
+              "src / dst must be 16-byte aligned");
+  return hip_status(moe::launch_hbm_stream(src, bytes, k, dst, ctx->cu_count,
+                                           as_stream(stream)),
+                    "hbm stream reference");
+}
+
 moe_status_t moe_fp8_tensor_quantize_workspace_size(int64_t n_seg,
                                                     size_t* bytes) {
   MOE_REQUIRE(bytes != nullptr && n_seg >= 0, MOE_ERR_INVALID_ARG,
@@ -714,7 +732,9 @@ moe_status_t moe_grouped_mlp_bwd_workspace_size(const moe_mlp_bwd_args* a,
   if (a->precision == MOE_PREC_BF16)
     *bytes = moe::mlp_bwd_bf16_ws_bytes(a->E, a->H, a->F, a->rows);
   else
-    *bytes = moe::mlp_bwd_mx_ws_bytes(a->E, a->H, a->F, a->rows);
+    *bytes = moe::mlp_bwd_mx_ws_bytes(a->E, a->H, a->F, a->rows,
+                                      a->w_gu_qt == nullptr ||
+                                          a->w_dn_qt == nullptr);
   return ok();
 }
 
@@ -737,6 +757,17 @@ moe_status_t moe_grouped_mlp_bwd(moe_ctx_t ctx, const moe_mlp_bwd_args* a,
   MOE_REQUIRE(a->w_perm != nullptr || a->dw_perm == nullptr ||
                   a->rows == 0,
               MOE_ERR_INVALID_ARG, "dw_perm needs w_perm");
+  const bool mxb = a->precision == MOE_PREC_MXFP8_E4M3;
+  MOE_REQUIRE(mxb || (!a->w_gu_qt && !a->w_gu_st && !a->w_dn_qt &&
+                      !a->w_dn_st),
+              MOE_ERR_INVALID_ARG, "pre-quantised weights are MXFP8 inputs");
+  MOE_REQUIRE(!a->w_gu_qt == !a->w_gu_st && !a->w_dn_qt == !a->w_dn_st,
+              MOE_ERR_INVALID_ARG, "codes and scales go together");
+  MOE_REQUIRE(aligned16(a->w_gu_qt) && aligned16(a->w_dn_qt) &&
+                  (reinterpret_cast<uintptr_t>(a->w_gu_st) & 3u) == 0 &&
+                  (reinterpret_cast<uintptr_t>(a->w_dn_st) & 3u) == 0,
+              MOE_ERR_UNSUPPORTED,
+              "pre-quantised codes 16-byte, scales 4-byte aligned");
   size_t need = 0;
   s = moe_grouped_mlp_bwd_workspace_size(a, &need);
   if (s != MOE_OK) return s;
@@ -754,7 +785,9 @@ moe_status_t moe_grouped_mlp_bwd(moe_ctx_t ctx, const moe_mlp_bwd_args* a,
                                a->w_dn, a->w_perm, a->offsets, a->h1_save,
                                a->a_save, a->dz_perm, a->dx_perm, a->dw_gu,
                                a->dw_dn, a->w_perm ? a->dw_perm : nullptr,
-                               a->ws, ctx->status, as_stream(stream));
+                               a->w_gu_qt, a->w_gu_st, a->w_dn_qt,
+                               a->w_dn_st, a->ws, ctx->status,
+                               as_stream(stream));
   return hip_status(e, "grouped_mlp_bwd");
 }
 

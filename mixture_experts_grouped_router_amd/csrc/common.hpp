@@ -11,6 +11,7 @@ namespace moe {
 constexpr int kWave = 64;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Streaming (non-temporal) 16-byte global load / store.
 __device__ __forceinline__ uint4 ld_nt(const uint4* p) {

@@ -223,7 +223,8 @@ int64_t tok_ld(int64_t rows, int E) {
   return (rows + (int64_t)kTokPad * E + kTokPad - 1) / kTokPad * kTokPad;
 }
 
-MxBwdWs carve_bwd(void* base, int E, int H, int F, int64_t rows) {
+MxBwdWs carve_bwd(void* base, int E, int H, int F, int64_t rows,
+                  bool quant_w) {
   MxBwdWs w{};
   char* p = static_cast<char*>(base);
   size_t off = 0;
@@ -245,9 +246,9 @@ MxBwdWs carve_bwd(void* base, int E, int H, int F, int64_t rows) {
   w.part = reinterpret_cast<float*>(take((size_t)tnf * rows * 4));
   w.dzq = take8((size_t)rows * H);
   w.dzs = take8(mx_tile_bytes(rows, H));
-  w.wdq = take8((size_t)E * H * F);
+  if (quant_w) w.wdq = take8((size_t)E * H * F);
   w.wds = take8((size_t)E * H * F / 32);
-  w.wgq = take8((size_t)E * F2 * H);
+  if (quant_w) w.wgq = take8((size_t)E * F2 * H);
   w.wgs = take8((size_t)E * F2 * H / 32);
   w.hq = take8((size_t)rows * F2);
   w.hs = take8(mx_tile_bytes(rows, F2));
@@ -306,8 +307,8 @@ hipError_t wgrad_mx(const char* name, int E, int M, int N, int64_t ld,
 
 }  // namespace
 
-size_t mlp_bwd_mx_ws_bytes(int E, int H, int F, int64_t rows) {
-  return carve_bwd(nullptr, E, H, F, rows).bytes;
+size_t mlp_bwd_mx_ws_bytes(int E, int H, int F, int64_t rows, bool quant_w) {
+  return carve_bwd(nullptr, E, H, F, rows, quant_w).bytes;
 }
 
 hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
@@ -316,9 +317,14 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
                              const int32_t* offsets, const void* h1_save,
                              const void* a_save, const void* dz_perm,
                              void* dx_perm, void* dw_gu, void* dw_dn,
-                             float* dw_perm, void* ws, int32_t* status,
-                             hipStream_t stream) {
-  MxBwdWs w = carve_bwd(ws, E, H, F, rows);
+                             float* dw_perm, const uint8_t* w_gu_qt,
+                             const uint8_t* w_gu_st, const uint8_t* w_dn_qt,
+                             const uint8_t* w_dn_st, void* ws,
+                             int32_t* status, hipStream_t stream) {
+  // the weights' codes along the dgrad GEMMs' K come from the caller
+  // (quantised once per weight update) or are made here
+  const bool quant_w = w_gu_qt == nullptr || w_dn_qt == nullptr;
+  MxBwdWs w = carve_bwd(ws, E, H, F, rows, quant_w);
   const int tnf = (F + BN - 1) / BN;
   const int tnh = (H + BN - 1) / BN;
   const int F2 = 2 * F;
@@ -335,10 +341,22 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
     if (err == hipSuccess)
       err = launch_mx_quant_rows(dz_perm, rows, H, w.dzq, w.dzs, stream,
                                  true);
-    if (err == hipSuccess)
-      err = launch_mx_quant_cols(w_dn, E, H, F, w.wdq, w.wds, stream, true);
-    if (err == hipSuccess)
-      err = launch_mx_quant_cols(w_gu, E, F2, H, w.wgq, w.wgs, stream, true);
+    if (quant_w) {
+      if (err == hipSuccess)
+        err = launch_mx_quant_cols(w_dn, E, H, F, w.wdq, w.wds, stream, true);
+      if (err == hipSuccess)
+        err = launch_mx_quant_cols(w_gu, E, F2, H, w.wgq, w.wgs, stream, true);
+    } else {
+      // row-major scales of the caller's codes -> the GEMM layout
+      w.wdq = const_cast<uint8_t*>(w_dn_qt);
+      w.wgq = const_cast<uint8_t*>(w_gu_qt);
+      if (err == hipSuccess)
+        err = launch_mx_scales_retile(w_dn_st, (int64_t)E * F, H, w.wds,
+                                      stream);
+      if (err == hipSuccess)
+        err = launch_mx_scales_retile(w_gu_st, (int64_t)E * H, F2, w.wgs,
+                                      stream);
+    }
     if (err != hipSuccess) return err;
 
     // dgrad2 + SwiGLU backward: dA = dZ W_dn[e]; B = W_dn[e]^T [F, H]

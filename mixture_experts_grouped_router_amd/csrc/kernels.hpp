@@ -61,6 +61,10 @@ hipError_t launch_mx_scales_retile(const uint8_t* src, int64_t rows,
                                    int64_t k, uint8_t* dst,
                                    hipStream_t stream);
 
+// achievable-bandwidth reference: read `bytes` once, write k copies
+hipError_t launch_hbm_stream(const void* src, int64_t bytes, int k, void* dst,
+                             int cu_count, hipStream_t stream);
+
 // bf16 grouped MLP
 size_t mlp_fwd_bf16_ws_bytes(int E, int H, int F, int64_t rows, bool need_a);
 hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
@@ -131,14 +135,16 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
                              void* h1_save, void* a_save, uint8_t* a_q_save,
                              uint8_t* a_s_save, void* ws, int cu_count,
                              int32_t* status, hipStream_t stream);
-size_t mlp_bwd_mx_ws_bytes(int E, int H, int F, int64_t rows);
+size_t mlp_bwd_mx_ws_bytes(int E, int H, int F, int64_t rows, bool quant_w);
 hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
                              const void* x_perm, const void* w_gu,
                              const void* w_dn, const float* w_perm,
                              const int32_t* offsets, const void* h1_save,
                              const void* a_save, const void* dz_perm,
                              void* dx_perm, void* dw_gu, void* dw_dn,
-                             float* dw_perm, void* ws, int32_t* status,
-                             hipStream_t stream);
+                             float* dw_perm, const uint8_t* w_gu_qt,
+                             const uint8_t* w_gu_st, const uint8_t* w_dn_qt,
+                             const uint8_t* w_dn_st, void* ws,
+                             int32_t* status, hipStream_t stream);
 
 }  // namespace moe

@@ -111,7 +111,11 @@ def _perm_case(m, T, H, E, k, zipf=0.0, seed=0, logits=None):
 
 @pytest.mark.parametrize("T,H,E,k,zipf", [
     (256, 128, 8, 2, 0.0), (2000, 264, 128, 8, 1.2), (1025, 64, 16, 4, 0.0),
-    (1, 8, 4, 2, 0.0), (3000, 2048, 128, 8, 1.2)])
+    (1, 8, 4, 2, 0.0), (3000, 2048, 128, 8, 1.2),
+    # row-copy kernel variants: four tokens per block (H <= 2048), two
+    # (H <= 4096), one with a loop over the row (larger H); odd T tails
+    (1023, 4096, 8, 2, 0.0), (3, 4096, 8, 2, 0.0), (301, 8192, 8, 3, 0.0),
+    (5, 2040, 4, 4, 0.0)])
 def test_permute_bit_exact(m, T, H, E, k, zipf):
     _perm_case(m, T, H, E, k, zipf)
 
@@ -412,8 +416,13 @@ def test_mxfp8_segments(m):
     np.testing.assert_array_equal(scales[:, :w // 32].cpu().numpy(), rs)
 
 
-def test_permute_fused_mxfp8_bit_exact(m):
-    T, H, E, k = 300, 256, 8, 2
+@pytest.mark.parametrize("T,H,E,k", [
+    (300, 256, 8, 2),      # four tokens per block, word scale stores
+    (301, 96, 8, 2),       # H % 128 != 0: byte scale stores
+    (257, 4096, 8, 2),     # two tokens per block
+    (33, 8192, 4, 3),      # one token per block, loop over the row
+    (130, 2048, 16, 8), (7, 160, 4, 1)])
+def test_permute_fused_mxfp8_bit_exact(m, T, H, E, k):
     d = generate(T, H, 64, E, k, want=("x", "logits"))
     ridx, rw = O.route_topk(d["logits"], k)
     out = m.moe_permute(dev_bf16(d["x"]), torch.from_numpy(ridx).cuda(), E,
@@ -798,6 +807,34 @@ def test_grouped_mlp_bwd_mxfp8(m, T, H, F, E, k, zipf):
             assert O.rel_err(gw_dn[e], rq["dw_dn"][e]) <= TOL_MX, e
     assert O.rel_err(gw_gu, rq["dw_gu"]) <= TOL_MX
     assert O.rel_err(gw_dn, rq["dw_dn"]) <= TOL_MX
+
+
+def test_mxfp8_bwd_prequantised_weights_equal_on_the_fly(m):
+    """The MXFP8 backward with the weights quantised once beforehand
+    (mxfp8_quantize COLWISE, the reuse contract) gives the bits of the call
+    that quantises them itself."""
+    T, H, F, E, k = 500, 256, 384, 8, 2
+    d = _mlp_case(T, H, F, E, k, 1.2, seed=13)
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
+    f = m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
+                              w_perm=p["w_perm"], precision=m.PREC_MXFP8,
+                              save=True)
+    dz = m.moe_gather_rows(dev_bf16(d["dy"]), p["row_map"], k)
+    g1 = m.moe_grouped_mlp_bwd(dz, p["x_perm"], wgu, wdn, p["offsets"],
+                               f["h1"], f["a"], w_perm=p["w_perm"],
+                               precision=m.PREC_MXFP8)
+    gqt = m.mxfp8_quantize(wgu, m.COLWISE)      # [E, H, 2F] along 2F
+    dqt = m.mxfp8_quantize(wdn, m.COLWISE)      # [E, F, H] along H
+    g2 = m.moe_grouped_mlp_bwd(dz, p["x_perm"], wgu, wdn, p["offsets"],
+                               f["h1"], f["a"], w_perm=p["w_perm"],
+                               precision=m.PREC_MXFP8, w_gu_qt=gqt,
+                               w_dn_qt=dqt)
+    for key in ("dx_perm", "dw_gu", "dw_dn"):
+        assert torch.equal(g1[key].view(torch.int16),
+                           g2[key].view(torch.int16)), key
+    assert torch.equal(g1["dw_perm"], g2["dw_perm"])
 
 
 def test_grouped_mlp_bwd_mxfp8_close_to_bf16(m):
