@@ -146,7 +146,7 @@ size_t mlp_fwd_bf16_ws_bytes(int E, int H, int F, int64_t rows, bool need_a) {
   size_t b = 2 * align256((size_t)(E + 1) * sizeof(int32_t));
   if (need_a) b += align256((size_t)rows * F * 2);
   const int sx = fwd_split_slots_x(E, H, F, rows);
-  b += split_part_bytes(sx) + split_cnt_bytes(sx);
+  b += split_part_bytes(sx) + counters_bytes(1, sx);
   return b;
 }
 
@@ -170,13 +170,16 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   const int sx = fwd_split_slots_x(E, H, F, rows);
   float* split_part = reinterpret_cast<float*>(wp);
   wp += split_part_bytes(sx);
-  uint32_t* split_cnt = reinterpret_cast<uint32_t*>(wp);
+  // the gate/up GEMM's persistent-launch counters, then the split counters
+  uint32_t* queues = reinterpret_cast<uint32_t*>(wp);
+  uint32_t* split_cnt = queues + kQueueWords;
   if (rows == 0) return hipSuccess;
 
   const int tn1 = (F + BN / 2 - 1) / (BN / 2);
   const int tn2 = (H + BN - 1) / BN;
   hipError_t err = launch_tile_table(offsets, E, rows, tn1, ts1, status,
-                                     stream, split_cnt, kXcds * sx);
+                                     stream, queues,
+                                     kQueueWords + kXcds * sx);
   if (err == hipSuccess)
     err = launch_tile_table(offsets, E, rows, tn2, ts2, status, stream);
   if (err != hipSuccess) return err;
@@ -210,11 +213,15 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   // 3% slower), so four waves run it there.
   if (H <= kW8MaxGateUpK) {
     set_split(p1);
-    err = launch_w8<EPI_SWIGLU>("gemm_gate_up_swiglu_bf16", p1,
-                                ragged_m_grid_split(rows, E, tn1, p1), stream);
-  } else
+    p1.queue = queues;
+    err = launch_w8<EPI_SWIGLU>(
+        "gemm_gate_up_swiglu_bf16", p1,
+        persistent_grid(cu_count, ragged_m_grid_split(rows, E, tn1, p1)),
+        stream);
+  } else {
     err = launch<P_BF16, KC, KC, RAGGED_M, EPI_SWIGLU>(
         "gemm_gate_up_swiglu_bf16", p1, ragged_m_grid(rows, E, tn1), stream);
+  }
   if (err != hipSuccess) return err;
 
   Params p2{};

@@ -30,6 +30,8 @@
 // contiguous run of tiles, M fastest inside groups of 4 N tiles: the tiles in
 // flight on one XCD share activation rows and weight panels in its L2.
 #pragma once
+
+#include <type_traits>
 #include <algorithm>
 
 #include "common.hpp"
@@ -49,12 +51,9 @@ constexpr int kThreads = 256;
 constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand stage
 constexpr int kGroupN = 4;                  // N tiles per scheduling group
 constexpr int kXcds = 8;
-#ifndef MOE_DEAL_K
-#define MOE_DEAL_K 4
-#endif
 // RAGGED_K launches: consecutive tiles (largest expert first) are dealt to
 // the XCDs in runs of this many, so every XCD gets a share of each expert
-constexpr int kDealK = MOE_DEAL_K;
+constexpr int kDealK = 4;
 
 enum Layout { KC = 0, MC = 1 };  // memory: [mn][k] or [k][mn]
 enum Group { RAGGED_M = 0, RAGGED_K = 1 };
@@ -69,9 +68,6 @@ enum Epi {
 // applied to the accumulators before the epilogue)
 enum Prec { P_BF16 = 0, P_FP8 = 1, P_FP8T = 2 };
 
-#ifndef MOE_SCHED_GROUPS
-#define MOE_SCHED_GROUPS 1
-#endif
 
 
 // Instruction schedule of one MFMA region: NR LDS reads interleaved one to
@@ -80,7 +76,6 @@ enum Prec { P_BF16 = 0, P_FP8 = 1, P_FP8T = 2 };
 // under the MFMAs (the default schedule issued them after most MFMAs).
 template <int NR, int NM>
 __device__ __forceinline__ void sched_reads_mfma() {
-#if MOE_SCHED_GROUPS
   if constexpr (NR <= NM) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -96,7 +91,6 @@ __device__ __forceinline__ void sched_reads_mfma() {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   }
-#endif
 }
 
 // As sched_reads_mfma, with the region's NV vector-memory instructions (the
@@ -105,7 +99,6 @@ __device__ __forceinline__ void sched_reads_mfma() {
 // on the load issue instead of issuing MFMAs.
 template <int NV, int NR, int NM, int VPM, int MPV = 1, int I = 0>
 __device__ __forceinline__ void sched_vmem_reads_mfma() {
-#if MOE_SCHED_GROUPS
   if constexpr (I < NM) {
     // before every MPV-th MFMA, VPM vector-memory instructions
     constexpr int rem = NV - (I / MPV) * VPM;
@@ -115,12 +108,8 @@ __device__ __forceinline__ void sched_vmem_reads_mfma() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     sched_vmem_reads_mfma<NV, NR, NM, VPM, MPV, I + 1>();
   }
-#endif
 }
 
-#ifndef MOE_LOAD_SPLIT
-#define MOE_LOAD_SPLIT 1
-#endif
 // Direct loads of the next K step issued per MFMA of the first slice(s):
 // bf16 (4 slices, loads spread over two of them) one per MFMA; the 8-bit
 // modes (2 slices, all 24 loads in the first) three per MFMA, which leaves
@@ -173,6 +162,9 @@ struct Params {
   uint32_t* split_cnt;
   int split_slots_x;
   int cus_per_xcd;
+  // Ragged-M launches, nullable: kQueueWords counters (zero on entry) of a
+  // persistent launch, one work-group per CU taking items from them
+  uint32_t* queue;
 };
 
 // Swizzle of the 16-byte chunk c of LDS tile row r.  It depends only on
@@ -403,8 +395,11 @@ struct MxScales {
   }
 };
 
+// 1 / (1 + e^-x) with the hardware reciprocal (1 ulp) instead of an IEEE
+// division (about ten instructions per value, most of a SwiGLU epilogue's
+// VALU time); every use rounds the result to bf16 or E4M3 afterwards
 __device__ __forceinline__ float fast_sigmoid(float x) {
-  return 1.0f / (1.0f + __expf(-x));
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
 // ---- MFMA fragments ---------------------------------------------------------
@@ -451,6 +446,30 @@ struct Frags<P_BF16> {
                                        int wm, int wn, int lane) {
     load_a(sa, kk, wm, lane);
     load_b(sb, kk, wn, lane);
+  }
+  // the same from the lane's offsets of the slice (oa, ob: block row /
+  // column of the wave included; from rot_offsets)
+  __device__ __forceinline__ void load_at(const char* sa, const char* sb,
+                                          const uint32_t (&oa)[2],
+                                          const uint32_t (&ob)[2]) {
+    a0 = at(sa + oa[0], 0 * 32 * kRowBytes);
+    a1 = at(sa + oa[0], 1 * 32 * kRowBytes);
+    a2 = at(sa + oa[0], 2 * 32 * kRowBytes);
+    a3 = at(sa + oa[0], 3 * 32 * kRowBytes);
+    b0 = at(sb + ob[0], 0 * 32 * kRowBytes);
+    b1 = at(sb + ob[0], 1 * 32 * kRowBytes);
+    b2 = at(sb + ob[0], 2 * 32 * kRowBytes);
+    b3 = at(sb + ob[0], 3 * 32 * kRowBytes);
+  }
+  // lane offsets of slice kk: one per operand
+  static __device__ __forceinline__ void rot_offsets(int kk, int wm, int wn,
+                                                     int lane,
+                                                     uint32_t (&oa)[2],
+                                                     uint32_t (&ob)[2]) {
+    const int o = frag_off(lane & 31, kk * 2 + (lane >> 5));
+    oa[0] = wm * (128 * kRowBytes) + o;
+    ob[0] = wn * (128 * kRowBytes) + o;
+    oa[1] = ob[1] = 0;
   }
   // 8 k values of the lane from a [k][mn] stage (McDirect layout): two
   // transposed 8-byte reads, k and k + 4 rows apart
@@ -504,6 +523,30 @@ struct Frags<P_FP8> {
     b1 = at(pb0, pb1, 1 * 32 * kRowBytes);
     b2 = at(pb0, pb1, 2 * 32 * kRowBytes);
     b3 = at(pb0, pb1, 3 * 32 * kRowBytes);
+  }
+  __device__ __forceinline__ void load_at(const char* sa, const char* sb,
+                                          const uint32_t (&oa)[2],
+                                          const uint32_t (&ob)[2]) {
+    a0 = at(sa + oa[0], sa + oa[1], 0 * 32 * kRowBytes);
+    a1 = at(sa + oa[0], sa + oa[1], 1 * 32 * kRowBytes);
+    a2 = at(sa + oa[0], sa + oa[1], 2 * 32 * kRowBytes);
+    a3 = at(sa + oa[0], sa + oa[1], 3 * 32 * kRowBytes);
+    b0 = at(sb + ob[0], sb + ob[1], 0 * 32 * kRowBytes);
+    b1 = at(sb + ob[0], sb + ob[1], 1 * 32 * kRowBytes);
+    b2 = at(sb + ob[0], sb + ob[1], 2 * 32 * kRowBytes);
+    b3 = at(sb + ob[0], sb + ob[1], 3 * 32 * kRowBytes);
+  }
+  // lane offsets of slice kk: its two chunks, per operand
+  static __device__ __forceinline__ void rot_offsets(int kk, int wm, int wn,
+                                                     int lane,
+                                                     uint32_t (&oa)[2],
+                                                     uint32_t (&ob)[2]) {
+    const int c0 = kk * 4 + (lane >> 5);
+    const int o0 = frag_off(lane & 31, c0), o1 = frag_off(lane & 31, c0 + 2);
+    oa[0] = wm * (128 * kRowBytes) + o0;
+    oa[1] = wm * (128 * kRowBytes) + o1;
+    ob[0] = wn * (128 * kRowBytes) + o0;
+    ob[1] = wn * (128 * kRowBytes) + o1;
   }
 };
 
@@ -620,11 +663,19 @@ __device__ __forceinline__ uint4 stage_chunk(const char* buf, int row, int c) {
 // Routing weights of the wave's 128 rows in the wave's own LDS array: lane l
 // loads rows l and 64 + l (clamped to the expert; 1 without weights) before
 // any store of the epilogue, so the wait for them waits for no store.
+// (WEXT: in wext, 512 bytes per wave that the kernel provides, when the
+// operand stages leave no LDS for an array of their own)
+template <bool WEXT>
 __device__ __forceinline__ float* row_weights(const Params& p,
                                               const TileCoord& tc, int mw,
-                                              int lane, int t) {
-  __shared__ float wrow_all[kThreads / 64][128];
-  float* wrow = wrow_all[t >> 6];
+                                              int lane, int t, float* wext) {
+  float* wrow;
+  if constexpr (WEXT) {
+    wrow = wext + (t >> 6) * 128;
+  } else {
+    __shared__ float wrow_all[kThreads / 64][128];
+    wrow = wrow_all[t >> 6];
+  }
   float w0 = 1.0f, w1 = 1.0f;
   if (p.w) {
     w0 = p.w[tc.seg0 + min(mw + lane, tc.seg_len - 1)];
@@ -653,11 +704,11 @@ __device__ __forceinline__ void silu_mul_in_place(f32x16_t (&acc)[4][4]) {
 // load also waits for every store issued before it.  So each epilogue issues
 // its loads (routing weights, saved g and u) ahead of the stores they would
 // otherwise wait behind, and reads LDS in batches before storing.
-template <int G, int EPI>
+template <int G, int EPI, bool WEXT = false>
 __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
                                          f32x16_t (&acc)[4][4], int n0,
                                          int wm, int wn, int lane, int t,
-                                         char* wbuf) {
+                                         char* wbuf, float* wext = nullptr) {
   // acc[i][j][r] is C[row][col] of the wave's block with
   //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
   //   col = wn*128 + j*32 + lane%32
@@ -671,7 +722,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
     // the wave's 64 (a quad of lanes holds one 32-value MXFP8 block).
     const int64_t ld1 = 2 * (int64_t)p.F;
     const bool fvalid = n0 + 64 * wn < p.F;   // F % 64 == 0: whole runs
-    float* wrow = row_weights(p, tc, mw, lane, t);
+    float* wrow = row_weights<WEXT>(p, tc, mw, lane, t, wext);
     if (p.c2) {
       // (g, u) save for the backward pass, through LDS as bf16: row r holds
       // g of the wave's 64 f in columns 0..63 and u in 64..127; on readback
@@ -820,7 +871,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
     __shared__ float red[2 * BM];   // row sums of the two N-waves
     const int64_t ld1 = 2 * (int64_t)p.F;
     const int c8 = lane & 7;
-    float* wrow = row_weights(p, tc, mw, lane, t);
+    float* wrow = row_weights<WEXT>(p, tc, mw, lane, t, wext);
     float rsum[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) rsum[q] = 0.0f;
@@ -963,48 +1014,116 @@ struct SplitRange {
   int id;        // arrival counter
 };
 
-__device__ __forceinline__ bool decode_tile_split(const Params& p, int nk,
-                                               TileCoord& tc,
-                                               SplitRange& sr) {
-  const int b = blockIdx.x;
-  const int total = p.tile_start[p.E];
-  const int per = (total + kXcds - 1) / kXcds;
-  const int x = b % kXcds, idx = b / kXcds;
-  const int cnt = min(per, total - x * per);   // tiles of this XCD
-  if (cnt <= 0) return false;
-  int S = 1, rem = 0;
+// Items of XCD x in a ragged-M launch: its contiguous share of the tile
+// list (ceil(total / 8) tiles, the last XCD fewer), all whole unless a
+// partial last round is split; then whole = cnt - rem and rem * S pieces.
+struct XcdItems {
+  int per, cnt, whole, rem, S;
+  __device__ __forceinline__ int count() const {
+    return S > 1 ? whole + rem * S : max(cnt, 0);
+  }
+};
+__device__ __forceinline__ XcdItems xcd_items(const Params& p, int nk, int x,
+                                              int total) {
+  XcdItems it;
+  it.per = (total + kXcds - 1) / kXcds;
+  it.cnt = min(it.per, total - x * it.per);
+  it.S = 1;
+  it.rem = 0;
   const int C = p.cus_per_xcd;
-  if (p.split_part != nullptr && C > 0) {
-    rem = cnt % C;
-    if (rem > 0 && 2 * rem <= C) {
-      S = min(min(C / rem, kMaxSplit),
-              min(p.split_slots_x / rem, nk / kMinSplitSteps));
-      if (S < 2) S = 1;
+  if (p.split_part != nullptr && C > 0 && it.cnt > 0) {
+    it.rem = it.cnt % C;
+    if (it.rem > 0 && 2 * it.rem <= C) {
+      it.S = min(min(C / it.rem, kMaxSplit),
+                 min(p.split_slots_x / it.rem, nk / kMinSplitSteps));
+      if (it.S < 2) it.S = 1;
     }
   }
-  const int whole = S > 1 ? cnt - rem : cnt;
+  it.whole = it.S > 1 ? it.cnt - it.rem : it.cnt;
+  return it;
+}
+
+// Item idx of XCD x: a whole tile, or a range of K steps of one of the
+// last round's tiles.
+__device__ __forceinline__ bool decode_item(const Params& p, int nk, int x,
+                                            int idx, TileCoord& tc,
+                                            SplitRange& sr) {
+  const int total = p.tile_start[p.E];
+  const XcdItems it = xcd_items(p, nk, x, total);
+  if (it.cnt <= 0) return false;
   sr.ks = 0;
   sr.ke = nk;
   sr.S = 1;
   sr.slot0 = sr.s = sr.id = 0;
   int L;
-  if (idx < whole) {
-    L = x * per + idx;
+  if (idx < it.whole) {
+    L = x * it.per + idx;
   } else {
-    if (S == 1) return false;
-    const int c = idx - whole;
-    if (c >= rem * S) return false;
-    const int rt = c / S;
-    sr.s = c - rt * S;
-    sr.S = S;
-    sr.ks = sr.s * nk / S;
-    sr.ke = (sr.s + 1) * nk / S;
-    sr.slot0 = x * p.split_slots_x + rt * S;
+    if (it.S == 1) return false;
+    const int c = idx - it.whole;
+    if (c >= it.rem * it.S) return false;
+    const int rt = c / it.S;
+    sr.s = c - rt * it.S;
+    sr.S = it.S;
+    sr.ks = sr.s * nk / it.S;
+    sr.ke = (sr.s + 1) * nk / it.S;
+    sr.slot0 = x * p.split_slots_x + rt * it.S;
     sr.id = x * p.split_slots_x + rt;
-    L = x * per + whole + rt;
+    L = x * it.per + it.whole + rt;
   }
   ragged_m_tile(p, L, tc);
   return true;
+}
+
+// Work-group b of a one-item-per-work-group launch: XCD b mod 8 (where the
+// dispatcher puts it), item b / 8 of that XCD.
+__device__ __forceinline__ bool decode_tile_split(const Params& p, int nk,
+                                                  TileCoord& tc,
+                                                  SplitRange& sr) {
+  const int b = blockIdx.x;
+  return decode_item(p, nk, b % kXcds, b / kXcds, tc, sr);
+}
+
+// ---- persistent ragged-M launches -------------------------------------------
+// One work-group per CU.  Per item a work-group on XCD x first takes the
+// next index of its own XCD's counter (so an expert's tiles keep sharing
+// that XCD's L2, as with one work-group per item), and once that share is
+// used up the next index of the other XCDs' counters in turn: an XCD that
+// runs slow (one of them takes ~5% longer per tile on the same work) no
+// longer holds the whole launch back, and no work-group waits for a new
+// launch between tiles (3-4 us per tile measured between one work-group's
+// end and the next one's start on a CU).  Every taken index past a
+// counter's share is wasted, so the counters only grow and every
+// work-group ends after at most 8 failed takes.
+constexpr int kQueueWords = 16;   // counters 0..7 used
+
+// This CU's XCD (hardware register XCC_ID).
+__device__ __forceinline__ int hw_xcd() {
+  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcds - 1));
+}
+
+// Thread 0: the next item (x, idx), or x = -1 when none is left.
+__device__ __forceinline__ void take_item(const Params& p, int nk, int xh,
+                                          int& x, int& idx) {
+  const int total = p.tile_start[p.E];
+  x = -1;
+  idx = 0;
+  for (int d = 0; d < kXcds; ++d) {
+    const int y = (xh + d) & (kXcds - 1);
+    const int n = xcd_items(p, nk, y, total).count();
+    if (n <= 0) continue;
+    if (d > 0 && __hip_atomic_load(p.queue + y, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)n)
+      continue;
+    const uint32_t i = __hip_atomic_fetch_add(p.queue + y, 1u,
+                                              __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (i < (uint32_t)n) {
+      x = y;
+      idx = (int)i;
+      return;
+    }
+  }
 }
 
 // Partial tile of a split work-group: float4 q of accumulator block (i, j)
@@ -1099,6 +1218,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // may split the K range of its last round of tiles
   constexpr bool kMaySplit = G == RAGGED_M && EPI == EPI_STORE && LA == KC &&
                              LB == KC;
+  // the tensor-scaled FP8 gate/up GEMM runs the five-buffer rotation
+  // (below); measured on the Mixtral shapes, ms per launch: FP8 tensor-
+  // scaled 1.78 -> 1.69-1.73, MXFP8 1.85 -> 1.85-1.87, bf16 3.20-3.24 ->
+  // 3.38-3.39 (3.45 with the barrier after the last MFMA)
+  constexpr bool kRot = P == P_FP8T && G == RAGGED_M &&
+                        LA == KC && LB == KC && EPI == EPI_SWIGLU;
+  float* wext = nullptr;   // rotation: the epilogue's row weights
   TileCoord tc;
   SplitRange sr;
   if constexpr (kMaySplit) {
@@ -1249,7 +1375,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   };
   // The next K step's loads go out over the first slice (or, split, A over
   // the first slice and B over the second), spread between the MFMAs.
-  constexpr bool kSplit = MOE_LOAD_SPLIT && kSl >= 3;
+  constexpr bool kSplit = kSl >= 3;
   constexpr int kVmA = 8 + (P == P_FP8 ? 8 : 0);   // A loads (+ scales)
   // bf16 dgrad (N-contiguous B): six per MFMA (Qwen3-shaped long-sequence
   // dgrad of the down projection with the SwiGLU backward: one 1.356, three
@@ -1296,91 +1422,247 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     }
   };
 
-  // Two K steps per loop trip, one per LDS stage, so each stage is a
-  // distinct LDS object: the compiler then knows that direct loads into one
-  // stage never alias fragment reads of the other and waits for them only
-  // at the barrier.  An odd last step computes on a zero stage.  The trip
-  // has no branches, so the MFMAs stay where they are written.
-  // Fragment reads run one K slice ahead of the MFMAs; the barrier that
-  // publishes the next stage follows the step's last MFMA (8-bit modes: the
-  // last slice's third row block of MFMAs), so the next stage's loads get
-  // (nearly) the whole step to land.  (With the barrier halfway
-  // through the last slice, the next stage's first fragment reads overlapped
-  // the MFMAs after it but the loads had half a slice less: Mixtral-shaped
-  // gate/up 3.298 -> 3.206 ms, MXFP8 gate/up 1.963 -> 1.911 ms, MXFP8 down
-  // 1.000 -> 0.971 ms with the barrier at the end.)
-  const int nk2 = (nk + 1) & ~1;
-  if (nk > 0) issue(sA0, sB0, 0, true);
-  __syncthreads();
-  take_scales();
-  Fr cur, nxt;
-  fload(cur, sA0, sB0, 0);
-
-  for (int kt = 0; kt < nk2; kt += 2) {
-    // stage kt from buffers 0 while stage kt+1 loads into buffers 1
-    issue_part(sA1, sB1, kt + 1, kt + 1 < nk, kSplit ? 1 : 3);
+  // Gate/up GEMMs (ragged M, K-contiguous operands): five 32 KiB operand
+  // buffers in rotation instead of two 64 KiB stages, so the loads run
+  // further ahead.  Buffer n % 5 takes A of K step k for n = 2k and B of step
+  // k for n = 2k + 1; step k computes on A_k, B_k while B_{k+1} (issued over
+  // its first slice) and A_{k+2} (issued over its second) land in the two
+  // buffers that A_{k-1} and B_{k-1} have just left.  A is in flight for two
+  // steps, B for one (three steps' worth of operands resident needs 192 KiB
+  // with two 64 KiB stages; a row segment of 64 bytes instead of 128 halves
+  // what the texture path delivers).  The barrier that publishes step k + 1
+  // waits for everything but A_{k+2}: vmcnt counts in issue order, and the
+  // slice fences keep B_{k+1} (and the scales of step k + 1) ahead of it.
+  if constexpr (kRot) {
+    __shared__ __attribute__((aligned(1024))) char sR4[kTileBytes];
+    wext = reinterpret_cast<float*>(sR4);
+    Fr cur_r, nxt_r;
+    // Lane offsets of every slice's fragments, passed through an empty asm
+    // at each use: the compiler then adds them to the buffer's address read
+    // by read instead of holding an address per buffer, slice and operand
+    // in registers (40 with five buffers, which spill, and the reloads'
+    // vmcnt waits would also wait for the loads in flight).
+    uint32_t ro_a[kSl][2], ro_b[kSl][2];
 #pragma unroll
-    for (int kk = 0; kk < kSl - 1; ++kk) {
-      if (kSplit && kk == 1) issue_part(sA1, sB1, kt + 1, kt + 1 < nk, 2);
-      fload(nxt, sA0, sB0, kk + 1);
-      if (kk == 0) Mma<PF>::template run<0>(cur, sa_cur, sb_cur, acc);
-      else Mma<PF>::template run<1>(cur, sa_cur, sb_cur, acc);
-      cur = nxt;
-      slice_sched(kk);
-      // keep the scheduler from hoisting later slices' reads (registers)
+    for (int kk = 0; kk < kSl; ++kk)
+      Fr::rot_offsets(kk, wm, wn, lane, ro_a[kk], ro_b[kk]);
+    // (the asm goes first in a slice: as a side effect it also pins the
+    // slice's direct loads, which must stay free to interleave)
+    struct Offs { uint32_t a[2], b[2]; };
+    auto launder = [&](int kk) {
+      Offs o = {{ro_a[kk][0], ro_a[kk][1]}, {ro_b[kk][0], ro_b[kk][1]}};
+      if constexpr (PF == P_BF16)
+        asm volatile("" : "+v"(o.a[0]), "+v"(o.b[0]));
+      else
+        asm volatile("" : "+v"(o.a[0]), "+v"(o.a[1]), "+v"(o.b[0]),
+                     "+v"(o.b[1]));
+      return o;
+    };
+    auto fload_r = [&](Fr& f, const char* sa, const char* sb, const Offs& o) {
+      f.load_at(sa, sb, o.a, o.b);
+    };
+    auto buf = [&](auto nc) -> char* {
+      constexpr int n = decltype(nc)::value % 5;
+      if constexpr (n == 0) return sA0;
+      else if constexpr (n == 1) return sB0;
+      else if constexpr (n == 2) return sA1;
+      else if constexpr (n == 3) return sB1;
+      else return sR4;
+    };
+    // vector-memory instructions of one A step (per wave): the barrier's
+    // vmcnt leaves exactly these outstanding
+    constexpr int kVmA2 = 8;
+    constexpr int kWait = (kVmA2 & 0xf) | ((kVmA2 >> 4) << 14) | (0x7 << 4);
+    static_assert(kVmA2 < 64, "vmcnt field");
+    // publish: this wave's B_{k+1} (and scales) have landed and its reads of
+    // the step's buffers are done, then every wave is (memory clobbers
+    // keep the compiler from moving LDS accesses across)
+    auto publish = [&]() {
+      __builtin_amdgcn_s_waitcnt(kWait);   // vmcnt(kVmA2) lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    constexpr int kVmB1 = 8 + (P == P_FP8 ? 8 : 0);   // B (+ scales) loads
+    using std::integral_constant;
+    int k = 0;
+    auto rstep = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      char* const a = buf(integral_constant<int, 2 * j>{});
+      char* const b = buf(integral_constant<int, 2 * j + 1>{});
+      char* const an = buf(integral_constant<int, 2 * j + 2>{});
+      char* const bn = buf(integral_constant<int, 2 * j + 3>{});
+      char* const an2 = buf(integral_constant<int, 2 * j + 4>{});
+      // slice 0: B_{k+1} (+ the scales of step k + 1)
+      const Offs o1 = launder(1);
+      db.issue(bn, (uint32_t)(k + 1) * kRowBytes, k + 1 < nk, wave);
+      if constexpr (P == P_FP8) ms.load(min(k + 1, nk - 1));
+      fload_r(nxt_r, a, b, o1);
+      Mma<PF>::template run<0>(cur_r, sa_cur, sb_cur, acc);
+      cur_r = nxt_r;
+      sched_vmem_reads_mfma<kVmB1, kNR, 16, kVpm>();
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (kBarQ) {
-      Mma<PF>::template run<kSl - 1, 3>(cur, sa_cur, sb_cur, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      fload(nxt, sA1, sB1, 0);
-      Mma<PF>::template run<kSl - 1, 4>(cur, sa_cur, sb_cur, acc);
-      cur = nxt;
+      if constexpr (kSl > 2) {
+        // slice 1: A_{k+2}
+        const Offs o2 = launder(2);
+        da.issue(an2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
+        fload_r(nxt_r, a, b, o2);
+        Mma<PF>::template run<1>(cur_r, sa_cur, sb_cur, acc);
+        cur_r = nxt_r;
+        sched_vmem_reads_mfma<kVmA2, kNR, 16, kVpm>();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 2; kk < kSl - 1; ++kk) {
+          const Offs o = launder(kk + 1);
+          fload_r(nxt_r, a, b, o);
+          Mma<PF>::template run<1>(cur_r, sa_cur, sb_cur, acc);
+          cur_r = nxt_r;
+          sched_reads_mfma<kNR, 16>();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // last slice: three row blocks, publish step k + 1, its first
+        // fragments under the last row block
+        Mma<PF>::template run<kSl - 1, 3>(cur_r, sa_cur, sb_cur, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // last slice: A_{k+2} under its first three row blocks
+        da.issue(an2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
+        Mma<PF>::template run<kSl - 1, 3>(cur_r, sa_cur, sb_cur, acc);
+        sched_vmem_reads_mfma<kVmA2, 0, 12, kVpm>();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const Offs o0 = launder(0);
+      publish();
+      fload_r(nxt_r, an, bn, o0);
+      Mma<PF>::template run<kSl - 1, 4>(cur_r, sa_cur, sb_cur, acc);
+      cur_r = nxt_r;
       take_scales();
       sched_reads_mfma<kNR, 4>();
       __builtin_amdgcn_sched_barrier(0);
-    } else {
-      Mma<PF>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      fload(nxt, sA1, sB1, 0);
-      cur = nxt;
-      take_scales();
-      __builtin_amdgcn_sched_barrier(0);
+    };
+    // prologue: A_0, B_0 (+ scales of step 0), then A_1
+    da.issue(sA0, 0u, true, wave);
+    db.issue(sB0, 0u, true, wave);
+    if constexpr (P == P_FP8) ms.load(0);
+    da.issue(sA1, (uint32_t)kRowBytes, 1 < nk, wave);
+    publish();
+    take_scales();
+    fload_r(cur_r, sA0, sB0, launder(0));
+    // whole trips of five steps (one loop exit, so the fragments carried
+    // round the loop keep their registers), then the last nk % 5 steps
+    const int trips = nk / 5, rem = nk - 5 * trips;
+    for (int tr = 0; tr < trips; ++tr) {
+      rstep(integral_constant<int, 0>{});
+      ++k;
+      rstep(integral_constant<int, 1>{});
+      ++k;
+      rstep(integral_constant<int, 2>{});
+      ++k;
+      rstep(integral_constant<int, 3>{});
+      ++k;
+      rstep(integral_constant<int, 4>{});
+      ++k;
     }
+    if (rem > 0) {
+      rstep(integral_constant<int, 0>{});
+      ++k;
+      if (rem > 1) {
+        rstep(integral_constant<int, 1>{});
+        ++k;
+        if (rem > 2) {
+          rstep(integral_constant<int, 2>{});
+          ++k;
+          if (rem > 3) rstep(integral_constant<int, 3>{});
+        }
+      }
+    }
+  } else {
+    // Two K steps per loop trip, one per LDS stage, so each stage is a
+    // distinct LDS object: the compiler then knows that direct loads into one
+    // stage never alias fragment reads of the other and waits for them only
+    // at the barrier.  An odd last step computes on a zero stage.  The trip
+    // has no branches, so the MFMAs stay where they are written.
+    // Fragment reads run one K slice ahead of the MFMAs; the barrier that
+    // publishes the next stage follows the step's last MFMA (8-bit modes: the
+    // last slice's third row block of MFMAs), so the next stage's loads get
+    // (nearly) the whole step to land.  (With the barrier halfway
+    // through the last slice, the next stage's first fragment reads overlapped
+    // the MFMAs after it but the loads had half a slice less: Mixtral-shaped
+    // gate/up 3.298 -> 3.206 ms, MXFP8 gate/up 1.963 -> 1.911 ms, MXFP8 down
+    // 1.000 -> 0.971 ms with the barrier at the end.)
+    const int nk2 = (nk + 1) & ~1;
+    if (nk > 0) issue(sA0, sB0, 0, true);
+    __syncthreads();
+    take_scales();
+    Fr cur, nxt;
+    fload(cur, sA0, sB0, 0);
 
-    // stage kt+1 from buffers 1 while stage kt+2 loads into buffers 0 (a
-    // step past nk2 is never computed; its zero loads are harmless)
-    issue_part(sA0, sB0, kt + 2, kt + 2 < nk, kSplit ? 1 : 3);
-#pragma unroll
-    for (int kk = 0; kk < kSl - 1; ++kk) {
-      if (kSplit && kk == 1) issue_part(sA0, sB0, kt + 2, kt + 2 < nk, 2);
-      fload(nxt, sA1, sB1, kk + 1);
-      if (kk == 0) Mma<PF>::template run<0>(cur, sa_cur, sb_cur, acc);
-      else Mma<PF>::template run<1>(cur, sa_cur, sb_cur, acc);
-      cur = nxt;
-      slice_sched(kk);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (kBarQ) {
-      Mma<PF>::template run<kSl - 1, 3>(cur, sa_cur, sb_cur, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      fload(nxt, sA0, sB0, 0);
-      Mma<PF>::template run<kSl - 1, 4>(cur, sa_cur, sb_cur, acc);
-      cur = nxt;
-      take_scales();
-      sched_reads_mfma<kNR, 4>();
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      Mma<PF>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      fload(nxt, sA0, sB0, 0);
-      cur = nxt;
-      take_scales();
-      __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < nk2; kt += 2) {
+      // stage kt from buffers 0 while stage kt+1 loads into buffers 1
+      issue_part(sA1, sB1, kt + 1, kt + 1 < nk, kSplit ? 1 : 3);
+  #pragma unroll
+      for (int kk = 0; kk < kSl - 1; ++kk) {
+        if (kSplit && kk == 1) issue_part(sA1, sB1, kt + 1, kt + 1 < nk, 2);
+        fload(nxt, sA0, sB0, kk + 1);
+        if (kk == 0) Mma<PF>::template run<0>(cur, sa_cur, sb_cur, acc);
+        else Mma<PF>::template run<1>(cur, sa_cur, sb_cur, acc);
+        cur = nxt;
+        slice_sched(kk);
+        // keep the scheduler from hoisting later slices' reads (registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (kBarQ) {
+        Mma<PF>::template run<kSl - 1, 3>(cur, sa_cur, sb_cur, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        fload(nxt, sA1, sB1, 0);
+        Mma<PF>::template run<kSl - 1, 4>(cur, sa_cur, sb_cur, acc);
+        cur = nxt;
+        take_scales();
+        sched_reads_mfma<kNR, 4>();
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        Mma<PF>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        fload(nxt, sA1, sB1, 0);
+        cur = nxt;
+        take_scales();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // stage kt+1 from buffers 1 while stage kt+2 loads into buffers 0 (a
+      // step past nk2 is never computed; its zero loads are harmless)
+      issue_part(sA0, sB0, kt + 2, kt + 2 < nk, kSplit ? 1 : 3);
+  #pragma unroll
+      for (int kk = 0; kk < kSl - 1; ++kk) {
+        if (kSplit && kk == 1) issue_part(sA0, sB0, kt + 2, kt + 2 < nk, 2);
+        fload(nxt, sA1, sB1, kk + 1);
+        if (kk == 0) Mma<PF>::template run<0>(cur, sa_cur, sb_cur, acc);
+        else Mma<PF>::template run<1>(cur, sa_cur, sb_cur, acc);
+        cur = nxt;
+        slice_sched(kk);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (kBarQ) {
+        Mma<PF>::template run<kSl - 1, 3>(cur, sa_cur, sb_cur, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        fload(nxt, sA0, sB0, 0);
+        Mma<PF>::template run<kSl - 1, 4>(cur, sa_cur, sb_cur, acc);
+        cur = nxt;
+        take_scales();
+        sched_reads_mfma<kNR, 4>();
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        Mma<PF>::template run<kSl - 1>(cur, sa_cur, sb_cur, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        fload(nxt, sA0, sB0, 0);
+        cur = nxt;
+        take_scales();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -1398,7 +1680,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] *= f;
   }
-  epilogue<G, EPI>(p, tc, acc, n0, wm, wn, lane, t, wbuf);
+  epilogue<G, EPI, kRot>(p, tc, acc, n0, wm, wn, lane, t, wbuf, wext);
 }
 
 // Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn
@@ -1442,6 +1724,18 @@ inline size_t split_part_bytes(int slots_x) {
 }
 inline size_t split_cnt_bytes(int slots_x) {
   return align256((size_t)kXcds * slots_x * sizeof(uint32_t));
+}
+// Workspace bytes of nq persistent launches' counters followed by the split
+// arrival counters (one zeroed range).
+inline size_t counters_bytes(int nq, int slots_x) {
+  return align256(((size_t)nq * kQueueWords + (size_t)kXcds * slots_x) *
+                  sizeof(uint32_t));
+}
+// Grid of a persistent launch: one work-group per CU (whole XCD rounds),
+// never more than the one-item-per-work-group grid.
+inline int persistent_grid(int cu_count, int grid) {
+  const int g = std::max(kXcds, cu_count / kXcds * kXcds);
+  return std::min(g, grid);
 }
 // Lets launch p split its tail (slots_x > 0); the counters must be zero.
 inline void enable_split(Params& p, float* part, uint32_t* cnt, int slots_x,

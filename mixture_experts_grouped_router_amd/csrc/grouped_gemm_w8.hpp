@@ -278,11 +278,33 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char sB0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sA1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sB1[kTileBytes];
+  const int nk_all = (p.K + kStepK - 1) / kStepK;
+  const int t = threadIdx.x;
+  // persistent launch (p.queue): items from the XCD counters, the next one
+  // taken during the last trip of the current one's K loop (an atomic's
+  // round trip then hides under a K step) and handed over through LDS
+  // (the down GEMM's items are too long for per-item gaps to matter, and a
+  // slow XCD's items are all taken before other XCDs run dry: there the
+  // one-item launch is kept)
+  constexpr bool kPers = EPI == EPI_SWIGLU;
+  const bool pers = kPers && p.queue != nullptr;
+  __shared__ int s_item[2];
+  int ix, iidx, xh = 0;
+  if (pers) {
+    xh = hw_xcd();
+    if (t == 0) take_item(p, nk_all, xh, s_item[0], s_item[1]);
+    __syncthreads();
+    ix = s_item[0];
+    iidx = s_item[1];
+  } else {
+    ix = blockIdx.x % kXcds;
+    iidx = blockIdx.x / kXcds;
+  }
+  for (;;) {
   TileCoord tc;
   SplitRange sr;
-  if (!decode_tile_split(p, (p.K + kStepK - 1) / kStepK, tc, sr)) return;
+  if (ix < 0 || !decode_item(p, nk_all, ix, iidx, tc, sr)) return;
 
-  const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave / S::WN;
@@ -374,21 +396,52 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int kt = 0; kt < nk2; kt += 2) {
-    step(sA0, sB0, sA1, sB1, kt + 1);
-    step(sA1, sB1, sA0, sB0, kt + 2);
+  int nx = -1, ni = 0;   // thread 0: the next item
+  if constexpr (kPers) {
+    // the last trip peeled off, so that the loop has no branch
+    int kt = 0;
+    for (; kt + 2 < nk2; kt += 2) {
+      step(sA0, sB0, sA1, sB1, kt + 1);
+      step(sA1, sB1, sA0, sB0, kt + 2);
+    }
+    if (pers && t == 0) take_item(p, nk_all, xh, nx, ni);
+    if (kt < nk2) {
+      step(sA0, sB0, sA1, sB1, kt + 1);
+      step(sA1, sB1, sA0, sB0, kt + 2);
+    }
+  } else {
+    for (int kt = 0; kt < nk2; kt += 2) {
+      step(sA0, sB0, sA1, sB1, kt + 1);
+      step(sA1, sB1, sA0, sB0, kt + 2);
+    }
   }
 
   // every wave is past its last read of the stages (and every direct load
   // has landed) before they become epilogue staging: 16 KiB per wave
   __syncthreads();
-  if (sr.S > 1 && !split_reduce<kThreads8>(p, sr, acc, t)) return;
-  char* wbuf = (wave < 2 ? sA0 : wave < 4 ? sB0 : wave < 6 ? sA1 : sB1) +
-               (wave & 1) * (kTileBytes / 2);
-  if constexpr (EPI == EPI_STORE)
-    epilogue_w8_store(p, tc, acc, n0, wm, wn, lane, wbuf);
-  else
-    epilogue_w8_swiglu(p, tc, acc, n0, wm, wn, lane, wave, wbuf);
+  if (pers && t == 0) {
+    s_item[0] = nx;
+    s_item[1] = ni;
+  }
+  if (sr.S == 1 || split_reduce<kThreads8>(p, sr, acc, t)) {
+    char* wbuf = (wave < 2 ? sA0 : wave < 4 ? sB0 : wave < 6 ? sA1 : sB1) +
+                 (wave & 1) * (kTileBytes / 2);
+    if constexpr (EPI == EPI_STORE)
+      epilogue_w8_store(p, tc, acc, n0, wm, wn, lane, wbuf);
+    else
+      epilogue_w8_swiglu(p, tc, acc, n0, wm, wn, lane, wave, wbuf);
+  }
+  if (!pers) return;
+  // every wave's staging reads are done before the next item's loads
+  // write the stages (its stores may still be in flight: they read
+  // registers, not LDS), and thread 0's next item is visible
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  ix = s_item[0];
+  iidx = s_item[1];
+  }
 }
 
 template <int EPI>
