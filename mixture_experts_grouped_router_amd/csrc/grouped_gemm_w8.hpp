@@ -356,13 +356,15 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   // kernel; fragment reads run one slice ahead of the MFMAs and the barrier
   // that publishes the next stage sits inside the last slice's MFMAs.
   const int nk2 = (nk + 1) & ~1;
+  const bool act = __builtin_amdgcn_readfirstlane(
+                       tc.m0 + wm * MI * 32 < tc.seg_len ? 1 : 0) != 0;
   if (nk > 0) {
     da.issue(sA0, 0, true, wave);
     db.issue(sB0, 0, true, wave);
   }
   __syncthreads();
   Frags8<MI, NJ> cur, nxt;
-  cur.load(sA0, sB0, 0, wm, wn, lane);
+  if (act) cur.load(sA0, sB0, 0, wm, wn, lane);
 
   auto step = [&](const char* sa, const char* sb, char* na, char* nb, int kn) {
     // compute the step in (sa, sb); step kn loads into (na, nb) (a step
@@ -396,8 +398,26 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  int nx = -1, ni = 0;   // thread 0: the next item
-  if constexpr (kPers) {
+  // A wave whose rows all lie past the expert's last row (the last tile of
+  // an expert with few rows) issues its share of the direct loads and meets
+  // the barriers, but reads no fragments and runs no MFMAs: with at most
+  // half a tile of valid rows, every SIMD then computes for one of its two
+  // waves.  Its accumulators stay zero and its epilogue would store nothing.
+  auto step_idle = [&](char* na, char* nb, int kn) {
+    const bool real = kn < nk;
+    da.issue(na, (uint32_t)kn * kRowBytes, real, wave);
+    db.issue(nb, (uint32_t)kn * kRowBytes, real, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int nx = -1, ni = 0;   // thread 0 (always in an active wave): next item
+  if (!act) {
+    for (int kt = 0; kt < nk2; kt += 2) {
+      step_idle(sA1, sB1, kt + 1);
+      step_idle(sA0, sB0, kt + 2);
+    }
+  } else if constexpr (kPers) {
     // the last trip peeled off, so that the loop has no branch
     int kt = 0;
     for (; kt + 2 < nk2; kt += 2) {
@@ -423,7 +443,9 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
     s_item[0] = nx;
     s_item[1] = ni;
   }
-  if (sr.S == 1 || split_reduce<kThreads8>(p, sr, acc, t)) {
+  // (every wave takes part in the hand-over of a split tile's partials)
+  const bool last = sr.S == 1 || split_reduce<kThreads8>(p, sr, acc, t);
+  if (last && act) {
     char* wbuf = (wave < 2 ? sA0 : wave < 4 ? sB0 : wave < 6 ? sA1 : sB1) +
                  (wave & 1) * (kTileBytes / 2);
     if constexpr (EPI == EPI_STORE)
