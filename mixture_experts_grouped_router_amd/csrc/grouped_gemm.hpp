@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "work_items.hpp"
 #include "timer.hpp"
 
 namespace moe {
@@ -45,12 +46,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 #define MOE_LDS __attribute__((address_space(3)))
 
-constexpr int BM = 256, BN = 256;
 constexpr int kRowBytes = 128;              // bytes of one K step per row
 constexpr int kThreads = 256;
 constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand stage
-constexpr int kGroupN = 4;                  // N tiles per scheduling group
-constexpr int kXcds = 8;
 // RAGGED_K launches: consecutive tiles (largest expert first) are dealt to
 // the XCDs in runs of this many, so every XCD gets a share of each expert
 constexpr int kDealK = 4;
@@ -179,36 +177,10 @@ __device__ __forceinline__ int lds_off(int r, int c) {
   return r * kRowBytes + ((c ^ swz32(r)) << 4);
 }
 
-struct TileCoord {
-  int e;        // expert
-  int m0;       // first row of the tile inside the expert's M range
-  int seg0;     // offsets[e]
-  int seg_len;  // rows of expert e
-  int nt;       // N tile index
-};
-
-// Coordinates of tile L of a RAGGED_M launch: tile_start[e] <= L <
-// tile_start[e+1] (experts without tiles have tile_start[e] ==
-// tile_start[e+1] and are never selected); groups of kGroupN N tiles, M
-// tiles fastest inside a group.
+// Coordinates of tile L of a RAGGED_M launch (work_items.hpp).
 __device__ __forceinline__ void ragged_m_tile(const Params& p, int L,
                                               TileCoord& tc) {
-  int lo = 0, hi = p.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.tile_start[mid] <= L) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int local = L - p.tile_start[e];
-  const int len = p.offsets[e + 1] - p.offsets[e];
-  const int mt_e = (len + BM - 1) / BM;
-  const int ng = local / (mt_e * kGroupN);
-  const int in_g = local - ng * mt_e * kGroupN;
-  tc.e = e;
-  tc.m0 = (in_g % mt_e) * BM;
-  tc.nt = ng * kGroupN + in_g / mt_e;
-  tc.seg0 = p.offsets[e];
-  tc.seg_len = len;
+  ragged_m_tile_at(p.tile_start, p.offsets, p.E, L, tc);
 }
 
 template <int G>
@@ -996,51 +968,10 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
 // their float32 partial tile to a slot of the workspace; the last to arrive
 // (an arrival counter per tile) adds the S partials in slot order and runs
 // the tile's epilogue.  The sums are fixed by the tile list alone, so the
-// result is deterministic.
-constexpr int kMaxSplit = 8;
-constexpr int kMaxSplitSlotsX = 32;   // slots (and counters) per XCD
-// Fewest K steps of a split work-group: the partial tile's round trip and
-// the cache write-back / invalidate of the hand-over cost ~15 microseconds
-// per split tile, which only long K ranges repay (the Mixtral-shaped down
-// GEMM, K = 14336, gains 10% in bf16 and 4% in MXFP8; the Qwen3-shaped
-// gate/up GEMM, K = 2048, loses 3% with 16-step ranges).
-constexpr int kMinSplitSteps = 32;
+// result is deterministic.  Items and pieces: work_items.hpp.
 
-struct SplitRange {
-  int ks, ke;    // K steps [ks, ke) of this work-group
-  int S;         // work-groups sharing the tile (1: not split)
-  int slot0;     // first partial slot of the tile; this one is slot0 + s
-  int s;
-  int id;        // arrival counter
-};
-
-// Items of XCD x in a ragged-M launch: its contiguous share of the tile
-// list (ceil(total / 8) tiles, the last XCD fewer), all whole unless a
-// partial last round is split; then whole = cnt - rem and rem * S pieces.
-struct XcdItems {
-  int per, cnt, whole, rem, S;
-  __device__ __forceinline__ int count() const {
-    return S > 1 ? whole + rem * S : max(cnt, 0);
-  }
-};
-__device__ __forceinline__ XcdItems xcd_items(const Params& p, int nk, int x,
-                                              int total) {
-  XcdItems it;
-  it.per = (total + kXcds - 1) / kXcds;
-  it.cnt = min(it.per, total - x * it.per);
-  it.S = 1;
-  it.rem = 0;
-  const int C = p.cus_per_xcd;
-  if (p.split_part != nullptr && C > 0 && it.cnt > 0) {
-    it.rem = it.cnt % C;
-    if (it.rem > 0 && 2 * it.rem <= C) {
-      it.S = min(min(C / it.rem, kMaxSplit),
-                 min(p.split_slots_x / it.rem, nk / kMinSplitSteps));
-      if (it.S < 2) it.S = 1;
-    }
-  }
-  it.whole = it.S > 1 ? it.cnt - it.rem : it.cnt;
-  return it;
+__device__ __forceinline__ SplitCfg split_cfg(const Params& p) {
+  return SplitCfg{p.split_part != nullptr, p.cus_per_xcd, p.split_slots_x};
 }
 
 // Item idx of XCD x: a whole tile, or a range of K steps of one of the
@@ -1048,31 +979,8 @@ __device__ __forceinline__ XcdItems xcd_items(const Params& p, int nk, int x,
 __device__ __forceinline__ bool decode_item(const Params& p, int nk, int x,
                                             int idx, TileCoord& tc,
                                             SplitRange& sr) {
-  const int total = p.tile_start[p.E];
-  const XcdItems it = xcd_items(p, nk, x, total);
-  if (it.cnt <= 0) return false;
-  sr.ks = 0;
-  sr.ke = nk;
-  sr.S = 1;
-  sr.slot0 = sr.s = sr.id = 0;
-  int L;
-  if (idx < it.whole) {
-    L = x * it.per + idx;
-  } else {
-    if (it.S == 1) return false;
-    const int c = idx - it.whole;
-    if (c >= it.rem * it.S) return false;
-    const int rt = c / it.S;
-    sr.s = c - rt * it.S;
-    sr.S = it.S;
-    sr.ks = sr.s * nk / it.S;
-    sr.ke = (sr.s + 1) * nk / it.S;
-    sr.slot0 = x * p.split_slots_x + rt * it.S;
-    sr.id = x * p.split_slots_x + rt;
-    L = x * it.per + it.whole + rt;
-  }
-  ragged_m_tile(p, L, tc);
-  return true;
+  return decode_item_at(p.tile_start, p.offsets, p.E, split_cfg(p), nk, x,
+                        idx, tc, sr);
 }
 
 // Work-group b of a one-item-per-work-group launch: XCD b mod 8 (where the
@@ -1092,9 +1000,7 @@ __device__ __forceinline__ bool decode_tile_split(const Params& p, int nk,
 // runs slow (one of them takes ~5% longer per tile on the same work) no
 // longer holds the whole launch back, and no work-group waits for a new
 // launch between tiles (3-4 us per tile measured between one work-group's
-// end and the next one's start on a CU).  Every taken index past a
-// counter's share is wasted, so the counters only grow and every
-// work-group ends after at most 8 failed takes.
+// end and the next one's start on a CU).
 constexpr int kQueueWords = 16;   // counters 0..7 used
 
 // This CU's XCD (hardware register XCC_ID).
@@ -1105,25 +1011,18 @@ __device__ __forceinline__ int hw_xcd() {
 // Thread 0: the next item (x, idx), or x = -1 when none is left.
 __device__ __forceinline__ void take_item(const Params& p, int nk, int xh,
                                           int& x, int& idx) {
-  const int total = p.tile_start[p.E];
-  x = -1;
-  idx = 0;
-  for (int d = 0; d < kXcds; ++d) {
-    const int y = (xh + d) & (kXcds - 1);
-    const int n = xcd_items(p, nk, y, total).count();
-    if (n <= 0) continue;
-    if (d > 0 && __hip_atomic_load(p.queue + y, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)n)
-      continue;
-    const uint32_t i = __hip_atomic_fetch_add(p.queue + y, 1u,
-                                              __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    if (i < (uint32_t)n) {
-      x = y;
-      idx = (int)i;
-      return;
-    }
-  }
+  uint32_t* q = p.queue;
+  take_item_with(
+      p.tile_start[p.E], split_cfg(p), nk, xh,
+      [q](int y) {
+        return __hip_atomic_load(q + y, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      },
+      [q](int y) {
+        return __hip_atomic_fetch_add(q + y, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      },
+      x, idx);
 }
 
 // Partial tile of a split work-group: float4 q of accumulator block (i, j)

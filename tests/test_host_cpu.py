@@ -122,6 +122,19 @@ def test_library_index_helpers(tmp_path):
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout
 
 
+def test_work_items_host_build(tmp_path):
+    """The ragged-M GEMMs' work items, built for the host: every tile of a
+    random tile table is one whole item or K-range pieces that partition its
+    K steps, split slots stay inside their XCD and apart, and the persistent
+    take protocol hands out every item once and lets every work-group end."""
+    exe = str(tmp_path / "work_items_check")
+    src = os.path.join(ROOT, "tests", "native", "work_items_check.cpp")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC, src, "-o", exe],
+                   check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout
+
+
 def test_offsets_guard_host_build(tmp_path):
     """The device-side offsets guard, built for the host: accepts exactly
     the arrays that run non-decreasing from 0 to rows (exhaustive over small
