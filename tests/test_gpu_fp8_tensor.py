@@ -63,6 +63,12 @@ FP8T_CASES = [
     (700, 256, 384, 5, 2, 1.2),     # ragged M, F not a multiple of 256
     (900, 128, 128, 16, 4, 1.2),    # many experts, some empty
     (512, 256, 8192, 4, 2, 0.0),    # down GEMM's last tiles split along K
+    # the gate/up GEMM's five-buffer rotation: K steps of 128 (nk = H / 128)
+    # in whole trips of five plus a tail of nk % 5 steps
+    (300, 640, 256, 4, 2, 1.2),     # nk = 5: one trip, no tail
+    (200, 768, 256, 3, 1, 0.0),     # nk = 6: one trip, tail of one
+    (300, 1152, 128, 4, 2, 0.0),    # nk = 9: one trip, tail of four
+    (260, 1920, 128, 5, 2, 1.2),    # nk = 15: three trips, no tail
 ]
 
 
