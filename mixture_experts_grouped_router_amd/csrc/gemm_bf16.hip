@@ -130,6 +130,13 @@ hipError_t launch_padded_offsets(const int32_t* offsets, int E, int64_t rows,
 using namespace gg;
 
 namespace {
+// The eight-wave GEMMs run the five-buffer rotation (weight rows two K
+// steps ahead; ms per launch, same box: Qwen3-shaped gate/up 0.884 ->
+// 0.838-0.845, down 0.529 -> 0.500-0.507; long-sequence gate/up 1.836 ->
+// 1.745-1.753, down 1.073 -> 1.012-1.014; Mixtral-shaped down 1.627 ->
+// 1.591).
+constexpr bool kW8RotGateUp = true;
+constexpr bool kW8RotDown = true;
 // Split slots per XCD of the eight-wave forward GEMMs (the gate/up GEMM
 // runs with eight waves up to H = kW8MaxGateUpK).
 int fwd_split_slots_x(int E, int H, int F, int64_t rows) {
@@ -208,16 +215,15 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p1.w = w_perm;
   p1.rows = rows;
   // Eight waves per tile hide more latency but read 50% more LDS per MFMA;
-  // on the gate/up GEMM with a long K loop over large expert weights the
-  // extra power lowers the clock by more than the latency gained (H = 4096:
-  // 3% slower), so four waves run it there.
+  // up to H = kW8MaxGateUpK the latency gained pays for it (measured up
+  // to H = 4096), above the four-wave kernel runs it.
   if (H <= kW8MaxGateUpK) {
     set_split(p1);
     p1.queue = queues;
     err = launch_w8<EPI_SWIGLU>(
         "gemm_gate_up_swiglu_bf16", p1,
         persistent_grid(cu_count, ragged_m_grid_split(rows, E, tn1, p1)),
-        stream);
+        kW8RotGateUp, stream);
   } else {
     err = launch<P_BF16, KC, KC, RAGGED_M, EPI_SWIGLU>(
         "gemm_gate_up_swiglu_bf16", p1, ragged_m_grid(rows, E, tn1), stream);
@@ -242,7 +248,8 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p2.rows = rows;
   set_split(p2);
   return launch_w8<EPI_STORE>("gemm_down_bf16", p2,
-                             ragged_m_grid_split(rows, E, tn2, p2), stream);
+                             ragged_m_grid_split(rows, E, tn2, p2),
+                             kW8RotDown, stream);
 }
 
 size_t mlp_bwd_bf16_ws_bytes(int E, int H, int F, int64_t rows) {

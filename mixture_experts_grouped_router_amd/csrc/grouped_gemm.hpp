@@ -1029,11 +1029,12 @@ __device__ __forceinline__ void take_item(const Params& p, int nk, int xh,
 // of thread t at float4 index ((i NJ + j) 4 + q) NT + t of its slot, so
 // every wave-wide store and load covers one contiguous KiB.  Returns true
 // for the last arrival, whose accumulators then hold the sum of the S
-// partials, added in slot order.
+// partials, added in slot order.  arrived: one word of LDS.
 template <int NT, int MI, int NJ>
 __device__ __forceinline__ bool split_reduce(const Params& p,
                                              const SplitRange& sr,
-                                             f32x16_t (&acc)[MI][NJ], int t) {
+                                             f32x16_t (&acc)[MI][NJ], int t,
+                                             uint32_t* arrived) {
   constexpr int kSlot4 = BM * BN / 4;   // float4 per slot
   float4* own = reinterpret_cast<float4*>(p.split_part) +
                 (int64_t)(sr.slot0 + sr.s) * kSlot4;
@@ -1051,13 +1052,12 @@ __device__ __forceinline__ bool split_reduce(const Params& p,
   // counter increment) publishes them all, instead of one per wave.
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
   __syncthreads();
-  __shared__ uint32_t arrived;
   if (t == 0)
-    arrived = __hip_atomic_fetch_add(p.split_cnt + sr.id, 1u,
+    *arrived = __hip_atomic_fetch_add(p.split_cnt + sr.id, 1u,
                                      __ATOMIC_RELEASE,
                                      __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (arrived != (uint32_t)(sr.S - 1)) return false;
+  if (*arrived != (uint32_t)(sr.S - 1)) return false;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
   for (int i = 0; i < MI; ++i)
@@ -1568,8 +1568,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // every wave is past its last LDS read of the operand stages (and every
   // direct load has landed) before the stages become epilogue staging
   __syncthreads();
-  if constexpr (kMaySplit)
-    if (sr.S > 1 && !split_reduce<kThreads>(p, sr, acc, t)) return;
+  if constexpr (kMaySplit) {
+    __shared__ uint32_t arrived;
+    if (sr.S > 1 && !split_reduce<kThreads>(p, sr, acc, t, &arrived)) return;
+  }
   char* wbuf = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
   if constexpr (P == P_FP8T) {
     // the two tensor scales

@@ -449,7 +449,9 @@ MLP_CASES = [
     (700, 192, 320, 5, 2, 1.2),     # ragged M, F tail (320 = 2.5 x 128)
     (900, 256, 128, 16, 4, 1.2),    # many experts, some empty
     (64, 64, 64, 4, 1, 0.0),        # tiles larger than the problem
-    (300, 2112, 192, 4, 2, 1.2),    # H > 2048: the four-wave gate/up GEMM
+    (300, 2112, 192, 4, 2, 1.2),    # eight-wave gate/up, 33 K steps
+    (400, 640, 320, 6, 2, 1.2),     # whole trips of the five-buffer rotation
+    (300, 4160, 192, 4, 2, 1.2),    # H > 4096: the four-wave gate/up GEMM
     (512, 256, 8192, 4, 2, 0.0),    # down GEMM's tiles split 4 ways along K
     (700, 256, 8192, 8, 2, 1.2),    # the same with empty and one-row experts
 ]
