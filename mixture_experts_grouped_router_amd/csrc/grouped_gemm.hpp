@@ -1117,12 +1117,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // may split the K range of its last round of tiles
   constexpr bool kMaySplit = G == RAGGED_M && EPI == EPI_STORE && LA == KC &&
                              LB == KC;
-  // the tensor-scaled FP8 gate/up GEMM runs the five-buffer rotation
-  // (below); measured on the Mixtral shapes, ms per launch: FP8 tensor-
-  // scaled 1.78 -> 1.69-1.73, MXFP8 1.85 -> 1.85-1.87, bf16 3.20-3.24 ->
-  // 3.38-3.39 (3.45 with the barrier after the last MFMA)
-  constexpr bool kRot = P == P_FP8T && G == RAGGED_M &&
-                        LA == KC && LB == KC && EPI == EPI_SWIGLU;
+  // The 8-bit gate/up GEMMs run the five-buffer rotation (below).
+  // Measured on the Mixtral shapes, ms per launch: with A two steps ahead,
+  // tensor-scaled FP8 1.78 -> 1.69-1.73, MXFP8 1.85 -> 1.85-1.87, bf16
+  // 3.20-3.24 -> 3.38-3.39; with B two steps ahead (kept), MXFP8 1.782 ->
+  // 1.744-1.752 (with the backward's saves 2.008 -> 1.955), tensor-scaled
+  // FP8 as with A ahead.  The 8-bit down GEMMs, whose split-tail state
+  // leaves no registers for it, spill 400-560 bytes in the K loop with it.
+  constexpr bool kRot = P != P_BF16 && G == RAGGED_M &&
+                        LA == KC && LB == KC &&
+                        (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX);
   float* wext = nullptr;   // rotation: the epilogue's row weights
   TileCoord tc;
   SplitRange sr;
@@ -1323,15 +1327,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 
   // Gate/up GEMMs (ragged M, K-contiguous operands): five 32 KiB operand
   // buffers in rotation instead of two 64 KiB stages, so the loads run
-  // further ahead.  Buffer n % 5 takes A of K step k for n = 2k and B of step
-  // k for n = 2k + 1; step k computes on A_k, B_k while B_{k+1} (issued over
-  // its first slice) and A_{k+2} (issued over its second) land in the two
-  // buffers that A_{k-1} and B_{k-1} have just left.  A is in flight for two
-  // steps, B for one (three steps' worth of operands resident needs 192 KiB
-  // with two 64 KiB stages; a row segment of 64 bytes instead of 128 halves
-  // what the texture path delivers).  The barrier that publishes step k + 1
-  // waits for everything but A_{k+2}: vmcnt counts in issue order, and the
-  // slice fences keep B_{k+1} (and the scales of step k + 1) ahead of it.
+  // further ahead.  Buffer n % 5 takes B of K step k for n = 2k and A of step
+  // k for n = 2k + 1; step k computes on A_k, B_k while A_{k+1} (issued over
+  // its first slice, with the scales of step k + 1) and B_{k+2} (issued over
+  // its second) land in the two buffers that B_{k-1} and A_{k-1} have just
+  // left.  The weight rows are in flight for two steps, the token rows for
+  // one (three steps' worth of operands resident needs 192 KiB with two
+  // 64 KiB stages; a row segment of 64 bytes instead of 128 halves what the
+  // texture path delivers).  The barrier that publishes step k + 1 waits
+  // for everything but B_{k+2}: vmcnt counts in issue order, and the slice
+  // fences keep A_{k+1} (and the scales) ahead of it.
   if constexpr (kRot) {
     __shared__ __attribute__((aligned(1024))) char sR4[kTileBytes];
     wext = reinterpret_cast<float*>(sR4);
@@ -1368,47 +1373,47 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       else if constexpr (n == 3) return sB1;
       else return sR4;
     };
-    // vector-memory instructions of one A step (per wave): the barrier's
+    // vector-memory instructions of one B step (per wave): the barrier's
     // vmcnt leaves exactly these outstanding
-    constexpr int kVmA2 = 8;
-    constexpr int kWait = (kVmA2 & 0xf) | ((kVmA2 >> 4) << 14) | (0x7 << 4);
-    static_assert(kVmA2 < 64, "vmcnt field");
-    // publish: this wave's B_{k+1} (and scales) have landed and its reads of
+    constexpr int kVmB2 = 8;
+    constexpr int kWait = (kVmB2 & 0xf) | ((kVmB2 >> 4) << 14) | (0x7 << 4);
+    static_assert(kVmB2 < 64, "vmcnt field");
+    // publish: this wave's A_{k+1} (and scales) have landed and its reads of
     // the step's buffers are done, then every wave is (memory clobbers
     // keep the compiler from moving LDS accesses across)
     auto publish = [&]() {
-      __builtin_amdgcn_s_waitcnt(kWait);   // vmcnt(kVmA2) lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(kWait);   // vmcnt(kVmB2) lgkmcnt(0)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
-    constexpr int kVmB1 = 8 + (P == P_FP8 ? 8 : 0);   // B (+ scales) loads
+    constexpr int kVmA1 = 8 + (P == P_FP8 ? 8 : 0);   // A (+ scales) loads
     using std::integral_constant;
     int k = 0;
     auto rstep = [&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      char* const a = buf(integral_constant<int, 2 * j>{});
-      char* const b = buf(integral_constant<int, 2 * j + 1>{});
-      char* const an = buf(integral_constant<int, 2 * j + 2>{});
-      char* const bn = buf(integral_constant<int, 2 * j + 3>{});
-      char* const an2 = buf(integral_constant<int, 2 * j + 4>{});
-      // slice 0: B_{k+1} (+ the scales of step k + 1)
+      char* const b = buf(integral_constant<int, 2 * j>{});
+      char* const a = buf(integral_constant<int, 2 * j + 1>{});
+      char* const bn = buf(integral_constant<int, 2 * j + 2>{});
+      char* const an = buf(integral_constant<int, 2 * j + 3>{});
+      char* const bn2 = buf(integral_constant<int, 2 * j + 4>{});
+      // slice 0: A_{k+1} (+ the scales of step k + 1)
       const Offs o1 = launder(1);
-      db.issue(bn, (uint32_t)(k + 1) * kRowBytes, k + 1 < nk, wave);
+      da.issue(an, (uint32_t)(k + 1) * kRowBytes, k + 1 < nk, wave);
       if constexpr (P == P_FP8) ms.load(min(k + 1, nk - 1));
       fload_r(nxt_r, a, b, o1);
       Mma<PF>::template run<0>(cur_r, sa_cur, sb_cur, acc);
       cur_r = nxt_r;
-      sched_vmem_reads_mfma<kVmB1, kNR, 16, kVpm>();
+      sched_vmem_reads_mfma<kVmA1, kNR, 16, kVpm>();
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kSl > 2) {
-        // slice 1: A_{k+2}
+        // slice 1: B_{k+2}
         const Offs o2 = launder(2);
-        da.issue(an2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
+        db.issue(bn2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
         fload_r(nxt_r, a, b, o2);
         Mma<PF>::template run<1>(cur_r, sa_cur, sb_cur, acc);
         cur_r = nxt_r;
-        sched_vmem_reads_mfma<kVmA2, kNR, 16, kVpm>();
+        sched_vmem_reads_mfma<kVmB2, kNR, 16, kVpm>();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 2; kk < kSl - 1; ++kk) {
@@ -1424,10 +1429,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
         Mma<PF>::template run<kSl - 1, 3>(cur_r, sa_cur, sb_cur, acc);
         __builtin_amdgcn_sched_barrier(0);
       } else {
-        // last slice: A_{k+2} under its first three row blocks
-        da.issue(an2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
+        // last slice: B_{k+2} under its first three row blocks
+        db.issue(bn2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
         Mma<PF>::template run<kSl - 1, 3>(cur_r, sa_cur, sb_cur, acc);
-        sched_vmem_reads_mfma<kVmA2, 0, 12, kVpm>();
+        sched_vmem_reads_mfma<kVmB2, 0, 12, kVpm>();
         __builtin_amdgcn_sched_barrier(0);
       }
       const Offs o0 = launder(0);
@@ -1439,14 +1444,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       sched_reads_mfma<kNR, 4>();
       __builtin_amdgcn_sched_barrier(0);
     };
-    // prologue: A_0, B_0 (+ scales of step 0), then A_1
-    da.issue(sA0, 0u, true, wave);
-    db.issue(sB0, 0u, true, wave);
+    // prologue: B_0 into buffer 0, A_0 (+ scales of step 0) into buffer 1,
+    // then B_1 into buffer 2
+    db.issue(sA0, 0u, true, wave);
+    da.issue(sB0, 0u, true, wave);
     if constexpr (P == P_FP8) ms.load(0);
-    da.issue(sA1, (uint32_t)kRowBytes, 1 < nk, wave);
+    db.issue(sA1, (uint32_t)kRowBytes, 1 < nk, wave);
     publish();
     take_scales();
-    fload_r(cur_r, sA0, sB0, launder(0));
+    fload_r(cur_r, sB0, sA0, launder(0));
     // whole trips of five steps (one loop exit, so the fragments carried
     // round the loop keep their registers), then the last nk % 5 steps
     const int trips = nk / 5, rem = nk - 5 * trips;
