@@ -67,7 +67,7 @@ def parse():
 
 # library kernel name -> template instantiations in profiler kernel names
 # (the bf16 forward runs the eight-wave kernel for the down GEMM, and for
-# gate/up up to H = 2048)
+# gate/up up to H = 4096)
 KERNEL_SYMBOL = {
     "gemm_gate_up_swiglu_bf16": ("grouped_gemm_kernel<0, 0, 0, 0, 1>",
                                  "grouped_gemm_w8_kernel<1,"),
