@@ -7,6 +7,7 @@
 // bf16 and its amax, then A is quantised with its own scale for the down
 // GEMM.  Kernel: grouped_gemm.hpp (P_FP8T).
 #include "grouped_gemm.hpp"
+#include "grouped_gemm_w8q.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -144,8 +145,8 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   p2.tsa = w.scale + 1;
   p2.tsb = w.scale + 2 + E;
   enable_split(p2, w.split_part, w.split_cnt, w.split_x, cu_count);
-  return launch<P_FP8T, KC, KC, RAGGED_M, EPI_STORE>(
-      "gemm_down_fp8t", p2, ragged_m_grid_split(rows, E, tn2, p2), stream);
+  return launch_w8q<P_FP8T>("gemm_down_fp8t", p2,
+                            ragged_m_grid_split(rows, E, tn2, p2), stream);
 }
 
 }  // namespace moe

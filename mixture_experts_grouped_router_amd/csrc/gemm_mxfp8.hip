@@ -13,6 +13,7 @@
 //   A codes  x  W_dn codes -> scaled-MFMA grouped GEMM -> bf16 Z
 // Backward: below.  Kernel: grouped_gemm.hpp.
 #include "grouped_gemm.hpp"
+#include "grouped_gemm_w8q.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -179,8 +180,8 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p2.ldc = H;
   p2.rows = rows;
   enable_split(p2, w.split_part, w.split_cnt, w.split_x, cu_count);
-  return launch<P_FP8, KC, KC, RAGGED_M, EPI_STORE>(
-      "gemm_down_mxfp8", p2, ragged_m_grid_split(rows, E, tn2, p2), stream);
+  return launch_w8q<P_FP8>("gemm_down_mxfp8", p2,
+                           ragged_m_grid_split(rows, E, tn2, p2), stream);
 }
 
 // ---- backward ----------------------------------------------------------------

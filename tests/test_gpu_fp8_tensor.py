@@ -69,6 +69,9 @@ FP8T_CASES = [
     (200, 768, 256, 3, 1, 0.0),     # nk = 6: one trip, tail of one
     (300, 1152, 128, 4, 2, 0.0),    # nk = 9: one trip, tail of four
     (260, 1920, 128, 5, 2, 1.2),    # nk = 15: three trips, no tail
+    # the down GEMM's rotation (nk = F / 128)
+    (300, 256, 640, 4, 2, 1.2),     # nk = 5
+    (300, 256, 1152, 4, 2, 0.0),    # nk = 9
 ]
 
 

@@ -668,6 +668,9 @@ MX_CASES = [
     (900, 384, 128, 16, 4, 1.2),    # many experts, some empty
     (512, 256, 8192, 4, 2, 0.0),    # down GEMM's last tiles split along K
     (700, 256, 8192, 8, 2, 1.2),    # the same with empty and one-row experts
+    # operand rotations in whole trips of five K steps plus nk % 5
+    (300, 640, 1152, 4, 2, 1.2),    # gate/up nk = 5, down nk = 9
+    (200, 1152, 640, 3, 1, 0.0),    # gate/up nk = 9, down nk = 5
 ]
 
 
