@@ -119,7 +119,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   p1.tsa = w.scale;
   p1.tsb = w.scale + 2;
   p1.amax_out = w.amax + 1;
-  err = launch<P_FP8T, KC, KC, RAGGED_M, EPI_SWIGLU>(
+  err = launch_w8q<P_FP8T, EPI_SWIGLU>(
       "gemm_gate_up_swiglu_fp8t", p1, ragged_m_grid(rows, E, tn1), stream);
   if (err == hipSuccess)
     err = launch_tensor_quant(a, rows * F, 1, w.amax + 1, w.aq, w.scale + 1,
@@ -145,7 +145,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   p2.tsa = w.scale + 1;
   p2.tsb = w.scale + 2 + E;
   enable_split(p2, w.split_part, w.split_cnt, w.split_x, cu_count);
-  return launch_w8q<P_FP8T>("gemm_down_fp8t", p2,
+  return launch_w8q<P_FP8T, EPI_STORE>("gemm_down_fp8t", p2,
                             ragged_m_grid_split(rows, E, tn2, p2), stream);
 }
 

@@ -154,7 +154,7 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p1.cs_rm = a_s_save;
   p1.w = w_perm;
   p1.rows = rows;
-  err = launch<P_FP8, KC, KC, RAGGED_M, EPI_SWIGLU_MX>(
+  err = launch_w8q<P_FP8, EPI_SWIGLU_MX>(
       "gemm_gate_up_swiglu_mxfp8", p1, ragged_m_grid(rows, E, tn1), stream);
   if (err != hipSuccess) return err;
 
@@ -180,7 +180,7 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p2.ldc = H;
   p2.rows = rows;
   enable_split(p2, w.split_part, w.split_cnt, w.split_x, cu_count);
-  return launch_w8q<P_FP8>("gemm_down_mxfp8", p2,
+  return launch_w8q<P_FP8, EPI_STORE>("gemm_down_mxfp8", p2,
                            ragged_m_grid_split(rows, E, tn2, p2), stream);
 }
 

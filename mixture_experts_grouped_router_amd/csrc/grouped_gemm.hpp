@@ -1089,7 +1089,8 @@ __device__ __forceinline__ bool split_reduce(const Params& p,
 
 template <int EPI>
 struct Shape8 {
-  static constexpr int MI = EPI == EPI_SWIGLU ? 2 : 4;  // 32-row A blocks
+  static constexpr int MI =                             // 32-row A blocks
+      EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX ? 2 : 4;
   static constexpr int NJ = 8 / MI;                     // 32-row B blocks
   static constexpr int WN = 8 / (8 / MI);               // waves along N
 };

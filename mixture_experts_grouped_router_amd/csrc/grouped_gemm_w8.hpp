@@ -39,7 +39,7 @@ struct KcDirect8 {
   __device__ __forceinline__ int row(int blk) const {
     if constexpr (!IS_B) {
       return r0 + 32 * blk + q;
-    } else if constexpr (EPI == EPI_SWIGLU) {
+    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
       const int f = min(n0 + (blk >> 1) * 32 + q, F - 1);
       return (blk & 1) ? F + f : f;
     } else {
@@ -173,7 +173,9 @@ __device__ __forceinline__ void epilogue_w8_store(const Params& p,
 // acc[i][2 jj + 1] is u of f = n0 + 64 wn + 32 jj + lane % 32 at row
 // acc_row(i, r).  Staging in 256-byte rows (stg_off): (g, u) as bf16 for the
 // save, then silu(g) * u as float32; the routing weight and the bf16
-// rounding of A happen per row on readback, as in the four-wave epilogue.
+// rounding of A (EPI_SWIGLU_MX: its MXFP8 quantisation, a quad of lanes per
+// 32-value block) happen per row on readback, as in the four-wave epilogue.
+template <int EPI = EPI_SWIGLU>
 __device__ __forceinline__ void epilogue_w8_swiglu(const Params& p,
                                                    const TileCoord& tc,
                                                    f32x16_t (&acc)[2][4],
@@ -247,6 +249,7 @@ __device__ __forceinline__ void epilogue_w8_swiglu(const Params& p,
   // lane l: rows 8 q + l / 8, f values 8 (l % 8) .. + 7
   const int c8 = lane & 7;
   const int f = f0 + 8 * c8;
+  uint32_t amx = 0;   // amax_out: largest |A| of the lane, bf16 bits
 #pragma unroll
   for (int qb = 0; qb < 8; qb += 4) {
     uint4 c0[4], c1[4];
@@ -261,17 +264,48 @@ __device__ __forceinline__ void epilogue_w8_swiglu(const Params& p,
       const int lr = 8 * (qb + q) + (lane >> 3);
       const int mrow = mw + lr;
       const float wr = wrow[lr];
-      if (fvalid && mrow < tc.seg_len) {
-        const float v[8] = {
-            __uint_as_float(c0[q].x) * wr, __uint_as_float(c0[q].y) * wr,
-            __uint_as_float(c0[q].z) * wr, __uint_as_float(c0[q].w) * wr,
-            __uint_as_float(c1[q].x) * wr, __uint_as_float(c1[q].y) * wr,
-            __uint_as_float(c1[q].z) * wr, __uint_as_float(c1[q].w) * wr};
-        *reinterpret_cast<uint4*>(p.c + (tc.seg0 + mrow) * p.ldc + f) =
+      const bool ok = fvalid && mrow < tc.seg_len;
+      const int64_t row = tc.seg0 + mrow;
+      const float v[8] = {
+          __uint_as_float(c0[q].x) * wr, __uint_as_float(c0[q].y) * wr,
+          __uint_as_float(c0[q].z) * wr, __uint_as_float(c0[q].w) * wr,
+          __uint_as_float(c1[q].x) * wr, __uint_as_float(c1[q].y) * wr,
+          __uint_as_float(c1[q].z) * wr, __uint_as_float(c1[q].w) * wr};
+      if constexpr (EPI == EPI_SWIGLU_MX) {
+        // F % 128 == 0: blocks are whole; every lane takes part in the
+        // quad reduction, rows past the expert just do not store
+        int sx;
+        const uint2 w8 = mx_quad_encode_f32(v, &sx);
+        if (ok) {
+          *reinterpret_cast<uint2*>(p.cq + row * p.F + f) = w8;
+          if ((c8 & 3) == 0) {
+            p.cs[mx_tile_off((uint32_t)row, (uint32_t)(f / 32),
+                             (uint32_t)(p.F / 128))] = (uint8_t)(sx + 127);
+            if (p.cs_rm)
+              p.cs_rm[row * (p.F / 32) + f / 32] = (uint8_t)(sx + 127);
+          }
+        }
+      }
+      if (ok && (EPI == EPI_SWIGLU || p.c)) {
+        const uint4 o =
             make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+        *reinterpret_cast<uint4*>(p.c + row * p.ldc + f) = o;
+        if (p.amax_out) {
+          const uint32_t w4[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            amx = max(amx, max(w4[d] & 0x7fffu, (w4[d] >> 16) & 0x7fffu));
+        }
       }
     }
+  }
+  if (p.amax_out) {
+    // the bf16 magnitudes order like their float32 bits
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+      amx = max(amx, (uint32_t)__shfl_xor((int)amx, off, 64));
+    if (lane == 0) atomicMax(p.amax_out, amx << 16);
   }
 }
 

@@ -1,19 +1,21 @@
-// The 8-bit forward down GEMM (MXFP8, or E4M3 with tensor scales; ragged M,
-// K-contiguous operands, bf16 store) with eight waves per 256 x 256 tile,
-// two per SIMD, and the five-buffer operand rotation of grouped_gemm_w8.hpp
-// (the weight rows two K steps ahead, the token rows one).  The tile list,
-// the split tail, the LDS layout of a step, the per-lane fragment chunks, the
+// The 8-bit forward grouped GEMMs (MXFP8, or E4M3 with tensor scales;
+// ragged M, K-contiguous operands) with eight waves per 256 x 256 tile, two
+// per SIMD, and the five-buffer operand rotation of grouped_gemm_w8.hpp (the
+// weight rows two K steps ahead, the token rows one).  The tile list, the
+// split tail, the LDS layout of a step, the per-lane fragment chunks, the
 // scale bytes and the scaled MFMA are those of the four-wave kernel in
 // grouped_gemm.hpp, so every output element is the same sum of the same
 // products (outputs are bit for bit those of the four-wave kernel, except in
 // split tiles, whose partial sums run in another order).
 //
-// Wave shape: 128 rows x 64 columns (a 2 x 4 wave grid), i.e. four 32-row A
-// blocks and two 32-row B blocks, eight MFMAs (32 x 32 x 64, one scale per
-// 32 K values) per 64-wide K slice, two slices per 128-wide K step.  With
-// 256 registers per wave, fragments are read half a slice ahead (two A
-// blocks, and the B blocks once per slice) instead of a whole slice: 64
-// registers of fragments instead of 96.
+// Wave shapes as in grouped_gemm_w8.hpp: EPI_STORE (down GEMM) 128 rows x 64
+// columns, four 32-row A blocks and two B blocks; the SwiGLU epilogues
+// (gate/up GEMM) 64 rows x 128 B rows, two A blocks and four B blocks (gate
+// and up of 64 f).  Eight MFMAs (32 x 32 x 64, one scale per 32 K values)
+// per 64-wide K slice, two slices per 128-wide K step.  With 256 registers
+// per wave, fragments are read half a slice ahead (two of the four blocks
+// of the operand that has four, the other operand's two once per slice)
+// instead of a whole slice: 64 registers of fragments instead of 96.
 #pragma once
 
 #include "grouped_gemm_w8.hpp"
@@ -33,10 +35,17 @@ __device__ __forceinline__ i32x8_t q_frag(const char* s, uint32_t o0,
   return v;
 }
 
-template <int P>
+template <int P, int EPI>
 __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   static_assert(P == P_FP8 || P == P_FP8T, "8-bit operands");
-  constexpr int MI = 4, NJ = 2;   // 32-row A / B blocks of a wave
+  static_assert(EPI == EPI_STORE ||
+                    (P == P_FP8 ? EPI == EPI_SWIGLU_MX : EPI == EPI_SWIGLU),
+                "forward epilogues");
+  using S = Shape8<EPI>;
+  constexpr int MI = S::MI, NJ = S::NJ;   // 32-row A / B blocks of a wave
+  // the operand with four blocks is read in halves (X), the other (Y)
+  // once per slice
+  constexpr bool kXa = MI == 4;
   constexpr int kStepK = 128;     // K values per step (one byte each)
   __shared__ __attribute__((aligned(1024))) char sA0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sB0[kTileBytes];
@@ -52,12 +61,12 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
 
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 2;   // 0..1: rows wm * 128
-  const int wn = wave & 3;    // 0..3: columns wn * 64
-  const int n0 = tc.nt * BN;
+  const int wm = wave / S::WN;   // rows wm * 32 MI
+  const int wn = wave % S::WN;   // B rows wn * 32 NJ
+  const int n0 = EPI == EPI_STORE ? tc.nt * BN : tc.nt * (BN / 2);
 
-  KcDirect8<EPI_STORE, false> da;
-  KcDirect8<EPI_STORE, true> db;
+  KcDirect8<EPI, false> da;
+  KcDirect8<EPI, true> db;
   const int q = 8 * (wave & 3) + (lane >> 3);
   const int cl = (lane & 7) ^ swz32(q);
   // rows past the expert's last read as zeros (buffer descriptor range);
@@ -85,7 +94,11 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   // the step, bytes (g, 2 + g) moved to (0, 1) so that the MFMA's opsel
   // picks slice kk's byte (as in the four-wave kernel).
   constexpr uint32_t kS0 = P == P_FP8T ? 0x7f7f7f7fu : 0u;
-  uint32_t sa[MI] = {kS0, kS0, kS0, kS0}, sb[NJ] = {kS0, kS0};
+  uint32_t sa[MI], sb[NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) sa[i] = kS0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) sb[j] = kS0;
   uint32_t na[MI], nb[NJ];
   uint32_t soa[MI], sob[NJ];
   const uint8_t* sca = nullptr;
@@ -97,17 +110,18 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
     scb = p.sb + (int64_t)tc.e * p.sb_es + kofs;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int ra = min(tc.m0 + wm * 128 + 32 * i + (lane & 31),
+      const int ra = min(tc.m0 + wm * 32 * MI + 32 * i + (lane & 31),
                          tc.seg_len - 1);
       soa[i] = mx_tile_off((uint32_t)(tc.seg0 + ra), 0, (uint32_t)p.ldsa);
     }
-    KcDirect8<EPI_STORE, true> m;   // B row of the lane's 32-row blocks
+    KcDirect8<EPI, true> m;   // B row of the lane's 32-row blocks
     m.q = lane & 31;
     m.n0 = n0;
+    m.F = p.F;
     m.N = p.N;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      sob[j] = mx_tile_off((uint32_t)m.row(2 * wn + j), 0, (uint32_t)p.ldsb);
+      sob[j] = mx_tile_off((uint32_t)m.row(NJ * wn + j), 0, (uint32_t)p.ldsb);
   }
   auto load_scales = [&](int ks) {
     if constexpr (P == P_FP8) {
@@ -140,7 +154,7 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   // A wave whose rows all lie past the expert's last row issues its share
   // of the direct loads and meets the barriers only (see grouped_gemm_w8.hpp)
   const bool act = __builtin_amdgcn_readfirstlane(
-                       tc.m0 + wm * 128 < tc.seg_len ? 1 : 0) != 0;
+                       tc.m0 + wm * 32 * MI < tc.seg_len ? 1 : 0) != 0;
 
   using std::integral_constant;
   auto buf = [&](auto nc) -> char* {
@@ -158,7 +172,8 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   // per buffer, slice, chunk and operand.
   const uint32_t rowoff = (uint32_t)((lane & 31) * kRowBytes);
   const uint32_t xsw = (uint32_t)(swz32(lane & 31) ^ (lane >> 5));
-  const int a_wave = wm * 128 * kRowBytes, b_wave = wn * 64 * kRowBytes;
+  const int a_wave = wm * 32 * MI * kRowBytes;
+  const int b_wave = wn * 32 * NJ * kRowBytes;
   struct Offs { uint32_t o0, o1; };
   auto offs = [&](int kk) {
     uint32_t r = rowoff, x = xsw;
@@ -166,30 +181,33 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
     return Offs{r + (((uint32_t)(4 * kk) ^ x) << 4),
                 r + (((uint32_t)(4 * kk + 2) ^ x) << 4)};
   };
-  // fragments: A blocks 0-1 (A0) and 2-3 (A1) of a slice, B of the slice
-  // (Bc for slice 0, Bn for slice 1)
-  i32x8_t A0[2], A1[2], Bc[2], Bn[2];
-  auto read_a = [&](i32x8_t (&f)[2], const char* s, const Offs& o, int half) {
+  // fragments: X blocks 0-1 (X0) and 2-3 (X1) of a slice, Y of the slice
+  // (Yc for slice 0, Yn for slice 1); X = A for EPI_STORE, else B
+  i32x8_t X0[2], X1[2], Yc[2], Yn[2];
+  const int x_wave = kXa ? a_wave : b_wave, y_wave = kXa ? b_wave : a_wave;
+  // (x, y: the step's A and B buffers in X / Y order)
+  auto read_x = [&](i32x8_t (&f)[2], const char* s, const Offs& o, int half) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
-      f[b] = q_frag(s, o.o0, o.o1, a_wave + (2 * half + b) * 32 * kRowBytes);
+      f[b] = q_frag(s, o.o0, o.o1, x_wave + (2 * half + b) * 32 * kRowBytes);
   };
-  auto read_b = [&](i32x8_t (&f)[2], const char* s, const Offs& o) {
+  auto read_y = [&](i32x8_t (&f)[2], const char* s, const Offs& o) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
-      f[b] = q_frag(s, o.o0, o.o1, b_wave + b * 32 * kRowBytes);
+      f[b] = q_frag(s, o.o0, o.o1, y_wave + b * 32 * kRowBytes);
   };
-  // MFMAs of A half `half` x B of slice KK; first / last n of the four
-  auto mma = [&](auto kkc, auto halfc, const i32x8_t (&fa)[2],
-                 const i32x8_t (&fb)[2], auto m0c, auto m1c) {
+  // MFMAs of X half `half` x Y of slice KK; first / last n of the four
+  auto mma = [&](auto kkc, auto halfc, const i32x8_t (&fx)[2],
+                 const i32x8_t (&fy)[2], auto m0c, auto m1c) {
     constexpr int KK = decltype(kkc)::value, H = decltype(halfc)::value;
     constexpr int M0 = decltype(m0c)::value, M1 = decltype(m1c)::value;
 #pragma unroll
     for (int m = M0; m < M1; ++m) {
-      const int ii = m >> 1, jj = m & 1;
-      acc[2 * H + ii][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          fa[ii], fb[jj], acc[2 * H + ii][jj], 0, 0, KK, (int)sa[2 * H + ii],
-          KK, (int)sb[jj]);
+      const int xx = m >> 1, yy = m & 1;
+      const int i = kXa ? 2 * H + xx : yy, j = kXa ? yy : 2 * H + xx;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          kXa ? fx[xx] : fy[yy], kXa ? fy[yy] : fx[xx], acc[i][j], 0, 0, KK,
+          (int)sa[i], KK, (int)sb[j]);
     }
   };
   using I0 = integral_constant<int, 0>;
@@ -216,44 +234,48 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
     char* const bn = buf(integral_constant<int, 2 * j + 2>{});
     char* const an = buf(integral_constant<int, 2 * j + 3>{});
     char* const bn2 = buf(integral_constant<int, 2 * j + 4>{});
-    // slice 0, A blocks 0-1: A_{k+1} and the scales out; A blocks 2-3 in
+    const char* const x = kXa ? a : b;
+    const char* const y = kXa ? b : a;
+    const char* const xn = kXa ? an : bn;
+    const char* const yn = kXa ? bn : an;
+    // slice 0, X blocks 0-1: A_{k+1} and the scales out; X blocks 2-3 in
     {
       const Offs o = offs(0);
       da.issue(an, (uint32_t)(k + 1) * kRowBytes, k + 1 < nk, wave);
       load_scales(min(k + 1, nk - 1));
-      read_a(A1, a, o, 1);
-      mma(I0{}, I0{}, A0, Bc, I0{}, I4{});
+      read_x(X1, x, o, 1);
+      mma(I0{}, I0{}, X0, Yc, I0{}, I4{});
       sched_vmem_reads_mfma<kVmA, 4, 4, 3>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    // slice 0, A blocks 2-3; slice 1's A blocks 0-1 and B in
+    // slice 0, X blocks 2-3; slice 1's X blocks 0-1 and Y in
     {
       const Offs o = offs(1);
-      read_a(A0, a, o, 0);
-      read_b(Bn, b, o);
-      mma(I0{}, I1{}, A1, Bc, I0{}, I4{});
+      read_x(X0, x, o, 0);
+      read_y(Yn, y, o);
+      mma(I0{}, I1{}, X1, Yc, I0{}, I4{});
       sched_reads_mfma<8, 4>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    // slice 1, A blocks 0-1: B_{k+2} out; A blocks 2-3 in
+    // slice 1, X blocks 0-1: B_{k+2} out; X blocks 2-3 in
     {
       const Offs o = offs(1);
       db.issue(bn2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
-      read_a(A1, a, o, 1);
-      mma(I1{}, I0{}, A0, Bn, I0{}, I4{});
+      read_x(X1, x, o, 1);
+      mma(I1{}, I0{}, X0, Yn, I0{}, I4{});
       sched_vmem_reads_mfma<4, 4, 4, 2>();
       __builtin_amdgcn_sched_barrier(0);
     }
-    // slice 1, A blocks 2-3: two MFMAs, publish step k + 1, its first
+    // slice 1, X blocks 2-3: two MFMAs, publish step k + 1, its first
     // fragments under the last two
     {
       const Offs o = offs(0);
-      mma(I1{}, I1{}, A1, Bn, I0{}, I2{});
+      mma(I1{}, I1{}, X1, Yn, I0{}, I2{});
       __builtin_amdgcn_sched_barrier(0);
       publish();
-      read_a(A0, an, o, 0);
-      read_b(Bc, bn, o);
-      mma(I1{}, I1{}, A1, Bn, I2{}, I4{});
+      read_x(X0, xn, o, 0);
+      read_y(Yc, yn, o);
+      mma(I1{}, I1{}, X1, Yn, I2{}, I4{});
       take_scales();
       sched_reads_mfma<8, 2>();
       __builtin_amdgcn_sched_barrier(0);
@@ -279,8 +301,8 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   if (act) {
     take_scales();
     const Offs o = offs(0);
-    read_a(A0, sB0, o, 0);
-    read_b(Bc, sA0, o);
+    read_x(X0, kXa ? sB0 : sA0, o, 0);
+    read_y(Yc, kXa ? sA0 : sB0, o);
   }
   // whole trips of five steps, then the last nk % 5
   const int trips = nk / 5, rem = nk - 5 * trips;
@@ -333,15 +355,19 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   }
   char* wbuf = (wave < 2 ? sA0 : wave < 4 ? sB0 : wave < 6 ? sA1 : sB1) +
                (wave & 1) * (kTileBytes / 2);
-  epilogue_w8_store(p, tc, acc, n0, wm, wn, lane, wbuf);
+  if constexpr (EPI == EPI_STORE)
+    epilogue_w8_store(p, tc, acc, n0, wm, wn, lane, wbuf);
+  else   // routing weights in the fifth buffer (64 floats per wave)
+    epilogue_w8_swiglu<EPI>(p, tc, acc, n0, wm, wn, lane, wave, wbuf,
+                            reinterpret_cast<float*>(sX4) + 64 * wave);
 }
 
-template <int P>
+template <int P, int EPI>
 hipError_t launch_w8q(const char* name, const Params& p, int grid,
                       hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   KernelScope ks(name, stream);
-  hipLaunchKernelGGL((grouped_gemm_w8q_kernel<P>), dim3(grid),
+  hipLaunchKernelGGL((grouped_gemm_w8q_kernel<P, EPI>), dim3(grid),
                      dim3(kThreads8), 0, stream, p);
   return hipGetLastError();
 }
