@@ -422,7 +422,7 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
     q.c = static_cast<uint16_t*>(dx_perm);
     q.ldc = H;
     q.rows = rows;
-    err = launch<P_FP8, KC, KC, RAGGED_M, EPI_STORE>(
+    err = launch_w8q<P_FP8, EPI_STORE>(
         "gemm_dgrad_gate_up_mxfp8", q, ragged_m_grid(rows, E, tnh), stream);
     if (err != hipSuccess) return err;
 
