@@ -302,7 +302,7 @@ hipError_t wgrad_mx(const char* name, int E, int M, int N, int64_t ld,
   p.c = static_cast<uint16_t*>(dw);
   p.ldc = N;
   p.c_es = (int64_t)M * N;
-  return launch<P_FP8, KC, KC, RAGGED_K, EPI_STORE>(
+  return launch_w8q<P_FP8, EPI_STORE, RAGGED_K>(
       name, p, ragged_k_grid(E, p.tiles_m, p.tiles_n), stream);
 }
 

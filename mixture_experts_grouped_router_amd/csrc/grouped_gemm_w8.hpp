@@ -121,7 +121,9 @@ __device__ __forceinline__ int stg8(int r, int c) {
 
 // EPI_STORE of a wave's 128 x 64 block (acc[i][j][r]: row acc_row(i, r),
 // column 32 j + lane % 32) through its 16 KiB of LDS: 128-byte rows of 64
-// bf16; on readback lane l takes chunk l % 8 of row 8 q + l / 8.
+// bf16; on readback lane l takes chunk l % 8 of row 8 q + l / 8.  RAGGED_K
+// (weight gradients): rows are those of expert e's [M, N] output.
+template <int G = RAGGED_M>
 __device__ __forceinline__ void epilogue_w8_store(const Params& p,
                                                   const TileCoord& tc,
                                                   f32x16_t (&acc)[4][2],
@@ -153,6 +155,10 @@ __device__ __forceinline__ void epilogue_w8_store(const Params& p,
   __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
   const int ch = lane & 7;
   const int col = n0 + wn * 64 + 8 * ch;   // N % 64 == 0
+  uint16_t* cbase = p.c;
+  if constexpr (G == RAGGED_K) cbase += (int64_t)tc.e * p.c_es;
+  const int mlim = G == RAGGED_M ? tc.seg_len : p.M;
+  const int64_t rbase = G == RAGGED_M ? tc.seg0 : 0;
 #pragma unroll
   for (int qb = 0; qb < 16; qb += 8) {
     uint4 v[8];
@@ -163,8 +169,8 @@ __device__ __forceinline__ void epilogue_w8_store(const Params& p,
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int mrow = mw + 8 * (qb + q) + (lane >> 3);
-      if (col < p.N && mrow < tc.seg_len)
-        *reinterpret_cast<uint4*>(p.c + (tc.seg0 + mrow) * p.ldc + col) = v[q];
+      if (col < p.N && mrow < mlim)
+        *reinterpret_cast<uint4*>(cbase + (rbase + mrow) * p.ldc + col) = v[q];
     }
   }
 }

@@ -8,6 +8,10 @@
 // products (outputs are bit for bit those of the four-wave kernel, except in
 // split tiles, whose partial sums run in another order).
 //
+// Ragged K (weight gradients, EPI_STORE): the tile list, operand ranges and
+// scales of the four-wave kernel's RAGGED_K case (expert e's [M, N] tiles,
+// K = its padded tokens; an expert without tokens stores zeros).
+//
 // Wave shapes as in grouped_gemm_w8.hpp: EPI_STORE (down GEMM) 128 rows x 64
 // columns, four 32-row A blocks and two B blocks; the SwiGLU epilogues
 // (gate/up GEMM) 64 rows x 128 B rows, two A blocks and four B blocks (gate
@@ -35,12 +39,13 @@ __device__ __forceinline__ i32x8_t q_frag(const char* s, uint32_t o0,
   return v;
 }
 
-template <int P, int EPI>
+template <int P, int EPI, int G>
 __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   static_assert(P == P_FP8 || P == P_FP8T, "8-bit operands");
   static_assert(EPI == EPI_STORE ||
                     (P == P_FP8 ? EPI == EPI_SWIGLU_MX : EPI == EPI_SWIGLU),
                 "forward epilogues");
+  static_assert(G == RAGGED_M || EPI == EPI_STORE, "ragged K: plain store");
   using S = Shape8<EPI>;
   constexpr int MI = S::MI, NJ = S::NJ;   // 32-row A / B blocks of a wave
   // the operand with four blocks is read in halves (X), the other (Y)
@@ -52,12 +57,20 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char sA1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sB1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sX4[kTileBytes];
-  const int nk_all = (p.K + kStepK - 1) / kStepK;
   const int t = threadIdx.x;
   TileCoord tc;
   SplitRange sr;
-  if (!decode_item(p, nk_all, blockIdx.x % kXcds, blockIdx.x / kXcds, tc, sr))
-    return;
+  if constexpr (G == RAGGED_M) {
+    const int nk_all = (p.K + kStepK - 1) / kStepK;
+    if (!decode_item(p, nk_all, blockIdx.x % kXcds, blockIdx.x / kXcds, tc,
+                     sr))
+      return;
+  } else {
+    if (!decode_tile<RAGGED_K>(p, tc)) return;
+    sr.ks = 0;
+    sr.ke = (tc.seg_len + kStepK - 1) / kStepK;   // 0 for an empty expert
+    sr.S = 1;
+  }
 
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -71,15 +84,24 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   const int cl = (lane & 7) ^ swz32(q);
   // rows past the expert's last read as zeros (buffer descriptor range);
   // a split work-group starts at K step ks
-  const uint32_t kofs = (uint32_t)sr.ks * kRowBytes;
-  da.base = p.a + (int64_t)tc.seg0 * p.lda + kofs;
-  da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda - kofs;
+  // (ragged K: the expert's K range starts at byte seg0 of every row of
+  // both operands, a multiple of the K step; rows past M read as zeros)
+  const uint32_t kofs =
+      G == RAGGED_M ? (uint32_t)sr.ks * kRowBytes : (uint32_t)tc.seg0;
+  if constexpr (G == RAGGED_M) {
+    da.base = p.a + (int64_t)tc.seg0 * p.lda + kofs;
+    da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda - kofs;
+    db.base = p.b + (int64_t)tc.e * p.b_es + kofs;
+  } else {
+    da.base = p.a + kofs;
+    da.rec = (uint32_t)p.M * (uint32_t)p.lda - kofs;
+    db.base = p.b + kofs;
+  }
   da.ld = p.lda;
   da.q = q;
   da.cl = cl;
   da.r0 = tc.m0;
   da.init(wave);
-  db.base = p.b + (int64_t)tc.e * p.b_es + kofs;
   db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb - kofs;
   db.ld = p.ldb;
   db.q = q;
@@ -105,14 +127,16 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   const uint8_t* scb = nullptr;
   const uint32_t sel = (lane >> 5) ? 0x0c0c0301u : 0x0c0c0200u;
   if constexpr (P == P_FP8) {
-    // scales of K step s at byte 128 s of a row block's run
+    // scales of K step s at byte 128 s of a row block's run (ragged K: the
+    // expert's first K step at byte seg0)
     sca = p.sa + kofs;
-    scb = p.sb + (int64_t)tc.e * p.sb_es + kofs;
+    scb = p.sb + (G == RAGGED_M ? (int64_t)tc.e * p.sb_es : 0) + kofs;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int ra = min(tc.m0 + wm * 32 * MI + 32 * i + (lane & 31),
-                         tc.seg_len - 1);
-      soa[i] = mx_tile_off((uint32_t)(tc.seg0 + ra), 0, (uint32_t)p.ldsa);
+                         (G == RAGGED_M ? tc.seg_len : p.M) - 1);
+      const uint32_t rabs = G == RAGGED_M ? (uint32_t)(tc.seg0 + ra) : ra;
+      soa[i] = mx_tile_off(rabs, 0, (uint32_t)p.ldsa);
     }
     KcDirect8<EPI, true> m;   // B row of the lane's 32-row blocks
     m.q = lane & 31;
@@ -153,8 +177,10 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   const int nk = sr.ke - sr.ks;
   // A wave whose rows all lie past the expert's last row issues its share
   // of the direct loads and meets the barriers only (see grouped_gemm_w8.hpp)
-  const bool act = __builtin_amdgcn_readfirstlane(
-                       tc.m0 + wm * 32 * MI < tc.seg_len ? 1 : 0) != 0;
+  const bool act =
+      __builtin_amdgcn_readfirstlane(
+          tc.m0 + wm * 32 * MI < (G == RAGGED_M ? tc.seg_len : p.M) ? 1
+                                                                     : 0) != 0;
 
   using std::integral_constant;
   auto buf = [&](auto nc) -> char* {
@@ -293,9 +319,9 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   };
   // prologue: B_0 into buffer 0, A_0 (+ scales of step 0) into buffer 1,
   // then B_1 into buffer 2 (left in flight)
-  db.issue(sA0, 0u, true, wave);
-  da.issue(sB0, 0u, true, wave);
-  if (act) load_scales(0);
+  db.issue(sA0, 0u, nk > 0, wave);
+  da.issue(sB0, 0u, nk > 0, wave);
+  if (act && nk > 0) load_scales(0);
   db.issue(sA1, (uint32_t)kRowBytes, 1 < nk, wave);
   publish();
   if (act) {
@@ -356,18 +382,18 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8q_kernel(Params p) {
   char* wbuf = (wave < 2 ? sA0 : wave < 4 ? sB0 : wave < 6 ? sA1 : sB1) +
                (wave & 1) * (kTileBytes / 2);
   if constexpr (EPI == EPI_STORE)
-    epilogue_w8_store(p, tc, acc, n0, wm, wn, lane, wbuf);
+    epilogue_w8_store<G>(p, tc, acc, n0, wm, wn, lane, wbuf);
   else   // routing weights in the fifth buffer (64 floats per wave)
     epilogue_w8_swiglu<EPI>(p, tc, acc, n0, wm, wn, lane, wave, wbuf,
                             reinterpret_cast<float*>(sX4) + 64 * wave);
 }
 
-template <int P, int EPI>
+template <int P, int EPI, int G = RAGGED_M>
 hipError_t launch_w8q(const char* name, const Params& p, int grid,
                       hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   KernelScope ks(name, stream);
-  hipLaunchKernelGGL((grouped_gemm_w8q_kernel<P, EPI>), dim3(grid),
+  hipLaunchKernelGGL((grouped_gemm_w8q_kernel<P, EPI, G>), dim3(grid),
                      dim3(kThreads8), 0, stream, p);
   return hipGetLastError();
 }

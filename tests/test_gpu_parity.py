@@ -769,6 +769,10 @@ MX_BWD_CASES = [
     (700, 256, 384, 5, 2, 1.2),     # ragged token segments, odd K steps
     (900, 384, 128, 16, 4, 1.2),    # many experts, some empty
     (130, 128, 128, 3, 1, 0.0),     # k = 1, segments shorter than a K step
+    # weight gradients with longer token segments: whole trips of the
+    # operand rotation (1200 tokens per expert, 10 K steps) and a tail
+    (1200, 256, 256, 2, 2, 0.0),
+    (1500, 128, 256, 3, 2, 1.2),
 ]
 
 
