@@ -66,16 +66,17 @@ def parse():
 
 
 # library kernel name -> template instantiations in profiler kernel names
-# (the bf16 forward runs the eight-wave kernel for the down GEMM, and for
-# gate/up up to H = 4096)
+# (the forward GEMMs run the eight-wave kernels: bf16 grouped_gemm_w8_kernel
+# <EPI, BAR_END, ROT> for the down GEMM and for gate/up up to H = 4096,
+# 8-bit grouped_gemm_w8q_kernel<P, EPI, G>)
 KERNEL_SYMBOL = {
     "gemm_gate_up_swiglu_bf16": ("grouped_gemm_kernel<0, 0, 0, 0, 1>",
                                  "grouped_gemm_w8_kernel<1,"),
     "gemm_down_bf16": ("grouped_gemm_w8_kernel<0,",),
-    "gemm_gate_up_swiglu_mxfp8": ("grouped_gemm_kernel<1, 0, 0, 0, 3>",),
-    "gemm_down_mxfp8": ("grouped_gemm_kernel<1, 0, 0, 0, 0>",),
-    "gemm_gate_up_swiglu_fp8t": ("grouped_gemm_kernel<2, 0, 0, 0, 1>",),
-    "gemm_down_fp8t": ("grouped_gemm_kernel<2, 0, 0, 0, 0>",),
+    "gemm_gate_up_swiglu_mxfp8": ("grouped_gemm_w8q_kernel<1, 3, 0>",),
+    "gemm_down_mxfp8": ("grouped_gemm_w8q_kernel<1, 0, 0>",),
+    "gemm_gate_up_swiglu_fp8t": ("grouped_gemm_w8q_kernel<2, 1, 0>",),
+    "gemm_down_fp8t": ("grouped_gemm_w8q_kernel<2, 0, 0>",),
 }
 
 
