@@ -12,6 +12,7 @@
 // the forward GEMMs grouped_gemm_w8.hpp (eight waves per tile).
 #include "grouped_gemm.hpp"
 #include "grouped_gemm_w8.hpp"
+#include "grouped_gemm_w8b.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -332,8 +333,8 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     q.c = static_cast<uint16_t*>(dx_perm);
     q.ldc = H;
     q.rows = rows;
-    err = launch<P_BF16, KC, MC, RAGGED_M, EPI_STORE>("gemm_dgrad_gate_up", q, ragged_m_grid(rows, E, tnh),
-                                              stream);
+    err = launch_w8b<KC, MC, RAGGED_M>("gemm_dgrad_gate_up", q,
+                                       ragged_m_grid(rows, E, tnh), stream);
     if (err != hipSuccess) return err;
   }
   // wgrad2: dW_dn[e] [H, F] = dZ_e^T A_e   (K = rows of expert e)
@@ -357,8 +358,7 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     p.c_es = (int64_t)H * F;
     p.rows = rows;
     const int grid = ragged_k_grid(E, p.tiles_m, p.tiles_n);
-    err = launch<P_BF16, MC, MC, RAGGED_K, EPI_STORE>("gemm_wgrad_down", p,
-                                                      grid, stream);
+    err = launch_w8b<MC, MC, RAGGED_K>("gemm_wgrad_down", p, grid, stream);
     if (err != hipSuccess) return err;
   }
   // wgrad1: dW_gu[e] [2F, H] = dH1_e^T X_e
@@ -380,8 +380,7 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     p.c_es = (int64_t)2 * F * H;
     p.rows = rows;
     const int grid = ragged_k_grid(E, p.tiles_m, p.tiles_n);
-    err = launch<P_BF16, MC, MC, RAGGED_K, EPI_STORE>("gemm_wgrad_gate_up",
-                                                      p, grid, stream);
+    err = launch_w8b<MC, MC, RAGGED_K>("gemm_wgrad_gate_up", p, grid, stream);
   }
   return err;
 }

@@ -627,6 +627,10 @@ BWD_CASES = [
     (256, 128, 256, 8, 2, 0.0),
     (700, 192, 320, 5, 2, 1.2),
     (900, 256, 128, 16, 4, 1.2),
+    # weight gradients over longer token segments (the operand rotation's
+    # whole trips and tails along the tokens)
+    (1200, 128, 256, 2, 2, 0.0),
+    (1000, 192, 192, 3, 1, 1.2),
 ]
 
 
