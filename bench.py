@@ -550,12 +550,50 @@ def hbm_extras(m, layer, cfg, st):
     ref = round(cb / (cms * 1e-3) / 1e9, 1)
     for v in res.values():
         v["frac_of_stream"] = round(v["GB/s"] / ref, 4)
-    del flush, src, dst
+    del src, dst
+    # the device's ceiling for each traffic mix: 256 MiB buffers (larger
+    # than the Infinity Cache), read r and write w of them, caches flushed
+    mb = 1 << 28
+    msrc = torch.empty(2 * mb, dtype=torch.uint8, device="cuda")
+    msrc.fill_(3)
+    mdst = torch.empty(2 * mb, dtype=torch.uint8, device="cuda")
+    mix = {}
+    for name, r, w in (("read", 1, 0), ("write", 0, 1), ("copy", 1, 1),
+                       ("1 read 2 writes (gather, k = 2)", 1, 2),
+                       ("2 reads 1 write (combine, k = 2)", 2, 1)):
+        ts = []
+        for _ in range(5):
+            flush.fill_(1.0)
+            m.reset_kernel_timing()
+            m.set_kernel_timing(True)
+            m._check(layer.lib.moe_hbm_stream_mix(
+                ctx, msrc.data_ptr(), mb, r, w, mdst.data_ptr(), st))
+            m.set_kernel_timing(False)
+            torch.cuda.synchronize()
+            n, tot = m.kernel_time("hbm_stream_mix")
+            ts.append(tot / max(n, 1))
+        gbs = (r + w) * mb / (float(np.median(ts)) * 1e-3) / 1e9
+        mix[name] = {"GB/s": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    m.reset_kernel_timing()
+    del flush, msrc, mdst
+    if cfg.k == 2:
+        # the MXFP8 gather writes about as many bytes as it reads
+        ceil = {"permute_gather": "1 read 2 writes (gather, k = 2)",
+                "permute_gather_mxfp8": "copy",
+                "unpermute": "2 reads 1 write (combine, k = 2)"}
+        for kname, v in res.items():
+            v["frac_of_mix_ceiling"] = round(
+                v["GB/s"] / mix[ceil[kname]]["GB/s"], 4)
     return {"kernels": res,
             "stream_reference": {
                 "GB/s": ref, "frac_hbm": round(ref / PEAK_HBM_GBS, 4),
                 "bytes": cb, "what": f"moe_hbm_stream_reference: read "
-                f"{nbytes} bytes once, write {cfg.k} copies, caches flushed"}}
+                f"{nbytes} bytes once, write {cfg.k} copies, caches flushed"},
+            "mix_ceilings": dict(
+                mix, what="moe_hbm_stream_mix: 256 MiB buffers, read r and "
+                "write w of them with 16-byte nontemporal vectors, caches "
+                "flushed (GB/s of bytes read + written)")}
 
 
 def dataclasses_replace(c):

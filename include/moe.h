@@ -127,6 +127,19 @@ moe_status_t moe_hbm_stream_reference(moe_ctx_t ctx, const void* src,
                                       int64_t bytes, int32_t k, void* dst,
                                       void* stream);
 
+/* moe_hbm_stream_mix -- a measurement aid, not a step of the path: reads
+ * `reads` (0..2) buffers of `bytes` each from src ([reads][bytes]) and
+ * writes `writes` (0..2) copies of their bitwise xor (of a constant when
+ * reads = 0) to dst ([writes][bytes]; with writes = 0 nothing is stored,
+ * dst must still hold 4 KiB), reads + writes >= 1, device memory, 16-byte
+ * aligned, bytes % 16 == 0: the HBM bandwidth of each traffic mix (read
+ * only, write only, copy, one read and two writes as the permute's gather,
+ * two reads and one write as the combine) on this device.  Kernel name
+ * "hbm_stream_mix" for moe_ctx_kernel_time. */
+moe_status_t moe_hbm_stream_mix(moe_ctx_t ctx, const void* src, int64_t bytes,
+                                int32_t reads, int32_t writes, void* dst,
+                                void* stream);
+
 /* ------------------------------------------------------------------------
  * moe_router_logits -- router projection in front of the top-k.
  * [PG3, practical-implications paragraph: Top-k routing; PG4, section

@@ -121,6 +121,7 @@ _SIGS = {
                                            ctypes.POINTER(_c_sz)],
     "moe_grouped_mlp_bwd": [_c_p, ctypes.POINTER(_BwdArgs), _c_p],
     "moe_hbm_stream_reference": [_c_p, _c_p, _c_i64, _c_i32, _c_p, _c_p],
+    "moe_hbm_stream_mix": [_c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_p, _c_p],
     "moe_ctx_set_kernel_timing": [_c_p, _c_i32],
     "moe_ctx_reset_kernel_timing": [_c_p],
     "moe_ctx_kernel_time": [_c_p, ctypes.c_char_p, ctypes.POINTER(_c_i64),

@@ -201,6 +201,26 @@ moe_status_t moe_hbm_stream_reference(moe_ctx_t ctx, const void* src,
                     "hbm stream reference");
 }
 
+moe_status_t moe_hbm_stream_mix(moe_ctx_t ctx, const void* src, int64_t bytes,
+                                int32_t reads, int32_t writes, void* dst,
+                                void* stream) {
+  moe_status_t s = check_ctx(ctx);
+  if (s != MOE_OK) return s;
+  TimerGuard tg(ctx);
+  MOE_REQUIRE(bytes >= 0 && reads >= 0 && reads <= 2 && writes >= 0 &&
+                  writes <= 2 && reads + writes >= 1,
+              MOE_ERR_INVALID_ARG, "bad sizes");
+  MOE_REQUIRE(bytes % 16 == 0, MOE_ERR_UNSUPPORTED, "bytes %% 16 != 0");
+  if (bytes == 0) return ok();
+  MOE_REQUIRE(dst && (src || reads == 0), MOE_ERR_INVALID_ARG,
+              "null pointer");
+  MOE_REQUIRE(aligned16(src) && aligned16(dst), MOE_ERR_UNSUPPORTED,
+              "src / dst must be 16-byte aligned");
+  return hip_status(moe::launch_hbm_mix(src, bytes, reads, writes, dst,
+                                        ctx->cu_count, as_stream(stream)),
+                    "hbm stream mix");
+}
+
 moe_status_t moe_fp8_tensor_quantize_workspace_size(int64_t n_seg,
                                                     size_t* bytes) {
   MOE_REQUIRE(bytes != nullptr && n_seg >= 0, MOE_ERR_INVALID_ARG,

@@ -7,7 +7,10 @@
 // and stores -- plain ones reached only 3.6-4.3 TB/s -- with each block
 // taking a contiguous 16 KiB per trip (four vectors per thread) and 32
 // blocks per CU: 5.43 TB/s at 64 MiB, 5.80 TB/s at 128 MiB; one block per
-// 8 KiB row (the gather's shape) 5.18 / 5.59 TB/s.
+// 8 KiB row (the gather's shape) 5.18 / 5.59 TB/s.  The mix stream reads 0-2
+// buffers and writes 0-2 copies (read only, write only, copy, the gather's
+// one read and two writes, the combine's two reads and one write), the
+// ceilings for each traffic mix.
 #include <algorithm>
 
 #include "common.hpp"
@@ -40,7 +43,74 @@ __global__ __launch_bounds__(256) void hbm_stream_kernel(
     }
   }
 }
+
+// Read R buffers of n16 vectors (R = 0..2) and write W copies (W = 0..2) of
+// their bitwise xor (of the float 1.0 in every word when R = 0); with W = 0
+// a block writes its xor only if it equals a value the data never holds,
+// so the loads are kept and nothing is stored.
+template <int R>
+__global__ __launch_bounds__(256) void hbm_mix_kernel(
+    const uint4* __restrict__ src, int64_t n16, int w,
+    uint4* __restrict__ dst) {
+  constexpr int64_t per = 256 * kStreamUnroll;
+  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+  for (int64_t b0 = (int64_t)blockIdx.x * per; b0 < n16;
+       b0 += (int64_t)gridDim.x * per) {
+    uint4 v[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u)
+      v[u] = R == 0 ? make_uint4(0x3f800000u, 0x3f800000u, 0x3f800000u,
+                                 0x3f800000u)
+                    : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        const int64_t i = b0 + 256 * u + threadIdx.x;
+        if (i < n16) {
+          const uint4 x = ld_nt(src + (int64_t)r * n16 + i);
+          v[u].x ^= x.x; v[u].y ^= x.y; v[u].z ^= x.z; v[u].w ^= x.w;
+        }
+      }
+    for (int j = 0; j < w; ++j) {
+#pragma unroll
+      for (int u = 0; u < kStreamUnroll; ++u) {
+        const int64_t i = b0 + 256 * u + threadIdx.x;
+        if (i < n16) st_nt(dst + (int64_t)j * n16 + i, v[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) {
+      acc.x ^= v[u].x; acc.y ^= v[u].y; acc.z ^= v[u].z; acc.w ^= v[u].w;
+    }
+  }
+  if (w == 0 && acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u &&
+      acc.z == 0x1u && acc.w == 0x2u)
+    dst[threadIdx.x] = acc;
+}
 }  // namespace
+
+hipError_t launch_hbm_mix(const void* src, int64_t bytes, int reads,
+                          int writes, void* dst, int cu_count,
+                          hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0 || reads + writes <= 0) return hipSuccess;
+  KernelScope ks("hbm_stream_mix", stream);
+  const int64_t want = (n16 + 256 * kStreamUnroll - 1) / (256 * kStreamUnroll);
+  const int64_t grid = std::min<int64_t>(want, (int64_t)cu_count * 32);
+  const uint4* s = static_cast<const uint4*>(src);
+  uint4* d = static_cast<uint4*>(dst);
+  if (reads == 0)
+    hipLaunchKernelGGL(hbm_mix_kernel<0>, dim3((unsigned)grid), dim3(256), 0,
+                       stream, s, n16, writes, d);
+  else if (reads == 1)
+    hipLaunchKernelGGL(hbm_mix_kernel<1>, dim3((unsigned)grid), dim3(256), 0,
+                       stream, s, n16, writes, d);
+  else
+    hipLaunchKernelGGL(hbm_mix_kernel<2>, dim3((unsigned)grid), dim3(256), 0,
+                       stream, s, n16, writes, d);
+  return hipGetLastError();
+}
 
 hipError_t launch_hbm_stream(const void* src, int64_t bytes, int k, void* dst,
                              int cu_count, hipStream_t stream) {

@@ -62,6 +62,9 @@ hipError_t launch_mx_scales_retile(const uint8_t* src, int64_t rows,
                                    hipStream_t stream);
 
 // achievable-bandwidth reference: read `bytes` once, write k copies
+hipError_t launch_hbm_mix(const void* src, int64_t bytes, int reads,
+                          int writes, void* dst, int cu_count,
+                          hipStream_t stream);
 hipError_t launch_hbm_stream(const void* src, int64_t bytes, int k, void* dst,
                              int cu_count, hipStream_t stream);
 
