@@ -419,30 +419,6 @@ struct Frags<P_BF16> {
     load_a(sa, kk, wm, lane);
     load_b(sb, kk, wn, lane);
   }
-  // the same from the lane's offsets of the slice (oa, ob: block row /
-  // column of the wave included; from rot_offsets)
-  __device__ __forceinline__ void load_at(const char* sa, const char* sb,
-                                          const uint32_t (&oa)[2],
-                                          const uint32_t (&ob)[2]) {
-    a0 = at(sa + oa[0], 0 * 32 * kRowBytes);
-    a1 = at(sa + oa[0], 1 * 32 * kRowBytes);
-    a2 = at(sa + oa[0], 2 * 32 * kRowBytes);
-    a3 = at(sa + oa[0], 3 * 32 * kRowBytes);
-    b0 = at(sb + ob[0], 0 * 32 * kRowBytes);
-    b1 = at(sb + ob[0], 1 * 32 * kRowBytes);
-    b2 = at(sb + ob[0], 2 * 32 * kRowBytes);
-    b3 = at(sb + ob[0], 3 * 32 * kRowBytes);
-  }
-  // lane offsets of slice kk: one per operand
-  static __device__ __forceinline__ void rot_offsets(int kk, int wm, int wn,
-                                                     int lane,
-                                                     uint32_t (&oa)[2],
-                                                     uint32_t (&ob)[2]) {
-    const int o = frag_off(lane & 31, kk * 2 + (lane >> 5));
-    oa[0] = wm * (128 * kRowBytes) + o;
-    ob[0] = wn * (128 * kRowBytes) + o;
-    oa[1] = ob[1] = 0;
-  }
   // 8 k values of the lane from a [k][mn] stage (McDirect layout): two
   // transposed 8-byte reads, k and k + 4 rows apart
   static __device__ __forceinline__ bf16x8_t tr8(const char* p) {
@@ -495,30 +471,6 @@ struct Frags<P_FP8> {
     b1 = at(pb0, pb1, 1 * 32 * kRowBytes);
     b2 = at(pb0, pb1, 2 * 32 * kRowBytes);
     b3 = at(pb0, pb1, 3 * 32 * kRowBytes);
-  }
-  __device__ __forceinline__ void load_at(const char* sa, const char* sb,
-                                          const uint32_t (&oa)[2],
-                                          const uint32_t (&ob)[2]) {
-    a0 = at(sa + oa[0], sa + oa[1], 0 * 32 * kRowBytes);
-    a1 = at(sa + oa[0], sa + oa[1], 1 * 32 * kRowBytes);
-    a2 = at(sa + oa[0], sa + oa[1], 2 * 32 * kRowBytes);
-    a3 = at(sa + oa[0], sa + oa[1], 3 * 32 * kRowBytes);
-    b0 = at(sb + ob[0], sb + ob[1], 0 * 32 * kRowBytes);
-    b1 = at(sb + ob[0], sb + ob[1], 1 * 32 * kRowBytes);
-    b2 = at(sb + ob[0], sb + ob[1], 2 * 32 * kRowBytes);
-    b3 = at(sb + ob[0], sb + ob[1], 3 * 32 * kRowBytes);
-  }
-  // lane offsets of slice kk: its two chunks, per operand
-  static __device__ __forceinline__ void rot_offsets(int kk, int wm, int wn,
-                                                     int lane,
-                                                     uint32_t (&oa)[2],
-                                                     uint32_t (&ob)[2]) {
-    const int c0 = kk * 4 + (lane >> 5);
-    const int o0 = frag_off(lane & 31, c0), o1 = frag_off(lane & 31, c0 + 2);
-    oa[0] = wm * (128 * kRowBytes) + o0;
-    oa[1] = wm * (128 * kRowBytes) + o1;
-    ob[0] = wn * (128 * kRowBytes) + o0;
-    ob[1] = wn * (128 * kRowBytes) + o1;
   }
 };
 
@@ -635,19 +587,11 @@ __device__ __forceinline__ uint4 stage_chunk(const char* buf, int row, int c) {
 // Routing weights of the wave's 128 rows in the wave's own LDS array: lane l
 // loads rows l and 64 + l (clamped to the expert; 1 without weights) before
 // any store of the epilogue, so the wait for them waits for no store.
-// (WEXT: in wext, 512 bytes per wave that the kernel provides, when the
-// operand stages leave no LDS for an array of their own)
-template <bool WEXT>
 __device__ __forceinline__ float* row_weights(const Params& p,
                                               const TileCoord& tc, int mw,
-                                              int lane, int t, float* wext) {
-  float* wrow;
-  if constexpr (WEXT) {
-    wrow = wext + (t >> 6) * 128;
-  } else {
-    __shared__ float wrow_all[kThreads / 64][128];
-    wrow = wrow_all[t >> 6];
-  }
+                                              int lane, int t) {
+  __shared__ float wrow_all[kThreads / 64][128];
+  float* wrow = wrow_all[t >> 6];
   float w0 = 1.0f, w1 = 1.0f;
   if (p.w) {
     w0 = p.w[tc.seg0 + min(mw + lane, tc.seg_len - 1)];
@@ -676,11 +620,11 @@ __device__ __forceinline__ void silu_mul_in_place(f32x16_t (&acc)[4][4]) {
 // load also waits for every store issued before it.  So each epilogue issues
 // its loads (routing weights, saved g and u) ahead of the stores they would
 // otherwise wait behind, and reads LDS in batches before storing.
-template <int G, int EPI, bool WEXT = false>
+template <int G, int EPI>
 __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
                                          f32x16_t (&acc)[4][4], int n0,
                                          int wm, int wn, int lane, int t,
-                                         char* wbuf, float* wext = nullptr) {
+                                         char* wbuf) {
   // acc[i][j][r] is C[row][col] of the wave's block with
   //   row = wm*128 + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
   //   col = wn*128 + j*32 + lane%32
@@ -694,7 +638,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
     // the wave's 64 (a quad of lanes holds one 32-value MXFP8 block).
     const int64_t ld1 = 2 * (int64_t)p.F;
     const bool fvalid = n0 + 64 * wn < p.F;   // F % 64 == 0: whole runs
-    float* wrow = row_weights<WEXT>(p, tc, mw, lane, t, wext);
+    float* wrow = row_weights(p, tc, mw, lane, t);
     if (p.c2) {
       // (g, u) save for the backward pass, through LDS as bf16: row r holds
       // g of the wave's 64 f in columns 0..63 and u in 64..127; on readback
@@ -843,7 +787,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
     __shared__ float red[2 * BM];   // row sums of the two N-waves
     const int64_t ld1 = 2 * (int64_t)p.F;
     const int c8 = lane & 7;
-    float* wrow = row_weights<WEXT>(p, tc, mw, lane, t, wext);
+    float* wrow = row_weights(p, tc, mw, lane, t);
     float rsum[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) rsum[q] = 0.0f;
@@ -1118,17 +1062,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // may split the K range of its last round of tiles
   constexpr bool kMaySplit = G == RAGGED_M && EPI == EPI_STORE && LA == KC &&
                              LB == KC;
-  // The 8-bit gate/up GEMMs run the five-buffer rotation (below).
-  // Measured on the Mixtral shapes, ms per launch: with A two steps ahead,
-  // tensor-scaled FP8 1.78 -> 1.69-1.73, MXFP8 1.85 -> 1.85-1.87, bf16
-  // 3.20-3.24 -> 3.38-3.39; with B two steps ahead (kept), MXFP8 1.782 ->
-  // 1.744-1.752 (with the backward's saves 2.008 -> 1.955), tensor-scaled
-  // FP8 as with A ahead.  The 8-bit down GEMMs, whose split-tail state
-  // leaves no registers for it, spill 400-560 bytes in the K loop with it.
-  constexpr bool kRot = P != P_BF16 && G == RAGGED_M &&
-                        LA == KC && LB == KC &&
-                        (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX);
-  float* wext = nullptr;   // rotation: the epilogue's row weights
   TileCoord tc;
   SplitRange sr;
   if constexpr (kMaySplit) {
@@ -1326,163 +1259,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     }
   };
 
-  // Gate/up GEMMs (ragged M, K-contiguous operands): five 32 KiB operand
-  // buffers in rotation instead of two 64 KiB stages, so the loads run
-  // further ahead.  Buffer n % 5 takes B of K step k for n = 2k and A of step
-  // k for n = 2k + 1; step k computes on A_k, B_k while A_{k+1} (issued over
-  // its first slice, with the scales of step k + 1) and B_{k+2} (issued over
-  // its second) land in the two buffers that B_{k-1} and A_{k-1} have just
-  // left.  The weight rows are in flight for two steps, the token rows for
-  // one (three steps' worth of operands resident needs 192 KiB with two
-  // 64 KiB stages; a row segment of 64 bytes instead of 128 halves what the
-  // texture path delivers).  The barrier that publishes step k + 1 waits
-  // for everything but B_{k+2}: vmcnt counts in issue order, and the slice
-  // fences keep A_{k+1} (and the scales) ahead of it.
-  if constexpr (kRot) {
-    __shared__ __attribute__((aligned(1024))) char sR4[kTileBytes];
-    wext = reinterpret_cast<float*>(sR4);
-    Fr cur_r, nxt_r;
-    // Lane offsets of every slice's fragments, passed through an empty asm
-    // at each use: the compiler then adds them to the buffer's address read
-    // by read instead of holding an address per buffer, slice and operand
-    // in registers (40 with five buffers, which spill, and the reloads'
-    // vmcnt waits would also wait for the loads in flight).
-    uint32_t ro_a[kSl][2], ro_b[kSl][2];
-#pragma unroll
-    for (int kk = 0; kk < kSl; ++kk)
-      Fr::rot_offsets(kk, wm, wn, lane, ro_a[kk], ro_b[kk]);
-    // (the asm goes first in a slice: as a side effect it also pins the
-    // slice's direct loads, which must stay free to interleave)
-    struct Offs { uint32_t a[2], b[2]; };
-    auto launder = [&](int kk) {
-      Offs o = {{ro_a[kk][0], ro_a[kk][1]}, {ro_b[kk][0], ro_b[kk][1]}};
-      if constexpr (PF == P_BF16)
-        asm volatile("" : "+v"(o.a[0]), "+v"(o.b[0]));
-      else
-        asm volatile("" : "+v"(o.a[0]), "+v"(o.a[1]), "+v"(o.b[0]),
-                     "+v"(o.b[1]));
-      return o;
-    };
-    auto fload_r = [&](Fr& f, const char* sa, const char* sb, const Offs& o) {
-      f.load_at(sa, sb, o.a, o.b);
-    };
-    auto buf = [&](auto nc) -> char* {
-      constexpr int n = decltype(nc)::value % 5;
-      if constexpr (n == 0) return sA0;
-      else if constexpr (n == 1) return sB0;
-      else if constexpr (n == 2) return sA1;
-      else if constexpr (n == 3) return sB1;
-      else return sR4;
-    };
-    // vector-memory instructions of one B step (per wave): the barrier's
-    // vmcnt leaves exactly these outstanding
-    constexpr int kVmB2 = 8;
-    constexpr int kWait = (kVmB2 & 0xf) | ((kVmB2 >> 4) << 14) | (0x7 << 4);
-    static_assert(kVmB2 < 64, "vmcnt field");
-    // publish: this wave's A_{k+1} (and scales) have landed and its reads of
-    // the step's buffers are done, then every wave is (memory clobbers
-    // keep the compiler from moving LDS accesses across)
-    auto publish = [&]() {
-      __builtin_amdgcn_s_waitcnt(kWait);   // vmcnt(kVmB2) lgkmcnt(0)
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
-    constexpr int kVmA1 = 8 + (P == P_FP8 ? 8 : 0);   // A (+ scales) loads
-    using std::integral_constant;
-    int k = 0;
-    auto rstep = [&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      char* const b = buf(integral_constant<int, 2 * j>{});
-      char* const a = buf(integral_constant<int, 2 * j + 1>{});
-      char* const bn = buf(integral_constant<int, 2 * j + 2>{});
-      char* const an = buf(integral_constant<int, 2 * j + 3>{});
-      char* const bn2 = buf(integral_constant<int, 2 * j + 4>{});
-      // slice 0: A_{k+1} (+ the scales of step k + 1)
-      const Offs o1 = launder(1);
-      da.issue(an, (uint32_t)(k + 1) * kRowBytes, k + 1 < nk, wave);
-      if constexpr (P == P_FP8) ms.load(min(k + 1, nk - 1));
-      fload_r(nxt_r, a, b, o1);
-      Mma<PF>::template run<0>(cur_r, sa_cur, sb_cur, acc);
-      cur_r = nxt_r;
-      sched_vmem_reads_mfma<kVmA1, kNR, 16, kVpm>();
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kSl > 2) {
-        // slice 1: B_{k+2}
-        const Offs o2 = launder(2);
-        db.issue(bn2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
-        fload_r(nxt_r, a, b, o2);
-        Mma<PF>::template run<1>(cur_r, sa_cur, sb_cur, acc);
-        cur_r = nxt_r;
-        sched_vmem_reads_mfma<kVmB2, kNR, 16, kVpm>();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 2; kk < kSl - 1; ++kk) {
-          const Offs o = launder(kk + 1);
-          fload_r(nxt_r, a, b, o);
-          Mma<PF>::template run<1>(cur_r, sa_cur, sb_cur, acc);
-          cur_r = nxt_r;
-          sched_reads_mfma<kNR, 16>();
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // last slice: three row blocks, publish step k + 1, its first
-        // fragments under the last row block
-        Mma<PF>::template run<kSl - 1, 3>(cur_r, sa_cur, sb_cur, acc);
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        // last slice: B_{k+2} under its first three row blocks
-        db.issue(bn2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
-        Mma<PF>::template run<kSl - 1, 3>(cur_r, sa_cur, sb_cur, acc);
-        sched_vmem_reads_mfma<kVmB2, 0, 12, kVpm>();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const Offs o0 = launder(0);
-      publish();
-      fload_r(nxt_r, an, bn, o0);
-      Mma<PF>::template run<kSl - 1, 4>(cur_r, sa_cur, sb_cur, acc);
-      cur_r = nxt_r;
-      take_scales();
-      sched_reads_mfma<kNR, 4>();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // prologue: B_0 into buffer 0, A_0 (+ scales of step 0) into buffer 1,
-    // then B_1 into buffer 2
-    db.issue(sA0, 0u, true, wave);
-    da.issue(sB0, 0u, true, wave);
-    if constexpr (P == P_FP8) ms.load(0);
-    db.issue(sA1, (uint32_t)kRowBytes, 1 < nk, wave);
-    publish();
-    take_scales();
-    fload_r(cur_r, sB0, sA0, launder(0));
-    // whole trips of five steps (one loop exit, so the fragments carried
-    // round the loop keep their registers), then the last nk % 5 steps
-    const int trips = nk / 5, rem = nk - 5 * trips;
-    for (int tr = 0; tr < trips; ++tr) {
-      rstep(integral_constant<int, 0>{});
-      ++k;
-      rstep(integral_constant<int, 1>{});
-      ++k;
-      rstep(integral_constant<int, 2>{});
-      ++k;
-      rstep(integral_constant<int, 3>{});
-      ++k;
-      rstep(integral_constant<int, 4>{});
-      ++k;
-    }
-    if (rem > 0) {
-      rstep(integral_constant<int, 0>{});
-      ++k;
-      if (rem > 1) {
-        rstep(integral_constant<int, 1>{});
-        ++k;
-        if (rem > 2) {
-          rstep(integral_constant<int, 2>{});
-          ++k;
-          if (rem > 3) rstep(integral_constant<int, 3>{});
-        }
-      }
-    }
-  } else {
+  {
     // Two K steps per loop trip, one per LDS stage, so each stage is a
     // distinct LDS object: the compiler then knows that direct loads into one
     // stage never alias fragment reads of the other and waits for them only
@@ -1588,7 +1365,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] *= f;
   }
-  epilogue<G, EPI, kRot>(p, tc, acc, n0, wm, wn, lane, t, wbuf, wext);
+  epilogue<G, EPI>(p, tc, acc, n0, wm, wn, lane, t, wbuf);
 }
 
 // Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn
