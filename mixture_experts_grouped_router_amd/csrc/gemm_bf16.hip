@@ -131,13 +131,6 @@ hipError_t launch_padded_offsets(const int32_t* offsets, int E, int64_t rows,
 using namespace gg;
 
 namespace {
-// The eight-wave GEMMs run the five-buffer rotation (weight rows two K
-// steps ahead; ms per launch, same box: Qwen3-shaped gate/up 0.884 ->
-// 0.838-0.845, down 0.529 -> 0.500-0.507; long-sequence gate/up 1.836 ->
-// 1.745-1.753, down 1.073 -> 1.012-1.014; Mixtral-shaped down 1.627 ->
-// 1.591).
-constexpr bool kW8RotGateUp = true;
-constexpr bool kW8RotDown = true;
 // Split slots per XCD of the eight-wave forward GEMMs (the gate/up GEMM
 // runs with eight waves up to H = kW8MaxGateUpK).
 int fwd_split_slots_x(int E, int H, int F, int64_t rows) {
@@ -224,7 +217,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
     err = launch_w8<EPI_SWIGLU>(
         "gemm_gate_up_swiglu_bf16", p1,
         persistent_grid(cu_count, ragged_m_grid_split(rows, E, tn1, p1)),
-        kW8RotGateUp, stream);
+        stream);
   } else {
     err = launch<P_BF16, KC, KC, RAGGED_M, EPI_SWIGLU>(
         "gemm_gate_up_swiglu_bf16", p1, ragged_m_grid(rows, E, tn1), stream);
@@ -249,8 +242,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p2.rows = rows;
   set_split(p2);
   return launch_w8<EPI_STORE>("gemm_down_bf16", p2,
-                             ragged_m_grid_split(rows, E, tn2, p2),
-                             kW8RotDown, stream);
+                             ragged_m_grid_split(rows, E, tn2, p2), stream);
 }
 
 size_t mlp_bwd_bf16_ws_bytes(int E, int H, int F, int64_t rows) {

@@ -72,17 +72,8 @@ struct Frags8 {
   static __device__ __forceinline__ bf16x8_t at(const char* s, int off) {
     return *reinterpret_cast<const bf16x8_t*>(s + off);
   }
-  __device__ __forceinline__ void load(const char* sa, const char* sb, int kk,
-                                       int wm, int wn, int lane) {
-    const int o = frag_off(lane & 31, kk * 2 + (lane >> 5));
-    const char* pa = sa + wm * (MI * 32 * kRowBytes) + o;
-    const char* pb = sb + wn * (NJ * 32 * kRowBytes) + o;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) a[i] = at(pa, i * 32 * kRowBytes);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) b[j] = at(pb, j * 32 * kRowBytes);
-  }
-  // the same reads at lane offsets oa, ob (slice and wave block included)
+  // reads at lane offsets oa, ob (slice and wave block included; from
+  // offsets())
   __device__ __forceinline__ void load_at(const char* sa, const char* sb,
                                           uint32_t oa, uint32_t ob) {
 #pragma unroll
@@ -323,8 +314,11 @@ __device__ __forceinline__ void epilogue_w8_swiglu(const Params& p,
 // down GEMM, K = 768: 0.525 -> 0.532 ms with BAR_END).
 constexpr int kW8BarEndMinSteps = 64;
 
-// ROT: five 32 KiB operand buffers in rotation instead of two 64 KiB
-// stages, so that the weight rows (B) are loaded two K steps ahead and the
+// Five 32 KiB operand buffers in rotation instead of two 64 KiB stages with
+// one K step in flight (ms per launch, same box: Qwen3-shaped gate/up 0.884
+// -> 0.838-0.845, down 0.529 -> 0.500-0.507; Mixtral-shaped down 1.627 ->
+// 1.591; Mixtral-shaped gate/up with eight waves 3.01-3.03 against 3.15
+// with four), so that the weight rows (B) are loaded two K steps ahead and the
 // token rows (A) one: buffer n % 5 takes B of step k for n = 2 k and A of
 // step k for n = 2 k + 1, and step k computes on B_k, A_k while A_{k+1}
 // (issued over its first slice) and B_{k+2} (over its second) land in the
@@ -336,7 +330,7 @@ constexpr int kW8BarEndMinSteps = 64;
 // but B_{k+2}: vmcnt counts in issue order.  The buffer that is free in the
 // epilogue holds the routing weights, the persistent hand-over and the
 // split tail's arrival count.
-template <int EPI, bool BAR_END, bool ROT>
+template <int EPI, bool BAR_END>
 __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU, "forward epilogues");
   using S = Shape8<EPI>;
@@ -350,14 +344,8 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   // small LDS: routing weights (64 floats per wave), then the persistent
   // hand-over (2 ints) and the split tail's arrival count
   constexpr int kMiscBytes = kThreads8 / 64 * 64 * 4 + 16;
-  char* misc;
-  if constexpr (ROT) {
-    __shared__ __attribute__((aligned(1024))) char sX4[kTileBytes];
-    misc = sX4;
-  } else {
-    __shared__ __attribute__((aligned(16))) char sMisc[kMiscBytes];
-    misc = sMisc;
-  }
+  __shared__ __attribute__((aligned(1024))) char sX4[kTileBytes];
+  char* const misc = sX4;
   int* const s_item = reinterpret_cast<int*>(misc + kMiscBytes - 16);
   uint32_t* const arrived =
       reinterpret_cast<uint32_t*>(misc + kMiscBytes - 8);
@@ -443,208 +431,129 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   int nx = -1, ni = 0;   // thread 0 (always in an active wave): next item
   Frags8<MI, NJ> cur, nxt;
 
-  if constexpr (ROT) {
-    using std::integral_constant;
-    auto buf = [&](auto nc) -> char* {
-      constexpr int n = decltype(nc)::value % 5;
-      if constexpr (n == 0) return sA0;
-      else if constexpr (n == 1) return sB0;
-      else if constexpr (n == 2) return sA1;
-      else if constexpr (n == 3) return sB1;
-      else return misc;
-    };
-    // Lane offsets of each slice's fragments, passed through an empty asm
-    // at each use, so that the compiler adds them to a buffer's address per
-    // read instead of holding an address per buffer, slice and operand.
-    uint32_t fo_a[kSl], fo_b[kSl];
+  using std::integral_constant;
+  auto buf = [&](auto nc) -> char* {
+    constexpr int n = decltype(nc)::value % 5;
+    if constexpr (n == 0) return sA0;
+    else if constexpr (n == 1) return sB0;
+    else if constexpr (n == 2) return sA1;
+    else if constexpr (n == 3) return sB1;
+    else return misc;
+  };
+  // Lane offsets of each slice's fragments, passed through an empty asm
+  // at each use, so that the compiler adds them to a buffer's address per
+  // read instead of holding an address per buffer, slice and operand.
+  uint32_t fo_a[kSl], fo_b[kSl];
 #pragma unroll
-    for (int kk = 0; kk < kSl; ++kk)
-      Frags8<MI, NJ>::offsets(kk, wm, wn, lane, fo_a[kk], fo_b[kk]);
-    struct Offs { uint32_t a, b; };
-    auto launder = [&](int kk) {
-      Offs o = {fo_a[kk], fo_b[kk]};
-      asm volatile("" : "+v"(o.a), "+v"(o.b));
-      return o;
-    };
-    // this wave's loads but the last four (B two steps ahead) have landed
-    // and its reads of the step's buffers are done, then every wave's
-    constexpr int kWait = (4 & 0xf) | (0x7 << 4);   // vmcnt(4) lgkmcnt(0)
-    auto publish = [&]() {
-      __builtin_amdgcn_s_waitcnt(kWait);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
-    int k = 0;
-    auto rstep = [&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      char* const sb = buf(integral_constant<int, 2 * j>{});
-      char* const sa = buf(integral_constant<int, 2 * j + 1>{});
-      char* const nb = buf(integral_constant<int, 2 * j + 2>{});
-      char* const na = buf(integral_constant<int, 2 * j + 3>{});
-      char* const nb2 = buf(integral_constant<int, 2 * j + 4>{});
+  for (int kk = 0; kk < kSl; ++kk)
+    Frags8<MI, NJ>::offsets(kk, wm, wn, lane, fo_a[kk], fo_b[kk]);
+  struct Offs { uint32_t a, b; };
+  auto launder = [&](int kk) {
+    Offs o = {fo_a[kk], fo_b[kk]};
+    asm volatile("" : "+v"(o.a), "+v"(o.b));
+    return o;
+  };
+  // this wave's loads but the last four (B two steps ahead) have landed
+  // and its reads of the step's buffers are done, then every wave's
+  constexpr int kWait = (4 & 0xf) | (0x7 << 4);   // vmcnt(4) lgkmcnt(0)
+  auto publish = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWait);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  int k = 0;
+  auto rstep = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    char* const sb = buf(integral_constant<int, 2 * j>{});
+    char* const sa = buf(integral_constant<int, 2 * j + 1>{});
+    char* const nb = buf(integral_constant<int, 2 * j + 2>{});
+    char* const na = buf(integral_constant<int, 2 * j + 3>{});
+    char* const nb2 = buf(integral_constant<int, 2 * j + 4>{});
 #pragma unroll
-      for (int kk = 0; kk < kSl - 1; ++kk) {
-        const Offs o = launder(kk + 1);
-        if (kk == 0)
-          da.issue(na, (uint32_t)(k + 1) * kRowBytes, k + 1 < nk, wave);
-        if (kk == 1)
-          db.issue(nb2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
-        nxt.load_at(sa, sb, o.a, o.b);
-        mfma_bf16_w8<2>(cur, acc);
-        cur = nxt;
-        slice_sched(kk);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const Offs o0 = launder(0);
-      if constexpr (BAR_END) {
-        mfma_bf16_w8<2>(cur, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        publish();
-        nxt.load_at(na, nb, o0.a, o0.b);
-        cur = nxt;
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        mfma_bf16_w8<0>(cur, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        publish();
-        nxt.load_at(na, nb, o0.a, o0.b);
-        mfma_bf16_w8<1>(cur, acc);
-        cur = nxt;
-        sched_reads_mfma<6, 4>();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    auto rstep_idle = [&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      char* const na = buf(integral_constant<int, 2 * j + 3>{});
-      char* const nb2 = buf(integral_constant<int, 2 * j + 4>{});
-      da.issue(na, (uint32_t)(k + 1) * kRowBytes, k + 1 < nk, wave);
-      db.issue(nb2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
+    for (int kk = 0; kk < kSl - 1; ++kk) {
+      const Offs o = launder(kk + 1);
+      if (kk == 0)
+        da.issue(na, (uint32_t)(k + 1) * kRowBytes, k + 1 < nk, wave);
+      if (kk == 1)
+        db.issue(nb2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
+      nxt.load_at(sa, sb, o.a, o.b);
+      mfma_bf16_w8<2>(cur, acc);
+      cur = nxt;
+      slice_sched(kk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const Offs o0 = launder(0);
+    if constexpr (BAR_END) {
+      mfma_bf16_w8<2>(cur, acc);
       __builtin_amdgcn_sched_barrier(0);
       publish();
+      nxt.load_at(na, nb, o0.a, o0.b);
+      cur = nxt;
       __builtin_amdgcn_sched_barrier(0);
-    };
-    // prologue: B_0, A_0, then B_1 (left in flight)
-    db.issue(sA0, 0u, true, wave);
-    da.issue(sB0, 0u, true, wave);
-    db.issue(sA1, (uint32_t)kRowBytes, 1 < nk, wave);
-    publish();
-    if (act) {
-      const Offs o = launder(0);
-      cur.load_at(sB0, sA0, o.a, o.b);
+    } else {
+      mfma_bf16_w8<0>(cur, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      publish();
+      nxt.load_at(na, nb, o0.a, o0.b);
+      mfma_bf16_w8<1>(cur, acc);
+      cur = nxt;
+      sched_reads_mfma<6, 4>();
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // whole trips of five steps, then the last nk % 5 (before which the
-    // persistent launch takes its next item)
-    const int trips = nk / 5, rem = nk - 5 * trips;
-    auto run = [&](auto st) {
-      for (int tr = 0; tr < trips; ++tr) {
-        st(integral_constant<int, 0>{});
-        ++k;
+  };
+  auto rstep_idle = [&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    char* const na = buf(integral_constant<int, 2 * j + 3>{});
+    char* const nb2 = buf(integral_constant<int, 2 * j + 4>{});
+    da.issue(na, (uint32_t)(k + 1) * kRowBytes, k + 1 < nk, wave);
+    db.issue(nb2, (uint32_t)(k + 2) * kRowBytes, k + 2 < nk, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    publish();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // prologue: B_0, A_0, then B_1 (left in flight)
+  db.issue(sA0, 0u, true, wave);
+  da.issue(sB0, 0u, true, wave);
+  db.issue(sA1, (uint32_t)kRowBytes, 1 < nk, wave);
+  publish();
+  if (act) {
+    const Offs o = launder(0);
+    cur.load_at(sB0, sA0, o.a, o.b);
+  }
+  // whole trips of five steps, then the last nk % 5 (before which the
+  // persistent launch takes its next item)
+  const int trips = nk / 5, rem = nk - 5 * trips;
+  auto run = [&](auto st) {
+    for (int tr = 0; tr < trips; ++tr) {
+      st(integral_constant<int, 0>{});
+      ++k;
+      st(integral_constant<int, 1>{});
+      ++k;
+      st(integral_constant<int, 2>{});
+      ++k;
+      st(integral_constant<int, 3>{});
+      ++k;
+      st(integral_constant<int, 4>{});
+      ++k;
+    }
+    if (pers && t == 0) take_item(p, nk_all, xh, nx, ni);
+    if (rem > 0) {
+      st(integral_constant<int, 0>{});
+      ++k;
+      if (rem > 1) {
         st(integral_constant<int, 1>{});
         ++k;
-        st(integral_constant<int, 2>{});
-        ++k;
-        st(integral_constant<int, 3>{});
-        ++k;
-        st(integral_constant<int, 4>{});
-        ++k;
-      }
-      if (pers && t == 0) take_item(p, nk_all, xh, nx, ni);
-      if (rem > 0) {
-        st(integral_constant<int, 0>{});
-        ++k;
-        if (rem > 1) {
-          st(integral_constant<int, 1>{});
+        if (rem > 2) {
+          st(integral_constant<int, 2>{});
           ++k;
-          if (rem > 2) {
-            st(integral_constant<int, 2>{});
-            ++k;
-            if (rem > 3) st(integral_constant<int, 3>{});
-          }
+          if (rem > 3) st(integral_constant<int, 3>{});
         }
       }
-    };
-    if (act) run(rstep);
-    else run(rstep_idle);
-  } else {
-    // Two K steps per loop trip, one per LDS stage, as in the four-wave
-    // kernel; fragment reads run one slice ahead of the MFMAs and the
-    // barrier that publishes the next stage sits inside the last slice's
-    // MFMAs.
-    const int nk2 = (nk + 1) & ~1;
-    if (nk > 0) {
-      da.issue(sA0, 0, true, wave);
-      db.issue(sB0, 0, true, wave);
     }
-    __syncthreads();
-    if (act) cur.load(sA0, sB0, 0, wm, wn, lane);
-
-    auto step = [&](const char* sa, const char* sb, char* na, char* nb,
-                    int kn) {
-      // compute the step in (sa, sb); step kn loads into (na, nb) (a step
-      // past nk reads zeros and is never computed)
-      const bool real = kn < nk;
-#pragma unroll
-      for (int kk = 0; kk < kSl - 1; ++kk) {
-        if (kk == 0) da.issue(na, (uint32_t)kn * kRowBytes, real, wave);
-        if (kk == 1) db.issue(nb, (uint32_t)kn * kRowBytes, real, wave);
-        nxt.load(sa, sb, kk + 1, wm, wn, lane);
-        mfma_bf16_w8<2>(cur, acc);
-        cur = nxt;
-        slice_sched(kk);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (BAR_END) {
-        mfma_bf16_w8<2>(cur, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        nxt.load(na, nb, 0, wm, wn, lane);
-        cur = nxt;
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        mfma_bf16_w8<0>(cur, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        nxt.load(na, nb, 0, wm, wn, lane);
-        mfma_bf16_w8<1>(cur, acc);
-        cur = nxt;
-        sched_reads_mfma<6, 4>();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    auto step_idle = [&](char* na, char* nb, int kn) {
-      const bool real = kn < nk;
-      da.issue(na, (uint32_t)kn * kRowBytes, real, wave);
-      db.issue(nb, (uint32_t)kn * kRowBytes, real, wave);
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    if (!act) {
-      for (int kt = 0; kt < nk2; kt += 2) {
-        step_idle(sA1, sB1, kt + 1);
-        step_idle(sA0, sB0, kt + 2);
-      }
-    } else if constexpr (kPers) {
-      // the last trip peeled off, so that the loop has no branch
-      int kt = 0;
-      for (; kt + 2 < nk2; kt += 2) {
-        step(sA0, sB0, sA1, sB1, kt + 1);
-        step(sA1, sB1, sA0, sB0, kt + 2);
-      }
-      if (pers && t == 0) take_item(p, nk_all, xh, nx, ni);
-      if (kt < nk2) {
-        step(sA0, sB0, sA1, sB1, kt + 1);
-        step(sA1, sB1, sA0, sB0, kt + 2);
-      }
-    } else {
-      for (int kt = 0; kt < nk2; kt += 2) {
-        step(sA0, sB0, sA1, sB1, kt + 1);
-        step(sA1, sB1, sA0, sB0, kt + 2);
-      }
-    }
-  }
+  };
+  if (act) run(rstep);
+  else run(rstep_idle);
 
   // every wave is past its last read of the stages (and every direct load
   // has landed) before they become epilogue staging: 16 KiB per wave
@@ -679,26 +588,16 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
 }
 
 template <int EPI>
-hipError_t launch_w8(const char* name, const Params& p, int grid, bool rot,
+hipError_t launch_w8(const char* name, const Params& p, int grid,
                      hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   KernelScope ks(name, stream);
-  const bool bar_end = (p.K + 63) / 64 >= kW8BarEndMinSteps;
-  if (rot) {
-    if (bar_end)
-      hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, true, true>),
-                         dim3(grid), dim3(kThreads8), 0, stream, p);
-    else
-      hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, false, true>),
-                         dim3(grid), dim3(kThreads8), 0, stream, p);
-  } else {
-    if (bar_end)
-      hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, true, false>),
-                         dim3(grid), dim3(kThreads8), 0, stream, p);
-    else
-      hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, false, false>),
-                         dim3(grid), dim3(kThreads8), 0, stream, p);
-  }
+  if ((p.K + 63) / 64 >= kW8BarEndMinSteps)
+    hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, true>), dim3(grid),
+                       dim3(kThreads8), 0, stream, p);
+  else
+    hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, false>), dim3(grid),
+                       dim3(kThreads8), 0, stream, p);
   return hipGetLastError();
 }
 
