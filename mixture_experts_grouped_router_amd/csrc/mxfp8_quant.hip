@@ -237,8 +237,11 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(
 // t & 7 and writes them transposed into LDS ([column][row]); then thread t
 // quantises rows 32 (t & 3) .. +31 of column t >> 2 from four 16-byte LDS
 // reads.  Segment mode: tiles of one segment (zero past its end), output at
-// offsets where every segment starts on a multiple of 128 * pad_tiles.
-template <bool SEG, bool TILED>
+// offsets where every segment starts on a multiple of 128 * pad_tiles; a
+// block there takes NCB consecutive 64-column chunks of its row tile, so
+// that its prologue (offsets check, segment scan and search) is paid once
+// per NCB chunks.
+template <bool SEG, bool TILED, int NCB = 1>
 __global__ __launch_bounds__(256) void mx_cols128_kernel(
     const uint4* __restrict__ src, int64_t rows, int64_t cols,
     const int32_t* __restrict__ seg_offsets, int n_seg, int pad_tiles,
@@ -248,7 +251,6 @@ __global__ __launch_bounds__(256) void mx_cols128_kernel(
   __shared__ int32_t tprefix[1025];
   const int t = threadIdx.x;
   const int64_t b = blockIdx.z;
-  const int64_t c0 = (int64_t)blockIdx.y * 64;
   int64_t r0, rend, out0;
   if (SEG) {
     const int pad = 128 * pad_tiles;
@@ -290,61 +292,66 @@ __global__ __launch_bounds__(256) void mx_cols128_kernel(
   }
   const int64_t cpr = cols / 8;   // 16-byte chunks per row (cols % 8 == 0)
   const uint4* base = src + b * rows * cpr;
-  {
-    const int ch = t & 7, rq = t >> 3;
-    const int64_t c = c0 / 8 + ch;
-    uint4 v[4];
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int64_t c0 = ((int64_t)blockIdx.y * NCB + cb) * 64;
+    if (c0 >= cols) break;
+    if (cb > 0) __syncthreads();   // the previous chunk's LDS reads are done
+    {
+      const int ch = t & 7, rq = t >> 3;
+      const int64_t c = c0 / 8 + ch;
+      uint4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + 4 * rq + i;
+        v[i] = (r < rend && c < cpr) ? ld_nt(base + r * cpr + c)
+                                     : make_uint4(0, 0, 0, 0);
+      }
+      const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w},
+                                {v[1].x, v[1].y, v[1].z, v[1].w},
+                                {v[2].x, v[2].y, v[2].z, v[2].w},
+                                {v[3].x, v[3].y, v[3].z, v[3].w}};
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const int sh = (cc & 1) * 16;
+        const uint32_t e0 = (w[0][cc >> 1] >> sh) & 0xffffu;
+        const uint32_t e1 = (w[1][cc >> 1] >> sh) & 0xffffu;
+        const uint32_t e2 = (w[2][cc >> 1] >> sh) & 0xffffu;
+        const uint32_t e3 = (w[3][cc >> 1] >> sh) & 0xffffu;
+        *reinterpret_cast<uint2*>(&tileT[8 * ch + cc][4 * rq]) =
+            make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+      }
+    }
+    __syncthreads();
+    const int col = t >> 2, q = t & 3;
+    const int64_t c = c0 + col;
+    const uint4* lp = reinterpret_cast<const uint4*>(&tileT[col][32 * q]);
+    uint32_t x[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t r = r0 + 4 * rq + i;
-      v[i] = (r < rend && c < cpr) ? ld_nt(base + r * cpr + c)
-                                   : make_uint4(0, 0, 0, 0);
+      const uint4 u = lp[i];
+      x[4 * i] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
     }
-    const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w},
-                              {v[1].x, v[1].y, v[1].z, v[1].w},
-                              {v[2].x, v[2].y, v[2].z, v[2].w},
-                              {v[3].x, v[3].y, v[3].z, v[3].w}};
+    uint32_t a = 0;
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const int sh = (cc & 1) * 16;
-      const uint32_t e0 = (w[0][cc >> 1] >> sh) & 0xffffu;
-      const uint32_t e1 = (w[1][cc >> 1] >> sh) & 0xffffu;
-      const uint32_t e2 = (w[2][cc >> 1] >> sh) & 0xffffu;
-      const uint32_t e3 = (w[3][cc >> 1] >> sh) & 0xffffu;
-      *reinterpret_cast<uint2*>(&tileT[8 * ch + cc][4 * rq]) =
-          make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+    for (int i = 0; i < 16; ++i)
+      a = umax(a, umax(x[i] & 0x7fffu, (x[i] >> 16) & 0x7fffu));
+    const int s = e8m0_exp_from_bf16_amax(a);
+    const float sc = mx_scale_f32(s);
+    uint32_t o[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] = e4m3x4_hw(x[2 * d], x[2 * d + 1], sc);
+    if (c < cols) {
+      const int64_t orow = b * cols + c;   // output row
+      uint4* dst = reinterpret_cast<uint4*>(codes + orow * ld_out + out0 + 32 * q);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      const int64_t kb = out0 / 32 + q;
+      if (TILED)
+        scales[mx_tile_off((uint32_t)orow, (uint32_t)kb,
+                           (uint32_t)(ld_out / 128))] = (uint8_t)(s + 127);
+      else
+        scales[orow * (ld_out / 32) + kb] = (uint8_t)(s + 127);
     }
-  }
-  __syncthreads();
-  const int col = t >> 2, q = t & 3;
-  const int64_t c = c0 + col;
-  const uint4* lp = reinterpret_cast<const uint4*>(&tileT[col][32 * q]);
-  uint32_t x[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 u = lp[i];
-    x[4 * i] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
-  }
-  uint32_t a = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i)
-    a = umax(a, umax(x[i] & 0x7fffu, (x[i] >> 16) & 0x7fffu));
-  const int s = e8m0_exp_from_bf16_amax(a);
-  const float sc = mx_scale_f32(s);
-  uint32_t o[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) o[d] = e4m3x4_hw(x[2 * d], x[2 * d + 1], sc);
-  if (c < cols) {
-    const int64_t orow = b * cols + c;   // output row
-    uint4* dst = reinterpret_cast<uint4*>(codes + orow * ld_out + out0 + 32 * q);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    const int64_t kb = out0 / 32 + q;
-    if (TILED)
-      scales[mx_tile_off((uint32_t)orow, (uint32_t)kb,
-                         (uint32_t)(ld_out / 128))] = (uint8_t)(s + 127);
-    else
-      scales[orow * (ld_out / 32) + kb] = (uint8_t)(s + 127);
   }
 }
 
@@ -441,14 +448,18 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
     const int pt = pad / 128;
     // sum_s ceil(n_s / pad) * pad / 128 <= rows / 128 + n_seg * pad / 128
     const int64_t tiles = rows / 128 + (int64_t)n_seg * pt;
-    const dim3 g128((unsigned)tiles, (unsigned)((cols + 63) / 64), 1);
+    constexpr int kNcb = 4;
+    const dim3 g128((unsigned)tiles, (unsigned)((cols + 64 * kNcb - 1) /
+                                                (64 * kNcb)), 1);
     if (tiled)
-      hipLaunchKernelGGL((mx_cols128_kernel<true, true>), g128, dim3(256), 0,
-                         stream, static_cast<const uint4*>(src), rows, cols,
+      hipLaunchKernelGGL((mx_cols128_kernel<true, true, kNcb>), g128,
+                         dim3(256), 0, stream,
+                         static_cast<const uint4*>(src), rows, cols,
                          seg_offsets, n_seg, pt, ld, codes, scales, status);
     else
-      hipLaunchKernelGGL((mx_cols128_kernel<true, false>), g128, dim3(256), 0,
-                         stream, static_cast<const uint4*>(src), rows, cols,
+      hipLaunchKernelGGL((mx_cols128_kernel<true, false, kNcb>), g128,
+                         dim3(256), 0, stream,
+                         static_cast<const uint4*>(src), rows, cols,
                          seg_offsets, n_seg, pt, ld, codes, scales, status);
     return hipGetLastError();
   }
