@@ -67,7 +67,7 @@ def parse():
 
 # library kernel name -> template instantiations in profiler kernel names
 # (the forward GEMMs run the eight-wave kernels: bf16 grouped_gemm_w8_kernel
-# <EPI, BAR_END> for the down GEMM and for gate/up up to H = 4096,
+# <EPI> for the down GEMM and for gate/up up to H = 4096,
 # 8-bit grouped_gemm_w8q_kernel<P, EPI, G>)
 KERNEL_SYMBOL = {
     "gemm_gate_up_swiglu_bf16": ("grouped_gemm_kernel<0, 0, 0, 0, 1>",

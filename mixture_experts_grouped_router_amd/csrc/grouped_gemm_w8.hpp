@@ -306,13 +306,13 @@ __device__ __forceinline__ void epilogue_w8_swiglu(const Params& p,
   }
 }
 
-// BAR_END: the stage barrier follows the step's last MFMA (the next stage's
-// loads get the whole step to land) instead of sitting halfway through the
-// last slice (the next stage's first fragment reads overlap the last four
-// MFMAs).  Long K loops gain from the former (Mixtral-shaped down GEMM,
-// K = 14336: 1.679 -> 1.656 ms), short ones from the latter (Qwen3-shaped
-// down GEMM, K = 768: 0.525 -> 0.532 ms with BAR_END).
-constexpr int kW8BarEndMinSteps = 64;
+// The barrier that publishes the next step sits halfway through the last
+// slice: the next step's first fragment reads overlap the last four MFMAs.
+// (Before the rotation, long K loops did better with it after the step's
+// last MFMA, which gives the next step's loads the whole step to land:
+// Mixtral-shaped down GEMM 1.679 -> 1.656 ms; with the rotation, whose
+// weight loads have two steps, halfway is faster there too: gate/up
+// 3.104-3.116 -> 3.085-3.089, down 1.659-1.668 -> 1.633-1.634 ms.)
 
 // Five 32 KiB operand buffers in rotation instead of two 64 KiB stages with
 // one K step in flight (ms per launch, same box: Qwen3-shaped gate/up 0.884
@@ -330,7 +330,7 @@ constexpr int kW8BarEndMinSteps = 64;
 // but B_{k+2}: vmcnt counts in issue order.  The buffer that is free in the
 // epilogue holds the routing weights, the persistent hand-over and the
 // split tail's arrival count.
-template <int EPI, bool BAR_END>
+template <int EPI>
 __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
   static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU, "forward epilogues");
   using S = Shape8<EPI>;
@@ -484,23 +484,14 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     const Offs o0 = launder(0);
-    if constexpr (BAR_END) {
-      mfma_bf16_w8<2>(cur, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      publish();
-      nxt.load_at(na, nb, o0.a, o0.b);
-      cur = nxt;
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      mfma_bf16_w8<0>(cur, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      publish();
-      nxt.load_at(na, nb, o0.a, o0.b);
-      mfma_bf16_w8<1>(cur, acc);
-      cur = nxt;
-      sched_reads_mfma<6, 4>();
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    mfma_bf16_w8<0>(cur, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    publish();
+    nxt.load_at(na, nb, o0.a, o0.b);
+    mfma_bf16_w8<1>(cur, acc);
+    cur = nxt;
+    sched_reads_mfma<6, 4>();
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto rstep_idle = [&](auto jc) {
     constexpr int j = decltype(jc)::value;
@@ -592,12 +583,8 @@ hipError_t launch_w8(const char* name, const Params& p, int grid,
                      hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   KernelScope ks(name, stream);
-  if ((p.K + 63) / 64 >= kW8BarEndMinSteps)
-    hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, true>), dim3(grid),
-                       dim3(kThreads8), 0, stream, p);
-  else
-    hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI, false>), dim3(grid),
-                       dim3(kThreads8), 0, stream, p);
+  hipLaunchKernelGGL((grouped_gemm_w8_kernel<EPI>), dim3(grid),
+                     dim3(kThreads8), 0, stream, p);
   return hipGetLastError();
 }
 
