@@ -76,6 +76,7 @@ typedef enum moe_mx_axis {
 #define MOE_DEVERR_NONE 0
 #define MOE_DEVERR_EXPERT_ID 1     /* topk_idx entry outside [0, E) */
 #define MOE_DEVERR_OFFSETS 2       /* offsets not non-decreasing from 0 to rows */
+#define MOE_DEVERR_LOGITS 3        /* a router logit is NaN or infinite */
 
 typedef struct moe_ctx* moe_ctx_t;
 
@@ -214,7 +215,9 @@ moe_status_t moe_router_bwd(moe_ctx_t ctx, const float* logits,
  *                           (renormalize != 0) or over all E (== 0),
  *                           evaluated in float64, rounded to float32.
  *  1 <= k <= min(E, 32), E <= 1024, T >= 0 (T = 0 is a no-op).
- *  Logits must be finite (NaN/Inf: unspecified selection).
+ *  Logits must be finite: a NaN or infinite logit records
+ *  MOE_DEVERR_LOGITS (moe_ctx_check_device_status) and leaves that token's
+ *  selection unspecified; every other token is routed as above.
  * ---------------------------------------------------------------------- */
 moe_status_t moe_route_topk(moe_ctx_t ctx, const float* logits, int64_t T,
                             int32_t E, int32_t k, int32_t renormalize,

@@ -338,7 +338,8 @@ moe_status_t moe_route_topk(moe_ctx_t ctx, const float* logits, int64_t T,
   MOE_REQUIRE(logits && topk_idx && topk_w, MOE_ERR_INVALID_ARG,
               "null tensor pointer");
   return hip_status(moe::launch_route_topk(logits, T, E, k, renormalize != 0,
-                                           topk_idx, topk_w, as_stream(stream)),
+                                           topk_idx, topk_w, ctx->status,
+                                           as_stream(stream)),
                     "route_topk launch");
 }
 

@@ -9,7 +9,7 @@ namespace moe {
 // router top-k
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
                              int renorm, int32_t* idx, float* w,
-                             hipStream_t stream);
+                             int32_t* status, hipStream_t stream);
 
 // permutation
 size_t permute_ws_bytes(int64_t T, int E, int k);

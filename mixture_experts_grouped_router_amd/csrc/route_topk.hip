@@ -9,7 +9,8 @@
 //
 // Each lane holds E/64 logits in registers.  k rounds of a wave-wide argmax
 // (larger value first, lower expert id on ties) pick the experts; lane j
-// keeps slot j.  No LDS, no atomics.
+// keeps slot j.  No LDS; a NaN or infinite logit (a precondition violation)
+// records MOE_DEVERR_LOGITS in the device status word.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "timer.hpp"
@@ -17,6 +18,9 @@
 namespace moe {
 
 namespace {
+
+// device status code (include/moe.h: MOE_DEVERR_LOGITS)
+constexpr int32_t kDevErrLogits = 3;
 
 struct Cand {
   float v;
@@ -32,7 +36,8 @@ __device__ __forceinline__ bool beats(float av, int ae, float bv, int be) {
 template <int VPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int renorm,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* status) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -40,12 +45,15 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 
   float v[VPL];
   uint32_t taken = 0;  // bit i: v[i] already selected
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
     v[i] = e < E ? row[e] : 0.0f;
     if (e >= E) taken |= 1u << i;
+    bad |= !__builtin_isfinite(v[i]);
   }
+  if (bad) report_error(status, kDevErrLogits);
 
   float my_v = 0.0f;  // lane j < k: logit of slot j
   int my_e = 0;
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
                              int renorm, int32_t* idx, float* w,
-                             hipStream_t stream) {
+                             int32_t* status, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int tokens_per_block = 4;
   const dim3 grid((unsigned)((T + tokens_per_block - 1) / tokens_per_block));
@@ -116,7 +124,7 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
 #define MOE_ROUTE_CASE(N)                                                      \
   case N:                                                                      \
     hipLaunchKernelGGL(route_topk_kernel<N>, grid, dim3(256), 0, stream,      \
-                       logits, T, E, k, renorm, idx, w);                       \
+                       logits, T, E, k, renorm, idx, w, status);               \
     break;
   switch (vpl) {
     MOE_ROUTE_CASE(1)
@@ -124,15 +132,17 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k,
     MOE_ROUTE_CASE(4)
     MOE_ROUTE_CASE(8)
     MOE_ROUTE_CASE(16)
-    case 3: hipLaunchKernelGGL(route_topk_kernel<4>, grid, dim3(256), 0, stream,
-                               logits, T, E, k, renorm, idx, w); break;
+    case 3:
+      hipLaunchKernelGGL(route_topk_kernel<4>, grid, dim3(256), 0, stream,
+                         logits, T, E, k, renorm, idx, w, status);
+      break;
     default:
       if (vpl <= 8)
         hipLaunchKernelGGL(route_topk_kernel<8>, grid, dim3(256), 0, stream,
-                           logits, T, E, k, renorm, idx, w);
+                           logits, T, E, k, renorm, idx, w, status);
       else
         hipLaunchKernelGGL(route_topk_kernel<16>, grid, dim3(256), 0, stream,
-                           logits, T, E, k, renorm, idx, w);
+                           logits, T, E, k, renorm, idx, w, status);
   }
 #undef MOE_ROUTE_CASE
   return hipGetLastError();

@@ -97,6 +97,9 @@ def route_topk(logits: np.ndarray, k: int, renormalize: bool = True
     T, E = lg.shape
     if not (1 <= k <= E):
         raise ValueError("need 1 <= k <= E")
+    if not np.all(np.isfinite(lg)):
+        # a precondition of the routing: no selection is defined for them
+        raise ValueError("router logits must be finite")
     lv = lg.astype(f64) + 0.0          # -0.0 + 0.0 == +0.0 (R2)
     # a stable sort keeps the lower expert id first among equal logits
     order = np.argsort(-lv, axis=1, kind="stable")

@@ -207,6 +207,27 @@ def test_device_check_flags_bad_expert_id(m):
     assert m.check_device_status() == 0  # cleared by the previous check
 
 
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_device_check_flags_nonfinite_logits(m, bad):
+    """A NaN or infinite router logit (written on the host) records the
+    logits device check; the finite tokens are routed as the oracle routes
+    them, and the kernel completes normally."""
+    T, E, k = 96, 128, 8
+    logits = np.random.default_rng(3).standard_normal((T, E)).astype(
+        np.float32)
+    logits[17, 40] = bad
+    assert m.check_device_status() == 0
+    idx, w = m.moe_route_topk(torch.from_numpy(logits).cuda(), k)
+    assert m.check_device_status() == 3
+    ok = np.ones(T, bool)
+    ok[17] = False
+    ri, rw = O.route_topk(logits[ok], k)
+    np.testing.assert_array_equal(idx.cpu().numpy()[ok], ri)
+    assert _ulp_diff_f32(w.cpu().numpy()[ok], rw).max() <= 1
+    idx, w = m.moe_route_topk(torch.from_numpy(logits[ok]).cuda(), k)
+    assert m.check_device_status() == 0
+
+
 def test_device_check_flags_bad_offsets(m):
     """Per-expert offsets written on the host that end below the row count
     (non-decreasing, so every access stays in bounds even unchecked) are

@@ -84,6 +84,14 @@ def test_route_weights_sum_to_one_and_k1():
     assert np.all(w1 == np.float32(1.0))
 
 
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_route_rejects_nonfinite_logits(bad):
+    lg = np.zeros((3, 4), np.float32)
+    lg[1, 2] = bad
+    with pytest.raises(ValueError):
+        O.route_topk(lg, 2)
+
+
 def test_route_hand_worked_golden():
     """tests/golden/route_hand.json: a routing example worked by hand."""
     with open(os.path.join(GOLDEN, "route_hand.json")) as f:
