@@ -71,8 +71,8 @@ def parse():
 # 8-bit grouped_gemm_w8q_kernel<P, EPI, G>)
 KERNEL_SYMBOL = {
     "gemm_gate_up_swiglu_bf16": ("grouped_gemm_kernel<0, 0, 0, 0, 1>",
-                                 "grouped_gemm_w8_kernel<1,"),
-    "gemm_down_bf16": ("grouped_gemm_w8_kernel<0,",),
+                                 "grouped_gemm_w8_kernel<1>"),
+    "gemm_down_bf16": ("grouped_gemm_w8_kernel<0>",),
     "gemm_gate_up_swiglu_mxfp8": ("grouped_gemm_w8q_kernel<1, 3, 0>",),
     "gemm_down_mxfp8": ("grouped_gemm_w8q_kernel<1, 0, 0>",),
     "gemm_gate_up_swiglu_fp8t": ("grouped_gemm_w8q_kernel<2, 1, 0>",),
