@@ -312,7 +312,8 @@ KERNELS = [
     "route_topk", "permute_index", "permute_gather", "permute_gather_mxfp8",
     "gemm_gate_up_swiglu_bf16", "gemm_down_bf16", "gemm_gate_up_swiglu_mxfp8",
     "gemm_down_mxfp8", "mxfp8_quantize_rows", "mxfp8_quantize_cols",
-    "mxfp8_quantize_segments", "mxfp8_scales_retile", "unpermute",
+    "mxfp8_quantize_segments", "mxfp8_quantize_segments_and_rows",
+    "mxfp8_scales_retile", "unpermute",
     "gemm_dgrad_down_swiglu_bwd", "gemm_dgrad_gate_up", "gemm_wgrad_down",
     "gemm_wgrad_gate_up", "gemm_dgrad_down_swiglu_bwd_mxfp8",
     "gemm_dgrad_gate_up_mxfp8", "gemm_wgrad_down_mxfp8",
@@ -337,11 +338,12 @@ MX_BYTES = 2.0 + 1.0 + 1.0 / 32   # bf16 read, E4M3 code + E8M0/32 written
 
 
 def _mx_rows_elems(c):
-    """Values quantised row-wise per step: both weight tensors in the
-    forward; with a backward pass also x_perm (forward), dZ and dH1."""
+    """Values quantised row-wise alone per step: both weight tensors in the
+    forward; with a backward pass also x_perm (forward).  dZ and dH1 are
+    quantised row-wise by the pass that also quantises them along tokens."""
     n = c.E * 3.0 * c.H * c.F
     if c.backward:
-        n += c.rows * c.H + c.rows * c.H + c.rows * 2.0 * c.F
+        n += c.rows * c.H
     return n
 
 
@@ -359,9 +361,12 @@ KERNEL_BYTES = {
     "mxfp8_quantize_rows": lambda c: _mx_rows_elems(c) * MX_BYTES,
     # backward: both weight tensors along their other dimension
     "mxfp8_quantize_cols": lambda c: c.E * 3.0 * c.H * c.F * MX_BYTES,
-    # backward: dZ, A, dH1, X along tokens (padding not counted)
-    "mxfp8_quantize_segments": lambda c: c.rows * (2.0 * c.H + 3.0 * c.F)
-    * MX_BYTES,
+    # backward: A and X along tokens (padding not counted)
+    "mxfp8_quantize_segments": lambda c: c.rows * (c.H + c.F) * MX_BYTES,
+    # backward: dZ and dH1 along tokens and row-wise in one pass (one bf16
+    # read, two sets of codes and scales written)
+    "mxfp8_quantize_segments_and_rows": lambda c: c.rows * (c.H + 2.0 * c.F)
+    * (2.0 + 2.0 * (1.0 + 1.0 / 32)),
     # tensor-scaled FP8: an amax read and a quantising pass (read bf16,
     # write codes) over both weight tensors, x_perm and A
     "fp8_amax": lambda c: 2.0 * (3.0 * c.E * c.H * c.F + c.rows * (c.H + c.F)),

@@ -195,6 +195,8 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
 // of the GEMM (128): the extra blocks are all zero, so the products are those
 // of the 32-padded layout.  The SwiGLU backward runs in float32 in the dgrad2
 // epilogue, which writes dH1 in bf16; dH1 is quantised from that bf16 copy.
+// dZ and dH1 are each quantised in both directions by one pass that reads
+// them once.
 namespace {
 
 constexpr int kTokPad = 128;   // token segments padded to one K step
@@ -338,10 +340,11 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
       err = launch_tile_table(offsets, E, rows, tnf, w.ts_f, status, stream);
     if (err == hipSuccess)
       err = launch_tile_table(offsets, E, rows, tnh, w.ts_h, status, stream);
-    // operands of the two dgrad GEMMs
+    // dZ for dgrad2 (row-wise) and wgrad2 (along tokens)
     if (err == hipSuccess)
-      err = launch_mx_quant_rows(dz_perm, rows, H, w.dzq, w.dzs, stream,
-                                 true);
+      err = launch_mx_quant_segments(dz_perm, rows, H, offsets, E, kTokPad,
+                                     w.ld, w.dzt, w.dzts, status, stream,
+                                     true, w.dzq, w.dzs);
     if (quant_w) {
       if (err == hipSuccess)
         err = launch_mx_quant_cols(w_dn, E, H, F, w.wdq, w.wds, stream, true);
@@ -398,8 +401,11 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
       if (err != hipSuccess) return err;
     }
 
-    // dgrad1: dX = dH1 W_gu[e]; B = W_gu[e]^T [H, 2F]
-    err = launch_mx_quant_rows(w.dh1, rows, F2, w.hq, w.hs, stream, true);
+    // dgrad1: dX = dH1 W_gu[e]; B = W_gu[e]^T [H, 2F]; dH1 for it
+    // (row-wise) and for wgrad1 (along tokens)
+    err = launch_mx_quant_segments(w.dh1, rows, F2, offsets, E, kTokPad,
+                                   w.ld, w.ht, w.hts, status, stream, true,
+                                   w.hq, w.hs);
     if (err != hipSuccess) return err;
     Params q{};
     q.a = reinterpret_cast<const char*>(w.hq);
@@ -426,15 +432,9 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
         "gemm_dgrad_gate_up_mxfp8", q, ragged_m_grid(rows, E, tnh), stream);
     if (err != hipSuccess) return err;
 
-    // token-direction operands of the two wgrad GEMMs
-    err = launch_mx_quant_segments(dz_perm, rows, H, offsets, E, kTokPad,
-                                   w.ld, w.dzt, w.dzts, status, stream, true);
-    if (err == hipSuccess)
-      err = launch_mx_quant_segments(a_save, rows, F, offsets, E, kTokPad,
-                                     w.ld, w.at, w.ats, status, stream, true);
-    if (err == hipSuccess)
-      err = launch_mx_quant_segments(w.dh1, rows, F2, offsets, E, kTokPad,
-                                     w.ld, w.ht, w.hts, status, stream, true);
+    // the other token-direction operands of the two wgrad GEMMs
+    err = launch_mx_quant_segments(a_save, rows, F, offsets, E, kTokPad,
+                                   w.ld, w.at, w.ats, status, stream, true);
     if (err == hipSuccess)
       err = launch_mx_quant_segments(x_perm, rows, H, offsets, E, kTokPad,
                                      w.ld, w.xt, w.xts, status, stream, true);

@@ -44,13 +44,18 @@ hipError_t launch_mx_quant_rows(const void* src, int64_t rows, int64_t cols,
 hipError_t launch_mx_quant_cols(const void* src, int64_t batch, int64_t rows,
                                 int64_t cols, uint8_t* codes, uint8_t* scales,
                                 hipStream_t stream, bool tiled = false);
-// pad: segments start at multiples of pad (a multiple of 32) in the output
+// pad: segments start at multiples of pad (a multiple of 32) in the output.
+// row_codes / row_scales (optional; pad and cols multiples of 128, tiled
+// scales): the same pass also writes the row-wise quantisation, codes
+// [rows][cols] and scales in the GEMM layout.
 hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
                                     int64_t cols, const int32_t* seg_offsets,
                                     int n_seg, int pad, int64_t ld,
                                     uint8_t* codes, uint8_t* scales,
                                     int32_t* status, hipStream_t stream,
-                                    bool tiled = false);
+                                    bool tiled = false,
+                                    uint8_t* row_codes = nullptr,
+                                    uint8_t* row_scales = nullptr);
 // row-wise MXFP8 of float32 values [n / cols][cols] (n % 32 == 0) with the
 // encoder of the MXFP8 gate/up epilogue; row-major scales [n / 32]
 hipError_t launch_mx_quant_f32(const float* src, int64_t n, uint8_t* codes,

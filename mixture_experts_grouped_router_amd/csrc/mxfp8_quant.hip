@@ -240,13 +240,18 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(
 // offsets where every segment starts on a multiple of 128 * pad_tiles; a
 // block there takes NCB consecutive 64-column chunks of its row tile, so
 // that its prologue (offsets check, segment scan and search) is paid once
-// per NCB chunks.
-template <bool SEG, bool TILED, int NCB = 1>
+// per NCB chunks.  ROWS: the same pass also writes the row-wise codes
+// [rows][cols] and scales (GEMM layout) of the rows it loads, each thread
+// encoding the four 8-value runs it holds, a quad of lanes per 32-value
+// block: one read of the tensor serves both directions.
+template <bool SEG, bool TILED, int NCB = 1, bool ROWS = false>
 __global__ __launch_bounds__(256) void mx_cols128_kernel(
     const uint4* __restrict__ src, int64_t rows, int64_t cols,
     const int32_t* __restrict__ seg_offsets, int n_seg, int pad_tiles,
     int64_t ld_out, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, int32_t* status) {
+    uint8_t* __restrict__ scales, int32_t* status,
+    uint2* __restrict__ row_codes = nullptr,
+    uint8_t* __restrict__ row_scales = nullptr) {
   __shared__ __attribute__((aligned(16))) uint16_t tileT[64][128 + 8];
   __shared__ int32_t tprefix[1025];
   const int t = threadIdx.x;
@@ -305,6 +310,25 @@ __global__ __launch_bounds__(256) void mx_cols128_kernel(
         const int64_t r = r0 + 4 * rq + i;
         v[i] = (r < rend && c < cpr) ? ld_nt(base + r * cpr + c)
                                      : make_uint4(0, 0, 0, 0);
+      }
+      if constexpr (ROWS) {
+        // every lane of a quad takes part; rows past the end do not store
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t a = amax8(v[i]);
+          a = umax(a, __shfl_xor(a, 1, 64));
+          a = umax(a, __shfl_xor(a, 2, 64));
+          const int s = e8m0_exp_from_bf16_amax(a);
+          const int64_t r = r0 + 4 * rq + i;
+          if (r < rend && c < cpr) {
+            const int64_t orow = b * rows + r;
+            row_codes[orow * cpr + c] = e4m3x8_hw(v[i], s);
+            if ((ch & 3) == 0)
+              row_scales[mx_tile_off((uint32_t)orow, (uint32_t)(c / 4),
+                                     (uint32_t)(cols / 128))] =
+                  (uint8_t)(s + 127);
+          }
+        }
       }
       const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w},
                                 {v[1].x, v[1].y, v[1].z, v[1].w},
@@ -441,9 +465,14 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
                                     int n_seg, int pad, int64_t ld,
                                     uint8_t* codes, uint8_t* scales,
                                     int32_t* status, hipStream_t stream,
-                                    bool tiled) {
+                                    bool tiled, uint8_t* row_codes,
+                                    uint8_t* row_scales) {
   if (rows * cols == 0) return hipSuccess;
-  KernelScope ks("mxfp8_quantize_segments", stream);
+  if (row_codes && (pad % 128 != 0 || !tiled || cols % 128 != 0))
+    return hipErrorInvalidValue;
+  KernelScope ks(row_codes ? "mxfp8_quantize_segments_and_rows"
+                           : "mxfp8_quantize_segments",
+                 stream);
   if (pad % 128 == 0) {
     const int pt = pad / 128;
     // sum_s ceil(n_s / pad) * pad / 128 <= rows / 128 + n_seg * pad / 128
@@ -451,7 +480,13 @@ hipError_t launch_mx_quant_segments(const void* src, int64_t rows,
     constexpr int kNcb = 4;
     const dim3 g128((unsigned)tiles, (unsigned)((cols + 64 * kNcb - 1) /
                                                 (64 * kNcb)), 1);
-    if (tiled)
+    if (row_codes)
+      hipLaunchKernelGGL((mx_cols128_kernel<true, true, kNcb, true>), g128,
+                         dim3(256), 0, stream,
+                         static_cast<const uint4*>(src), rows, cols,
+                         seg_offsets, n_seg, pt, ld, codes, scales, status,
+                         reinterpret_cast<uint2*>(row_codes), row_scales);
+    else if (tiled)
       hipLaunchKernelGGL((mx_cols128_kernel<true, true, kNcb>), g128,
                          dim3(256), 0, stream,
                          static_cast<const uint4*>(src), rows, cols,
