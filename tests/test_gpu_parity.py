@@ -62,7 +62,10 @@ def assert_rows_close(got, ref, tol, name):
 @pytest.mark.parametrize("T,E,k,renorm,seed", [
     (256, 8, 2, True, 0), (1000, 128, 8, True, 1), (333, 100, 5, False, 2),
     (64, 8, 8, True, 3), (1, 3, 1, True, 4), (513, 1024, 32, True, 5),
-    (200, 64, 6, False, 6)])
+    (200, 64, 6, False, 6),
+    # 16 lanes per token up to k = 16 and E = 256, one wave beyond
+    (300, 256, 16, False, 8), (300, 256, 17, True, 9), (77, 40, 16, True, 10),
+    (129, 257, 4, False, 11)])
 def test_route_topk_matches_oracle(m, T, E, k, renorm, seed):
     lg = np.random.default_rng(seed).standard_normal((T, E)).astype(np.float32)
     idx, w = m.moe_route_topk(torch.from_numpy(lg).cuda(), k, renorm)
@@ -71,12 +74,13 @@ def test_route_topk_matches_oracle(m, T, E, k, renorm, seed):
     assert _ulp_diff_f32(w.cpu().numpy(), rw).max() <= 1
 
 
-def test_route_topk_ties_and_signed_zero(m):
+@pytest.mark.parametrize("E,k", [(16, 4), (128, 8), (300, 8)])
+def test_route_topk_ties_and_signed_zero(m, E, k):
     rng = np.random.default_rng(7)
-    lg = rng.integers(-2, 3, size=(4096, 16)).astype(np.float32)
+    lg = rng.integers(-2, 3, size=(4096, E)).astype(np.float32)
     lg[rng.random(lg.shape) < 0.2] = -0.0
-    idx, w = m.moe_route_topk(torch.from_numpy(lg).cuda(), 4)
-    ridx, rw = O.route_topk(lg, 4)
+    idx, w = m.moe_route_topk(torch.from_numpy(lg).cuda(), k)
+    ridx, rw = O.route_topk(lg, k)
     np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
     assert _ulp_diff_f32(w.cpu().numpy(), rw).max() <= 1
 
