@@ -151,10 +151,19 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t base = (int64_t)blockIdx.x * kChunk;
-  for (int i = 0; i < kChunk; i += 64) {
-    const int64_t p = base + i + lane;
-    int e = -1;
-    if (p < n_pairs) e = topk_idx[p];
+  // every expert id of the chunk is loaded up front (the loop's barriers
+  // would otherwise hold each load's latency)
+  constexpr int kPer = kChunk / 64;
+  int ev[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t p = base + 64 * u + lane;
+    ev[u] = p < n_pairs ? topk_idx[p] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t p = base + 64 * u + lane;
+    const int e = ev[u];
     const bool ok = (unsigned)e < (unsigned)E;
     // lanes holding the same expert id: intersect ballots bit by bit
     uint64_t same = __ballot(ok);
@@ -167,11 +176,13 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(
       rank = __popcll(same & lt_mask);
       basev = run[e];
     }
-    __builtin_amdgcn_wave_barrier();
-    __syncthreads();
+    // the block is one wave, whose LDS accesses complete in program order:
+    // the compiler barriers keep that order (a block barrier would also
+    // wait for the previous pairs' global stores)
+    asm volatile("" ::: "memory");
     // the highest lane of each group advances the running counter
     if (ok && (same >> lane) == 1ull) run[e] = basev + rank + 1;
-    __syncthreads();
+    asm volatile("" ::: "memory");
     if (p < n_pairs) {
       if (ok) {
         const int32_t r = basev + rank;
