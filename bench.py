@@ -109,7 +109,6 @@ def write_traffic(workload, dbs, cmd):
             data = json.load(fh)
     except (OSError, ValueError):
         data = {"records": []}
-    dig = sources_digest()
     recs = [r for r in data.get("records", [])
             if r.get("workload") != workload]
     for kname, syms in KERNEL_SYMBOL.items():
@@ -118,7 +117,8 @@ def write_traffic(workload, dbs, cmd):
         if not fk or not wk:
             continue
         recs.append({
-            "kernel": kname, "workload": workload, "source_digest": dig,
+            "kernel": kname, "workload": workload,
+            "source_digest": sources_digest(kname),
             "fetch_kib_per_launch": round(fk[0], 1),
             "write_kib_per_launch": round(wk[0], 1),
             "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
@@ -375,17 +375,23 @@ KERNEL_BYTES = {
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_gemm.json")
-GEMM_SOURCES = [os.path.join(ROOT, "mixture_experts_grouped_router_amd",
-                             "csrc", f) for f in
-                ("grouped_gemm.hpp", "grouped_gemm_w8.hpp", "gemm_bf16.hip",
-                 "gemm_mxfp8.hip", "gemm_fp8t.hip")]
+# the sources each precision's GEMM kernels are built from: a traffic record
+# holds for the kernel only while their digest matches
+_GEMM_DIR = os.path.join(ROOT, "mixture_experts_grouped_router_amd", "csrc")
+_GEMM_HDRS = ("grouped_gemm.hpp", "grouped_gemm_w8.hpp",
+              "grouped_gemm_w8q.hpp", "work_items.hpp", "common.hpp",
+              "mx_codec.hpp")
+GEMM_SOURCES = {"bf16": _GEMM_HDRS + ("gemm_bf16.hip",),
+                "mxfp8": _GEMM_HDRS + ("gemm_mxfp8.hip",),
+                "fp8t": _GEMM_HDRS + ("gemm_fp8t.hip",)}
 
 
-def sources_digest():
+def sources_digest(kernel):
+    """Digest of the sources of `kernel` (named ..._bf16, _mxfp8, _fp8t)."""
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
-        with open(f, "rb") as fh:
+    for f in GEMM_SOURCES[kernel.rsplit("_", 1)[-1]]:
+        with open(os.path.join(_GEMM_DIR, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -400,7 +406,7 @@ def traffic_for(kernel, cfg):
             recs = json.load(fh)
     except (OSError, ValueError):
         return None
-    dig = sources_digest()
+    dig = sources_digest(kernel)
     for r in recs.get("records", []):
         if r.get("kernel") == kernel and r.get("workload") == cfg.name and \
                 r.get("source_digest") == dig:
