@@ -254,6 +254,11 @@ __global__ __launch_bounds__(256) void mx_cols128_kernel(
     uint8_t* __restrict__ row_scales = nullptr) {
   __shared__ __attribute__((aligned(16))) uint16_t tileT[64][128 + 8];
   __shared__ int32_t tprefix[1025];
+  // ROWS: the row-wise scale bytes of the block's rows, [row][block of 32
+  // along the NCB chunks], stored after the chunks as one dword per row and
+  // four blocks (the GEMM layout keeps those four bytes together)
+  __shared__ __attribute__((aligned(4))) uint8_t rsc[ROWS ? 128 : 1]
+                                                    [ROWS ? 2 * NCB : 1];
   const int t = threadIdx.x;
   const int64_t b = blockIdx.z;
   int64_t r0, rend, out0;
@@ -297,6 +302,7 @@ __global__ __launch_bounds__(256) void mx_cols128_kernel(
   }
   const int64_t cpr = cols / 8;   // 16-byte chunks per row (cols % 8 == 0)
   const uint4* base = src + b * rows * cpr;
+  uint2 pend[4];   // ROWS: row codes of the previous (even) chunk
   for (int cb = 0; cb < NCB; ++cb) {
     const int64_t c0 = ((int64_t)blockIdx.y * NCB + cb) * 64;
     if (c0 >= cols) break;
@@ -320,14 +326,20 @@ __global__ __launch_bounds__(256) void mx_cols128_kernel(
           a = umax(a, __shfl_xor(a, 2, 64));
           const int s = e8m0_exp_from_bf16_amax(a);
           const int64_t r = r0 + 4 * rq + i;
-          if (r < rend && c < cpr) {
-            const int64_t orow = b * rows + r;
-            row_codes[orow * cpr + c] = e4m3x8_hw(v[i], s);
-            if ((ch & 3) == 0)
-              row_scales[mx_tile_off((uint32_t)orow, (uint32_t)(c / 4),
-                                     (uint32_t)(cols / 128))] =
-                  (uint8_t)(s + 127);
+          // a 128-byte line of codes spans two chunks: the even chunk's
+          // codes wait in registers and go out with the odd chunk's
+          const uint2 cw = e4m3x8_hw(v[i], s);
+          if (cb & 1) {
+            if (r < rend && c < cpr) {
+              uint2* rc = row_codes + (b * rows + r) * cpr + c;
+              rc[-8] = pend[i];
+              rc[0] = cw;
+            }
+          } else {
+            pend[i] = cw;
           }
+          if ((ch & 3) == 0) rsc[4 * rq + i][2 * cb + (ch >> 2)] =
+              (uint8_t)(s + 127);
         }
       }
       const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w},
@@ -375,6 +387,22 @@ __global__ __launch_bounds__(256) void mx_cols128_kernel(
                            (uint32_t)(ld_out / 128))] = (uint8_t)(s + 127);
       else
         scales[orow * (ld_out / 32) + kb] = (uint8_t)(s + 127);
+    }
+  }
+  if constexpr (ROWS) {
+    // thread t: row t % 128, group g = t / 128 of four 32-value blocks
+    // (NCB = 4: two groups)
+    static_assert(NCB == 4, "two groups of four blocks per row");
+    __syncthreads();
+    const int lr = t & 127, g = t >> 7;
+    const int64_t r = r0 + lr;
+    const int64_t kb0 = (int64_t)blockIdx.y * NCB * 2 + 4 * g;   // first block
+    if (r < rend && 32 * kb0 < cols) {
+      const int64_t orow = b * rows + r;
+      const uint32_t wd = *reinterpret_cast<const uint32_t*>(&rsc[lr][4 * g]);
+      *reinterpret_cast<uint32_t*>(
+          row_scales + mx_tile_off((uint32_t)orow, (uint32_t)kb0,
+                                   (uint32_t)(cols / 128))) = wd;
     }
   }
 }
