@@ -22,11 +22,12 @@ namespace gg {
 // With unit = BM it counts GEMM tiles; with unit = tn = P it gives the
 // offsets of segments padded to multiples of P.  Offsets that do not run
 // non-decreasing from 0 to rows give an all-zero table (no tile runs, every
-// padded segment is empty) and record MOE_DEVERR_OFFSETS.
+// padded segment is empty) and record MOE_DEVERR_OFFSETS.  With mrec (GEMM
+// tiles, unit = BM) thread e also writes the records of e's M tiles.
 __global__ __launch_bounds__(1024) void tile_table_kernel(
     const int32_t* __restrict__ offsets, int E, int64_t rows, int unit,
     int tn, int32_t* __restrict__ tile_start, uint32_t* __restrict__ zero,
-    int nzero, int32_t* status) {
+    int nzero, int32_t* status, int32_t* __restrict__ mrec) {
   __shared__ int32_t wsum[16];
   const int e = threadIdx.x;
   for (int i = e; i < nzero; i += 1024) zero[i] = 0u;
@@ -58,6 +59,12 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(
   const int32_t excl = incl - v + wsum[wid];
   if (e < E) tile_start[e] = excl;
   if (e == E - 1) tile_start[E] = excl + v;
+  if (mrec && e < E && v > 0) {
+    const int32_t first = excl / tn, n = v / tn;
+    const int4 r = make_int4(e, first, offsets[e], offsets[e + 1] - offsets[e]);
+    for (int i = 0; i < n; ++i)
+      reinterpret_cast<int4*>(mrec)[first + i] = r;
+  }
 }
 
 // Rank of expert e by rows, descending; equal counts keep index order.
@@ -104,7 +111,7 @@ hipError_t launch_tile_table(const int32_t* offsets, int E, int64_t rows,
   KernelScope ks("tile_table", stream);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
                      offsets, E, rows, BM, tn, tile_start, zero, nzero,
-                     status);
+                     status, tile_start + tile_rec_offset(E));
   return hipGetLastError();
 }
 
@@ -122,7 +129,8 @@ hipError_t launch_padded_offsets(const int32_t* offsets, int E, int64_t rows,
                                  hipStream_t stream) {
   KernelScope ks("padded_offsets", stream);
   hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream,
-                     offsets, E, rows, pad, pad, poff, nullptr, 0, status);
+                     offsets, E, rows, pad, pad, poff, nullptr, 0, status,
+                     nullptr);
   return hipGetLastError();
 }
 
@@ -144,7 +152,7 @@ int fwd_split_slots_x(int E, int H, int F, int64_t rows) {
 }  // namespace
 
 size_t mlp_fwd_bf16_ws_bytes(int E, int H, int F, int64_t rows, bool need_a) {
-  size_t b = 2 * align256((size_t)(E + 1) * sizeof(int32_t));
+  size_t b = 2 * tile_table_bytes(E, rows);
   if (need_a) b += align256((size_t)rows * F * 2);
   const int sx = fwd_split_slots_x(E, H, F, rows);
   b += split_part_bytes(sx) + counters_bytes(1, sx);
@@ -160,9 +168,9 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
                                hipStream_t stream) {
   char* wp = static_cast<char*>(ws);
   int32_t* ts1 = reinterpret_cast<int32_t*>(wp);
-  wp += align256((size_t)(E + 1) * sizeof(int32_t));
+  wp += tile_table_bytes(E, rows);
   int32_t* ts2 = reinterpret_cast<int32_t*>(wp);
-  wp += align256((size_t)(E + 1) * sizeof(int32_t));
+  wp += tile_table_bytes(E, rows);
   uint16_t* a_buf = static_cast<uint16_t*>(a_save);
   if (!a_buf) {
     a_buf = reinterpret_cast<uint16_t*>(wp);
@@ -202,6 +210,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p1.E = E;
   p1.offsets = offsets;
   p1.tile_start = ts1;
+  p1.mrec = tile_records(ts1, E);
   p1.tiles_n = tn1;
   p1.c = a_buf;
   p1.ldc = F;
@@ -236,6 +245,7 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
   p2.E = E;
   p2.offsets = offsets;
   p2.tile_start = ts2;
+  p2.mrec = tile_records(ts2, E);
   p2.tiles_n = tn2;
   p2.c = static_cast<uint16_t*>(z_perm);
   p2.ldc = H;
@@ -247,7 +257,8 @@ hipError_t launch_mlp_fwd_bf16(int E, int H, int F, int64_t rows,
 
 size_t mlp_bwd_bf16_ws_bytes(int E, int H, int F, int64_t rows) {
   const int tnf = (F + BN - 1) / BN;
-  size_t b = 3 * align256((size_t)(E + 1) * sizeof(int32_t));
+  size_t b = 2 * tile_table_bytes(E, rows) +
+             align256((size_t)(E + 1) * sizeof(int32_t));
   b += align256((size_t)rows * 2 * F * 2);        // dH1
   b += align256((size_t)tnf * rows * sizeof(float));  // dw partials
   return b;
@@ -265,9 +276,9 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
   const int tnh = (H + BN - 1) / BN;
   char* wp = static_cast<char*>(ws);
   int32_t* ts_f = reinterpret_cast<int32_t*>(wp);
-  wp += align256((size_t)(E + 1) * sizeof(int32_t));
+  wp += tile_table_bytes(E, rows);
   int32_t* ts_h = reinterpret_cast<int32_t*>(wp);
-  wp += align256((size_t)(E + 1) * sizeof(int32_t));
+  wp += tile_table_bytes(E, rows);
   int32_t* order = reinterpret_cast<int32_t*>(wp);
   wp += align256((size_t)(E + 1) * sizeof(int32_t));
   uint16_t* dh1 = reinterpret_cast<uint16_t*>(wp);
@@ -294,6 +305,7 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     p.E = E;
     p.offsets = offsets;
     p.tile_start = ts_f;
+    p.mrec = tile_records(ts_f, E);
     p.tiles_n = tnf;
     p.c = dh1;
     p.h1 = static_cast<const uint16_t*>(h1_save);
@@ -321,6 +333,7 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     q.E = E;
     q.offsets = offsets;
     q.tile_start = ts_h;
+    q.mrec = tile_records(ts_h, E);
     q.tiles_n = tnh;
     q.c = static_cast<uint16_t*>(dx_perm);
     q.ldc = H;

@@ -38,8 +38,8 @@ Fp8tWs carve(void* base, int E, int H, int F, int64_t rows, bool need_a) {
   };
   w.amax = reinterpret_cast<uint32_t*>(take((size_t)(2 + 2 * E) * 4));
   w.scale = reinterpret_cast<float*>(take((size_t)(2 + 2 * E) * 4));
-  w.ts1 = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
-  w.ts2 = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  w.ts1 = reinterpret_cast<int32_t*>(take(tile_table_bytes(E, rows)));
+  w.ts2 = reinterpret_cast<int32_t*>(take(tile_table_bytes(E, rows)));
   w.xq = reinterpret_cast<uint8_t*>(take((size_t)rows * H));
   w.guq = reinterpret_cast<uint8_t*>(take((size_t)E * 2 * F * H));
   w.dnq = reinterpret_cast<uint8_t*>(take((size_t)E * H * F));
@@ -110,6 +110,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   p1.E = E;
   p1.offsets = offsets;
   p1.tile_start = w.ts1;
+  p1.mrec = tile_records(w.ts1, E);
   p1.tiles_n = tn1;
   p1.c = a;
   p1.ldc = F;
@@ -138,6 +139,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   p2.E = E;
   p2.offsets = offsets;
   p2.tile_start = w.ts2;
+  p2.mrec = tile_records(w.ts2, E);
   p2.tiles_n = tn2;
   p2.c = static_cast<uint16_t*>(z_perm);
   p2.ldc = H;

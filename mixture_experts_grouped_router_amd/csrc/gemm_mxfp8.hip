@@ -52,8 +52,8 @@ MxFwdWs carve_fwd(void* base, int E, int H, int F, int64_t rows, bool quant_x,
     return q;
   };
   auto take8 = [&](size_t n) { return reinterpret_cast<uint8_t*>(take(n)); };
-  w.ts1 = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
-  w.ts2 = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  w.ts1 = reinterpret_cast<int32_t*>(take(tile_table_bytes(E, rows)));
+  w.ts2 = reinterpret_cast<int32_t*>(take(tile_table_bytes(E, rows)));
   w.aq = take8((size_t)rows * F);
   w.as = take8(mx_tile_bytes(rows, F));
   if (quant_x) w.xq = take8((size_t)rows * H);
@@ -145,6 +145,7 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p1.E = E;
   p1.offsets = offsets;
   p1.tile_start = w.ts1;
+  p1.mrec = tile_records(w.ts1, E);
   p1.tiles_n = tn1;
   p1.c = static_cast<uint16_t*>(a_save);
   p1.ldc = F;
@@ -175,6 +176,7 @@ hipError_t launch_mlp_fwd_mx(int E, int H, int F, int64_t rows,
   p2.E = E;
   p2.offsets = offsets;
   p2.tile_start = w.ts2;
+  p2.mrec = tile_records(w.ts2, E);
   p2.tiles_n = tn2;
   p2.c = static_cast<uint16_t*>(z_perm);
   p2.ldc = H;
@@ -241,8 +243,8 @@ MxBwdWs carve_bwd(void* base, int E, int H, int F, int64_t rows,
   const size_t F2 = 2 * (size_t)F;
   w.ld = tok_ld(rows, E);
   const size_t ld = (size_t)w.ld;
-  w.ts_f = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
-  w.ts_h = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
+  w.ts_f = reinterpret_cast<int32_t*>(take(tile_table_bytes(E, rows)));
+  w.ts_h = reinterpret_cast<int32_t*>(take(tile_table_bytes(E, rows)));
   w.poff = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
   w.order = reinterpret_cast<int32_t*>(take((size_t)(E + 1) * 4));
   w.dh1 = reinterpret_cast<uint16_t*>(take((size_t)rows * F2 * 2));
@@ -382,6 +384,7 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
     p.E = E;
     p.offsets = offsets;
     p.tile_start = w.ts_f;
+    p.mrec = tile_records(w.ts_f, E);
     p.tiles_n = tnf;
     p.c = w.dh1;
     p.h1 = static_cast<const uint16_t*>(h1_save);
@@ -424,6 +427,7 @@ hipError_t launch_mlp_bwd_mx(int E, int H, int F, int64_t rows,
     q.E = E;
     q.offsets = offsets;
     q.tile_start = w.ts_h;
+    q.mrec = tile_records(w.ts_h, E);
     q.tiles_n = tnh;
     q.c = static_cast<uint16_t*>(dx_perm);
     q.ldc = H;

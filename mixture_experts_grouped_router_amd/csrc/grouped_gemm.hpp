@@ -126,6 +126,8 @@ struct Params {
   int E;
   const int32_t* offsets;     // [E+1] rows per expert
   const int32_t* tile_start;  // RAGGED_M: [E+1] tile prefix
+  const int32_t* mrec;        // RAGGED_M, nullable: M-tile records (the
+                              // tile_start search when null)
   const int32_t* order;       // RAGGED_K: experts by decreasing rows
   int tiles_n;                // tiles along N
   int tiles_m;                // RAGGED_K: tiles along M
@@ -180,7 +182,7 @@ __device__ __forceinline__ int lds_off(int r, int c) {
 // Coordinates of tile L of a RAGGED_M launch (work_items.hpp).
 __device__ __forceinline__ void ragged_m_tile(const Params& p, int L,
                                               TileCoord& tc) {
-  ragged_m_tile_at(p.tile_start, p.offsets, p.E, L, tc);
+  ragged_m_tile_at(p.tile_start, p.offsets, p.E, L, tc, p.mrec, p.tiles_n);
 }
 
 template <int G>
@@ -924,7 +926,7 @@ __device__ __forceinline__ bool decode_item(const Params& p, int nk, int x,
                                             int idx, TileCoord& tc,
                                             SplitRange& sr) {
   return decode_item_at(p.tile_start, p.offsets, p.E, split_cfg(p), nk, x,
-                        idx, tc, sr);
+                        idx, tc, sr, p.mrec, p.tiles_n);
 }
 
 // Work-group b of a one-item-per-work-group launch: XCD b mod 8 (where the
@@ -1369,11 +1371,22 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 }
 
 // Prefix over experts: tile_start[e] = sum_{e' < e} ceil(M_e'/unit) * tn
-// (all zero, and MOE_DEVERR_OFFSETS recorded, for invalid offsets).
+// (all zero, and MOE_DEVERR_OFFSETS recorded, for invalid offsets); with
+// mrec, also the M-tile records (work_items.hpp).
 __global__ __launch_bounds__(1024) void tile_table_kernel(
     const int32_t* __restrict__ offsets, int E, int64_t rows, int unit,
     int tn, int32_t* __restrict__ tile_start, uint32_t* __restrict__ zero,
-    int nzero, int32_t* status);
+    int nzero, int32_t* status, int32_t* __restrict__ mrec);
+
+// Workspace bytes of a tile table with M-tile records (tile_table_ints)
+inline size_t tile_table_bytes(int E, int64_t rows) {
+  return ((size_t)tile_table_ints(E, rows) * sizeof(int32_t) + 255) &
+         ~(size_t)255;
+}
+// The records of a tile table of that size
+inline const int32_t* tile_records(const int32_t* tile_start, int E) {
+  return tile_start + tile_rec_offset(E);
+}
 
 // Grid for a RAGGED_M launch: sum_e ceil(M_e / BM) <= rows / BM + E tiles
 // per N tile, rounded up to whole XCD rounds.
@@ -1450,7 +1463,9 @@ hipError_t launch(const char* name, const Params& p, int grid,
 // Each of these checks offsets (non-decreasing from 0 to rows) and, if
 // they are not, records MOE_DEVERR_OFFSETS in *status and publishes an
 // empty table, so that no GEMM tile and no segment is processed.
-// (also clears zero[0 .. nzero), e.g. the split tiles' arrival counters)
+// (also clears zero[0 .. nzero), e.g. the split tiles' arrival counters).
+// tile_start holds tile_table_bytes(E, rows): the prefix and the M-tile
+// records.
 hipError_t launch_tile_table(const int32_t* offsets, int E, int64_t rows,
                              int tn, int32_t* tile_start, int32_t* status,
                              hipStream_t stream, uint32_t* zero = nullptr,

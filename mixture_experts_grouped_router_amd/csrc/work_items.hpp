@@ -57,24 +57,46 @@ MOE_HD inline int wi_min(int a, int b) { return a < b ? a : b; }
 // Coordinates of tile L (0 <= L < tile_start[E]): the expert by binary
 // search (experts without tiles have tile_start[e] == tile_start[e+1] and
 // are never selected), then the group and the tile inside it.
+// M-tile records: after the tile prefix tile_start[0..E] (at int offset
+// tile_rec_offset(E), 16-byte aligned) one record per M tile of the launch
+// in tile-list order, {expert e, e's first M tile, offsets[e], rows of e}.
+// Tile L of a launch with tn N tiles per M tile belongs to M tile L / tn,
+// so one 16-byte read replaces the search over tile_start.
+MOE_HD inline int tile_rec_offset(int E) { return (E + 1 + 3) & ~3; }
+// ints of a tile table with records for a launch of at most rows routed rows
+MOE_HD inline int64_t tile_table_ints(int E, int64_t rows) {
+  return tile_rec_offset(E) + 4 * (rows / BM + E);
+}
+
 MOE_HD inline void ragged_m_tile_at(const int32_t* tile_start,
                                     const int32_t* offsets, int E, int L,
-                                    TileCoord& tc) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_start[mid] <= L) lo = mid; else hi = mid;
+                                    TileCoord& tc, const int32_t* mrec = nullptr,
+                                    int tn = 0) {
+  int e, local, len, seg0;
+  if (mrec) {
+    const int32_t* r = mrec + 4 * (L / tn);
+    e = r[0];
+    local = L - r[1] * tn;
+    seg0 = r[2];
+    len = r[3];
+  } else {
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_start[mid] <= L) lo = mid; else hi = mid;
+    }
+    e = lo;
+    local = L - tile_start[e];
+    seg0 = offsets[e];
+    len = offsets[e + 1] - seg0;
   }
-  const int e = lo;
-  const int local = L - tile_start[e];
-  const int len = offsets[e + 1] - offsets[e];
   const int mt_e = (len + BM - 1) / BM;
   const int ng = local / (mt_e * kGroupN);
   const int in_g = local - ng * mt_e * kGroupN;
   tc.e = e;
   tc.m0 = (in_g % mt_e) * BM;
   tc.nt = ng * kGroupN + in_g / mt_e;
-  tc.seg0 = offsets[e];
+  tc.seg0 = seg0;
   tc.seg_len = len;
 }
 
@@ -117,7 +139,8 @@ MOE_HD inline XcdItems xcd_items_at(int total, int x, const SplitCfg& sc,
 MOE_HD inline bool decode_item_at(const int32_t* tile_start,
                                   const int32_t* offsets, int E,
                                   const SplitCfg& sc, int nk, int x, int idx,
-                                  TileCoord& tc, SplitRange& sr) {
+                                  TileCoord& tc, SplitRange& sr,
+                                  const int32_t* mrec = nullptr, int tn = 0) {
   const int total = tile_start[E];
   const XcdItems it = xcd_items_at(total, x, sc, nk);
   if (it.cnt <= 0 || idx < 0) return false;
@@ -141,7 +164,7 @@ MOE_HD inline bool decode_item_at(const int32_t* tile_start,
     sr.id = x * sc.slots_x + rt;
     L = x * it.per + it.whole + rt;
   }
-  ragged_m_tile_at(tile_start, offsets, E, L, tc);
+  ragged_m_tile_at(tile_start, offsets, E, L, tc, mrec, tn);
   return true;
 }
 

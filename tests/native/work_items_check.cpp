@@ -2,7 +2,8 @@
 // grouped GEMM kernels decode them.  For random expert row counts, N tile
 // counts, K step counts and split settings it checks:
 //   - the tile table's tiles map one to one onto (expert, M tile, N tile),
-//     every M tile inside its expert's rows;
+//     every M tile inside its expert's rows; the decode through the M-tile
+//     records gives the same coordinates as the search over the prefix;
 //   - over all XCDs, every tile is one whole item or exactly S pieces whose
 //     K ranges are non-empty and partition [0, nk), and no item decodes
 //     past an XCD's count;
@@ -52,12 +53,33 @@ int main() {
     for (int e = 0; e < E; ++e)
       ts[e + 1] = ts[e] + ((off[e + 1] - off[e] + BM - 1) / BM) * tn;
     const int total = ts[E];
+    // M-tile records as the tile-table kernel writes them, after the prefix
+    // in one array of tile_table_ints(E, rows) ints
+    std::vector<int32_t> table(tile_table_ints(E, off[E]), -7);
+    for (int e = 0; e <= E; ++e) table[e] = ts[e];
+    int32_t* rec = table.data() + tile_rec_offset(E);
+    if ((tile_rec_offset(E) & 3) != 0) fail("records not 16-byte aligned", E, tn, nk, C);
+    for (int e = 0; e < E; ++e) {
+      const int first = ts[e] / tn, n = (ts[e + 1] - ts[e]) / tn;
+      for (int i = 0; i < n; ++i) {
+        if (4 * (first + i) + 3 >= (int)table.size() - tile_rec_offset(E))
+          fail("records past the table", E, tn, nk, C);
+        else {
+          int32_t* r = rec + 4 * (first + i);
+          r[0] = e; r[1] = first; r[2] = off[e]; r[3] = off[e + 1] - off[e];
+        }
+      }
+    }
 
     // tile table <-> (expert, M tile, N tile)
     std::set<std::tuple<int, int, int>> coords;
     for (int L = 0; L < total; ++L) {
-      TileCoord tc;
+      TileCoord tc, tr;
       ragged_m_tile_at(ts.data(), off.data(), E, L, tc);
+      ragged_m_tile_at(ts.data(), off.data(), E, L, tr, rec, tn);
+      if (tr.e != tc.e || tr.m0 != tc.m0 || tr.nt != tc.nt ||
+          tr.seg0 != tc.seg0 || tr.seg_len != tc.seg_len)
+        fail("record decode differs from the search", E, tn, nk, C);
       const int len = off[tc.e + 1] - off[tc.e];
       if (tc.e < 0 || tc.e >= E || tc.m0 < 0 || tc.m0 % BM || tc.m0 >= len ||
           tc.nt < 0 || tc.nt >= tn || tc.seg0 != off[tc.e] ||
@@ -80,7 +102,8 @@ int main() {
         TileCoord tc;
         SplitRange sr;
         const bool ok =
-            decode_item_at(ts.data(), off.data(), E, sc, nk, x, idx, tc, sr);
+            decode_item_at(ts.data(), off.data(), E, sc, nk, x, idx, tc, sr,
+                           rec, tn);
         if (idx >= n) {
           if (ok) fail("item past the count decodes", E, tn, nk, C);
           continue;

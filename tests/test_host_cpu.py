@@ -123,8 +123,10 @@ def test_library_index_helpers(tmp_path):
 
 
 def test_work_items_host_build(tmp_path):
-    """The ragged-M GEMMs' work items, built for the host: every tile of a
-    random tile table is one whole item or K-range pieces that partition its
+    """The ragged-M GEMMs' work items, built for the host: the M-tile
+    records decode every tile as the search over the tile prefix does, every
+    tile of a random tile table is one whole item or K-range pieces that
+    partition its
     K steps, split slots stay inside their XCD and apart, and the persistent
     take protocol hands out every item once and lets every work-group end."""
     exe = str(tmp_path / "work_items_check")
