@@ -614,18 +614,26 @@ def dataclasses_replace(c):
 
 
 def prequantised_step(m, layer, cfg, st, K):
-    """MXFP8 step with the weights quantised once beforehand (as a trainer
-    does once per weight update and reuses for every micro-batch): row-wise
-    codes for the forward call, column-wise codes for the backward, instead
-    of quantising them inside every call."""
+    """8-bit step with the weights quantised once beforehand (as a trainer
+    does once per weight update and reuses for every micro-batch) instead
+    of inside every call: MXFP8 row-wise codes for the forward call and
+    column-wise codes for the backward; tensor-scaled FP8 codes with one
+    scale per expert."""
     import torch
     E, H, F = cfg.E, cfg.H, cfg.F
-    gq = m.mxfp8_quantize(layer.w_gu.reshape(E * 2 * F, H), m.ROWWISE)
-    dq = m.mxfp8_quantize(layer.w_dn.reshape(E * H, F), m.ROWWISE)
     fa = layer.fa
-    saved = (fa.w_gu_q, fa.w_gu_s, fa.w_dn_q, fa.w_dn_s, fa.ws, fa.ws_bytes)
-    fa.w_gu_q, fa.w_gu_s = gq[0].data_ptr(), gq[1].data_ptr()
-    fa.w_dn_q, fa.w_dn_s = dq[0].data_ptr(), dq[1].data_ptr()
+    saved = (fa.w_gu_q, fa.w_gu_s, fa.w_dn_q, fa.w_dn_s, fa.w_gu_ts,
+             fa.w_dn_ts, fa.ws, fa.ws_bytes)
+    if cfg.mode == "fp8t":
+        gq = m.fp8_tensor_quantize(layer.w_gu, E)
+        dq = m.fp8_tensor_quantize(layer.w_dn, E)
+        fa.w_gu_q, fa.w_gu_ts = gq[0].data_ptr(), gq[1].data_ptr()
+        fa.w_dn_q, fa.w_dn_ts = dq[0].data_ptr(), dq[1].data_ptr()
+    else:
+        gq = m.mxfp8_quantize(layer.w_gu.reshape(E * 2 * F, H), m.ROWWISE)
+        dq = m.mxfp8_quantize(layer.w_dn.reshape(E * H, F), m.ROWWISE)
+        fa.w_gu_q, fa.w_gu_s = gq[0].data_ptr(), gq[1].data_ptr()
+        fa.w_dn_q, fa.w_dn_s = dq[0].data_ptr(), dq[1].data_ptr()
     n = ctypes.c_size_t()
     m._check(layer.lib.moe_grouped_mlp_fwd_workspace_size(ctypes.byref(fa),
                                                           ctypes.byref(n)))
@@ -658,16 +666,19 @@ def prequantised_step(m, layer, cfg, st, K):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
-    (fa.w_gu_q, fa.w_gu_s, fa.w_dn_q, fa.w_dn_s, fa.ws, fa.ws_bytes) = saved
+    (fa.w_gu_q, fa.w_gu_s, fa.w_dn_q, fa.w_dn_s, fa.w_gu_ts, fa.w_dn_ts,
+     fa.ws, fa.ws_bytes) = saved
     if layer.bwd:
         (ba.w_gu_qt, ba.w_gu_st, ba.w_dn_qt, ba.w_dn_st, ba.ws,
          ba.ws_bytes) = bsaved
     flop = cfg.fwd_flop() + (cfg.bwd_flop() if cfg.backward else 0.0)
     return {"ms_per_step": round(ms, 4),
             "value": round(flop / (ms * 1e-3) / 1e12, 2),
-            "what": "weights quantised once outside the timed step (row-wise "
-                    "for the forward" + (", column-wise for the backward"
-                                          if layer.bwd else "") + ")"}
+            "what": "weights quantised once outside the timed step (" +
+                    ("one scale per expert" if cfg.mode == "fp8t" else
+                     "row-wise for the forward" +
+                     (", column-wise for the backward" if layer.bwd
+                      else "")) + ")"}
 
 
 def expert_loop_extra(m, layer, cfg, st, K):
@@ -972,7 +983,7 @@ def config_run(m, cfg, d, dev, K, W):
            "mfma_frac_step": round(tf / peak, 4),
            "dominant": {"kernel": dom, **gemms.get(dom, {})},
            "gemms": gemms, "hbm_kernels": hbm}
-    if cfg.mode == "mxfp8":
+    if cfg.mode in ("mxfp8", "fp8t"):
         out["prequantised_weights"] = prequantised_step(m, layer, cfg, st,
                                                         max(2, K // 2))
     del layer
@@ -1081,7 +1092,7 @@ def main():
     extras = {"peak_device_mem_GiB": round(peak_mem / 2**30, 2)}
     if not args.no_extras:
         extras["hbm_flushed"] = hbm_extras(m, layer, cfg, st)
-        if cfg.mode == "mxfp8":
+        if cfg.mode in ("mxfp8", "fp8t"):
             extras["prequantised_weights"] = prequantised_step(
                 m, layer, cfg, st, max(1, K // 2))
         if cfg.mode == "bf16" and not cfg.backward:

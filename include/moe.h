@@ -417,7 +417,8 @@ moe_status_t moe_fp8_tensor_quantize(moe_ctx_t ctx, const void* src,
  * float32(v / s), as in moe_fp8_tensor_quantize; the GEMMs multiply the
  * E4M3 products by the two scales; a (bf16, over all rows) is quantised the
  * same way for the down GEMM; h1_save / a_save hold the bf16 values.
- * x_perm_scale and the pre-quantised weight fields must be NULL.
+ * x_perm_scale, w_gu_s and w_dn_s must be NULL; the weights may come
+ * pre-quantised (w_gu_q + w_gu_ts, w_dn_q + w_dn_ts, below).
  * Sizes: 1 <= E <= 1024; H and F multiples of 64 (bf16) or 128 (8-bit);
  * one expert's operands must stay below 4 GiB (byte offsets are 32-bit).
  * Errors: MOE_ERR_INVALID_ARG (null required pointer, bad sizes),
@@ -460,6 +461,16 @@ typedef struct moe_mlp_fwd_args {
    * and E8M0 scales [rows, F/32] (row-major), as the down GEMM reads them */
   uint8_t* a_q_save;
   uint8_t* a_s_save;
+  /* FP8 tensor-scaled only, optional (with w_gu_q / w_dn_q, each pair both
+   * set or both NULL): the weights already quantised, as
+   * moe_fp8_tensor_quantize(w, n_seg = E) returns them: w_gu_q [E, 2F, H]
+   * E4M3 codes + w_gu_ts float32 [E] scales, w_dn_q [E, H, F] + w_dn_ts
+   * [E].  NULL: quantised from w_gu / w_dn inside the call.  Reuse
+   * contract as for the MXFP8 codes: they must be the quantisation of this
+   * call's w_gu / w_dn (not checked); a caller quantises them once per
+   * weight update. */
+  const float* w_gu_ts;
+  const float* w_dn_ts;
 } moe_mlp_fwd_args;
 
 moe_status_t moe_grouped_mlp_fwd_workspace_size(const moe_mlp_fwd_args* args,

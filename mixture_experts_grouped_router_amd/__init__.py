@@ -62,6 +62,7 @@ class _FwdArgs(ctypes.Structure):
         ("z_perm", _c_p), ("h1_save", _c_p), ("a_save", _c_p),
         ("ws", _c_p), ("ws_bytes", _c_sz),
         ("a_q_save", _c_p), ("a_s_save", _c_p),
+        ("w_gu_ts", _c_p), ("w_dn_ts", _c_p),
     ]
 
 
@@ -519,7 +520,10 @@ def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gu: torch.Tensor,
     """Grouped gate/up GEMM -> ScaledSwiGLU x w -> grouped down GEMM.
     Returns {"z": bf16 [rows, H]} (+ "h1", "a" when save=True; + "a_q",
     "a_s", A's MXFP8 codes and row-major scales, when save_a_codes=True in
-    MXFP8 mode)."""
+    MXFP8 mode).  w_gu_q / w_dn_q (optional, both or neither): the weights
+    quantised beforehand, (codes, E8M0 scales) from mxfp8_quantize ROWWISE
+    in MXFP8 mode, (codes, float32 scale per expert) from
+    fp8_tensor_quantize(w, E) in tensor-scaled FP8 mode."""
     E, F2, H = w_gu.shape
     F = F2 // 2
     rows = x_perm.shape[0]
@@ -547,10 +551,22 @@ def moe_grouped_mlp_fwd(x_perm: torch.Tensor, w_gu: torch.Tensor,
     args.x_perm = _ptr(x_perm)
     args.x_perm_scale = _ptr(x_perm_scale)
     args.w_gu, args.w_dn = _ptr(w_gu), _ptr(w_dn)
-    if w_gu_q is not None:
-        args.w_gu_q, args.w_gu_s = _ptr(w_gu_q[0]), _ptr(w_gu_q[1])
-    if w_dn_q is not None:
-        args.w_dn_q, args.w_dn_s = _ptr(w_dn_q[0]), _ptr(w_dn_q[1])
+    if precision == PREC_FP8_TENSOR:
+        # (E4M3 codes, float32 scale per expert) as fp8_tensor_quantize
+        # (w, n_seg=E) returns them
+        if w_gu_q is not None:
+            _need(w_gu_q[0], torch.uint8, (E, 2 * F, H), "w_gu_q codes")
+            _need(w_gu_q[1], torch.float32, (E,), "w_gu_q scales")
+            args.w_gu_q, args.w_gu_ts = _ptr(w_gu_q[0]), _ptr(w_gu_q[1])
+        if w_dn_q is not None:
+            _need(w_dn_q[0], torch.uint8, (E, H, F), "w_dn_q codes")
+            _need(w_dn_q[1], torch.float32, (E,), "w_dn_q scales")
+            args.w_dn_q, args.w_dn_ts = _ptr(w_dn_q[0]), _ptr(w_dn_q[1])
+    else:
+        if w_gu_q is not None:
+            args.w_gu_q, args.w_gu_s = _ptr(w_gu_q[0]), _ptr(w_gu_q[1])
+        if w_dn_q is not None:
+            args.w_dn_q, args.w_dn_s = _ptr(w_dn_q[0]), _ptr(w_dn_q[1])
     args.w_perm = _ptr(w_perm)
     args.offsets = _ptr(offsets)
     args.z_perm = _ptr(z)

@@ -605,7 +605,8 @@ moe_status_t moe_grouped_mlp_fwd_workspace_size(const moe_mlp_fwd_args* a,
                                         a->a_save == nullptr);
   else if (a->precision == MOE_PREC_FP8_TENSOR)
     *bytes = moe::mlp_fwd_fp8t_ws_bytes(a->E, a->H, a->F, a->rows,
-                                        a->a_save == nullptr);
+                                        a->a_save == nullptr,
+                                        a->w_gu_q == nullptr);
   else
     *bytes = moe::mlp_fwd_mx_ws_bytes(
         a->E, a->H, a->F, a->rows, a->x_perm_scale == nullptr,
@@ -626,12 +627,23 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
               "null x_perm / z_perm");
   const bool mx = a->precision == MOE_PREC_MXFP8_E4M3;
   const bool f8t = a->precision == MOE_PREC_FP8_TENSOR;
-  if (f8t)
-    MOE_REQUIRE(!a->x_perm_scale && !a->w_gu_q && !a->w_gu_s && !a->w_dn_q &&
-                    !a->w_dn_s,
+  if (f8t) {
+    MOE_REQUIRE(!a->x_perm_scale && !a->w_gu_s && !a->w_dn_s,
                 MOE_ERR_INVALID_ARG,
-                "FP8 tensor mode takes bf16 x_perm and bf16 weights");
-  if (!mx || a->w_gu_q == nullptr || a->w_dn_q == nullptr)
+                "FP8 tensor mode takes bf16 x_perm (and float32 weight "
+                "scales in w_gu_ts / w_dn_ts)");
+    const bool any = a->w_gu_q || a->w_gu_ts || a->w_dn_q || a->w_dn_ts;
+    MOE_REQUIRE(!any || (a->w_gu_q && a->w_gu_ts && a->w_dn_q && a->w_dn_ts),
+                MOE_ERR_INVALID_ARG,
+                "pre-quantised FP8 weights: all of w_gu_q, w_gu_ts, w_dn_q, "
+                "w_dn_ts or none");
+  } else {
+    MOE_REQUIRE(!a->w_gu_ts && !a->w_dn_ts, MOE_ERR_INVALID_ARG,
+                "w_gu_ts / w_dn_ts are FP8 tensor-scaled inputs");
+  }
+  const bool preq = (mx || f8t) && a->w_gu_q != nullptr &&
+                    a->w_dn_q != nullptr;
+  if (!preq)
     MOE_REQUIRE(a->w_gu && a->w_dn, MOE_ERR_INVALID_ARG, "null weights");
   if (mx && a->w_gu_q) MOE_REQUIRE(a->w_gu_s, MOE_ERR_INVALID_ARG, "w_gu_s");
   if (mx && a->w_dn_q) MOE_REQUIRE(a->w_dn_s, MOE_ERR_INVALID_ARG, "w_dn_s");
@@ -660,7 +672,8 @@ moe_status_t moe_grouped_mlp_fwd(moe_ctx_t ctx, const moe_mlp_fwd_args* a,
     MOE_REQUIRE(aligned16(a->h1_save) && aligned16(a->a_save),
                 MOE_ERR_UNSUPPORTED, "saves must be 16-byte aligned");
     e = moe::launch_mlp_fwd_fp8t(a->E, a->H, a->F, a->rows, a->x_perm,
-                                 a->w_gu, a->w_dn, a->w_perm, a->offsets,
+                                 a->w_gu, a->w_dn, a->w_gu_q, a->w_gu_ts,
+                                 a->w_dn_q, a->w_dn_ts, a->w_perm, a->offsets,
                                  a->z_perm, a->h1_save, a->a_save, a->ws,
                                  ctx->cu_count, ctx->status,
                                  as_stream(stream));

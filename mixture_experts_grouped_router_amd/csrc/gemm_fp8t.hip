@@ -27,7 +27,8 @@ struct Fp8tWs {
   size_t bytes;
 };
 
-Fp8tWs carve(void* base, int E, int H, int F, int64_t rows, bool need_a) {
+Fp8tWs carve(void* base, int E, int H, int F, int64_t rows, bool need_a,
+             bool quant_w) {
   Fp8tWs w{};
   char* p = static_cast<char*>(base);
   size_t off = 0;
@@ -41,8 +42,10 @@ Fp8tWs carve(void* base, int E, int H, int F, int64_t rows, bool need_a) {
   w.ts1 = reinterpret_cast<int32_t*>(take(tile_table_bytes(E, rows)));
   w.ts2 = reinterpret_cast<int32_t*>(take(tile_table_bytes(E, rows)));
   w.xq = reinterpret_cast<uint8_t*>(take((size_t)rows * H));
-  w.guq = reinterpret_cast<uint8_t*>(take((size_t)E * 2 * F * H));
-  w.dnq = reinterpret_cast<uint8_t*>(take((size_t)E * H * F));
+  if (quant_w) {
+    w.guq = reinterpret_cast<uint8_t*>(take((size_t)E * 2 * F * H));
+    w.dnq = reinterpret_cast<uint8_t*>(take((size_t)E * H * F));
+  }
   w.aq = reinterpret_cast<uint8_t*>(take((size_t)rows * F));
   w.a = need_a ? reinterpret_cast<uint16_t*>(take((size_t)rows * F * 2))
                : nullptr;
@@ -57,31 +60,46 @@ Fp8tWs carve(void* base, int E, int H, int F, int64_t rows, bool need_a) {
 
 }  // namespace
 
-size_t mlp_fwd_fp8t_ws_bytes(int E, int H, int F, int64_t rows, bool need_a) {
-  return carve(nullptr, E, H, F, rows, need_a).bytes;
+size_t mlp_fwd_fp8t_ws_bytes(int E, int H, int F, int64_t rows, bool need_a,
+                             bool quant_w) {
+  return carve(nullptr, E, H, F, rows, need_a, quant_w).bytes;
 }
 
 hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
                                const void* x_perm, const void* w_gu,
-                               const void* w_dn, const float* w_perm,
+                               const void* w_dn, const uint8_t* w_gu_q,
+                               const float* w_gu_ts, const uint8_t* w_dn_q,
+                               const float* w_dn_ts, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
                                int cu_count, int32_t* status,
                                hipStream_t stream) {
-  Fp8tWs w = carve(ws, E, H, F, rows, a_save == nullptr);
+  const bool quant_w = w_gu_q == nullptr;
+  Fp8tWs w = carve(ws, E, H, F, rows, a_save == nullptr, quant_w);
   uint16_t* a = a_save ? static_cast<uint16_t*>(a_save) : w.a;
-  // scale slots: 0 x, 1 A, 2 + e W_gu[e], 2 + E + e W_dn[e]
+  // scale slots: 0 x, 1 A, 2 + e W_gu[e], 2 + E + e W_dn[e] (the weights'
+  // slots unused when the caller passes their codes and scales)
+  const uint8_t* guq = w_gu_q;
+  const uint8_t* dnq = w_dn_q;
+  const float* gus = w_gu_ts;
+  const float* dns = w_dn_ts;
   hipError_t err = launch_zero_u32(w.amax, 2 + 2 * E, stream);
-  if (err == hipSuccess)
-    err = launch_seg_amax(w_gu, (int64_t)2 * F * H, E, w.amax + 2, stream);
-  if (err == hipSuccess)
-    err = launch_seg_amax(w_dn, (int64_t)H * F, E, w.amax + 2 + E, stream);
-  if (err == hipSuccess)
-    err = launch_tensor_quant(w_gu, (int64_t)2 * F * H, E, w.amax + 2, w.guq,
-                              w.scale + 2, stream);
-  if (err == hipSuccess)
-    err = launch_tensor_quant(w_dn, (int64_t)H * F, E, w.amax + 2 + E, w.dnq,
-                              w.scale + 2 + E, stream);
+  if (quant_w) {
+    guq = w.guq;
+    dnq = w.dnq;
+    gus = w.scale + 2;
+    dns = w.scale + 2 + E;
+    if (err == hipSuccess)
+      err = launch_seg_amax(w_gu, (int64_t)2 * F * H, E, w.amax + 2, stream);
+    if (err == hipSuccess)
+      err = launch_seg_amax(w_dn, (int64_t)H * F, E, w.amax + 2 + E, stream);
+    if (err == hipSuccess)
+      err = launch_tensor_quant(w_gu, (int64_t)2 * F * H, E, w.amax + 2,
+                                w.guq, w.scale + 2, stream);
+    if (err == hipSuccess)
+      err = launch_tensor_quant(w_dn, (int64_t)H * F, E, w.amax + 2 + E,
+                                w.dnq, w.scale + 2 + E, stream);
+  }
   if (err != hipSuccess || rows == 0) return err;
   err = launch_seg_amax(x_perm, rows * H, 1, w.amax, stream);
   if (err == hipSuccess)
@@ -100,7 +118,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   Params p1{};
   p1.a = reinterpret_cast<const char*>(w.xq);
   p1.lda = H;
-  p1.b = reinterpret_cast<const char*>(w.guq);
+  p1.b = reinterpret_cast<const char*>(guq);
   p1.ldb = H;
   p1.b_es = (int64_t)2 * F * H;
   p1.N = 2 * F;
@@ -118,7 +136,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   p1.w = w_perm;
   p1.rows = rows;
   p1.tsa = w.scale;
-  p1.tsb = w.scale + 2;
+  p1.tsb = gus;
   p1.amax_out = w.amax + 1;
   err = launch_w8q<P_FP8T, EPI_SWIGLU>(
       "gemm_gate_up_swiglu_fp8t", p1, ragged_m_grid(rows, E, tn1), stream);
@@ -130,7 +148,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   Params p2{};
   p2.a = reinterpret_cast<const char*>(w.aq);
   p2.lda = F;
-  p2.b = reinterpret_cast<const char*>(w.dnq);
+  p2.b = reinterpret_cast<const char*>(dnq);
   p2.ldb = F;
   p2.b_es = (int64_t)H * F;
   p2.N = H;
@@ -145,7 +163,7 @@ hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
   p2.ldc = H;
   p2.rows = rows;
   p2.tsa = w.scale + 1;
-  p2.tsb = w.scale + 2 + E;
+  p2.tsb = dns;
   enable_split(p2, w.split_part, w.split_cnt, w.split_x, cu_count);
   return launch_w8q<P_FP8T, EPI_STORE>("gemm_down_fp8t", p2,
                             ragged_m_grid_split(rows, E, tn2, p2), stream);

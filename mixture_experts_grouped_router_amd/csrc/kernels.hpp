@@ -89,10 +89,15 @@ hipError_t launch_seg_amax(const void* src, int64_t seg_elems, int n_seg,
 hipError_t launch_tensor_quant(const void* src, int64_t seg_elems, int n_seg,
                                const uint32_t* amax_bits, uint8_t* codes,
                                float* scales, hipStream_t stream);
-size_t mlp_fwd_fp8t_ws_bytes(int E, int H, int F, int64_t rows, bool need_a);
+// quant_w: the weights are quantised inside the call (else w_gu_q/_ts and
+// w_dn_q/_ts, quantised by the caller, are used)
+size_t mlp_fwd_fp8t_ws_bytes(int E, int H, int F, int64_t rows, bool need_a,
+                             bool quant_w);
 hipError_t launch_mlp_fwd_fp8t(int E, int H, int F, int64_t rows,
                                const void* x_perm, const void* w_gu,
-                               const void* w_dn, const float* w_perm,
+                               const void* w_dn, const uint8_t* w_gu_q,
+                               const float* w_gu_ts, const uint8_t* w_dn_q,
+                               const float* w_dn_ts, const float* w_perm,
                                const int32_t* offsets, void* z_perm,
                                void* h1_save, void* a_save, void* ws,
                                int cu_count, int32_t* status,

@@ -124,3 +124,45 @@ def test_fp8_tensor_backward_is_rejected(m):
         m.moe_grouped_mlp_bwd(dev_bf16(d["dy"]), x, dev_bf16(d["w_gu"]),
                               dev_bf16(d["w_dn"]), off, h1, a,
                               precision=m.PREC_FP8_TENSOR)
+
+
+@pytest.mark.parametrize("T,H,F,E,k,zipf", [(700, 256, 384, 5, 2, 1.2),
+                                           (512, 256, 8192, 4, 2, 0.0)])
+def test_fp8_tensor_prequantised_weights_equal_on_the_fly(m, T, H, F, E, k,
+                                                          zipf):
+    """The forward with the weights quantised once beforehand
+    (fp8_tensor_quantize with one tensor per expert, the reuse contract)
+    gives the bits of the call that quantises them itself; the weights'
+    codes and scales equal the oracle's."""
+    d = generate(T, H, F, E, k, zipf=zipf, seed=9,
+                 want=("x", "logits", "w_gu", "w_dn"))
+    idx, w = m.moe_route_topk(torch.from_numpy(d["logits"]).cuda(), k)
+    p = m.moe_permute(dev_bf16(d["x"]), idx, E, topk_w=w)
+    wgu, wdn = dev_bf16(d["w_gu"]), dev_bf16(d["w_dn"])
+    r1 = m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
+                               w_perm=p["w_perm"],
+                               precision=m.PREC_FP8_TENSOR, save=True)
+    gq = m.fp8_tensor_quantize(wgu, E)
+    dq = m.fp8_tensor_quantize(wdn, E)
+    rc, rs = O.fp8_tensor_quantize(d["w_gu"][1])
+    np.testing.assert_array_equal(gq[0][1].cpu().numpy().ravel(),
+                                  np.asarray(rc).ravel())
+    assert gq[1][1].item() == rs
+    r2 = m.moe_grouped_mlp_fwd(p["x_perm"], wgu, wdn, p["offsets"],
+                               w_perm=p["w_perm"],
+                               precision=m.PREC_FP8_TENSOR, save=True,
+                               w_gu_q=gq, w_dn_q=dq)
+    for key in ("z", "h1", "a"):
+        assert torch.equal(r1[key].view(torch.int16),
+                           r2[key].view(torch.int16)), key
+
+
+def test_fp8_tensor_prequantised_weights_need_both(m):
+    T, H, F, E, k = 64, 128, 128, 4, 1
+    d = generate(T, H, F, E, k, seed=6, want=("x", "w_gu", "w_dn"))
+    off = torch.tensor([0, 16, 32, 48, 64], dtype=torch.int32, device="cuda")
+    wgu = dev_bf16(d["w_gu"])
+    with pytest.raises(m.MoEError):
+        m.moe_grouped_mlp_fwd(dev_bf16(d["x"]), wgu, dev_bf16(d["w_dn"]),
+                              off, precision=m.PREC_FP8_TENSOR,
+                              w_gu_q=m.fp8_tensor_quantize(wgu, E))

@@ -74,6 +74,16 @@ def test_workspace_queries(lib):
     a.precision = 1
     assert lib.moe_expert_loop_mlp_fwd_workspace_size(ctypes.byref(a),
                                                       ctypes.byref(n)) == 2
+    # tensor-scaled FP8: weights quantised by the caller leave their codes
+    # (E * 3 * H * F bytes) out of the workspace
+    a.precision = 2
+    assert lib.moe_grouped_mlp_fwd_workspace_size(ctypes.byref(a),
+                                                  ctypes.byref(n)) == 0
+    own = n.value
+    a.w_gu_q, a.w_dn_q = 4096, 8192   # only their presence counts here
+    assert lib.moe_grouped_mlp_fwd_workspace_size(ctypes.byref(a),
+                                                  ctypes.byref(n)) == 0
+    assert own - n.value >= 8 * 3 * 4096 * 14336
 
 
 @pytest.fixture(scope="module")
