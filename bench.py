@@ -910,7 +910,7 @@ def router_extra(m, layer, cfg, d, st, K):
 
 # the other workloads, each timed in the default run after the headline one
 CONFIG_EXTRAS = ("tiny", "qwen3", "mixtral_mxfp8", "mixtral_mxfp8_bwd",
-                 "qwen3_long")
+                 "mixtral_fp8t", "qwen3_long")
 
 
 def _config_data(cfg, base_cfg, base_d):
