@@ -223,20 +223,6 @@ __device__ __forceinline__ bool decode_tile(const Params& p, TileCoord& tc) {
   return true;
 }
 
-// B operand row of tile row rr.  SwiGLU epilogues: 32-row blocks alternate
-// gate / up rows for the same 32 f columns, so one tile row block of 64 holds
-// both halves of 32 outputs.
-template <int EPI>
-__device__ __forceinline__ int b_row(const Params& p, int n0, int rr) {
-  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
-    const int blk = rr >> 5;
-    const int f = min(n0 + (blk >> 1) * 32 + (rr & 31), p.F - 1);
-    return (blk & 1) ? p.F + f : f;
-  } else {
-    return min(n0 + rr, p.N - 1);
-  }
-}
-
 // ---- K-contiguous operand: direct global -> LDS ----------------------------
 // buffer_load_dwordx4 ... lds: each wave instruction fills one contiguous KiB
 // of LDS.  Wave w, instruction j fills KiB 4 j + w of the tile = tile rows
@@ -261,7 +247,8 @@ struct KcDirect {
   __device__ __forceinline__ int row(int j) const {
     if constexpr (!IS_B) {
       return r0 + 32 * j + q;   // past the expert's rows: out of range -> 0
-    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      // 32-row blocks alternate gate / up rows for the same 32 f columns
       const int f = min(n0 + (j >> 1) * 32 + q, F - 1);
       return (j & 1) ? F + f : f;
     } else {
@@ -430,11 +417,6 @@ struct Frags<P_BF16> {
         (MOE_LDS i16x4_t*)(p + 4 * 512));
     const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8_t, v);
-  }
-  __device__ __forceinline__ void load_a_tr(const char* sa, int kk,
-                                            const uint32_t (&o)[4]) {
-    const char* s = sa + kk * 16 * 512;
-    a0 = tr8(s + o[0]); a1 = tr8(s + o[1]); a2 = tr8(s + o[2]); a3 = tr8(s + o[3]);
   }
   __device__ __forceinline__ void load_b_tr(const char* sb, int kk,
                                             const uint32_t (&o)[4]) {
@@ -632,12 +614,11 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
   //   col = wn*128 + j*32 + lane%32
   const int colw = lane & 31;
   const int mw = tc.m0 + wm * 128;   // first row of the wave's block
-  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
+  if constexpr (EPI == EPI_SWIGLU) {
     // B rows of block j: gate f-block (2 wn + j/2) for even j, up for odd j.
-    // silu(g) * u goes through LDS (float32); the routing weight, the
-    // bf16 / MXFP8 encoding and the stores happen per row on readback,
-    // where lane l owns rows 8 q + l / 8 and f values 8 (l % 8) .. + 7 of
-    // the wave's 64 (a quad of lanes holds one 32-value MXFP8 block).
+    // silu(g) * u goes through LDS (float32); the routing weight, the bf16
+    // rounding and the stores happen per row on readback, where lane l owns
+    // rows 8 q + l / 8 and f values 8 (l % 8) .. + 7 of the wave's 64.
     const int64_t ld1 = 2 * (int64_t)p.F;
     const bool fvalid = n0 + 64 * wn < p.F;   // F % 64 == 0: whole runs
     float* wrow = row_weights(p, tc, mw, lane, t);
@@ -689,7 +670,6 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
     const int c8 = lane & 7;
     const int f = n0 + 64 * wn + 8 * c8;
-    uint32_t amx = 0;   // amax_out: largest |A| of the lane, bf16 bits
 #pragma unroll
     for (int qb = 0; qb < 16; qb += 4) {
       uint4 c0[4], c1[4];
@@ -711,41 +691,11 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
                       __uint_as_float(c1[q].z), __uint_as_float(c1[q].w)};
 #pragma unroll
         for (int c = 0; c < 8; ++c) v[c] *= wr;
-        if constexpr (EPI == EPI_SWIGLU_MX) {
-          // F % 128 == 0: blocks are whole; every lane takes part in the
-          // quad reduction, rows past the expert just do not store
-          int sx;
-          const uint2 w8 = mx_quad_encode_f32(v, &sx);
-          if (ok) {
-            *reinterpret_cast<uint2*>(p.cq + row * p.F + f) = w8;
-            if ((c8 & 3) == 0) {
-              p.cs[mx_tile_off((uint32_t)row, (uint32_t)(f / 32),
-                               (uint32_t)(p.F / 128))] = (uint8_t)(sx + 127);
-              if (p.cs_rm)
-                p.cs_rm[row * (p.F / 32) + f / 32] = (uint8_t)(sx + 127);
-            }
-          }
-        }
-        if (ok && (EPI == EPI_SWIGLU || p.c)) {
-          const uint4 o =
+        if (ok)
+          *reinterpret_cast<uint4*>(p.c + row * p.ldc + f) =
               make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-          *reinterpret_cast<uint4*>(p.c + row * p.ldc + f) = o;
-          if (p.amax_out) {
-            const uint32_t w4[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-              amx = max(amx, max(w4[d] & 0x7fffu, (w4[d] >> 16) & 0x7fffu));
-          }
-        }
       }
-    }
-    if (p.amax_out) {
-      // the bf16 magnitudes order like their float32 bits
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1)
-        amx = max(amx, (uint32_t)__shfl_xor((int)amx, off, 64));
-      if (lane == 0) atomicMax(p.amax_out, amx << 16);
     }
   } else if constexpr (EPI == EPI_STORE) {
     // bf16 C through LDS; on readback lane l takes chunk l % 16 (8 columns)
@@ -759,11 +709,10 @@ __device__ __forceinline__ void epilogue(const Params& p, const TileCoord& tc,
           stage_bf16(wbuf, acc_row(i, r, lane), j * 32 + colw, acc[i][j][r]);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
     uint16_t* cbase = p.c;
-    if constexpr (G == RAGGED_K) cbase += (int64_t)tc.e * p.c_es;
     const int ch = lane & 15;
     const int col = n0 + wn * 128 + 8 * ch;   // N % 64 == 0
-    const int mlim = G == RAGGED_M ? tc.seg_len : p.M;
-    const int64_t rbase = G == RAGGED_M ? tc.seg0 : 0;
+    const int mlim = tc.seg_len;
+    const int64_t rbase = tc.seg0;
 #pragma unroll
     for (int qb = 0; qb < 32; qb += 16) {
       uint4 v[16];
@@ -929,15 +878,6 @@ __device__ __forceinline__ bool decode_item(const Params& p, int nk, int x,
                         idx, tc, sr, p.mrec, p.tiles_n);
 }
 
-// Work-group b of a one-item-per-work-group launch: XCD b mod 8 (where the
-// dispatcher puts it), item b / 8 of that XCD.
-__device__ __forceinline__ bool decode_tile_split(const Params& p, int nk,
-                                                  TileCoord& tc,
-                                                  SplitRange& sr) {
-  const int b = blockIdx.x;
-  return decode_item(p, nk, b % kXcds, b / kXcds, tc, sr);
-}
-
 // ---- persistent ragged-M launches -------------------------------------------
 // One work-group per CU.  Per item a work-group on XCD x first takes the
 // next index of its own XCD's counter (so an expert's tiles keep sharing
@@ -1041,16 +981,18 @@ struct Shape8 {
   static constexpr int WN = 8 / (8 / MI);               // waves along N
 };
 
+// The four-wave kernel serves the GEMMs the eight-wave kernels do not take:
+// ragged M with a K-contiguous A, a bf16 or MXFP8 B (bf16 B may be
+// N-contiguous): the per-expert loop's plain store, the bf16 gate/up GEMM
+// with H above kW8MaxGateUpK, and the dgrad of the down projection with the
+// SwiGLU-backward epilogue (bf16 and MXFP8).
 template <int P, int LA, int LB, int G, int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
-  static_assert(P == P_BF16 || (LA == KC && LB == KC),
-                "MXFP8 operands are K-contiguous");
-  // RAGGED_K with K-contiguous operands needs every expert's K range padded
-  // to whole K steps (the MXFP8 token-direction layout)
-  static_assert(G == RAGGED_M || P != P_BF16 || (LA == MC && LB == MC),
-                "bf16 RAGGED_K operands are MN-contiguous");
-  // the 8-bit modes share fragments and MFMAs (unit scales for P_FP8T)
-  constexpr int PF = P == P_BF16 ? P_BF16 : P_FP8;
+  static_assert(G == RAGGED_M && LA == KC, "ragged M, K-contiguous A");
+  static_assert(P == P_BF16 || (P == P_FP8 && LB == KC),
+                "bf16, or MXFP8 with a K-contiguous B");
+  static_assert(EPI != EPI_SWIGLU_MX, "the MXFP8 gate/up is eight-wave");
+  constexpr int PF = P;
   using Fr = Frags<PF>;
   constexpr int kSl = Fr::kSlices;
   constexpr int kElemBytes = P == P_BF16 ? 2 : 1;
@@ -1060,21 +1002,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char sB0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sA1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sB1[kTileBytes];
-  // the forward down GEMM (ragged M, K-contiguous operands, plain store)
-  // may split the K range of its last round of tiles
-  constexpr bool kMaySplit = G == RAGGED_M && EPI == EPI_STORE && LA == KC &&
-                             LB == KC;
   TileCoord tc;
-  SplitRange sr;
-  if constexpr (kMaySplit) {
-    if (!decode_tile_split(p, (p.K + kStepK - 1) / kStepK, tc, sr)) return;
-  } else {
-    if (!decode_tile<G>(p, tc)) return;
-    sr.ks = 0;
-    sr.S = 1;
-  }
-  // a split work-group starts at K step ks (bytes into every row)
-  const uint32_t kofs = (uint32_t)sr.ks * kRowBytes;
+  if (!decode_tile<G>(p, tc)) return;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -1083,56 +1012,29 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   const int wn = wave & 1;    // 0..1
 
   // ---- tile geometry ----
-  int kdim, n0;
-  if constexpr (G == RAGGED_M) kdim = p.K;
-  else kdim = tc.seg_len;
-  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX)
-    n0 = tc.nt * (BN / 2);   // f units
-  else
-    n0 = tc.nt * BN;
+  const int kdim = p.K;
+  const int n0 = EPI == EPI_SWIGLU ? tc.nt * (BN / 2)   // f units
+                                   : tc.nt * BN;
 
   // ---- operand sources ----
   KcDirect<EPI, false> da;
   KcDirect<EPI, true> db;
-  McDirect ma, mb;
+  McDirect mb;
   MxScales ms;
   const int q = 8 * wave + (lane >> 3);   // direct-load row inside 32 rows
   const int cl = (lane & 7) ^ swz32(q);   // its logical chunk
-  if constexpr (LA == KC) {
-    if constexpr (G == RAGGED_M) {
-      // rows seg0 + m0 + r; rows past the expert's last read as zeros
-      da.base = p.a + (int64_t)tc.seg0 * p.lda + kofs;
-      da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda - kofs;
-    } else {
-      // A [M][K]: the expert's K range starts at element seg0 of every row
-      // (a multiple of the K step); rows past M read as zeros
-      const uint32_t kofs = (uint32_t)tc.seg0 * kElemBytes;
-      da.base = p.a + kofs;
-      da.rec = (uint32_t)p.M * (uint32_t)p.lda - kofs;
-    }
-    da.ld = p.lda;
-    da.q = q;
-    da.cl = cl;
-    da.r0 = tc.m0;
-    da.init();
-  } else {
-    // A element (m, k) at a + (seg0 + k) * lda + 2 m (RAGGED_K: k = token)
-    ma.base = p.a + (int64_t)tc.seg0 * p.lda + 2 * (int64_t)tc.m0;
-    ma.rec = (uint32_t)kdim * (uint32_t)p.lda - 2u * (uint32_t)tc.m0;
-    ma.ld = p.lda;
-    ma.init(wave, lane);
-  }
+  // rows seg0 + m0 + r; rows past the expert's last read as zeros
+  da.base = p.a + (int64_t)tc.seg0 * p.lda;
+  da.rec = (uint32_t)tc.seg_len * (uint32_t)p.lda;
+  da.ld = p.lda;
+  da.q = q;
+  da.cl = cl;
+  da.r0 = tc.m0;
+  da.init();
   const char* bexp = p.b + (int64_t)tc.e * p.b_es;
   if constexpr (LB == KC) {
-    if constexpr (G == RAGGED_M) {
-      db.base = bexp + kofs;
-      db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb - kofs;
-    } else {
-      // B [N][K], same K range as A
-      const uint32_t kofs = (uint32_t)tc.seg0 * kElemBytes;
-      db.base = p.b + kofs;
-      db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb - kofs;
-    }
+    db.base = bexp;
+    db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb;
     db.ld = p.ldb;
     db.q = q;
     db.cl = cl;
@@ -1141,31 +1043,23 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     db.N = p.N;
     db.init();
   } else {
-    // B element (n, k) at b_e + k * ldb + 2 n (RAGGED_K: b + (seg0 + k) ...)
-    if constexpr (G == RAGGED_M) mb.base = bexp + 2 * (int64_t)n0;
-    else mb.base = p.b + (int64_t)tc.seg0 * p.ldb + 2 * (int64_t)n0;
+    // B element (n, k) at b_e + k * ldb + 2 n
+    mb.base = bexp + 2 * (int64_t)n0;
     mb.rec = (uint32_t)kdim * (uint32_t)p.ldb - 2u * (uint32_t)n0;
     mb.ld = p.ldb;
     mb.init(wave, lane);
   }
-  // transposed-read offsets of the MN-contiguous sides
-  uint32_t tra[4], trb[4];
-  if constexpr (LA == MC) McDirect::frag_offsets(wm, lane, tra);
+  // transposed-read offsets of an N-contiguous B
+  uint32_t trb[4];
   if constexpr (LB == MC) McDirect::frag_offsets(wn, lane, trb);
-  // E8M0 scale bytes of the current K step (P_FP8T: 127 = 2^0 throughout)
-  constexpr uint32_t kS0 = P == P_FP8T ? 0x7f7f7f7fu : 0u;
-  uint32_t sa_cur[4] = {kS0, kS0, kS0, kS0}, sb_cur[4] = {kS0, kS0, kS0, kS0};
+  // E8M0 scale bytes of the current K step
+  uint32_t sa_cur[4] = {0, 0, 0, 0}, sb_cur[4] = {0, 0, 0, 0};
   // byte selector for v_perm: lane group g takes scale bytes (g, 2 + g)
   const uint32_t sel = (lane >> 5) ? 0x0c0c0301u : 0x0c0c0200u;
   if constexpr (P == P_FP8) {
-    if constexpr (G == RAGGED_M) {
-      // scales of K step s at byte 128 s of a row block's run
-      ms.a = p.sa + kofs;
-      ms.b = p.sb + (int64_t)tc.e * p.sb_es + kofs;
-    } else {   // the expert's first K step (seg0 is a multiple of 128)
-      ms.a = p.sa + tc.seg0;
-      ms.b = p.sb + tc.seg0;
-    }
+    // scales of K step s at byte 128 s of a row block's run
+    ms.a = p.sa;
+    ms.b = p.sb + (int64_t)tc.e * p.sb_es;
     KcDirect<EPI, true> m;   // B row mapping of the lane's 32-row blocks
     m.q = lane & 31;
     m.n0 = n0;
@@ -1174,8 +1068,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ra = min(tc.m0 + wm * 128 + 32 * i + (lane & 31),
-                         (G == RAGGED_M ? tc.seg_len : p.M) - 1);
-      const uint32_t rabs = G == RAGGED_M ? (uint32_t)(tc.seg0 + ra) : ra;
+                         tc.seg_len - 1);
+      const uint32_t rabs = (uint32_t)(tc.seg0 + ra);
       ms.oa[i] = mx_tile_off(rabs, 0, (uint32_t)p.ldsa);
       // B tile row wn*128 + 32 i + lane%32 is direct-load block 4 wn + i
       ms.ob[i] = mx_tile_off((uint32_t)m.row(4 * wn + i), 0,
@@ -1189,19 +1083,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  const int nk = kMaySplit ? sr.ke - sr.ks : (kdim + kStepK - 1) / kStepK;
-  // LDS reads per K slice: 4 per K-contiguous side (16-byte reads), 8 per
-  // MN-contiguous side (two 8-byte transposed reads per block); MXFP8 16
-  constexpr int kNR = P != P_BF16 ? 16
-                                 : (LA == KC ? 4 : 8) + (LB == KC ? 4 : 8);
+  const int nk = (kdim + kStepK - 1) / kStepK;
+  // LDS reads per K slice: 4 per K-contiguous side (16-byte reads), 8 for
+  // an N-contiguous B (two 8-byte transposed reads per block); MXFP8 16
+  constexpr int kNR = P != P_BF16 ? 16 : 4 + (LB == KC ? 4 : 8);
   // part 1: A (and the MXFP8 scales), part 2: B, 3: both
   auto issue_part = [&](char* bufa, char* bufb, int kt, bool real, int part) {
     // a padding step (real == false) reads zeros: empty descriptors for
     // direct loads, k rows past kvalid for staged loads; its scales are
     // those of the last real step (finite; they multiply zeros)
     if (part & 1) {
-      if constexpr (LA == KC) da.issue(bufa, (uint32_t)kt * kRowBytes, real, wave);
-      else ma.issue(bufa, kt, real, wave);
+      da.issue(bufa, (uint32_t)kt * kRowBytes, real, wave);
       if constexpr (P == P_FP8) ms.load(min(kt, nk - 1));
     }
     if (part & 2) {
@@ -1219,10 +1111,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // bf16 dgrad (N-contiguous B): six per MFMA (Qwen3-shaped long-sequence
   // dgrad of the down projection with the SwiGLU backward: one 1.356, three
   // 1.329-1.334, six 1.311-1.313 ms; the 8-bit modes did best with three);
-  // the wgrads, both operands M-contiguous, stay at one (1.546 -> 1.57 ms
-  // with three)
+  // the four-wave wgrads, both operands M-contiguous, did best with one
+  // (1.546 -> 1.57 ms with three)
   constexpr int kVpm = P != P_BF16 ? kLoadVpm8
-                       : (LA == KC && LB == MC) ? 6 : kLoadVpmBf16;
+                       : LB == MC ? 6 : kLoadVpmBf16;
   // 8-bit modes: the stage barrier after three of the last slice's four
   // row blocks of MFMAs, the last four overlapping the next stage's first
   // fragment reads (MXFP8 gate/up 1.888-1.903 -> 1.857-1.868 ms, down
@@ -1242,13 +1134,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   };
   // fragments of K slice kk from stage (sa, sb)
   auto fload = [&](Fr& f, const char* sa, const char* sb, int kk) {
-    if constexpr (LA == KC && LB == KC) {
+    if constexpr (LB == KC) {
       f.load(sa, sb, kk, wm, wn, lane);
     } else {
-      if constexpr (LA == MC) f.load_a_tr(sa, kk, tra);
-      else f.load_a(sa, kk, wm, lane);
-      if constexpr (LB == MC) f.load_b_tr(sb, kk, trb);
-      else f.load_b(sb, kk, wn, lane);
+      f.load_a(sa, kk, wm, lane);
+      f.load_b_tr(sb, kk, trb);
     }
   };
   auto take_scales = [&]() {
@@ -1354,19 +1244,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // every wave is past its last LDS read of the operand stages (and every
   // direct load has landed) before the stages become epilogue staging
   __syncthreads();
-  if constexpr (kMaySplit) {
-    __shared__ uint32_t arrived;
-    if (sr.S > 1 && !split_reduce<kThreads>(p, sr, acc, t, &arrived)) return;
-  }
   char* wbuf = wave == 0 ? sA0 : wave == 1 ? sB0 : wave == 2 ? sA1 : sB1;
-  if constexpr (P == P_FP8T) {
-    // the two tensor scales
-    const float f = p.tsa[0] * p.tsb[tc.e];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] *= f;
-  }
   epilogue<G, EPI>(p, tc, acc, n0, wm, wn, lane, t, wbuf);
 }
 
