@@ -312,7 +312,7 @@ hipError_t launch_mlp_bwd_bf16(int E, int H, int F, int64_t rows,
     p.w = w_perm;
     p.dw_part = dw_perm ? part : nullptr;
     p.rows = rows;
-    err = launch<P_BF16, KC, MC, RAGGED_M, EPI_SWIGLU_BWD>(
+    err = launch_w8b<KC, MC, RAGGED_M, EPI_SWIGLU_BWD>(
         "gemm_dgrad_down_swiglu_bwd", p, ragged_m_grid(rows, E, tnf),
                                                    stream);
     if (err != hipSuccess) return err;

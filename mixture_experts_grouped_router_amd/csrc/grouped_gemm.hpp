@@ -274,60 +274,6 @@ struct KcDirect {
   }
 };
 
-// ---- MN-contiguous bf16 operand: direct global -> LDS, transposed reads -----
-// The stage holds the step's 64 k rows of the tile's 256 mn values (512
-// bytes each) as they lie in memory; 16-byte chunk c of row k sits at chunk
-// c ^ 4 (k & 3).  Wave w, instruction j fills KiB 4 j + w = rows
-// 2 (4 j + w) + lane / 32, and each lane loads the logical chunk that
-// belongs at its slot.  MFMA fragments come from ds_read_b64_tr_b16: in a
-// group of 16 lanes, lane i receives element i % 4 of the 8 bytes addressed
-// by lane 4 j + i / 4 as its element j; with lane 4 j + q addressing row
-// k0 + j, mn mb + 4 q .. +3, lane i gets mn mb + i at k0 .. k0 + 3.  Two
-// such reads (k and k + 4) give a lane its 8 k values; the swizzle puts the
-// 4 rows x 2 groups of a read on 16 distinct chunks (no bank conflicts).
-// Rows at or past kvalid read as zeros through the buffer descriptor; mn
-// past the operand's end reads the next row (or zeros): those outputs are
-// never stored.
-struct McDirect {
-  const char* base;  // wave-uniform: element (k = 0, mn = tile start)
-  uint32_t rec;      // valid bytes from base
-  int64_t ld;        // bytes per k row
-  uint32_t off[8];   // per instruction: byte offset of the lane's chunk
-  __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 2 * (4 * j + wave) + (lane >> 5);
-      const int c = (lane & 31) ^ (4 * (row & 3));
-      off[j] = (uint32_t)row * (uint32_t)ld + (uint32_t)(c * 16);
-    }
-  }
-  __device__ __forceinline__ void issue(char* lds_tile, int kt, bool real,
-                                        int wave) const {
-    const uint32_t kb = (uint32_t)kt * 64u * (uint32_t)ld;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(base + kb), (short)0, (int)(real ? rec - kb : 0u),
-        kBufFlags);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      MOE_LDS void* dst =
-          (MOE_LDS void*)(lds_tile + (4 * j + wave) * 1024);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off[j], 0, 0, 0);
-    }
-  }
-  // lane's byte offsets of its 4 32-row blocks (K slice 0, first read) in
-  // the wave's half (side = wm or wn) of the stage
-  static __device__ __forceinline__ void frag_offsets(int side, int lane,
-                                                      uint32_t (&o)[4]) {
-    const int G = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
-    const int k0 = 8 * (G >> 1) + j;
-    const int x = 2 * (G & 1) + (q >> 1) + 16 * side;   // chunk, bits 2-3 clear
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)(k0 * 512 + (((x + 4 * i) ^ (4 * j)) * 16) +
-                        (q & 1) * 8);
-  }
-};
-
 // ---- MXFP8 scales of one K step --------------------------------------------
 // Lane l needs, for each of its 4 A row blocks and 4 B row blocks, the scale
 // bytes of K blocks g and 2+g of the step (g = l/32): one dword (4 blocks)
@@ -408,7 +354,7 @@ struct Frags<P_BF16> {
     load_a(sa, kk, wm, lane);
     load_b(sb, kk, wn, lane);
   }
-  // 8 k values of the lane from a [k][mn] stage (McDirect layout): two
+  // 8 k values of the lane from a [k][mn] stage (McDirect8 layout): two
   // transposed 8-byte reads, k and k + 4 rows apart
   static __device__ __forceinline__ bf16x8_t tr8(const char* p) {
     const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -417,11 +363,6 @@ struct Frags<P_BF16> {
         (MOE_LDS i16x4_t*)(p + 4 * 512));
     const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8_t, v);
-  }
-  __device__ __forceinline__ void load_b_tr(const char* sb, int kk,
-                                            const uint32_t (&o)[4]) {
-    const char* s = sb + kk * 16 * 512;
-    b0 = tr8(s + o[0]); b1 = tr8(s + o[1]); b2 = tr8(s + o[2]); b3 = tr8(s + o[3]);
   }
 };
 
@@ -981,16 +922,15 @@ struct Shape8 {
   static constexpr int WN = 8 / (8 / MI);               // waves along N
 };
 
-// The four-wave kernel serves the GEMMs the eight-wave kernels do not take:
-// ragged M with a K-contiguous A, a bf16 or MXFP8 B (bf16 B may be
-// N-contiguous): the per-expert loop's plain store, the bf16 gate/up GEMM
-// with H above kW8MaxGateUpK, and the dgrad of the down projection with the
-// SwiGLU-backward epilogue (bf16 and MXFP8).
+// The four-wave kernel serves the GEMMs the eight-wave kernels do not take,
+// all ragged M with K-contiguous operands: the per-expert loop's plain
+// store, the bf16 gate/up GEMM with H above kW8MaxGateUpK, and the MXFP8
+// dgrad of the down projection with the SwiGLU-backward epilogue.
 template <int P, int LA, int LB, int G, int EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
-  static_assert(G == RAGGED_M && LA == KC, "ragged M, K-contiguous A");
-  static_assert(P == P_BF16 || (P == P_FP8 && LB == KC),
-                "bf16, or MXFP8 with a K-contiguous B");
+  static_assert(G == RAGGED_M && LA == KC && LB == KC,
+                "ragged M, K-contiguous operands");
+  static_assert(P == P_BF16 || P == P_FP8, "bf16 or MXFP8");
   static_assert(EPI != EPI_SWIGLU_MX, "the MXFP8 gate/up is eight-wave");
   constexpr int PF = P;
   using Fr = Frags<PF>;
@@ -1019,7 +959,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // ---- operand sources ----
   KcDirect<EPI, false> da;
   KcDirect<EPI, true> db;
-  McDirect mb;
   MxScales ms;
   const int q = 8 * wave + (lane >> 3);   // direct-load row inside 32 rows
   const int cl = (lane & 7) ^ swz32(q);   // its logical chunk
@@ -1032,26 +971,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   da.r0 = tc.m0;
   da.init();
   const char* bexp = p.b + (int64_t)tc.e * p.b_es;
-  if constexpr (LB == KC) {
-    db.base = bexp;
-    db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb;
-    db.ld = p.ldb;
-    db.q = q;
-    db.cl = cl;
-    db.n0 = n0;
-    db.F = p.F;
-    db.N = p.N;
-    db.init();
-  } else {
-    // B element (n, k) at b_e + k * ldb + 2 n
-    mb.base = bexp + 2 * (int64_t)n0;
-    mb.rec = (uint32_t)kdim * (uint32_t)p.ldb - 2u * (uint32_t)n0;
-    mb.ld = p.ldb;
-    mb.init(wave, lane);
-  }
-  // transposed-read offsets of an N-contiguous B
-  uint32_t trb[4];
-  if constexpr (LB == MC) McDirect::frag_offsets(wn, lane, trb);
+  db.base = bexp;
+  db.rec = (uint32_t)p.b_rows * (uint32_t)p.ldb;
+  db.ld = p.ldb;
+  db.q = q;
+  db.cl = cl;
+  db.n0 = n0;
+  db.F = p.F;
+  db.N = p.N;
+  db.init();
   // E8M0 scale bytes of the current K step
   uint32_t sa_cur[4] = {0, 0, 0, 0}, sb_cur[4] = {0, 0, 0, 0};
   // byte selector for v_perm: lane group g takes scale bytes (g, 2 + g)
@@ -1086,7 +1014,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   const int nk = (kdim + kStepK - 1) / kStepK;
   // LDS reads per K slice: 4 per K-contiguous side (16-byte reads), 8 for
   // an N-contiguous B (two 8-byte transposed reads per block); MXFP8 16
-  constexpr int kNR = P != P_BF16 ? 16 : 4 + (LB == KC ? 4 : 8);
+  constexpr int kNR = P != P_BF16 ? 16 : 8;
   // part 1: A (and the MXFP8 scales), part 2: B, 3: both
   auto issue_part = [&](char* bufa, char* bufb, int kt, bool real, int part) {
     // a padding step (real == false) reads zeros: empty descriptors for
@@ -1097,8 +1025,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
       if constexpr (P == P_FP8) ms.load(min(kt, nk - 1));
     }
     if (part & 2) {
-      if constexpr (LB == KC) db.issue(bufb, (uint32_t)kt * kRowBytes, real, wave);
-      else mb.issue(bufb, kt, real, wave);
+      db.issue(bufb, (uint32_t)kt * kRowBytes, real, wave);
     }
   };
   auto issue = [&](char* bufa, char* bufb, int kt, bool real) {
@@ -1108,13 +1035,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // the first slice and B over the second), spread between the MFMAs.
   constexpr bool kSplit = kSl >= 3;
   constexpr int kVmA = 8 + (P == P_FP8 ? 8 : 0);   // A loads (+ scales)
-  // bf16 dgrad (N-contiguous B): six per MFMA (Qwen3-shaped long-sequence
-  // dgrad of the down projection with the SwiGLU backward: one 1.356, three
-  // 1.329-1.334, six 1.311-1.313 ms; the 8-bit modes did best with three);
-  // the four-wave wgrads, both operands M-contiguous, did best with one
-  // (1.546 -> 1.57 ms with three)
-  constexpr int kVpm = P != P_BF16 ? kLoadVpm8
-                       : LB == MC ? 6 : kLoadVpmBf16;
+  constexpr int kVpm = P != P_BF16 ? kLoadVpm8 : kLoadVpmBf16;
   // 8-bit modes: the stage barrier after three of the last slice's four
   // row blocks of MFMAs, the last four overlapping the next stage's first
   // fragment reads (MXFP8 gate/up 1.888-1.903 -> 1.857-1.868 ms, down
@@ -1134,12 +1055,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   };
   // fragments of K slice kk from stage (sa, sb)
   auto fload = [&](Fr& f, const char* sa, const char* sb, int kk) {
-    if constexpr (LB == KC) {
-      f.load(sa, sb, kk, wm, wn, lane);
-    } else {
-      f.load_a(sa, kk, wm, lane);
-      f.load_b_tr(sb, kk, trb);
-    }
+    f.load(sa, sb, kk, wm, wn, lane);
   };
   auto take_scales = [&]() {
     if constexpr (P == P_FP8) {

@@ -306,6 +306,145 @@ __device__ __forceinline__ void epilogue_w8_swiglu(const Params& p,
   }
 }
 
+// EPI_SWIGLU_BWD (dgrad of the down projection and the SwiGLU backward) of
+// a wave's 128 rows x 64 f (acc[i][j][r] = dA at row acc_row(i, r), f =
+// n0 + 64 wn + 32 j + lane % 32), in two passes of 32 f through the wave's
+// 16 KiB of LDS (float32, 128-byte rows, stg8).  On readback lane l owns
+// rows 16 q + l / 4 and f values 8 (l % 4) .. + 7 of the pass: it reads the
+// saved (g, u) of those f with 16-byte loads, writes dg and du with 16-byte
+// stores and sums dA silu(g) u for the routing-weight gradient; the four
+// lanes of a row, then the tile's four N waves (in wave order, through red)
+// add their sums.  wrow: 128 floats per wave; red: 4 x 256 floats.  A wave
+// without rows (act false) only meets the barrier.
+__device__ __forceinline__ void epilogue_w8_swiglu_bwd(
+    const Params& p, const TileCoord& tc, f32x16_t (&acc)[4][2], int n0,
+    int wm, int wn, int lane, int t, bool act, char* wbuf, float* wrow,
+    float* red) {
+  const int64_t ld1 = 2 * (int64_t)p.F;
+  const int mw = tc.m0 + wm * 128;
+  const int c4 = lane & 3;
+  float rsum[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) rsum[q] = 0.0f;
+  if (act) {
+    const int colw = lane & 31;
+    wrow[lane] = p.w ? p.w[tc.seg0 + min(mw + lane, tc.seg_len - 1)] : 1.0f;
+    wrow[64 + lane] =
+        p.w ? p.w[tc.seg0 + min(mw + 64 + lane, tc.seg_len - 1)] : 1.0f;
+    auto fpass = [&](int pass) { return n0 + wn * 64 + 32 * pass; };
+    // batch b: pass b / 2, rows q = 4 (b % 2) .. + 3
+    auto load_gu = [&](int b, uint4 (&g4)[4], uint4 (&u4)[4]) {
+      const int f = fpass(b >> 1) + 8 * c4;
+      if (fpass(b >> 1) >= p.F) return;   // F % 32 == 0
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int mrow = min(mw + 16 * (4 * (b & 1) + q) + (lane >> 2),
+                             tc.seg_len - 1);
+        const uint16_t* h = p.h1 + (tc.seg0 + mrow) * ld1 + f;
+        g4[q] = *reinterpret_cast<const uint4*>(h);
+        u4[q] = *reinterpret_cast<const uint4*>(h + p.F);
+      }
+    };
+    auto stage_pass = [&](int pass) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row(i, r, lane);
+          *reinterpret_cast<float*>(wbuf + stg8(row, colw >> 2) +
+                                    (colw & 3) * 4) = acc[i][pass][r];
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): staging written
+    };
+    auto run_batch = [&](int b, const uint4 (&g4)[4], const uint4 (&u4)[4]) {
+      const int pass = b >> 1;
+      const int f = fpass(pass) + 8 * c4;
+      if (fpass(pass) >= p.F) return;
+      uint4 c0[4], c1[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lr = 16 * (4 * (b & 1) + q) + (lane >> 2);
+        c0[q] = *reinterpret_cast<const uint4*>(wbuf + stg8(lr, 2 * c4));
+        c1[q] = *reinterpret_cast<const uint4*>(wbuf + stg8(lr, 2 * c4 + 1));
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int qq = 4 * (b & 1) + q;
+        const int lr = 16 * qq + (lane >> 2);
+        const int mrow = mw + lr;
+        const float da[8] = {
+            __uint_as_float(c0[q].x), __uint_as_float(c0[q].y),
+            __uint_as_float(c0[q].z), __uint_as_float(c0[q].w),
+            __uint_as_float(c1[q].x), __uint_as_float(c1[q].y),
+            __uint_as_float(c1[q].z), __uint_as_float(c1[q].w)};
+        const uint32_t gw[4] = {g4[q].x, g4[q].y, g4[q].z, g4[q].w};
+        const uint32_t uw[4] = {u4[q].x, u4[q].y, u4[q].z, u4[q].w};
+        const float wr = wrow[lr];
+        uint32_t dgw[4], duw[4];
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float dgv[2], duv[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float g = hh ? bf16hi(gw[e]) : bf16lo(gw[e]);
+            const float u = hh ? bf16hi(uw[e]) : bf16lo(uw[e]);
+            const float a = da[2 * e + hh];
+            const float sgm = fast_sigmoid(g);
+            const float sg = g * sgm;
+            dgv[hh] = a * wr * u * (sgm * (1.0f + g * (1.0f - sgm)));
+            duv[hh] = a * wr * sg;
+            part += a * sg * u;
+          }
+          dgw[e] = pack_bf16x2(dgv[0], dgv[1]);
+          duw[e] = pack_bf16x2(duv[0], duv[1]);
+        }
+        if (mrow < tc.seg_len) {
+          uint16_t* d = p.c + (tc.seg0 + mrow) * ld1 + f;
+          *reinterpret_cast<uint4*>(d) =
+              make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]);
+          *reinterpret_cast<uint4*>(d + p.F) =
+              make_uint4(duw[0], duw[1], duw[2], duw[3]);
+          rsum[qq] += part;
+        }
+      }
+    };
+    uint4 gA[4], uA[4], gB[4], uB[4];
+    load_gu(0, gA, uA);
+    stage_pass(0);
+    load_gu(1, gB, uB);
+    run_batch(0, gA, uA);
+    load_gu(2, gA, uA);
+    run_batch(1, gB, uB);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // pass 0 readback done
+    stage_pass(1);
+    load_gu(3, gB, uB);
+    run_batch(2, gA, uA);
+    run_batch(3, gB, uB);
+  }
+  if (p.dw_part) {
+    if (act) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float v = rsum[q];
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        if (c4 == 0) red[wn * BM + wm * 128 + 16 * q + (lane >> 2)] = v;
+      }
+    }
+    __syncthreads();
+    if (t < BM) {
+      const int mrow = tc.m0 + t;
+      if (mrow < tc.seg_len) {
+        const float s = ((red[t] + red[BM + t]) + red[2 * BM + t]) +
+                        red[3 * BM + t];
+        p.dw_part[(int64_t)tc.nt * p.rows + tc.seg0 + mrow] = s;
+      }
+    }
+  }
+}
+
+
 // The barrier that publishes the next step sits halfway through the last
 // slice: the next step's first fragment reads overlap the last four MFMAs.
 // (Before the rotation, long K loops did better with it after the step's

@@ -18,9 +18,20 @@
 namespace moe {
 namespace gg {
 
-// N-contiguous operand, eight waves: wave w, instruction j (of 4) fills KiB
-// 8 j + w of the stage = k rows 2 (8 j + w) + lane / 32, each lane the
-// logical chunk that belongs at its slot (the layout McDirect fills).
+// ---- MN-contiguous bf16 operand: direct global -> LDS, transposed reads -----
+// The stage holds the step's 64 k rows of the tile's 256 mn values (512
+// bytes each) as they lie in memory; 16-byte chunk c of row k sits at chunk
+// c ^ 4 (k & 3).  With eight waves, wave w, instruction j (of 4) fills KiB
+// 8 j + w of the stage = k rows 2 (8 j + w) + lane / 32, each lane loading
+// the logical chunk that belongs at its slot.  MFMA fragments come from
+// ds_read_b64_tr_b16: in a group of 16 lanes, lane i receives element i % 4
+// of the 8 bytes addressed by lane 4 j + i / 4 as its element j; with lane
+// 4 j + q addressing row k0 + j, mn mb + 4 q .. +3, lane i gets mn mb + i
+// at k0 .. k0 + 3.  Two such reads (k and k + 4) give a lane its 8 k values;
+// the swizzle puts the 4 rows x 2 groups of a read on 16 distinct chunks (no
+// bank conflicts).  Rows at or past kvalid read as zeros through the buffer
+// descriptor; mn past the operand's end reads the next row (or zeros):
+// those outputs are never stored.
 struct McDirect8 {
   const char* base;  // wave-uniform: element (k = 0, mn = tile start)
   uint32_t rec;      // valid bytes from base
@@ -47,7 +58,7 @@ struct McDirect8 {
     }
   }
   // lane's byte offsets of its nb 32-wide blocks (K slice 0, first of the
-  // two reads) starting at mn chunk xb of the stage rows (McDirect layout)
+  // two reads) starting at mn chunk xb of the stage rows
   template <int NB>
   static __device__ __forceinline__ void frag_offsets(int xb, int lane,
                                                       uint32_t (&o)[NB]) {
@@ -61,11 +72,14 @@ struct McDirect8 {
   }
 };
 
-template <int LA, int LB, int G>
+template <int LA, int LB, int G, int EPI = EPI_STORE>
 __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8b_kernel(Params p) {
   static_assert((G == RAGGED_M && LA == KC && LB == MC) ||
                     (G == RAGGED_K && LA == MC && LB == MC),
                 "backward operand layouts");
+  // the dgrad of the down projection may carry the SwiGLU backward
+  static_assert(EPI == EPI_STORE || (EPI == EPI_SWIGLU_BWD && G == RAGGED_M),
+                "plain store, or the SwiGLU backward on a ragged-M dgrad");
   constexpr int MI = 4, NJ = 2;   // 32-row A / 32-column B blocks of a wave
   constexpr int kSl = 4;          // 16-wide K slices per 64-wide step
   constexpr int kStepK = 64;
@@ -291,18 +305,26 @@ __global__ __launch_bounds__(kThreads8) void grouped_gemm_w8b_kernel(Params p) {
   // every wave is past its last read of the buffers (and every direct load
   // has landed) before they become epilogue staging: 16 KiB per wave
   __syncthreads();
-  if (!act) return;
   char* wbuf = (wave < 2 ? sA0 : wave < 4 ? sB0 : wave < 6 ? sA1 : sB1) +
                (wave & 1) * (kTileBytes / 2);
+  if constexpr (EPI == EPI_SWIGLU_BWD) {
+    // routing weights (128 per wave), then the four N waves' row sums, in
+    // the fifth buffer; every wave meets the row-sum barrier
+    float* misc = reinterpret_cast<float*>(sX4);
+    epilogue_w8_swiglu_bwd(p, tc, acc, n0, wm, wn, lane, t, act, wbuf,
+                           misc + 128 * wave, misc + 128 * 8);
+    return;
+  }
+  if (!act) return;
   epilogue_w8_store<G>(p, tc, acc, n0, wm, wn, lane, wbuf);
 }
 
-template <int LA, int LB, int G>
+template <int LA, int LB, int G, int EPI = EPI_STORE>
 hipError_t launch_w8b(const char* name, const Params& p, int grid,
                       hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   KernelScope ks(name, stream);
-  hipLaunchKernelGGL((grouped_gemm_w8b_kernel<LA, LB, G>), dim3(grid),
+  hipLaunchKernelGGL((grouped_gemm_w8b_kernel<LA, LB, G, EPI>), dim3(grid),
                      dim3(kThreads8), 0, stream, p);
   return hipGetLastError();
 }
